@@ -1,0 +1,227 @@
+/*
+ * ar.h -- C ABI of the barrier-free small/medium-message AllReduce (sum) for N ranks emulated on
+ * one MI355X (gfx950).
+ *
+ * Each emulated rank is a group of co-resident workgroups with its own input, output and block
+ * of a symmetric scratch allocation (Every µs Matters: Achieving Near Speed-of-Light Latency in
+ * GPU Collectives, §II.B "symmetric memory": every participant's object has the same size and
+ * layout and is addressed by participant index plus offset). Ranks exchange data only through
+ * global stores into each other's scratch and polling of their own; no device-wide barrier is
+ * used (§IV "Designing Barrier-Free Collectives"). Latencies measured through this interface are
+ * on-chip (L2 / MALL / HBM), not interconnect latencies.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are plain `void*` from any HIP allocator (hipMalloc, torch); host pointers
+ *     are ordinary host memory. `stream` is a hipStream_t passed as `void*` (NULL = null stream).
+ *   - Integer returns are AR_OK (0) or a negative AR_E* code; ar_last_error() then holds a
+ *     message for the calling thread. Functions returning a pointer return NULL on error.
+ *   - A handle is not thread-safe. Calls on one handle must be issued in order on one stream:
+ *     the sequence number and the scratch reuse depend on call order (as with a communicator).
+ */
+#ifndef LATENCY_COLLECTIVES_AR_H
+#define LATENCY_COLLECTIVES_AR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_INT32 = 2 } ar_dtype;
+
+/*
+ * Algorithms (Every µs Matters, §III.A and §IV; the LL128 atomic two-shot of Fig. 5 as described
+ * in the Pith review of the paper):
+ *   AR_ONESHOT_LL       one-shot push; each 8 bytes travel with their step's sequence number in
+ *                       one 16-byte store, polled as one line (§IV "LL").
+ *   AR_ONESHOT_SENTINEL one-shot push into sentinel-filled scratch, polled until the sentinel is
+ *                       gone, then re-armed (§IV "Sentinel").
+ *   AR_TWOSHOT          reduce-scatter to partition owners + all-gather, sentinel synchronised
+ *                       (§III.A "Two-shot AllReduce").
+ *   AR_LL128_ATOMIC     reduce-scatter by atomic adds into the owner's shared destination, then
+ *                       the two-shot all-gather. fp32 and int32 only. The fp32 summation order
+ *                       is not deterministic.
+ *   AR_BARRIER2         one-shot push between two cross-rank flag barriers: the conventional
+ *                       design whose barrier cost the pages measure (§III.B). A baseline.
+ *   AR_BARRIER_ONLY     (ar_bench only) one cross-rank barrier per iteration, no data: the
+ *                       barrier latency versus N (§III.B, Fig. 3).
+ *   AR_ALGO_AUTO        picks one of the above from the message size.
+ * Every algorithm except AR_LL128_ATOMIC adds in rank order 0..N-1 (fp32 accumulation for
+ * bf16, rounded once to nearest even; wrapping int32) and is bit-reproducible.
+ * Double buffering (§IV "Bidirectional Communication Double Buffering", Fig. 4) is used by
+ * every algorithm except AR_BARRIER2: step s uses scratch buffer s & 1.
+ */
+typedef enum {
+  AR_ALGO_AUTO = 0,
+  AR_ONESHOT_LL = 1,
+  AR_ONESHOT_SENTINEL = 2,
+  AR_TWOSHOT = 3,
+  AR_LL128_ATOMIC = 4,
+  AR_BARRIER2 = 5,
+  AR_BARRIER_ONLY = 6
+} ar_algo;
+
+enum {
+  AR_OK = 0,
+  AR_EINVAL = -1,   /* bad argument */
+  AR_ETOOBIG = -2,  /* count * sizeof(dtype) > max_bytes of the handle */
+  AR_ENOTSUP = -3,  /* algorithm / dtype combination not provided */
+  AR_EHIP = -4,     /* a HIP runtime call failed */
+  AR_ETIMEOUT = -5, /* a poll timed out on the device; the handle is poisoned (sticky) */
+  AR_ENORES = -6    /* the workgroups of all ranks cannot be co-resident */
+};
+
+/* Placement of the emulated ranks on the XCDs (ar_set_option AR_OPT_PLACEMENT, ar_sol). */
+typedef enum { AR_PLACE_XCD = 0, AR_PLACE_SAME = 1, AR_PLACE_LINEAR = 2 } ar_placement;
+
+typedef struct ar_handle ar_handle;
+
+/*
+ * ar_create: build a handle for `nranks` emulated ranks (1..16) exchanging messages of up to
+ * `max_bytes` bytes per rank (1..2^31-1) of `dtype`.
+ *
+ * Allocates the symmetric scratch in device memory (one allocation, rank r's block at
+ * base + r * stride) and fills it: LL lines, atomic destinations, counters and barrier flags
+ * with zeros, sentinel slots with the dtype's sentinel (fp32 0xFFFFFFFF, bf16 0xFFFF: negative
+ * quiet NaNs, compared bitwise; int32 INT32_MIN). The sequence number starts at 1. Scratch
+ * per rank per protocol is capped by the environment variables AR_SCRATCH_ONESHOT and
+ * AR_SCRATCH_TWOSHOT (bytes, default 256 MiB each); larger messages are sent in equal chunks.
+ * AR_POLL_TIMEOUT_US sets the initial poll timeout (default 2000000).
+ * Synchronous on the current device. Returns NULL on error (see ar_last_error()).
+ *
+ * Caller obligation (§IV "Sentinel"): input values must never equal the sentinel bit pattern.
+ */
+ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype);
+
+/*
+ * ar_allreduce: out[r][i] = in[0][i] + in[1][i] + ... + in[N-1][i] for every rank r and element
+ * i < count (Every µs Matters, §III.A: after the collective every rank holds the complete
+ * reduction).
+ *   in, out : host arrays of N device pointers, each to count * sizeof(dtype) bytes, 16-byte
+ *             aligned. out[r] == in[r] (in place) is allowed; any other overlap is AR_EINVAL.
+ *   count   : elements per rank; 0 is a no-op (the sequence number still advances).
+ *   algo    : see ar_algo; AR_BARRIER_ONLY is not accepted here.
+ *   stream  : hipStream_t; the call only enqueues work and returns.
+ * The caller keeps ownership of every buffer; they must stay valid until the stream has run
+ * the work. Device timeouts are reported asynchronously through ar_check().
+ */
+int ar_allreduce(ar_handle* h, const void* const in[], void* const out[], size_t count,
+                 ar_algo algo, void* stream);
+
+/* ar_destroy: synchronise the handle's last stream and free everything. NULL is ignored. */
+void ar_destroy(ar_handle* h);
+
+/* ar_last_error: message of the last failing call on this thread ("" if none). */
+const char* ar_last_error(void);
+
+/*
+ * ar_check: wait for the work of the handle's last stream and report a device-side poll
+ * timeout. Returns AR_OK, AR_ETIMEOUT (the message names rank, peer, step and algorithm; the
+ * handle stays poisoned and every later call returns AR_ETIMEOUT) or AR_EHIP.
+ */
+int ar_check(ar_handle* h);
+
+/*
+ * ar_bench: run `iters` AllReduces back to back inside ONE persistent launch, with no host
+ * involvement between iterations. Iteration k uses input/output set k % nsets:
+ *   in_sets, out_sets : host arrays of nsets * N device pointers, set-major (set j, rank r at
+ *                       index j * N + r); nsets in [1, 65536].
+ *   t_start, t_end    : host arrays of iters * N entries (iteration-major) receiving, per
+ *                       iteration and rank, the device wall-clock tick at which the rank's
+ *                       first wave entered the iteration (before its first input load) and the
+ *                       tick at which its last wave had completed its last output store.
+ *                       Either may be NULL to skip timestamps.
+ *   elapsed_ms        : if not NULL, the launch's duration from HIP events on `stream`.
+ * Synchronous. Ticks convert to seconds with ar_wallclock_hz(). AR_BARRIER_ONLY measures one
+ * cross-rank barrier per iteration and ignores the data arguments (they may be NULL).
+ */
+int ar_bench(ar_handle* h, const void* const* in_sets, void* const* out_sets, int nsets,
+             size_t count, ar_algo algo, int iters, uint64_t* t_start, uint64_t* t_end,
+             double* elapsed_ms, void* stream);
+
+/* Rate of the device wall clock used by ar_bench and ar_sol, in Hz (0 on error). */
+double ar_wallclock_hz(void);
+
+/*
+ * Per-handle options (defaults in brackets). Values are checked; AR_EINVAL when out of range.
+ *   AR_OPT_TIMEOUT_US    poll timeout in microseconds [AR_POLL_TIMEOUT_US or 2000000]
+ *   AR_OPT_WITHHOLD_RANK fault injection: this rank sends nothing, so its peers' polls time out
+ *                        and ar_check reports AR_ETIMEOUT [-1 = off]
+ *   AR_OPT_CTAS          workgroups per rank [0 = chosen from the message size]
+ *   AR_OPT_THREADS       threads per workgroup, 64, 128 or 256 [0 = chosen]
+ *   AR_OPT_PLACEMENT     ar_placement of ranks on XCDs [AR_PLACE_XCD]
+ *   AR_OPT_DRIFT         ar_bench only: each rank sleeps a pseudo-random 0..value units of ~3 µs
+ *                        before each iteration, to stress the double-buffer credits [0]
+ */
+typedef enum {
+  AR_OPT_TIMEOUT_US = 0,
+  AR_OPT_WITHHOLD_RANK = 1,
+  AR_OPT_CTAS = 2,
+  AR_OPT_THREADS = 3,
+  AR_OPT_PLACEMENT = 4,
+  AR_OPT_DRIFT = 5
+} ar_option;
+int ar_set_option(ar_handle* h, ar_option opt, int64_t value);
+
+/*
+ * Scratch regions (for tests that check that sentinel slots are re-armed after a call).
+ * ar_read_region copies `bytes` bytes of region `region` of rank `rank` to host memory
+ * (synchronous, after the handle's last stream has finished); ar_region_bytes gives the size.
+ *   0 = one-shot / reduce-scatter sentinel slots  1 = all-gather sentinel slots
+ *   2 = LL lines  3 = atomic destination  4 = arrival counters  5 = barrier flags
+ *   6 = barrier-baseline data
+ */
+int64_t ar_region_bytes(ar_handle* h, int region);
+int ar_read_region(ar_handle* h, int rank, int region, void* host_dst, size_t bytes);
+
+/* Sequence number the next step will use. */
+uint64_t ar_epoch(ar_handle* h);
+
+/*
+ * ar_sol: speed-of-light microbenchmarks on the current device (the pages' bound
+ * L_SoL = 2 * L_L2 + L_remote_store; Every µs Matters §VI as summarised in the Pith review).
+ * `placement` is AR_PLACE_XCD (the two workgroups of the ping-pong on different XCDs) or
+ * AR_PLACE_SAME (same XCD). Fills `res` (all latencies in nanoseconds). Synchronous.
+ */
+typedef struct {
+  double fence_ns;         /* plain store + agent-scope release fence, per iteration        */
+  double l2_load_ns;       /* dependent load, 1 MiB footprint (L2 hit, per-CU cache miss)    */
+  double coherent_load_ns; /* dependent load with the agent-coherent (sc1) policy, 1 MiB     */
+  double mall_load_ns;     /* dependent load, 64 MiB footprint (beyond L2)                   */
+  double hbm_load_ns;      /* dependent load, 1 GiB footprint (beyond the 256 MiB MALL)      */
+  double store_half_rtt_ns;/* store -> poll ping-pong (sc1 store, sc1 poll), half round trip */
+  double floor_ns;         /* 2 * l2_load_ns + store_half_rtt_ns                             */
+  double floor_fence_ns;   /* the pages' form: 2 * fence_ns + store_half_rtt_ns              */
+  int xcc_a, xcc_b;        /* XCC ids the two ping-pong workgroups ran on                     */
+} ar_sol_result;
+int ar_sol(int placement, ar_sol_result* res);
+
+/*
+ * ar_pingpong: the store -> poll ping-pong alone with explicit cache policies, for studying
+ * the coherence options. store_policy / load_policy: 0 plain, 1 sc0, 2 nt, 16 sc1, 17 sc0|sc1.
+ * Returns the half round trip in nanoseconds through *half_rtt_ns; xcc ids through xcc[2].
+ */
+int ar_pingpong(int placement, int store_policy, int load_policy, int rounds, double* half_rtt_ns,
+                int* xcc);
+
+/*
+ * ar_torn_lines: 16-byte single-copy atomicity probe. One workgroup rewrites `nlines` 16-byte
+ * lines (1..64) `gens` times with one 16-byte store each while a workgroup on another XCD
+ * (placement AR_PLACE_XCD) or the same XCD reads them; *torn counts reads whose four words came
+ * from different writes, *reads the reads made. Synchronous.
+ */
+int ar_torn_lines(int placement, int nlines, int gens, uint64_t* torn, uint64_t* reads);
+
+/*
+ * ar_stream_copy: copy `bytes` (a multiple of 16) from device `src` to device `dst` with a
+ * streaming 16-byte-vector kernel on `stream` (measures achievable HBM bandwidth; scales rocprof
+ * byte counters). Asynchronous.
+ */
+int ar_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LATENCY_COLLECTIVES_AR_H */

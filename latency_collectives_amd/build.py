@@ -1,0 +1,60 @@
+"""Build the HIP library (libar.so) for gfx950 in-tree.
+
+    python -m latency_collectives_amd.build
+
+compiles every ``csrc/*.hip`` file with hipcc into ``latency_collectives_amd/libar.so``.
+"""
+
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libar.so")
+ARCH = os.environ.get("AR_OFFLOAD_ARCH", "gfx950")
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # Never let the compiler form packed fp32 instructions.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library unconditionally and return its path."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = LIB + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed to build libar.so")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def ensure_built() -> str:
+    """Build only when no library exists yet (tests and tools call this)."""
+    if not os.path.exists(LIB):
+        build()
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

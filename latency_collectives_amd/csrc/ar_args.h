@@ -1,0 +1,87 @@
+// Kernel argument block and scratch geometry shared by the host runtime and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace ar {
+
+constexpr int kMaxRanks = 16;
+constexpr int kMaxCtasPerRank = 256;
+constexpr int kMaxWavesPerCta = 4;  // blocks of at most 256 threads
+constexpr int kWave = 64;
+
+// Algorithms (values match ar_algo in include/ar.h).
+enum Algo : int {
+  ALGO_ONESHOT_LL = 1,
+  ALGO_ONESHOT_SENTINEL = 2,
+  ALGO_TWOSHOT = 3,
+  ALGO_LL128_ATOMIC = 4,
+  ALGO_BARRIER2 = 5,
+  ALGO_BARRIER_ONLY = 6,
+};
+
+// How workgroups map to emulated ranks (values match ar_placement in include/ar.h).
+enum Placement : int {
+  PLACE_XCD = 0,     // rank r on XCD r % 8 (workgroups are dispatched round-robin over XCDs)
+  PLACE_SAME = 1,    // every rank on XCD 0
+  PLACE_LINEAR = 2,  // rank = workgroup / ctas (each rank spread over all XCDs)
+};
+
+// One protocol region inside every rank's block of the symmetric scratch allocation.
+struct Region {
+  uint64_t off;    // byte offset of the region inside a rank block
+  uint32_t bytes;  // region bytes per rank
+  uint32_t slot;   // bytes of one (buffer, source) slot, or of one buffer for `acc`
+};
+
+// Control words (device memory). The host-visible status copy lives in pinned host memory.
+enum Ctl : int {
+  CTL_ABORT = 0,   // set to 1 by the first wave that times out; polls give up when they see it
+  CTL_WORDS = 16,
+};
+enum Status : int {
+  ST_CODE = 0,     // 0 ok, 1 poll timed out
+  ST_RANK = 1,
+  ST_PEER = 2,
+  ST_STEP_LO = 3,
+  ST_STEP_HI = 4,
+  ST_ALGO = 5,
+  ST_WORDS = 8,
+};
+
+struct Args {
+  const void* in[kMaxRanks];
+  void* out[kMaxRanks];
+  const void* const* in_tab;  // optional device table [nsets][nranks] (persistent benchmark)
+  void* const* out_tab;
+  uint8_t* base;              // symmetric scratch: rank r's block starts at base + r * stride
+  uint64_t stride;
+  Region p1;    // one-shot sentinel slots / two-shot reduce-scatter slots (sentinel)
+  Region p2;    // two-shot all-gather slots (sentinel)
+  Region ll;    // one-shot LL lines (zeroed, epoch flags)
+  Region acc;   // LL128-style shared atomic destination (zeroed)
+  Region cnt;   // LL128-style arrival counters [buf][cta][wave] (zeroed)
+  Region bar;   // barrier flags [src][cta] (zeroed, monotonic)
+  Region bdat;  // barrier-baseline data slots [src] (single buffer, plain)
+  uint32_t* ctl;        // device control words
+  uint32_t* status;     // host-mapped status words (pinned host memory)
+  uint64_t* ts_start;   // optional [iters][nranks][ctas][waves] timestamps
+  uint64_t* ts_end;
+  uint64_t e0;          // sequence number of the first step of this launch
+  uint64_t timeout_ticks;
+  uint32_t nbytes;      // bytes per rank
+  uint32_t chunk_units; // units per chunk: one-shot message chunk, or two-shot partition chunk
+  uint32_t part_units;  // two-shot partition size in units (a multiple of chunk_units)
+  int nranks;
+  int ctas;             // workgroups per rank
+  int ranks_per_xcd;
+  int placement;
+  int iters;
+  int chunks;
+  int nsets;
+  int withhold;         // fault injection: this rank sends nothing (-1: off)
+  int drift;            // rank-drift stress: up to this many sleeps per iteration (0: off)
+  int algo;
+};
+
+}  // namespace ar

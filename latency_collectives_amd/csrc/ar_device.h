@@ -1,0 +1,260 @@
+// Device-side primitives for the barrier-free AllReduce kernels (gfx950 / CDNA4).
+//
+// Memory access model. Every access to scratch goes through a buffer resource descriptor that
+// covers exactly one region, so an access outside that region is dropped by the hardware instead
+// of faulting. Accesses that another rank (another group of workgroups, usually on another XCD
+// with its own L2) must observe carry the agent-coherent cache policy `sc1`: it is what the
+// compiler emits for agent-scope relaxed atomic loads and stores on gfx950, here applied to
+// 16-byte vector accesses. Poll loops put a compiler memory clobber between iterations so the
+// load is re-issued every time.
+//
+// Synchronisation techniques (Every µs Matters: Achieving Near Speed-of-Light Latency in GPU
+// Collectives, §IV "Designing Barrier-Free Collectives"):
+//   * LL: one 16-byte store carries 8 bytes of payload and an 8-byte flag equal to the step's
+//     sequence number; the receiver polls the line until the flag matches (§IV "LL").
+//   * Sentinel: scratch is pre-filled with a value that valid data never takes; the receiver
+//     polls until no element equals it, then writes the sentinel back (§IV "Sentinel").
+//   * Double buffering: step s uses buffer s & 1; receiving a peer's data for step s+1 is the
+//     credit to overwrite that peer's buffer of step s (§IV "Bidirectional Communication Double
+//     Buffering", Fig. 4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ar {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// gfx950 cache-policy bits of the `aux` operand of buffer instructions.
+constexpr int kPlain = 0;
+constexpr int kSc0 = 1;
+constexpr int kNt = 2;
+constexpr int kSc1 = 16;
+// Agent-coherent policy used for every cross-rank access (loads and stores).
+constexpr int kCoh = kSc1;
+
+// Data-format word of a raw (untyped, stride 0) buffer descriptor on CDNA: 32-bit data format.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+template <int CP>
+__device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ void st16(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ u32x2 ld8(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ void st8(rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ uint32_t ld4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ void st4(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ uint16_t ld2(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ void st2(rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, CP);
+}
+
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Agent-scope release / acquire (what the compiler emits for HIP agent-scope fences).
+__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Constant-rate device clock shared by all CUs (100 MHz on MI300-class parts).
+__device__ __forceinline__ uint64_t now_ticks() {
+  compiler_fence();
+  uint64_t t = wall_clock64();
+  compiler_fence();
+  return t;
+}
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xFu;
+}
+
+// ------------------------------------------------------------------ data types
+
+enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_I32 = 2 };
+
+template <int DT>
+struct Ty;
+template <>
+struct Ty<DT_F32> {
+  static constexpr int kElem = 4;
+  static constexpr uint32_t kSentinelWord = 0xFFFFFFFFu;  // negative quiet NaN, all mantissa set
+  __device__ static bool word_clear(uint32_t w) { return w != 0xFFFFFFFFu; }
+};
+template <>
+struct Ty<DT_BF16> {
+  static constexpr int kElem = 2;
+  static constexpr uint32_t kSentinelWord = 0xFFFFFFFFu;  // two bf16 negative quiet NaNs
+  __device__ static bool word_clear(uint32_t w) {
+    return (w & 0xFFFFu) != 0xFFFFu && (w >> 16) != 0xFFFFu;
+  }
+};
+template <>
+struct Ty<DT_I32> {
+  static constexpr int kElem = 4;
+  static constexpr uint32_t kSentinelWord = 0x80000000u;  // INT32_MIN, outside valid sums
+  __device__ static bool word_clear(uint32_t w) { return w != 0x80000000u; }
+};
+
+// binary32 -> bfloat16, round to nearest even, by the add-bias method: adding 0x7FFF plus the
+// kept low bit makes exact halfway cases carry only when the kept part is odd.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Fixed rank-order fold of W 32-bit payload words. Binary32 accumulation for fp32 and bf16
+// (bf16 rounded once when the result is packed), wrapping 32-bit integer addition for int32.
+template <int DT, int W>
+struct Fold;
+template <int W>
+struct Fold<DT_F32, W> {
+  float a[W];
+  __device__ __forceinline__ void init(const uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) a[i] = __uint_as_float(w[i]);
+  }
+  __device__ __forceinline__ void add(const uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) a[i] = a[i] + __uint_as_float(w[i]);
+  }
+  __device__ __forceinline__ void pack(uint32_t* w) const {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = __float_as_uint(a[i]);
+  }
+};
+template <int W>
+struct Fold<DT_BF16, W> {
+  float a[2 * W];
+  __device__ __forceinline__ void init(const uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      a[2 * i] = __uint_as_float(w[i] << 16);
+      a[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ __forceinline__ void add(const uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      a[2 * i] = a[2 * i] + __uint_as_float(w[i] << 16);
+      a[2 * i + 1] = a[2 * i + 1] + __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ __forceinline__ void pack(uint32_t* w) const {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = bf16_rne(a[2 * i]) | (bf16_rne(a[2 * i + 1]) << 16);
+  }
+};
+template <int W>
+struct Fold<DT_I32, W> {
+  uint32_t a[W];
+  __device__ __forceinline__ void init(const uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) a[i] = w[i];
+  }
+  __device__ __forceinline__ void add(const uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) a[i] = a[i] + w[i];
+  }
+  __device__ __forceinline__ void pack(uint32_t* w) const {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = a[i];
+  }
+};
+
+template <int DT>
+__device__ __forceinline__ bool vec_clear(u32x4 v) {
+  return Ty<DT>::word_clear(v.x) && Ty<DT>::word_clear(v.y) && Ty<DT>::word_clear(v.z) &&
+         Ty<DT>::word_clear(v.w);
+}
+
+// ------------------------------------------------------------------ user buffers
+
+// Load one unit (UB bytes, 8 or 16) of a user buffer of `nbytes` bytes at byte offset `off`.
+// A unit that runs past the end is assembled element by element and zero-padded; a unit wholly
+// past the end reads as zeros.
+template <int DT, int UB>
+__device__ __forceinline__ void load_unit(rsrc_t r, uint32_t off, uint32_t nbytes, uint32_t* w) {
+  if (off + UB <= nbytes) {
+    if constexpr (UB == 16) {
+      u32x4 v = ld16<kPlain>(r, off);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+      u32x2 v = ld8<kPlain>(r, off);
+      w[0] = v.x; w[1] = v.y;
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < UB / 4; ++i) w[i] = 0u;
+  if (off >= nbytes) return;
+  if constexpr (Ty<DT>::kElem == 4) {
+    for (int i = 0; i < UB / 4; ++i)
+      if (off + 4u * i < nbytes) w[i] = ld4<kPlain>(r, off + 4u * i);
+  } else {
+    for (int i = 0; i < UB / 2; ++i)
+      if (off + 2u * i < nbytes) {
+        uint32_t h = ld2<kPlain>(r, off + 2u * i);
+        w[i >> 1] |= (i & 1) ? (h << 16) : h;
+      }
+  }
+}
+
+// Store one unit to a user buffer, dropping the bytes past `nbytes`.
+template <int DT, int UB, int CP = kPlain>
+__device__ __forceinline__ void store_unit(rsrc_t r, uint32_t off, uint32_t nbytes,
+                                           const uint32_t* w) {
+  if (off + UB <= nbytes) {
+    if constexpr (UB == 16) {
+      st16<CP>(r, off, u32x4{w[0], w[1], w[2], w[3]});
+    } else {
+      st8<CP>(r, off, u32x2{w[0], w[1]});
+    }
+    return;
+  }
+  if (off >= nbytes) return;
+  if constexpr (Ty<DT>::kElem == 4) {
+    for (int i = 0; i < UB / 4; ++i)
+      if (off + 4u * i < nbytes) st4<CP>(r, off + 4u * i, w[i]);
+  } else {
+    for (int i = 0; i < UB / 2; ++i)
+      if (off + 2u * i < nbytes) {
+        uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+        st2<CP>(r, off + 2u * i, static_cast<uint16_t>(h));
+      }
+  }
+}
+
+}  // namespace ar

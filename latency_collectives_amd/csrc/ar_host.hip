@@ -1,0 +1,602 @@
+// Host runtime and C ABI: handle, symmetric scratch allocator, sequence numbers, launch
+// geometry, the persistent benchmark driver and error reporting.
+//
+// Scratch layout (one device allocation; rank r's block at base + r * stride, every region at the
+// same offset in every block, as in symmetric memory, Every µs Matters §II.B):
+//   p1   [buffer 2][source N][slot]   sentinel   one-shot slots / two-shot reduce-scatter slots
+//   p2   [buffer 2][source N][slot]   sentinel   two-shot all-gather slots
+//   ll   [buffer 2][source N][slot]   zero       LL lines, 16 bytes per 8 bytes of payload
+//   acc  [buffer 2][slot]             zero       LL128-style shared atomic destination
+//   cnt  [buffer 2][cta][wave] u32    zero       LL128-style arrival counters
+//   bar  [source][cta] u64            zero       barrier flags (monotonic)
+//   bdat [source N][slot]             any        barrier-baseline data slots
+// The two buffers implement double buffering: step s uses buffer s & 1 (Fig. 4 and §IV
+// "Bidirectional Communication Double Buffering"; Fig. 7's per-epoch alternating sub-buffers).
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/ar.h"
+#include "ar_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+constexpr int kRegions = 7;
+enum RegionId { RG_P1 = 0, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT };
+constexpr uint64_t kDefaultCap = 256ull << 20;
+constexpr uint64_t kMaxCap = 1ull << 31;
+constexpr int kXcds = 8;
+
+uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+uint64_t ceil_div(uint64_t x, uint64_t a) { return (x + a - 1) / a; }
+
+uint64_t env_u64(const char* name, uint64_t dflt) {
+  const char* v = std::getenv(name);
+  if (v == nullptr || *v == '\0') return dflt;
+  char* end = nullptr;
+  unsigned long long x = std::strtoull(v, &end, 10);
+  if (end == v) return dflt;
+  return static_cast<uint64_t>(x);
+}
+
+int elem_bytes(int dt) { return dt == AR_BFLOAT16 ? 2 : 4; }
+
+uint32_t sentinel_word(int dt) { return dt == AR_INT32 ? 0x80000000u : 0xFFFFFFFFu; }
+
+std::mutex g_occ_mu;
+std::map<const void*, int> g_occ;
+
+int occupancy(ar_kernel_fn fn, int threads) {
+  std::lock_guard<std::mutex> lk(g_occ_mu);
+  const void* key = reinterpret_cast<const void*>(fn);
+  auto key2 = reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(key) ^ threads);
+  auto it = g_occ.find(key2);
+  if (it != g_occ.end()) return it->second;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn),
+                                                   threads, 0) != hipSuccess)
+    nb = 0;
+  g_occ[key2] = nb;
+  return nb;
+}
+
+}  // namespace
+
+int ar_fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ar_fail_hip(hipError_t e, const char* what) {
+  return ar_fail(AR_EHIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+struct ar_handle {
+  int nranks = 0;
+  int dtype = 0;
+  size_t max_bytes = 0;
+  int device = 0;
+  uint8_t* base = nullptr;
+  uint64_t stride = 0;
+  ar::Region rg[kRegions] = {};
+  uint32_t* ctl = nullptr;          // device control words
+  uint32_t* status_host = nullptr;  // pinned host status words
+  uint32_t* status_dev = nullptr;   // device view of the same memory
+  uint64_t epoch = 1;
+  bool poisoned = false;
+  int64_t timeout_us = 2000000;
+  int withhold = -1;
+  int ctas = 0;
+  int threads = 0;
+  int placement = AR_PLACE_XCD;
+  int drift = 0;
+  void** tab = nullptr;
+  size_t tab_cap = 0;
+  uint64_t* ts = nullptr;
+  size_t ts_cap = 0;
+  hipStream_t last_stream = nullptr;
+  int cu_count = 0;
+  double clock_hz = 0.0;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+};
+
+namespace {
+
+struct Launch {
+  ar_kernel_fn fn = nullptr;
+  int chunks = 1;
+  uint32_t chunk_units = 0;
+  uint32_t part_units = 0;
+  int threads = 64;
+  int ctas = 1;
+  int ranks_per_xcd = 1;
+  unsigned grid = 1;
+};
+
+// Chunk geometry and launch shape for one AllReduce of `nbytes` bytes per rank.
+int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
+  const int N = h->nranks;
+  const int nmax = N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16;
+  L.fn = ar_select_kernel(algo, h->dtype, nmax);
+  if (L.fn == nullptr)
+    return ar_fail(AR_ENOTSUP, "algorithm %d is not provided for dtype %d", algo, h->dtype);
+  uint64_t cap_units = 0, units = 0;
+  switch (algo) {
+    case AR_ONESHOT_LL:
+      units = ceil_div(nbytes, 8);
+      cap_units = h->rg[RG_LL].slot / 16;
+      break;
+    case AR_ONESHOT_SENTINEL:
+      units = ceil_div(nbytes, 16);
+      cap_units = h->rg[RG_P1].slot / 16;
+      break;
+    case AR_BARRIER2:
+      units = ceil_div(nbytes, 16);
+      cap_units = h->rg[RG_BDAT].slot / 16;
+      break;
+    case AR_TWOSHOT:
+    case AR_LL128_ATOMIC:
+      units = ceil_div(ceil_div(nbytes, 16), N);  // one partition
+      cap_units = std::min({h->rg[RG_P1].slot, h->rg[RG_P2].slot, h->rg[RG_ACC].slot}) / 16;
+      break;
+    case AR_BARRIER_ONLY:
+      units = 0;
+      cap_units = 1;
+      break;
+    default:
+      return ar_fail(AR_EINVAL, "unknown algorithm %d", algo);
+  }
+  if (cap_units == 0) return ar_fail(AR_EINVAL, "scratch slots are too small");
+  const uint64_t K = units == 0 ? 1 : ceil_div(units, cap_units);
+  const uint64_t C = units == 0 ? 0 : ceil_div(units, K);
+  L.chunks = static_cast<int>(K);
+  L.chunk_units = static_cast<uint32_t>(C);
+  L.part_units = static_cast<uint32_t>(K * C);
+  L.threads = h->threads ? h->threads : (C <= 64 ? 64 : 256);
+  const int occ = occupancy(L.fn, L.threads);
+  if (occ <= 0) return ar_fail(AR_ENORES, "kernel cannot be resident with %d threads", L.threads);
+  const int cus_per_xcd = std::max(1, h->cu_count / kXcds);
+  int max_ctas;
+  if (h->placement == AR_PLACE_XCD) {
+    L.ranks_per_xcd = static_cast<int>(ceil_div(N, kXcds));
+    max_ctas = cus_per_xcd * occ / L.ranks_per_xcd;
+  } else if (h->placement == AR_PLACE_SAME) {
+    max_ctas = cus_per_xcd * occ / N;
+  } else {
+    max_ctas = h->cu_count * occ / N;
+  }
+  max_ctas = std::min(max_ctas, ar::kMaxCtasPerRank);
+  if (max_ctas < 1) return ar_fail(AR_ENORES, "%d ranks cannot be co-resident", N);
+  int ctas = h->ctas;
+  if (ctas == 0) {
+    const uint64_t want = std::max<uint64_t>(1, ceil_div(C, static_cast<uint64_t>(L.threads)));
+    ctas = static_cast<int>(std::min<uint64_t>(want, static_cast<uint64_t>(max_ctas)));
+  }
+  if (ctas > max_ctas)
+    return ar_fail(AR_ENORES, "%d workgroups per rank exceed the co-resident limit %d", ctas,
+                   max_ctas);
+  L.ctas = ctas;
+  if (h->placement == AR_PLACE_XCD)
+    L.grid = static_cast<unsigned>(kXcds * L.ranks_per_xcd * ctas);
+  else if (h->placement == AR_PLACE_SAME)
+    L.grid = static_cast<unsigned>(kXcds * N * ctas);
+  else
+    L.grid = static_cast<unsigned>(N * ctas);
+  return AR_OK;
+}
+
+ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
+  ar::Args a;
+  std::memset(&a, 0, sizeof a);
+  a.base = h->base;
+  a.stride = h->stride;
+  a.p1 = h->rg[RG_P1];
+  a.p2 = h->rg[RG_P2];
+  a.ll = h->rg[RG_LL];
+  a.acc = h->rg[RG_ACC];
+  a.cnt = h->rg[RG_CNT];
+  a.bar = h->rg[RG_BAR];
+  a.bdat = h->rg[RG_BDAT];
+  a.ctl = h->ctl;
+  a.status = h->status_dev;
+  a.e0 = h->epoch;
+  const double ticks = static_cast<double>(h->timeout_us) * h->clock_hz * 1e-6;
+  a.timeout_ticks = ticks < 1.0 ? 1ull : static_cast<uint64_t>(ticks);
+  a.nbytes = static_cast<uint32_t>(nbytes);
+  a.chunk_units = L.chunk_units;
+  a.part_units = L.part_units;
+  a.nranks = h->nranks;
+  a.ctas = L.ctas;
+  a.ranks_per_xcd = L.ranks_per_xcd;
+  a.placement = h->placement;
+  a.iters = 1;
+  a.chunks = L.chunks;
+  a.nsets = 1;
+  a.withhold = h->withhold;
+  a.drift = 0;
+  a.algo = algo;
+  return a;
+}
+
+int resolve_algo(ar_handle* h, int algo, uint64_t nbytes) {
+  if (algo != AR_ALGO_AUTO) return algo;
+  // Provisional size rule (one-shot for small messages, two-shot for large ones, as on the
+  // pages' §VIII selection); thresholds to be replaced by measured ones.
+  if (h->nranks == 1) return AR_ONESHOT_SENTINEL;
+  if (nbytes <= 2048) return AR_ONESHOT_LL;
+  if (nbytes <= (256u << 10)) return AR_ONESHOT_SENTINEL;
+  return AR_TWOSHOT;
+}
+
+bool overlap(const void* a, const void* b, uint64_t n) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + n && y < x + n;
+}
+
+int check_status(ar_handle* h) {
+  if (h->poisoned) return ar_fail(AR_ETIMEOUT, "handle is poisoned by an earlier poll timeout");
+  const uint32_t code = __atomic_load_n(&h->status_host[ar::ST_CODE], __ATOMIC_ACQUIRE);
+  if (code != 0) {
+    h->poisoned = true;
+    const uint64_t step = (static_cast<uint64_t>(h->status_host[ar::ST_STEP_HI]) << 32) |
+                          h->status_host[ar::ST_STEP_LO];
+    return ar_fail(AR_ETIMEOUT,
+                   "poll timed out on the device: rank %u waiting for peer %d at step %llu "
+                   "(algorithm %u)",
+                   h->status_host[ar::ST_RANK], static_cast<int>(h->status_host[ar::ST_PEER]),
+                   static_cast<unsigned long long>(step), h->status_host[ar::ST_ALGO]);
+  }
+  return AR_OK;
+}
+
+int launch(ar_kernel_fn fn, unsigned grid, int threads, ar::Args& a, hipStream_t stream) {
+  void* args[] = {&a};
+  AR_HIP(hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(threads), args, 0,
+                         stream));
+  return AR_OK;
+}
+
+void release(ar_handle* h) {
+  if (h->base) (void)hipFree(h->base);
+  if (h->ctl) (void)hipFree(h->ctl);
+  if (h->status_host) (void)hipHostFree(h->status_host);
+  if (h->tab) (void)hipFree(h->tab);
+  if (h->ts) (void)hipFree(h->ts);
+  if (h->ev0) (void)hipEventDestroy(h->ev0);
+  if (h->ev1) (void)hipEventDestroy(h->ev1);
+  delete h;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ar_last_error(void) { return g_err.c_str(); }
+
+double ar_wallclock_hz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0.0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0.0;
+  return static_cast<double>(khz) * 1e3;
+}
+
+ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
+  g_err.clear();
+  if (nranks < 1 || nranks > ar::kMaxRanks) {
+    ar_fail(AR_EINVAL, "nranks must be in [1, %d], got %d", ar::kMaxRanks, nranks);
+    return nullptr;
+  }
+  if (max_bytes < 1 || max_bytes > 0x7FFFFFFFull) {
+    ar_fail(AR_EINVAL, "max_bytes must be in [1, 2^31 - 1], got %zu", max_bytes);
+    return nullptr;
+  }
+  if (dtype != AR_FLOAT32 && dtype != AR_BFLOAT16 && dtype != AR_INT32) {
+    ar_fail(AR_EINVAL, "unknown dtype %d", static_cast<int>(dtype));
+    return nullptr;
+  }
+  ar_handle* h = new ar_handle();
+  h->nranks = nranks;
+  h->dtype = dtype;
+  h->max_bytes = max_bytes;
+  const int N = nranks;
+  const uint64_t cap_os = std::min(env_u64("AR_SCRATCH_ONESHOT", kDefaultCap), kMaxCap);
+  const uint64_t cap_ts = std::min(env_u64("AR_SCRATCH_TWOSHOT", kDefaultCap), kMaxCap);
+  h->timeout_us = static_cast<int64_t>(env_u64("AR_POLL_TIMEOUT_US", 2000000));
+  auto fail = [&](hipError_t e, const char* what) {
+    ar_fail_hip(e, what);
+    release(h);
+    return static_cast<ar_handle*>(nullptr);
+  };
+  hipError_t e;
+  if ((e = hipGetDevice(&h->device)) != hipSuccess) return fail(e, "hipGetDevice");
+  if ((e = hipDeviceGetAttribute(&h->cu_count, hipDeviceAttributeMultiprocessorCount,
+                                 h->device)) != hipSuccess)
+    return fail(e, "hipDeviceGetAttribute");
+  h->clock_hz = ar_wallclock_hz();
+  if (h->clock_hz <= 0.0) h->clock_hz = 100e6;
+
+  // Slot sizes: large enough for the whole message unless the per-protocol cap says otherwise.
+  const uint64_t need_os = round_up(max_bytes, 16);
+  const uint64_t need_ts = ceil_div(ceil_div(max_bytes, 16), N) * 16;
+  const uint64_t per_slot_os = std::max<uint64_t>(256, (cap_os / (2 * N)) / 256 * 256);
+  const uint64_t per_slot_ts = std::max<uint64_t>(256, (cap_ts / (2 * N)) / 256 * 256);
+  const uint64_t slot_os = std::min(round_up(need_os, 256), per_slot_os);
+  const uint64_t slot_ts = std::min(round_up(need_ts, 256), per_slot_ts);
+  const uint64_t ll_payload = std::min(round_up(max_bytes, 8), std::max<uint64_t>(128, per_slot_os / 2));
+  const uint64_t slot_ll = round_up(2 * ll_payload, 256);
+  struct { uint64_t slot, bytes; } sz[kRegions];
+  sz[RG_P1] = {std::max(slot_os, slot_ts), 2ull * N * std::max(slot_os, slot_ts)};
+  sz[RG_P2] = {slot_ts, 2ull * N * slot_ts};
+  sz[RG_LL] = {slot_ll, 2ull * N * slot_ll};
+  sz[RG_ACC] = {slot_ts, 2ull * slot_ts};
+  sz[RG_CNT] = {0, 2ull * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 4};
+  sz[RG_BAR] = {0, 1ull * ar::kMaxRanks * ar::kMaxCtasPerRank * 8};
+  sz[RG_BDAT] = {slot_os, 1ull * N * slot_os};
+  uint64_t off = 0;
+  for (int i = 0; i < kRegions; ++i) {
+    if (sz[i].bytes >= (1ull << 32)) {
+      ar_fail(AR_ETOOBIG, "scratch region %d would exceed 4 GiB per rank", i);
+      release(h);
+      return nullptr;
+    }
+    h->rg[i].off = off;
+    h->rg[i].bytes = static_cast<uint32_t>(sz[i].bytes);
+    h->rg[i].slot = static_cast<uint32_t>(sz[i].slot);
+    off = round_up(off + sz[i].bytes, 4096);
+  }
+  h->stride = round_up(off, 1 << 16);
+  const uint64_t total = h->stride * N;
+  if ((e = hipMalloc(reinterpret_cast<void**>(&h->base), total)) != hipSuccess)
+    return fail(e, "hipMalloc(scratch)");
+  if ((e = hipMemset(h->base, 0, total)) != hipSuccess) return fail(e, "hipMemset(scratch)");
+  const uint32_t sw = sentinel_word(dtype);
+  ar_launch_fill(h->base, h->stride, N, h->rg[RG_P1].off, h->rg[RG_P1].bytes, sw, nullptr);
+  ar_launch_fill(h->base, h->stride, N, h->rg[RG_P2].off, h->rg[RG_P2].bytes, sw, nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return fail(e, "scratch fill launch");
+  if ((e = hipMalloc(reinterpret_cast<void**>(&h->ctl), ar::CTL_WORDS * 4)) != hipSuccess)
+    return fail(e, "hipMalloc(ctl)");
+  if ((e = hipMemset(h->ctl, 0, ar::CTL_WORDS * 4)) != hipSuccess) return fail(e, "hipMemset(ctl)");
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&h->status_host), ar::ST_WORDS * 4,
+                         hipHostMallocMapped)) != hipSuccess)
+    return fail(e, "hipHostMalloc(status)");
+  std::memset(h->status_host, 0, ar::ST_WORDS * 4);
+  if ((e = hipHostGetDevicePointer(reinterpret_cast<void**>(&h->status_dev), h->status_host, 0)) !=
+      hipSuccess)
+    return fail(e, "hipHostGetDevicePointer(status)");
+  if ((e = hipEventCreate(&h->ev0)) != hipSuccess) return fail(e, "hipEventCreate");
+  if ((e = hipEventCreate(&h->ev1)) != hipSuccess) return fail(e, "hipEventCreate");
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return fail(e, "hipDeviceSynchronize");
+  h->epoch = 1;
+  return h;
+}
+
+void ar_destroy(ar_handle* h) {
+  if (h == nullptr) return;
+  if (h->last_stream) (void)hipStreamSynchronize(h->last_stream);
+  (void)hipDeviceSynchronize();
+  release(h);
+}
+
+int ar_set_option(ar_handle* h, ar_option opt, int64_t v) {
+  if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
+  switch (opt) {
+    case AR_OPT_TIMEOUT_US:
+      if (v < 1 || v > 3600ll * 1000000ll) return ar_fail(AR_EINVAL, "timeout out of range");
+      h->timeout_us = v;
+      return AR_OK;
+    case AR_OPT_WITHHOLD_RANK:
+      if (v < -1 || v >= h->nranks) return ar_fail(AR_EINVAL, "withhold rank out of range");
+      h->withhold = static_cast<int>(v);
+      return AR_OK;
+    case AR_OPT_CTAS:
+      if (v < 0 || v > ar::kMaxCtasPerRank) return ar_fail(AR_EINVAL, "ctas out of range");
+      h->ctas = static_cast<int>(v);
+      return AR_OK;
+    case AR_OPT_THREADS:
+      if (v != 0 && v != 64 && v != 128 && v != 256)
+        return ar_fail(AR_EINVAL, "threads must be 0, 64, 128 or 256");
+      h->threads = static_cast<int>(v);
+      return AR_OK;
+    case AR_OPT_PLACEMENT:
+      if (v < AR_PLACE_XCD || v > AR_PLACE_LINEAR) return ar_fail(AR_EINVAL, "bad placement");
+      h->placement = static_cast<int>(v);
+      return AR_OK;
+    case AR_OPT_DRIFT:
+      if (v < 0 || v > 1000) return ar_fail(AR_EINVAL, "drift out of range");
+      h->drift = static_cast<int>(v);
+      return AR_OK;
+  }
+  return ar_fail(AR_EINVAL, "unknown option %d", static_cast<int>(opt));
+}
+
+uint64_t ar_epoch(ar_handle* h) { return h ? h->epoch : 0; }
+
+int ar_allreduce(ar_handle* h, const void* const in[], void* const out[], size_t count,
+                 ar_algo algo, void* stream) {
+  if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
+  if (in == nullptr || out == nullptr) return ar_fail(AR_EINVAL, "null pointer table");
+  if (algo < AR_ALGO_AUTO || algo > AR_BARRIER2)
+    return ar_fail(AR_EINVAL, "algorithm %d is not valid for ar_allreduce", static_cast<int>(algo));
+  int rc = check_status(h);
+  if (rc != AR_OK) return rc;
+  const int N = h->nranks;
+  const uint64_t nbytes = static_cast<uint64_t>(count) * elem_bytes(h->dtype);
+  if (count != 0 && nbytes / count != static_cast<uint64_t>(elem_bytes(h->dtype)))
+    return ar_fail(AR_ETOOBIG, "count overflows");
+  if (nbytes > h->max_bytes)
+    return ar_fail(AR_ETOOBIG, "%llu bytes per rank exceed max_bytes %zu",
+                   static_cast<unsigned long long>(nbytes), h->max_bytes);
+  for (int r = 0; r < N; ++r) {
+    if (in[r] == nullptr || out[r] == nullptr)
+      return ar_fail(AR_EINVAL, "null buffer for rank %d", r);
+    if ((reinterpret_cast<uintptr_t>(in[r]) | reinterpret_cast<uintptr_t>(out[r])) & 15u)
+      return ar_fail(AR_EINVAL, "buffers of rank %d are not 16-byte aligned", r);
+  }
+  if (nbytes > 0) {
+    for (int r = 0; r < N; ++r)
+      for (int q = 0; q < N; ++q) {
+        if (q != r && overlap(out[r], out[q], nbytes))
+          return ar_fail(AR_EINVAL, "outputs of ranks %d and %d overlap", r, q);
+        if (overlap(out[r], in[q], nbytes) && !(q == r && out[r] == in[r]))
+          return ar_fail(AR_EINVAL, "output of rank %d overlaps input of rank %d", r, q);
+      }
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (nbytes == 0) {
+    h->epoch += 1;
+    return AR_OK;
+  }
+  const int alg = resolve_algo(h, algo, nbytes);
+  Launch L;
+  rc = plan(h, alg, nbytes, L);
+  if (rc != AR_OK) return rc;
+  ar::Args a = base_args(h, alg, nbytes, L);
+  for (int r = 0; r < N; ++r) {
+    a.in[r] = in[r];
+    a.out[r] = out[r];
+  }
+  rc = launch(L.fn, L.grid, L.threads, a, s);
+  if (rc != AR_OK) return rc;
+  h->epoch += static_cast<uint64_t>(L.chunks);
+  h->last_stream = s;
+  return AR_OK;
+}
+
+int ar_check(ar_handle* h) {
+  if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
+  hipError_t e = h->last_stream ? hipStreamSynchronize(h->last_stream) : hipDeviceSynchronize();
+  if (e != hipSuccess) return ar_fail_hip(e, "synchronize");
+  return check_status(h);
+}
+
+int ar_bench(ar_handle* h, const void* const* in_sets, void* const* out_sets, int nsets,
+             size_t count, ar_algo algo, int iters, uint64_t* t_start, uint64_t* t_end,
+             double* elapsed_ms, void* stream) {
+  if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
+  if (iters < 1 || iters > 1000000) return ar_fail(AR_EINVAL, "iters must be in [1, 1e6]");
+  if (algo < AR_ALGO_AUTO || algo > AR_BARRIER_ONLY)
+    return ar_fail(AR_EINVAL, "unknown algorithm %d", static_cast<int>(algo));
+  int rc = check_status(h);
+  if (rc != AR_OK) return rc;
+  const int N = h->nranks;
+  const bool barrier_only = algo == AR_BARRIER_ONLY;
+  uint64_t nbytes = 0;
+  if (!barrier_only) {
+    if (in_sets == nullptr || out_sets == nullptr) return ar_fail(AR_EINVAL, "null set tables");
+    if (nsets < 1 || nsets > 65536) return ar_fail(AR_EINVAL, "nsets must be in [1, 65536]");
+    nbytes = static_cast<uint64_t>(count) * elem_bytes(h->dtype);
+    if (nbytes == 0) return ar_fail(AR_EINVAL, "ar_bench needs count > 0");
+    if (nbytes > h->max_bytes) return ar_fail(AR_ETOOBIG, "message exceeds max_bytes");
+    for (int i = 0; i < nsets * N; ++i) {
+      if (in_sets[i] == nullptr || out_sets[i] == nullptr)
+        return ar_fail(AR_EINVAL, "null buffer in set table");
+      if ((reinterpret_cast<uintptr_t>(in_sets[i]) | reinterpret_cast<uintptr_t>(out_sets[i])) & 15u)
+        return ar_fail(AR_EINVAL, "set buffers must be 16-byte aligned");
+    }
+  } else {
+    nsets = 1;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int alg = resolve_algo(h, algo, nbytes);
+  Launch L;
+  rc = plan(h, alg, nbytes, L);
+  if (rc != AR_OK) return rc;
+  ar::Args a = base_args(h, alg, nbytes, L);
+  a.iters = iters;
+  a.drift = h->drift;
+  a.nsets = nsets;
+  if (!barrier_only) {
+    const size_t need = 2ull * nsets * N;
+    if (h->tab_cap < need) {
+      if (h->tab) (void)hipFree(h->tab);
+      h->tab = nullptr;
+      h->tab_cap = 0;
+      AR_HIP(hipMalloc(reinterpret_cast<void**>(&h->tab), need * sizeof(void*)));
+      h->tab_cap = need;
+    }
+    std::vector<const void*> host_tab(need);
+    for (size_t i = 0; i < static_cast<size_t>(nsets) * N; ++i) {
+      host_tab[i] = in_sets[i];
+      host_tab[static_cast<size_t>(nsets) * N + i] = out_sets[i];
+    }
+    AR_HIP(hipMemcpy(h->tab, host_tab.data(), need * sizeof(void*), hipMemcpyHostToDevice));
+    a.in_tab = const_cast<const void* const*>(h->tab);
+    a.out_tab = h->tab + static_cast<size_t>(nsets) * N;
+  }
+  const int wpb = L.threads / ar::kWave;
+  const size_t per = static_cast<size_t>(iters) * N * L.ctas * wpb;
+  const bool want_ts = t_start != nullptr || t_end != nullptr;
+  if (want_ts) {
+    if (h->ts_cap < 2 * per) {
+      if (h->ts) (void)hipFree(h->ts);
+      h->ts = nullptr;
+      h->ts_cap = 0;
+      AR_HIP(hipMalloc(reinterpret_cast<void**>(&h->ts), 2 * per * sizeof(uint64_t)));
+      h->ts_cap = 2 * per;
+    }
+    a.ts_start = h->ts;
+    a.ts_end = h->ts + per;
+  }
+  AR_HIP(hipEventRecord(h->ev0, s));
+  rc = launch(L.fn, L.grid, L.threads, a, s);
+  if (rc != AR_OK) return rc;
+  AR_HIP(hipEventRecord(h->ev1, s));
+  h->epoch += static_cast<uint64_t>(iters) * L.chunks;
+  h->last_stream = s;
+  AR_HIP(hipStreamSynchronize(s));
+  rc = check_status(h);
+  if (rc != AR_OK) return rc;
+  if (elapsed_ms != nullptr) {
+    float ms = 0.f;
+    AR_HIP(hipEventElapsedTime(&ms, h->ev0, h->ev1));
+    *elapsed_ms = ms;
+  }
+  if (want_ts) {
+    std::vector<uint64_t> ts(2 * per);
+    AR_HIP(hipMemcpy(ts.data(), h->ts, 2 * per * sizeof(uint64_t), hipMemcpyDeviceToHost));
+    const size_t group = static_cast<size_t>(L.ctas) * wpb;
+    for (size_t g = 0; g < static_cast<size_t>(iters) * N; ++g) {
+      uint64_t lo = UINT64_MAX, hi = 0;
+      for (size_t j = 0; j < group; ++j) {
+        lo = std::min(lo, ts[g * group + j]);
+        hi = std::max(hi, ts[per + g * group + j]);
+      }
+      if (t_start) t_start[g] = lo;
+      if (t_end) t_end[g] = hi;
+    }
+  }
+  return AR_OK;
+}
+
+int64_t ar_region_bytes(ar_handle* h, int region) {
+  if (h == nullptr || region < 0 || region >= kRegions) return ar_fail(AR_EINVAL, "bad region");
+  return static_cast<int64_t>(h->rg[region].bytes);
+}
+
+int ar_read_region(ar_handle* h, int rank, int region, void* host_dst, size_t bytes) {
+  if (h == nullptr || host_dst == nullptr) return ar_fail(AR_EINVAL, "null argument");
+  if (rank < 0 || rank >= h->nranks || region < 0 || region >= kRegions)
+    return ar_fail(AR_EINVAL, "bad rank or region");
+  if (bytes > h->rg[region].bytes) return ar_fail(AR_EINVAL, "read past the region");
+  if (h->last_stream) AR_HIP(hipStreamSynchronize(h->last_stream));
+  AR_HIP(hipDeviceSynchronize());
+  AR_HIP(hipMemcpy(host_dst, h->base + static_cast<uint64_t>(rank) * h->stride + h->rg[region].off,
+                   bytes, hipMemcpyDeviceToHost));
+  return AR_OK;
+}
+
+}  // extern "C"

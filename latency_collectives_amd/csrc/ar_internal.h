@@ -1,0 +1,24 @@
+// Host-side declarations shared by the runtime translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ar_args.h"
+
+typedef void (*ar_kernel_fn)(ar::Args);
+
+// Defined in ar_kernels.hip.
+ar_kernel_fn ar_select_kernel(int algo, int dt, int nmax);
+void ar_launch_fill(uint8_t* base, uint64_t stride, int nranks, uint64_t off, uint32_t bytes,
+                    uint32_t word, hipStream_t stream);
+
+// Defined in ar_host.hip: record an error message for ar_last_error() and return `code`.
+int ar_fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int ar_fail_hip(hipError_t e, const char* what);
+
+#define AR_HIP(call)                                   \
+  do {                                                 \
+    hipError_t e_ = (call);                            \
+    if (e_ != hipSuccess) return ar_fail_hip(e_, #call); \
+  } while (0)

@@ -1,0 +1,694 @@
+// Barrier-free AllReduce (sum) kernels for N ranks emulated on one gfx950 device.
+//
+// Every emulated rank is a group of `ctas` co-resident workgroups with its own input, output and
+// block of the symmetric scratch allocation. Ranks exchange data only through global stores into
+// another rank's scratch block and polling of their own block; no kernel uses a device-wide
+// barrier. Workgroup c of rank r only ever talks to workgroup c of the other ranks, and inside
+// it a unit (8 or 16 bytes of payload) is always handled by the same lane, so every credit of
+// the double-buffering scheme is a per-lane fact.
+//
+// One launch runs `iters` AllReduces back to back (1 for an ordinary call); an AllReduce whose
+// message does not fit the scratch slots is split into `chunks` equal chunks. Each (iteration,
+// chunk) pair is a step with its own sequence number s = e0 + it * chunks + k; step s uses
+// scratch buffer s & 1.
+//
+// Sources: Every µs Matters: Achieving Near Speed-of-Light Latency in GPU Collectives —
+// §III.A (one-shot push and two-shot AllReduce), §III.B (memory-barrier cost; the baseline),
+// §IV (LL, Sentinel, Bidirectional Communication Double Buffering, Fig. 4); the two-shot
+// LL128 atomic AllReduce (Fig. 5) as described in the Pith review of the same paper
+// ("Assumptions & free parameters", referee report on §IV.4).
+
+#include "ar_args.h"
+#include "ar_device.h"
+
+namespace ar {
+
+struct Ctx {
+  int rank, cta, wave, lane, wpb;
+  uint32_t T;   // threads per rank
+  uint32_t t0;  // first unit index of this wave inside a chunk (lane adds its own offset)
+};
+
+__device__ __forceinline__ bool decode(const Args& a, Ctx& c) {
+  const int w = blockIdx.x;
+  int rank, cta;
+  if (a.placement == PLACE_XCD) {
+    const int xcd = w & 7, j = w >> 3, R = a.ranks_per_xcd;
+    rank = xcd + 8 * (j % R);
+    cta = j / R;
+  } else if (a.placement == PLACE_SAME) {
+    if ((w & 7) != 0) return false;
+    const int j = w >> 3;
+    rank = j / a.ctas;
+    cta = j % a.ctas;
+  } else {
+    rank = w / a.ctas;
+    cta = w % a.ctas;
+  }
+  if (rank >= a.nranks || cta >= a.ctas) return false;
+  c.rank = rank;
+  c.cta = cta;
+  c.wave = threadIdx.x >> 6;
+  c.lane = threadIdx.x & 63;
+  c.wpb = blockDim.x >> 6;
+  c.T = a.ctas * blockDim.x;
+  c.t0 = cta * blockDim.x + c.wave * kWave;
+  return true;
+}
+
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ rsrc_t region_rsrc(const Args& a, int rank, const Region& g) {
+  return make_rsrc(a.base + static_cast<uint64_t>(rank) * a.stride + g.off, g.bytes);
+}
+
+// Where a poll loop reports a timeout: the few kernel arguments the slow path needs, passed by
+// value so that the argument block never has to be copied to private memory.
+struct PollEnv {
+  uint32_t* ctl;
+  uint32_t* status;
+  uint64_t timeout_ticks;
+  int algo;
+};
+
+__device__ __forceinline__ PollEnv poll_env(const Args& a) {
+  return PollEnv{a.ctl, a.status, a.timeout_ticks, a.algo};
+}
+
+// Called after every 1024 unsuccessful polls. Returns false when the wave must give up: either
+// another wave already aborted, or this poll has waited longer than the timeout, in which case
+// this wave raises the abort flag and, if it is the first, records where it stopped.
+__device__ __noinline__ bool poll_check(PollEnv e, uint64_t& t_first, int rank, int peer,
+                                        uint64_t step) {
+  const uint64_t now = wall_clock64();
+  if (t_first == 0) {
+    t_first = now;
+    return true;
+  }
+  const uint32_t ab = uni(__hip_atomic_load(&e.ctl[CTL_ABORT], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT));
+  if (ab != 0) return false;
+  if (now - t_first <= e.timeout_ticks) return true;
+  if (threadIdx.x % kWave == static_cast<unsigned>(__builtin_ctzll(__ballot(1)))) {
+    if (__hip_atomic_exchange(&e.ctl[CTL_ABORT], 1u, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT) == 0) {
+      __hip_atomic_store(&e.status[ST_RANK], static_cast<uint32_t>(rank), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(&e.status[ST_PEER], static_cast<uint32_t>(peer), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(&e.status[ST_STEP_LO], static_cast<uint32_t>(step), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(&e.status[ST_STEP_HI], static_cast<uint32_t>(step >> 32),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(&e.status[ST_ALGO], static_cast<uint32_t>(e.algo), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(&e.status[ST_CODE], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
+  return false;
+}
+
+// Poll the 16-byte lines of every source whose bit is set in `pend` (source q's line sits at
+// off0 + q * qstride in `own`) until `ready` accepts each of them. All outstanding loads of a
+// lane are in flight together; only the lines that are not ready yet are loaded again.
+template <int NMAX, class Ready>
+__device__ __forceinline__ bool poll_lines(const Args& a, rsrc_t own, uint32_t off0,
+                                           uint32_t qstride, uint32_t pend, u32x4 (&v)[NMAX],
+                                           Ready ready, int rank, uint64_t step) {
+  uint32_t spins = 0;
+  uint64_t t_first = 0;
+  while (true) {
+#pragma unroll
+    for (int q = 0; q < NMAX; ++q)
+      if (pend & (1u << q)) v[q] = ld16<kCoh>(own, off0 + static_cast<uint32_t>(q) * qstride);
+    compiler_fence();
+#pragma unroll
+    for (int q = 0; q < NMAX; ++q)
+      if ((pend & (1u << q)) && ready(v[q])) pend &= ~(1u << q);
+    const uint64_t waiting = __ballot(pend != 0);
+    if (waiting == 0) return true;
+    if ((++spins & 1023u) == 0) {
+      const int lane = __builtin_ctzll(waiting);
+      const uint32_t p = __shfl(pend, lane);
+      if (!poll_check(poll_env(a), t_first, rank, __builtin_ctz(p), step)) return false;
+    }
+  }
+}
+
+// Fold the N sources of one unit in rank order 0..N-1; the rank's own value is `x`.
+template <int DT, int NMAX, int W>
+__device__ __forceinline__ void fold_rank_order(int N, int r, const uint32_t* x,
+                                                const u32x4 (&v)[NMAX], uint32_t* o) {
+  Fold<DT, W> f;
+#pragma unroll
+  for (int q = 0; q < NMAX; ++q) {
+    if (q < N) {
+      uint32_t src[W];
+      const uint32_t vw[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+      for (int i = 0; i < W; ++i) src[i] = (q == r) ? x[i] : vw[i];
+      if (q == 0)
+        f.init(src);
+      else
+        f.add(src);
+    }
+  }
+  f.pack(o);
+}
+
+__device__ __forceinline__ uint32_t peer_mask(int N, int r) {
+  return ((N >= 32) ? 0xFFFFFFFFu : ((1u << N) - 1u)) & ~(1u << r);
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 sentinel_vec() {
+  const uint32_t s = Ty<DT>::kSentinelWord;
+  return u32x4{s, s, s, s};
+}
+
+// ------------------------------------------------------------------ one-shot, LL protocol
+//
+// Push: every 8 bytes of the rank's chunk go to every peer as one 16-byte line {payload, s}
+// (§IV "LL"). Receive: poll each peer's line until its flag equals s, then fold in rank order.
+// Nothing needs resetting: an old line carries an older sequence number.
+template <int DT, int NMAX>
+__device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
+                                rsrc_t out_r, int k) {
+  const int N = a.nranks, r = c.rank;
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t elo = static_cast<uint32_t>(s), ehi = static_cast<uint32_t>(s >> 32);
+  const uint32_t slot = a.ll.slot, CU = a.chunk_units;
+  const uint32_t unit0 = static_cast<uint32_t>(k) * CU;
+  if (r != a.withhold) {
+    const uint32_t mine = (b * N + r) * slot;
+    for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+      const uint32_t i = i0 + c.lane;
+      if (i < CU) {
+        uint32_t w[2];
+        load_unit<DT, 8>(in_r, (unit0 + i) * 8u, a.nbytes, w);
+        const u32x4 line = {w[0], w[1], elo, ehi};
+#pragma unroll
+        for (int j = 1; j < NMAX; ++j) {
+          if (j < N) {
+            int q = r + j;
+            if (q >= N) q -= N;
+            st16<kCoh>(region_rsrc(a, q, a.ll), mine + i * 16u, line);
+          }
+        }
+      }
+    }
+  }
+  const rsrc_t own = region_rsrc(a, r, a.ll);
+  const uint32_t peers = peer_mask(N, r);
+  auto ready = [elo, ehi](u32x4 l) { return l.z == elo && l.w == ehi; };
+  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+    const uint32_t i = i0 + c.lane;
+    const bool act = i < CU;
+    uint32_t x[2] = {0u, 0u};
+    if (act) load_unit<DT, 8>(in_r, (unit0 + i) * 8u, a.nbytes, x);
+    u32x4 v[NMAX];
+#pragma unroll
+    for (int q = 0; q < NMAX; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
+    if (!poll_lines<NMAX>(a, own, b * N * slot + i * 16u, slot, act ? peers : 0u, v, ready, r, s))
+      return false;
+    if (act) {
+      uint32_t o[2];
+      fold_rank_order<DT, NMAX, 2>(N, r, x, v, o);
+      store_unit<DT, 8>(out_r, (unit0 + i) * 8u, a.nbytes, o);
+    }
+  }
+  return true;
+}
+
+// ------------------------------------------------------------------ one-shot, sentinel protocol
+//
+// Push raw 16-byte units into every peer's slot (§IV "Sentinel"). Receive: poll until no element
+// of a peer's unit equals the sentinel, fold in rank order, then write the sentinel back so the
+// slot is armed for step s+2 (the same buffer).
+template <int DT, int NMAX>
+__device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
+                                      rsrc_t out_r, int k) {
+  const int N = a.nranks, r = c.rank;
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t slot = a.p1.slot, CU = a.chunk_units;
+  const uint32_t unit0 = static_cast<uint32_t>(k) * CU;
+  if (r != a.withhold) {
+    const uint32_t mine = (b * N + r) * slot;
+    for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+      const uint32_t i = i0 + c.lane;
+      if (i < CU) {
+        uint32_t w[4];
+        load_unit<DT, 16>(in_r, (unit0 + i) * 16u, a.nbytes, w);
+        const u32x4 x = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+        for (int j = 1; j < NMAX; ++j) {
+          if (j < N) {
+            int q = r + j;
+            if (q >= N) q -= N;
+            st16<kCoh>(region_rsrc(a, q, a.p1), mine + i * 16u, x);
+          }
+        }
+      }
+    }
+  }
+  const rsrc_t own = region_rsrc(a, r, a.p1);
+  const uint32_t peers = peer_mask(N, r);
+  const u32x4 sent = sentinel_vec<DT>();
+  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+    const uint32_t i = i0 + c.lane;
+    const bool act = i < CU;
+    uint32_t x[4] = {0u, 0u, 0u, 0u};
+    if (act) load_unit<DT, 16>(in_r, (unit0 + i) * 16u, a.nbytes, x);
+    u32x4 v[NMAX];
+#pragma unroll
+    for (int q = 0; q < NMAX; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
+    const uint32_t off0 = b * N * slot + i * 16u;
+    if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+    if (act) {
+      uint32_t o[4];
+      fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
+      store_unit<DT, 16>(out_r, (unit0 + i) * 16u, a.nbytes, o);
+#pragma unroll
+      for (int q = 0; q < NMAX; ++q)
+        if (q < N && q != r) st16<kCoh>(own, off0 + static_cast<uint32_t>(q) * slot, sent);
+    }
+  }
+  return true;
+}
+
+// ------------------------------------------------------------------ two-shot helpers
+//
+// The message is cut into N partitions of `part_units` units (the last ones padded with zeros);
+// partition p belongs to owner p. Chunk k of every partition moves in step k. Lane i of a wave
+// handles unit i of the chunk in every partition.
+
+// All-gather receive: poll the reduced unit i of every other owner, copy it to `out`, re-arm.
+template <int DT, int NMAX>
+__device__ __forceinline__ bool allgather_recv(const Args& a, const Ctx& c, uint64_t s,
+                                               rsrc_t out_r, int k) {
+  const int N = a.nranks, r = c.rank;
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t slot = a.p2.slot, CU = a.chunk_units, P = a.part_units;
+  const rsrc_t own = region_rsrc(a, r, a.p2);
+  const uint32_t peers = peer_mask(N, r);
+  const u32x4 sent = sentinel_vec<DT>();
+  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+    const uint32_t i = i0 + c.lane;
+    const bool act = i < CU;
+    u32x4 v[NMAX];
+#pragma unroll
+    for (int q = 0; q < NMAX; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
+    const uint32_t off0 = b * N * slot + i * 16u;
+    if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+    if (act) {
+#pragma unroll
+      for (int p = 0; p < NMAX; ++p) {
+        if (p < N && p != r) {
+          const uint32_t o[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+          store_unit<DT, 16>(out_r, (p * P + k * CU + i) * 16u, a.nbytes, o);
+          st16<kCoh>(own, off0 + static_cast<uint32_t>(p) * slot, sent);
+        }
+      }
+    }
+  }
+  return true;
+}
+
+// Owner r pushes its reduced unit i to every peer's all-gather slot r.
+template <int NMAX>
+__device__ __forceinline__ void allgather_push(const Args& a, int r, uint32_t b, uint32_t i,
+                                               u32x4 res) {
+  const int N = a.nranks;
+  const uint32_t mine = (b * N + r) * a.p2.slot + i * 16u;
+#pragma unroll
+  for (int j = 1; j < NMAX; ++j) {
+    if (j < N) {
+      int q = r + j;
+      if (q >= N) q -= N;
+      st16<kCoh>(region_rsrc(a, q, a.p2), mine, res);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ two-shot (RS + AG)
+template <int DT, int NMAX>
+__device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r, rsrc_t out_r,
+                             int k) {
+  const int N = a.nranks, r = c.rank;
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t slot = a.p1.slot, CU = a.chunk_units, P = a.part_units;
+  const bool sends = r != a.withhold;
+  // Reduce-scatter push: partition p's chunk goes to owner p's slot r.
+  if (sends) {
+    const uint32_t mine = (b * N + r) * slot;
+    for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+      const uint32_t i = i0 + c.lane;
+      if (i < CU) {
+#pragma unroll
+        for (int j = 1; j < NMAX; ++j) {
+          if (j < N) {
+            int p = r + j;
+            if (p >= N) p -= N;
+            uint32_t w[4];
+            load_unit<DT, 16>(in_r, (p * P + k * CU + i) * 16u, a.nbytes, w);
+            st16<kCoh>(region_rsrc(a, p, a.p1), mine + i * 16u, u32x4{w[0], w[1], w[2], w[3]});
+          }
+        }
+      }
+    }
+  }
+  // Owner: reduce its partition in rank order, keep the result, push it to every peer.
+  const rsrc_t own = region_rsrc(a, r, a.p1);
+  const uint32_t peers = peer_mask(N, r);
+  const u32x4 sent = sentinel_vec<DT>();
+  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+    const uint32_t i = i0 + c.lane;
+    const bool act = i < CU;
+    uint32_t x[4] = {0u, 0u, 0u, 0u};
+    const uint32_t uoff = (r * P + k * CU + i) * 16u;
+    if (act) load_unit<DT, 16>(in_r, uoff, a.nbytes, x);
+    u32x4 v[NMAX];
+#pragma unroll
+    for (int q = 0; q < NMAX; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
+    const uint32_t off0 = b * N * slot + i * 16u;
+    if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+    if (act) {
+      uint32_t o[4];
+      fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
+      store_unit<DT, 16>(out_r, uoff, a.nbytes, o);
+      if (sends) allgather_push<NMAX>(a, r, b, i, u32x4{o[0], o[1], o[2], o[3]});
+#pragma unroll
+      for (int q = 0; q < NMAX; ++q)
+        if (q < N && q != r) st16<kCoh>(own, off0 + static_cast<uint32_t>(q) * slot, sent);
+    }
+  }
+  return allgather_recv<DT, NMAX>(a, c, s, out_r, k);
+}
+
+// ------------------------------------------------------------------ LL128-style atomic two-shot
+//
+// Reduce-scatter by atomic addition: every rank (the owner included) adds its chunk of
+// partition p into owner p's shared destination, then counts itself in on the owner's arrival
+// counter for this (buffer, workgroup, wave). The page's design detects completion with a flag
+// inside each 128-byte line, which needs 128-byte atomicity of the interconnect; here each
+// contributor publishes with an agent-scope release followed by one counter increment, and the
+// owner reads the sums after it sees N arrivals (acquire). The owner then clears the
+// destination and the counter and runs the all-gather of the plain two-shot.
+template <int DT, int NMAX>
+__device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r, rsrc_t out_r,
+                           int k) {
+  static_assert(DT == DT_F32 || DT == DT_I32, "atomic reduction is for fp32 and int32");
+  const int N = a.nranks, r = c.rank;
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t CU = a.chunk_units, P = a.part_units;
+  const bool has_units = c.t0 < CU;
+  const uint32_t cnt_idx = (b * kMaxCtasPerRank + c.cta) * kMaxWavesPerCta + c.wave;
+  if (has_units && r != a.withhold) {
+    for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+      const uint32_t i = i0 + c.lane;
+      if (i < CU) {
+#pragma unroll
+        for (int j = 0; j < NMAX; ++j) {
+          if (j < N) {
+            int p = r + j;
+            if (p >= N) p -= N;
+            uint32_t w[4];
+            load_unit<DT, 16>(in_r, (p * P + k * CU + i) * 16u, a.nbytes, w);
+            uint8_t* dst = a.base + static_cast<uint64_t>(p) * a.stride + a.acc.off +
+                           static_cast<uint64_t>(b) * a.acc.slot + static_cast<uint64_t>(i) * 16u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if constexpr (DT == DT_F32) {
+                __hip_atomic_fetch_add(reinterpret_cast<float*>(dst) + e, __uint_as_float(w[e]),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              } else {
+                __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(dst) + e, w[e],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+            }
+          }
+        }
+      }
+    }
+    release_agent();
+    if (c.lane < N) {
+      uint32_t* cnt = reinterpret_cast<uint32_t*>(a.base + static_cast<uint64_t>(c.lane) * a.stride +
+                                                  a.cnt.off) + cnt_idx;
+      __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (has_units) {
+    uint32_t* my_cnt =
+        reinterpret_cast<uint32_t*>(a.base + static_cast<uint64_t>(r) * a.stride + a.cnt.off) +
+        cnt_idx;
+    uint32_t spins = 0;
+    uint64_t t_first = 0;
+    while (uni(__hip_atomic_load(my_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) !=
+           static_cast<uint32_t>(N)) {
+      if ((++spins & 1023u) == 0 && !poll_check(poll_env(a), t_first, r, -1, s)) return false;
+    }
+    acquire_agent();
+    const rsrc_t acc = region_rsrc(a, r, a.acc);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+      const uint32_t i = i0 + c.lane;
+      if (i < CU) {
+        const uint32_t aoff = b * a.acc.slot + i * 16u;
+        const u32x4 v = ld16<kCoh>(acc, aoff);
+        const uint32_t o[4] = {v.x, v.y, v.z, v.w};
+        store_unit<DT, 16>(out_r, (r * P + k * CU + i) * 16u, a.nbytes, o);
+        if (r != a.withhold) allgather_push<NMAX>(a, r, b, i, v);
+        st16<kCoh>(acc, aoff, zero);
+      }
+    }
+    if (c.lane == 0) __hip_atomic_store(my_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return allgather_recv<DT, NMAX>(a, c, s, out_r, k);
+}
+
+// ------------------------------------------------------------------ barrier baseline
+//
+// Workgroup-level cross-rank barrier (§III.B): every workgroup writes `val` into its flag slot
+// of every peer, then waits until every peer's flag in its own block has reached `val`. Flags
+// only grow, so they never need resetting. Wave 0 does the signalling; the other waves wait at
+// the workgroup barrier. A timeout is shared through LDS so that every wave leaves together.
+// Set once when a wave of the workgroup gives up on a barrier; cleared only at kernel start, so
+// every wave reads the same value after the closing workgroup barrier.
+__shared__ int g_bar_fail;
+
+__device__ __forceinline__ void barrier_init() {
+  if (threadIdx.x == 0) g_bar_fail = 0;
+  __syncthreads();
+}
+
+__device__ bool xrank_barrier(const Args& a, const Ctx& c, uint64_t val, uint64_t s) {
+  const int N = a.nranks, r = c.rank;
+  __syncthreads();
+  if (c.wave == 0) {
+    const int q = c.lane;
+    const bool peer = q < N && q != r;
+    if (peer && r != a.withhold) {
+      const uint32_t off = (static_cast<uint32_t>(r) * kMaxCtasPerRank + c.cta) * 8u;
+      st8<kCoh>(region_rsrc(a, q, a.bar), off,
+                u32x2{static_cast<uint32_t>(val), static_cast<uint32_t>(val >> 32)});
+    }
+    const rsrc_t own = region_rsrc(a, r, a.bar);
+    const uint32_t off = (static_cast<uint32_t>(q) * kMaxCtasPerRank + c.cta) * 8u;
+    bool need = peer;
+    uint32_t spins = 0;
+    uint64_t t_first = 0;
+    while (true) {
+      if (need) {
+        const u32x2 f = ld8<kCoh>(own, off);
+        compiler_fence();
+        const uint64_t fv = (static_cast<uint64_t>(f.y) << 32) | f.x;
+        if (fv >= val) need = false;
+      }
+      if (__ballot(need) == 0) break;
+      if ((++spins & 1023u) == 0 && !poll_check(poll_env(a), t_first, r, q, s)) {
+        if (c.lane == 0) g_bar_fail = 1;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  return g_bar_fail == 0;
+}
+
+// Two-barrier one-shot (the conventional design the pages measure): barrier so that every peer
+// has finished with the data slots, plain push, release, barrier so that the data is there,
+// acquire, reduce.
+template <int DT, int NMAX>
+__device__ bool step_barrier2(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
+                              rsrc_t out_r, int k) {
+  const int N = a.nranks, r = c.rank;
+  const uint32_t slot = a.bdat.slot, CU = a.chunk_units;
+  const uint32_t unit0 = static_cast<uint32_t>(k) * CU;
+  if (!xrank_barrier(a, c, 2 * s, s)) return false;
+  if (r != a.withhold) {
+    for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+      const uint32_t i = i0 + c.lane;
+      if (i < CU) {
+        uint32_t w[4];
+        load_unit<DT, 16>(in_r, (unit0 + i) * 16u, a.nbytes, w);
+        const u32x4 x = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+        for (int j = 1; j < NMAX; ++j) {
+          if (j < N) {
+            int q = r + j;
+            if (q >= N) q -= N;
+            st16<kCoh>(region_rsrc(a, q, a.bdat), r * slot + i * 16u, x);
+          }
+        }
+      }
+    }
+  }
+  release_agent();
+  if (!xrank_barrier(a, c, 2 * s + 1, s)) return false;
+  acquire_agent();
+  const rsrc_t own = region_rsrc(a, r, a.bdat);
+  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+    const uint32_t i = i0 + c.lane;
+    if (i < CU) {
+      uint32_t x[4];
+      load_unit<DT, 16>(in_r, (unit0 + i) * 16u, a.nbytes, x);
+      u32x4 v[NMAX];
+#pragma unroll
+      for (int q = 0; q < NMAX; ++q)
+        v[q] = (q < N && q != r) ? ld16<kCoh>(own, static_cast<uint32_t>(q) * slot + i * 16u)
+                                 : u32x4{0u, 0u, 0u, 0u};
+      uint32_t o[4];
+      fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
+      store_unit<DT, 16>(out_r, (unit0 + i) * 16u, a.nbytes, o);
+    }
+  }
+  return true;
+}
+
+// ------------------------------------------------------------------ persistent driver
+
+__device__ __forceinline__ void drift_sleep(const Args& a, int it, int r, int cta) {
+  uint32_t h = static_cast<uint32_t>(it) * 0x9E3779B1u ^ static_cast<uint32_t>(r) * 0x85EBCA77u ^
+               static_cast<uint32_t>(cta) * 0xC2B2AE3Du;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  const uint32_t n = uni(h % static_cast<uint32_t>(a.drift + 1));
+  for (uint32_t z = 0; z < n; ++z) __builtin_amdgcn_s_sleep(64);
+}
+
+template <int ALGO, int DT, int NMAX>
+__global__ __launch_bounds__(256) void ar_kernel(Args a) {
+  Ctx c;
+  if (!decode(a, c)) return;
+  const int N = a.nranks;
+  const int wpb = c.wpb;
+  // Sentinel-type protocols re-arm (or clear) slots at the end of a step; those stores must be
+  // visible before this rank's next push can let a peer write the same buffer again.
+  constexpr bool kRearm = ALGO == ALGO_ONESHOT_SENTINEL || ALGO == ALGO_TWOSHOT ||
+                          ALGO == ALGO_LL128_ATOMIC;
+  const uint64_t nsteps = static_cast<uint64_t>(a.iters) * a.chunks;
+  if constexpr (ALGO == ALGO_BARRIER2 || ALGO == ALGO_BARRIER_ONLY) barrier_init();
+  for (int it = 0; it < a.iters; ++it) {
+    const int set = a.in_tab ? it % a.nsets : 0;
+    const void* inp = a.in_tab ? a.in_tab[set * N + c.rank] : a.in[c.rank];
+    void* outp = a.out_tab ? a.out_tab[set * N + c.rank] : a.out[c.rank];
+    const rsrc_t in_r = make_rsrc(inp, a.nbytes);
+    const rsrc_t out_r = make_rsrc(outp, a.nbytes);
+    if (a.drift > 0) drift_sleep(a, it, c.rank, c.cta);
+    const uint64_t ts_idx =
+        ((static_cast<uint64_t>(it) * N + c.rank) * a.ctas + c.cta) * wpb + c.wave;
+    if (a.ts_start != nullptr && c.lane == 0) a.ts_start[ts_idx] = now_ticks();
+    for (int k = 0; k < a.chunks; ++k) {
+      const uint64_t step = static_cast<uint64_t>(it) * a.chunks + k;
+      const uint64_t s = a.e0 + step;
+      bool ok;
+      if constexpr (ALGO == ALGO_ONESHOT_LL) {
+        ok = step_oneshot_ll<DT, NMAX>(a, c, s, in_r, out_r, k);
+      } else if constexpr (ALGO == ALGO_ONESHOT_SENTINEL) {
+        ok = step_oneshot_sentinel<DT, NMAX>(a, c, s, in_r, out_r, k);
+      } else if constexpr (ALGO == ALGO_TWOSHOT) {
+        ok = step_twoshot<DT, NMAX>(a, c, s, in_r, out_r, k);
+      } else if constexpr (ALGO == ALGO_LL128_ATOMIC) {
+        ok = step_ll128<DT, NMAX>(a, c, s, in_r, out_r, k);
+      } else if constexpr (ALGO == ALGO_BARRIER2) {
+        ok = step_barrier2<DT, NMAX>(a, c, s, in_r, out_r, k);
+      } else {
+        ok = xrank_barrier(a, c, 2 * s, s);
+      }
+      if (!ok) return;
+      if (kRearm && step + 1 < nsteps) release_agent();
+    }
+    if (a.ts_end != nullptr) {
+      wait_all_mem();
+      if (c.lane == 0) a.ts_end[ts_idx] = now_ticks();
+    }
+  }
+}
+
+// Fill `bytes` of every rank's block at `off` with the 32-bit word `word` (scratch set-up).
+__global__ void fill_region(uint8_t* base, uint64_t stride, int nranks, uint64_t off,
+                            uint32_t bytes, uint32_t word) {
+  const uint32_t vecs = bytes / 16u;
+  const uint64_t total = static_cast<uint64_t>(vecs) * nranks;
+  const u32x4 v = {word, word, word, word};
+  for (uint64_t g = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+       g += static_cast<uint64_t>(gridDim.x) * blockDim.x) {
+    const uint64_t r = g / vecs, i = g % vecs;
+    *reinterpret_cast<u32x4*>(base + r * stride + off + i * 16u) = v;
+  }
+}
+
+}  // namespace ar
+
+// ------------------------------------------------------------------ host-visible kernel table
+
+typedef void (*ar_kernel_fn)(ar::Args);
+
+template <int ALGO, int DT>
+static ar_kernel_fn pick_n(int nmax) {
+  switch (nmax) {
+    case 2: return ar::ar_kernel<ALGO, DT, 2>;
+    case 4: return ar::ar_kernel<ALGO, DT, 4>;
+    case 8: return ar::ar_kernel<ALGO, DT, 8>;
+    default: return ar::ar_kernel<ALGO, DT, 16>;
+  }
+}
+
+template <int ALGO>
+static ar_kernel_fn pick_dt(int dt, int nmax) {
+  switch (dt) {
+    case ar::DT_F32: return pick_n<ALGO, ar::DT_F32>(nmax);
+    case ar::DT_BF16: return pick_n<ALGO, ar::DT_BF16>(nmax);
+    default: return pick_n<ALGO, ar::DT_I32>(nmax);
+  }
+}
+
+// Returns the kernel for (algo, dtype, nmax) or nullptr when the combination is not supported.
+ar_kernel_fn ar_select_kernel(int algo, int dt, int nmax) {
+  switch (algo) {
+    case ar::ALGO_ONESHOT_LL: return pick_dt<ar::ALGO_ONESHOT_LL>(dt, nmax);
+    case ar::ALGO_ONESHOT_SENTINEL: return pick_dt<ar::ALGO_ONESHOT_SENTINEL>(dt, nmax);
+    case ar::ALGO_TWOSHOT: return pick_dt<ar::ALGO_TWOSHOT>(dt, nmax);
+    case ar::ALGO_LL128_ATOMIC:
+      if (dt == ar::DT_F32) return pick_n<ar::ALGO_LL128_ATOMIC, ar::DT_F32>(nmax);
+      if (dt == ar::DT_I32) return pick_n<ar::ALGO_LL128_ATOMIC, ar::DT_I32>(nmax);
+      return nullptr;
+    case ar::ALGO_BARRIER2: return pick_dt<ar::ALGO_BARRIER2>(dt, nmax);
+    case ar::ALGO_BARRIER_ONLY: return pick_n<ar::ALGO_BARRIER_ONLY, ar::DT_F32>(nmax);
+    default: return nullptr;
+  }
+}
+
+void ar_launch_fill(uint8_t* base, uint64_t stride, int nranks, uint64_t off, uint32_t bytes,
+                    uint32_t word, hipStream_t stream) {
+  const uint64_t vecs = static_cast<uint64_t>(bytes / 16u) * nranks;
+  uint64_t blocks = (vecs + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) return;
+  hipLaunchKernelGGL(ar::fill_region, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     base, stride, nranks, off, bytes, word);
+}

@@ -1,0 +1,353 @@
+// Speed-of-light microbenchmarks and hardware probes for the emulated-rank AllReduce.
+//
+// The pages bound small-message AllReduce latency by L_SoL = 2 * L_L2 + L_remote_store, with
+// L_L2 taken as the latency of a device-scope memory fence and L_remote_store from a two-GPU
+// store/poll ping-pong (Every µs Matters, §VI as summarised by the Pith review: "Section VI, L_SoL
+// formula"; the review's concrete test proposes a dependent pointer chase for the L2 term and a
+// ping-pong without fences for the store term). On one gfx950 device the "remote" store is a
+// store by one workgroup that another workgroup, on the same or on another XCD, polls for.
+//
+// Every kernel here runs a bounded number of iterations and every wait is bounded by a spin
+// limit, so a probe always ends.
+
+#include "ar_args.h"
+#include "ar_device.h"
+
+namespace ar {
+
+// --------------------------------------------------------------- fence latency
+// One wave: `iters` times {store to a line with the coherent policy, agent-scope release fence}.
+// out[0] = ticks for the whole loop.
+__global__ void sol_fence(uint32_t* buf, int iters, uint64_t* out) {
+  if (blockIdx.x != 0 || threadIdx.x >= kWave) return;
+  const rsrc_t r = make_rsrc(buf, 4096);
+  st4<kCoh>(r, threadIdx.x * 4u, 0u);
+  wait_all_mem();
+  const uint64_t t0 = now_ticks();
+  for (int i = 0; i < iters; ++i) {
+    if (threadIdx.x == 0) st4<kPlain>(r, 0, static_cast<uint32_t>(i));
+    release_agent();
+  }
+  const uint64_t t1 = now_ticks();
+  if (threadIdx.x == 0) out[0] = t1 - t0;
+}
+
+// --------------------------------------------------------------- dependent load latency
+// One lane follows a pointer chain (each 32-bit word holds the byte offset of the next node)
+// `hops` times with cache policy CP. A first pass over the whole chain warms the caches.
+// out[0] = ticks for the timed pass, out[1] = final offset (keeps the chain live).
+template <int CP>
+__global__ void sol_chase(const uint32_t* chain, uint32_t bytes, int hops, int warm_hops,
+                          uint64_t* out) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  const rsrc_t r = make_rsrc(chain, bytes);
+  uint32_t off = 0;
+  for (int i = 0; i < warm_hops; ++i) off = ld4<CP>(r, off);
+  wait_all_mem();
+  const uint64_t t0 = now_ticks();
+  for (int i = 0; i < hops; ++i) off = ld4<CP>(r, off);
+  wait_all_mem();
+  compiler_fence();
+  const uint64_t t1 = now_ticks();
+  out[0] = t1 - t0;
+  out[1] = off;
+}
+
+// --------------------------------------------------------------- store -> poll ping-pong
+// Two single-wave workgroups, A = blockIdx a_blk and B = blockIdx b_blk (the other workgroups
+// exit). Round i: A stores i to flag_a and polls flag_b until it reads i; B polls flag_a for i,
+// then stores i to flag_b. No fences: a store with the coherent policy followed by polling loads
+// with the coherent policy. out = {ticks for all rounds, completed rounds, xcc of A, xcc of B}.
+template <int CPS, int CPL>
+__global__ void sol_pingpong(uint32_t* flags, int rounds, int a_blk, int b_blk, uint32_t spin_cap,
+                             uint64_t* out) {
+  const int me = blockIdx.x;
+  if ((me != a_blk && me != b_blk) || threadIdx.x != 0) return;
+  const rsrc_t r = make_rsrc(flags, 1024);
+  const bool is_a = me == a_blk;
+  const uint32_t fa = 0, fb = 512;
+  out[is_a ? 2 : 3] = xcc_id();
+  uint64_t t0 = 0;
+  int done = 0;
+  if (is_a) t0 = now_ticks();
+  for (int i = 1; i <= rounds; ++i) {
+    uint32_t spins = 0;
+    if (is_a) {
+      st4<CPS>(r, fa, static_cast<uint32_t>(i));
+      while (true) {
+        const uint32_t v = ld4<CPL>(r, fb);
+        compiler_fence();
+        if (v == static_cast<uint32_t>(i) || ++spins > spin_cap) break;
+      }
+    } else {
+      while (true) {
+        const uint32_t v = ld4<CPL>(r, fa);
+        compiler_fence();
+        if (v == static_cast<uint32_t>(i) || ++spins > spin_cap) break;
+      }
+      st4<CPS>(r, fb, static_cast<uint32_t>(i));
+    }
+    if (spins > spin_cap) break;
+    done = i;
+  }
+  if (is_a) {
+    out[0] = now_ticks() - t0;
+    out[1] = static_cast<uint64_t>(done);
+  }
+}
+
+// --------------------------------------------------------------- torn 16-byte line probe
+// Writer workgroup (blockIdx w_blk, one lane per line) stores generations g = 1..gens into
+// `lines` 16-byte lines as {g, ~g, g * 0x9E3779B1, g ^ 0x5A5A5A5A} with one 16-byte coherent
+// store each; reader workgroup (blockIdx r_blk) polls the same lines with 16-byte coherent loads
+// and counts lines whose four words do not belong to one generation (a torn line). Zero-filled
+// lines (never written) are valid. out = {torn, reads, xcc writer, xcc reader}.
+__global__ void sol_torn(u32x4* lines, int nlines, int gens, int w_blk, int r_blk,
+                         uint32_t read_cap, unsigned long long* out) {
+  const int me = blockIdx.x;
+  if (me != w_blk && me != r_blk) return;
+  const int l = threadIdx.x;
+  if (l >= nlines) return;
+  const rsrc_t r = make_rsrc(lines, static_cast<uint32_t>(nlines) * 16u);
+  if (me == w_blk) {
+    if (l == 0) out[2] = xcc_id();
+    for (int g = 1; g <= gens; ++g) {
+      const uint32_t u = static_cast<uint32_t>(g);
+      st16<kCoh>(r, l * 16u, u32x4{u, ~u, u * 0x9E3779B1u, u ^ 0x5A5A5A5Au});
+    }
+    return;
+  }
+  if (l == 0) out[3] = xcc_id();
+  unsigned long long torn = 0, reads = 0;
+  for (uint32_t k = 0; k < read_cap; ++k) {
+    const u32x4 v = ld16<kCoh>(r, l * 16u);
+    compiler_fence();
+    ++reads;
+    const bool zero = v.x == 0u && v.y == 0u && v.z == 0u && v.w == 0u;
+    const bool ok = zero || (v.y == ~v.x && v.z == v.x * 0x9E3779B1u && v.w == (v.x ^ 0x5A5A5A5Au));
+    if (!ok) ++torn;
+    if (v.x == static_cast<uint32_t>(gens) && ok) break;
+  }
+  atomicAdd(&out[0], torn);
+  atomicAdd(&out[1], reads);
+}
+
+// --------------------------------------------------------------- streaming copy
+// Grid-stride copy of `bytes` (a multiple of 16) with 16-byte loads and stores; used to measure
+// the achievable HBM bandwidth and to scale rocprof byte counters.
+__global__ void stream_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n16) {
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    dst[i] = a;
+    dst[i + stride] = b;
+    dst[i + 2 * stride] = c;
+    dst[i + 3 * stride] = d;
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+}  // namespace ar
+
+// ================================================================ host side
+
+#include <algorithm>
+#include <cstring>
+#include <random>
+#include <vector>
+
+#include "../../include/ar.h"
+#include "ar_internal.h"
+
+namespace {
+
+struct DevBuf {
+  void* p = nullptr;
+  ~DevBuf() {
+    if (p) (void)hipFree(p);
+  }
+};
+
+
+typedef void (*pp_fn)(uint32_t*, int, int, int, uint32_t, uint64_t*);
+
+template <int CPS>
+pp_fn pp_by_load(int cpl) {
+  switch (cpl) {
+    case 0: return ar::sol_pingpong<CPS, 0>;
+    case 1: return ar::sol_pingpong<CPS, 1>;
+    case 2: return ar::sol_pingpong<CPS, 2>;
+    case 16: return ar::sol_pingpong<CPS, 16>;
+    case 17: return ar::sol_pingpong<CPS, 17>;
+    default: return nullptr;
+  }
+}
+
+pp_fn pp_select(int cps, int cpl) {
+  switch (cps) {
+    case 0: return pp_by_load<0>(cpl);
+    case 1: return pp_by_load<1>(cpl);
+    case 2: return pp_by_load<2>(cpl);
+    case 16: return pp_by_load<16>(cpl);
+    case 17: return pp_by_load<17>(cpl);
+    default: return nullptr;
+  }
+}
+
+// Blocks 0 and 1 land on different XCDs (round-robin dispatch); blocks 0 and 8 on the same one.
+void pair_blocks(int placement, int& a, int& b) {
+  a = 0;
+  b = placement == AR_PLACE_SAME ? 8 : 1;
+}
+
+int run_pingpong(int placement, int cps, int cpl, int rounds, double* half_ns, int* xcc) {
+  pp_fn fn = pp_select(cps, cpl);
+  if (fn == nullptr) return ar_fail(AR_EINVAL, "cache policy must be 0, 1, 2, 16 or 17");
+  if (rounds < 1 || rounds > 1000000) return ar_fail(AR_EINVAL, "rounds out of range");
+  DevBuf flags, out;
+  AR_HIP(hipMalloc(&flags.p, 1024));
+  AR_HIP(hipMalloc(&out.p, 4 * sizeof(uint64_t)));
+  AR_HIP(hipMemset(flags.p, 0, 1024));
+  AR_HIP(hipMemset(out.p, 0, 4 * sizeof(uint64_t)));
+  int a = 0, b = 0;
+  pair_blocks(placement, a, b);
+  hipLaunchKernelGGL(fn, dim3(16), dim3(64), 0, nullptr, static_cast<uint32_t*>(flags.p), rounds,
+                     a, b, 1000000u, static_cast<uint64_t*>(out.p));
+  AR_HIP(hipGetLastError());
+  AR_HIP(hipDeviceSynchronize());
+  uint64_t o[4];
+  AR_HIP(hipMemcpy(o, out.p, sizeof o, hipMemcpyDeviceToHost));
+  if (xcc) {
+    xcc[0] = static_cast<int>(o[2]);
+    xcc[1] = static_cast<int>(o[3]);
+  }
+  if (o[1] < static_cast<uint64_t>(rounds))
+    return ar_fail(AR_ETIMEOUT, "ping-pong stalled after %llu of %d rounds (policies %d/%d)",
+                   static_cast<unsigned long long>(o[1]), rounds, cps, cpl);
+  const double hz = ar_wallclock_hz();
+  *half_ns = static_cast<double>(o[0]) / hz * 1e9 / (2.0 * rounds);
+  return AR_OK;
+}
+
+// Random cyclic pointer chain over `bytes` with one node per 128 bytes (Sattolo's shuffle gives a
+// single cycle through every node); returns the average ns per dependent load with policy CP.
+template <int CP>
+int run_chase(uint64_t bytes, int hops, bool warm_full, double* ns) {
+  const uint64_t nodes = bytes / 128;
+  std::vector<uint32_t> order(nodes);
+  for (uint64_t i = 0; i < nodes; ++i) order[i] = static_cast<uint32_t>(i);
+  std::mt19937_64 g(12345);
+  for (uint64_t i = nodes - 1; i > 0; --i) {
+    std::uniform_int_distribution<uint64_t> d(0, i - 1);
+    std::swap(order[i], order[d(g)]);
+  }
+  std::vector<uint32_t> image(bytes / 4, 0u);
+  for (uint64_t i = 0; i < nodes; ++i)
+    image[static_cast<uint64_t>(i) * 32] = order[i] * 128u;  // node i -> node order[i]
+  DevBuf chain, out;
+  AR_HIP(hipMalloc(&chain.p, bytes));
+  AR_HIP(hipMalloc(&out.p, 2 * sizeof(uint64_t)));
+  AR_HIP(hipMemcpy(chain.p, image.data(), bytes, hipMemcpyHostToDevice));
+  const int warm = warm_full ? static_cast<int>(std::min<uint64_t>(nodes, 1u << 22)) : 1000;
+  hipLaunchKernelGGL(ar::sol_chase<CP>, dim3(1), dim3(64), 0, nullptr,
+                     static_cast<const uint32_t*>(chain.p), static_cast<uint32_t>(bytes), hops,
+                     warm, static_cast<uint64_t*>(out.p));
+  AR_HIP(hipGetLastError());
+  AR_HIP(hipDeviceSynchronize());
+  uint64_t o[2];
+  AR_HIP(hipMemcpy(o, out.p, sizeof o, hipMemcpyDeviceToHost));
+  *ns = static_cast<double>(o[0]) / ar_wallclock_hz() * 1e9 / hops;
+  return AR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ar_pingpong(int placement, int store_policy, int load_policy, int rounds, double* half_rtt_ns,
+                int* xcc) {
+  if (half_rtt_ns == nullptr) return ar_fail(AR_EINVAL, "null result pointer");
+  return run_pingpong(placement, store_policy, load_policy, rounds, half_rtt_ns, xcc);
+}
+
+int ar_sol(int placement, ar_sol_result* res) {
+  if (res == nullptr) return ar_fail(AR_EINVAL, "null result pointer");
+  if (placement != AR_PLACE_XCD && placement != AR_PLACE_SAME)
+    return ar_fail(AR_EINVAL, "placement must be AR_PLACE_XCD or AR_PLACE_SAME");
+  std::memset(res, 0, sizeof *res);
+  const double hz = ar_wallclock_hz();
+  if (hz <= 0) return ar_fail(AR_EHIP, "no device wall clock");
+  {
+    DevBuf buf, out;
+    AR_HIP(hipMalloc(&buf.p, 4096));
+    AR_HIP(hipMalloc(&out.p, sizeof(uint64_t)));
+    const int iters = 20000;
+    hipLaunchKernelGGL(ar::sol_fence, dim3(1), dim3(64), 0, nullptr,
+                       static_cast<uint32_t*>(buf.p), iters, static_cast<uint64_t*>(out.p));
+    AR_HIP(hipGetLastError());
+    AR_HIP(hipDeviceSynchronize());
+    uint64_t t = 0;
+    AR_HIP(hipMemcpy(&t, out.p, sizeof t, hipMemcpyDeviceToHost));
+    res->fence_ns = static_cast<double>(t) / hz * 1e9 / iters;
+  }
+  int rc;
+  if ((rc = run_chase<ar::kPlain>(1ull << 20, 20000, true, &res->l2_load_ns)) != AR_OK) return rc;
+  if ((rc = run_chase<ar::kSc1>(1ull << 20, 20000, true, &res->coherent_load_ns)) != AR_OK)
+    return rc;
+  if ((rc = run_chase<ar::kPlain>(64ull << 20, 20000, true, &res->mall_load_ns)) != AR_OK)
+    return rc;
+  if ((rc = run_chase<ar::kPlain>(1ull << 30, 20000, false, &res->hbm_load_ns)) != AR_OK)
+    return rc;
+  int xcc[2] = {-1, -1};
+  if ((rc = run_pingpong(placement, ar::kSc1, ar::kSc1, 5000, &res->store_half_rtt_ns, xcc)) !=
+      AR_OK)
+    return rc;
+  res->xcc_a = xcc[0];
+  res->xcc_b = xcc[1];
+  res->floor_ns = 2.0 * res->l2_load_ns + res->store_half_rtt_ns;
+  res->floor_fence_ns = 2.0 * res->fence_ns + res->store_half_rtt_ns;
+  return AR_OK;
+}
+
+int ar_torn_lines(int placement, int nlines, int gens, uint64_t* torn, uint64_t* reads) {
+  if (torn == nullptr || reads == nullptr) return ar_fail(AR_EINVAL, "null result pointer");
+  if (nlines < 1 || nlines > 64 || gens < 1 || gens > 10000000)
+    return ar_fail(AR_EINVAL, "nlines must be in [1, 64] and gens in [1, 1e7]");
+  DevBuf lines, out;
+  AR_HIP(hipMalloc(&lines.p, 64 * 16));
+  AR_HIP(hipMalloc(&out.p, 4 * sizeof(unsigned long long)));
+  AR_HIP(hipMemset(lines.p, 0, 64 * 16));
+  AR_HIP(hipMemset(out.p, 0, 4 * sizeof(unsigned long long)));
+  int a = 0, b = 0;
+  pair_blocks(placement, a, b);
+  hipLaunchKernelGGL(ar::sol_torn, dim3(16), dim3(64), 0, nullptr,
+                     static_cast<ar::u32x4*>(lines.p), nlines, gens, a, b,
+                     static_cast<uint32_t>(std::min<int64_t>(4ll * gens + 1000000, 100000000)),
+                     static_cast<unsigned long long*>(out.p));
+  AR_HIP(hipGetLastError());
+  AR_HIP(hipDeviceSynchronize());
+  unsigned long long o[4];
+  AR_HIP(hipMemcpy(o, out.p, sizeof o, hipMemcpyDeviceToHost));
+  *torn = o[0];
+  *reads = o[1];
+  return AR_OK;
+}
+
+int ar_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (dst == nullptr || src == nullptr) return ar_fail(AR_EINVAL, "null buffer");
+  if (bytes % 16 != 0) return ar_fail(AR_EINVAL, "bytes must be a multiple of 16");
+  if (((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15u) != 0)
+    return ar_fail(AR_EINVAL, "buffers must be 16-byte aligned");
+  const uint64_t n16 = bytes / 16;
+  if (n16 == 0) return AR_OK;
+  uint64_t blocks = (n16 + 255) / 256;
+  blocks = std::min<uint64_t>(blocks, 8192);
+  hipLaunchKernelGGL(ar::stream_copy, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const ar::u32x4*>(src),
+                     static_cast<ar::u32x4*>(dst), n16);
+  AR_HIP(hipGetLastError());
+  return AR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,237 @@
+"""GPU parity: every algorithm, through the C ABI, against the CPU oracle.
+
+Bar: int32 and fixed-rank-order fp32 / bf16 bit-exact; the LL128-style atomic fp32 path within
+N * 2^-23 * sum_r |x_r| per element, and bit-exact on dyadic inputs whose partial sums are exact
+in any order.
+"""
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import (ALGO_NAMES, assert_matches, draw, elem_bytes, from_device, handle,
+                            run_allreduce, supports, to_device)
+
+pytestmark = pytest.mark.gpu
+
+COUNTS = [1, 3, 8, 33, 257, 1000, 4099, 70001]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
+def test_all_algorithms_ragged_counts(n, dtype):
+    maxc = max(COUNTS)
+    with handle(n, maxc * elem_bytes(dtype), dtype) as h:
+        for algo in ALGO_NAMES:
+            if not supports(algo, dtype):
+                continue
+            for i, count in enumerate(COUNTS):
+                _say(f"case n={n} dtype={dtype} algo={algo} count={count}")
+                x = draw(dtype, n, count, seed=1000 * n + i)
+                got = run_allreduce(h, x, algo)
+                assert_matches(got, x, algo, dtype)
+
+
+@pytest.mark.parametrize("algo", ALGO_NAMES)
+def test_in_place(algo):
+    n, dtype, count = 4, "f32", 5000
+    with handle(n, count * 4, dtype) as h:
+        x = draw(dtype, n, count, seed=7)
+        got = run_allreduce(h, x, algo, inplace=True)
+        assert_matches(got, x, algo, dtype)
+
+
+@pytest.mark.parametrize("algo", ALGO_NAMES)
+def test_chunked_scratch(algo):
+    """Scratch capped far below the message: the call runs as many equal chunks, each a step with
+    its own sequence number and alternating buffer (double-buffer credits inside one call)."""
+    n, count = 4, 100003
+    for dtype in ("f32", "i32"):
+        env = {"AR_SCRATCH_ONESHOT": 64 << 10, "AR_SCRATCH_TWOSHOT": 64 << 10}
+        with handle(n, count * 4, dtype, env=env) as h:
+            _say(f"case chunked algo={algo} dtype={dtype}")
+            x = draw(dtype, n, count, seed=11)
+            got = run_allreduce(h, x, algo)
+            assert_matches(got, x, algo, dtype)
+
+
+def test_ll128_dyadic_exact():
+    """Dyadic inputs k * 2^-10: every partial sum is exact, so the atomic path must equal the
+    oracle bit for bit whatever order the additions happened in."""
+    for n in (2, 8, 16):
+        count = 20000
+        with handle(n, count * 4, "f32") as h:
+            x = draw("f32", n, count, seed=n, dist="dyadic")
+            got = run_allreduce(h, x, "ll128_atomic")
+            from tests.gpu_util import oracle_sum
+
+            want = oracle_sum(x)
+            assert np.array_equal(got[0].view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("algo", ALGO_NAMES)
+def test_rank_constant_invariant(algo):
+    """Rank r filled with r: every output is N(N-1)/2."""
+    for n in (2, 8, 16):
+        count = 3001
+        with handle(n, count * 4, "f32") as h:
+            x = draw("f32", n, count, seed=0, dist="rankconst")
+            got = run_allreduce(h, x, algo)
+            assert np.all(got == n * (n - 1) // 2)
+
+
+@pytest.mark.parametrize("algo", ["oneshot_sentinel", "twoshot", "ll128_atomic"])
+def test_scratch_rearmed_after_call(algo):
+    """After a call every sentinel slot holds the sentinel again and the atomic destination and
+    arrival counters are back to zero."""
+    from latency_collectives_amd import _ar as A
+
+    n, dtype, count = 4, "f32", 7777
+    with handle(n, count * 4, dtype) as h:
+        for it in range(3):
+            x = draw(dtype, n, count, seed=50 + it)
+            run_allreduce(h, x, algo)
+        for r in range(n):
+            for reg in (A.REGION_P1, A.REGION_P2):
+                w = A.ar_read_region(h, r, reg).view(np.uint32)
+                assert np.all(w == 0xFFFFFFFF), f"rank {r} region {reg} not re-armed"
+            for reg in (A.REGION_ACC, A.REGION_CNT):
+                w = A.ar_read_region(h, r, reg).view(np.uint32)
+                assert np.all(w == 0), f"rank {r} region {reg} not cleared"
+
+
+def test_count_zero_and_epoch():
+    from latency_collectives_amd import _ar as A
+
+    with handle(2, 1024, "f32") as h:
+        e0 = A.ar_epoch(h)
+        import torch
+
+        t = [torch.zeros(4, device="cuda"), torch.zeros(4, device="cuda")]
+        A.ar_allreduce(h, t, t, 0, A.AR_ONESHOT_LL)
+        assert A.ar_epoch(h) == e0 + 1
+        A.ar_check(h)
+
+
+def test_argument_errors_on_device():
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    with handle(2, 1024, "f32") as h:
+        a = [torch.zeros(300, device="cuda") for _ in range(2)]
+        with pytest.raises(A.ArError) as e:
+            A.ar_allreduce(h, a, a, 300, A.AR_ONESHOT_LL)  # 1200 bytes > max_bytes
+        assert e.value.code == A.AR_ETOOBIG
+        b = [torch.zeros(64, device="cuda") for _ in range(2)]
+        with pytest.raises(A.ArError) as e:
+            A.ar_allreduce(h, b, [b[0], b[0]], 64, A.AR_ONESHOT_LL)
+        assert e.value.code == A.AR_EINVAL
+    with handle(2, 1024, "bf16") as h:
+        b = [torch.zeros(64, dtype=torch.int16, device="cuda") for _ in range(2)]
+        with pytest.raises(A.ArError) as e:
+            A.ar_allreduce(h, b, [torch.empty_like(t) for t in b], 64, A.AR_LL128_ATOMIC)
+        assert e.value.code == A.AR_ENOTSUP
+
+
+@pytest.mark.parametrize("algo", ALGO_NAMES)
+def test_withheld_rank_times_out_without_hang(algo):
+    """Fault injection forced from the host: rank 1 sends nothing, its peers' bounded polls give
+    up after 20 ms, ar_check reports AR_ETIMEOUT, and the handle stays poisoned."""
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    n, count = 4, 4096
+    dtype = "f32"
+    with handle(n, count * 4, dtype, timeout_us=20000, withhold_rank=1) as h:
+        x = draw(dtype, n, count, seed=3)
+        ins = to_device(x)
+        outs = [torch.empty_like(t) for t in ins]
+        A.ar_allreduce(h, ins, outs, count, A.ALGOS[algo])
+        with pytest.raises(A.ArError) as e:
+            A.ar_check(h)
+        assert e.value.code == A.AR_ETIMEOUT
+        assert "timed out" in str(e.value)
+        with pytest.raises(A.ArError) as e:
+            A.ar_allreduce(h, ins, outs, count, A.ALGOS[algo])
+        assert e.value.code == A.AR_ETIMEOUT
+
+
+@pytest.mark.parametrize("algo", ALGO_NAMES)
+@pytest.mark.parametrize("drift", [0, 3])
+def test_persistent_loop_every_iteration(algo, drift):
+    """ar_bench: many AllReduces in one launch with fresh inputs per iteration; every
+    iteration's output is checked (double-buffer credits across iterations, optionally with a
+    random per-rank delay before each iteration)."""
+    from latency_collectives_amd import _ar as A
+
+    n, dtype, count, iters = 4, "f32", 1500, 60
+    with handle(n, count * 4, dtype, drift=drift) as h:
+        xs = [draw(dtype, n, count, seed=200 + k) for k in range(iters)]
+        ins, outs = [], []
+        import torch
+
+        for x in xs:
+            d = to_device(x)
+            ins += d
+            outs += [torch.empty_like(t) for t in d]
+        ts, te, ms = A.ar_bench(h, ins, outs, iters, count, A.ALGOS[algo], iters)
+        assert ms > 0
+        for k in range(iters):
+            got = from_device(outs[k * n:(k + 1) * n], np.float32)
+            assert_matches(got, xs[k], algo, dtype)
+        assert np.all(te.reshape(iters, n) >= ts.reshape(iters, n))
+
+
+def test_c1_shape_1000_iterations_all_checked():
+    """2 ranks, fp32, 32 elements, one-shot LL, 1000 back-to-back iterations with fresh inputs;
+    all 1000 outputs checked bit for bit."""
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    n, count, iters = 2, 32, 1000
+    with handle(n, 128, "f32") as h:
+        xs = [draw("f32", n, count, seed=k) for k in range(iters)]
+        big = np.concatenate(xs, axis=0)
+        dev = to_device(big)
+        outs = [torch.empty_like(t) for t in dev]
+        A.ar_bench(h, dev, outs, iters, count, A.AR_ONESHOT_LL, iters)
+        for k in range(iters):
+            got = from_device(outs[k * n:(k + 1) * n], np.float32)
+            assert_matches(got, xs[k], "oneshot_ll", "f32")
+
+
+@pytest.mark.parametrize("placement", [0, 1, 2])
+def test_placements(placement):
+    n, dtype, count = 8, "bf16", 9000
+    with handle(n, count * 2, dtype, placement=placement) as h:
+        for algo in ("oneshot_ll", "oneshot_sentinel", "twoshot"):
+            x = draw(dtype, n, count, seed=placement)
+            got = run_allreduce(h, x, algo)
+            assert_matches(got, x, algo, dtype)
+
+
+def test_sol_microbench_sane():
+    from latency_collectives_amd import _ar as A
+
+    x = A.ar_sol(A.AR_PLACE_XCD)
+    _say("sol xcd", x)
+    assert x["l2_load_ns"] > 0 and x["store_half_rtt_ns"] > 0 and x["fence_ns"] > 0
+    assert x["xcc_a"] != x["xcc_b"]
+    s = A.ar_sol(A.AR_PLACE_SAME)
+    _say("sol same", s)
+    assert s["xcc_a"] == s["xcc_b"]
+    assert x["floor_ns"] == pytest.approx(2 * x["l2_load_ns"] + x["store_half_rtt_ns"])
+
+
+def test_sixteen_byte_lines_not_torn():
+    """The LL protocol's 16-byte line must arrive whole; count torn reads across XCDs."""
+    from latency_collectives_amd import _ar as A
+
+    for placement in (A.AR_PLACE_XCD, A.AR_PLACE_SAME):
+        torn, reads = A.ar_torn_lines(placement, 64, 200000)
+        _say(f"torn-line probe placement={placement}: torn={torn} reads={reads}")
+        assert reads > 0
+        assert torn == 0
