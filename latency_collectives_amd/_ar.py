@@ -77,6 +77,11 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m latency_collectives_amd.build`")
+    # torch bundles its own HIP runtime with the same soname as /opt/rocm's. Loading torch first
+    # makes libar.so bind to that one runtime, so torch's streams and allocations are valid in
+    # the library (two runtimes in one process would not share devices or streams).
+    import torch  # noqa: F401
+
     L = ctypes.CDLL(LIB_PATH)
     vp, sz, i32, i64, u64 = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int64,
                              ctypes.c_uint64)
