@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the barrier-free AllReduce on one MI355X with emulated ranks.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--all --report out.json]
+
+Default workload: 4 emulated ranks, bf16 sum, one-shot sentinel with double buffering, messages
+of 1 KiB .. 256 KiB per rank (powers of two). A step is one AllReduce of every message size of
+the workload; K steps run back to back inside one persistent launch per size (no host work
+between iterations), each iteration on a fresh input set. Per iteration k the latency is
+max_r t_end[r][k] - max_r t_start[r][k] on the device wall clock (from the moment the last rank
+enters until the last rank has completed its last output store). The JSON line reports the p50,
+the on-chip latency floor 2 * L_L2 + L_store measured in the same run, the roofline of the
+dominant kernel (algorithmic bytes per launch / launch time from HIP events on the launch
+stream) and the single-threaded CPU oracle on a bounded sample.
+
+Only one GPU is used: ranks are emulated on it. ``--gpus`` above 1 is refused.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "p50 AllReduce latency µs @128B–1MB; algBW GB/s @≥16MB (1 GPU)"
+HBM_PEAK_GBPS = 8000.0
+
+
+def alg_bytes(algo: str, n: int, s: int) -> int:
+    """Algorithmic bytes one AllReduce moves (all ranks; s bytes per rank), counting each
+    logical read and write once: inputs read, pushes written, polled slots read, re-arm writes,
+    outputs written. LL lines carry 8 payload bytes in 16."""
+    if algo == "oneshot_ll":
+        return 2 * n * s + 4 * n * (n - 1) * s
+    if algo == "oneshot_sentinel":
+        return 2 * n * s + 3 * n * (n - 1) * s
+    if algo == "twoshot":
+        return (n + 1) * s + 7 * (n - 1) * s
+    if algo == "ll128_atomic":
+        # inputs read, one atomic update per input element, owner read + clear, own output,
+        # all-gather write, read, re-arm, output
+        return 2 * n * s + 2 * s + s + 4 * (n - 1) * s
+    if algo == "barrier2":
+        return 2 * n * s + 2 * n * (n - 1) * s
+    return 0
+
+
+def _to_device(x):
+    import torch
+
+    out = []
+    for r in range(x.shape[0]):
+        row = np.ascontiguousarray(x[r])
+        if row.dtype == np.uint16:
+            row = row.view(np.int16)
+        out.append(torch.from_numpy(row).cuda())
+    return out
+
+
+def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str, iters: int,
+               warmup: int, hz: float, set_cap_bytes: int = 256 << 20, check: bool = True):
+    import torch
+
+    n, dt = wl["nranks"], wl["dtype"]
+    eb = I.ELEM_BYTES[dt]
+    count = size // eb
+    nsets = max(1, min(iters, set_cap_bytes // (n * size)))
+    host_sets = []
+    ins, outs = [], []
+    for k in range(nsets):
+        if n * size <= (8 << 20):
+            x = I.rank_inputs(wl["dist"], dt, n, count, wid, size_idx, k, wl["sigma"])
+            I.assert_finite(x, dt)
+            if check and k == nsets - 1:
+                host_sets.append((k, x))
+            d = _to_device(x)
+        else:
+            d = I.device_draw(wl["dist"], dt, n, count, wid, size_idx, k, wl["sigma"])
+        ins += d
+        outs += [torch.empty_like(t) for t in d]
+    torch.cuda.synchronize()
+    aid = A.ALGOS[algo]
+    if warmup > 0:
+        A.ar_bench(h, ins, outs, nsets, count, aid, warmup, timestamps=False)
+    ts, te, ms = A.ar_bench(h, ins, outs, nsets, count, aid, iters)
+    ts = ts.reshape(iters, n).astype(np.int64)
+    te = te.reshape(iters, n).astype(np.int64)
+    lat_us = (te.max(axis=1) - ts.max(axis=1)) / hz * 1e6
+    ends = te.max(axis=1)
+    period_us = float((ends[-1] - ends[0]) / (iters - 1) / hz * 1e6) if iters > 1 else float("nan")
+    res = {
+        "bytes": size,
+        "count": count,
+        "p50_us": float(np.percentile(lat_us, 50)),
+        "p99_us": float(np.percentile(lat_us, 99)),
+        "mean_us": float(lat_us.mean()),
+        "period_us": period_us,
+        "launch_ms": float(ms),
+        "iters": iters,
+        "alg_bytes_per_call": alg_bytes(algo, n, size),
+    }
+    res["algbw_GBps"] = size / (res["p50_us"] * 1e-6) / 1e9
+    res["busbw_like_GBps"] = res["alg_bytes_per_call"] * iters / (ms * 1e-3) / 1e9 if ms > 0 else 0
+    if check and host_sets:
+        # spot check: the last set's output equals the oracle's result (the parity tests proper
+        # live in tests/)
+        from oracle import oracle
+
+        k, x = host_sets[-1]
+        want = oracle.allreduce([np.ascontiguousarray(x[r]) for r in range(n)])[0]
+        got = outs[k * n].cpu().numpy().view(want.dtype)
+        if algo == "ll128_atomic":
+            ok = np.allclose(got.astype(np.float64), want.astype(np.float64), rtol=0,
+                             atol=float(n * 2.0 ** -23 * np.abs(x.astype(np.float64)).sum(0).max()))
+        else:
+            ok = np.array_equal(got.view(np.uint8), want.view(np.uint8))
+        res["spot_check"] = bool(ok)
+        if not ok:
+            raise AssertionError(f"spot check failed: {algo} n={n} size={size}")
+    del ins, outs
+    return res
+
+
+def cpu_baseline(I, wid: int, wl: dict, budget_s: float = 12.0) -> dict:
+    """The oracle as it stands, single-threaded, timed on this host on the workload's sizes."""
+    from oracle import oracle
+
+    n, dt = wl["nranks"], wl["dtype"]
+    sizes = wl["sizes"]
+    per_size = []
+    per_budget = budget_s / len(sizes)
+    for si, size in enumerate(sizes):
+        count = size // I.ELEM_BYTES[dt]
+        x = I.rank_inputs(wl["dist"], dt, n, count, wid, si, 0, wl["sigma"])
+        rows = [np.ascontiguousarray(x[r]) for r in range(n)]
+        t1 = oracle.time_allreduce(rows, 1)
+        reps = max(1, min(100000, int(per_budget / max(t1, 1e-7))))
+        t = oracle.time_allreduce(rows, reps)
+        per_size.append({"bytes": size, "reps": reps, "us_per_call": t / reps * 1e6})
+    gm = math.exp(sum(math.log(p["us_per_call"]) for p in per_size) / len(per_size))
+    return {
+        "value": gm,
+        "unit": "us",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"single-threaded C++ oracle (left fold, -O2), {n} ranks {dt}, each of the "
+                   f"{len(sizes)} message sizes repeated for ~{per_budget:.1f} s; value = "
+                   "geometric mean over sizes of the mean time per AllReduce"),
+        "host_threads_available": os.cpu_count(),
+        "per_size": per_size,
+    }
+
+
+def run_workload(A, I, wid: int, algo: str | None, iters: int | None, warmup: int, hz: float,
+                 placement: int, sizes=None):
+    wl = dict(I.WORKLOADS[wid])
+    if sizes is not None:
+        wl["sizes"] = sizes
+    algo = algo or wl["algo"]
+    iters = iters or wl["iters"]
+    h = A.ar_create(wl["nranks"], max(wl["sizes"]), A.DTYPES[wl["dtype"]])
+    try:
+        A.ar_set_option(h, A.AR_OPT_PLACEMENT, placement)
+        rows = []
+        for si, size in enumerate(wl["sizes"]):
+            rows.append(bench_size(A, I, h, wid, wl, si, size, algo, iters, warmup, hz))
+            print(f"# workload {wid} {algo} size {size}: p50 {rows[-1]['p50_us']:.3f} us "
+                  f"p99 {rows[-1]['p99_us']:.3f} us", file=sys.stderr, flush=True)
+    finally:
+        A.ar_destroy(h)
+    return wl, algo, iters, rows
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed iterations per size")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=sorted([1, 2, 3, 4, 5]))
+    ap.add_argument("--algo", default=None)
+    ap.add_argument("--placement", type=int, default=0, help="0 XCD per rank, 1 same XCD")
+    ap.add_argument("--all", action="store_true", help="also run every workload; see --report")
+    ap.add_argument("--report", default=None, help="write the full per-size report here")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the ranks are emulated on a single MI355X; "
+              f"--gpus {args.gpus} (world size {world}) is not supported.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from latency_collectives_amd import _ar as A
+    from latency_collectives_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    hz = A.ar_wallclock_hz()
+    sol = A.ar_sol(args.placement)
+    print(f"# sol {json.dumps(sol)}", file=sys.stderr, flush=True)
+
+    wid = args.workload
+    wl, algo, iters, rows = run_workload(A, I, wid, args.algo, args.steps, args.warmup, hz,
+                                         args.placement)
+    p50s = [r["p50_us"] for r in rows]
+    value = math.exp(sum(math.log(v) for v in p50s) / len(p50s))
+    total_launch_ms = sum(r["launch_ms"] for r in rows)
+    floor_us = sol["floor_ns"] * 1e-3
+    # Dominant kernel: the one this workload runs; roofline over all its timed launches.
+    tot_bytes = sum(r["alg_bytes_per_call"] * r["iters"] for r in rows)
+    achieved = tot_bytes / (total_launch_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": iters,
+        "warmup": args.warmup,
+        "ms_per_step": total_launch_ms / iters,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl["dtype"],
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{wl['nranks']} emulated ranks on one MI355X, {wl['dtype']} sum "
+                         f"(fp32 accumulation), {algo}, {min(wl['sizes'])}-{max(wl['sizes'])} "
+                         f"bytes per rank (powers of two), {iters} back-to-back iterations per "
+                         "size, fresh inputs per iteration"),
+            "nranks": wl["nranks"],
+            "algo": algo,
+            "placement": ["rank per XCD", "all ranks on one XCD"][args.placement],
+            "sizes_bytes": wl["sizes"],
+        },
+        "value_definition": ("geometric mean over the message sizes of the per-size p50 "
+                             "latency (device wall clock, last rank in to last rank out)"),
+        "per_size": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                     for r in rows],
+        "latency_floor": {
+            "floor_us": floor_us,
+            "formula": "2*L_L2 + L_store (dependent-load L2 latency; store->poll half RTT)",
+            "l2_load_ns": sol["l2_load_ns"],
+            "store_half_rtt_ns": sol["store_half_rtt_ns"],
+            "fence_ns": sol["fence_ns"],
+            "p50_smallest_over_floor": p50s[0] / floor_us,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "kernel": f"ar_kernel<{algo}, {wl['dtype']}, N={wl['nranks']}>",
+            "bytes_definition": "alg_bytes() per call x iterations, over all timed launches",
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(I, wid, wl)
+    report = {"main": line, "sol": sol}
+    if args.all:
+        report["workloads"] = run_all(A, I, hz, args.warmup, args.placement)
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump(report, f, indent=1)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_all(A, I, hz, warmup, placement):
+    out = {}
+    plan = [
+        (1, ["oneshot_ll", "oneshot_sentinel", "barrier2"]),
+        (2, ["oneshot_sentinel", "oneshot_ll", "twoshot", "barrier2"]),
+        (3, ["twoshot", "oneshot_sentinel", "barrier2"]),
+        (4, ["ll128_atomic", "oneshot_ll", "oneshot_sentinel", "twoshot", "barrier2"]),
+        (5, ["twoshot"]),
+    ]
+    for wid, algos in plan:
+        for algo in algos:
+            wl, algo, iters, rows = run_workload(A, I, wid, algo, None, warmup, hz, placement)
+            out[f"{wid}:{algo}:{wl['dtype']}"] = rows
+        if wid == 5:
+            wl = dict(I.WORKLOADS[5], dtype="f32", dist="uniform")
+            h = A.ar_create(8, max(wl["sizes"]), A.AR_FLOAT32)
+            try:
+                rows = [bench_size(A, I, h, 5, wl, si, s, "twoshot", wl["iters"], warmup, hz)
+                        for si, s in enumerate(wl["sizes"])]
+            finally:
+                A.ar_destroy(h)
+            out["5:twoshot:f32"] = rows
+    # barrier latency versus N (one cross-rank barrier per iteration)
+    bar = []
+    for n in (2, 4, 8, 16):
+        h = A.ar_create(n, 16, A.AR_FLOAT32)
+        try:
+            A.ar_set_option(h, A.AR_OPT_PLACEMENT, placement)
+            A.ar_bench(h, None, None, 1, 0, A.AR_BARRIER_ONLY, 50)
+            _, _, ms = A.ar_bench(h, None, None, 1, 0, A.AR_BARRIER_ONLY, 2000)
+            bar.append({"nranks": n, "us_per_barrier": ms * 1e3 / 2000})
+        finally:
+            A.ar_destroy(h)
+    out["barrier_only"] = bar
+    return out
+
+
+if __name__ == "__main__":
+    sys.exit(main())

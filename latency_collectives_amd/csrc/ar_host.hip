@@ -166,7 +166,11 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
   L.chunks = static_cast<int>(K);
   L.chunk_units = static_cast<uint32_t>(C);
   L.part_units = static_cast<uint32_t>(K * C);
-  L.threads = h->threads ? h->threads : (C <= 64 ? 64 : 256);
+  // Small chunks: one workgroup just wide enough that no wave is idle; larger ones: 256-thread
+  // workgroups, one unit per lane per pass.
+  L.threads = h->threads ? h->threads
+                         : (C <= 256 ? static_cast<int>(std::max<uint64_t>(64, round_up(C, 64)))
+                                     : 256);
   const int occ = occupancy(L.fn, L.threads);
   if (occ <= 0) return ar_fail(AR_ENORES, "kernel cannot be resident with %d threads", L.threads);
   const int cus_per_xcd = std::max(1, h->cu_count / kXcds);

@@ -393,10 +393,12 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
 // Reduce-scatter by atomic addition: every rank (the owner included) adds its chunk of
 // partition p into owner p's shared destination, then counts itself in on the owner's arrival
 // counter for this (buffer, workgroup, wave). The page's design detects completion with a flag
-// inside each 128-byte line, which needs 128-byte atomicity of the interconnect; here each
-// contributor publishes with an agent-scope release followed by one counter increment, and the
-// owner reads the sums after it sees N arrivals (acquire). The owner then clears the
-// destination and the counter and runs the all-gather of the plain two-shot.
+// inside each 128-byte line, which needs 128-byte atomicity of the interconnect. Here a
+// contributor waits until its own atomic adds have been performed (they execute at one coherence
+// point for the whole device) and only then increments the counter; the owner, once it reads N
+// arrivals, takes each sum with an atomic exchange against zero, which both reads the final value
+// at that coherence point and clears the destination for step s+2. It then resets the counter
+// and runs the all-gather of the plain two-shot.
 template <int DT, int NMAX>
 __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r, rsrc_t out_r,
                            int k) {
@@ -433,7 +435,7 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
         }
       }
     }
-    release_agent();
+    wait_all_mem();  // every add of this wave has been performed
     if (c.lane < N) {
       uint32_t* cnt = reinterpret_cast<uint32_t*>(a.base + static_cast<uint64_t>(c.lane) * a.stride +
                                                   a.cnt.off) + cnt_idx;
@@ -450,18 +452,20 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
            static_cast<uint32_t>(N)) {
       if ((++spins & 1023u) == 0 && !poll_check(poll_env(a), t_first, r, -1, s)) return false;
     }
-    acquire_agent();
-    const rsrc_t acc = region_rsrc(a, r, a.acc);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    uint8_t* acc = a.base + static_cast<uint64_t>(r) * a.stride + a.acc.off +
+                   static_cast<uint64_t>(b) * a.acc.slot;
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
       if (i < CU) {
-        const uint32_t aoff = b * a.acc.slot + i * 16u;
-        const u32x4 v = ld16<kCoh>(acc, aoff);
+        uint64_t* q = reinterpret_cast<uint64_t*>(acc + static_cast<uint64_t>(i) * 16u);
+        const uint64_t lo = __hip_atomic_exchange(q, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t hi =
+            __hip_atomic_exchange(q + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const u32x4 v = {static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
+                         static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
         const uint32_t o[4] = {v.x, v.y, v.z, v.w};
         store_unit<DT, 16>(out_r, (r * P + k * CU + i) * 16u, a.nbytes, o);
         if (r != a.withhold) allgather_push<NMAX>(a, r, b, i, v);
-        st16<kCoh>(acc, aoff, zero);
       }
     }
     if (c.lane == 0) __hip_atomic_store(my_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -474,13 +478,21 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
 // Workgroup-level cross-rank barrier (§III.B): every workgroup writes `val` into its flag slot
 // of every peer, then waits until every peer's flag in its own block has reached `val`. Flags
 // only grow, so they never need resetting. Wave 0 does the signalling; the other waves wait at
-// the workgroup barrier. A timeout is shared through LDS so that every wave leaves together.
-// Set once when a wave of the workgroup gives up on a barrier; cleared only at kernel start, so
-// every wave reads the same value after the closing workgroup barrier.
-__shared__ int g_bar_fail;
+// the workgroup barrier.
+//
+// Failure flags in LDS, each set by at most the waves that give up and never cleared after
+// kernel start: every wave reads a flag only after a workgroup barrier that follows every write
+// to it, so all waves of a workgroup take the same exit together.
+__shared__ int g_bar_fail;   // a cross-rank barrier timed out
+__shared__ int g_step_fail;  // a poll inside a step gave up
+__shared__ int g_join_fail;  // the rank-local join timed out
 
-__device__ __forceinline__ void barrier_init() {
-  if (threadIdx.x == 0) g_bar_fail = 0;
+__device__ __forceinline__ void fail_flags_init() {
+  if (threadIdx.x == 0) {
+    g_bar_fail = 0;
+    g_step_fail = 0;
+    g_join_fail = 0;
+  }
   __syncthreads();
 }
 
@@ -546,7 +558,7 @@ __device__ bool step_barrier2(const Args& a, const Ctx& c, uint64_t s, rsrc_t in
       }
     }
   }
-  release_agent();
+  wait_all_mem();  // the coherent pushes are performed before the flag that announces them
   if (!xrank_barrier(a, c, 2 * s + 1, s)) return false;
   acquire_agent();
   const rsrc_t own = region_rsrc(a, r, a.bdat);
@@ -580,18 +592,65 @@ __device__ __forceinline__ void drift_sleep(const Args& a, int it, int r, int ct
   for (uint32_t z = 0; z < n; ++z) __builtin_amdgcn_s_sleep(64);
 }
 
+// Rank-local join between two iterations of the persistent loop: every wave of every workgroup
+// of this rank has finished iteration `it` before any starts the next one. It stands in for the
+// kernel boundary that separates two AllReduce calls on one GPU and involves no other rank.
+// Workgroup c publishes `token` (the last sequence number of the iteration, which only grows)
+// in its slot of the rank's own row of the flag region, then waits for the rank's other slots.
+__device__ bool rank_join(const Args& a, const Ctx& c, uint64_t token, bool failed) {
+  if (failed) g_step_fail = 1;
+  __syncthreads();
+  if (g_step_fail != 0) return false;
+  if (a.ctas > 1) {
+    if (c.wave == 0) {
+      const rsrc_t own = region_rsrc(a, c.rank, a.bar);
+      const uint32_t row = static_cast<uint32_t>(c.rank) * kMaxCtasPerRank * 8u;
+      const u32x2 tv = {static_cast<uint32_t>(token), static_cast<uint32_t>(token >> 32)};
+      if (c.lane == 0) st8<kCoh>(own, row + c.cta * 8u, tv);
+      uint32_t need = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxCtasPerRank / kWave; ++j)
+        if (c.lane + j * kWave < a.ctas) need |= 1u << j;
+      uint32_t spins = 0;
+      uint64_t t_first = 0;
+      while (true) {
+#pragma unroll
+        for (int j = 0; j < kMaxCtasPerRank / kWave; ++j) {
+          if (need & (1u << j)) {
+            const u32x2 f = ld8<kCoh>(own, row + (c.lane + j * kWave) * 8u);
+            compiler_fence();
+            if (((static_cast<uint64_t>(f.y) << 32) | f.x) >= token) need &= ~(1u << j);
+          }
+        }
+        if (__ballot(need != 0) == 0) break;
+        if ((++spins & 1023u) == 0 && !poll_check(poll_env(a), t_first, c.rank, c.rank, token)) {
+          if (c.lane == 0) g_join_fail = 1;
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    if (g_join_fail != 0) return false;
+  }
+  return true;
+}
+
 template <int ALGO, int DT, int NMAX>
 __global__ __launch_bounds__(256) void ar_kernel(Args a) {
   Ctx c;
   if (!decode(a, c)) return;
   const int N = a.nranks;
   const int wpb = c.wpb;
-  // Sentinel-type protocols re-arm (or clear) slots at the end of a step; those stores must be
-  // visible before this rank's next push can let a peer write the same buffer again.
+  // Sentinel-type protocols re-arm (or clear) slots at the end of a step. Those stores use the
+  // coherent policy, so once they have completed they are visible to every rank; waiting for
+  // them before the next step's pushes keeps a peer from writing the same buffer (step s+2)
+  // before the re-arm of step s has landed.
   constexpr bool kRearm = ALGO == ALGO_ONESHOT_SENTINEL || ALGO == ALGO_TWOSHOT ||
                           ALGO == ALGO_LL128_ATOMIC;
+  constexpr bool kBarrier = ALGO == ALGO_BARRIER2 || ALGO == ALGO_BARRIER_ONLY;
+  const bool join = a.iters > 1 && ALGO != ALGO_BARRIER_ONLY;
+  if (kBarrier || join) fail_flags_init();
   const uint64_t nsteps = static_cast<uint64_t>(a.iters) * a.chunks;
-  if constexpr (ALGO == ALGO_BARRIER2 || ALGO == ALGO_BARRIER_ONLY) barrier_init();
   for (int it = 0; it < a.iters; ++it) {
     const int set = a.in_tab ? it % a.nsets : 0;
     const void* inp = a.in_tab ? a.in_tab[set * N + c.rank] : a.in[c.rank];
@@ -602,9 +661,11 @@ __global__ __launch_bounds__(256) void ar_kernel(Args a) {
     const uint64_t ts_idx =
         ((static_cast<uint64_t>(it) * N + c.rank) * a.ctas + c.cta) * wpb + c.wave;
     if (a.ts_start != nullptr && c.lane == 0) a.ts_start[ts_idx] = now_ticks();
+    bool failed = false;
+    uint64_t s = 0;
     for (int k = 0; k < a.chunks; ++k) {
       const uint64_t step = static_cast<uint64_t>(it) * a.chunks + k;
-      const uint64_t s = a.e0 + step;
+      s = a.e0 + step;
       bool ok;
       if constexpr (ALGO == ALGO_ONESHOT_LL) {
         ok = step_oneshot_ll<DT, NMAX>(a, c, s, in_r, out_r, k);
@@ -619,12 +680,20 @@ __global__ __launch_bounds__(256) void ar_kernel(Args a) {
       } else {
         ok = xrank_barrier(a, c, 2 * s, s);
       }
-      if (!ok) return;
-      if (kRearm && step + 1 < nsteps) release_agent();
+      if (!ok) {
+        failed = true;
+        break;
+      }
+      if (kRearm && step + 1 < nsteps) wait_all_mem();
     }
-    if (a.ts_end != nullptr) {
+    if (!failed && a.ts_end != nullptr) {
       wait_all_mem();
       if (c.lane == 0) a.ts_end[ts_idx] = now_ticks();
+    }
+    if (join) {
+      if (!rank_join(a, c, s, failed)) return;
+    } else if (failed) {
+      return;
     }
   }
 }

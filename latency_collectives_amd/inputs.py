@@ -114,3 +114,35 @@ WORKLOADS = {
     5: dict(name="twoshot_n8_bandwidth_16M-256M", nranks=8, dtype=I32, dist="int20", sigma=1.0,
             sizes=[1 << k for k in range(24, 29)], iters=20, algo="twoshot"),
 }
+
+
+def device_draw(dist: str, dtype: str, nranks: int, count: int, workload: int, size_idx: int,
+                iteration: int, sigma: float = 1.0):
+    """Like :func:`rank_inputs` but drawn on the GPU with a seeded torch generator (for
+    messages too large to generate on the host quickly). Returns a list of nranks device
+    tensors (bfloat16 data as int16 bit patterns). The stream differs from the host recipe."""
+    import torch
+
+    seed = int(np.random.SeedSequence([workload, size_idx, iteration, 1 << 20]).generate_state(1)[0])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    out = []
+    for r in range(nranks):
+        if dist == "rankconst":
+            t = torch.full((count,), r, device="cuda",
+                           dtype={F32: torch.float32, I32: torch.int32, BF16: torch.float32}[dtype])
+            if dtype == BF16:
+                t = t.to(torch.bfloat16).view(torch.int16)
+        elif dist == "uniform":
+            t = torch.rand(count, generator=g, device="cuda", dtype=torch.float32) * 2.0 - 1.0
+        elif dist == "int20":
+            t = torch.randint(-(1 << 20), (1 << 20) + 1, (count,), generator=g, device="cuda",
+                              dtype=torch.int32)
+        elif dist == "normal":
+            t = torch.randn(count, generator=g, device="cuda", dtype=torch.float32) * sigma
+            if dtype == BF16:
+                t = t.to(torch.bfloat16).view(torch.int16)
+        else:
+            raise ValueError(f"no device recipe for {dist!r}")
+        out.append(t.contiguous())
+    return out
