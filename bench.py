@@ -75,22 +75,34 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
     count = size // eb
     nsets = max(1, min(iters, set_cap_bytes // (n * size)))
     host_sets = []
-    ins, outs = [], []
-    for k in range(nsets):
-        if n * size <= (8 << 20):
+    if n * size <= (8 << 20):
+        xs = []
+        for k in range(nsets):
             x = I.rank_inputs(wl["dist"], dt, n, count, wid, size_idx, k, wl["sigma"])
             I.assert_finite(x, dt)
-            if check and k == nsets - 1:
-                host_sets.append((k, x))
-            d = _to_device(x)
-        else:
-            d = I.device_draw(wl["dist"], dt, n, count, wid, size_idx, k, wl["sigma"])
-        ins += d
-        outs += [torch.empty_like(t) for t in d]
+            xs.append(x)
+        if check:
+            host_sets.append((nsets - 1, xs[-1]))
+        # one contiguous [nsets, count] buffer per rank: set k of rank r is a slice, so the
+        # sets are evenly spaced and the persistent loop addresses them without a table
+        big = [torch.from_numpy(np.ascontiguousarray(
+            np.stack([xs[k][r] for k in range(nsets)]).view(
+                np.int16 if dt == "bf16" else xs[0].dtype))).cuda() for r in range(n)]
+        del xs
+    else:
+        big = [t.view(1, -1) for t in
+               I.device_draw(wl["dist"], dt, n, count, wid, size_idx, 0, wl["sigma"])]
+        nsets = 1
+    outs_big = [torch.empty_like(b) for b in big]
+    ins = [big[r][k] for k in range(nsets) for r in range(n)]
+    outs = [outs_big[r][k] for k in range(nsets) for r in range(n)]
     torch.cuda.synchronize()
     aid = A.ALGOS[algo]
-    if warmup > 0:
-        A.ar_bench(h, ins, outs, nsets, count, aid, warmup, timestamps=False)
+    # Untimed pass over every input set first: the timed iterations then find the sets where the
+    # preceding computation would have left them (in the caches while they fit).
+    warm = max(warmup, nsets)
+    if warm > 0:
+        A.ar_bench(h, ins, outs, nsets, count, aid, warm, timestamps=False)
     ts, te, ms = A.ar_bench(h, ins, outs, nsets, count, aid, iters)
     ts = ts.reshape(iters, n).astype(np.int64)
     te = te.reshape(iters, n).astype(np.int64)
@@ -126,7 +138,7 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
         res["spot_check"] = bool(ok)
         if not ok:
             raise AssertionError(f"spot check failed: {algo} n={n} size={size}")
-    del ins, outs
+    del ins, outs, big, outs_big
     return res
 
 

@@ -54,6 +54,8 @@ struct Args {
   void* out[kMaxRanks];
   const void* const* in_tab;  // optional device table [nsets][nranks] (persistent benchmark)
   void* const* out_tab;
+  int64_t in_set_stride;      // when the sets are evenly spaced: set j of rank r is
+  int64_t out_set_stride;     //   in[r] + j * in_set_stride (no table; 0 = use the table)
   uint8_t* base;              // symmetric scratch: rank r's block starts at base + r * stride
   uint64_t stride;
   Region p1;    // one-shot sentinel slots / two-shot reduce-scatter slots (sentinel)

@@ -39,8 +39,28 @@ constexpr int kCoh = kSc1;
 // Data-format word of a raw (untyped, stride 0) buffer descriptor on CDNA: 32-bit data format.
 constexpr int kRsrcWord3 = 0x00020000;
 
+// A buffer descriptor lives in scalar registers, so its base must be the same in every lane.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, kRsrcWord3);
+}
+
+// Out-of-range offset: at or beyond num_records of every descriptor (regions are below 1 GiB and
+// user buffers below 2 GiB), so a load there returns zeros and a store there is dropped by the
+// buffer unit. Using it instead of a branch keeps runs of stores in one basic block: on gfx9
+// loads and stores share one in-order counter, and a store that follows a control-flow join
+// otherwise gets a full s_waitcnt in front of it, which would serialise the write-through stores
+// to the peers.
+constexpr uint32_t kDrop = 0x80000000u;
+
+// For a base that is wave-uniform by construction but reaches the compiler through a memory
+// load (a pointer read from a table): readfirstlane tells the compiler it is uniform, so the
+// accesses are not wrapped in a loop over distinct descriptor values. Never use it for a base
+// that may differ between lanes.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }

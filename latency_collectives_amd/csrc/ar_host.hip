@@ -33,7 +33,7 @@ thread_local std::string g_err;
 constexpr int kRegions = 7;
 enum RegionId { RG_P1 = 0, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT };
 constexpr uint64_t kDefaultCap = 256ull << 20;
-constexpr uint64_t kMaxCap = 1ull << 31;
+constexpr uint64_t kMaxCap = 1ull << 30;  // keeps every region below the drop offset (2 GiB)
 constexpr int kXcds = 8;
 
 uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
@@ -352,8 +352,8 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
   sz[RG_BDAT] = {slot_os, 1ull * N * slot_os};
   uint64_t off = 0;
   for (int i = 0; i < kRegions; ++i) {
-    if (sz[i].bytes >= (1ull << 32)) {
-      ar_fail(AR_ETOOBIG, "scratch region %d would exceed 4 GiB per rank", i);
+    if (sz[i].bytes >= (1ull << 31)) {
+      ar_fail(AR_ETOOBIG, "scratch region %d would exceed 2 GiB per rank", i);
       release(h);
       return nullptr;
     }
@@ -523,7 +523,29 @@ int ar_bench(ar_handle* h, const void* const* in_sets, void* const* out_sets, in
   a.iters = iters;
   a.drift = h->drift;
   a.nsets = nsets;
-  if (!barrier_only) {
+  // Evenly spaced sets (set j of rank r at set 0's address + j * stride) need no table.
+  bool affine = !barrier_only && nsets > 1;
+  int64_t sin = 0, sout = 0;
+  if (affine) {
+    sin = reinterpret_cast<intptr_t>(in_sets[N]) - reinterpret_cast<intptr_t>(in_sets[0]);
+    sout = reinterpret_cast<intptr_t>(out_sets[N]) - reinterpret_cast<intptr_t>(out_sets[0]);
+    for (int j = 0; j < nsets && affine; ++j)
+      for (int r = 0; r < N && affine; ++r) {
+        affine = reinterpret_cast<intptr_t>(in_sets[j * N + r]) ==
+                     reinterpret_cast<intptr_t>(in_sets[r]) + j * sin &&
+                 reinterpret_cast<intptr_t>(out_sets[j * N + r]) ==
+                     reinterpret_cast<intptr_t>(out_sets[r]) + j * sout;
+      }
+    if (sin == 0 && sout == 0) affine = false;
+  }
+  if (!barrier_only && (affine || nsets == 1)) {
+    for (int r = 0; r < N; ++r) {
+      a.in[r] = in_sets[r];
+      a.out[r] = out_sets[r];
+    }
+    a.in_set_stride = affine ? sin : 0;
+    a.out_set_stride = affine ? sout : 0;
+  } else if (!barrier_only) {
     const size_t need = 2ull * nsets * N;
     if (h->tab_cap < need) {
       if (h->tab) (void)hipFree(h->tab);

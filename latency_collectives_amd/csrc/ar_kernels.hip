@@ -62,6 +62,16 @@ __device__ __forceinline__ rsrc_t region_rsrc(const Args& a, int rank, const Reg
   return make_rsrc(a.base + static_cast<uint64_t>(rank) * a.stride + g.off, g.bytes);
 }
 
+// Region of the j-th peer after rank r (q = (r + j) mod N), or a descriptor that drops every
+// access when j >= N (the peer does not exist); keeps the push loops free of branches.
+__device__ __forceinline__ rsrc_t peer_rsrc(const Args& a, int r, int j, const Region& g) {
+  int q = r + j;
+  if (q >= a.nranks) q -= a.nranks;
+  const bool live = j < a.nranks;
+  return make_rsrc(a.base + static_cast<uint64_t>(live ? q : 0) * a.stride + g.off,
+                   live ? g.bytes : 0u);
+}
+
 // Where a poll loop reports a timeout: the few kernel arguments the slow path needs, passed by
 // value so that the argument block never has to be copied to private memory.
 struct PollEnv {
@@ -118,13 +128,22 @@ __device__ __forceinline__ bool poll_lines(const Args& a, rsrc_t own, uint32_t o
   uint32_t spins = 0;
   uint64_t t_first = 0;
   while (true) {
+    // one load per possible source, in one basic block; lines already received (or sources
+    // that do not exist) are loaded from the drop offset and not kept
+    u32x4 t[NMAX];
 #pragma unroll
-    for (int q = 0; q < NMAX; ++q)
-      if (pend & (1u << q)) v[q] = ld16<kCoh>(own, off0 + static_cast<uint32_t>(q) * qstride);
+    for (int q = 0; q < NMAX; ++q) {
+      const bool want = (pend >> q) & 1u;
+      t[q] = ld16<kCoh>(own, want ? off0 + static_cast<uint32_t>(q) * qstride : kDrop);
+    }
     compiler_fence();
 #pragma unroll
-    for (int q = 0; q < NMAX; ++q)
-      if ((pend & (1u << q)) && ready(v[q])) pend &= ~(1u << q);
+    for (int q = 0; q < NMAX; ++q) {
+      if ((pend >> q) & 1u) {
+        v[q] = t[q];
+        if (ready(t[q])) pend &= ~(1u << q);
+      }
+    }
     const uint64_t waiting = __ballot(pend != 0);
     if (waiting == 0) return true;
     if ((++spins & 1023u) == 0) {
@@ -166,11 +185,25 @@ __device__ __forceinline__ u32x4 sentinel_vec() {
   return u32x4{s, s, s, s};
 }
 
+// Write the sentinel back into the slots of the sources in `mask` (source q's line at
+// off0 + q * qstride), branch-free.
+template <int NMAX>
+__device__ __forceinline__ void rearm(rsrc_t own, uint32_t off0, uint32_t qstride, uint32_t mask,
+                                      u32x4 sent) {
+#pragma unroll
+  for (int q = 0; q < NMAX; ++q)
+    st16<kCoh>(own, ((mask >> q) & 1u) ? off0 + static_cast<uint32_t>(q) * qstride : kDrop, sent);
+}
+
 // ------------------------------------------------------------------ one-shot, LL protocol
 //
 // Push: every 8 bytes of the rank's chunk go to every peer as one 16-byte line {payload, s}
 // (§IV "LL"). Receive: poll each peer's line until its flag equals s, then fold in rank order.
 // Nothing needs resetting: an old line carries an older sequence number.
+//
+// When the rank has at least one lane per unit (small messages, the latency regime) every lane
+// owns at most one unit: it keeps its own payload in registers from the push to the fold. With
+// more units than lanes the units are taken in passes of T lanes, the push of all passes first.
 template <int DT, int NMAX>
 __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
                                 rsrc_t out_r, int k) {
@@ -179,43 +212,51 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
   const uint32_t elo = static_cast<uint32_t>(s), ehi = static_cast<uint32_t>(s >> 32);
   const uint32_t slot = a.ll.slot, CU = a.chunk_units;
   const uint32_t unit0 = static_cast<uint32_t>(k) * CU;
-  if (r != a.withhold) {
-    const uint32_t mine = (b * N + r) * slot;
-    for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
-      const uint32_t i = i0 + c.lane;
-      if (i < CU) {
-        uint32_t w[2];
-        load_unit<DT, 8>(in_r, (unit0 + i) * 8u, a.nbytes, w);
-        const u32x4 line = {w[0], w[1], elo, ehi};
-#pragma unroll
-        for (int j = 1; j < NMAX; ++j) {
-          if (j < N) {
-            int q = r + j;
-            if (q >= N) q -= N;
-            st16<kCoh>(region_rsrc(a, q, a.ll), mine + i * 16u, line);
-          }
-        }
-      }
-    }
-  }
+  const bool sends = r != a.withhold;
+  const uint32_t mine = (b * N + r) * slot;
   const rsrc_t own = region_rsrc(a, r, a.ll);
   const uint32_t peers = peer_mask(N, r);
+  auto push = [&](uint32_t i, bool act, const uint32_t* w) {
+    const u32x4 line = {w[0], w[1], elo, ehi};
+    const uint32_t off = act ? mine + i * 16u : kDrop;
+#pragma unroll
+    for (int j = 1; j < NMAX; ++j) st16<kCoh>(peer_rsrc(a, r, j, a.ll), off, line);
+  };
   auto ready = [elo, ehi](u32x4 l) { return l.z == elo && l.w == ehi; };
-  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
-    const uint32_t i = i0 + c.lane;
-    const bool act = i < CU;
-    uint32_t x[2] = {0u, 0u};
-    if (act) load_unit<DT, 8>(in_r, (unit0 + i) * 8u, a.nbytes, x);
+  auto recv = [&](uint32_t i, bool act, const uint32_t* x) -> bool {
     u32x4 v[NMAX];
 #pragma unroll
     for (int q = 0; q < NMAX; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
     if (!poll_lines<NMAX>(a, own, b * N * slot + i * 16u, slot, act ? peers : 0u, v, ready, r, s))
       return false;
-    if (act) {
-      uint32_t o[2];
-      fold_rank_order<DT, NMAX, 2>(N, r, x, v, o);
-      store_unit<DT, 8>(out_r, (unit0 + i) * 8u, a.nbytes, o);
+    uint32_t o[2];
+    fold_rank_order<DT, NMAX, 2>(N, r, x, v, o);
+    store_unit<DT, 8>(out_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, o);
+    return true;
+  };
+  if (c.T >= CU) {
+    const uint32_t i = c.t0 + c.lane;
+    const bool act = i < CU;
+    uint32_t x[2] = {0u, 0u};
+    load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, x);
+    if (sends) push(i, act, x);
+    return recv(i, act, x);
+  }
+  if (sends) {
+    for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+      const uint32_t i = i0 + c.lane;
+      const bool act = i < CU;
+      uint32_t w[2];
+      load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, w);
+      push(i, act, w);
     }
+  }
+  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+    const uint32_t i = i0 + c.lane;
+    const bool act = i < CU;
+    uint32_t x[2] = {0u, 0u};
+    load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, x);
+    if (!recv(i, act, x)) return false;
   }
   return true;
 }
@@ -224,7 +265,7 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
 //
 // Push raw 16-byte units into every peer's slot (§IV "Sentinel"). Receive: poll until no element
 // of a peer's unit equals the sentinel, fold in rank order, then write the sentinel back so the
-// slot is armed for step s+2 (the same buffer).
+// slot is armed for step s+2 (the same buffer). Passes as in the LL step.
 template <int DT, int NMAX>
 __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
                                       rsrc_t out_r, int k) {
@@ -232,47 +273,53 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t slot = a.p1.slot, CU = a.chunk_units;
   const uint32_t unit0 = static_cast<uint32_t>(k) * CU;
-  if (r != a.withhold) {
-    const uint32_t mine = (b * N + r) * slot;
-    for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
-      const uint32_t i = i0 + c.lane;
-      if (i < CU) {
-        uint32_t w[4];
-        load_unit<DT, 16>(in_r, (unit0 + i) * 16u, a.nbytes, w);
-        const u32x4 x = {w[0], w[1], w[2], w[3]};
-#pragma unroll
-        for (int j = 1; j < NMAX; ++j) {
-          if (j < N) {
-            int q = r + j;
-            if (q >= N) q -= N;
-            st16<kCoh>(region_rsrc(a, q, a.p1), mine + i * 16u, x);
-          }
-        }
-      }
-    }
-  }
+  const bool sends = r != a.withhold;
+  const uint32_t mine = (b * N + r) * slot;
   const rsrc_t own = region_rsrc(a, r, a.p1);
   const uint32_t peers = peer_mask(N, r);
   const u32x4 sent = sentinel_vec<DT>();
+  auto push = [&](uint32_t i, bool act, const uint32_t* w) {
+    const u32x4 x = {w[0], w[1], w[2], w[3]};
+    const uint32_t off = act ? mine + i * 16u : kDrop;
+#pragma unroll
+    for (int j = 1; j < NMAX; ++j) st16<kCoh>(peer_rsrc(a, r, j, a.p1), off, x);
+  };
   auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
-  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
-    const uint32_t i = i0 + c.lane;
-    const bool act = i < CU;
-    uint32_t x[4] = {0u, 0u, 0u, 0u};
-    if (act) load_unit<DT, 16>(in_r, (unit0 + i) * 16u, a.nbytes, x);
+  auto recv = [&](uint32_t i, bool act, const uint32_t* x) -> bool {
     u32x4 v[NMAX];
 #pragma unroll
     for (int q = 0; q < NMAX; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
     const uint32_t off0 = b * N * slot + i * 16u;
     if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
-    if (act) {
-      uint32_t o[4];
-      fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
-      store_unit<DT, 16>(out_r, (unit0 + i) * 16u, a.nbytes, o);
-#pragma unroll
-      for (int q = 0; q < NMAX; ++q)
-        if (q < N && q != r) st16<kCoh>(own, off0 + static_cast<uint32_t>(q) * slot, sent);
+    uint32_t o[4];
+    fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
+    rearm<NMAX>(own, off0, slot, act ? peers : 0u, sent);
+    store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, o);
+    return true;
+  };
+  if (c.T >= CU) {
+    const uint32_t i = c.t0 + c.lane;
+    const bool act = i < CU;
+    uint32_t x[4] = {0u, 0u, 0u, 0u};
+    load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
+    if (sends) push(i, act, x);
+    return recv(i, act, x);
+  }
+  if (sends) {
+    for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+      const uint32_t i = i0 + c.lane;
+      const bool act = i < CU;
+      uint32_t w[4];
+      load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, w);
+      push(i, act, w);
     }
+  }
+  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+    const uint32_t i = i0 + c.lane;
+    const bool act = i < CU;
+    uint32_t x[4] = {0u, 0u, 0u, 0u};
+    load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
+    if (!recv(i, act, x)) return false;
   }
   return true;
 }
@@ -301,16 +348,14 @@ __device__ __forceinline__ bool allgather_recv(const Args& a, const Ctx& c, uint
 #pragma unroll
     for (int q = 0; q < NMAX; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
     const uint32_t off0 = b * N * slot + i * 16u;
-    if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
-    if (act) {
+    const uint32_t mask = act ? peers : 0u;
+    if (!poll_lines<NMAX>(a, own, off0, slot, mask, v, ready, r, s)) return false;
+    rearm<NMAX>(own, off0, slot, mask, sent);
 #pragma unroll
-      for (int p = 0; p < NMAX; ++p) {
-        if (p < N && p != r) {
-          const uint32_t o[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
-          store_unit<DT, 16>(out_r, (p * P + k * CU + i) * 16u, a.nbytes, o);
-          st16<kCoh>(own, off0 + static_cast<uint32_t>(p) * slot, sent);
-        }
-      }
+    for (int p = 0; p < NMAX; ++p) {
+      const uint32_t o[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+      store_unit<DT, 16>(out_r, ((mask >> p) & 1u) ? (p * P + k * CU + i) * 16u : kDrop,
+                         a.nbytes, o);
     }
   }
   return true;
@@ -319,16 +364,28 @@ __device__ __forceinline__ bool allgather_recv(const Args& a, const Ctx& c, uint
 // Owner r pushes its reduced unit i to every peer's all-gather slot r.
 template <int NMAX>
 __device__ __forceinline__ void allgather_push(const Args& a, int r, uint32_t b, uint32_t i,
-                                               u32x4 res) {
-  const int N = a.nranks;
-  const uint32_t mine = (b * N + r) * a.p2.slot + i * 16u;
+                                               bool act, u32x4 res) {
+  const uint32_t off = act ? (b * a.nranks + r) * a.p2.slot + i * 16u : kDrop;
 #pragma unroll
-  for (int j = 1; j < NMAX; ++j) {
-    if (j < N) {
-      int q = r + j;
-      if (q >= N) q -= N;
-      st16<kCoh>(region_rsrc(a, q, a.p2), mine, res);
-    }
+  for (int j = 1; j < NMAX; ++j) st16<kCoh>(peer_rsrc(a, r, j, a.p2), off, res);
+}
+
+// Load unit i of the chunk in the partition of the j-th peer after rank r, for j = 1..N-1
+// (zeros for peers that do not exist or an idle lane); all loads are issued before any use.
+template <int DT, int NMAX>
+__device__ __forceinline__ void load_partitions(const Args& a, int r, rsrc_t in_r, int k,
+                                                uint32_t i, bool act, int jfirst,
+                                                uint32_t (&w)[NMAX][4]) {
+  const int N = a.nranks;
+  const uint32_t CU = a.chunk_units, P = a.part_units;
+#pragma unroll
+  for (int j = 0; j < NMAX; ++j) {
+    w[j][0] = w[j][1] = w[j][2] = w[j][3] = 0u;
+    if (j < jfirst) continue;
+    int p = r + j;
+    if (p >= N) p -= N;
+    const bool live = act && j < N;
+    load_unit<DT, 16>(in_r, live ? (p * P + k * CU + i) * 16u : kDrop, a.nbytes, w[j]);
   }
 }
 
@@ -340,23 +397,19 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t slot = a.p1.slot, CU = a.chunk_units, P = a.part_units;
   const bool sends = r != a.withhold;
-  // Reduce-scatter push: partition p's chunk goes to owner p's slot r.
+  // Reduce-scatter push: partition p's chunk goes to owner p's slot r (loads first, then the
+  // stores in one block).
   if (sends) {
     const uint32_t mine = (b * N + r) * slot;
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
-      if (i < CU) {
+      const bool act = i < CU;
+      uint32_t w[NMAX][4];
+      load_partitions<DT, NMAX>(a, r, in_r, k, i, act, 1, w);
+      const uint32_t off = act ? mine + i * 16u : kDrop;
 #pragma unroll
-        for (int j = 1; j < NMAX; ++j) {
-          if (j < N) {
-            int p = r + j;
-            if (p >= N) p -= N;
-            uint32_t w[4];
-            load_unit<DT, 16>(in_r, (p * P + k * CU + i) * 16u, a.nbytes, w);
-            st16<kCoh>(region_rsrc(a, p, a.p1), mine + i * 16u, u32x4{w[0], w[1], w[2], w[3]});
-          }
-        }
-      }
+      for (int j = 1; j < NMAX; ++j)
+        st16<kCoh>(peer_rsrc(a, r, j, a.p1), off, u32x4{w[j][0], w[j][1], w[j][2], w[j][3]});
     }
   }
   // Owner: reduce its partition in rank order, keep the result, push it to every peer.
@@ -369,21 +422,18 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
     const bool act = i < CU;
     uint32_t x[4] = {0u, 0u, 0u, 0u};
     const uint32_t uoff = (r * P + k * CU + i) * 16u;
-    if (act) load_unit<DT, 16>(in_r, uoff, a.nbytes, x);
+    load_unit<DT, 16>(in_r, act ? uoff : kDrop, a.nbytes, x);
     u32x4 v[NMAX];
 #pragma unroll
     for (int q = 0; q < NMAX; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
     const uint32_t off0 = b * N * slot + i * 16u;
-    if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
-    if (act) {
-      uint32_t o[4];
-      fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
-      store_unit<DT, 16>(out_r, uoff, a.nbytes, o);
-      if (sends) allgather_push<NMAX>(a, r, b, i, u32x4{o[0], o[1], o[2], o[3]});
-#pragma unroll
-      for (int q = 0; q < NMAX; ++q)
-        if (q < N && q != r) st16<kCoh>(own, off0 + static_cast<uint32_t>(q) * slot, sent);
-    }
+    const uint32_t mask = act ? peers : 0u;
+    if (!poll_lines<NMAX>(a, own, off0, slot, mask, v, ready, r, s)) return false;
+    uint32_t o[4];
+    fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
+    if (sends) allgather_push<NMAX>(a, r, b, i, act, u32x4{o[0], o[1], o[2], o[3]});
+    rearm<NMAX>(own, off0, slot, mask, sent);
+    store_unit<DT, 16>(out_r, act ? uoff : kDrop, a.nbytes, o);
   }
   return allgather_recv<DT, NMAX>(a, c, s, out_r, k);
 }
@@ -411,26 +461,21 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
   if (has_units && r != a.withhold) {
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
-      if (i < CU) {
+      const bool act = i < CU;
+      uint32_t w[NMAX][4];
+      load_partitions<DT, NMAX>(a, r, in_r, k, i, act, 0, w);
+      const uint32_t off = act ? b * a.acc.slot + i * 16u : kDrop;
 #pragma unroll
-        for (int j = 0; j < NMAX; ++j) {
-          if (j < N) {
-            int p = r + j;
-            if (p >= N) p -= N;
-            uint32_t w[4];
-            load_unit<DT, 16>(in_r, (p * P + k * CU + i) * 16u, a.nbytes, w);
-            uint8_t* dst = a.base + static_cast<uint64_t>(p) * a.stride + a.acc.off +
-                           static_cast<uint64_t>(b) * a.acc.slot + static_cast<uint64_t>(i) * 16u;
+      for (int j = 0; j < NMAX; ++j) {
+        const rsrc_t dst = j == 0 ? region_rsrc(a, r, a.acc) : peer_rsrc(a, r, j, a.acc);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if constexpr (DT == DT_F32) {
-                __hip_atomic_fetch_add(reinterpret_cast<float*>(dst) + e, __uint_as_float(w[e]),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              } else {
-                __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(dst) + e, w[e],
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              }
-            }
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (DT == DT_F32) {
+            (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(__uint_as_float(w[j][e]), dst,
+                                                                 off + 4u * e, 0, 0);
+          } else {
+            (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(static_cast<int>(w[j][e]), dst,
+                                                                off + 4u * e, 0, 0);
           }
         }
       }
@@ -456,17 +501,20 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
                    static_cast<uint64_t>(b) * a.acc.slot;
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
-      if (i < CU) {
+      const bool act = i < CU;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (act) {
         uint64_t* q = reinterpret_cast<uint64_t*>(acc + static_cast<uint64_t>(i) * 16u);
-        const uint64_t lo = __hip_atomic_exchange(q, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t lo =
+            __hip_atomic_exchange(q, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint64_t hi =
             __hip_atomic_exchange(q + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const u32x4 v = {static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
-                         static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
-        const uint32_t o[4] = {v.x, v.y, v.z, v.w};
-        store_unit<DT, 16>(out_r, (r * P + k * CU + i) * 16u, a.nbytes, o);
-        if (r != a.withhold) allgather_push<NMAX>(a, r, b, i, v);
+        v = u32x4{static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
+                  static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
       }
+      if (r != a.withhold) allgather_push<NMAX>(a, r, b, i, act, v);
+      const uint32_t o[4] = {v.x, v.y, v.z, v.w};
+      store_unit<DT, 16>(out_r, act ? (r * P + k * CU + i) * 16u : kDrop, a.nbytes, o);
     }
     if (c.lane == 0) __hip_atomic_store(my_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -500,27 +548,31 @@ __device__ bool xrank_barrier(const Args& a, const Ctx& c, uint64_t val, uint64_
   const int N = a.nranks, r = c.rank;
   __syncthreads();
   if (c.wave == 0) {
+    // lane q signals peer q and watches peer q's flag in this rank's block
     const int q = c.lane;
     const bool peer = q < N && q != r;
     if (peer && r != a.withhold) {
-      const uint32_t off = (static_cast<uint32_t>(r) * kMaxCtasPerRank + c.cta) * 8u;
-      st8<kCoh>(region_rsrc(a, q, a.bar), off,
-                u32x2{static_cast<uint32_t>(val), static_cast<uint32_t>(val >> 32)});
+      uint64_t* theirs = reinterpret_cast<uint64_t*>(a.base + static_cast<uint64_t>(q) * a.stride +
+                                                     a.bar.off) +
+                         (static_cast<uint32_t>(r) * kMaxCtasPerRank + c.cta);
+      __hip_atomic_store(theirs, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    const rsrc_t own = region_rsrc(a, r, a.bar);
-    const uint32_t off = (static_cast<uint32_t>(q) * kMaxCtasPerRank + c.cta) * 8u;
+    const uint64_t* mine =
+        reinterpret_cast<const uint64_t*>(a.base + static_cast<uint64_t>(r) * a.stride +
+                                          a.bar.off) +
+        (static_cast<uint32_t>(peer ? q : 0) * kMaxCtasPerRank + c.cta);
     bool need = peer;
     uint32_t spins = 0;
     uint64_t t_first = 0;
     while (true) {
       if (need) {
-        const u32x2 f = ld8<kCoh>(own, off);
-        compiler_fence();
-        const uint64_t fv = (static_cast<uint64_t>(f.y) << 32) | f.x;
+        const uint64_t fv = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (fv >= val) need = false;
       }
-      if (__ballot(need) == 0) break;
-      if ((++spins & 1023u) == 0 && !poll_check(poll_env(a), t_first, r, q, s)) {
+      const uint64_t waiting = __ballot(need);
+      if (waiting == 0) break;
+      if ((++spins & 1023u) == 0 &&
+          !poll_check(poll_env(a), t_first, r, __builtin_ctzll(waiting), s)) {
         if (c.lane == 0) g_bar_fail = 1;
         break;
       }
@@ -543,39 +595,33 @@ __device__ bool step_barrier2(const Args& a, const Ctx& c, uint64_t s, rsrc_t in
   if (r != a.withhold) {
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
-      if (i < CU) {
-        uint32_t w[4];
-        load_unit<DT, 16>(in_r, (unit0 + i) * 16u, a.nbytes, w);
-        const u32x4 x = {w[0], w[1], w[2], w[3]};
+      const bool act = i < CU;
+      uint32_t w[4];
+      load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, w);
+      const u32x4 x = {w[0], w[1], w[2], w[3]};
+      const uint32_t off = act ? r * slot + i * 16u : kDrop;
 #pragma unroll
-        for (int j = 1; j < NMAX; ++j) {
-          if (j < N) {
-            int q = r + j;
-            if (q >= N) q -= N;
-            st16<kCoh>(region_rsrc(a, q, a.bdat), r * slot + i * 16u, x);
-          }
-        }
-      }
+      for (int j = 1; j < NMAX; ++j) st16<kCoh>(peer_rsrc(a, r, j, a.bdat), off, x);
     }
   }
   wait_all_mem();  // the coherent pushes are performed before the flag that announces them
   if (!xrank_barrier(a, c, 2 * s + 1, s)) return false;
   acquire_agent();
   const rsrc_t own = region_rsrc(a, r, a.bdat);
+  const uint32_t peers = peer_mask(N, r);
   for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
     const uint32_t i = i0 + c.lane;
-    if (i < CU) {
-      uint32_t x[4];
-      load_unit<DT, 16>(in_r, (unit0 + i) * 16u, a.nbytes, x);
-      u32x4 v[NMAX];
+    const bool act = i < CU;
+    const uint32_t mask = act ? peers : 0u;
+    uint32_t x[4];
+    load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
+    u32x4 v[NMAX];
 #pragma unroll
-      for (int q = 0; q < NMAX; ++q)
-        v[q] = (q < N && q != r) ? ld16<kCoh>(own, static_cast<uint32_t>(q) * slot + i * 16u)
-                                 : u32x4{0u, 0u, 0u, 0u};
-      uint32_t o[4];
-      fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
-      store_unit<DT, 16>(out_r, (unit0 + i) * 16u, a.nbytes, o);
-    }
+    for (int q = 0; q < NMAX; ++q)
+      v[q] = ld16<kCoh>(own, ((mask >> q) & 1u) ? static_cast<uint32_t>(q) * slot + i * 16u : kDrop);
+    uint32_t o[4];
+    fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
+    store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, o);
   }
   return true;
 }
@@ -648,19 +694,36 @@ __global__ __launch_bounds__(256) void ar_kernel(Args a) {
   constexpr bool kRearm = ALGO == ALGO_ONESHOT_SENTINEL || ALGO == ALGO_TWOSHOT ||
                           ALGO == ALGO_LL128_ATOMIC;
   constexpr bool kBarrier = ALGO == ALGO_BARRIER2 || ALGO == ALGO_BARRIER_ONLY;
-  const bool join = a.iters > 1 && ALGO != ALGO_BARRIER_ONLY;
+  // A rank that is a single wave needs no join: its iterations are already in program order.
+  const bool join = a.iters > 1 && ALGO != ALGO_BARRIER_ONLY && (a.ctas > 1 || wpb > 1);
   if (kBarrier || join) fail_flags_init();
   const uint64_t nsteps = static_cast<uint64_t>(a.iters) * a.chunks;
+  // Buffers of iteration `it`: evenly spaced sets are addressed arithmetically; otherwise the
+  // set table is read one iteration ahead so that its latency stays off the timed path.
+  const bool affine = a.in_set_stride != 0 || a.out_set_stride != 0;
+  const bool table = !affine && a.in_tab != nullptr;
+  const void* next_in = table ? a.in_tab[c.rank] : a.in[c.rank];
+  void* next_out = table ? a.out_tab[c.rank] : a.out[c.rank];
+  int set = 0;
   for (int it = 0; it < a.iters; ++it) {
-    const int set = a.in_tab ? it % a.nsets : 0;
-    const void* inp = a.in_tab ? a.in_tab[set * N + c.rank] : a.in[c.rank];
-    void* outp = a.out_tab ? a.out_tab[set * N + c.rank] : a.out[c.rank];
-    const rsrc_t in_r = make_rsrc(inp, a.nbytes);
-    const rsrc_t out_r = make_rsrc(outp, a.nbytes);
+    const void* inp = next_in;
+    void* outp = next_out;
+    if (affine) {
+      inp = static_cast<const uint8_t*>(a.in[c.rank]) + set * a.in_set_stride;
+      outp = static_cast<uint8_t*>(a.out[c.rank]) + set * a.out_set_stride;
+    }
+    if (++set == a.nsets) set = 0;
+    const rsrc_t in_r = make_rsrc(uniform_ptr(inp), a.nbytes);
+    const rsrc_t out_r = make_rsrc(uniform_ptr(outp), a.nbytes);
     if (a.drift > 0) drift_sleep(a, it, c.rank, c.cta);
     const uint64_t ts_idx =
         ((static_cast<uint64_t>(it) * N + c.rank) * a.ctas + c.cta) * wpb + c.wave;
-    if (a.ts_start != nullptr && c.lane == 0) a.ts_start[ts_idx] = now_ticks();
+    uint64_t t_start = 0;
+    if (a.ts_start != nullptr) t_start = now_ticks();
+    if (table && it + 1 < a.iters) {
+      next_in = a.in_tab[set * N + c.rank];
+      next_out = a.out_tab[set * N + c.rank];
+    }
     bool failed = false;
     uint64_t s = 0;
     for (int k = 0; k < a.chunks; ++k) {
@@ -688,7 +751,11 @@ __global__ __launch_bounds__(256) void ar_kernel(Args a) {
     }
     if (!failed && a.ts_end != nullptr) {
       wait_all_mem();
-      if (c.lane == 0) a.ts_end[ts_idx] = now_ticks();
+      const uint64_t t_end = now_ticks();
+      if (c.lane == 0) {
+        a.ts_start[ts_idx] = t_start;
+        a.ts_end[ts_idx] = t_end;
+      }
     }
     if (join) {
       if (!rank_join(a, c, s, failed)) return;

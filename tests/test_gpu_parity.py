@@ -194,12 +194,15 @@ def test_c1_shape_1000_iterations_all_checked():
     n, count, iters = 2, 32, 1000
     with handle(n, 128, "f32") as h:
         xs = [draw("f32", n, count, seed=k) for k in range(iters)]
-        big = np.concatenate(xs, axis=0)
-        dev = to_device(big)
-        outs = [torch.empty_like(t) for t in dev]
-        A.ar_bench(h, dev, outs, iters, count, A.AR_ONESHOT_LL, iters)
+        # evenly spaced sets (one [iters, count] buffer per rank): the table-free path
+        big = [torch.from_numpy(np.stack([xs[k][r] for k in range(iters)])).cuda()
+               for r in range(n)]
+        obig = [torch.empty_like(b) for b in big]
+        ins = [big[r][k] for k in range(iters) for r in range(n)]
+        outs = [obig[r][k] for k in range(iters) for r in range(n)]
+        A.ar_bench(h, ins, outs, iters, count, A.AR_ONESHOT_LL, iters)
         for k in range(iters):
-            got = from_device(outs[k * n:(k + 1) * n], np.float32)
+            got = np.stack([obig[r][k].cpu().numpy() for r in range(n)])
             assert_matches(got, xs[k], "oneshot_ll", "f32")
 
 
