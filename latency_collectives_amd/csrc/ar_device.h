@@ -221,60 +221,69 @@ __device__ __forceinline__ bool vec_clear(u32x4 v) {
 }
 
 // ------------------------------------------------------------------ user buffers
+//
+// A user buffer of `nbytes` bytes is read through a descriptor whose num_records is nbytes
+// rounded up to a multiple of 4 (in_rsrc) and written through one whose num_records is nbytes
+// (out_rsrc). The buffer unit checks the range per 32-bit word: words past the end read as zero
+// and are not written. So one vector access per unit handles every tail of 4-byte elements and
+// every unit of an even bf16 count without a branch. A bf16 message of odd length ends in the
+// low half of a word whose high half is not part of the buffer: the load clears that half, and
+// the store writes that last element with one 2-byte store.
 
-// Load one unit (UB bytes, 8 or 16) of a user buffer of `nbytes` bytes at byte offset `off`.
-// A unit that runs past the end is assembled element by element and zero-padded; a unit wholly
-// past the end reads as zeros.
+__device__ __forceinline__ rsrc_t in_rsrc(const void* base, uint32_t nbytes) {
+  return make_rsrc(base, (nbytes + 3u) & ~3u);
+}
+__device__ __forceinline__ rsrc_t out_rsrc(void* base, uint32_t nbytes) {
+  return make_rsrc(base, nbytes);
+}
+
+// Load one unit (UB bytes, 8 or 16) at byte offset `off`; zeros past the end (or for kDrop).
 template <int DT, int UB>
 __device__ __forceinline__ void load_unit(rsrc_t r, uint32_t off, uint32_t nbytes, uint32_t* w) {
-  if (off + UB <= nbytes) {
-    if constexpr (UB == 16) {
-      u32x4 v = ld16<kPlain>(r, off);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else {
-      u32x2 v = ld8<kPlain>(r, off);
-      w[0] = v.x; w[1] = v.y;
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < UB / 4; ++i) w[i] = 0u;
-  if (off >= nbytes) return;
-  if constexpr (Ty<DT>::kElem == 4) {
-    for (int i = 0; i < UB / 4; ++i)
-      if (off + 4u * i < nbytes) w[i] = ld4<kPlain>(r, off + 4u * i);
+  if constexpr (UB == 16) {
+    const u32x4 v = ld16<kPlain>(r, off);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else {
-    for (int i = 0; i < UB / 2; ++i)
-      if (off + 2u * i < nbytes) {
-        uint32_t h = ld2<kPlain>(r, off + 2u * i);
-        w[i >> 1] |= (i & 1) ? (h << 16) : h;
-      }
+    const u32x2 v = ld8<kPlain>(r, off);
+    w[0] = v.x; w[1] = v.y;
+  }
+  if constexpr (Ty<DT>::kElem == 2) {
+    const uint32_t last = nbytes & ~3u;  // word holding the last element when nbytes % 4 == 2
+    const bool odd = (nbytes & 2u) != 0u;
+#pragma unroll
+    for (int k = 0; k < UB / 4; ++k)
+      w[k] = (odd && off + 4u * k == last) ? (w[k] & 0xFFFFu) : w[k];
   }
 }
 
-// Store one unit to a user buffer, dropping the bytes past `nbytes`.
+// Store one unit at byte offset `off`; nothing past the end (or for kDrop) is written.
 template <int DT, int UB, int CP = kPlain>
 __device__ __forceinline__ void store_unit(rsrc_t r, uint32_t off, uint32_t nbytes,
                                            const uint32_t* w) {
-  if (off + UB <= nbytes) {
-    if constexpr (UB == 16) {
-      st16<CP>(r, off, u32x4{w[0], w[1], w[2], w[3]});
-    } else {
-      st8<CP>(r, off, u32x2{w[0], w[1]});
-    }
-    return;
-  }
-  if (off >= nbytes) return;
-  if constexpr (Ty<DT>::kElem == 4) {
-    for (int i = 0; i < UB / 4; ++i)
-      if (off + 4u * i < nbytes) st4<CP>(r, off + 4u * i, w[i]);
+  if constexpr (UB == 16) {
+    st16<CP>(r, off, u32x4{w[0], w[1], w[2], w[3]});
   } else {
-    for (int i = 0; i < UB / 2; ++i)
-      if (off + 2u * i < nbytes) {
-        uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-        st2<CP>(r, off + 2u * i, static_cast<uint16_t>(h));
-      }
+    st8<CP>(r, off, u32x2{w[0], w[1]});
   }
+  if constexpr (Ty<DT>::kElem == 2) {
+    // the last element of an odd-length message: one 2-byte store (dropped in every other unit)
+    const uint32_t last = nbytes & ~3u;
+    const bool tail = (nbytes & 2u) != 0u && off <= last && last < off + UB;
+    uint32_t word = w[0];
+#pragma unroll
+    for (int k = 1; k < UB / 4; ++k) word = (off + 4u * k == last) ? w[k] : word;
+    st2<CP>(r, tail ? last : kDrop, static_cast<uint16_t>(word & 0xFFFFu));
+  }
+}
+
+// s_waitcnt that waits until at most `n` vector memory operations of this wave are outstanding
+// and does not wait on the other counters (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8). Vector memory operations complete in issue order, so this waits for
+// everything issued before the last `n`.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 }  // namespace ar

@@ -85,20 +85,20 @@ __device__ __forceinline__ PollEnv poll_env(const Args& a) {
   return PollEnv{a.ctl, a.status, a.timeout_ticks, a.algo};
 }
 
-// Called after every 1024 unsuccessful polls. Returns false when the wave must give up: either
-// another wave already aborted, or this poll has waited longer than the timeout, in which case
-// this wave raises the abort flag and, if it is the first, records where it stopped.
-__device__ __noinline__ bool poll_check(PollEnv e, uint64_t& t_first, int rank, int peer,
-                                        uint64_t step) {
+// Called after every 1024 unsuccessful polls with the clock value of the first such call (0 on
+// the first call). Returns that start value (set now if it was 0) while the wave may keep
+// polling, and 0 when it must give up: either another wave already aborted, or this poll has
+// waited longer than the timeout, in which case this wave raises the abort flag and, if it is
+// the first, records where it stopped. Everything is passed by value so that no kernel keeps
+// state in private memory for it.
+__device__ __noinline__ uint64_t poll_check(PollEnv e, uint64_t t_first, int rank, int peer,
+                                            uint64_t step) {
   const uint64_t now = wall_clock64();
-  if (t_first == 0) {
-    t_first = now;
-    return true;
-  }
+  if (t_first == 0) return now == 0 ? 1 : now;
   const uint32_t ab = uni(__hip_atomic_load(&e.ctl[CTL_ABORT], __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT));
-  if (ab != 0) return false;
-  if (now - t_first <= e.timeout_ticks) return true;
+  if (ab != 0) return 0;
+  if (now - t_first <= e.timeout_ticks) return t_first;
   if (threadIdx.x % kWave == static_cast<unsigned>(__builtin_ctzll(__ballot(1)))) {
     if (__hip_atomic_exchange(&e.ctl[CTL_ABORT], 1u, __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_AGENT) == 0) {
@@ -115,27 +115,28 @@ __device__ __noinline__ bool poll_check(PollEnv e, uint64_t& t_first, int rank, 
       __hip_atomic_store(&e.status[ST_CODE], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
-  return false;
+  return 0;
 }
 
-// Poll the 16-byte lines of every source whose bit is set in `pend` (source q's line sits at
-// off0 + q * qstride in `own`) until `ready` accepts each of them. All outstanding loads of a
-// lane are in flight together; only the lines that are not ready yet are loaded again.
+// Issue one round of poll loads: one 16-byte coherent load per possible source into t[q], in
+// one basic block. Sources already received (or that do not exist) read the drop offset.
+template <int NMAX>
+__device__ __forceinline__ void poll_issue(rsrc_t own, uint32_t off0, uint32_t qstride,
+                                           uint32_t pend, u32x4 (&t)[NMAX]) {
+#pragma unroll
+  for (int q = 0; q < NMAX; ++q)
+    t[q] = ld16<kCoh>(own, ((pend >> q) & 1u) ? off0 + static_cast<uint32_t>(q) * qstride : kDrop);
+}
+
+// Finish polling the sources in `pend`, whose first round of loads is already in t[]: keep each
+// line that `ready` accepts in v[] and load the others again until none is missing.
 template <int NMAX, class Ready>
-__device__ __forceinline__ bool poll_lines(const Args& a, rsrc_t own, uint32_t off0,
-                                           uint32_t qstride, uint32_t pend, u32x4 (&v)[NMAX],
-                                           Ready ready, int rank, uint64_t step) {
+__device__ __forceinline__ bool poll_rest(const Args& a, rsrc_t own, uint32_t off0,
+                                          uint32_t qstride, uint32_t pend, u32x4 (&t)[NMAX],
+                                          u32x4 (&v)[NMAX], Ready ready, int rank, uint64_t step) {
   uint32_t spins = 0;
   uint64_t t_first = 0;
   while (true) {
-    // one load per possible source, in one basic block; lines already received (or sources
-    // that do not exist) are loaded from the drop offset and not kept
-    u32x4 t[NMAX];
-#pragma unroll
-    for (int q = 0; q < NMAX; ++q) {
-      const bool want = (pend >> q) & 1u;
-      t[q] = ld16<kCoh>(own, want ? off0 + static_cast<uint32_t>(q) * qstride : kDrop);
-    }
     compiler_fence();
 #pragma unroll
     for (int q = 0; q < NMAX; ++q) {
@@ -149,9 +150,20 @@ __device__ __forceinline__ bool poll_lines(const Args& a, rsrc_t own, uint32_t o
     if ((++spins & 1023u) == 0) {
       const int lane = __builtin_ctzll(waiting);
       const uint32_t p = __shfl(pend, lane);
-      if (!poll_check(poll_env(a), t_first, rank, __builtin_ctz(p), step)) return false;
+      t_first = poll_check(poll_env(a), t_first, rank, __builtin_ctz(p), step);
+      if (t_first == 0) return false;
     }
+    poll_issue<NMAX>(own, off0, qstride, pend, t);
   }
+}
+
+template <int NMAX, class Ready>
+__device__ __forceinline__ bool poll_lines(const Args& a, rsrc_t own, uint32_t off0,
+                                           uint32_t qstride, uint32_t pend, u32x4 (&v)[NMAX],
+                                           Ready ready, int rank, uint64_t step) {
+  u32x4 t[NMAX];
+  poll_issue<NMAX>(own, off0, qstride, pend, t);
+  return poll_rest<NMAX>(a, own, off0, qstride, pend, t, v, ready, rank, step);
 }
 
 // Fold the N sources of one unit in rank order 0..N-1; the rank's own value is `x`.
@@ -186,7 +198,7 @@ __device__ __forceinline__ u32x4 sentinel_vec() {
 }
 
 // Write the sentinel back into the slots of the sources in `mask` (source q's line at
-// off0 + q * qstride), branch-free.
+// off0 + q * qstride): NMAX stores, branch-free.
 template <int NMAX>
 __device__ __forceinline__ void rearm(rsrc_t own, uint32_t off0, uint32_t qstride, uint32_t mask,
                                       u32x4 sent) {
@@ -195,15 +207,31 @@ __device__ __forceinline__ void rearm(rsrc_t own, uint32_t off0, uint32_t qstrid
     st16<kCoh>(own, ((mask >> q) & 1u) ? off0 + static_cast<uint32_t>(q) * qstride : kDrop, sent);
 }
 
+// Push one 16-byte line to the j-th peer after r, for j = 1..NMAX-1 (NMAX-1 stores, branch-free;
+// peers that do not exist and idle lanes drop their store).
+template <int NMAX>
+__device__ __forceinline__ void push_peers(const Args& a, int r, const Region& g, uint32_t off,
+                                           u32x4 line) {
+#pragma unroll
+  for (int j = 1; j < NMAX; ++j) st16<kCoh>(peer_rsrc(a, r, j, g), off, line);
+}
+
+// Ordering of a step (every step function follows it):
+//  * Before its first push a step waits until every store of the previous step has completed.
+//    The re-arm (or clearing) stores of step s must be visible before this rank's push of step
+//    s+1, because that push is the credit that lets a peer write the same buffer again in step
+//    s+2. Coherent stores are visible once they have completed.
+//  * A step returns only after its output stores have completed.
+// In the latency path (each lane owns at most one unit) a single wait after the input load
+// covers both: the load and every older store have completed when the pushes are issued. The
+// polls follow the pushes: in lockstep a poll issued before this rank's own push reaches memory
+// before the peers' data can have landed and only costs a round trip.
+
 // ------------------------------------------------------------------ one-shot, LL protocol
 //
 // Push: every 8 bytes of the rank's chunk go to every peer as one 16-byte line {payload, s}
 // (§IV "LL"). Receive: poll each peer's line until its flag equals s, then fold in rank order.
 // Nothing needs resetting: an old line carries an older sequence number.
-//
-// When the rank has at least one lane per unit (small messages, the latency regime) every lane
-// owns at most one unit: it keeps its own payload in registers from the push to the fold. With
-// more units than lanes the units are taken in passes of T lanes, the push of all passes first.
 template <int DT, int NMAX>
 __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
                                 rsrc_t out_r, int k) {
@@ -216,48 +244,48 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
   const uint32_t mine = (b * N + r) * slot;
   const rsrc_t own = region_rsrc(a, r, a.ll);
   const uint32_t peers = peer_mask(N, r);
-  auto push = [&](uint32_t i, bool act, const uint32_t* w) {
-    const u32x4 line = {w[0], w[1], elo, ehi};
-    const uint32_t off = act ? mine + i * 16u : kDrop;
-#pragma unroll
-    for (int j = 1; j < NMAX; ++j) st16<kCoh>(peer_rsrc(a, r, j, a.ll), off, line);
-  };
   auto ready = [elo, ehi](u32x4 l) { return l.z == elo && l.w == ehi; };
-  auto recv = [&](uint32_t i, bool act, const uint32_t* x) -> bool {
-    u32x4 v[NMAX];
-#pragma unroll
-    for (int q = 0; q < NMAX; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
-    if (!poll_lines<NMAX>(a, own, b * N * slot + i * 16u, slot, act ? peers : 0u, v, ready, r, s))
-      return false;
+  auto finish = [&](uint32_t i, bool act, const uint32_t* x, const u32x4 (&v)[NMAX]) {
     uint32_t o[2];
     fold_rank_order<DT, NMAX, 2>(N, r, x, v, o);
     store_unit<DT, 8>(out_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, o);
-    return true;
   };
   if (c.T >= CU) {
     const uint32_t i = c.t0 + c.lane;
     const bool act = i < CU;
-    uint32_t x[2] = {0u, 0u};
+    const uint32_t off0 = b * N * slot + i * 16u;
+    uint32_t x[2];
     load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, x);
-    if (sends) push(i, act, x);
-    return recv(i, act, x);
+    compiler_fence();
+    wait_vm<0>();
+    if (sends) push_peers<NMAX>(a, r, a.ll, act ? mine + i * 16u : kDrop, u32x4{x[0], x[1], elo, ehi});
+    u32x4 v[NMAX];
+    if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+    finish(i, act, x, v);
+    wait_all_mem();
+    return true;
   }
+  wait_all_mem();
   if (sends) {
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
       const bool act = i < CU;
       uint32_t w[2];
       load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, w);
-      push(i, act, w);
+      push_peers<NMAX>(a, r, a.ll, act ? mine + i * 16u : kDrop, u32x4{w[0], w[1], elo, ehi});
     }
   }
   for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
     const uint32_t i = i0 + c.lane;
     const bool act = i < CU;
-    uint32_t x[2] = {0u, 0u};
+    uint32_t x[2];
     load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, x);
-    if (!recv(i, act, x)) return false;
+    u32x4 v[NMAX];
+    if (!poll_lines<NMAX>(a, own, b * N * slot + i * 16u, slot, act ? peers : 0u, v, ready, r, s))
+      return false;
+    finish(i, act, x, v);
   }
+  wait_all_mem();
   return true;
 }
 
@@ -265,7 +293,8 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
 //
 // Push raw 16-byte units into every peer's slot (§IV "Sentinel"). Receive: poll until no element
 // of a peer's unit equals the sentinel, fold in rank order, then write the sentinel back so the
-// slot is armed for step s+2 (the same buffer). Passes as in the LL step.
+// slot is armed for step s+2 (the same buffer). The output store is issued before the re-arm so
+// that the step can return as soon as the output has landed.
 template <int DT, int NMAX>
 __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
                                       rsrc_t out_r, int k) {
@@ -278,49 +307,51 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
   const rsrc_t own = region_rsrc(a, r, a.p1);
   const uint32_t peers = peer_mask(N, r);
   const u32x4 sent = sentinel_vec<DT>();
-  auto push = [&](uint32_t i, bool act, const uint32_t* w) {
-    const u32x4 x = {w[0], w[1], w[2], w[3]};
-    const uint32_t off = act ? mine + i * 16u : kDrop;
-#pragma unroll
-    for (int j = 1; j < NMAX; ++j) st16<kCoh>(peer_rsrc(a, r, j, a.p1), off, x);
-  };
   auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
-  auto recv = [&](uint32_t i, bool act, const uint32_t* x) -> bool {
-    u32x4 v[NMAX];
-#pragma unroll
-    for (int q = 0; q < NMAX; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
-    const uint32_t off0 = b * N * slot + i * 16u;
-    if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+  auto finish = [&](uint32_t i, bool act, const uint32_t* x, const u32x4 (&v)[NMAX],
+                    uint32_t off0) {
     uint32_t o[4];
     fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
-    rearm<NMAX>(own, off0, slot, act ? peers : 0u, sent);
     store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, o);
-    return true;
+    rearm<NMAX>(own, off0, slot, act ? peers : 0u, sent);
   };
   if (c.T >= CU) {
     const uint32_t i = c.t0 + c.lane;
     const bool act = i < CU;
-    uint32_t x[4] = {0u, 0u, 0u, 0u};
+    const uint32_t off0 = b * N * slot + i * 16u;
+    uint32_t x[4];
     load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
-    if (sends) push(i, act, x);
-    return recv(i, act, x);
+    compiler_fence();
+    wait_vm<0>();
+    if (sends) push_peers<NMAX>(a, r, a.p1, act ? mine + i * 16u : kDrop, u32x4{x[0], x[1], x[2], x[3]});
+    u32x4 v[NMAX];
+    if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+    finish(i, act, x, v, off0);
+    compiler_fence();
+    wait_vm<NMAX>();  // the output store(s) have landed; the NMAX re-arm stores may be in flight
+    return true;
   }
+  wait_all_mem();
   if (sends) {
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
       const bool act = i < CU;
       uint32_t w[4];
       load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, w);
-      push(i, act, w);
+      push_peers<NMAX>(a, r, a.p1, act ? mine + i * 16u : kDrop, u32x4{w[0], w[1], w[2], w[3]});
     }
   }
   for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
     const uint32_t i = i0 + c.lane;
     const bool act = i < CU;
-    uint32_t x[4] = {0u, 0u, 0u, 0u};
+    const uint32_t off0 = b * N * slot + i * 16u;
+    uint32_t x[4];
     load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
-    if (!recv(i, act, x)) return false;
+    u32x4 v[NMAX];
+    if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+    finish(i, act, x, v, off0);
   }
+  wait_all_mem();
   return true;
 }
 
@@ -330,48 +361,8 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
 // partition p belongs to owner p. Chunk k of every partition moves in step k. Lane i of a wave
 // handles unit i of the chunk in every partition.
 
-// All-gather receive: poll the reduced unit i of every other owner, copy it to `out`, re-arm.
-template <int DT, int NMAX>
-__device__ __forceinline__ bool allgather_recv(const Args& a, const Ctx& c, uint64_t s,
-                                               rsrc_t out_r, int k) {
-  const int N = a.nranks, r = c.rank;
-  const uint32_t b = static_cast<uint32_t>(s & 1u);
-  const uint32_t slot = a.p2.slot, CU = a.chunk_units, P = a.part_units;
-  const rsrc_t own = region_rsrc(a, r, a.p2);
-  const uint32_t peers = peer_mask(N, r);
-  const u32x4 sent = sentinel_vec<DT>();
-  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
-  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
-    const uint32_t i = i0 + c.lane;
-    const bool act = i < CU;
-    u32x4 v[NMAX];
-#pragma unroll
-    for (int q = 0; q < NMAX; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
-    const uint32_t off0 = b * N * slot + i * 16u;
-    const uint32_t mask = act ? peers : 0u;
-    if (!poll_lines<NMAX>(a, own, off0, slot, mask, v, ready, r, s)) return false;
-    rearm<NMAX>(own, off0, slot, mask, sent);
-#pragma unroll
-    for (int p = 0; p < NMAX; ++p) {
-      const uint32_t o[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
-      store_unit<DT, 16>(out_r, ((mask >> p) & 1u) ? (p * P + k * CU + i) * 16u : kDrop,
-                         a.nbytes, o);
-    }
-  }
-  return true;
-}
-
-// Owner r pushes its reduced unit i to every peer's all-gather slot r.
-template <int NMAX>
-__device__ __forceinline__ void allgather_push(const Args& a, int r, uint32_t b, uint32_t i,
-                                               bool act, u32x4 res) {
-  const uint32_t off = act ? (b * a.nranks + r) * a.p2.slot + i * 16u : kDrop;
-#pragma unroll
-  for (int j = 1; j < NMAX; ++j) st16<kCoh>(peer_rsrc(a, r, j, a.p2), off, res);
-}
-
-// Load unit i of the chunk in the partition of the j-th peer after rank r, for j = 1..N-1
-// (zeros for peers that do not exist or an idle lane); all loads are issued before any use.
+// Load unit i of the chunk in the partition of the j-th peer after rank r into w[j], for
+// j = jfirst..NMAX-1 (zeros for peers that do not exist or an idle lane): NMAX-jfirst loads.
 template <int DT, int NMAX>
 __device__ __forceinline__ void load_partitions(const Args& a, int r, rsrc_t in_r, int k,
                                                 uint32_t i, bool act, int jfirst,
@@ -380,8 +371,10 @@ __device__ __forceinline__ void load_partitions(const Args& a, int r, rsrc_t in_
   const uint32_t CU = a.chunk_units, P = a.part_units;
 #pragma unroll
   for (int j = 0; j < NMAX; ++j) {
-    w[j][0] = w[j][1] = w[j][2] = w[j][3] = 0u;
-    if (j < jfirst) continue;
+    if (j < jfirst) {
+      w[j][0] = w[j][1] = w[j][2] = w[j][3] = 0u;
+      continue;
+    }
     int p = r + j;
     if (p >= N) p -= N;
     const bool live = act && j < N;
@@ -389,53 +382,110 @@ __device__ __forceinline__ void load_partitions(const Args& a, int r, rsrc_t in_
   }
 }
 
+// All-gather receive of unit i: the reduced unit of every other owner, already polled into v[],
+// is copied to `out` and its slot re-armed.
+template <int DT, int NMAX>
+__device__ __forceinline__ void allgather_out(const Args& a, int r, rsrc_t out_r, rsrc_t own2,
+                                              uint32_t off0, uint32_t mask, int k, uint32_t i,
+                                              const u32x4 (&v)[NMAX], u32x4 sent) {
+  const uint32_t CU = a.chunk_units, P = a.part_units;
+#pragma unroll
+  for (int p = 0; p < NMAX; ++p) {
+    const uint32_t o[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+    store_unit<DT, 16>(out_r, ((mask >> p) & 1u) ? (p * P + k * CU + i) * 16u : kDrop, a.nbytes,
+                       o);
+  }
+  rearm<NMAX>(own2, off0, a.p2.slot, mask, sent);
+}
+
 // ------------------------------------------------------------------ two-shot (RS + AG)
+//
+// Reduce-scatter: partition p's chunk goes to owner p's slot r. The owner folds its partition in
+// rank order, writes it to its own output and pushes the result to every peer's all-gather slot
+// r; every rank copies the other owners' results into its output (§III.A "Two-shot").
 template <int DT, int NMAX>
 __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r, rsrc_t out_r,
                              int k) {
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
-  const uint32_t slot = a.p1.slot, CU = a.chunk_units, P = a.part_units;
+  const uint32_t slot1 = a.p1.slot, slot2 = a.p2.slot, CU = a.chunk_units, P = a.part_units;
   const bool sends = r != a.withhold;
-  // Reduce-scatter push: partition p's chunk goes to owner p's slot r (loads first, then the
-  // stores in one block).
+  const rsrc_t own1 = region_rsrc(a, r, a.p1);
+  const rsrc_t own2 = region_rsrc(a, r, a.p2);
+  const uint32_t peers = peer_mask(N, r);
+  const u32x4 sent = sentinel_vec<DT>();
+  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+  const uint32_t mine1 = (b * N + r) * slot1, mine2 = (b * N + r) * slot2;
+  if (c.T >= CU) {
+    const uint32_t i = c.t0 + c.lane;
+    const bool act = i < CU;
+    const uint32_t mask = act ? peers : 0u;
+    const uint32_t off1 = b * N * slot1 + i * 16u, off2 = b * N * slot2 + i * 16u;
+    const uint32_t uoff = (r * P + k * CU + i) * 16u;
+    uint32_t w[NMAX][4];
+    load_partitions<DT, NMAX>(a, r, in_r, k, i, act, 0, w);  // w[0] is the own partition
+    compiler_fence();
+    wait_vm<0>();
+    if (sends) {
+      const uint32_t off = act ? mine1 + i * 16u : kDrop;
+#pragma unroll
+      for (int j = 1; j < NMAX; ++j)
+        st16<kCoh>(peer_rsrc(a, r, j, a.p1), off, u32x4{w[j][0], w[j][1], w[j][2], w[j][3]});
+    }
+    u32x4 v[NMAX];
+    if (!poll_lines<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
+    uint32_t o[4];
+    fold_rank_order<DT, NMAX, 4>(N, r, w[0], v, o);
+    if (sends) push_peers<NMAX>(a, r, a.p2, act ? mine2 + i * 16u : kDrop, u32x4{o[0], o[1], o[2], o[3]});
+    store_unit<DT, 16>(out_r, act ? uoff : kDrop, a.nbytes, o);
+    rearm<NMAX>(own1, off1, slot1, mask, sent);
+    u32x4 v2[NMAX];
+    if (!poll_lines<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
+    allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v2, sent);
+    compiler_fence();
+    wait_vm<NMAX>();  // every output store has landed; the NMAX re-arm stores may be in flight
+    return true;
+  }
+  wait_all_mem();
   if (sends) {
-    const uint32_t mine = (b * N + r) * slot;
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
       const bool act = i < CU;
       uint32_t w[NMAX][4];
       load_partitions<DT, NMAX>(a, r, in_r, k, i, act, 1, w);
-      const uint32_t off = act ? mine + i * 16u : kDrop;
+      const uint32_t off = act ? mine1 + i * 16u : kDrop;
 #pragma unroll
       for (int j = 1; j < NMAX; ++j)
         st16<kCoh>(peer_rsrc(a, r, j, a.p1), off, u32x4{w[j][0], w[j][1], w[j][2], w[j][3]});
     }
   }
-  // Owner: reduce its partition in rank order, keep the result, push it to every peer.
-  const rsrc_t own = region_rsrc(a, r, a.p1);
-  const uint32_t peers = peer_mask(N, r);
-  const u32x4 sent = sentinel_vec<DT>();
-  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
   for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
     const uint32_t i = i0 + c.lane;
     const bool act = i < CU;
-    uint32_t x[4] = {0u, 0u, 0u, 0u};
+    const uint32_t mask = act ? peers : 0u;
+    const uint32_t off1 = b * N * slot1 + i * 16u;
     const uint32_t uoff = (r * P + k * CU + i) * 16u;
+    uint32_t x[4];
     load_unit<DT, 16>(in_r, act ? uoff : kDrop, a.nbytes, x);
     u32x4 v[NMAX];
-#pragma unroll
-    for (int q = 0; q < NMAX; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
-    const uint32_t off0 = b * N * slot + i * 16u;
-    const uint32_t mask = act ? peers : 0u;
-    if (!poll_lines<NMAX>(a, own, off0, slot, mask, v, ready, r, s)) return false;
+    if (!poll_lines<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
     uint32_t o[4];
     fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
-    if (sends) allgather_push<NMAX>(a, r, b, i, act, u32x4{o[0], o[1], o[2], o[3]});
-    rearm<NMAX>(own, off0, slot, mask, sent);
+    if (sends) push_peers<NMAX>(a, r, a.p2, act ? mine2 + i * 16u : kDrop, u32x4{o[0], o[1], o[2], o[3]});
     store_unit<DT, 16>(out_r, act ? uoff : kDrop, a.nbytes, o);
+    rearm<NMAX>(own1, off1, slot1, mask, sent);
   }
-  return allgather_recv<DT, NMAX>(a, c, s, out_r, k);
+  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+    const uint32_t i = i0 + c.lane;
+    const bool act = i < CU;
+    const uint32_t mask = act ? peers : 0u;
+    const uint32_t off2 = b * N * slot2 + i * 16u;
+    u32x4 v[NMAX];
+    if (!poll_lines<NMAX>(a, own2, off2, slot2, mask, v, ready, r, s)) return false;
+    allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v, sent);
+  }
+  wait_all_mem();
+  return true;
 }
 
 // ------------------------------------------------------------------ LL128-style atomic two-shot
@@ -458,6 +508,12 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
   const uint32_t CU = a.chunk_units, P = a.part_units;
   const bool has_units = c.t0 < CU;
   const uint32_t cnt_idx = (b * kMaxCtasPerRank + c.cta) * kMaxWavesPerCta + c.wave;
+  const rsrc_t own2 = region_rsrc(a, r, a.p2);
+  const uint32_t slot2 = a.p2.slot;
+  const uint32_t peers = peer_mask(N, r);
+  const u32x4 sent = sentinel_vec<DT>();
+  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+  wait_all_mem();
   if (has_units && r != a.withhold) {
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
@@ -495,7 +551,10 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
     uint64_t t_first = 0;
     while (uni(__hip_atomic_load(my_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) !=
            static_cast<uint32_t>(N)) {
-      if ((++spins & 1023u) == 0 && !poll_check(poll_env(a), t_first, r, -1, s)) return false;
+      if ((++spins & 1023u) == 0) {
+        t_first = poll_check(poll_env(a), t_first, r, -1, s);
+        if (t_first == 0) return false;
+      }
     }
     uint8_t* acc = a.base + static_cast<uint64_t>(r) * a.stride + a.acc.off +
                    static_cast<uint64_t>(b) * a.acc.slot;
@@ -512,13 +571,24 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
         v = u32x4{static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
                   static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
       }
-      if (r != a.withhold) allgather_push<NMAX>(a, r, b, i, act, v);
+      if (r != a.withhold)
+        push_peers<NMAX>(a, r, a.p2, act ? (b * N + r) * slot2 + i * 16u : kDrop, v);
       const uint32_t o[4] = {v.x, v.y, v.z, v.w};
       store_unit<DT, 16>(out_r, act ? (r * P + k * CU + i) * 16u : kDrop, a.nbytes, o);
     }
     if (c.lane == 0) __hip_atomic_store(my_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  return allgather_recv<DT, NMAX>(a, c, s, out_r, k);
+  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+    const uint32_t i = i0 + c.lane;
+    const bool act = i < CU;
+    const uint32_t mask = act ? peers : 0u;
+    const uint32_t off2 = b * N * slot2 + i * 16u;
+    u32x4 v[NMAX];
+    if (!poll_lines<NMAX>(a, own2, off2, slot2, mask, v, ready, r, s)) return false;
+    allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v, sent);
+  }
+  wait_all_mem();
+  return true;
 }
 
 // ------------------------------------------------------------------ barrier baseline
@@ -571,10 +641,12 @@ __device__ bool xrank_barrier(const Args& a, const Ctx& c, uint64_t val, uint64_
       }
       const uint64_t waiting = __ballot(need);
       if (waiting == 0) break;
-      if ((++spins & 1023u) == 0 &&
-          !poll_check(poll_env(a), t_first, r, __builtin_ctzll(waiting), s)) {
-        if (c.lane == 0) g_bar_fail = 1;
-        break;
+      if ((++spins & 1023u) == 0) {
+        t_first = poll_check(poll_env(a), t_first, r, __builtin_ctzll(waiting), s);
+        if (t_first == 0) {
+          if (c.lane == 0) g_bar_fail = 1;
+          break;
+        }
       }
     }
   }
@@ -623,6 +695,7 @@ __device__ bool step_barrier2(const Args& a, const Ctx& c, uint64_t s, rsrc_t in
     fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
     store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, o);
   }
+  wait_all_mem();
   return true;
 }
 
@@ -669,9 +742,12 @@ __device__ bool rank_join(const Args& a, const Ctx& c, uint64_t token, bool fail
           }
         }
         if (__ballot(need != 0) == 0) break;
-        if ((++spins & 1023u) == 0 && !poll_check(poll_env(a), t_first, c.rank, c.rank, token)) {
-          if (c.lane == 0) g_join_fail = 1;
-          break;
+        if ((++spins & 1023u) == 0) {
+          t_first = poll_check(poll_env(a), t_first, c.rank, c.rank, token);
+          if (t_first == 0) {
+            if (c.lane == 0) g_join_fail = 1;
+            break;
+          }
         }
       }
     }
@@ -687,23 +763,21 @@ __global__ __launch_bounds__(256) void ar_kernel(Args a) {
   if (!decode(a, c)) return;
   const int N = a.nranks;
   const int wpb = c.wpb;
-  // Sentinel-type protocols re-arm (or clear) slots at the end of a step. Those stores use the
-  // coherent policy, so once they have completed they are visible to every rank; waiting for
-  // them before the next step's pushes keeps a peer from writing the same buffer (step s+2)
-  // before the re-arm of step s has landed.
-  constexpr bool kRearm = ALGO == ALGO_ONESHOT_SENTINEL || ALGO == ALGO_TWOSHOT ||
-                          ALGO == ALGO_LL128_ATOMIC;
   constexpr bool kBarrier = ALGO == ALGO_BARRIER2 || ALGO == ALGO_BARRIER_ONLY;
   // A rank that is a single wave needs no join: its iterations are already in program order.
   const bool join = a.iters > 1 && ALGO != ALGO_BARRIER_ONLY && (a.ctas > 1 || wpb > 1);
   if (kBarrier || join) fail_flags_init();
-  const uint64_t nsteps = static_cast<uint64_t>(a.iters) * a.chunks;
   // Buffers of iteration `it`: evenly spaced sets are addressed arithmetically; otherwise the
   // set table is read one iteration ahead so that its latency stays off the timed path.
   const bool affine = a.in_set_stride != 0 || a.out_set_stride != 0;
   const bool table = !affine && a.in_tab != nullptr;
   const void* next_in = table ? a.in_tab[c.rank] : a.in[c.rank];
   void* next_out = table ? a.out_tab[c.rank] : a.out[c.rank];
+  // timestamps of this wave: [iteration][rank][workgroup][wave]
+  const uint64_t ts_first = (static_cast<uint64_t>(c.rank) * a.ctas + c.cta) * wpb + c.wave;
+  const uint64_t ts_step = static_cast<uint64_t>(N) * a.ctas * wpb;
+  uint64_t* ts_s = a.ts_start + ts_first;
+  uint64_t* ts_e = a.ts_end + ts_first;
   int set = 0;
   for (int it = 0; it < a.iters; ++it) {
     const void* inp = next_in;
@@ -713,11 +787,9 @@ __global__ __launch_bounds__(256) void ar_kernel(Args a) {
       outp = static_cast<uint8_t*>(a.out[c.rank]) + set * a.out_set_stride;
     }
     if (++set == a.nsets) set = 0;
-    const rsrc_t in_r = make_rsrc(uniform_ptr(inp), a.nbytes);
-    const rsrc_t out_r = make_rsrc(uniform_ptr(outp), a.nbytes);
+    const rsrc_t in_r = in_rsrc(uniform_ptr(inp), a.nbytes);
+    const rsrc_t out_r = out_rsrc(const_cast<void*>(uniform_ptr(outp)), a.nbytes);
     if (a.drift > 0) drift_sleep(a, it, c.rank, c.cta);
-    const uint64_t ts_idx =
-        ((static_cast<uint64_t>(it) * N + c.rank) * a.ctas + c.cta) * wpb + c.wave;
     uint64_t t_start = 0;
     if (a.ts_start != nullptr) t_start = now_ticks();
     if (table && it + 1 < a.iters) {
@@ -747,15 +819,16 @@ __global__ __launch_bounds__(256) void ar_kernel(Args a) {
         failed = true;
         break;
       }
-      if (kRearm && step + 1 < nsteps) wait_all_mem();
     }
+    // every step returns once its output stores have completed
     if (!failed && a.ts_end != nullptr) {
-      wait_all_mem();
       const uint64_t t_end = now_ticks();
       if (c.lane == 0) {
-        a.ts_start[ts_idx] = t_start;
-        a.ts_end[ts_idx] = t_end;
+        *ts_s = t_start;
+        *ts_e = t_end;
       }
+      ts_s += ts_step;
+      ts_e += ts_step;
     }
     if (join) {
       if (!rank_join(a, c, s, failed)) return;
