@@ -203,6 +203,11 @@ def main() -> int:
     ap.add_argument("--all", action="store_true", help="also run every workload; see --report")
     ap.add_argument("--report", default=None, help="write the full per-size report here")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sizes", default=None,
+                    help="comma-separated message sizes in bytes (default: the workload's)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run the streaming copy kernel over MIB MiB (5 times) and exit; "
+                         "its known byte count scales rocprof FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -219,13 +224,31 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        A.ar_stream_copy(dst, src, nbytes)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(5):
+            A.ar_stream_copy(dst, src, nbytes)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / 5
+        print(json.dumps({"calibrate_copy_bytes_read": nbytes, "bytes_written": nbytes,
+                          "ms_per_copy": ms, "GBps_read_plus_write": 2 * nbytes / ms / 1e6}),
+              flush=True)
+        return 0
     hz = A.ar_wallclock_hz()
     sol = A.ar_sol(args.placement)
     print(f"# sol {json.dumps(sol)}", file=sys.stderr, flush=True)
 
     wid = args.workload
+    sizes = [int(x) for x in args.sizes.split(",")] if args.sizes else None
     wl, algo, iters, rows = run_workload(A, I, wid, args.algo, args.steps, args.warmup, hz,
-                                         args.placement)
+                                         args.placement, sizes)
     p50s = [r["p50_us"] for r in rows]
     value = math.exp(sum(math.log(v) for v in p50s) / len(p50s))
     total_launch_ms = sum(r["launch_ms"] for r in rows)
