@@ -136,7 +136,7 @@ struct Ty<DT_BF16> {
   static constexpr int kElem = 2;
   static constexpr uint32_t kSentinelWord = 0xFFFFFFFFu;  // two bf16 negative quiet NaNs
   __device__ static bool word_clear(uint32_t w) {
-    return (w & 0xFFFFu) != 0xFFFFu && (w >> 16) != 0xFFFFu;
+    return ((w & 0xFFFFu) != 0xFFFFu) & (w < 0xFFFF0000u);
   }
 };
 template <>
@@ -146,13 +146,10 @@ struct Ty<DT_I32> {
   __device__ static bool word_clear(uint32_t w) { return w != 0x80000000u; }
 };
 
-// binary32 -> bfloat16, round to nearest even, by the add-bias method: adding 0x7FFF plus the
-// kept low bit makes exact halfway cases carry only when the kept part is odd.
+// binary32 -> bfloat16, round to nearest even: gfx950's conversion instruction
+// (v_cvt_pk_bf16_f32, rounding per the default round-to-nearest-even mode).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Fixed rank-order fold of W 32-bit payload words. Binary32 accumulation for fp32 and bf16
@@ -214,9 +211,10 @@ struct Fold<DT_I32, W> {
   }
 };
 
+// Branch-free (bitwise and): no element of the unit equals the sentinel.
 template <int DT>
 __device__ __forceinline__ bool vec_clear(u32x4 v) {
-  return Ty<DT>::word_clear(v.x) && Ty<DT>::word_clear(v.y) && Ty<DT>::word_clear(v.z) &&
+  return Ty<DT>::word_clear(v.x) & Ty<DT>::word_clear(v.y) & Ty<DT>::word_clear(v.z) &
          Ty<DT>::word_clear(v.w);
 }
 

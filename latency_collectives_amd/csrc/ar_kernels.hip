@@ -157,6 +157,33 @@ __device__ __forceinline__ bool poll_rest(const Args& a, rsrc_t own, uint32_t of
   }
 }
 
+// Latency-path poll: every source in `mask` is loaded straight into v[q] each round, whether
+// or not it has arrived (a slot that has arrived keeps its value until this rank re-arms it),
+// until all of them pass `ready`. No per-source branches or copies: after the last load returns
+// only the readiness test and the ballot stand between the data and the fold.
+template <int NMAX, class Ready>
+__device__ __forceinline__ bool poll_all(const Args& a, rsrc_t own, uint32_t off0,
+                                         uint32_t qstride, uint32_t mask, u32x4 (&v)[NMAX],
+                                         Ready ready, int rank, uint64_t step) {
+  uint32_t spins = 0;
+  uint64_t t_first = 0;
+  while (true) {
+#pragma unroll
+    for (int q = 0; q < NMAX; ++q)
+      v[q] = ld16<kCoh>(own, ((mask >> q) & 1u) ? off0 + static_cast<uint32_t>(q) * qstride : kDrop);
+    compiler_fence();
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < NMAX; ++q) ok = ok & (((mask >> q) & 1u) == 0u || ready(v[q]));
+    const uint64_t waiting = __ballot(!ok);
+    if (waiting == 0) return true;
+    if ((++spins & 1023u) == 0) {
+      t_first = poll_check(poll_env(a), t_first, rank, -1, step);
+      if (t_first == 0) return false;
+    }
+  }
+}
+
 template <int NMAX, class Ready>
 __device__ __forceinline__ bool poll_lines(const Args& a, rsrc_t own, uint32_t off0,
                                            uint32_t qstride, uint32_t pend, u32x4 (&v)[NMAX],
@@ -244,7 +271,7 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
   const uint32_t mine = (b * N + r) * slot;
   const rsrc_t own = region_rsrc(a, r, a.ll);
   const uint32_t peers = peer_mask(N, r);
-  auto ready = [elo, ehi](u32x4 l) { return l.z == elo && l.w == ehi; };
+  auto ready = [elo, ehi](u32x4 l) { return (l.z == elo) & (l.w == ehi); };
   auto finish = [&](uint32_t i, bool act, const uint32_t* x, const u32x4 (&v)[NMAX]) {
     uint32_t o[2];
     fold_rank_order<DT, NMAX, 2>(N, r, x, v, o);
@@ -260,7 +287,7 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
     wait_vm<0>();
     if (sends) push_peers<NMAX>(a, r, a.ll, act ? mine + i * 16u : kDrop, u32x4{x[0], x[1], elo, ehi});
     u32x4 v[NMAX];
-    if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+    if (!poll_all<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
     finish(i, act, x, v);
     wait_all_mem();
     return true;
@@ -325,7 +352,7 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
     wait_vm<0>();
     if (sends) push_peers<NMAX>(a, r, a.p1, act ? mine + i * 16u : kDrop, u32x4{x[0], x[1], x[2], x[3]});
     u32x4 v[NMAX];
-    if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+    if (!poll_all<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
     finish(i, act, x, v, off0);
     compiler_fence();
     wait_vm<NMAX>();  // the output store(s) have landed; the NMAX re-arm stores may be in flight
@@ -433,14 +460,14 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
         st16<kCoh>(peer_rsrc(a, r, j, a.p1), off, u32x4{w[j][0], w[j][1], w[j][2], w[j][3]});
     }
     u32x4 v[NMAX];
-    if (!poll_lines<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
+    if (!poll_all<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
     uint32_t o[4];
     fold_rank_order<DT, NMAX, 4>(N, r, w[0], v, o);
     if (sends) push_peers<NMAX>(a, r, a.p2, act ? mine2 + i * 16u : kDrop, u32x4{o[0], o[1], o[2], o[3]});
     store_unit<DT, 16>(out_r, act ? uoff : kDrop, a.nbytes, o);
     rearm<NMAX>(own1, off1, slot1, mask, sent);
     u32x4 v2[NMAX];
-    if (!poll_lines<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
+    if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
     allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v2, sent);
     compiler_fence();
     wait_vm<NMAX>();  // every output store has landed; the NMAX re-arm stores may be in flight
