@@ -142,6 +142,58 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
     return res
 
 
+def copy_peak(A, mib: int = 1024, reps: int = 5) -> dict:
+    """Achievable HBM bandwidth on this machine: the library's streaming copy over `mib` MiB, every
+    byte read once and written once, timed with events on the stream it runs on."""
+    import torch
+
+    nbytes = mib << 20
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    A.ar_stream_copy(dst, src, nbytes)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        A.ar_stream_copy(dst, src, nbytes)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    del src, dst
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms,
+            "GBps": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources and the C header: counters taken on another version of the
+    kernels do not describe this one."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "latency_collectives_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "ar.h"))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_key: str):
+    """HBM bytes per timed launch from the committed counter summary (profiles/traffic.json),
+    or None when there is none for this workload or the kernels have changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec
+
+
 def cpu_baseline(I, wid: int, wl: dict, budget_s: float = 12.0) -> dict:
     """The oracle as it stands, single-threaded, timed on this host on the workload's sizes."""
     from oracle import oracle
@@ -203,6 +255,7 @@ def main() -> int:
     ap.add_argument("--all", action="store_true", help="also run every workload; see --report")
     ap.add_argument("--report", default=None, help="write the full per-size report here")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-barrier-baseline", action="store_true")
     ap.add_argument("--sizes", default=None,
                     help="comma-separated message sizes in bytes (default: the workload's)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -244,6 +297,8 @@ def main() -> int:
     hz = A.ar_wallclock_hz()
     sol = A.ar_sol(args.placement)
     print(f"# sol {json.dumps(sol)}", file=sys.stderr, flush=True)
+    peak = copy_peak(A)
+    print(f"# streaming copy {peak['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
 
     wid = args.workload
     sizes = [int(x) for x in args.sizes.split(",")] if args.sizes else None
@@ -251,11 +306,28 @@ def main() -> int:
                                          args.placement, sizes)
     p50s = [r["p50_us"] for r in rows]
     value = math.exp(sum(math.log(v) for v in p50s) / len(p50s))
+    barrier = None
+    if algo != "barrier2" and not args.no_barrier_baseline:
+        # the two-barrier baseline at the same sizes, same inputs, same run
+        _, _, _, brows = run_workload(A, I, wid, "barrier2", args.steps, args.warmup, hz,
+                                      args.placement, sizes)
+        bp50 = [r["p50_us"] for r in brows]
+        barrier = {
+            "algo": "barrier2",
+            "value": math.exp(sum(math.log(v) for v in bp50) / len(bp50)),
+            "unit": "us",
+            "p50_us": [round(v, 4) for v in bp50],
+            "p99_us": [round(r["p99_us"], 4) for r in brows],
+        }
     total_launch_ms = sum(r["launch_ms"] for r in rows)
     floor_us = sol["floor_ns"] * 1e-3
     # Dominant kernel: the one this workload runs; roofline over all its timed launches.
     tot_bytes = sum(r["alg_bytes_per_call"] * r["iters"] for r in rows)
     achieved = tot_bytes / (total_launch_ms * 1e-3) / 1e9
+    launches = len(rows)
+    tkey = f"workload{wid}:{algo}:{wl['dtype']}:" + ",".join(str(x) for x in wl["sizes"]) + \
+        f":steps{iters}"
+    traffic_rec = measured_traffic(tkey)
     line = {
         "metric": METRIC,
         "value": value,
@@ -297,11 +369,23 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": (traffic_rec["hbm_bytes_per_launch"] if traffic_rec else None),
+            "alg_bytes_per_launch": tot_bytes / launches,
+            "launches": launches,
+            "mean_launch_ms": total_launch_ms / launches,
             "kernel": f"ar_kernel<{algo}, {wl['dtype']}, N={wl['nranks']}>",
-            "bytes_definition": "alg_bytes() per call x iterations, over all timed launches",
+            "bytes_definition": ("alg_bytes() per AllReduce x iterations per launch; achieved = "
+                                 "bytes over all timed launches / their summed event time"),
+            "traffic_definition": ("rocprofv3 FETCH_SIZE + WRITE_SIZE per timed launch, each "
+                                   "scaled by the streaming copy's counter-to-bytes factor "
+                                   "(profiles/traffic.json); null when the kernel sources "
+                                   "differ from those the counters were taken on"),
+            "copy_peak_GBps": peak["GBps"],
+            "frac_of_copy_peak": achieved / peak["GBps"],
         },
     }
+    if barrier is not None:
+        line["barrier_baseline"] = barrier
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(I, wid, wl)
     report = {"main": line, "sol": sol}

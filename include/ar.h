@@ -214,9 +214,11 @@ int ar_pingpong(int placement, int store_policy, int load_policy, int rounds, do
 int ar_torn_lines(int placement, int nlines, int gens, uint64_t* torn, uint64_t* reads);
 
 /*
- * ar_stream_copy: copy `bytes` (a multiple of 16) from device `src` to device `dst` with a
- * streaming 16-byte-vector kernel on `stream` (measures achievable HBM bandwidth; scales rocprof
- * byte counters). Asynchronous.
+ * ar_stream_copy: copy `bytes` (a multiple of 16) from device `src` to device `dst` (both 16-byte
+ * aligned, not overlapping) on `stream`, with non-temporal 16-byte loads and stores in launches
+ * of at most 1 GiB each. It is the box's reference for achievable HBM bandwidth (every byte read
+ * once and written once) and the kernel of known size that scales rocprof's HBM byte counters.
+ * Asynchronous; AR_EINVAL for null, misaligned or ragged arguments.
  */
 int ar_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
 

@@ -18,6 +18,7 @@ enum Algo : int {
   ALGO_LL128_ATOMIC = 4,
   ALGO_BARRIER2 = 5,
   ALGO_BARRIER_ONLY = 6,
+  ALGO_TWOSHOT_BULK = 7,  // internal: the two-shot kernel for chunks wider than one pass
 };
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).

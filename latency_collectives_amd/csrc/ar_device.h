@@ -236,13 +236,13 @@ __device__ __forceinline__ rsrc_t out_rsrc(void* base, uint32_t nbytes) {
 }
 
 // Load one unit (UB bytes, 8 or 16) at byte offset `off`; zeros past the end (or for kDrop).
-template <int DT, int UB>
+template <int DT, int UB, int CP = kPlain>
 __device__ __forceinline__ void load_unit(rsrc_t r, uint32_t off, uint32_t nbytes, uint32_t* w) {
   if constexpr (UB == 16) {
-    const u32x4 v = ld16<kPlain>(r, off);
+    const u32x4 v = ld16<CP>(r, off);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else {
-    const u32x2 v = ld8<kPlain>(r, off);
+    const u32x2 v = ld8<CP>(r, off);
     w[0] = v.x; w[1] = v.y;
   }
   if constexpr (Ty<DT>::kElem == 2) {

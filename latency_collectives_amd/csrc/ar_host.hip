@@ -171,25 +171,34 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
   L.threads = h->threads ? h->threads
                          : (C <= 256 ? static_cast<int>(std::max<uint64_t>(64, round_up(C, 64)))
                                      : 256);
-  const int occ = occupancy(L.fn, L.threads);
-  if (occ <= 0) return ar_fail(AR_ENORES, "kernel cannot be resident with %d threads", L.threads);
   const int cus_per_xcd = std::max(1, h->cu_count / kXcds);
-  int max_ctas;
-  if (h->placement == AR_PLACE_XCD) {
-    L.ranks_per_xcd = static_cast<int>(ceil_div(N, kXcds));
-    max_ctas = cus_per_xcd * occ / L.ranks_per_xcd;
-  } else if (h->placement == AR_PLACE_SAME) {
-    max_ctas = cus_per_xcd * occ / N;
-  } else {
-    max_ctas = h->cu_count * occ / N;
-  }
-  max_ctas = std::min(max_ctas, ar::kMaxCtasPerRank);
-  if (max_ctas < 1) return ar_fail(AR_ENORES, "%d ranks cannot be co-resident", N);
-  int ctas = h->ctas;
-  if (ctas == 0) {
+  L.ranks_per_xcd = h->placement == AR_PLACE_XCD ? static_cast<int>(ceil_div(N, kXcds)) : 1;
+  // Workgroups per rank that can all be resident at once with kernel `fn`.
+  auto co_resident = [&](ar_kernel_fn fn) {
+    const int occ = occupancy(fn, L.threads);
+    int m;
+    if (h->placement == AR_PLACE_XCD)
+      m = cus_per_xcd * occ / L.ranks_per_xcd;
+    else if (h->placement == AR_PLACE_SAME)
+      m = cus_per_xcd * occ / N;
+    else
+      m = h->cu_count * occ / N;
+    return std::min(m, ar::kMaxCtasPerRank);
+  };
+  auto pick_ctas = [&](int max_ctas) {
+    if (h->ctas) return h->ctas;
     const uint64_t want = std::max<uint64_t>(1, ceil_div(C, static_cast<uint64_t>(L.threads)));
-    ctas = static_cast<int>(std::min<uint64_t>(want, static_cast<uint64_t>(max_ctas)));
+    return static_cast<int>(std::min<uint64_t>(want, static_cast<uint64_t>(max_ctas)));
+  };
+  int max_ctas = co_resident(L.fn);
+  int ctas = pick_ctas(max_ctas);
+  if (algo == AR_TWOSHOT && static_cast<uint64_t>(ctas) * L.threads < C) {
+    // the chunk does not fit one pass: the bandwidth-regime kernel streams it
+    L.fn = ar_select_kernel(ar::ALGO_TWOSHOT_BULK, h->dtype, nmax);
+    max_ctas = co_resident(L.fn);
+    ctas = pick_ctas(max_ctas);
   }
+  if (max_ctas < 1) return ar_fail(AR_ENORES, "%d ranks cannot be co-resident", N);
   if (ctas > max_ctas)
     return ar_fail(AR_ENORES, "%d workgroups per rank exceed the co-resident limit %d", ctas,
                    max_ctas);

@@ -390,7 +390,7 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
 
 // Load unit i of the chunk in the partition of the j-th peer after rank r into w[j], for
 // j = jfirst..NMAX-1 (zeros for peers that do not exist or an idle lane): NMAX-jfirst loads.
-template <int DT, int NMAX>
+template <int DT, int NMAX, int CP = kPlain>
 __device__ __forceinline__ void load_partitions(const Args& a, int r, rsrc_t in_r, int k,
                                                 uint32_t i, bool act, int jfirst,
                                                 uint32_t (&w)[NMAX][4]) {
@@ -405,13 +405,13 @@ __device__ __forceinline__ void load_partitions(const Args& a, int r, rsrc_t in_
     int p = r + j;
     if (p >= N) p -= N;
     const bool live = act && j < N;
-    load_unit<DT, 16>(in_r, live ? (p * P + k * CU + i) * 16u : kDrop, a.nbytes, w[j]);
+    load_unit<DT, 16, CP>(in_r, live ? (p * P + k * CU + i) * 16u : kDrop, a.nbytes, w[j]);
   }
 }
 
 // All-gather receive of unit i: the reduced unit of every other owner, already polled into v[],
 // is copied to `out` and its slot re-armed.
-template <int DT, int NMAX>
+template <int DT, int NMAX, int CP = kPlain>
 __device__ __forceinline__ void allgather_out(const Args& a, int r, rsrc_t out_r, rsrc_t own2,
                                               uint32_t off0, uint32_t mask, int k, uint32_t i,
                                               const u32x4 (&v)[NMAX], u32x4 sent) {
@@ -419,8 +419,8 @@ __device__ __forceinline__ void allgather_out(const Args& a, int r, rsrc_t out_r
 #pragma unroll
   for (int p = 0; p < NMAX; ++p) {
     const uint32_t o[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
-    store_unit<DT, 16>(out_r, ((mask >> p) & 1u) ? (p * P + k * CU + i) * 16u : kDrop, a.nbytes,
-                       o);
+    store_unit<DT, 16, CP>(out_r, ((mask >> p) & 1u) ? (p * P + k * CU + i) * 16u : kDrop,
+                           a.nbytes, o);
   }
   rearm<NMAX>(own2, off0, a.p2.slot, mask, sent);
 }
@@ -443,7 +443,9 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
   const u32x4 sent = sentinel_vec<DT>();
   auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
   const uint32_t mine1 = (b * N + r) * slot1, mine2 = (b * N + r) * slot2;
-  if (c.T >= CU) {
+  // one pass: the plan gives this rank at least one lane per unit of the chunk (wider chunks
+  // run step_twoshot_bulk)
+  {
     const uint32_t i = c.t0 + c.lane;
     const bool act = i < CU;
     const uint32_t mask = act ? peers : 0u;
@@ -473,13 +475,34 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
     wait_vm<NMAX>();  // every output store has landed; the NMAX re-arm stores may be in flight
     return true;
   }
+}
+
+// Bulk two-shot, for chunks wider than one pass of the rank's workgroups (the bandwidth
+// regime). Same protocol as above in three streaming phases per chunk: push the peers'
+// partitions, then fold the own partition and push the result, then receive the other owners'
+// results. Inputs are read once and outputs written once, so both carry the non-temporal hint;
+// the cross-rank accesses keep the plain agent-coherent policy (adding the hint to them measured
+// slower). It runs in its own kernel, built for higher occupancy.
+template <int DT, int NMAX>
+__device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
+                                  rsrc_t out_r, int k) {
+  const int N = a.nranks, r = c.rank;
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t slot1 = a.p1.slot, slot2 = a.p2.slot, CU = a.chunk_units, P = a.part_units;
+  const bool sends = r != a.withhold;
+  const rsrc_t own1 = region_rsrc(a, r, a.p1);
+  const rsrc_t own2 = region_rsrc(a, r, a.p2);
+  const uint32_t peers = peer_mask(N, r);
+  const u32x4 sent = sentinel_vec<DT>();
+  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+  const uint32_t mine1 = (b * N + r) * slot1, mine2 = (b * N + r) * slot2;
   wait_all_mem();
   if (sends) {
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
       const bool act = i < CU;
       uint32_t w[NMAX][4];
-      load_partitions<DT, NMAX>(a, r, in_r, k, i, act, 1, w);
+      load_partitions<DT, NMAX, kNt>(a, r, in_r, k, i, act, 1, w);
       const uint32_t off = act ? mine1 + i * 16u : kDrop;
 #pragma unroll
       for (int j = 1; j < NMAX; ++j)
@@ -493,13 +516,13 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
     const uint32_t off1 = b * N * slot1 + i * 16u;
     const uint32_t uoff = (r * P + k * CU + i) * 16u;
     uint32_t x[4];
-    load_unit<DT, 16>(in_r, act ? uoff : kDrop, a.nbytes, x);
+    load_unit<DT, 16, kNt>(in_r, act ? uoff : kDrop, a.nbytes, x);
     u32x4 v[NMAX];
-    if (!poll_lines<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
+    if (!poll_all<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
     uint32_t o[4];
     fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
     if (sends) push_peers<NMAX>(a, r, a.p2, act ? mine2 + i * 16u : kDrop, u32x4{o[0], o[1], o[2], o[3]});
-    store_unit<DT, 16>(out_r, act ? uoff : kDrop, a.nbytes, o);
+    store_unit<DT, 16, kNt>(out_r, act ? uoff : kDrop, a.nbytes, o);
     rearm<NMAX>(own1, off1, slot1, mask, sent);
   }
   for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
@@ -508,8 +531,8 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
     const uint32_t mask = act ? peers : 0u;
     const uint32_t off2 = b * N * slot2 + i * 16u;
     u32x4 v[NMAX];
-    if (!poll_lines<NMAX>(a, own2, off2, slot2, mask, v, ready, r, s)) return false;
-    allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v, sent);
+    if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v, ready, r, s)) return false;
+    allgather_out<DT, NMAX, kNt>(a, r, out_r, own2, off2, mask, k, i, v, sent);
   }
   wait_all_mem();
   return true;
@@ -785,7 +808,7 @@ __device__ bool rank_join(const Args& a, const Ctx& c, uint64_t token, bool fail
 }
 
 template <int ALGO, int DT, int NMAX>
-__global__ __launch_bounds__(256) void ar_kernel(Args a) {
+__device__ __forceinline__ void ar_body(const Args& a) {
   Ctx c;
   if (!decode(a, c)) return;
   const int N = a.nranks;
@@ -835,6 +858,8 @@ __global__ __launch_bounds__(256) void ar_kernel(Args a) {
         ok = step_oneshot_sentinel<DT, NMAX>(a, c, s, in_r, out_r, k);
       } else if constexpr (ALGO == ALGO_TWOSHOT) {
         ok = step_twoshot<DT, NMAX>(a, c, s, in_r, out_r, k);
+      } else if constexpr (ALGO == ALGO_TWOSHOT_BULK) {
+        ok = step_twoshot_bulk<DT, NMAX>(a, c, s, in_r, out_r, k);
       } else if constexpr (ALGO == ALGO_LL128_ATOMIC) {
         ok = step_ll128<DT, NMAX>(a, c, s, in_r, out_r, k);
       } else if constexpr (ALGO == ALGO_BARRIER2) {
@@ -865,6 +890,20 @@ __global__ __launch_bounds__(256) void ar_kernel(Args a) {
   }
 }
 
+template <int ALGO, int DT, int NMAX>
+__global__ __launch_bounds__(256) void ar_kernel(Args a) {
+  ar_body<ALGO, DT, NMAX>(a);
+}
+
+// The bandwidth-regime two-shot in a kernel of its own, with a register budget (at most 128
+// VGPRs) that lets 4 waves share every SIMD: twice the streaming loads in flight per compute
+// unit of the latency kernel, which needs 178 VGPRs. At 8 waves per SIMD it would spill.
+template <int DT, int NMAX>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void ar_kernel_bulk(Args a) {
+  ar_body<ALGO_TWOSHOT_BULK, DT, NMAX>(a);
+}
+
 // Fill `bytes` of every rank's block at `off` with the 32-bit word `word` (scratch set-up).
 __global__ void fill_region(uint8_t* base, uint64_t stride, int nranks, uint64_t off,
                             uint32_t bytes, uint32_t word) {
@@ -886,11 +925,20 @@ typedef void (*ar_kernel_fn)(ar::Args);
 
 template <int ALGO, int DT>
 static ar_kernel_fn pick_n(int nmax) {
-  switch (nmax) {
-    case 2: return ar::ar_kernel<ALGO, DT, 2>;
-    case 4: return ar::ar_kernel<ALGO, DT, 4>;
-    case 8: return ar::ar_kernel<ALGO, DT, 8>;
-    default: return ar::ar_kernel<ALGO, DT, 16>;
+  if constexpr (ALGO == ar::ALGO_TWOSHOT_BULK) {
+    switch (nmax) {
+      case 2: return ar::ar_kernel_bulk<DT, 2>;
+      case 4: return ar::ar_kernel_bulk<DT, 4>;
+      case 8: return ar::ar_kernel_bulk<DT, 8>;
+      default: return ar::ar_kernel_bulk<DT, 16>;
+    }
+  } else {
+    switch (nmax) {
+      case 2: return ar::ar_kernel<ALGO, DT, 2>;
+      case 4: return ar::ar_kernel<ALGO, DT, 4>;
+      case 8: return ar::ar_kernel<ALGO, DT, 8>;
+      default: return ar::ar_kernel<ALGO, DT, 16>;
+    }
   }
 }
 
@@ -909,6 +957,7 @@ ar_kernel_fn ar_select_kernel(int algo, int dt, int nmax) {
     case ar::ALGO_ONESHOT_LL: return pick_dt<ar::ALGO_ONESHOT_LL>(dt, nmax);
     case ar::ALGO_ONESHOT_SENTINEL: return pick_dt<ar::ALGO_ONESHOT_SENTINEL>(dt, nmax);
     case ar::ALGO_TWOSHOT: return pick_dt<ar::ALGO_TWOSHOT>(dt, nmax);
+    case ar::ALGO_TWOSHOT_BULK: return pick_dt<ar::ALGO_TWOSHOT_BULK>(dt, nmax);
     case ar::ALGO_LL128_ATOMIC:
       if (dt == ar::DT_F32) return pick_n<ar::ALGO_LL128_ATOMIC, ar::DT_F32>(nmax);
       if (dt == ar::DT_I32) return pick_n<ar::ALGO_LL128_ATOMIC, ar::DT_I32>(nmax);

@@ -133,19 +133,20 @@ __global__ void sol_torn(u32x4* lines, int nlines, int gens, int w_blk, int r_bl
 }
 
 // --------------------------------------------------------------- streaming copy
-// Grid-stride copy of `bytes` (a multiple of 16) with 16-byte loads and stores; used to measure
-// the achievable HBM bandwidth and to scale rocprof byte counters.
-__global__ void stream_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n16) {
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
-  uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    dst[i] = a;
-    dst[i + stride] = b;
-    dst[i + 2 * stride] = c;
-    dst[i + 3 * stride] = d;
+// Copy `bytes` (a multiple of 16, below 2^31) with non-temporal 16-byte loads and stores, two
+// units per lane per round: the reference point for HBM bandwidth on the box (a plain copy
+// reads and writes every byte once) and the kernel of known size that scales the HBM byte
+// counters.
+__global__ __launch_bounds__(512) void stream_copy(const void* src, void* dst, uint32_t bytes) {
+  const rsrc_t s = make_rsrc(src, bytes), d = make_rsrc(dst, bytes);
+  const uint32_t stride = gridDim.x * blockDim.x * 16u;
+  uint32_t o = (blockIdx.x * blockDim.x + threadIdx.x) * 16u;
+  for (; o + stride < bytes; o += 2u * stride) {
+    const u32x4 a = ld16<kNt>(s, o), b = ld16<kNt>(s, o + stride);
+    st16<kNt>(d, o, a);
+    st16<kNt>(d, o + stride, b);
   }
-  for (; i < n16; i += stride) dst[i] = src[i];
+  if (o < bytes) st16<kNt>(d, o, ld16<kNt>(s, o));
 }
 
 }  // namespace ar
@@ -339,14 +340,17 @@ int ar_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
   if (bytes % 16 != 0) return ar_fail(AR_EINVAL, "bytes must be a multiple of 16");
   if (((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15u) != 0)
     return ar_fail(AR_EINVAL, "buffers must be 16-byte aligned");
-  const uint64_t n16 = bytes / 16;
-  if (n16 == 0) return AR_OK;
-  uint64_t blocks = (n16 + 255) / 256;
-  blocks = std::min<uint64_t>(blocks, 8192);
-  hipLaunchKernelGGL(ar::stream_copy, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), static_cast<const ar::u32x4*>(src),
-                     static_cast<ar::u32x4*>(dst), n16);
-  AR_HIP(hipGetLastError());
+  // pieces of at most 1 GiB, each within one buffer descriptor's 32-bit range
+  constexpr size_t kPiece = size_t(1) << 30;
+  constexpr uint64_t kThreads = 512, kMaxBlocks = 16384;
+  for (size_t off = 0; off < bytes; off += kPiece) {
+    const uint32_t n = static_cast<uint32_t>(std::min(kPiece, bytes - off));
+    const uint64_t blocks = std::min<uint64_t>(kMaxBlocks, (n / 16 + 2 * kThreads - 1) / (2 * kThreads));
+    hipLaunchKernelGGL(ar::stream_copy, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream),
+                       static_cast<const uint8_t*>(src) + off, static_cast<uint8_t*>(dst) + off, n);
+    AR_HIP(hipGetLastError());
+  }
   return AR_OK;
 }
 

@@ -1,0 +1,207 @@
+"""GPU parity of the bandwidth-regime two-shot kernel and of every workload at its full size.
+
+The bulk two-shot runs whenever a chunk is wider than one pass of the rank's workgroups. The
+first tests force it at small sizes by capping the workgroups per rank, so that ragged tails,
+multi-chunk calls, re-arming and the timeout path are all covered where the oracle is quick.
+The full-size tests run the workloads' own shapes in the launch configuration the benchmark
+uses: the messages are compared element by element with the oracle (which is a plain fold and
+finishes these sizes in seconds), and all ranks' outputs with each other.
+"""
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import (assert_matches, draw, from_device, handle, run_allreduce,
+                            to_device)
+
+pytestmark = pytest.mark.gpu
+
+BULK_COUNTS = [4099, 70001, 250007]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("n", [2, 3, 4, 8, 16])
+def test_bulk_twoshot_forced(n, dtype):
+    """One or three workgroups per rank: every chunk needs several passes."""
+    eb = {"f32": 4, "bf16": 2, "i32": 4}[dtype]
+    for ctas in (1, 3):
+        with handle(n, max(BULK_COUNTS) * eb, dtype, ctas=ctas) as h:
+            for i, count in enumerate(BULK_COUNTS):
+                _say(f"case bulk n={n} dtype={dtype} ctas={ctas} count={count}")
+                x = draw(dtype, n, count, seed=500 + 10 * n + i)
+                got = run_allreduce(h, x, "twoshot")
+                assert_matches(got, x, "twoshot", dtype)
+
+
+def test_bulk_twoshot_chunked_and_rearmed():
+    """Scratch capped at 64 KiB: many chunks per call, alternating buffers; afterwards every
+    sentinel slot holds the sentinel again."""
+    from latency_collectives_amd import _ar as A
+
+    n, count = 4, 300007
+    env = {"AR_SCRATCH_TWOSHOT": 64 << 10}
+    for dtype in ("f32", "bf16", "i32"):
+        eb = 2 if dtype == "bf16" else 4
+        with handle(n, count * eb, dtype, env=env, ctas=1) as h:
+            for it in range(2):
+                _say(f"case bulk chunked dtype={dtype} it={it}")
+                x = draw(dtype, n, count, seed=77 + it)
+                got = run_allreduce(h, x, "twoshot")
+                assert_matches(got, x, "twoshot", dtype)
+            sentinel = 0x80000000 if dtype == "i32" else 0xFFFFFFFF
+            for r in range(n):
+                for reg in (A.REGION_P1, A.REGION_P2):
+                    w = A.ar_read_region(h, r, reg).view(np.uint32)
+                    assert np.all(w == sentinel), f"rank {r} region {reg} not re-armed"
+
+
+def test_bulk_twoshot_withheld_rank_times_out():
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    n, count = 4, 70001
+    with handle(n, count * 4, "f32", ctas=1, timeout_us=20000, withhold_rank=2) as h:
+        x = draw("f32", n, count, seed=5)
+        ins = to_device(x)
+        outs = [torch.empty_like(t) for t in ins]
+        A.ar_allreduce(h, ins, outs, count, A.AR_TWOSHOT)
+        with pytest.raises(A.ArError) as e:
+            A.ar_check(h)
+        assert e.value.code == A.AR_ETIMEOUT
+
+
+def test_bulk_twoshot_persistent_loop():
+    """Several bulk AllReduces in one persistent launch (credits across iterations)."""
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    n, dtype, count, iters = 8, "bf16", 100001, 6
+    with handle(n, count * 2, dtype, ctas=2) as h:
+        xs = [draw(dtype, n, count, seed=900 + k) for k in range(iters)]
+        ins, outs = [], []
+        for x in xs:
+            d = to_device(x)
+            ins += d
+            outs += [torch.empty_like(t) for t in d]
+        A.ar_bench(h, ins, outs, iters, count, A.AR_TWOSHOT, iters)
+        for k in range(iters):
+            got = from_device(outs[k * n:(k + 1) * n], np.uint16)
+            assert_matches(got, xs[k], "twoshot", dtype)
+
+
+# ------------------------------------------------------------------ full workload sizes
+
+
+def _bench_sets(h, xs, algo, dtype):
+    """Run the sets xs[k] ([N, count] each) through one persistent launch, as the benchmark
+    does (evenly spaced sets of one buffer per rank), and check every set."""
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    n, count = xs[0].shape
+    view = np.int16 if dtype == "bf16" else xs[0].dtype
+    big = [torch.from_numpy(np.ascontiguousarray(np.stack([x[r] for x in xs]).view(view))).cuda()
+           for r in range(n)]
+    obig = [torch.empty_like(b) for b in big]
+    ins = [big[r][k] for k in range(len(xs)) for r in range(n)]
+    outs = [obig[r][k] for k in range(len(xs)) for r in range(n)]
+    A.ar_bench(h, ins, outs, len(xs), count, A.ALGOS[algo], 2 * len(xs))
+    for k, x in enumerate(xs):
+        got = np.stack([obig[r][k].cpu().numpy().view(x.dtype) for r in range(n)])
+        assert_matches(got, x, algo, dtype)
+
+
+def test_full_size_c2_oneshot_sentinel():
+    """4 ranks, bf16 normal(0,1), 1 KiB .. 256 KiB per rank."""
+    from latency_collectives_amd import inputs as I
+
+    wl = I.WORKLOADS[2]
+    with handle(4, max(wl["sizes"]), "bf16") as h:
+        for si, size in enumerate(wl["sizes"]):
+            _say(f"case c2 size={size}")
+            xs = [I.rank_inputs("normal", "bf16", 4, size // 2, 2, si, k) for k in range(3)]
+            _bench_sets(h, xs, "oneshot_sentinel", "bf16")
+
+
+def test_full_size_c3_twoshot():
+    """8 ranks, bf16 normal(0,0.5), [tokens, 8192] for tokens 1..64 (16 KiB .. 1 MiB)."""
+    from latency_collectives_amd import inputs as I
+
+    wl = I.WORKLOADS[3]
+    with handle(8, max(wl["sizes"]), "bf16") as h:
+        for si, size in enumerate(wl["sizes"]):
+            _say(f"case c3 size={size}")
+            xs = [I.rank_inputs("normal", "bf16", 8, size // 2, 3, si, k, 0.5) for k in range(2)]
+            for algo in ("twoshot", "oneshot_sentinel"):
+                _bench_sets(h, xs, algo, "bf16")
+
+
+def test_full_size_c4_sixteen_ranks():
+    """16 ranks, fp32 uniform[-1,1], 4 KiB .. 4 MiB: LL128-style atomic, one-shot LL, barrier
+    baseline."""
+    from latency_collectives_amd import inputs as I
+
+    wl = I.WORKLOADS[4]
+    with handle(16, max(wl["sizes"]), "f32") as h:
+        for si, size in enumerate(wl["sizes"]):
+            x = I.rank_inputs("uniform", "f32", 16, size // 4, 4, si, 0)
+            for algo in ("ll128_atomic", "oneshot_ll", "barrier2"):
+                _say(f"case c4 size={size} algo={algo}")
+                got = run_allreduce(h, x, algo)
+                assert_matches(got, x, algo, "f32")
+
+
+def _device_check(outs, want: np.ndarray):
+    """All ranks' outputs equal rank 0's (on the device); rank 0's equals `want` bit for bit."""
+    import torch
+
+    for r in range(1, len(outs)):
+        assert torch.equal(outs[r], outs[0]), f"rank {r} output differs from rank 0"
+    got = outs[0].cpu().numpy()
+    bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, f"mismatch at {bad[:8]}: got {got[bad[:8]]} want {want[bad[:8]]}"
+
+
+@pytest.mark.parametrize("size_mib", [16, 256])
+@pytest.mark.parametrize("dtype", ["i32", "f32"])
+def test_full_size_c5_twoshot(dtype, size_mib):
+    """8 ranks, 16 MiB and 256 MiB per rank, two-shot in the benchmark's launch shape: int32
+    uniform in [-2^20, 2^20] and fp32 uniform[-1,1], every element against the oracle."""
+    from latency_collectives_amd import _ar as A
+    from latency_collectives_amd import inputs as I
+    from oracle import oracle
+    import torch
+
+    n = 8
+    count = (size_mib << 20) // 4
+    dist = "int20" if dtype == "i32" else "uniform"
+    _say(f"case c5 dtype={dtype} size={size_mib} MiB")
+    with handle(n, size_mib << 20, dtype) as h:
+        ins = I.device_draw(dist, dtype, n, count, 5, size_mib, 0)
+        outs = [torch.empty_like(t) for t in ins]
+        A.ar_allreduce(h, ins, outs, count, A.AR_TWOSHOT)
+        A.ar_check(h)
+        host = [t.cpu().numpy() for t in ins]
+        want = oracle.allreduce(host)[0]
+        del host
+        _device_check(outs, want)
+
+
+def test_full_size_c5_rank_constant():
+    """Rank r filled with r at 64 MiB per rank: every element of every output is N(N-1)/2."""
+    from latency_collectives_amd import _ar as A
+    from latency_collectives_amd import inputs as I
+    import torch
+
+    n, count = 8, (64 << 20) // 4
+    with handle(n, 64 << 20, "i32") as h:
+        ins = I.device_draw("rankconst", "i32", n, count, 5, 0, 0)
+        outs = [torch.empty_like(t) for t in ins]
+        A.ar_allreduce(h, ins, outs, count, A.AR_TWOSHOT)
+        A.ar_check(h)
+        for r in range(n):
+            assert bool(torch.all(outs[r] == n * (n - 1) // 2)), f"rank {r}"
