@@ -19,6 +19,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <utility>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -52,20 +53,23 @@ int elem_bytes(int dt) { return dt == AR_BFLOAT16 ? 2 : 4; }
 
 uint32_t sentinel_word(int dt) { return dt == AR_INT32 ? 0x80000000u : 0xFFFFFFFFu; }
 
+// Resident workgroups per compute unit for (kernel, block size), cached. The key keeps both
+// parts: the host handles of different kernels are only a few bytes apart, so any mixing of the
+// two into one number could give a kernel the occupancy of another, and a grid planned on a
+// too-high occupancy cannot be co-resident.
 std::mutex g_occ_mu;
-std::map<const void*, int> g_occ;
+std::map<std::pair<const void*, int>, int> g_occ;
 
 int occupancy(ar_kernel_fn fn, int threads) {
   std::lock_guard<std::mutex> lk(g_occ_mu);
-  const void* key = reinterpret_cast<const void*>(fn);
-  auto key2 = reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(key) ^ threads);
-  auto it = g_occ.find(key2);
+  const auto key = std::make_pair(reinterpret_cast<const void*>(fn), threads);
+  auto it = g_occ.find(key);
   if (it != g_occ.end()) return it->second;
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn),
                                                    threads, 0) != hipSuccess)
     nb = 0;
-  g_occ[key2] = nb;
+  g_occ[key] = nb;
   return nb;
 }
 
