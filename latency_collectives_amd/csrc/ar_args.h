@@ -23,7 +23,8 @@ enum Algo : int {
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).
 enum Placement : int {
-  PLACE_XCD = 0,     // rank r on XCD r % 8 (workgroups are dispatched round-robin over XCDs)
+  PLACE_XCD = 0,     // rank r's first workgroup on XCD r % 8 (workgroups are dispatched
+                     // round-robin over XCDs); a rank spans 8 / N XCDs when N divides 8
   PLACE_SAME = 1,    // every rank on XCD 0
   PLACE_LINEAR = 2,  // rank = workgroup / ctas (each rank spread over all XCDs)
 };
@@ -77,7 +78,8 @@ struct Args {
   uint32_t part_units;  // two-shot partition size in units (a multiple of chunk_units)
   int nranks;
   int ctas;             // workgroups per rank
-  int ranks_per_xcd;
+  int ranks_per_xcd;    // rank placement on XCDs (PLACE_XCD): ranks sharing one XCD when N > 8
+  int xcds_per_rank;    //   or XCDs one rank spans when N divides 8
   int placement;
   int iters;
   int chunks;

@@ -128,6 +128,7 @@ struct Launch {
   int threads = 64;
   int ctas = 1;
   int ranks_per_xcd = 1;
+  int xcds_per_rank = 1;
   unsigned grid = 1;
 };
 
@@ -177,12 +178,15 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
                                      : 256);
   const int cus_per_xcd = std::max(1, h->cu_count / kXcds);
   L.ranks_per_xcd = h->placement == AR_PLACE_XCD ? static_cast<int>(ceil_div(N, kXcds)) : 1;
+  // With N dividing 8 every rank gets 8 / N XCDs (its first workgroup stays on XCD r); the other
+  // counts leave 8 - N XCDs idle rather than split a rank unevenly.
+  L.xcds_per_rank = (h->placement == AR_PLACE_XCD && N < kXcds && kXcds % N == 0) ? kXcds / N : 1;
   // Workgroups per rank that can all be resident at once with kernel `fn`.
   auto co_resident = [&](ar_kernel_fn fn) {
     const int occ = occupancy(fn, L.threads);
     int m;
     if (h->placement == AR_PLACE_XCD)
-      m = cus_per_xcd * occ / L.ranks_per_xcd;
+      m = cus_per_xcd * occ * L.xcds_per_rank / L.ranks_per_xcd;
     else if (h->placement == AR_PLACE_SAME)
       m = cus_per_xcd * occ / N;
     else
@@ -208,7 +212,8 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
                    max_ctas);
   L.ctas = ctas;
   if (h->placement == AR_PLACE_XCD)
-    L.grid = static_cast<unsigned>(kXcds * L.ranks_per_xcd * ctas);
+    L.grid = static_cast<unsigned>(kXcds * L.ranks_per_xcd *
+                                   ceil_div(static_cast<uint64_t>(ctas), L.xcds_per_rank));
   else if (h->placement == AR_PLACE_SAME)
     L.grid = static_cast<unsigned>(kXcds * N * ctas);
   else
@@ -239,6 +244,7 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
   a.nranks = h->nranks;
   a.ctas = L.ctas;
   a.ranks_per_xcd = L.ranks_per_xcd;
+  a.xcds_per_rank = L.xcds_per_rank;
   a.placement = h->placement;
   a.iters = 1;
   a.chunks = L.chunks;

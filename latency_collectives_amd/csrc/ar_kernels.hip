@@ -33,9 +33,16 @@ __device__ __forceinline__ bool decode(const Args& a, Ctx& c) {
   const int w = blockIdx.x;
   int rank, cta;
   if (a.placement == PLACE_XCD) {
-    const int xcd = w & 7, j = w >> 3, R = a.ranks_per_xcd;
-    rank = xcd + 8 * (j % R);
-    cta = j / R;
+    // Dispatch round j puts workgroup 8j + x on XCD x. With N > 8, R ranks share every XCD; with
+    // N dividing 8, XCDs x, x + N, ... all belong to rank x and its workgroups alternate over them.
+    const int xcd = w & 7, j = w >> 3, R = a.ranks_per_xcd, X = a.xcds_per_rank;
+    if (X > 1) {
+      rank = xcd % a.nranks;
+      cta = j * X + xcd / a.nranks;
+    } else {
+      rank = xcd + 8 * (j % R);
+      cta = j / R;
+    }
   } else if (a.placement == PLACE_SAME) {
     if ((w & 7) != 0) return false;
     const int j = w >> 3;
