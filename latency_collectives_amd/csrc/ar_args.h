@@ -18,7 +18,10 @@ enum Algo : int {
   ALGO_LL128_ATOMIC = 4,
   ALGO_BARRIER2 = 5,
   ALGO_BARRIER_ONLY = 6,
-  ALGO_TWOSHOT_BULK = 7,  // internal: the two-shot kernel for chunks wider than one pass
+  // internal: kernels for chunks wider than one pass of the rank's workgroups
+  ALGO_TWOSHOT_BULK = 7,
+  ALGO_ONESHOT_LL_MULTI = 8,
+  ALGO_ONESHOT_SENTINEL_MULTI = 9,
 };
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).

@@ -113,6 +113,17 @@ __device__ __forceinline__ uint64_t now_ticks() {
   return t;
 }
 
+// Start stamp of one AllReduce. Every step takes it itself, after its set-up and right before
+// its first input load, and only the first step of a call keeps it (`k` is the chunk index).
+__device__ __forceinline__ void stamp_start(uint64_t& t0, int k) {
+  const uint64_t t = now_ticks();
+  t0 = k == 0 ? t : t0;
+}
+
+// Make the compiler compute `x` before this point (it cannot sink the work behind a later
+// stamp).
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
 __device__ __forceinline__ uint32_t xcc_id() {
   uint32_t v;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));

@@ -200,11 +200,18 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
   };
   int max_ctas = co_resident(L.fn);
   int ctas = pick_ctas(max_ctas);
-  if (algo == AR_TWOSHOT && static_cast<uint64_t>(ctas) * L.threads < C) {
-    // the chunk does not fit one pass: the bandwidth-regime kernel streams it
-    L.fn = ar_select_kernel(ar::ALGO_TWOSHOT_BULK, h->dtype, nmax);
-    max_ctas = co_resident(L.fn);
-    ctas = pick_ctas(max_ctas);
+  if (static_cast<uint64_t>(ctas) * L.threads < C) {
+    // The chunk does not fit one pass of the rank's lanes: the kernels built for one pass (the
+    // latency path) hand it to their multi-pass counterparts.
+    const int multi = algo == AR_TWOSHOT             ? ar::ALGO_TWOSHOT_BULK
+                      : algo == AR_ONESHOT_LL        ? ar::ALGO_ONESHOT_LL_MULTI
+                      : algo == AR_ONESHOT_SENTINEL  ? ar::ALGO_ONESHOT_SENTINEL_MULTI
+                                                     : 0;
+    if (multi != 0) {
+      L.fn = ar_select_kernel(multi, h->dtype, nmax);
+      max_ctas = co_resident(L.fn);
+      ctas = pick_ctas(max_ctas);
+    }
   }
   if (max_ctas < 1) return ar_fail(AR_ENORES, "%d ranks cannot be co-resident", N);
   if (ctas > max_ctas)

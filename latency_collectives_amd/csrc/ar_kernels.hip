@@ -266,9 +266,9 @@ __device__ __forceinline__ void push_peers(const Args& a, int r, const Region& g
 // Push: every 8 bytes of the rank's chunk go to every peer as one 16-byte line {payload, s}
 // (§IV "LL"). Receive: poll each peer's line until its flag equals s, then fold in rank order.
 // Nothing needs resetting: an old line carries an older sequence number.
-template <int DT, int NMAX>
+template <int DT, int NMAX, bool kMulti>
 __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
-                                rsrc_t out_r, int k) {
+                                rsrc_t out_r, int k, uint64_t& t0) {
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t elo = static_cast<uint32_t>(s), ehi = static_cast<uint32_t>(s >> 32);
@@ -284,43 +284,52 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
     fold_rank_order<DT, NMAX, 2>(N, r, x, v, o);
     store_unit<DT, 8>(out_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, o);
   };
-  if (c.T >= CU) {
+  if constexpr (!kMulti) {
+    // one pass: the plan gives this rank at least one lane per unit of the chunk
     const uint32_t i = c.t0 + c.lane;
     const bool act = i < CU;
-    const uint32_t off0 = b * N * slot + i * 16u;
+    uint32_t off0 = b * N * slot + i * 16u;
+    uint32_t in_off = act ? (unit0 + i) * 8u : kDrop;
+    uint32_t push_off = act ? mine + i * 16u : kDrop;
+    pin(off0);
+    pin(in_off);
+    pin(push_off);
+    stamp_start(t0, k);
     uint32_t x[2];
-    load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, x);
+    load_unit<DT, 8>(in_r, in_off, a.nbytes, x);
     compiler_fence();
     wait_vm<0>();
-    if (sends) push_peers<NMAX>(a, r, a.ll, act ? mine + i * 16u : kDrop, u32x4{x[0], x[1], elo, ehi});
+    if (sends) push_peers<NMAX>(a, r, a.ll, push_off, u32x4{x[0], x[1], elo, ehi});
     u32x4 v[NMAX];
     if (!poll_all<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
     finish(i, act, x, v);
     wait_all_mem();
     return true;
-  }
-  wait_all_mem();
-  if (sends) {
+  } else {
+    stamp_start(t0, k);
+    wait_all_mem();
+    if (sends) {
+      for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+        const uint32_t i = i0 + c.lane;
+        const bool act = i < CU;
+        uint32_t w[2];
+        load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, w);
+        push_peers<NMAX>(a, r, a.ll, act ? mine + i * 16u : kDrop, u32x4{w[0], w[1], elo, ehi});
+      }
+    }
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
       const bool act = i < CU;
-      uint32_t w[2];
-      load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, w);
-      push_peers<NMAX>(a, r, a.ll, act ? mine + i * 16u : kDrop, u32x4{w[0], w[1], elo, ehi});
+      uint32_t x[2];
+      load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, x);
+      u32x4 v[NMAX];
+      if (!poll_lines<NMAX>(a, own, b * N * slot + i * 16u, slot, act ? peers : 0u, v, ready, r, s))
+        return false;
+      finish(i, act, x, v);
     }
+    wait_all_mem();
+    return true;
   }
-  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
-    const uint32_t i = i0 + c.lane;
-    const bool act = i < CU;
-    uint32_t x[2];
-    load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, x);
-    u32x4 v[NMAX];
-    if (!poll_lines<NMAX>(a, own, b * N * slot + i * 16u, slot, act ? peers : 0u, v, ready, r, s))
-      return false;
-    finish(i, act, x, v);
-  }
-  wait_all_mem();
-  return true;
 }
 
 // ------------------------------------------------------------------ one-shot, sentinel protocol
@@ -329,9 +338,9 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
 // of a peer's unit equals the sentinel, fold in rank order, then write the sentinel back so the
 // slot is armed for step s+2 (the same buffer). The output store is issued before the re-arm so
 // that the step can return as soon as the output has landed.
-template <int DT, int NMAX>
+template <int DT, int NMAX, bool kMulti>
 __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
-                                      rsrc_t out_r, int k) {
+                                      rsrc_t out_r, int k, uint64_t& t0) {
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t slot = a.p1.slot, CU = a.chunk_units;
@@ -349,44 +358,53 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
     store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, o);
     rearm<NMAX>(own, off0, slot, act ? peers : 0u, sent);
   };
-  if (c.T >= CU) {
+  if constexpr (!kMulti) {
+    // one pass: the plan gives this rank at least one lane per unit of the chunk
     const uint32_t i = c.t0 + c.lane;
     const bool act = i < CU;
-    const uint32_t off0 = b * N * slot + i * 16u;
+    uint32_t off0 = b * N * slot + i * 16u;
+    uint32_t in_off = act ? (unit0 + i) * 16u : kDrop;
+    uint32_t push_off = act ? mine + i * 16u : kDrop;
+    pin(off0);
+    pin(in_off);
+    pin(push_off);
+    stamp_start(t0, k);
     uint32_t x[4];
-    load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
+    load_unit<DT, 16>(in_r, in_off, a.nbytes, x);
     compiler_fence();
     wait_vm<0>();
-    if (sends) push_peers<NMAX>(a, r, a.p1, act ? mine + i * 16u : kDrop, u32x4{x[0], x[1], x[2], x[3]});
+    if (sends) push_peers<NMAX>(a, r, a.p1, push_off, u32x4{x[0], x[1], x[2], x[3]});
     u32x4 v[NMAX];
     if (!poll_all<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
     finish(i, act, x, v, off0);
     compiler_fence();
     wait_vm<NMAX>();  // the output store(s) have landed; the NMAX re-arm stores may be in flight
     return true;
-  }
-  wait_all_mem();
-  if (sends) {
+  } else {
+    stamp_start(t0, k);
+    wait_all_mem();
+    if (sends) {
+      for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+        const uint32_t i = i0 + c.lane;
+        const bool act = i < CU;
+        uint32_t w[4];
+        load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, w);
+        push_peers<NMAX>(a, r, a.p1, act ? mine + i * 16u : kDrop, u32x4{w[0], w[1], w[2], w[3]});
+      }
+    }
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
       const bool act = i < CU;
-      uint32_t w[4];
-      load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, w);
-      push_peers<NMAX>(a, r, a.p1, act ? mine + i * 16u : kDrop, u32x4{w[0], w[1], w[2], w[3]});
+      const uint32_t off0 = b * N * slot + i * 16u;
+      uint32_t x[4];
+      load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
+      u32x4 v[NMAX];
+      if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+      finish(i, act, x, v, off0);
     }
+    wait_all_mem();
+    return true;
   }
-  for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
-    const uint32_t i = i0 + c.lane;
-    const bool act = i < CU;
-    const uint32_t off0 = b * N * slot + i * 16u;
-    uint32_t x[4];
-    load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
-    u32x4 v[NMAX];
-    if (!poll_lines<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
-    finish(i, act, x, v, off0);
-  }
-  wait_all_mem();
-  return true;
 }
 
 // ------------------------------------------------------------------ two-shot helpers
@@ -439,7 +457,7 @@ __device__ __forceinline__ void allgather_out(const Args& a, int r, rsrc_t out_r
 // r; every rank copies the other owners' results into its output (§III.A "Two-shot").
 template <int DT, int NMAX>
 __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r, rsrc_t out_r,
-                             int k) {
+                             int k, uint64_t& t0) {
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t slot1 = a.p1.slot, slot2 = a.p2.slot, CU = a.chunk_units, P = a.part_units;
@@ -456,8 +474,11 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
     const uint32_t i = c.t0 + c.lane;
     const bool act = i < CU;
     const uint32_t mask = act ? peers : 0u;
-    const uint32_t off1 = b * N * slot1 + i * 16u, off2 = b * N * slot2 + i * 16u;
+    uint32_t off1 = b * N * slot1 + i * 16u;
+    const uint32_t off2 = b * N * slot2 + i * 16u;
     const uint32_t uoff = (r * P + k * CU + i) * 16u;
+    pin(off1);
+    stamp_start(t0, k);
     uint32_t w[NMAX][4];
     load_partitions<DT, NMAX>(a, r, in_r, k, i, act, 0, w);  // w[0] is the own partition
     compiler_fence();
@@ -492,7 +513,7 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
 // slower). It runs in its own kernel, built for higher occupancy.
 template <int DT, int NMAX>
 __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
-                                  rsrc_t out_r, int k) {
+                                  rsrc_t out_r, int k, uint64_t& t0) {
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t slot1 = a.p1.slot, slot2 = a.p2.slot, CU = a.chunk_units, P = a.part_units;
@@ -503,6 +524,7 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
   const u32x4 sent = sentinel_vec<DT>();
   auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
   const uint32_t mine1 = (b * N + r) * slot1, mine2 = (b * N + r) * slot2;
+  stamp_start(t0, k);
   wait_all_mem();
   if (sends) {
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
@@ -558,7 +580,7 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
 // and runs the all-gather of the plain two-shot.
 template <int DT, int NMAX>
 __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r, rsrc_t out_r,
-                           int k) {
+                           int k, uint64_t& t0) {
   static_assert(DT == DT_F32 || DT == DT_I32, "atomic reduction is for fp32 and int32");
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
@@ -570,6 +592,7 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
   const uint32_t peers = peer_mask(N, r);
   const u32x4 sent = sentinel_vec<DT>();
   auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+  stamp_start(t0, k);
   wait_all_mem();
   if (has_units && r != a.withhold) {
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
@@ -716,10 +739,11 @@ __device__ bool xrank_barrier(const Args& a, const Ctx& c, uint64_t val, uint64_
 // acquire, reduce.
 template <int DT, int NMAX>
 __device__ bool step_barrier2(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
-                              rsrc_t out_r, int k) {
+                              rsrc_t out_r, int k, uint64_t& t0) {
   const int N = a.nranks, r = c.rank;
   const uint32_t slot = a.bdat.slot, CU = a.chunk_units;
   const uint32_t unit0 = static_cast<uint32_t>(k) * CU;
+  stamp_start(t0, k);
   if (!xrank_barrier(a, c, 2 * s, s)) return false;
   if (r != a.withhold) {
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
@@ -847,12 +871,11 @@ __device__ __forceinline__ void ar_body(const Args& a) {
     const rsrc_t in_r = in_rsrc(uniform_ptr(inp), a.nbytes);
     const rsrc_t out_r = out_rsrc(const_cast<void*>(uniform_ptr(outp)), a.nbytes);
     if (a.drift > 0) drift_sleep(a, it, c.rank, c.cta);
-    uint64_t t_start = 0;
-    if (a.ts_start != nullptr) t_start = now_ticks();
     if (table && it + 1 < a.iters) {
       next_in = a.in_tab[set * N + c.rank];
       next_out = a.out_tab[set * N + c.rank];
     }
+    uint64_t t_start = 0;  // stamped by the first step right before its first input load
     bool failed = false;
     uint64_t s = 0;
     for (int k = 0; k < a.chunks; ++k) {
@@ -860,18 +883,23 @@ __device__ __forceinline__ void ar_body(const Args& a) {
       s = a.e0 + step;
       bool ok;
       if constexpr (ALGO == ALGO_ONESHOT_LL) {
-        ok = step_oneshot_ll<DT, NMAX>(a, c, s, in_r, out_r, k);
+        ok = step_oneshot_ll<DT, NMAX, false>(a, c, s, in_r, out_r, k, t_start);
+      } else if constexpr (ALGO == ALGO_ONESHOT_LL_MULTI) {
+        ok = step_oneshot_ll<DT, NMAX, true>(a, c, s, in_r, out_r, k, t_start);
       } else if constexpr (ALGO == ALGO_ONESHOT_SENTINEL) {
-        ok = step_oneshot_sentinel<DT, NMAX>(a, c, s, in_r, out_r, k);
+        ok = step_oneshot_sentinel<DT, NMAX, false>(a, c, s, in_r, out_r, k, t_start);
+      } else if constexpr (ALGO == ALGO_ONESHOT_SENTINEL_MULTI) {
+        ok = step_oneshot_sentinel<DT, NMAX, true>(a, c, s, in_r, out_r, k, t_start);
       } else if constexpr (ALGO == ALGO_TWOSHOT) {
-        ok = step_twoshot<DT, NMAX>(a, c, s, in_r, out_r, k);
+        ok = step_twoshot<DT, NMAX>(a, c, s, in_r, out_r, k, t_start);
       } else if constexpr (ALGO == ALGO_TWOSHOT_BULK) {
-        ok = step_twoshot_bulk<DT, NMAX>(a, c, s, in_r, out_r, k);
+        ok = step_twoshot_bulk<DT, NMAX>(a, c, s, in_r, out_r, k, t_start);
       } else if constexpr (ALGO == ALGO_LL128_ATOMIC) {
-        ok = step_ll128<DT, NMAX>(a, c, s, in_r, out_r, k);
+        ok = step_ll128<DT, NMAX>(a, c, s, in_r, out_r, k, t_start);
       } else if constexpr (ALGO == ALGO_BARRIER2) {
-        ok = step_barrier2<DT, NMAX>(a, c, s, in_r, out_r, k);
+        ok = step_barrier2<DT, NMAX>(a, c, s, in_r, out_r, k, t_start);
       } else {
+        stamp_start(t_start, k);
         ok = xrank_barrier(a, c, 2 * s, s);
       }
       if (!ok) {
@@ -963,6 +991,9 @@ ar_kernel_fn ar_select_kernel(int algo, int dt, int nmax) {
   switch (algo) {
     case ar::ALGO_ONESHOT_LL: return pick_dt<ar::ALGO_ONESHOT_LL>(dt, nmax);
     case ar::ALGO_ONESHOT_SENTINEL: return pick_dt<ar::ALGO_ONESHOT_SENTINEL>(dt, nmax);
+    case ar::ALGO_ONESHOT_LL_MULTI: return pick_dt<ar::ALGO_ONESHOT_LL_MULTI>(dt, nmax);
+    case ar::ALGO_ONESHOT_SENTINEL_MULTI:
+      return pick_dt<ar::ALGO_ONESHOT_SENTINEL_MULTI>(dt, nmax);
     case ar::ALGO_TWOSHOT: return pick_dt<ar::ALGO_TWOSHOT>(dt, nmax);
     case ar::ALGO_TWOSHOT_BULK: return pick_dt<ar::ALGO_TWOSHOT_BULK>(dt, nmax);
     case ar::ALGO_LL128_ATOMIC:
