@@ -171,6 +171,8 @@ int ar_set_option(ar_handle* h, ar_option opt, int64_t value);
  *   0 = one-shot / reduce-scatter sentinel slots  1 = all-gather sentinel slots
  *   2 = LL lines  3 = atomic destination  4 = arrival counters  5 = barrier flags
  *   6 = barrier-baseline data
+ *   7, 8, 9 = the near LL, one-shot / reduce-scatter and all-gather regions that small messages
+ *   use (slots of at most 8 KiB at a 16 KiB pitch, each in the granule homed near its rank)
  */
 int64_t ar_region_bytes(ar_handle* h, int region);
 int ar_read_region(ar_handle* h, int rank, int region, void* host_dst, size_t bytes);
@@ -190,7 +192,9 @@ typedef struct {
   double coherent_load_ns; /* dependent load with the agent-coherent (sc1) policy, 1 MiB     */
   double mall_load_ns;     /* dependent load, 64 MiB footprint (beyond L2)                   */
   double hbm_load_ns;      /* dependent load, 1 GiB footprint (beyond the 256 MiB MALL)      */
-  double store_half_rtt_ns;/* store -> poll ping-pong (sc1 store, sc1 poll), half round trip */
+  double store_half_rtt_ns;/* store -> poll ping-pong (sc1 store, sc1 poll), half round trip,
+                              on a line homed in the workgroups' half of the chip            */
+  double store_half_rtt_far_ns; /* the same on a line homed in the other half                */
   double floor_ns;         /* 2 * l2_load_ns + store_half_rtt_ns                             */
   double floor_fence_ns;   /* the pages' form: 2 * fence_ns + store_half_rtt_ns              */
   int xcc_a, xcc_b;        /* XCC ids the two ping-pong workgroups ran on                     */

@@ -23,7 +23,8 @@ AR_OK, AR_EINVAL, AR_ETOOBIG, AR_ENOTSUP, AR_EHIP, AR_ETIMEOUT, AR_ENORES = 0, -
 AR_PLACE_XCD, AR_PLACE_SAME, AR_PLACE_LINEAR = 0, 1, 2
 (AR_OPT_TIMEOUT_US, AR_OPT_WITHHOLD_RANK, AR_OPT_CTAS, AR_OPT_THREADS, AR_OPT_PLACEMENT,
  AR_OPT_DRIFT) = range(6)
-REGION_P1, REGION_P2, REGION_LL, REGION_ACC, REGION_CNT, REGION_BAR, REGION_BDAT = range(7)
+(REGION_P1, REGION_P2, REGION_LL, REGION_ACC, REGION_CNT, REGION_BAR, REGION_BDAT,
+ REGION_LL_NEAR, REGION_P1_NEAR, REGION_P2_NEAR) = range(10)
 
 ALGOS = {
     "auto": AR_ALGO_AUTO,
@@ -58,6 +59,7 @@ class ar_sol_result(ctypes.Structure):
         ("mall_load_ns", ctypes.c_double),
         ("hbm_load_ns", ctypes.c_double),
         ("store_half_rtt_ns", ctypes.c_double),
+        ("store_half_rtt_far_ns", ctypes.c_double),
         ("floor_ns", ctypes.c_double),
         ("floor_fence_ns", ctypes.c_double),
         ("xcc_a", ctypes.c_int),

@@ -10,6 +10,9 @@
 //   cnt  [buffer 2][cta][wave] u32    zero       LL128-style arrival counters
 //   bar  [source][cta] u64            zero       barrier flags (monotonic)
 //   bdat [source N][slot]             any        barrier-baseline data slots
+// Every block starts with a 2 MiB near area holding small-message copies of ll, p1 and p2 whose
+// slots have a 16 KiB pitch (two 8 KiB granules); a rank's slots use the granule of each pitch
+// that is homed in its XCD's half of the chip (calibrated at creation, see ar_args.h).
 // The two buffers implement double buffering: step s uses buffer s & 1 (Fig. 4 and §IV
 // "Bidirectional Communication Double Buffering"; Fig. 7's per-epoch alternating sub-buffers).
 
@@ -31,8 +34,11 @@ namespace {
 
 thread_local std::string g_err;
 
-constexpr int kRegions = 7;
-enum RegionId { RG_P1 = 0, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT };
+constexpr int kRegions = 10;
+enum RegionId {
+  RG_P1 = 0, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT,
+  RG_LLN, RG_P1N, RG_P2N,  // near copies of ll, p1, p2 for small messages
+};
 constexpr uint64_t kDefaultCap = 256ull << 20;
 constexpr uint64_t kMaxCap = 1ull << 30;  // keeps every region below the drop offset (2 GiB)
 constexpr int kXcds = 8;
@@ -94,8 +100,10 @@ struct ar_handle {
   int dtype = 0;
   size_t max_bytes = 0;
   int device = 0;
+  void* raw = nullptr;      // the allocation; base is its first 2 MiB boundary
   uint8_t* base = nullptr;
   uint64_t stride = 0;
+  float near_ns[ar::kMaxRanks][4][ar::kNearPositions] = {};  // calibrated position latencies
   ar::Region rg[kRegions] = {};
   uint32_t* ctl = nullptr;          // device control words
   uint32_t* status_host = nullptr;  // pinned host status words
@@ -129,6 +137,8 @@ struct Launch {
   int ctas = 1;
   int ranks_per_xcd = 1;
   int xcds_per_rank = 1;
+  bool near = false;        // small message: slots in the near regions
+  uint64_t home_pos = 0;    // with `near`: each rank's data position in the near pitch
   unsigned grid = 1;
 };
 
@@ -167,10 +177,21 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
   }
   if (cap_units == 0) return ar_fail(AR_EINVAL, "scratch slots are too small");
   const uint64_t K = units == 0 ? 1 : ceil_div(units, cap_units);
-  const uint64_t C = units == 0 ? 0 : ceil_div(units, K);
+  uint64_t C = units == 0 ? 0 : ceil_div(units, K);
   L.chunks = static_cast<int>(K);
   L.chunk_units = static_cast<uint32_t>(C);
   L.part_units = static_cast<uint32_t>(K * C);
+  // Messages whose slots fit one granule use the near regions (one chunk, 16 bytes per unit).
+  constexpr uint64_t kNearUnits = ar::kGranule / 16;
+  L.near = units > 0 && units <= kNearUnits &&
+           (algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL || algo == AR_TWOSHOT ||
+            (algo == AR_LL128_ATOMIC && units <= h->rg[RG_ACC].slot / 16));
+  if (L.near) {
+    L.chunks = 1;
+    L.chunk_units = static_cast<uint32_t>(units);
+    L.part_units = static_cast<uint32_t>(units);
+    C = units;
+  }
   // Small chunks: one workgroup just wide enough that no wave is idle; larger ones: 256-thread
   // workgroups, one unit per lane per pass.
   L.threads = h->threads ? h->threads
@@ -218,6 +239,21 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
     return ar_fail(AR_ENORES, "%d workgroups per rank exceed the co-resident limit %d", ctas,
                    max_ctas);
   L.ctas = ctas;
+  if (L.near) {
+    // Each rank's slot data goes to the fastest calibrated position, for the XCD pair of the
+    // XCD of its first workgroup, among those where the slot's data fits its granule.
+    const uint64_t data = algo == AR_ONESHOT_LL ? units * 16 : C * 16;
+    const int max_sub = static_cast<int>((ar::kGranule - data) / ar::kNearSub);
+    for (int r = 0; r < N; ++r) {
+      const int x = h->placement == AR_PLACE_XCD    ? r % kXcds
+                    : h->placement == AR_PLACE_SAME ? 0
+                                                    : (r * ctas) % kXcds;
+      int best = 0;
+      for (int k = 0; k < ar::kNearPositions; ++k)
+        if (k % 4 <= max_sub && h->near_ns[r][x / 2][k] < h->near_ns[r][x / 2][best]) best = k;
+      L.home_pos |= static_cast<uint64_t>(best) << (4 * r);
+    }
+  }
   if (h->placement == AR_PLACE_XCD)
     L.grid = static_cast<unsigned>(kXcds * L.ranks_per_xcd *
                                    ceil_div(static_cast<uint64_t>(ctas), L.xcds_per_rank));
@@ -233,9 +269,10 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
   std::memset(&a, 0, sizeof a);
   a.base = h->base;
   a.stride = h->stride;
-  a.p1 = h->rg[RG_P1];
-  a.p2 = h->rg[RG_P2];
-  a.ll = h->rg[RG_LL];
+  a.p1 = h->rg[L.near ? RG_P1N : RG_P1];
+  a.p2 = h->rg[L.near ? RG_P2N : RG_P2];
+  a.ll = h->rg[L.near ? RG_LLN : RG_LL];
+  a.home_pos = L.home_pos;
   a.acc = h->rg[RG_ACC];
   a.cnt = h->rg[RG_CNT];
   a.bar = h->rg[RG_BAR];
@@ -301,7 +338,7 @@ int launch(ar_kernel_fn fn, unsigned grid, int threads, ar::Args& a, hipStream_t
 }
 
 void release(ar_handle* h) {
-  if (h->base) (void)hipFree(h->base);
+  if (h->raw) (void)hipFree(h->raw);
   if (h->ctl) (void)hipFree(h->ctl);
   if (h->status_host) (void)hipHostFree(h->status_host);
   if (h->tab) (void)hipFree(h->tab);
@@ -376,8 +413,18 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
   sz[RG_CNT] = {0, 2ull * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 4};
   sz[RG_BAR] = {0, 1ull * ar::kMaxRanks * ar::kMaxCtasPerRank * 8};
   sz[RG_BDAT] = {slot_os, 1ull * N * slot_os};
+  // near area: three regions of 2 * N slots at a 16 KiB pitch, together at most 1.5 MiB
+  for (int i = RG_LLN; i <= RG_P2N; ++i) sz[i] = {ar::kNearPitch, 2ull * N * ar::kNearPitch};
   uint64_t off = 0;
-  for (int i = 0; i < kRegions; ++i) {
+  for (int i = RG_LLN; i <= RG_P2N; ++i) {
+    h->rg[i].off = off;
+    h->rg[i].bytes = static_cast<uint32_t>(sz[i].bytes);
+    h->rg[i].slot = static_cast<uint32_t>(sz[i].slot);
+    h->rg[i].home = 1;
+    off += sz[i].bytes;
+  }
+  off = ar::kNearArea;
+  for (int i = 0; i < RG_LLN; ++i) {
     if (sz[i].bytes >= (1ull << 31)) {
       ar_fail(AR_ETOOBIG, "scratch region %d would exceed 2 GiB per rank", i);
       release(h);
@@ -388,14 +435,20 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
     h->rg[i].slot = static_cast<uint32_t>(sz[i].slot);
     off = round_up(off + sz[i].bytes, 4096);
   }
-  h->stride = round_up(off, 1 << 16);
+  // Rank blocks start on 2 MiB boundaries so that every near area is one 2 MiB page.
+  h->stride = round_up(off, ar::kNearArea);
   const uint64_t total = h->stride * N;
-  if ((e = hipMalloc(reinterpret_cast<void**>(&h->base), total)) != hipSuccess)
+  if ((e = hipMalloc(&h->raw, total + ar::kNearArea)) != hipSuccess)
     return fail(e, "hipMalloc(scratch)");
+  h->base = reinterpret_cast<uint8_t*>(round_up(reinterpret_cast<uintptr_t>(h->raw), ar::kNearArea));
   if ((e = hipMemset(h->base, 0, total)) != hipSuccess) return fail(e, "hipMemset(scratch)");
+  if (ar_near_positions(h->base, h->stride, N, h->near_ns) != AR_OK) {
+    release(h);
+    return nullptr;
+  }
   const uint32_t sw = sentinel_word(dtype);
-  ar_launch_fill(h->base, h->stride, N, h->rg[RG_P1].off, h->rg[RG_P1].bytes, sw, nullptr);
-  ar_launch_fill(h->base, h->stride, N, h->rg[RG_P2].off, h->rg[RG_P2].bytes, sw, nullptr);
+  for (int i : {RG_P1, RG_P2, RG_P1N, RG_P2N})
+    ar_launch_fill(h->base, h->stride, N, h->rg[i].off, h->rg[i].bytes, sw, nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return fail(e, "scratch fill launch");
   if ((e = hipMalloc(reinterpret_cast<void**>(&h->ctl), ar::CTL_WORDS * 4)) != hipSuccess)
     return fail(e, "hipMalloc(ctl)");

@@ -65,8 +65,15 @@ __device__ __forceinline__ bool decode(const Args& a, Ctx& c) {
 
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Start of region g in rank `rank`'s block; in a near region every slot's data starts at the
+// rank's position inside the slot's pitch.
+__device__ __forceinline__ uint8_t* region_base(const Args& a, int rank, const Region& g) {
+  const uint32_t pos = g.home * static_cast<uint32_t>((a.home_pos >> (4 * rank)) & 7u);
+  return a.base + static_cast<uint64_t>(rank) * a.stride + g.off + pos * kNearSub;
+}
+
 __device__ __forceinline__ rsrc_t region_rsrc(const Args& a, int rank, const Region& g) {
-  return make_rsrc(a.base + static_cast<uint64_t>(rank) * a.stride + g.off, g.bytes);
+  return make_rsrc(region_base(a, rank, g), g.bytes);
 }
 
 // Region of the j-th peer after rank r (q = (r + j) mod N), or a descriptor that drops every
@@ -75,8 +82,7 @@ __device__ __forceinline__ rsrc_t peer_rsrc(const Args& a, int r, int j, const R
   int q = r + j;
   if (q >= a.nranks) q -= a.nranks;
   const bool live = j < a.nranks;
-  return make_rsrc(a.base + static_cast<uint64_t>(live ? q : 0) * a.stride + g.off,
-                   live ? g.bytes : 0u);
+  return make_rsrc(region_base(a, live ? q : 0, g), live ? g.bytes : 0u);
 }
 
 // Where a poll loop reports a timeout: the few kernel arguments the slow path needs, passed by

@@ -96,6 +96,44 @@ __global__ void sol_pingpong(uint32_t* flags, int rounds, int a_blk, int b_blk, 
   }
 }
 
+// --------------------------------------------------------------- near-position probe
+// Workgroups a and b (on two XCDs) ping-pong `rounds` times on each of kNearPositions positions of
+// one 2 MiB page: position k = granule k / 4, 2 KiB sub-block k % 4, flag words at +1024 and
+// +1536 inside the sub-block (zero before the probe). out[k] = ticks of position k's rounds.
+__global__ void near_probe(uint32_t* page, int rounds, int a_blk, int b_blk, uint32_t spin_cap,
+                           uint64_t* out) {
+  const int me = blockIdx.x;
+  if ((me != a_blk && me != b_blk) || threadIdx.x != 0) return;
+  const bool is_a = me == a_blk;
+  for (int k = 0; k < kNearPositions; ++k) {
+    const uint32_t base = (k / 4) * kGranule + (k % 4) * 2048u;
+    const rsrc_t r = make_rsrc(reinterpret_cast<uint8_t*>(page) + base, 2048);
+    const uint64_t t0 = now_ticks();
+    int done = 0;
+    for (int i = 1; i <= rounds; ++i) {
+      uint32_t spins = 0;
+      if (is_a) {
+        st4<kCoh>(r, 1024, static_cast<uint32_t>(i));
+        while (true) {
+          const uint32_t v = ld4<kCoh>(r, 1536);
+          compiler_fence();
+          if (v == static_cast<uint32_t>(i) || ++spins > spin_cap) break;
+        }
+      } else {
+        while (true) {
+          const uint32_t v = ld4<kCoh>(r, 1024);
+          compiler_fence();
+          if (v == static_cast<uint32_t>(i) || ++spins > spin_cap) break;
+        }
+        st4<kCoh>(r, 1536, static_cast<uint32_t>(i));
+      }
+      if (spins > spin_cap) break;
+      done = i;
+    }
+    if (is_a) out[k] = done == rounds ? now_ticks() - t0 : ~0ull;
+  }
+}
+
 // --------------------------------------------------------------- torn 16-byte line probe
 // Writer workgroup (blockIdx w_blk, one lane per line) stores generations g = 1..gens into
 // `lines` 16-byte lines as {g, ~g, g * 0x9E3779B1, g ^ 0x5A5A5A5A} with one 16-byte coherent
@@ -202,19 +240,18 @@ void pair_blocks(int placement, int& a, int& b) {
   b = placement == AR_PLACE_SAME ? 8 : 1;
 }
 
-int run_pingpong(int placement, int cps, int cpl, int rounds, double* half_ns, int* xcc) {
+// Ping-pong between workgroups a and b (of 16; workgroup w runs on XCD w % 8) on the two flag
+// words at `flags` and `flags` + 512 bytes (the caller zeroes them).
+int run_pingpong_at(uint32_t* flags, int a, int b, int cps, int cpl, int rounds, double* half_ns,
+                    int* xcc) {
   pp_fn fn = pp_select(cps, cpl);
   if (fn == nullptr) return ar_fail(AR_EINVAL, "cache policy must be 0, 1, 2, 16 or 17");
   if (rounds < 1 || rounds > 1000000) return ar_fail(AR_EINVAL, "rounds out of range");
-  DevBuf flags, out;
-  AR_HIP(hipMalloc(&flags.p, 1024));
+  DevBuf out;
   AR_HIP(hipMalloc(&out.p, 4 * sizeof(uint64_t)));
-  AR_HIP(hipMemset(flags.p, 0, 1024));
   AR_HIP(hipMemset(out.p, 0, 4 * sizeof(uint64_t)));
-  int a = 0, b = 0;
-  pair_blocks(placement, a, b);
-  hipLaunchKernelGGL(fn, dim3(16), dim3(64), 0, nullptr, static_cast<uint32_t*>(flags.p), rounds,
-                     a, b, 1000000u, static_cast<uint64_t*>(out.p));
+  hipLaunchKernelGGL(fn, dim3(16), dim3(64), 0, nullptr, flags, rounds, a, b, 1000000u,
+                     static_cast<uint64_t*>(out.p));
   AR_HIP(hipGetLastError());
   AR_HIP(hipDeviceSynchronize());
   uint64_t o[4];
@@ -229,6 +266,51 @@ int run_pingpong(int placement, int cps, int cpl, int rounds, double* half_ns, i
   const double hz = ar_wallclock_hz();
   *half_ns = static_cast<double>(o[0]) / hz * 1e9 / (2.0 * rounds);
   return AR_OK;
+}
+
+// 2 MiB-aligned device buffer of `bytes` bytes (the allocation is padded and aligned by hand).
+struct PageBuf {
+  DevBuf raw;
+  uint8_t* p = nullptr;
+  int alloc(uint64_t bytes) {
+    AR_HIP(hipMalloc(&raw.p, bytes + ar::kNearArea));
+    const uintptr_t x = reinterpret_cast<uintptr_t>(raw.p);
+    p = reinterpret_cast<uint8_t*>((x + ar::kNearArea - 1) / ar::kNearArea * ar::kNearArea);
+    AR_HIP(hipMemset(raw.p, 0, bytes + ar::kNearArea));
+    return AR_OK;
+  }
+};
+
+// Half round trips of the store -> poll ping-pong between workgroups a and b at every position
+// of the near probe on a 2 MiB page (zero before and after).
+int pingpong_positions(uint8_t* page, int a, int b, int rounds, float ns[ar::kNearPositions]) {
+  DevBuf out;
+  AR_HIP(hipMalloc(&out.p, ar::kNearPositions * sizeof(uint64_t)));
+  hipLaunchKernelGGL(ar::near_probe, dim3(16), dim3(64), 0, nullptr,
+                     reinterpret_cast<uint32_t*>(page), rounds, a, b, 1000000u,
+                     static_cast<uint64_t*>(out.p));
+  AR_HIP(hipGetLastError());
+  uint64_t o[ar::kNearPositions];
+  AR_HIP(hipMemcpy(o, out.p, sizeof o, hipMemcpyDeviceToHost));
+  const double hz = ar_wallclock_hz();
+  for (int k = 0; k < ar::kNearPositions; ++k) {
+    if (o[k] == ~0ull) return ar_fail(AR_ETIMEOUT, "near-position probe stalled");
+    ns[k] = static_cast<float>(static_cast<double>(o[k]) / hz * 1e9 / (2.0 * rounds));
+  }
+  AR_HIP(hipMemset(page, 0, 2 * ar::kGranule));
+  return AR_OK;
+}
+
+int run_pingpong(int placement, int cps, int cpl, int rounds, double* half_ns, int* xcc) {
+  if (pp_select(cps, cpl) == nullptr)
+    return ar_fail(AR_EINVAL, "cache policy must be 0, 1, 2, 16 or 17");
+  if (rounds < 1 || rounds > 1000000) return ar_fail(AR_EINVAL, "rounds out of range");
+  DevBuf flags;
+  AR_HIP(hipMalloc(&flags.p, 1024));
+  AR_HIP(hipMemset(flags.p, 0, 1024));
+  int a = 0, b = 0;
+  pair_blocks(placement, a, b);
+  return run_pingpong_at(static_cast<uint32_t*>(flags.p), a, b, cps, cpl, rounds, half_ns, xcc);
 }
 
 // Random cyclic pointer chain over `bytes` with one node per 128 bytes (Sattolo's shuffle gives a
@@ -263,6 +345,20 @@ int run_chase(uint64_t bytes, int hops, bool warm_full, double* ns) {
 }
 
 }  // namespace
+
+int ar_near_positions(uint8_t* base, uint64_t stride, int nranks,
+                      float (*ns)[4][ar::kNearPositions]) {
+  // For every rank block's near area and every pair of XCDs {2p, 2p+1}: the half round trip of
+  // the pair's ping-pong at each of the positions. The area is zero before and after.
+  for (int r = 0; r < nranks; ++r) {
+    uint8_t* page = base + static_cast<uint64_t>(r) * stride;
+    for (int p = 0; p < 4; ++p) {
+      const int rc = pingpong_positions(page, 2 * p, 2 * p + 1, 24, ns[r][p]);
+      if (rc != AR_OK) return rc;
+    }
+  }
+  return AR_OK;
+}
 
 extern "C" {
 
@@ -300,10 +396,21 @@ int ar_sol(int placement, ar_sol_result* res) {
     return rc;
   if ((rc = run_chase<ar::kPlain>(1ull << 30, 20000, false, &res->hbm_load_ns)) != AR_OK)
     return rc;
+  // The store term on a line homed near the two XCDs and on one homed in the other half.
   int xcc[2] = {-1, -1};
-  if ((rc = run_pingpong(placement, ar::kSc1, ar::kSc1, 5000, &res->store_half_rtt_ns, xcc)) !=
-      AR_OK)
-    return rc;
+  {
+    PageBuf page;
+    if ((rc = page.alloc(ar::kNearArea)) != AR_OK) return rc;
+    int a = 0, b = 0;
+    pair_blocks(placement, a, b);
+    float half[ar::kNearPositions];
+    if ((rc = pingpong_positions(page.p, a, b, 1000, half)) != AR_OK) return rc;
+    res->store_half_rtt_ns = *std::min_element(half, half + ar::kNearPositions);
+    res->store_half_rtt_far_ns = *std::max_element(half, half + ar::kNearPositions);
+    // the XCC ids of the two workgroups, from the plain ping-pong on the same pair
+    double unused;
+    if ((rc = run_pingpong(placement, ar::kSc1, ar::kSc1, 10, &unused, xcc)) != AR_OK) return rc;
+  }
   res->xcc_a = xcc[0];
   res->xcc_b = xcc[1];
   res->floor_ns = 2.0 * res->l2_load_ns + res->store_half_rtt_ns;

@@ -86,16 +86,19 @@ def test_rank_constant_invariant(algo):
 @pytest.mark.parametrize("algo", ["oneshot_sentinel", "twoshot", "ll128_atomic"])
 def test_scratch_rearmed_after_call(algo):
     """After a call every sentinel slot holds the sentinel again and the atomic destination and
-    arrival counters are back to zero."""
+    arrival counters are back to zero: for a message that uses the regular regions and, at
+    1000 elements, for one that uses the near regions."""
     from latency_collectives_amd import _ar as A
 
     n, dtype, count = 4, "f32", 7777
     with handle(n, count * 4, dtype) as h:
         for it in range(3):
-            x = draw(dtype, n, count, seed=50 + it)
-            run_allreduce(h, x, algo)
+            for c in (count, 1000):
+                x = draw(dtype, n, c, seed=50 + it)
+                got = run_allreduce(h, x, algo)
+                assert_matches(got, x, algo, dtype)
         for r in range(n):
-            for reg in (A.REGION_P1, A.REGION_P2):
+            for reg in (A.REGION_P1, A.REGION_P2, A.REGION_P1_NEAR, A.REGION_P2_NEAR):
                 w = A.ar_read_region(h, r, reg).view(np.uint32)
                 assert np.all(w == 0xFFFFFFFF), f"rank {r} region {reg} not re-armed"
             for reg in (A.REGION_ACC, A.REGION_CNT):
@@ -227,6 +230,8 @@ def test_sol_microbench_sane():
     _say("sol same", s)
     assert s["xcc_a"] == s["xcc_b"]
     assert x["floor_ns"] == pytest.approx(2 * x["l2_load_ns"] + x["store_half_rtt_ns"])
+    # the floor's store term is the line homed near the pair; the other half's is reported too
+    assert x["store_half_rtt_far_ns"] >= x["store_half_rtt_ns"] > 0
 
 
 def test_sixteen_byte_lines_not_torn():
