@@ -104,6 +104,16 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
     if warm > 0:
         A.ar_bench(h, ins, outs, nsets, count, aid, warm, timestamps=False)
     ts, te, ms = A.ar_bench(h, ins, outs, nsets, count, aid, iters)
+    # launch-inclusive: host-issued ar_allreduce calls back to back, timed with events
+    calls = 50
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    A.ar_allreduce(h, ins[:n], outs[:n], count, aid)
+    ev0.record()
+    for _ in range(calls):
+        A.ar_allreduce(h, ins[:n], outs[:n], count, aid)
+    ev1.record()
+    torch.cuda.synchronize()
+    launch_us = ev0.elapsed_time(ev1) * 1e3 / calls
     ts = ts.reshape(iters, n).astype(np.int64)
     te = te.reshape(iters, n).astype(np.int64)
     lat_us = (te.max(axis=1) - ts.max(axis=1)) / hz * 1e6
@@ -117,6 +127,7 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
         "mean_us": float(lat_us.mean()),
         "period_us": period_us,
         "launch_ms": float(ms),
+        "launch_inclusive_us": float(launch_us),
         "iters": iters,
         "alg_bytes_per_call": alg_bytes(algo, n, size),
     }

@@ -202,9 +202,13 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
   // With N dividing 8 every rank gets 8 / N XCDs (its first workgroup stays on XCD r); the other
   // counts leave 8 - N XCDs idle rather than split a rank unevenly.
   L.xcds_per_rank = (h->placement == AR_PLACE_XCD && N < kXcds && kXcds % N == 0) ? kXcds / N : 1;
-  // Workgroups per rank that can all be resident at once with kernel `fn`.
+  // Workgroups per rank that can all be resident at once with kernel `fn`. A grid planned at the
+  // occupancy limit itself (every compute unit full) was once seen not to become resident as a
+  // whole (a rank-local join timed out), so one workgroup per compute unit is left free whenever
+  // the kernel fits more than one.
   auto co_resident = [&](ar_kernel_fn fn) {
-    const int occ = occupancy(fn, L.threads);
+    const int occ_api = occupancy(fn, L.threads);
+    const int occ = occ_api > 1 ? occ_api - 1 : occ_api;
     int m;
     if (h->placement == AR_PLACE_XCD)
       m = cus_per_xcd * occ * L.xcds_per_rank / L.ranks_per_xcd;
