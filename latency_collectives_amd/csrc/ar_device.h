@@ -157,10 +157,14 @@ struct Ty<DT_I32> {
   __device__ static bool word_clear(uint32_t w) { return w != 0x80000000u; }
 };
 
-// binary32 -> bfloat16, round to nearest even: gfx950's conversion instruction
-// (v_cvt_pk_bf16_f32, rounding per the default round-to-nearest-even mode).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+// Two binary32 values -> two bfloat16 in one word (lo in bits 15:0), round to nearest even:
+// one gfx950 conversion instruction (v_cvt_pk_bf16_f32, rounding per the default
+// round-to-nearest-even mode).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 // Fixed rank-order fold of W 32-bit payload words. Binary32 accumulation for fp32 and bf16
@@ -202,7 +206,7 @@ struct Fold<DT_BF16, W> {
   }
   __device__ __forceinline__ void pack(uint32_t* w) const {
 #pragma unroll
-    for (int i = 0; i < W; ++i) w[i] = bf16_rne(a[2 * i]) | (bf16_rne(a[2 * i + 1]) << 16);
+    for (int i = 0; i < W; ++i) w[i] = bf16x2_rne(a[2 * i], a[2 * i + 1]);
   }
 };
 template <int W>

@@ -274,7 +274,8 @@ __device__ __forceinline__ void push_peers(const Args& a, int r, const Region& g
 // Nothing needs resetting: an old line carries an older sequence number.
 template <int DT, int NMAX, bool kMulti>
 __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
-                                rsrc_t out_r, int k, uint64_t& t0) {
+                                rsrc_t out_r, int k, uint64_t& t0,
+                                uint64_t& t1) {
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t elo = static_cast<uint32_t>(s), ehi = static_cast<uint32_t>(s >> 32);
@@ -310,6 +311,7 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
     if (!poll_all<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
     finish(i, act, x, v);
     wait_all_mem();
+    t1 = now_ticks();
     return true;
   } else {
     stamp_start(t0, k);
@@ -334,6 +336,7 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
       finish(i, act, x, v);
     }
     wait_all_mem();
+    t1 = now_ticks();
     return true;
   }
 }
@@ -346,7 +349,8 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
 // that the step can return as soon as the output has landed.
 template <int DT, int NMAX, bool kMulti>
 __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
-                                      rsrc_t out_r, int k, uint64_t& t0) {
+                                      rsrc_t out_r, int k, uint64_t& t0,
+                                      uint64_t& t1) {
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t slot = a.p1.slot, CU = a.chunk_units;
@@ -385,6 +389,7 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
     finish(i, act, x, v, off0);
     compiler_fence();
     wait_vm<NMAX>();  // the output store(s) have landed; the NMAX re-arm stores may be in flight
+    t1 = now_ticks();
     return true;
   } else {
     stamp_start(t0, k);
@@ -409,6 +414,7 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
       finish(i, act, x, v, off0);
     }
     wait_all_mem();
+    t1 = now_ticks();
     return true;
   }
 }
@@ -463,7 +469,8 @@ __device__ __forceinline__ void allgather_out(const Args& a, int r, rsrc_t out_r
 // r; every rank copies the other owners' results into its output (§III.A "Two-shot").
 template <int DT, int NMAX>
 __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r, rsrc_t out_r,
-                             int k, uint64_t& t0) {
+                             int k, uint64_t& t0,
+                             uint64_t& t1) {
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t slot1 = a.p1.slot, slot2 = a.p2.slot, CU = a.chunk_units, P = a.part_units;
@@ -507,6 +514,7 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
     allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v2, sent);
     compiler_fence();
     wait_vm<NMAX>();  // every output store has landed; the NMAX re-arm stores may be in flight
+    t1 = now_ticks();
     return true;
   }
 }
@@ -519,7 +527,8 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
 // slower). It runs in its own kernel, built for higher occupancy.
 template <int DT, int NMAX>
 __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
-                                  rsrc_t out_r, int k, uint64_t& t0) {
+                                  rsrc_t out_r, int k, uint64_t& t0,
+                                  uint64_t& t1) {
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t slot1 = a.p1.slot, slot2 = a.p2.slot, CU = a.chunk_units, P = a.part_units;
@@ -570,6 +579,7 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
     allgather_out<DT, NMAX, kNt>(a, r, out_r, own2, off2, mask, k, i, v, sent);
   }
   wait_all_mem();
+  t1 = now_ticks();
   return true;
 }
 
@@ -586,7 +596,8 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
 // and runs the all-gather of the plain two-shot.
 template <int DT, int NMAX>
 __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r, rsrc_t out_r,
-                           int k, uint64_t& t0) {
+                           int k, uint64_t& t0,
+                           uint64_t& t1) {
   static_assert(DT == DT_F32 || DT == DT_I32, "atomic reduction is for fp32 and int32");
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
@@ -674,6 +685,7 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
     allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v, sent);
   }
   wait_all_mem();
+  t1 = now_ticks();
   return true;
 }
 
@@ -745,7 +757,8 @@ __device__ bool xrank_barrier(const Args& a, const Ctx& c, uint64_t val, uint64_
 // acquire, reduce.
 template <int DT, int NMAX>
 __device__ bool step_barrier2(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
-                              rsrc_t out_r, int k, uint64_t& t0) {
+                              rsrc_t out_r, int k, uint64_t& t0,
+                              uint64_t& t1) {
   const int N = a.nranks, r = c.rank;
   const uint32_t slot = a.bdat.slot, CU = a.chunk_units;
   const uint32_t unit0 = static_cast<uint32_t>(k) * CU;
@@ -783,6 +796,7 @@ __device__ bool step_barrier2(const Args& a, const Ctx& c, uint64_t s, rsrc_t in
     store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, o);
   }
   wait_all_mem();
+  t1 = now_ticks();
   return true;
 }
 
@@ -882,6 +896,7 @@ __device__ __forceinline__ void ar_body(const Args& a) {
       next_out = a.out_tab[set * N + c.rank];
     }
     uint64_t t_start = 0;  // stamped by the first step right before its first input load
+    uint64_t t_end = 0;    // stamped by the last step right after its output stores completed
     bool failed = false;
     uint64_t s = 0;
     for (int k = 0; k < a.chunks; ++k) {
@@ -889,24 +904,25 @@ __device__ __forceinline__ void ar_body(const Args& a) {
       s = a.e0 + step;
       bool ok;
       if constexpr (ALGO == ALGO_ONESHOT_LL) {
-        ok = step_oneshot_ll<DT, NMAX, false>(a, c, s, in_r, out_r, k, t_start);
+        ok = step_oneshot_ll<DT, NMAX, false>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_ONESHOT_LL_MULTI) {
-        ok = step_oneshot_ll<DT, NMAX, true>(a, c, s, in_r, out_r, k, t_start);
+        ok = step_oneshot_ll<DT, NMAX, true>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_ONESHOT_SENTINEL) {
-        ok = step_oneshot_sentinel<DT, NMAX, false>(a, c, s, in_r, out_r, k, t_start);
+        ok = step_oneshot_sentinel<DT, NMAX, false>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_ONESHOT_SENTINEL_MULTI) {
-        ok = step_oneshot_sentinel<DT, NMAX, true>(a, c, s, in_r, out_r, k, t_start);
+        ok = step_oneshot_sentinel<DT, NMAX, true>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_TWOSHOT) {
-        ok = step_twoshot<DT, NMAX>(a, c, s, in_r, out_r, k, t_start);
+        ok = step_twoshot<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_TWOSHOT_BULK) {
-        ok = step_twoshot_bulk<DT, NMAX>(a, c, s, in_r, out_r, k, t_start);
+        ok = step_twoshot_bulk<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_ATOMIC) {
-        ok = step_ll128<DT, NMAX>(a, c, s, in_r, out_r, k, t_start);
+        ok = step_ll128<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_BARRIER2) {
-        ok = step_barrier2<DT, NMAX>(a, c, s, in_r, out_r, k, t_start);
+        ok = step_barrier2<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else {
         stamp_start(t_start, k);
         ok = xrank_barrier(a, c, 2 * s, s);
+        t_end = now_ticks();
       }
       if (!ok) {
         failed = true;
@@ -915,7 +931,7 @@ __device__ __forceinline__ void ar_body(const Args& a) {
     }
     // every step returns once its output stores have completed
     if (!failed && a.ts_end != nullptr) {
-      const uint64_t t_end = now_ticks();
+
       if (c.lane == 0) {
         *ts_s = t_start;
         *ts_e = t_end;
