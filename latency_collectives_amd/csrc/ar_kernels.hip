@@ -197,6 +197,54 @@ __device__ __forceinline__ bool poll_all(const Args& a, rsrc_t own, uint32_t off
   }
 }
 
+// The same with two rounds of loads in flight, the second issued about half a coherent round trip
+// after the first: a line that lands just after one round passed the coherence point is seen by
+// the other round half a round trip later instead of a whole one. Each round is NMAX loads, so
+// "the older round has returned" is `vmcnt <= NMAX` (vector memory operations complete in issue
+// order). A round still in flight at exit writes only its own registers.
+template <int NMAX, class Ready>
+__device__ __forceinline__ bool poll_all2(const Args& a, rsrc_t own, uint32_t off0,
+                                          uint32_t qstride, uint32_t mask, u32x4 (&v)[NMAX],
+                                          Ready ready, int rank, uint64_t step) {
+  u32x4 w[NMAX];
+  auto issue = [&](u32x4 (&t)[NMAX]) {
+#pragma unroll
+    for (int q = 0; q < NMAX; ++q)
+      t[q] = ld16<kCoh>(own, ((mask >> q) & 1u) ? off0 + static_cast<uint32_t>(q) * qstride : kDrop);
+  };
+  auto all_ready = [&](const u32x4 (&t)[NMAX]) {
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < NMAX; ++q) ok = ok & (((mask >> q) & 1u) == 0u || ready(t[q]));
+    return __ballot(!ok) == 0;
+  };
+  uint32_t spins = 0;
+  uint64_t t_first = 0;
+  issue(v);
+  compiler_fence();
+  __builtin_amdgcn_s_sleep(2);
+  while (true) {
+    issue(w);  // round B of this pass, issued only here so that it never needs a copy
+    compiler_fence();
+    wait_vm<NMAX>();  // round A has returned
+    compiler_fence();
+    if (all_ready(v)) return true;
+    issue(v);
+    compiler_fence();
+    wait_vm<NMAX>();  // round B has returned
+    compiler_fence();
+    if (all_ready(w)) {
+#pragma unroll
+      for (int q = 0; q < NMAX; ++q) v[q] = w[q];
+      return true;
+    }
+    if ((++spins & 511u) == 0) {
+      t_first = poll_check(poll_env(a), t_first, rank, -1, step);
+      if (t_first == 0) return false;
+    }
+  }
+}
+
 template <int NMAX, class Ready>
 __device__ __forceinline__ bool poll_lines(const Args& a, rsrc_t own, uint32_t off0,
                                            uint32_t qstride, uint32_t pend, u32x4 (&v)[NMAX],
@@ -308,7 +356,11 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
     wait_vm<0>();
     if (sends) push_peers<NMAX>(a, r, a.ll, push_off, u32x4{x[0], x[1], elo, ehi});
     u32x4 v[NMAX];
-    if (!poll_all<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+    if constexpr (NMAX <= 8) {
+      if (!poll_all2<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+    } else {
+      if (!poll_all<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
+    }
     finish(i, act, x, v);
     wait_all_mem();
     t1 = now_ticks();
@@ -385,6 +437,8 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
     wait_vm<0>();
     if (sends) push_peers<NMAX>(a, r, a.p1, push_off, u32x4{x[0], x[1], x[2], x[3]});
     u32x4 v[NMAX];
+    // one round of polls at a time: with a second round in flight the sentinel path measured
+    // slower (the exit then waits for the other round's loads)
     if (!poll_all<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
     finish(i, act, x, v, off0);
     compiler_fence();
