@@ -264,6 +264,8 @@ def main() -> int:
     ap.add_argument("--algo", default=None)
     ap.add_argument("--placement", type=int, default=0, help="0 XCD per rank, 1 same XCD")
     ap.add_argument("--all", action="store_true", help="also run every workload; see --report")
+    ap.add_argument("--auto-sweep", action="store_true",
+                    help="only measure the one-shot / two-shot crossovers behind AR_ALGO_AUTO")
     ap.add_argument("--report", default=None, help="write the full per-size report here")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-barrier-baseline", action="store_true")
@@ -306,6 +308,10 @@ def main() -> int:
               flush=True)
         return 0
     hz = A.ar_wallclock_hz()
+    if args.auto_sweep:
+        rows = auto_sweep(A, I, hz, args.warmup, args.placement)
+        print(json.dumps({"auto_sweep": rows}), flush=True)
+        return 0
     sol = A.ar_sol(args.placement)
     print(f"# sol {json.dumps(sol)}", file=sys.stderr, flush=True)
     peak = copy_peak(A)
@@ -407,6 +413,31 @@ def main() -> int:
             json.dump(report, f, indent=1)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def auto_sweep(A, I, hz, warmup, placement, iters=100):
+    """p50 of the one-shot LL, one-shot sentinel and two-shot kernels for N in {2,3,4,8,16} and
+    per-rank sizes 128 B .. 2 MiB (fp32, uniform inputs): the measurements behind the automatic
+    algorithm choice (ar_allreduce with AR_ALGO_AUTO)."""
+    sizes = [128 << (2 * k) for k in range(7)] + [2 << 20]
+    out = []
+    for n in (2, 3, 4, 8, 16):
+        wl = dict(nranks=n, dtype="f32", dist="uniform", sigma=1.0, sizes=sizes)
+        h = A.ar_create(n, max(sizes), A.AR_FLOAT32)
+        try:
+            A.ar_set_option(h, A.AR_OPT_PLACEMENT, placement)
+            for si, size in enumerate(sizes):
+                row = {"nranks": n, "bytes": size}
+                for algo in ("oneshot_ll", "oneshot_sentinel", "twoshot"):
+                    r = bench_size(A, I, h, 6, wl, si, size, algo, iters, warmup, hz)
+                    row[algo] = round(r["p50_us"], 3)
+                best = min(("oneshot_ll", "oneshot_sentinel", "twoshot"), key=lambda a: row[a])
+                row["best"] = best
+                print(f"# sweep {json.dumps(row)}", file=sys.stderr, flush=True)
+                out.append(row)
+        finally:
+            A.ar_destroy(h)
+    return out
 
 
 def run_all(A, I, hz, warmup, placement):

@@ -46,7 +46,8 @@ typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_INT32 = 2 } ar_dtype;
  *                       design whose barrier cost the pages measure (§III.B). A baseline.
  *   AR_BARRIER_ONLY     (ar_bench only) one cross-rank barrier per iteration, no data: the
  *                       barrier latency versus N (§III.B, Fig. 3).
- *   AR_ALGO_AUTO        picks one of the above from the message size.
+ *   AR_ALGO_AUTO        picks one-shot LL, one-shot sentinel or two-shot from the rank count and
+ *                       the message size, by a table of the fastest measured on MI355X.
  * Every algorithm except AR_LL128_ATOMIC adds in rank order 0..N-1 (fp32 accumulation for
  * bf16, rounded once to nearest even; wrapping int32) and is bit-reproducible.
  * Double buffering (§IV "Bidirectional Communication Double Buffering", Fig. 4) is used by

@@ -303,14 +303,34 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
   return a;
 }
 
+// Automatic choice by rank count and message size (the pages select by size and rank count,
+// Fig. 12): the fastest of one-shot LL (L), one-shot sentinel (S) and two-shot (T) measured on
+// MI355X (`python bench.py --auto-sweep`, fp32, p50 of 100 back-to-back calls) for
+// N in {2,3,4,8,16} and 128 B .. 2 MiB per rank. A call uses the row of the smallest measured N
+// >= its N and the column of the smallest measured size >= its size; above 2 MiB, two-shot.
+constexpr int kAutoN[5] = {2, 3, 4, 8, 16};
+constexpr uint64_t kAutoBytes[8] = {128, 512, 2048, 8192, 32768, 131072, 524288, 2097152};
+constexpr char kAutoTable[5][9] = {
+    "LLSSLLSS",  // N = 2 (LL and sentinel within 10 % of each other at most sizes)
+    "LLLSLSTL",  // N = 3
+    "LLLLLSTT",  // N = 4
+    "LLLLSTTT",  // N = 8
+    "LLLSSTTT",  // N = 16
+};
+
 int resolve_algo(ar_handle* h, int algo, uint64_t nbytes) {
   if (algo != AR_ALGO_AUTO) return algo;
-  // Provisional size rule (one-shot for small messages, two-shot for large ones, as on the
-  // pages' §VIII selection); thresholds to be replaced by measured ones.
   if (h->nranks == 1) return AR_ONESHOT_SENTINEL;
-  if (nbytes <= 2048) return AR_ONESHOT_LL;
-  if (nbytes <= (256u << 10)) return AR_ONESHOT_SENTINEL;
-  return AR_TWOSHOT;
+  int row = 0;
+  while (row < 4 && kAutoN[row] < h->nranks) ++row;
+  int col = 0;
+  while (col < 8 && kAutoBytes[col] < nbytes) ++col;
+  if (col == 8) return AR_TWOSHOT;
+  switch (kAutoTable[row][col]) {
+    case 'L': return AR_ONESHOT_LL;
+    case 'S': return AR_ONESHOT_SENTINEL;
+    default: return AR_TWOSHOT;
+  }
 }
 
 bool overlap(const void* a, const void* b, uint64_t n) {

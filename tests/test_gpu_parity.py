@@ -35,6 +35,16 @@ def test_all_algorithms_ragged_counts(n, dtype):
                 assert_matches(got, x, algo, dtype)
 
 
+def test_auto_selection_matches_oracle():
+    """AR_ALGO_AUTO over rank counts and sizes that select each of its three kernels."""
+    for n in (2, 3, 4, 6, 8, 16):
+        for count in (32, 700, 5000, 40000, 300000):
+            with handle(n, count * 4, "f32") as h:
+                x = draw("f32", n, count, seed=n * 7 + count % 97)
+                got = run_allreduce(h, x, "auto")
+                assert_matches(got, x, "oneshot_ll", "f32")
+
+
 @pytest.mark.parametrize("algo", ALGO_NAMES)
 def test_in_place(algo):
     n, dtype, count = 4, "f32", 5000
