@@ -200,8 +200,11 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
   const int cus_per_xcd = std::max(1, h->cu_count / kXcds);
   L.ranks_per_xcd = h->placement == AR_PLACE_XCD ? static_cast<int>(ceil_div(N, kXcds)) : 1;
   // With N dividing 8 every rank gets 8 / N XCDs (its first workgroup stays on XCD r); the other
-  // counts leave 8 - N XCDs idle rather than split a rank unevenly.
-  L.xcds_per_rank = (h->placement == AR_PLACE_XCD && N < kXcds && kXcds % N == 0) ? kXcds / N : 1;
+  // counts leave 8 - N XCDs idle rather than split a rank unevenly. Messages in the near regions
+  // stay on the rank's first XCD: their slots are homed near that XCD's half of the chip.
+  L.xcds_per_rank = (h->placement == AR_PLACE_XCD && N < kXcds && kXcds % N == 0 && !L.near)
+                        ? kXcds / N
+                        : 1;
   // Workgroups per rank that can all be resident at once with kernel `fn`. A grid planned at the
   // occupancy limit itself (every compute unit full) was once seen not to become resident as a
   // whole (a rank-local join timed out), so one workgroup per compute unit is left free whenever
