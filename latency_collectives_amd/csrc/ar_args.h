@@ -34,22 +34,26 @@ enum Placement : int {
 
 // One protocol region inside every rank's block of the symmetric scratch allocation.
 struct Region {
-  uint64_t off;    // byte offset of the region inside a rank block
-  uint32_t bytes;  // region bytes per rank
-  uint32_t slot;   // bytes of one (buffer, source) slot (its pitch), or of one buffer for `acc`
-  uint32_t home;   // 1: a near region, whose slots start at each rank's Args::home_pos
+  uint64_t off;       // byte offset of the region inside a rank block
+  uint32_t bytes;     // region bytes per rank
+  uint32_t slot;      // bytes of one (buffer, source) slot (its pitch), or of one buffer for `acc`
+  uint64_t home_pos;  // near region: bits 4r..4r+2 = position of rank r's data in each pitch
+  uint32_t near;      // 1: a near region (slot data in 8 KiB chunks, one per 16 KiB of pitch)
   uint32_t pad;
 };
 
 // Memory homes (measured on MI355X): the device's memory is interleaved over the two halves of
 // the chip (XCDs 0-3 and 4-7) in 8 KiB granules, alternating inside every 2 MiB page. A store
 // from one XCD becomes visible to a poll from another XCD of the same half in ~370 ns when the
-// line lives in a granule of that half, ~600 ns when it lives in the other half. Near regions
-// give every small-message slot a 16 KiB pitch (one granule of each class) and keep its data in
-// one 8 KiB granule, the one homed near the receiving rank.
+// line lives in a granule of that half, ~600 ns when it lives in the other half. A near region
+// is one 2 MiB page per rank block; its slots lay their data out in 8 KiB chunks, one chunk per
+// 16 KiB of pitch (one granule of each class), always in the granule homed near the receiving
+// rank.
 constexpr uint32_t kGranule = 8192;
-constexpr uint32_t kNearPitch = 2 * kGranule;
-constexpr uint64_t kNearArea = 2ull << 20;  // the near regions of a rank block, one 2 MiB page
+constexpr uint32_t kChunkUnits = kGranule / 16;  // 16-byte units per chunk
+constexpr uint64_t kNearPage = 2ull << 20;       // one near region of a rank block
+constexpr int kNearRegions = 3;                  // LL, p1, p2
+constexpr uint64_t kNearArea = kNearRegions * kNearPage;
 // Within the pitch a rank's slot data may start at any of 8 positions (2 KiB sub-blocks of the two
 // granules; the sub-blocks of one granule differ by a few tens of ns as well).
 constexpr int kNearPositions = 8;
@@ -86,7 +90,6 @@ struct Args {
   Region cnt;   // LL128-style arrival counters [buf][cta][wave] (zeroed)
   Region bar;   // barrier flags [src][cta] (zeroed, monotonic)
   Region bdat;  // barrier-baseline data slots [src] (single buffer, plain)
-  uint64_t home_pos;    // bits 4r..4r+2: position of rank r's slot data in each near pitch
   uint32_t* ctl;        // device control words
   uint32_t* status;     // host-mapped status words (pinned host memory)
   uint64_t* ts_start;   // optional [iters][nranks][ctas][waves] timestamps

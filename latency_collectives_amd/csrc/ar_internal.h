@@ -13,11 +13,11 @@ ar_kernel_fn ar_select_kernel(int algo, int dt, int nmax);
 void ar_launch_fill(uint8_t* base, uint64_t stride, int nranks, uint64_t off, uint32_t bytes,
                     uint32_t word, hipStream_t stream);
 
-// Defined in ar_sol.hip: calibrate every rank block's near area (the first kNearArea bytes of
-// each block, 2 MiB aligned, zero): ns[r][p][k] = store -> poll half round trip between XCDs 2p
-// and 2p+1 at position k (granule k / 4, 2 KiB sub-block k % 4).
+// Defined in ar_sol.hip: calibrate every near page of every rank block (the first kNearArea
+// bytes of each block, 2 MiB aligned, zero): ns[r][g][p][k] = store -> poll half round trip
+// between XCDs 2p and 2p+1 at position k (granule k / 4, 2 KiB sub-block k % 4) of page g.
 int ar_near_positions(uint8_t* base, uint64_t stride, int nranks,
-                      float (*ns)[4][ar::kNearPositions]);
+                      float (*ns)[ar::kNearRegions][4][ar::kNearPositions]);
 
 // Defined in ar_host.hip: record an error message for ar_last_error() and return `code`.
 int ar_fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

@@ -68,8 +68,14 @@ __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_re
 // Start of region g in rank `rank`'s block; in a near region every slot's data starts at the
 // rank's position inside the slot's pitch.
 __device__ __forceinline__ uint8_t* region_base(const Args& a, int rank, const Region& g) {
-  const uint32_t pos = g.home * static_cast<uint32_t>((a.home_pos >> (4 * rank)) & 7u);
+  const uint32_t pos = static_cast<uint32_t>((g.home_pos >> (4 * rank)) & 7u);
   return a.base + static_cast<uint64_t>(rank) * a.stride + g.off + pos * kNearSub;
+}
+
+// Byte offset of 16-byte unit i inside a slot: contiguous in the regular regions; in a near
+// region, chunks of kChunkUnits units, one per 16 KiB (2 granules) of the slot's pitch.
+__device__ __forceinline__ uint32_t slot_off(const Region& g, uint32_t i) {
+  return g.near ? ((i / kChunkUnits) * (2 * kGranule) + (i % kChunkUnits) * 16u) : i * 16u;
 }
 
 __device__ __forceinline__ rsrc_t region_rsrc(const Args& a, int rank, const Region& g) {
@@ -343,9 +349,9 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
     // one pass: the plan gives this rank at least one lane per unit of the chunk
     const uint32_t i = c.t0 + c.lane;
     const bool act = i < CU;
-    uint32_t off0 = b * N * slot + i * 16u;
+    uint32_t off0 = b * N * slot + slot_off(a.ll, i);
     uint32_t in_off = act ? (unit0 + i) * 8u : kDrop;
-    uint32_t push_off = act ? mine + i * 16u : kDrop;
+    uint32_t push_off = act ? mine + slot_off(a.ll, i) : kDrop;
     pin(off0);
     pin(in_off);
     pin(push_off);
@@ -374,7 +380,8 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
         const bool act = i < CU;
         uint32_t w[2];
         load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, w);
-        push_peers<NMAX>(a, r, a.ll, act ? mine + i * 16u : kDrop, u32x4{w[0], w[1], elo, ehi});
+        push_peers<NMAX>(a, r, a.ll, act ? mine + slot_off(a.ll, i) : kDrop,
+                         u32x4{w[0], w[1], elo, ehi});
       }
     }
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
@@ -383,7 +390,8 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
       uint32_t x[2];
       load_unit<DT, 8>(in_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, x);
       u32x4 v[NMAX];
-      if (!poll_lines<NMAX>(a, own, b * N * slot + i * 16u, slot, act ? peers : 0u, v, ready, r, s))
+      if (!poll_lines<NMAX>(a, own, b * N * slot + slot_off(a.ll, i), slot, act ? peers : 0u, v,
+                            ready, r, s))
         return false;
       finish(i, act, x, v);
     }
@@ -424,9 +432,9 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
     // one pass: the plan gives this rank at least one lane per unit of the chunk
     const uint32_t i = c.t0 + c.lane;
     const bool act = i < CU;
-    uint32_t off0 = b * N * slot + i * 16u;
+    uint32_t off0 = b * N * slot + slot_off(a.p1, i);
     uint32_t in_off = act ? (unit0 + i) * 16u : kDrop;
-    uint32_t push_off = act ? mine + i * 16u : kDrop;
+    uint32_t push_off = act ? mine + slot_off(a.p1, i) : kDrop;
     pin(off0);
     pin(in_off);
     pin(push_off);
@@ -454,13 +462,14 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
         const bool act = i < CU;
         uint32_t w[4];
         load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, w);
-        push_peers<NMAX>(a, r, a.p1, act ? mine + i * 16u : kDrop, u32x4{w[0], w[1], w[2], w[3]});
+        push_peers<NMAX>(a, r, a.p1, act ? mine + slot_off(a.p1, i) : kDrop,
+                         u32x4{w[0], w[1], w[2], w[3]});
       }
     }
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
       const bool act = i < CU;
-      const uint32_t off0 = b * N * slot + i * 16u;
+      const uint32_t off0 = b * N * slot + slot_off(a.p1, i);
       uint32_t x[4];
       load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
       u32x4 v[NMAX];
@@ -541,8 +550,8 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
     const uint32_t i = c.t0 + c.lane;
     const bool act = i < CU;
     const uint32_t mask = act ? peers : 0u;
-    uint32_t off1 = b * N * slot1 + i * 16u;
-    const uint32_t off2 = b * N * slot2 + i * 16u;
+    uint32_t off1 = b * N * slot1 + slot_off(a.p1, i);
+    const uint32_t off2 = b * N * slot2 + slot_off(a.p2, i);
     const uint32_t uoff = (r * P + k * CU + i) * 16u;
     pin(off1);
     stamp_start(t0, k);
@@ -551,7 +560,7 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
     compiler_fence();
     wait_vm<0>();
     if (sends) {
-      const uint32_t off = act ? mine1 + i * 16u : kDrop;
+      const uint32_t off = act ? mine1 + slot_off(a.p1, i) : kDrop;
 #pragma unroll
       for (int j = 1; j < NMAX; ++j)
         st16<kCoh>(peer_rsrc(a, r, j, a.p1), off, u32x4{w[j][0], w[j][1], w[j][2], w[j][3]});
@@ -560,7 +569,9 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
     if (!poll_all<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
     uint32_t o[4];
     fold_rank_order<DT, NMAX, 4>(N, r, w[0], v, o);
-    if (sends) push_peers<NMAX>(a, r, a.p2, act ? mine2 + i * 16u : kDrop, u32x4{o[0], o[1], o[2], o[3]});
+    if (sends)
+      push_peers<NMAX>(a, r, a.p2, act ? mine2 + slot_off(a.p2, i) : kDrop,
+                       u32x4{o[0], o[1], o[2], o[3]});
     store_unit<DT, 16>(out_r, act ? uoff : kDrop, a.nbytes, o);
     rearm<NMAX>(own1, off1, slot1, mask, sent);
     u32x4 v2[NMAX];
@@ -601,7 +612,7 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
       const bool act = i < CU;
       uint32_t w[NMAX][4];
       load_partitions<DT, NMAX, kNt>(a, r, in_r, k, i, act, 1, w);
-      const uint32_t off = act ? mine1 + i * 16u : kDrop;
+      const uint32_t off = act ? mine1 + slot_off(a.p1, i) : kDrop;
 #pragma unroll
       for (int j = 1; j < NMAX; ++j)
         st16<kCoh>(peer_rsrc(a, r, j, a.p1), off, u32x4{w[j][0], w[j][1], w[j][2], w[j][3]});
@@ -611,7 +622,7 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
     const uint32_t i = i0 + c.lane;
     const bool act = i < CU;
     const uint32_t mask = act ? peers : 0u;
-    const uint32_t off1 = b * N * slot1 + i * 16u;
+    const uint32_t off1 = b * N * slot1 + slot_off(a.p1, i);
     const uint32_t uoff = (r * P + k * CU + i) * 16u;
     uint32_t x[4];
     load_unit<DT, 16, kNt>(in_r, act ? uoff : kDrop, a.nbytes, x);
@@ -619,7 +630,9 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
     if (!poll_all<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
     uint32_t o[4];
     fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
-    if (sends) push_peers<NMAX>(a, r, a.p2, act ? mine2 + i * 16u : kDrop, u32x4{o[0], o[1], o[2], o[3]});
+    if (sends)
+      push_peers<NMAX>(a, r, a.p2, act ? mine2 + slot_off(a.p2, i) : kDrop,
+                       u32x4{o[0], o[1], o[2], o[3]});
     store_unit<DT, 16, kNt>(out_r, act ? uoff : kDrop, a.nbytes, o);
     rearm<NMAX>(own1, off1, slot1, mask, sent);
   }
@@ -627,7 +640,7 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
     const uint32_t i = i0 + c.lane;
     const bool act = i < CU;
     const uint32_t mask = act ? peers : 0u;
-    const uint32_t off2 = b * N * slot2 + i * 16u;
+    const uint32_t off2 = b * N * slot2 + slot_off(a.p2, i);
     u32x4 v[NMAX];
     if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v, ready, r, s)) return false;
     allgather_out<DT, NMAX, kNt>(a, r, out_r, own2, off2, mask, k, i, v, sent);
@@ -723,7 +736,7 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
                   static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
       }
       if (r != a.withhold)
-        push_peers<NMAX>(a, r, a.p2, act ? (b * N + r) * slot2 + i * 16u : kDrop, v);
+        push_peers<NMAX>(a, r, a.p2, act ? (b * N + r) * slot2 + slot_off(a.p2, i) : kDrop, v);
       const uint32_t o[4] = {v.x, v.y, v.z, v.w};
       store_unit<DT, 16>(out_r, act ? (r * P + k * CU + i) * 16u : kDrop, a.nbytes, o);
     }
@@ -733,7 +746,7 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
     const uint32_t i = i0 + c.lane;
     const bool act = i < CU;
     const uint32_t mask = act ? peers : 0u;
-    const uint32_t off2 = b * N * slot2 + i * 16u;
+    const uint32_t off2 = b * N * slot2 + slot_off(a.p2, i);
     u32x4 v[NMAX];
     if (!poll_lines<NMAX>(a, own2, off2, slot2, mask, v, ready, r, s)) return false;
     allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v, sent);

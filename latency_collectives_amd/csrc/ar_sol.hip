@@ -273,10 +273,10 @@ struct PageBuf {
   DevBuf raw;
   uint8_t* p = nullptr;
   int alloc(uint64_t bytes) {
-    AR_HIP(hipMalloc(&raw.p, bytes + ar::kNearArea));
+    AR_HIP(hipMalloc(&raw.p, bytes + ar::kNearPage));
     const uintptr_t x = reinterpret_cast<uintptr_t>(raw.p);
-    p = reinterpret_cast<uint8_t*>((x + ar::kNearArea - 1) / ar::kNearArea * ar::kNearArea);
-    AR_HIP(hipMemset(raw.p, 0, bytes + ar::kNearArea));
+    p = reinterpret_cast<uint8_t*>((x + ar::kNearPage - 1) / ar::kNearPage * ar::kNearPage);
+    AR_HIP(hipMemset(raw.p, 0, bytes + ar::kNearPage));
     return AR_OK;
   }
 };
@@ -347,14 +347,16 @@ int run_chase(uint64_t bytes, int hops, bool warm_full, double* ns) {
 }  // namespace
 
 int ar_near_positions(uint8_t* base, uint64_t stride, int nranks,
-                      float (*ns)[4][ar::kNearPositions]) {
-  // For every rank block's near area and every pair of XCDs {2p, 2p+1}: the half round trip of
-  // the pair's ping-pong at each of the positions. The area is zero before and after.
+                      float (*ns)[ar::kNearRegions][4][ar::kNearPositions]) {
+  // For every near page of every rank block and every pair of XCDs {2p, 2p+1}: the half round
+  // trip of the pair's ping-pong at each of the positions. The pages are zero before and after.
   for (int r = 0; r < nranks; ++r) {
-    uint8_t* page = base + static_cast<uint64_t>(r) * stride;
-    for (int p = 0; p < 4; ++p) {
-      const int rc = pingpong_positions(page, 2 * p, 2 * p + 1, 24, ns[r][p]);
-      if (rc != AR_OK) return rc;
+    for (int g = 0; g < ar::kNearRegions; ++g) {
+      uint8_t* page = base + static_cast<uint64_t>(r) * stride + g * ar::kNearPage;
+      for (int p = 0; p < 4; ++p) {
+        const int rc = pingpong_positions(page, 2 * p, 2 * p + 1, 24, ns[r][g][p]);
+        if (rc != AR_OK) return rc;
+      }
     }
   }
   return AR_OK;
@@ -400,7 +402,7 @@ int ar_sol(int placement, ar_sol_result* res) {
   int xcc[2] = {-1, -1};
   {
     PageBuf page;
-    if ((rc = page.alloc(ar::kNearArea)) != AR_OK) return rc;
+    if ((rc = page.alloc(ar::kNearPage)) != AR_OK) return rc;
     int a = 0, b = 0;
     pair_blocks(placement, a, b);
     float half[ar::kNearPositions];
