@@ -35,25 +35,6 @@ METRIC = "p50 AllReduce latency µs @128B–1MB; algBW GB/s @≥16MB (1 GPU)"
 HBM_PEAK_GBPS = 8000.0
 
 
-def alg_bytes(algo: str, n: int, s: int) -> int:
-    """Algorithmic bytes one AllReduce moves (all ranks; s bytes per rank), counting each
-    logical read and write once: inputs read, pushes written, polled slots read, re-arm writes,
-    outputs written. LL lines carry 8 payload bytes in 16."""
-    if algo == "oneshot_ll":
-        return 2 * n * s + 4 * n * (n - 1) * s
-    if algo == "oneshot_sentinel":
-        return 2 * n * s + 3 * n * (n - 1) * s
-    if algo == "twoshot":
-        return (n + 1) * s + 7 * (n - 1) * s
-    if algo == "ll128_atomic":
-        # inputs read, one atomic update per input element, owner read + clear, own output,
-        # all-gather write, read, re-arm, output
-        return 2 * n * s + 2 * s + s + 4 * (n - 1) * s
-    if algo == "barrier2":
-        return 2 * n * s + 2 * n * (n - 1) * s
-    return 0
-
-
 def _to_device(x):
     import torch
 
@@ -129,7 +110,7 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
         "launch_ms": float(ms),
         "launch_inclusive_us": float(launch_us),
         "iters": iters,
-        "alg_bytes_per_call": alg_bytes(algo, n, size),
+        "alg_bytes_per_call": A.ar_alg_bytes(h, count, aid),
     }
     res["algbw_GBps"] = size / (res["p50_us"] * 1e-6) / 1e9
     res["busbw_like_GBps"] = res["alg_bytes_per_call"] * iters / (ms * 1e-3) / 1e9 if ms > 0 else 0
@@ -391,7 +372,7 @@ def main() -> int:
             "launches": launches,
             "mean_launch_ms": total_launch_ms / launches,
             "kernel": f"ar_kernel<{algo}, {wl['dtype']}, N={wl['nranks']}>",
-            "bytes_definition": ("alg_bytes() per AllReduce x iterations per launch; achieved = "
+            "bytes_definition": ("ar_alg_bytes() per AllReduce x iterations per launch; achieved = "
                                  "bytes over all timed launches / their summed event time"),
             "traffic_definition": ("rocprofv3 FETCH_SIZE + WRITE_SIZE per timed launch, each "
                                    "scaled by the streaming copy's counter-to-bytes factor "

@@ -173,9 +173,22 @@ int ar_set_option(ar_handle* h, ar_option opt, int64_t value);
  *   2 = LL lines  3 = atomic destination  4 = arrival counters  5 = barrier flags
  *   6 = barrier-baseline data
  *   7, 8, 9 = the near LL, one-shot / reduce-scatter and all-gather regions that small messages
- *   use (slots of at most 8 KiB at a 16 KiB pitch, each in the granule homed near its rank)
+ *   use (slot data in 8 KiB chunks, each in the granule homed near its rank)
+ *   10, 11 = bulk two-shot reduce-scatter and all-gather data slots  12 = their completion flags
  */
 int64_t ar_region_bytes(ar_handle* h, int region);
+
+/*
+ * ar_alg_bytes: the algorithmic bytes one ar_allreduce of `count` elements with `algo` moves on
+ * handle h, summed over all ranks, for the kernel and protocol the library would launch: every
+ * logical read and write counted once (inputs, pushes to peers, slot reads, sentinel re-arms,
+ * outputs; an LL line is 16 bytes per 8 bytes of payload). One-shot LL 2NS + 4N(N-1)S; one-shot
+ * sentinel 2NS + 3N(N-1)S; two-shot (one pass) (N+1)S + 7(N-1)S; two-shot (bulk, completion
+ * flags) (N+1)S + 5(N-1)S; LL128-style 2NS + 3S + 4(N-1)S; two-barrier 2NS + 2N(N-1)S, with S
+ * the bytes per rank. Returns the count, or a negative error code (bad handle or algorithm,
+ * AR_ETOOBIG).
+ */
+int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo);
 int ar_read_region(ar_handle* h, int rank, int region, void* host_dst, size_t bytes);
 
 /* Sequence number the next step will use. */

@@ -24,7 +24,7 @@ AR_PLACE_XCD, AR_PLACE_SAME, AR_PLACE_LINEAR = 0, 1, 2
 (AR_OPT_TIMEOUT_US, AR_OPT_WITHHOLD_RANK, AR_OPT_CTAS, AR_OPT_THREADS, AR_OPT_PLACEMENT,
  AR_OPT_DRIFT) = range(6)
 (REGION_P1, REGION_P2, REGION_LL, REGION_ACC, REGION_CNT, REGION_BAR, REGION_BDAT,
- REGION_LL_NEAR, REGION_P1_NEAR, REGION_P2_NEAR) = range(10)
+ REGION_LL_NEAR, REGION_P1_NEAR, REGION_P2_NEAR, REGION_PF1, REGION_PF2, REGION_FLG) = range(13)
 
 ALGOS = {
     "auto": AR_ALGO_AUTO,
@@ -40,7 +40,8 @@ DTYPES = {"f32": AR_FLOAT32, "bf16": AR_BFLOAT16, "i32": AR_INT32}
 # Every symbol include/ar.h declares.
 EXPORTS = (
     "ar_create", "ar_allreduce", "ar_destroy", "ar_last_error", "ar_check", "ar_bench",
-    "ar_wallclock_hz", "ar_set_option", "ar_region_bytes", "ar_read_region", "ar_epoch",
+    "ar_wallclock_hz", "ar_set_option", "ar_region_bytes", "ar_alg_bytes", "ar_read_region",
+    "ar_epoch",
     "ar_sol", "ar_pingpong", "ar_torn_lines", "ar_stream_copy",
 )
 
@@ -100,6 +101,7 @@ def lib() -> ctypes.CDLL:
         "ar_wallclock_hz": ([], ctypes.c_double),
         "ar_set_option": ([vp, i32, i64], i32),
         "ar_region_bytes": ([vp, i32], i64),
+        "ar_alg_bytes": ([vp, sz, i32], i64),
         "ar_read_region": ([vp, i32, i32, vp, sz], i32),
         "ar_epoch": ([vp], u64),
         "ar_sol": ([i32, ctypes.POINTER(ar_sol_result)], i32),
@@ -196,6 +198,13 @@ def ar_wallclock_hz() -> float:
 
 def ar_set_option(h: int, opt: int, value: int) -> None:
     _ok(lib().ar_set_option(h, int(opt), int(value)))
+
+
+def ar_alg_bytes(h: int, count: int, algo: int) -> int:
+    v = int(lib().ar_alg_bytes(h, int(count), int(algo)))
+    if v < 0:
+        raise ArError(v, ar_last_error())
+    return v
 
 
 def ar_region_bytes(h: int, region: int) -> int:

@@ -90,6 +90,9 @@ struct Args {
   Region cnt;   // LL128-style arrival counters [buf][cta][wave] (zeroed)
   Region bar;   // barrier flags [src][cta] (zeroed, monotonic)
   Region bdat;  // barrier-baseline data slots [src] (single buffer, plain)
+  Region pf1;   // bulk two-shot reduce-scatter slots (data only; completion flags below)
+  Region pf2;   // bulk two-shot all-gather slots
+  Region flg;   // bulk two-shot completion flags [phase 2][src][cta][wave] u64 (zeroed, monotonic)
   uint32_t* ctl;        // device control words
   uint32_t* status;     // host-mapped status words (pinned host memory)
   uint64_t* ts_start;   // optional [iters][nranks][ctas][waves] timestamps

@@ -10,6 +10,9 @@
 //   cnt  [buffer 2][cta][wave] u32    zero       LL128-style arrival counters
 //   bar  [source][cta] u64            zero       barrier flags (monotonic)
 //   bdat [source N][slot]             any        barrier-baseline data slots
+//   pf1  [buffer 2][source N][slot]   any        bulk two-shot reduce-scatter slots
+//   pf2  [buffer 2][source N][slot]   any        bulk two-shot all-gather slots
+//   flg  [phase 2][source][cta][wave] zero       bulk two-shot completion flags (monotonic)
 // Every block starts with three 2 MiB near pages holding copies of ll, p1 and p2 for messages
 // whose 2 * N slots fit a page: slot data in 8 KiB chunks, one per 16 KiB of pitch, each in the
 // granule homed in the rank's XCD half (per-page positions calibrated at creation, ar_args.h).
@@ -34,10 +37,11 @@ namespace {
 
 thread_local std::string g_err;
 
-constexpr int kRegions = 10;
+constexpr int kRegions = 13;
 enum RegionId {
   RG_P1 = 0, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT,
   RG_LLN, RG_P1N, RG_P2N,  // near copies of ll, p1, p2 for small messages
+  RG_PF1, RG_PF2, RG_FLG,  // bulk two-shot data slots and completion flags
 };
 constexpr uint64_t kDefaultCap = 256ull << 20;
 constexpr uint64_t kMaxCap = 1ull << 30;  // keeps every region below the drop offset (2 GiB)
@@ -131,6 +135,7 @@ namespace {
 
 struct Launch {
   ar_kernel_fn fn = nullptr;
+  int kernel_algo = 0;  // the kernel family actually launched (public or internal algorithm id)
   int chunks = 1;
   uint32_t chunk_units = 0;
   uint32_t part_units = 0;
@@ -148,6 +153,7 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
   const int N = h->nranks;
   const int nmax = N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16;
   L.fn = ar_select_kernel(algo, h->dtype, nmax);
+  L.kernel_algo = algo;
   if (L.fn == nullptr)
     return ar_fail(AR_ENOTSUP, "algorithm %d is not provided for dtype %d", algo, h->dtype);
   uint64_t cap_units = 0, units = 0;
@@ -167,7 +173,9 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
     case AR_TWOSHOT:
     case AR_LL128_ATOMIC:
       units = ceil_div(ceil_div(nbytes, 16), N);  // one partition
-      cap_units = std::min({h->rg[RG_P1].slot, h->rg[RG_P2].slot, h->rg[RG_ACC].slot}) / 16;
+      cap_units = std::min({h->rg[RG_P1].slot, h->rg[RG_P2].slot, h->rg[RG_ACC].slot,
+                            h->rg[RG_PF1].slot, h->rg[RG_PF2].slot}) /
+                  16;
       break;
     case AR_BARRIER_ONLY:
       units = 0;
@@ -238,6 +246,7 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
                       : algo == AR_ONESHOT_SENTINEL  ? ar::ALGO_ONESHOT_SENTINEL_MULTI
                                                      : 0;
     if (multi != 0) {
+      L.kernel_algo = multi;
       L.fn = ar_select_kernel(multi, h->dtype, nmax);
       max_ctas = co_resident(L.fn);
       ctas = pick_ctas(max_ctas);
@@ -292,6 +301,9 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
   a.cnt = h->rg[RG_CNT];
   a.bar = h->rg[RG_BAR];
   a.bdat = h->rg[RG_BDAT];
+  a.pf1 = h->rg[RG_PF1];
+  a.pf2 = h->rg[RG_PF2];
+  a.flg = h->rg[RG_FLG];
   a.ctl = h->ctl;
   a.status = h->status_dev;
   a.e0 = h->epoch;
@@ -448,6 +460,9 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
   sz[RG_CNT] = {0, 2ull * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 4};
   sz[RG_BAR] = {0, 1ull * ar::kMaxRanks * ar::kMaxCtasPerRank * 8};
   sz[RG_BDAT] = {slot_os, 1ull * N * slot_os};
+  sz[RG_PF1] = {slot_ts, 2ull * N * slot_ts};
+  sz[RG_PF2] = {slot_ts, 2ull * N * slot_ts};
+  sz[RG_FLG] = {0, 2ull * ar::kMaxRanks * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 8};
   // near area: the near ll, p1 and p2 regions, one 2 MiB page each (pitch set per launch)
   uint64_t off = 0;
   for (int i = RG_LLN; i <= RG_P2N; ++i) {
@@ -457,7 +472,7 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
     h->rg[i].near = 1;
     off += ar::kNearPage;
   }
-  for (int i = 0; i < RG_LLN; ++i) {
+  for (int i : {RG_P1, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT, RG_PF1, RG_PF2, RG_FLG}) {
     if (sz[i].bytes >= (1ull << 31)) {
       ar_fail(AR_ETOOBIG, "scratch region %d would exceed 2 GiB per rank", i);
       release(h);
@@ -718,6 +733,33 @@ int ar_bench(ar_handle* h, const void* const* in_sets, void* const* out_sets, in
     }
   }
   return AR_OK;
+}
+
+int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
+  if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
+  if (algo < AR_ALGO_AUTO || algo > AR_BARRIER2)
+    return ar_fail(AR_EINVAL, "algorithm %d is not valid", static_cast<int>(algo));
+  const uint64_t S = static_cast<uint64_t>(count) * elem_bytes(h->dtype);
+  if (S > h->max_bytes) return ar_fail(AR_ETOOBIG, "message exceeds max_bytes");
+  if (S == 0) return 0;
+  const int alg = resolve_algo(h, algo, S);
+  Launch L;
+  const int rc = plan(h, alg, S, L);
+  if (rc != AR_OK) return rc;
+  const uint64_t N = static_cast<uint64_t>(h->nranks);
+  // every logical read and write once: inputs, pushes, slot reads, re-arms, outputs
+  switch (L.kernel_algo) {
+    case AR_ONESHOT_LL:
+    case ar::ALGO_ONESHOT_LL_MULTI: return static_cast<int64_t>(2 * N * S + 4 * N * (N - 1) * S);
+    case AR_ONESHOT_SENTINEL:
+    case ar::ALGO_ONESHOT_SENTINEL_MULTI:
+      return static_cast<int64_t>(2 * N * S + 3 * N * (N - 1) * S);
+    case AR_TWOSHOT: return static_cast<int64_t>((N + 1) * S + 7 * (N - 1) * S);
+    case ar::ALGO_TWOSHOT_BULK: return static_cast<int64_t>((N + 1) * S + 5 * (N - 1) * S);
+    case AR_LL128_ATOMIC: return static_cast<int64_t>(2 * N * S + 3 * S + 4 * (N - 1) * S);
+    case AR_BARRIER2: return static_cast<int64_t>(2 * N * S + 2 * N * (N - 1) * S);
+    default: return 0;
+  }
 }
 
 int64_t ar_region_bytes(ar_handle* h, int region) {

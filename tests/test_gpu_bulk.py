@@ -205,3 +205,19 @@ def test_full_size_c5_rank_constant():
         A.ar_check(h)
         for r in range(n):
             assert bool(torch.all(outs[r] == n * (n - 1) // 2)), f"rank {r}"
+
+
+def test_alg_bytes_follow_the_launched_kernel():
+    """ar_alg_bytes counts each logical read and write once for the protocol actually used: the
+    one-pass two-shot re-arms sentinels (58 S at N = 8), the bulk two-shot uses completion flags
+    (44 S)."""
+    from latency_collectives_amd import _ar as A
+
+    n = 8
+    with handle(n, 64 << 20, "f32") as h:
+        s_small, s_big = 4096 * 4, 16 << 20
+        assert A.ar_alg_bytes(h, s_small // 4, A.AR_TWOSHOT) == (n + 1) * s_small + 7 * (n - 1) * s_small
+        assert A.ar_alg_bytes(h, s_big // 4, A.AR_TWOSHOT) == (n + 1) * s_big + 5 * (n - 1) * s_big
+        assert A.ar_alg_bytes(h, 1000, A.AR_ONESHOT_LL) == 2 * n * 4000 + 4 * n * (n - 1) * 4000
+        assert A.ar_alg_bytes(h, 0, A.AR_ONESHOT_SENTINEL) == 0
+
