@@ -193,7 +193,7 @@ __device__ __forceinline__ bool poll_all(const Args& a, rsrc_t own, uint32_t off
     compiler_fence();
     bool ok = true;
 #pragma unroll
-    for (int q = 0; q < NMAX; ++q) ok = ok & (((mask >> q) & 1u) == 0u || ready(v[q]));
+    for (int q = 0; q < NMAX; ++q) ok = ok & ((((mask >> q) & 1u) == 0u) | ready(v[q]));
     const uint64_t waiting = __ballot(!ok);
     if (waiting == 0) return true;
     if ((++spins & 1023u) == 0) {
@@ -221,7 +221,7 @@ __device__ __forceinline__ bool poll_all2(const Args& a, rsrc_t own, uint32_t of
   auto all_ready = [&](const u32x4 (&t)[NMAX]) {
     bool ok = true;
 #pragma unroll
-    for (int q = 0; q < NMAX; ++q) ok = ok & (((mask >> q) & 1u) == 0u || ready(t[q]));
+    for (int q = 0; q < NMAX; ++q) ok = ok & ((((mask >> q) & 1u) == 0u) | ready(t[q]));
     return __ballot(!ok) == 0;
   };
   uint32_t spins = 0;
