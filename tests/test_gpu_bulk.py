@@ -74,13 +74,15 @@ def test_bulk_twoshot_withheld_rank_times_out():
         assert e.value.code == A.AR_ETIMEOUT
 
 
-def test_bulk_twoshot_persistent_loop():
-    """Several bulk AllReduces in one persistent launch (credits across iterations)."""
+@pytest.mark.parametrize("drift", [0, 3])
+def test_bulk_twoshot_persistent_loop(drift):
+    """Several bulk AllReduces in one persistent launch (completion flags and double-buffer
+    credits across iterations), optionally with a random per-rank delay before each iteration."""
     from latency_collectives_amd import _ar as A
     import torch
 
     n, dtype, count, iters = 8, "bf16", 100001, 6
-    with handle(n, count * 2, dtype, ctas=2) as h:
+    with handle(n, count * 2, dtype, ctas=2, drift=drift) as h:
         xs = [draw(dtype, n, count, seed=900 + k) for k in range(iters)]
         ins, outs = [], []
         for x in xs:
@@ -220,4 +222,24 @@ def test_alg_bytes_follow_the_launched_kernel():
         assert A.ar_alg_bytes(h, s_big // 4, A.AR_TWOSHOT) == (n + 1) * s_big + 5 * (n - 1) * s_big
         assert A.ar_alg_bytes(h, 1000, A.AR_ONESHOT_LL) == 2 * n * 4000 + 4 * n * (n - 1) * 4000
         assert A.ar_alg_bytes(h, 0, A.AR_ONESHOT_SENTINEL) == 0
+
+
+def test_launch_shape_beyond_co_residency_is_refused():
+    """Asking for more workgroups per rank than can be resident at once fails with AR_ENORES
+    before anything is launched (a persistent grid that is not co-resident would never finish)."""
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    n, count = 16, 1 << 20
+    with handle(n, count * 4, "f32", ctas=256) as h:
+        x = [torch.zeros(count, device="cuda") for _ in range(n)]
+        y = [torch.empty_like(t) for t in x]
+        with pytest.raises(A.ArError) as e:
+            A.ar_allreduce(h, x, y, count, A.AR_ONESHOT_SENTINEL)
+        assert e.value.code == A.AR_ENORES
+        # the handle stays usable with the automatic shape
+        A.ar_set_option(h, A.AR_OPT_CTAS, 0)
+        A.ar_allreduce(h, x, y, count, A.AR_ONESHOT_SENTINEL)
+        A.ar_check(h)
+        assert bool(torch.all(y[3] == 0))
 
