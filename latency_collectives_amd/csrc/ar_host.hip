@@ -185,78 +185,85 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
       return ar_fail(AR_EINVAL, "unknown algorithm %d", algo);
   }
   if (cap_units == 0) return ar_fail(AR_EINVAL, "scratch slots are too small");
-  const uint64_t K = units == 0 ? 1 : ceil_div(units, cap_units);
-  uint64_t C = units == 0 ? 0 : ceil_div(units, K);
-  L.chunks = static_cast<int>(K);
-  L.chunk_units = static_cast<uint32_t>(C);
-  L.part_units = static_cast<uint32_t>(K * C);
   // Messages whose 2 * N slots fit a near page in one chunk use the near regions: the slot data
   // (16 bytes per unit) goes in 8 KiB chunks at a pitch of 16 KiB per chunk.
   const uint64_t near_chunks = ceil_div(units, ar::kChunkUnits);
-  L.near = units > 0 && 2ull * N * near_chunks * 2 * ar::kGranule <= ar::kNearPage &&
-           (algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL || algo == AR_TWOSHOT ||
-            (algo == AR_LL128_ATOMIC && units <= h->rg[RG_ACC].slot / 16));
-  if (L.near) {
-    L.chunks = 1;
-    L.chunk_units = static_cast<uint32_t>(units);
-    L.part_units = static_cast<uint32_t>(units);
-    C = units;
-  }
-  // Small chunks: one workgroup just wide enough that no wave is idle; larger ones: 256-thread
-  // workgroups, one unit per lane per pass.
-  L.threads = h->threads ? h->threads
-                         : (C <= 256 ? static_cast<int>(std::max<uint64_t>(64, round_up(C, 64)))
-                                     : 256);
+  const bool near_fits = units > 0 && 2ull * N * near_chunks * 2 * ar::kGranule <= ar::kNearPage &&
+                         (algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL ||
+                          algo == AR_TWOSHOT ||
+                          (algo == AR_LL128_ATOMIC && units <= h->rg[RG_ACC].slot / 16));
   const int cus_per_xcd = std::max(1, h->cu_count / kXcds);
   L.ranks_per_xcd = h->placement == AR_PLACE_XCD ? static_cast<int>(ceil_div(N, kXcds)) : 1;
-  // With N dividing 8 every rank gets 8 / N XCDs (its first workgroup stays on XCD r); the other
-  // counts leave 8 - N XCDs idle rather than split a rank unevenly. Messages in the near regions
-  // stay on the rank's first XCD: their slots are homed near that XCD's half of the chip.
-  L.xcds_per_rank = (h->placement == AR_PLACE_XCD && N < kXcds && kXcds % N == 0 && !L.near)
-                        ? kXcds / N
-                        : 1;
-  // Workgroups per rank that can all be resident at once with kernel `fn`. A grid planned at the
-  // occupancy limit itself (every compute unit full) was once seen not to become resident as a
-  // whole (a rank-local join timed out), so one workgroup per compute unit is left free whenever
-  // the kernel fits more than one.
-  auto co_resident = [&](ar_kernel_fn fn) {
-    const int occ_api = occupancy(fn, L.threads);
-    const int occ = occ_api > 1 ? occ_api - 1 : occ_api;
-    int m;
-    if (h->placement == AR_PLACE_XCD)
-      m = cus_per_xcd * occ * L.xcds_per_rank / L.ranks_per_xcd;
-    else if (h->placement == AR_PLACE_SAME)
-      m = cus_per_xcd * occ / N;
-    else
-      m = h->cu_count * occ / N;
-    return std::min(m, ar::kMaxCtasPerRank);
-  };
-  auto pick_ctas = [&](int max_ctas) {
-    if (h->ctas) return h->ctas;
-    const uint64_t want = std::max<uint64_t>(1, ceil_div(C, static_cast<uint64_t>(L.threads)));
-    return static_cast<int>(std::min<uint64_t>(want, static_cast<uint64_t>(max_ctas)));
-  };
-  int max_ctas = co_resident(L.fn);
-  int ctas = pick_ctas(max_ctas);
-  if (static_cast<uint64_t>(ctas) * L.threads < C) {
-    // The chunk does not fit one pass of the rank's lanes: the kernels built for one pass (the
-    // latency path) hand it to their multi-pass counterparts.
-    const int multi = algo == AR_TWOSHOT             ? ar::ALGO_TWOSHOT_BULK
-                      : algo == AR_ONESHOT_LL        ? ar::ALGO_ONESHOT_LL_MULTI
-                      : algo == AR_ONESHOT_SENTINEL  ? ar::ALGO_ONESHOT_SENTINEL_MULTI
-                                                     : 0;
-    if (multi != 0) {
-      L.kernel_algo = multi;
-      L.fn = ar_select_kernel(multi, h->dtype, nmax);
-      max_ctas = co_resident(L.fn);
-      ctas = pick_ctas(max_ctas);
+  // Chunk geometry, workgroup shape and kernel for the near or the regular slots.
+  auto shape = [&](bool near) -> int {
+    L.fn = ar_select_kernel(algo, h->dtype, nmax);
+    L.kernel_algo = algo;
+    L.near = near;
+    const uint64_t K = near || units == 0 ? 1 : ceil_div(units, cap_units);
+    const uint64_t C = units == 0 ? 0 : ceil_div(units, K);
+    L.chunks = static_cast<int>(K);
+    L.chunk_units = static_cast<uint32_t>(C);
+    L.part_units = static_cast<uint32_t>(K * C);
+    // Small chunks: one workgroup just wide enough that no wave is idle; larger ones: 256-thread
+    // workgroups, one unit per lane per pass.
+    L.threads = h->threads ? h->threads
+                           : (C <= 256 ? static_cast<int>(std::max<uint64_t>(64, round_up(C, 64)))
+                                       : 256);
+    // With N dividing 8 every rank gets 8 / N XCDs (its first workgroup stays on XCD r); the
+    // other counts leave 8 - N XCDs idle rather than split a rank unevenly. Messages in the near
+    // regions stay on the rank's first XCD: their slots are homed near that XCD's half of the
+    // chip.
+    L.xcds_per_rank = (h->placement == AR_PLACE_XCD && N < kXcds && kXcds % N == 0 && !near)
+                          ? kXcds / N
+                          : 1;
+    // Workgroups per rank that can all be resident at once with kernel `fn`. A grid planned at
+    // the occupancy limit itself (every compute unit full) was once seen not to become resident
+    // as a whole (a rank-local join timed out), so one workgroup per compute unit is left free
+    // whenever the kernel fits more than one.
+    auto co_resident = [&](ar_kernel_fn fn) {
+      const int occ_api = occupancy(fn, L.threads);
+      const int occ = occ_api > 1 ? occ_api - 1 : occ_api;
+      int m;
+      if (h->placement == AR_PLACE_XCD)
+        m = cus_per_xcd * occ * L.xcds_per_rank / L.ranks_per_xcd;
+      else if (h->placement == AR_PLACE_SAME)
+        m = cus_per_xcd * occ / N;
+      else
+        m = h->cu_count * occ / N;
+      return std::min(m, ar::kMaxCtasPerRank);
+    };
+    auto pick_ctas = [&](int max_ctas) {
+      if (h->ctas) return h->ctas;
+      const uint64_t want = std::max<uint64_t>(1, ceil_div(C, static_cast<uint64_t>(L.threads)));
+      return static_cast<int>(std::min<uint64_t>(want, static_cast<uint64_t>(max_ctas)));
+    };
+    int max_ctas = co_resident(L.fn);
+    int ctas = pick_ctas(max_ctas);
+    if (static_cast<uint64_t>(ctas) * L.threads < C) {
+      // The chunk does not fit one pass of the rank's lanes: the kernels built for one pass (the
+      // latency path) hand it to their multi-pass counterparts.
+      const int multi = algo == AR_TWOSHOT             ? ar::ALGO_TWOSHOT_BULK
+                        : algo == AR_ONESHOT_LL        ? ar::ALGO_ONESHOT_LL_MULTI
+                        : algo == AR_ONESHOT_SENTINEL  ? ar::ALGO_ONESHOT_SENTINEL_MULTI
+                                                       : 0;
+      if (multi != 0) {
+        L.kernel_algo = multi;
+        L.fn = ar_select_kernel(multi, h->dtype, nmax);
+        max_ctas = co_resident(L.fn);
+        ctas = pick_ctas(max_ctas);
+      }
     }
-  }
-  if (max_ctas < 1) return ar_fail(AR_ENORES, "%d ranks cannot be co-resident", N);
-  if (ctas > max_ctas)
-    return ar_fail(AR_ENORES, "%d workgroups per rank exceed the co-resident limit %d", ctas,
-                   max_ctas);
-  L.ctas = ctas;
+    if (max_ctas < 1) return ar_fail(AR_ENORES, "%d ranks cannot be co-resident", N);
+    if (ctas > max_ctas)
+      return ar_fail(AR_ENORES, "%d workgroups per rank exceed the co-resident limit %d", ctas,
+                     max_ctas);
+    L.ctas = ctas;
+    return AR_OK;
+  };
+  int rc = shape(near_fits);
+  // The bulk two-shot has slots of its own (no near copies): it takes the regular chunking.
+  if (rc == AR_OK && L.near && L.kernel_algo == ar::ALGO_TWOSHOT_BULK) rc = shape(false);
+  if (rc != AR_OK) return rc;
   if (L.near) {
     // Each rank's slot data goes to the fastest calibrated position of each near region, for the
     // XCD pair of the XCD of its first workgroup: any 2 KiB sub-block of either granule where a
@@ -270,7 +277,7 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
       for (int r = 0; r < N; ++r) {
         const int x = h->placement == AR_PLACE_XCD    ? r % kXcds
                       : h->placement == AR_PLACE_SAME ? 0
-                                                      : (r * ctas) % kXcds;
+                                                      : (r * L.ctas) % kXcds;
         const float* ns = h->near_ns[r][g][x / 2];
         int best = 0;
         for (int k = 0; k < ar::kNearPositions; ++k)
@@ -281,11 +288,11 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
   }
   if (h->placement == AR_PLACE_XCD)
     L.grid = static_cast<unsigned>(kXcds * L.ranks_per_xcd *
-                                   ceil_div(static_cast<uint64_t>(ctas), L.xcds_per_rank));
+                                   ceil_div(static_cast<uint64_t>(L.ctas), L.xcds_per_rank));
   else if (h->placement == AR_PLACE_SAME)
-    L.grid = static_cast<unsigned>(kXcds * N * ctas);
+    L.grid = static_cast<unsigned>(kXcds * N * L.ctas);
   else
-    L.grid = static_cast<unsigned>(N * ctas);
+    L.grid = static_cast<unsigned>(N * L.ctas);
   return AR_OK;
 }
 

@@ -59,6 +59,26 @@ def test_bulk_twoshot_chunked_and_rearmed():
                     assert np.all(w == sentinel), f"rank {r} region {reg} not re-armed"
 
 
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_bulk_twoshot_small_slots_near_sized(n):
+    """A message small enough for the near regions but forced onto one workgroup per rank runs
+    the bulk two-shot, whose own slots are capped at 8 KiB here: the call must use the regular
+    chunking (several chunks), not the near regions' single chunk."""
+    from latency_collectives_amd import _ar as A
+
+    count = n * 2000 * 4 + 5  # about 2000 units per partition, more than one 512-unit slot
+    env = {"AR_SCRATCH_TWOSHOT": (2 * n * 8) << 10}
+    with handle(n, count * 4, "f32", env=env, ctas=1) as h:
+        for it in range(3):
+            _say(f"case bulk near-sized n={n} it={it}")
+            x = draw("f32", n, count, seed=900 + 10 * n + it)
+            got = run_allreduce(h, x, "twoshot")
+            assert_matches(got, x, "twoshot", "f32")
+        S = count * 4
+        assert A.ar_alg_bytes(h, count, A.AR_TWOSHOT) == (n + 1) * S + 5 * (n - 1) * S, \
+            "the bulk two-shot kernel was not the one planned"
+
+
 def test_bulk_twoshot_withheld_rank_times_out():
     from latency_collectives_amd import _ar as A
     import torch
