@@ -735,22 +735,40 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
   wait_all_mem();
   if (has_units && r != a.withhold) {
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
-      const uint32_t i = i0 + c.lane;
-      const bool act = i < CU;
+      // The wave's 64 units are 256 words; lane l takes words e * 64 + l (e = 0..3), so that
+      // every atomic instruction adds into 256 contiguous bytes (whole cache lines) rather than
+      // one word of each of 64 units.
+      uint32_t woff[4];
+      bool wact[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t d = i0 * 4u + static_cast<uint32_t>(e) * 64u + c.lane;  // word in chunk
+        wact[e] = d < CU * 4u;
+        woff[e] = d * 4u;
+      }
       uint32_t w[NMAX][4];
-      load_partitions<DT, NMAX>(a, r, in_r, k, i, act, 0, w);
-      const uint32_t off = act ? b * a.acc.slot + i * 16u : kDrop;
+#pragma unroll
+      for (int j = 0; j < NMAX; ++j) {
+        int p = r + j;
+        if (p >= N) p -= N;
+        const bool live = j < N;
+        const uint32_t pbase = (p * P + k * CU) * 16u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[j][e] = ld4<kPlain>(in_r, live && wact[e] ? pbase + woff[e] : kDrop);
+      }
 #pragma unroll
       for (int j = 0; j < NMAX; ++j) {
         const rsrc_t dst = j == 0 ? region_rsrc(a, r, a.acc) : peer_rsrc(a, r, j, a.acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          const uint32_t off = wact[e] ? b * a.acc.slot + woff[e] : kDrop;
           if constexpr (DT == DT_F32) {
             (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(__uint_as_float(w[j][e]), dst,
-                                                                 off + 4u * e, 0, 0);
+                                                                 off, 0, 0);
           } else {
             (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(static_cast<int>(w[j][e]), dst,
-                                                                off + 4u * e, 0, 0);
+                                                                off, 0, 0);
           }
         }
       }
