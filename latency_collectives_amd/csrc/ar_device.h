@@ -250,8 +250,26 @@ __device__ __forceinline__ rsrc_t out_rsrc(void* base, uint32_t nbytes) {
   return make_rsrc(base, nbytes);
 }
 
+// For a bf16 message of odd length: clear the half word past the end in the unit of `w` that was
+// loaded from byte offset `off` (any other unit is left as it is).
+template <int UB>
+__device__ __forceinline__ void clear_odd_tail(uint32_t off, uint32_t nbytes, uint32_t* w) {
+  const uint32_t last = nbytes & ~3u;  // word holding the last element
+#pragma unroll
+  for (int k = 0; k < UB / 4; ++k) w[k] = (off + 4u * k == last) ? (w[k] & 0xFFFFu) : w[k];
+}
+
+// True for a bf16 message of odd length. nbytes is the same in every lane, so a branch on this is
+// a scalar branch that even lengths skip; the empty asm in the branch keeps the compiler from
+// turning the block into selects that every unit executes.
+template <int DT>
+__device__ __forceinline__ bool odd_tail(uint32_t nbytes) {
+  return Ty<DT>::kElem == 2 && (nbytes & 2u) != 0u;
+}
+
 // Load one unit (UB bytes, 8 or 16) at byte offset `off`; zeros past the end (or for kDrop).
-template <int DT, int UB, int CP = kPlain>
+// kTail = false leaves an odd bf16 tail to the caller (clear_odd_tail after a batch of loads).
+template <int DT, int UB, int CP = kPlain, bool kTail = true>
 __device__ __forceinline__ void load_unit(rsrc_t r, uint32_t off, uint32_t nbytes, uint32_t* w) {
   if constexpr (UB == 16) {
     const u32x4 v = ld16<CP>(r, off);
@@ -260,12 +278,11 @@ __device__ __forceinline__ void load_unit(rsrc_t r, uint32_t off, uint32_t nbyte
     const u32x2 v = ld8<CP>(r, off);
     w[0] = v.x; w[1] = v.y;
   }
-  if constexpr (Ty<DT>::kElem == 2) {
-    const uint32_t last = nbytes & ~3u;  // word holding the last element when nbytes % 4 == 2
-    const bool odd = (nbytes & 2u) != 0u;
-#pragma unroll
-    for (int k = 0; k < UB / 4; ++k)
-      w[k] = (odd && off + 4u * k == last) ? (w[k] & 0xFFFFu) : w[k];
+  if constexpr (kTail && Ty<DT>::kElem == 2) {
+    if (odd_tail<DT>(nbytes)) {
+      asm volatile("");
+      clear_odd_tail<UB>(off, nbytes, w);
+    }
   }
 }
 
@@ -280,12 +297,15 @@ __device__ __forceinline__ void store_unit(rsrc_t r, uint32_t off, uint32_t nbyt
   }
   if constexpr (Ty<DT>::kElem == 2) {
     // the last element of an odd-length message: one 2-byte store (dropped in every other unit)
-    const uint32_t last = nbytes & ~3u;
-    const bool tail = (nbytes & 2u) != 0u && off <= last && last < off + UB;
-    uint32_t word = w[0];
+    if (odd_tail<DT>(nbytes)) {
+      asm volatile("");
+      const uint32_t last = nbytes & ~3u;
+      const bool tail = off <= last && last < off + UB;
+      uint32_t word = w[0];
 #pragma unroll
-    for (int k = 1; k < UB / 4; ++k) word = (off + 4u * k == last) ? w[k] : word;
-    st2<CP>(r, tail ? last : kDrop, static_cast<uint16_t>(word & 0xFFFFu));
+      for (int k = 1; k < UB / 4; ++k) word = (off + 4u * k == last) ? w[k] : word;
+      st2<CP>(r, tail ? last : kDrop, static_cast<uint16_t>(word & 0xFFFFu));
+    }
   }
 }
 

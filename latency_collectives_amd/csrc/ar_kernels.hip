@@ -505,7 +505,17 @@ __device__ __forceinline__ void load_partitions(const Args& a, int r, rsrc_t in_
     int p = r + j;
     if (p >= N) p -= N;
     const bool live = act && j < N;
-    load_unit<DT, 16, CP>(in_r, live ? (p * P + k * CU + i) * 16u : kDrop, a.nbytes, w[j]);
+    load_unit<DT, 16, CP, false>(in_r, live ? (p * P + k * CU + i) * 16u : kDrop, a.nbytes, w[j]);
+  }
+  // all loads are in flight before the one scalar branch for an odd bf16 tail
+  if (odd_tail<DT>(a.nbytes)) {
+    asm volatile("");
+#pragma unroll
+    for (int j = jfirst; j < NMAX; ++j) {
+      int p = r + j;
+      if (p >= N) p -= N;
+      clear_odd_tail<16>((p * P + k * CU + i) * 16u, a.nbytes, w[j]);
+    }
   }
 }
 
@@ -566,7 +576,11 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
         st16<kCoh>(peer_rsrc(a, r, j, a.p1), off, u32x4{w[j][0], w[j][1], w[j][2], w[j][3]});
     }
     u32x4 v[NMAX];
-    if (!poll_all<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
+    if constexpr (NMAX <= 8) {
+      if (!poll_all2<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
+    } else {
+      if (!poll_all<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
+    }
     uint32_t o[4];
     fold_rank_order<DT, NMAX, 4>(N, r, w[0], v, o);
     if (sends)
@@ -575,7 +589,11 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
     store_unit<DT, 16>(out_r, act ? uoff : kDrop, a.nbytes, o);
     rearm<NMAX>(own1, off1, slot1, mask, sent);
     u32x4 v2[NMAX];
-    if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
+    if constexpr (NMAX <= 8) {
+      if (!poll_all2<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
+    } else {
+      if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
+    }
     allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v2, sent);
     compiler_fence();
     wait_vm<NMAX>();  // every output store has landed; the NMAX re-arm stores may be in flight
