@@ -154,6 +154,10 @@ double ar_wallclock_hz(void);
  *   AR_OPT_PLACEMENT     ar_placement of ranks on XCDs [AR_PLACE_XCD]
  *   AR_OPT_DRIFT         ar_bench only: each rank sleeps a pseudo-random 0..value units of ~3 µs
  *                        before each iteration, to stress the double-buffer credits [0]
+ *   AR_OPT_NARROW        1: when the launch shape is not forced (AR_OPT_CTAS and AR_OPT_THREADS
+ *                        are 0), the one-pass sentinel kernels (one-shot and two-shot) move
+ *                        8-byte units if the message still fits one pass of co-resident lanes
+ *                        (twice the lanes, half the fold per lane); 0: always 16-byte units [1]
  */
 typedef enum {
   AR_OPT_TIMEOUT_US = 0,
@@ -161,7 +165,8 @@ typedef enum {
   AR_OPT_CTAS = 2,
   AR_OPT_THREADS = 3,
   AR_OPT_PLACEMENT = 4,
-  AR_OPT_DRIFT = 5
+  AR_OPT_DRIFT = 5,
+  AR_OPT_NARROW = 6
 } ar_option;
 int ar_set_option(ar_handle* h, ar_option opt, int64_t value);
 

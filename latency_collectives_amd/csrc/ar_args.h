@@ -22,6 +22,9 @@ enum Algo : int {
   ALGO_TWOSHOT_BULK = 7,
   ALGO_ONESHOT_LL_MULTI = 8,
   ALGO_ONESHOT_SENTINEL_MULTI = 9,
+  // internal: one-pass sentinel kernels with 8-byte units (two lanes per 16 bytes)
+  ALGO_ONESHOT_SENTINEL_NARROW = 10,
+  ALGO_TWOSHOT_NARROW = 11,
 };
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).

@@ -232,6 +232,49 @@ __device__ __forceinline__ bool vec_clear(u32x4 v) {
   return Ty<DT>::word_clear(v.x) & Ty<DT>::word_clear(v.y) & Ty<DT>::word_clear(v.z) &
          Ty<DT>::word_clear(v.w);
 }
+template <int DT>
+__device__ __forceinline__ bool vec_clear(u32x2 v) {
+  return Ty<DT>::word_clear(v.x) & Ty<DT>::word_clear(v.y);
+}
+
+// A slot unit of UB bytes (16: four words, 8: two words) and its loads and stores.
+template <int UB>
+struct UnitVec;
+template <>
+struct UnitVec<16> {
+  using type = u32x4;
+};
+template <>
+struct UnitVec<8> {
+  using type = u32x2;
+};
+template <int UB>
+using unit_t = typename UnitVec<UB>::type;
+
+template <int CP>
+__device__ __forceinline__ void ld_vec(rsrc_t r, uint32_t off, u32x4& v) {
+  v = ld16<CP>(r, off);
+}
+template <int CP>
+__device__ __forceinline__ void ld_vec(rsrc_t r, uint32_t off, u32x2& v) {
+  v = ld8<CP>(r, off);
+}
+template <int CP>
+__device__ __forceinline__ void st_vec(rsrc_t r, uint32_t off, u32x4 v) {
+  st16<CP>(r, off, v);
+}
+template <int CP>
+__device__ __forceinline__ void st_vec(rsrc_t r, uint32_t off, u32x2 v) {
+  st8<CP>(r, off, v);
+}
+
+template <int DT, int UB>
+__device__ __forceinline__ unit_t<UB> sentinel_unit() {
+  unit_t<UB> v;
+#pragma unroll
+  for (int k = 0; k < UB / 4; ++k) v[k] = Ty<DT>::kSentinelWord;
+  return v;
+}
 
 // ------------------------------------------------------------------ user buffers
 //

@@ -121,6 +121,7 @@ struct ar_handle {
   int threads = 0;
   int placement = AR_PLACE_XCD;
   int drift = 0;
+  int narrow = 1;  // one-pass sentinel kernels may use 8-byte units
   void** tab = nullptr;
   size_t tab_cap = 0;
   uint64_t* ts = nullptr;
@@ -148,23 +149,31 @@ struct Launch {
   unsigned grid = 1;
 };
 
-// Chunk geometry and launch shape for one AllReduce of `nbytes` bytes per rank.
-int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
+// Plan with slot units of `ub` bytes (16, or 8 for the narrow one-pass sentinel kernels). With
+// ub == 8 the plan only succeeds for a chunk that fits one pass of co-resident lanes; otherwise
+// it returns kNoNarrow without recording an error.
+constexpr int kNoNarrow = 1;
+int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   const int N = h->nranks;
   const int nmax = N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16;
-  L.fn = ar_select_kernel(algo, h->dtype, nmax);
-  L.kernel_algo = algo;
+  const int one_pass = ub == 8 ? (algo == AR_TWOSHOT ? ar::ALGO_TWOSHOT_NARROW
+                                                     : ar::ALGO_ONESHOT_SENTINEL_NARROW)
+                               : algo;
+  L.fn = ar_select_kernel(one_pass, h->dtype, nmax);
+  L.kernel_algo = one_pass;
   if (L.fn == nullptr)
     return ar_fail(AR_ENOTSUP, "algorithm %d is not provided for dtype %d", algo, h->dtype);
   uint64_t cap_units = 0, units = 0;
+  uint64_t line = static_cast<uint64_t>(ub);  // slot bytes per unit
   switch (algo) {
     case AR_ONESHOT_LL:
       units = ceil_div(nbytes, 8);
+      line = 16;
       cap_units = h->rg[RG_LL].slot / 16;
       break;
     case AR_ONESHOT_SENTINEL:
-      units = ceil_div(nbytes, 16);
-      cap_units = h->rg[RG_P1].slot / 16;
+      units = ceil_div(nbytes, line);
+      cap_units = h->rg[RG_P1].slot / line;
       break;
     case AR_BARRIER2:
       units = ceil_div(nbytes, 16);
@@ -172,10 +181,10 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
       break;
     case AR_TWOSHOT:
     case AR_LL128_ATOMIC:
-      units = ceil_div(ceil_div(nbytes, 16), N);  // one partition
+      units = ceil_div(ceil_div(nbytes, line), N);  // one partition
       cap_units = std::min({h->rg[RG_P1].slot, h->rg[RG_P2].slot, h->rg[RG_ACC].slot,
                             h->rg[RG_PF1].slot, h->rg[RG_PF2].slot}) /
-                  16;
+                  line;
       break;
     case AR_BARRIER_ONLY:
       units = 0;
@@ -186,8 +195,8 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
   }
   if (cap_units == 0) return ar_fail(AR_EINVAL, "scratch slots are too small");
   // Messages whose 2 * N slots fit a near page in one chunk use the near regions: the slot data
-  // (16 bytes per unit) goes in 8 KiB chunks at a pitch of 16 KiB per chunk.
-  const uint64_t near_chunks = ceil_div(units, ar::kChunkUnits);
+  // goes in 8 KiB chunks at a pitch of 16 KiB per chunk.
+  const uint64_t near_chunks = ceil_div(units * line, ar::kGranule);
   const bool near_fits = units > 0 && 2ull * N * near_chunks * 2 * ar::kGranule <= ar::kNearPage &&
                          (algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL ||
                           algo == AR_TWOSHOT ||
@@ -196,8 +205,8 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
   L.ranks_per_xcd = h->placement == AR_PLACE_XCD ? static_cast<int>(ceil_div(N, kXcds)) : 1;
   // Chunk geometry, workgroup shape and kernel for the near or the regular slots.
   auto shape = [&](bool near) -> int {
-    L.fn = ar_select_kernel(algo, h->dtype, nmax);
-    L.kernel_algo = algo;
+    L.fn = ar_select_kernel(one_pass, h->dtype, nmax);
+    L.kernel_algo = one_pass;
     L.near = near;
     const uint64_t K = near || units == 0 ? 1 : ceil_div(units, cap_units);
     const uint64_t C = units == 0 ? 0 : ceil_div(units, K);
@@ -239,6 +248,17 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
     };
     int max_ctas = co_resident(L.fn);
     int ctas = pick_ctas(max_ctas);
+    if (ub == 8) {
+      // Narrow units only while the rank's workgroups still get a compute unit each: beyond
+      // that the doubled lane count measured slower than 16-byte units (128 KiB and more per
+      // rank at N = 4).
+      const int rank_cus = h->placement == AR_PLACE_XCD
+                               ? cus_per_xcd * L.xcds_per_rank / L.ranks_per_xcd
+                           : h->placement == AR_PLACE_SAME ? cus_per_xcd / N
+                                                           : h->cu_count / N;
+      if (static_cast<uint64_t>(ctas) * L.threads < C || ctas > std::max(1, rank_cus))
+        return kNoNarrow;
+    }
     if (static_cast<uint64_t>(ctas) * L.threads < C) {
       // The chunk does not fit one pass of the rank's lanes: the kernels built for one pass (the
       // latency path) hand it to their multi-pass counterparts.
@@ -268,7 +288,7 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
     // Each rank's slot data goes to the fastest calibrated position of each near region, for the
     // XCD pair of the XCD of its first workgroup: any 2 KiB sub-block of either granule where a
     // single chunk fits, else the start of either granule.
-    const uint64_t data = units * 16;
+    const uint64_t data = units * line;
     const int max_sub = near_chunks == 1 ? static_cast<int>((ar::kGranule - data) / ar::kNearSub) : 0;
     for (int g = 0; g < ar::kNearRegions; ++g) {
       ar::Region& rg = L.near_rg[g];
@@ -294,6 +314,23 @@ int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
   else
     L.grid = static_cast<unsigned>(N * L.ctas);
   return AR_OK;
+}
+
+// Chunk geometry and launch shape for one AllReduce of `nbytes` bytes per rank. The one-pass
+// sentinel kernels (one-shot and two-shot) move 8-byte units when the chunk still fits one pass
+// of co-resident lanes and the launch shape is not forced; 16-byte units otherwise.
+int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
+  if ((algo == AR_ONESHOT_SENTINEL || algo == AR_TWOSHOT) && h->narrow && h->ctas == 0 &&
+      h->threads == 0 && nbytes > 0) {
+    Launch narrow;
+    const int rc = plan_units(h, algo, nbytes, 8, narrow);
+    if (rc == AR_OK) {
+      L = narrow;
+      return AR_OK;
+    }
+    if (rc != kNoNarrow) return rc;
+  }
+  return plan_units(h, algo, nbytes, 16, L);
 }
 
 ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
@@ -557,6 +594,10 @@ int ar_set_option(ar_handle* h, ar_option opt, int64_t v) {
       if (v < 0 || v > 1000) return ar_fail(AR_EINVAL, "drift out of range");
       h->drift = static_cast<int>(v);
       return AR_OK;
+    case AR_OPT_NARROW:
+      if (v != 0 && v != 1) return ar_fail(AR_EINVAL, "narrow must be 0 or 1");
+      h->narrow = static_cast<int>(v);
+      return AR_OK;
   }
   return ar_fail(AR_EINVAL, "unknown option %d", static_cast<int>(opt));
 }
@@ -760,8 +801,10 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
     case ar::ALGO_ONESHOT_LL_MULTI: return static_cast<int64_t>(2 * N * S + 4 * N * (N - 1) * S);
     case AR_ONESHOT_SENTINEL:
     case ar::ALGO_ONESHOT_SENTINEL_MULTI:
+    case ar::ALGO_ONESHOT_SENTINEL_NARROW:
       return static_cast<int64_t>(2 * N * S + 3 * N * (N - 1) * S);
-    case AR_TWOSHOT: return static_cast<int64_t>((N + 1) * S + 7 * (N - 1) * S);
+    case AR_TWOSHOT:
+    case ar::ALGO_TWOSHOT_NARROW: return static_cast<int64_t>((N + 1) * S + 7 * (N - 1) * S);
     case ar::ALGO_TWOSHOT_BULK: return static_cast<int64_t>((N + 1) * S + 5 * (N - 1) * S);
     case AR_LL128_ATOMIC: return static_cast<int64_t>(2 * N * S + 3 * S + 4 * (N - 1) * S);
     case AR_BARRIER2: return static_cast<int64_t>(2 * N * S + 2 * N * (N - 1) * S);

@@ -72,10 +72,12 @@ __device__ __forceinline__ uint8_t* region_base(const Args& a, int rank, const R
   return a.base + static_cast<uint64_t>(rank) * a.stride + g.off + pos * kNearSub;
 }
 
-// Byte offset of 16-byte unit i inside a slot: contiguous in the regular regions; in a near
-// region, chunks of kChunkUnits units, one per 16 KiB (2 granules) of the slot's pitch.
+// Byte offset of unit i (UB bytes) inside a slot: contiguous in the regular regions; in a near
+// region, 8 KiB chunks of units, one per 16 KiB (2 granules) of the slot's pitch.
+template <int UB = 16>
 __device__ __forceinline__ uint32_t slot_off(const Region& g, uint32_t i) {
-  return g.near ? ((i / kChunkUnits) * (2 * kGranule) + (i % kChunkUnits) * 16u) : i * 16u;
+  const uint32_t byte = i * static_cast<uint32_t>(UB);
+  return g.near ? ((byte / kGranule) * (2 * kGranule) + byte % kGranule) : byte;
 }
 
 __device__ __forceinline__ rsrc_t region_rsrc(const Args& a, int rank, const Region& g) {
@@ -179,17 +181,19 @@ __device__ __forceinline__ bool poll_rest(const Args& a, rsrc_t own, uint32_t of
 // Latency-path poll: every source in `mask` is loaded straight into v[q] each round, whether
 // or not it has arrived (a slot that has arrived keeps its value until this rank re-arms it),
 // until all of them pass `ready`. No per-source branches or copies: after the last load returns
-// only the readiness test and the ballot stand between the data and the fold.
-template <int NMAX, class Ready>
+// only the readiness test and the ballot stand between the data and the fold. V is the unit
+// (u32x4 or u32x2).
+template <int NMAX, class Ready, class V>
 __device__ __forceinline__ bool poll_all(const Args& a, rsrc_t own, uint32_t off0,
-                                         uint32_t qstride, uint32_t mask, u32x4 (&v)[NMAX],
+                                         uint32_t qstride, uint32_t mask, V (&v)[NMAX],
                                          Ready ready, int rank, uint64_t step) {
   uint32_t spins = 0;
   uint64_t t_first = 0;
   while (true) {
 #pragma unroll
     for (int q = 0; q < NMAX; ++q)
-      v[q] = ld16<kCoh>(own, ((mask >> q) & 1u) ? off0 + static_cast<uint32_t>(q) * qstride : kDrop);
+      ld_vec<kCoh>(own, ((mask >> q) & 1u) ? off0 + static_cast<uint32_t>(q) * qstride : kDrop,
+                   v[q]);
     compiler_fence();
     bool ok = true;
 #pragma unroll
@@ -260,18 +264,18 @@ __device__ __forceinline__ bool poll_lines(const Args& a, rsrc_t own, uint32_t o
   return poll_rest<NMAX>(a, own, off0, qstride, pend, t, v, ready, rank, step);
 }
 
-// Fold the N sources of one unit in rank order 0..N-1; the rank's own value is `x`.
-template <int DT, int NMAX, int W>
+// Fold the N sources of one unit in rank order 0..N-1; the rank's own value is `x`. The first W
+// words of each v[q] are payload.
+template <int DT, int NMAX, int W, class V>
 __device__ __forceinline__ void fold_rank_order(int N, int r, const uint32_t* x,
-                                                const u32x4 (&v)[NMAX], uint32_t* o) {
+                                                const V (&v)[NMAX], uint32_t* o) {
   Fold<DT, W> f;
 #pragma unroll
   for (int q = 0; q < NMAX; ++q) {
     if (q < N) {
       uint32_t src[W];
-      const uint32_t vw[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
-      for (int i = 0; i < W; ++i) src[i] = (q == r) ? x[i] : vw[i];
+      for (int i = 0; i < W; ++i) src[i] = (q == r) ? x[i] : v[q][i];
       if (q == 0)
         f.init(src);
       else
@@ -285,29 +289,24 @@ __device__ __forceinline__ uint32_t peer_mask(int N, int r) {
   return ((N >= 32) ? 0xFFFFFFFFu : ((1u << N) - 1u)) & ~(1u << r);
 }
 
-template <int DT>
-__device__ __forceinline__ u32x4 sentinel_vec() {
-  const uint32_t s = Ty<DT>::kSentinelWord;
-  return u32x4{s, s, s, s};
-}
-
-// Write the sentinel back into the slots of the sources in `mask` (source q's line at
+// Write the sentinel unit back into the slots of the sources in `mask` (source q's unit at
 // off0 + q * qstride): NMAX stores, branch-free.
-template <int NMAX>
+template <int NMAX, class V>
 __device__ __forceinline__ void rearm(rsrc_t own, uint32_t off0, uint32_t qstride, uint32_t mask,
-                                      u32x4 sent) {
+                                      V sent) {
 #pragma unroll
   for (int q = 0; q < NMAX; ++q)
-    st16<kCoh>(own, ((mask >> q) & 1u) ? off0 + static_cast<uint32_t>(q) * qstride : kDrop, sent);
+    st_vec<kCoh>(own, ((mask >> q) & 1u) ? off0 + static_cast<uint32_t>(q) * qstride : kDrop,
+                 sent);
 }
 
-// Push one 16-byte line to the j-th peer after r, for j = 1..NMAX-1 (NMAX-1 stores, branch-free;
-// peers that do not exist and idle lanes drop their store).
-template <int NMAX>
+// Push one unit (a 16-byte line or an 8-byte unit) to the j-th peer after r, for j = 1..NMAX-1
+// (NMAX-1 stores, branch-free; peers that do not exist and idle lanes drop their store).
+template <int NMAX, class V>
 __device__ __forceinline__ void push_peers(const Args& a, int r, const Region& g, uint32_t off,
-                                           u32x4 line) {
+                                           V line) {
 #pragma unroll
-  for (int j = 1; j < NMAX; ++j) st16<kCoh>(peer_rsrc(a, r, j, g), off, line);
+  for (int j = 1; j < NMAX; ++j) st_vec<kCoh>(peer_rsrc(a, r, j, g), off, line);
 }
 
 // Ordering of a step (every step function follows it):
@@ -403,14 +402,19 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
 
 // ------------------------------------------------------------------ one-shot, sentinel protocol
 //
-// Push raw 16-byte units into every peer's slot (§IV "Sentinel"). Receive: poll until no element
-// of a peer's unit equals the sentinel, fold in rank order, then write the sentinel back so the
-// slot is armed for step s+2 (the same buffer). The output store is issued before the re-arm so
-// that the step can return as soon as the output has landed.
-template <int DT, int NMAX, bool kMulti>
+// Push raw units into every peer's slot (§IV "Sentinel"). Receive: poll until no element of a
+// peer's unit equals the sentinel, fold in rank order, then write the sentinel back so the slot
+// is armed for step s+2 (the same buffer). The output store is issued before the re-arm so that
+// the step can return as soon as the output has landed. A unit is UB = 16 bytes, or 8 bytes in
+// the narrow one-pass kernel: twice the lanes, each folding half as many words, which shortens
+// the serial fold of every wave (the fold is one dependent add chain per word and source).
+template <int DT, int NMAX, bool kMulti, int UB = 16>
 __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
                                       rsrc_t out_r, int k, uint64_t& t0,
                                       uint64_t& t1) {
+  static_assert(!kMulti || UB == 16, "the multi-pass path moves 16-byte units");
+  using V = unit_t<UB>;
+  constexpr int W = UB / 4;
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t slot = a.p1.slot, CU = a.chunk_units;
@@ -419,32 +423,37 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
   const uint32_t mine = (b * N + r) * slot;
   const rsrc_t own = region_rsrc(a, r, a.p1);
   const uint32_t peers = peer_mask(N, r);
-  const u32x4 sent = sentinel_vec<DT>();
-  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
-  auto finish = [&](uint32_t i, bool act, const uint32_t* x, const u32x4 (&v)[NMAX],
+  const V sent = sentinel_unit<DT, UB>();
+  auto ready = [](V l) { return vec_clear<DT>(l); };
+  auto finish = [&](uint32_t i, bool act, const uint32_t* x, const V (&v)[NMAX],
                     uint32_t off0) {
-    uint32_t o[4];
-    fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
-    store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, o);
+    uint32_t o[W];
+    fold_rank_order<DT, NMAX, W>(N, r, x, v, o);
+    store_unit<DT, UB>(out_r, act ? (unit0 + i) * UB : kDrop, a.nbytes, o);
     rearm<NMAX>(own, off0, slot, act ? peers : 0u, sent);
   };
   if constexpr (!kMulti) {
     // one pass: the plan gives this rank at least one lane per unit of the chunk
     const uint32_t i = c.t0 + c.lane;
     const bool act = i < CU;
-    uint32_t off0 = b * N * slot + slot_off(a.p1, i);
-    uint32_t in_off = act ? (unit0 + i) * 16u : kDrop;
-    uint32_t push_off = act ? mine + slot_off(a.p1, i) : kDrop;
+    uint32_t off0 = b * N * slot + slot_off<UB>(a.p1, i);
+    uint32_t in_off = act ? (unit0 + i) * UB : kDrop;
+    uint32_t push_off = act ? mine + slot_off<UB>(a.p1, i) : kDrop;
     pin(off0);
     pin(in_off);
     pin(push_off);
     stamp_start(t0, k);
-    uint32_t x[4];
-    load_unit<DT, 16>(in_r, in_off, a.nbytes, x);
+    uint32_t x[W];
+    load_unit<DT, UB>(in_r, in_off, a.nbytes, x);
     compiler_fence();
     wait_vm<0>();
-    if (sends) push_peers<NMAX>(a, r, a.p1, push_off, u32x4{x[0], x[1], x[2], x[3]});
-    u32x4 v[NMAX];
+    if (sends) {
+      V line;
+#pragma unroll
+      for (int e = 0; e < W; ++e) line[e] = x[e];
+      push_peers<NMAX>(a, r, a.p1, push_off, line);
+    }
+    V v[NMAX];
     // one round of polls at a time: with a second round in flight the sentinel path measured
     // slower (the exit then waits for the other round's loads)
     if (!poll_all<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
@@ -490,22 +499,23 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
 
 // Load unit i of the chunk in the partition of the j-th peer after rank r into w[j], for
 // j = jfirst..NMAX-1 (zeros for peers that do not exist or an idle lane): NMAX-jfirst loads.
-template <int DT, int NMAX, int CP = kPlain>
+template <int DT, int NMAX, int CP = kPlain, int UB = 16>
 __device__ __forceinline__ void load_partitions(const Args& a, int r, rsrc_t in_r, int k,
                                                 uint32_t i, bool act, int jfirst,
-                                                uint32_t (&w)[NMAX][4]) {
+                                                uint32_t (&w)[NMAX][UB / 4]) {
   const int N = a.nranks;
   const uint32_t CU = a.chunk_units, P = a.part_units;
 #pragma unroll
   for (int j = 0; j < NMAX; ++j) {
     if (j < jfirst) {
-      w[j][0] = w[j][1] = w[j][2] = w[j][3] = 0u;
+#pragma unroll
+      for (int e = 0; e < UB / 4; ++e) w[j][e] = 0u;
       continue;
     }
     int p = r + j;
     if (p >= N) p -= N;
     const bool live = act && j < N;
-    load_unit<DT, 16, CP, false>(in_r, live ? (p * P + k * CU + i) * 16u : kDrop, a.nbytes, w[j]);
+    load_unit<DT, UB, CP, false>(in_r, live ? (p * P + k * CU + i) * UB : kDrop, a.nbytes, w[j]);
   }
   // all loads are in flight before the one scalar branch for an odd bf16 tail
   if (odd_tail<DT>(a.nbytes)) {
@@ -514,22 +524,24 @@ __device__ __forceinline__ void load_partitions(const Args& a, int r, rsrc_t in_
     for (int j = jfirst; j < NMAX; ++j) {
       int p = r + j;
       if (p >= N) p -= N;
-      clear_odd_tail<16>((p * P + k * CU + i) * 16u, a.nbytes, w[j]);
+      clear_odd_tail<UB>((p * P + k * CU + i) * UB, a.nbytes, w[j]);
     }
   }
 }
 
 // All-gather receive of unit i: the reduced unit of every other owner, already polled into v[],
 // is copied to `out` and its slot re-armed.
-template <int DT, int NMAX>
+template <int DT, int NMAX, int UB = 16>
 __device__ __forceinline__ void allgather_out(const Args& a, int r, rsrc_t out_r, rsrc_t own2,
                                               uint32_t off0, uint32_t mask, int k, uint32_t i,
-                                              const u32x4 (&v)[NMAX], u32x4 sent) {
+                                              const unit_t<UB> (&v)[NMAX], unit_t<UB> sent) {
   const uint32_t CU = a.chunk_units, P = a.part_units;
 #pragma unroll
   for (int p = 0; p < NMAX; ++p) {
-    const uint32_t o[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
-    store_unit<DT, 16>(out_r, ((mask >> p) & 1u) ? (p * P + k * CU + i) * 16u : kDrop, a.nbytes,
+    uint32_t o[UB / 4];
+#pragma unroll
+    for (int e = 0; e < UB / 4; ++e) o[e] = v[p][e];
+    store_unit<DT, UB>(out_r, ((mask >> p) & 1u) ? (p * P + k * CU + i) * UB : kDrop, a.nbytes,
                        o);
   }
   rearm<NMAX>(own2, off0, a.p2.slot, mask, sent);
@@ -540,10 +552,12 @@ __device__ __forceinline__ void allgather_out(const Args& a, int r, rsrc_t out_r
 // Reduce-scatter: partition p's chunk goes to owner p's slot r. The owner folds its partition in
 // rank order, writes it to its own output and pushes the result to every peer's all-gather slot
 // r; every rank copies the other owners' results into its output (§III.A "Two-shot").
-template <int DT, int NMAX>
+template <int DT, int NMAX, int UB = 16>
 __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r, rsrc_t out_r,
                              int k, uint64_t& t0,
                              uint64_t& t1) {
+  using V = unit_t<UB>;
+  constexpr int W = UB / 4;
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t slot1 = a.p1.slot, slot2 = a.p2.slot, CU = a.chunk_units, P = a.part_units;
@@ -551,8 +565,8 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
   const rsrc_t own1 = region_rsrc(a, r, a.p1);
   const rsrc_t own2 = region_rsrc(a, r, a.p2);
   const uint32_t peers = peer_mask(N, r);
-  const u32x4 sent = sentinel_vec<DT>();
-  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+  const V sent = sentinel_unit<DT, UB>();
+  auto ready = [](V l) { return vec_clear<DT>(l); };
   const uint32_t mine1 = (b * N + r) * slot1, mine2 = (b * N + r) * slot2;
   // one pass: the plan gives this rank at least one lane per unit of the chunk (wider chunks
   // run step_twoshot_bulk)
@@ -560,41 +574,40 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
     const uint32_t i = c.t0 + c.lane;
     const bool act = i < CU;
     const uint32_t mask = act ? peers : 0u;
-    uint32_t off1 = b * N * slot1 + slot_off(a.p1, i);
-    const uint32_t off2 = b * N * slot2 + slot_off(a.p2, i);
-    const uint32_t uoff = (r * P + k * CU + i) * 16u;
+    uint32_t off1 = b * N * slot1 + slot_off<UB>(a.p1, i);
+    const uint32_t off2 = b * N * slot2 + slot_off<UB>(a.p2, i);
+    const uint32_t uoff = (r * P + k * CU + i) * UB;
     pin(off1);
     stamp_start(t0, k);
-    uint32_t w[NMAX][4];
-    load_partitions<DT, NMAX>(a, r, in_r, k, i, act, 0, w);  // w[0] is the own partition
+    uint32_t w[NMAX][W];
+    load_partitions<DT, NMAX, kPlain, UB>(a, r, in_r, k, i, act, 0, w);  // w[0]: own partition
     compiler_fence();
     wait_vm<0>();
     if (sends) {
-      const uint32_t off = act ? mine1 + slot_off(a.p1, i) : kDrop;
+      const uint32_t off = act ? mine1 + slot_off<UB>(a.p1, i) : kDrop;
 #pragma unroll
-      for (int j = 1; j < NMAX; ++j)
-        st16<kCoh>(peer_rsrc(a, r, j, a.p1), off, u32x4{w[j][0], w[j][1], w[j][2], w[j][3]});
+      for (int j = 1; j < NMAX; ++j) {
+        V line;
+#pragma unroll
+        for (int e = 0; e < W; ++e) line[e] = w[j][e];
+        st_vec<kCoh>(peer_rsrc(a, r, j, a.p1), off, line);
+      }
     }
-    u32x4 v[NMAX];
-    if constexpr (NMAX <= 8) {
-      if (!poll_all2<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
-    } else {
-      if (!poll_all<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
+    V v[NMAX];
+    if (!poll_all<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
+    uint32_t o[W];
+    fold_rank_order<DT, NMAX, W>(N, r, w[0], v, o);
+    if (sends) {
+      V line;
+#pragma unroll
+      for (int e = 0; e < W; ++e) line[e] = o[e];
+      push_peers<NMAX>(a, r, a.p2, act ? mine2 + slot_off<UB>(a.p2, i) : kDrop, line);
     }
-    uint32_t o[4];
-    fold_rank_order<DT, NMAX, 4>(N, r, w[0], v, o);
-    if (sends)
-      push_peers<NMAX>(a, r, a.p2, act ? mine2 + slot_off(a.p2, i) : kDrop,
-                       u32x4{o[0], o[1], o[2], o[3]});
-    store_unit<DT, 16>(out_r, act ? uoff : kDrop, a.nbytes, o);
+    store_unit<DT, UB>(out_r, act ? uoff : kDrop, a.nbytes, o);
     rearm<NMAX>(own1, off1, slot1, mask, sent);
-    u32x4 v2[NMAX];
-    if constexpr (NMAX <= 8) {
-      if (!poll_all2<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
-    } else {
-      if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
-    }
-    allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v2, sent);
+    V v2[NMAX];
+    if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
+    allgather_out<DT, NMAX, UB>(a, r, out_r, own2, off2, mask, k, i, v2, sent);
     compiler_fence();
     wait_vm<NMAX>();  // every output store has landed; the NMAX re-arm stores may be in flight
     t1 = now_ticks();
@@ -747,7 +760,7 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
   const rsrc_t own2 = region_rsrc(a, r, a.p2);
   const uint32_t slot2 = a.p2.slot;
   const uint32_t peers = peer_mask(N, r);
-  const u32x4 sent = sentinel_vec<DT>();
+  const u32x4 sent = sentinel_unit<DT, 16>();
   auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
   stamp_start(t0, k);
   wait_all_mem();
@@ -1069,8 +1082,12 @@ __device__ __forceinline__ void ar_body(const Args& a) {
         ok = step_oneshot_sentinel<DT, NMAX, false>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_ONESHOT_SENTINEL_MULTI) {
         ok = step_oneshot_sentinel<DT, NMAX, true>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_ONESHOT_SENTINEL_NARROW) {
+        ok = step_oneshot_sentinel<DT, NMAX, false, 8>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_TWOSHOT) {
         ok = step_twoshot<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_TWOSHOT_NARROW) {
+        ok = step_twoshot<DT, NMAX, 8>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_TWOSHOT_BULK) {
         ok = step_twoshot_bulk<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_ATOMIC) {
@@ -1174,7 +1191,10 @@ ar_kernel_fn ar_select_kernel(int algo, int dt, int nmax) {
     case ar::ALGO_ONESHOT_LL_MULTI: return pick_dt<ar::ALGO_ONESHOT_LL_MULTI>(dt, nmax);
     case ar::ALGO_ONESHOT_SENTINEL_MULTI:
       return pick_dt<ar::ALGO_ONESHOT_SENTINEL_MULTI>(dt, nmax);
+    case ar::ALGO_ONESHOT_SENTINEL_NARROW:
+      return pick_dt<ar::ALGO_ONESHOT_SENTINEL_NARROW>(dt, nmax);
     case ar::ALGO_TWOSHOT: return pick_dt<ar::ALGO_TWOSHOT>(dt, nmax);
+    case ar::ALGO_TWOSHOT_NARROW: return pick_dt<ar::ALGO_TWOSHOT_NARROW>(dt, nmax);
     case ar::ALGO_TWOSHOT_BULK: return pick_dt<ar::ALGO_TWOSHOT_BULK>(dt, nmax);
     case ar::ALGO_LL128_ATOMIC:
       if (dt == ar::DT_F32) return pick_n<ar::ALGO_LL128_ATOMIC, ar::DT_F32>(nmax);
