@@ -35,6 +35,29 @@ def test_all_algorithms_ragged_counts(n, dtype):
                 assert_matches(got, x, algo, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("n", [2, 3, 4, 8, 16])
+def test_sentinel_kernels_both_unit_widths(n, dtype):
+    """The one-pass sentinel kernels (one-shot and two-shot) with 8-byte units (the default where
+    they fit) and with 16-byte units (AR_OPT_NARROW = 0): both match the oracle, ragged counts
+    included, and give bit-identical outputs."""
+    maxc = max(COUNTS)
+    outs = {}
+    for narrow in (1, 0):
+        with handle(n, maxc * elem_bytes(dtype), dtype, narrow=narrow) as h:
+            for algo in ("oneshot_sentinel", "twoshot"):
+                for i, count in enumerate(COUNTS):
+                    _say(f"case n={n} dtype={dtype} algo={algo} narrow={narrow} count={count}")
+                    x = draw(dtype, n, count, seed=3000 * n + i)
+                    got = run_allreduce(h, x, algo)
+                    assert_matches(got, x, algo, dtype)
+                    outs[(narrow, algo, count)] = got
+    for (narrow, algo, count), got in outs.items():
+        if narrow == 1:
+            assert np.array_equal(got.view(np.uint8), outs[(0, algo, count)].view(np.uint8)), \
+                f"{algo} count={count}: 8-byte and 16-byte units differ"
+
+
 def test_auto_selection_matches_oracle():
     """AR_ALGO_AUTO over rank counts and sizes that select each of its three kernels."""
     for n in (2, 3, 4, 6, 8, 16):
@@ -93,15 +116,16 @@ def test_rank_constant_invariant(algo):
             assert np.all(got == n * (n - 1) // 2)
 
 
+@pytest.mark.parametrize("narrow", [1, 0])
 @pytest.mark.parametrize("algo", ["oneshot_sentinel", "twoshot", "ll128_atomic"])
-def test_scratch_rearmed_after_call(algo):
+def test_scratch_rearmed_after_call(algo, narrow):
     """After a call every sentinel slot holds the sentinel again and the atomic destination and
     arrival counters are back to zero: for a message that uses the regular regions and, at
-    1000 elements, for one that uses the near regions."""
+    1000 elements, for one that uses the near regions; with 8- and 16-byte units."""
     from latency_collectives_amd import _ar as A
 
     n, dtype, count = 4, "f32", 7777
-    with handle(n, count * 4, dtype) as h:
+    with handle(n, count * 4, dtype, narrow=narrow) as h:
         for it in range(3):
             for c in (count, 1000):
                 x = draw(dtype, n, c, seed=50 + it)
