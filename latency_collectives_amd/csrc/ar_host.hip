@@ -378,11 +378,11 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
 constexpr int kAutoN[5] = {2, 3, 4, 8, 16};
 constexpr uint64_t kAutoBytes[8] = {128, 512, 2048, 8192, 32768, 131072, 524288, 2097152};
 constexpr char kAutoTable[5][9] = {
-    "LLSSLLSS",  // N = 2 (LL and sentinel within 10 % of each other at most sizes)
-    "LLLSLSTL",  // N = 3
-    "LLLLLSTT",  // N = 4
-    "LLLLSTTT",  // N = 8
-    "LLLSSTTT",  // N = 16
+    "SLSLSSSS",  // N = 2 (LL and sentinel within 10 % of each other up to 32 KiB)
+    "SSLLLSTL",  // N = 3
+    "SSLLSSTT",  // N = 4
+    "SSLLSTTT",  // N = 8
+    "SSSSSTTT",  // N = 16
 };
 
 int resolve_algo(ar_handle* h, int algo, uint64_t nbytes) {
