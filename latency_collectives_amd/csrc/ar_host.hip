@@ -213,11 +213,6 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
     L.chunks = static_cast<int>(K);
     L.chunk_units = static_cast<uint32_t>(C);
     L.part_units = static_cast<uint32_t>(K * C);
-    // Small chunks: one workgroup just wide enough that no wave is idle; larger ones: 256-thread
-    // workgroups, one unit per lane per pass.
-    L.threads = h->threads ? h->threads
-                           : (C <= 256 ? static_cast<int>(std::max<uint64_t>(64, round_up(C, 64)))
-                                       : 256);
     // With N dividing 8 every rank gets 8 / N XCDs (its first workgroup stays on XCD r); the
     // other counts leave 8 - N XCDs idle rather than split a rank unevenly. Messages in the near
     // regions stay on the rank's first XCD: their slots are homed near that XCD's half of the
@@ -225,6 +220,21 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
     L.xcds_per_rank = (h->placement == AR_PLACE_XCD && N < kXcds && kXcds % N == 0 && !near)
                           ? kXcds / N
                           : 1;
+    const int rank_cus = std::max(1, h->placement == AR_PLACE_XCD
+                                         ? cus_per_xcd * L.xcds_per_rank / L.ranks_per_xcd
+                                     : h->placement == AR_PLACE_SAME ? cus_per_xcd / N
+                                                                     : h->cu_count / N);
+    // One-pass latency kernels: the smallest workgroup (whole waves) that covers the chunk with
+    // at most one workgroup per compute unit of the rank, so that each wave has a compute unit's
+    // memory pipeline to itself (measured 5-19 % lower p50 than one wider workgroup at
+    // N = 4..16). Other kernels: one workgroup just wide enough that no wave is idle for small
+    // chunks, 256-thread workgroups for larger ones.
+    const bool one_pass =
+        algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL || algo == AR_TWOSHOT;
+    const uint64_t spread = round_up(ceil_div(C, static_cast<uint64_t>(rank_cus)), 64);
+    L.threads = h->threads ? h->threads
+                : one_pass ? static_cast<int>(std::min<uint64_t>(256, std::max<uint64_t>(64, spread)))
+                : (C <= 256 ? static_cast<int>(std::max<uint64_t>(64, round_up(C, 64))) : 256);
     // Workgroups per rank that can all be resident at once with kernel `fn`. A grid planned at
     // the occupancy limit itself (every compute unit full) was once seen not to become resident
     // as a whole (a rank-local join timed out), so one workgroup per compute unit is left free
@@ -252,12 +262,7 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
       // Narrow units only while the rank's workgroups still get a compute unit each: beyond
       // that the doubled lane count measured slower than 16-byte units (128 KiB and more per
       // rank at N = 4).
-      const int rank_cus = h->placement == AR_PLACE_XCD
-                               ? cus_per_xcd * L.xcds_per_rank / L.ranks_per_xcd
-                           : h->placement == AR_PLACE_SAME ? cus_per_xcd / N
-                                                           : h->cu_count / N;
-      if (static_cast<uint64_t>(ctas) * L.threads < C || ctas > std::max(1, rank_cus))
-        return kNoNarrow;
+      if (static_cast<uint64_t>(ctas) * L.threads < C || ctas > rank_cus) return kNoNarrow;
     }
     if (static_cast<uint64_t>(ctas) * L.threads < C) {
       // The chunk does not fit one pass of the rank's lanes: the kernels built for one pass (the
@@ -269,6 +274,7 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
       if (multi != 0) {
         L.kernel_algo = multi;
         L.fn = ar_select_kernel(multi, h->dtype, nmax);
+        if (h->threads == 0) L.threads = 256;
         max_ctas = co_resident(L.fn);
         ctas = pick_ctas(max_ctas);
       }
