@@ -224,13 +224,13 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
                                          ? cus_per_xcd * L.xcds_per_rank / L.ranks_per_xcd
                                      : h->placement == AR_PLACE_SAME ? cus_per_xcd / N
                                                                      : h->cu_count / N);
-    // One-pass latency kernels: the smallest workgroup (whole waves) that covers the chunk with
-    // at most one workgroup per compute unit of the rank, so that each wave has a compute unit's
-    // memory pipeline to itself (measured 5-19 % lower p50 than one wider workgroup at
-    // N = 4..16). Other kernels: one workgroup just wide enough that no wave is idle for small
-    // chunks, 256-thread workgroups for larger ones.
-    const bool one_pass =
-        algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL || algo == AR_TWOSHOT;
+    // Every kernel of the public algorithms starts from the smallest workgroup (whole waves)
+    // that covers the chunk with at most one workgroup per compute unit of the rank, so that each
+    // wave has a compute unit's memory pipeline to itself (measured 5-33 % lower p50 than one
+    // wider workgroup at N = 4..16, the barrier baseline included). The multi-pass and bulk
+    // kernels that take over wider chunks use 256-thread workgroups.
+    const bool one_pass = algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL ||
+                          algo == AR_TWOSHOT || algo == AR_LL128_ATOMIC || algo == AR_BARRIER2;
     const uint64_t spread = round_up(ceil_div(C, static_cast<uint64_t>(rank_cus)), 64);
     L.threads = h->threads ? h->threads
                 : one_pass ? static_cast<int>(std::min<uint64_t>(256, std::max<uint64_t>(64, spread)))
