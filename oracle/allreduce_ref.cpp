@@ -21,6 +21,19 @@
 //            defined behaviour in C++).
 //   * fp64 : the same fold in binary64; the tests use it only as a near-exact yardstick.
 //
+// The standalone collectives below are the building blocks the paper names when it notes that
+// AllReduce is commonly decomposed into ReduceScatter + AllGather or Reduce + Broadcast
+// (§III "Low-Latency AllReduce Algorithms", opening paragraph), and that the Pith review says
+// can be rebuilt from the same barrier-free primitives ("If this is right"). The pages print no
+// definitions for them; the plainest reading, used here, is the usual one:
+//   * reduce-scatter: rank r's input holds N partitions of `recvcount` elements; rank r's output
+//     is the sum over ranks of partition r (the same left fold and precision as AllReduce):
+//         out[r][i] = x_0[r*recvcount + i] + ... + x_{N-1}[r*recvcount + i]
+//   * all-gather: out[r][q*sendcount + i] = x_q[i] for every rank r (a byte copy);
+//   * broadcast: out[r][i] = x_root[i] for every rank r (a byte copy).
+// With these readings, an all-gather of a reduce-scatter is exactly the AllReduce above (the
+// decomposition the paper cites), which is how the tests pin them.
+//
 // Every function returns 0 on success and -1 on a bad argument (nranks outside [1, 64], a
 // null pointer table or a null rank pointer while count > 0). count == 0 is a no-op.
 // Output buffers may alias the matching input buffer (in-place); the fold for element i reads
@@ -86,6 +99,37 @@ int fold_all(int nranks, const T* const* in, T* const* out, size_t count, Load l
   return 0;
 }
 
+// Reduce-scatter with the AllReduce fold: partition r of every rank's input summed into rank
+// r's output. Inputs and outputs must not overlap (the partition being folded would be
+// overwritten while later ranks still read it otherwise).
+template <typename T, typename Acc, typename Load, typename Store>
+int fold_scatter(int nranks, const T* const* in, T* const* out, size_t recvcount, Load load,
+                 Store store) {
+  if (recvcount == 0) return 0;
+  if (bad_args(nranks, in, out)) return -1;
+  for (int r = 0; r < nranks; ++r) {
+    if (in[r] == nullptr || out[r] == nullptr) return -1;
+  }
+  for (int r = 0; r < nranks; ++r) {
+    const size_t base = static_cast<size_t>(r) * recvcount;
+    for (size_t i = 0; i < recvcount; ++i) {
+      Acc acc = load(in[0][base + i]);
+      for (int q = 1; q < nranks; ++q) {
+        acc = acc + load(in[q][base + i]);
+      }
+      out[r][i] = store(acc);
+    }
+  }
+  return 0;
+}
+
+uint32_t i32_bits(int32_t v) { return static_cast<uint32_t>(v); }
+int32_t bits_i32(uint32_t a) {
+  int32_t s;
+  std::memcpy(&s, &a, sizeof s);
+  return s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,6 +158,60 @@ int oracle_allreduce_i32(int nranks, const int32_t* const* in, int32_t* const* o
         std::memcpy(&s, &a, sizeof s);
         return s;
       });
+}
+
+int oracle_reducescatter_f32(int nranks, const float* const* in, float* const* out,
+                              size_t recvcount) {
+  return fold_scatter<float, float>(
+      nranks, in, out, recvcount, [](float v) { return v; }, [](float a) { return a; });
+}
+
+int oracle_reducescatter_f64(int nranks, const double* const* in, double* const* out,
+                              size_t recvcount) {
+  return fold_scatter<double, double>(
+      nranks, in, out, recvcount, [](double v) { return v; }, [](double a) { return a; });
+}
+
+int oracle_reducescatter_bf16(int nranks, const uint16_t* const* in, uint16_t* const* out,
+                               size_t recvcount) {
+  return fold_scatter<uint16_t, float>(nranks, in, out, recvcount, widen_bf16, narrow_to_bf16);
+}
+
+int oracle_reducescatter_i32(int nranks, const int32_t* const* in, int32_t* const* out,
+                              size_t recvcount) {
+  return fold_scatter<int32_t, uint32_t>(nranks, in, out, recvcount, i32_bits, bits_i32);
+}
+
+// All-gather of `bytes` per rank: rank q's input lands at byte q*bytes of every output.
+int oracle_allgather(int nranks, const uint8_t* const* in, uint8_t* const* out, size_t bytes) {
+  if (bytes == 0) return 0;
+  if (bad_args(nranks, in, out)) return -1;
+  for (int r = 0; r < nranks; ++r) {
+    if (in[r] == nullptr || out[r] == nullptr) return -1;
+  }
+  for (int r = 0; r < nranks; ++r) {
+    for (int q = 0; q < nranks; ++q) {
+      for (size_t j = 0; j < bytes; ++j) {
+        out[r][static_cast<size_t>(q) * bytes + j] = in[q][j];
+      }
+    }
+  }
+  return 0;
+}
+
+// Broadcast of `bytes` from the root's buffer into every rank's output.
+int oracle_broadcast(int nranks, const uint8_t* root_in, uint8_t* const* out, size_t bytes) {
+  if (bytes == 0) return 0;
+  if (nranks < 1 || nranks > kMaxRanks || root_in == nullptr || out == nullptr) return -1;
+  for (int r = 0; r < nranks; ++r) {
+    if (out[r] == nullptr) return -1;
+  }
+  for (int r = 0; r < nranks; ++r) {
+    for (size_t j = 0; j < bytes; ++j) {
+      out[r][j] = root_in[j];
+    }
+  }
+  return 0;
 }
 
 uint16_t oracle_f32_to_bf16(float f) { return narrow_to_bf16(f); }

@@ -49,6 +49,13 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [ctypes.c_int, pp, pp, ctypes.c_size_t]
             fn.restype = ctypes.c_int
+        for name in ("oracle_reducescatter_f32", "oracle_reducescatter_f64",
+                     "oracle_reducescatter_bf16", "oracle_reducescatter_i32", "oracle_allgather"):
+            fn = getattr(L, name)
+            fn.argtypes = [ctypes.c_int, pp, pp, ctypes.c_size_t]
+            fn.restype = ctypes.c_int
+        L.oracle_broadcast.argtypes = [ctypes.c_int, ctypes.c_void_p, pp, ctypes.c_size_t]
+        L.oracle_broadcast.restype = ctypes.c_int
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         L.oracle_f32_to_bf16.restype = ctypes.c_uint16
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
@@ -100,6 +107,51 @@ def allreduce(arrays, out=None):
     _check(out)
     fn = getattr(lib(), _FN[dt])
     rc = fn(len(arrays), _ptr_table(arrays), _ptr_table(out), n)
+    if rc != 0:
+        raise ValueError(f"oracle rejected arguments (rc={rc})")
+    return out
+
+
+_RS_FN = {
+    np.dtype(np.float32): "oracle_reducescatter_f32",
+    np.dtype(np.float64): "oracle_reducescatter_f64",
+    np.dtype(np.uint16): "oracle_reducescatter_bf16",
+    np.dtype(np.int32): "oracle_reducescatter_i32",
+}
+
+
+def reducescatter(arrays):
+    """Reduce-scatter-sum: ``arrays`` holds one 1-D input per rank, N partitions of
+    ``size // N`` elements each; returns rank r's output (the fold of partition r over ranks)."""
+    dt, n = _check(arrays)
+    N = len(arrays)
+    if n % N != 0:
+        raise ValueError("input length must be a multiple of the rank count")
+    rc_n = n // N
+    out = [np.empty(rc_n, dtype=dt) for _ in arrays]
+    rc = getattr(lib(), _RS_FN[dt])(N, _ptr_table(arrays), _ptr_table(out), rc_n)
+    if rc != 0:
+        raise ValueError(f"oracle rejected arguments (rc={rc})")
+    return out
+
+
+def allgather(arrays):
+    """All-gather: returns, per rank, the concatenation of every rank's input in rank order."""
+    dt, n = _check(arrays)
+    N = len(arrays)
+    out = [np.empty(N * n, dtype=dt) for _ in arrays]
+    rc = lib().oracle_allgather(N, _ptr_table(arrays), _ptr_table(out), n * dt.itemsize)
+    if rc != 0:
+        raise ValueError(f"oracle rejected arguments (rc={rc})")
+    return out
+
+
+def broadcast(root_in: np.ndarray, nranks: int):
+    """Broadcast: returns ``nranks`` outputs, each a copy of ``root_in``."""
+    root_in = np.ascontiguousarray(root_in)
+    out = [np.empty_like(root_in) for _ in range(nranks)]
+    rc = lib().oracle_broadcast(int(nranks), root_in.ctypes.data, _ptr_table(out),
+                                root_in.nbytes)
     if rc != 0:
         raise ValueError(f"oracle rejected arguments (rc={rc})")
     return out

@@ -289,3 +289,91 @@ def test_bf16_allreduce_vs_float64_then_round(oracle_mod):
                     for v in exact])
     # one bf16 rounding (half an ulp) plus the binary32 fold error, far below an ulp here
     assert np.all(np.abs(got - exact) <= ulp)
+
+
+# ---------------------------------------------------------------- standalone collectives
+#
+# Reduce-scatter, all-gather and broadcast have no printed worked example on the pages; they are
+# pinned by the decomposition the paper cites (an all-gather of a reduce-scatter is the
+# AllReduce, itself pinned above), by integer arithmetic done in numpy with an independent
+# formula, and by tagged inputs whose positions can be decoded.
+
+def _rand_rows(g, n, count, dt):
+    if dt == np.int32:
+        return [g.integers(-(1 << 20), (1 << 20) + 1, size=count).astype(np.int32) for _ in range(n)]
+    if dt == np.uint16:
+        import torch
+        return [torch.from_numpy(g.normal(size=count).astype(np.float32)).to(torch.bfloat16)
+                .view(torch.int16).numpy().view(np.uint16).copy() for _ in range(n)]
+    return [g.uniform(-1, 1, size=count).astype(dt) for _ in range(n)]
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("dt", [np.float32, np.uint16, np.int32, np.float64])
+def test_allgather_of_reducescatter_is_allreduce(oracle_mod, n, dt):
+    """The decomposition AllReduce = AllGather(ReduceScatter) holds bit for bit (a wrong
+    partition index, a transposed rank/partition loop or a different fold order breaks it)."""
+    g = np.random.default_rng(100 + n)
+    rc = 13
+    x = _rand_rows(g, n, n * rc, dt)
+    rs = oracle_mod.reducescatter(x)
+    ag = oracle_mod.allgather(rs)
+    ar = oracle_mod.allreduce(x)
+    for r in range(n):
+        assert rs[r].size == rc
+        assert np.array_equal(ag[r].view(np.uint8), ar[r].view(np.uint8))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("rc", [1, 2, 3])
+def test_reducescatter_int_brute_force(oracle_mod, n, rc):
+    """Small integer inputs against numpy's column sums of the [rank, partition, element] view
+    (an independent formula: exact integer arithmetic, no fold)."""
+    g = np.random.default_rng(7 * n + rc)
+    for _ in range(20):
+        x = g.integers(-2, 3, size=(n, n * rc)).astype(np.int32)
+        got = oracle_mod.reducescatter([x[q].copy() for q in range(n)])
+        want = x.reshape(n, n, rc).astype(np.int64).sum(axis=0)
+        for r in range(n):
+            assert np.array_equal(got[r].astype(np.int64), want[r])
+
+
+@pytest.mark.parametrize("n", [2, 5, 16])
+def test_reducescatter_rank_constant(oracle_mod, n):
+    """Rank q filled with q: every element of every output is N(N-1)/2."""
+    x = [np.full(n * 9, q, dtype=np.float32) for q in range(n)]
+    for o in oracle_mod.reducescatter(x):
+        assert np.array_equal(o, np.full(9, n * (n - 1) // 2, dtype=np.float32))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 8, 16])
+def test_allgather_tagged_positions(oracle_mod, n):
+    """Element i of rank q's input carries q * 100000 + i; in every output, position
+    q * count + i must decode back to (q, i)."""
+    count = 37
+    x = [(q * 100000 + np.arange(count)).astype(np.int32) for q in range(n)]
+    for o in oracle_mod.allgather(x):
+        assert o.size == n * count
+        pos = np.arange(n * count)
+        assert np.array_equal(o // 100000, pos // count)
+        assert np.array_equal(o % 100000, pos % count)
+
+
+@pytest.mark.parametrize("dt", [np.uint16, np.float32])
+def test_allgather_single_rank_and_bytes(oracle_mod, dt):
+    """N = 1 is a copy; every byte pattern (NaNs included) passes through untouched."""
+    g = np.random.default_rng(3)
+    raw = g.integers(0, 256, size=64 * np.dtype(dt).itemsize).astype(np.uint8)
+    x = raw.view(dt).copy()
+    assert np.array_equal(oracle_mod.allgather([x])[0].view(np.uint8), raw)
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 16])
+def test_broadcast_copies_root(oracle_mod, n):
+    """Every output equals the root's input byte for byte, for any byte pattern."""
+    g = np.random.default_rng(n)
+    root = g.integers(0, 256, size=1001).astype(np.uint8)
+    outs = oracle_mod.broadcast(root, n)
+    assert len(outs) == n
+    for o in outs:
+        assert np.array_equal(o, root)
