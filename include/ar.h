@@ -60,7 +60,12 @@ typedef enum {
   AR_TWOSHOT = 3,
   AR_LL128_ATOMIC = 4,
   AR_BARRIER2 = 5,
-  AR_BARRIER_ONLY = 6
+  AR_BARRIER_ONLY = 6,
+  /* values 7..11 are internal kernel families; the standalone collectives below are called
+     through their own entry points and named by these ids in ar_bench and ar_alg_bytes */
+  AR_REDUCESCATTER = 12,
+  AR_ALLGATHER = 13,
+  AR_BROADCAST = 14
 } ar_algo;
 
 enum {
@@ -110,6 +115,47 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype);
 int ar_allreduce(ar_handle* h, const void* const in[], void* const out[], size_t count,
                  ar_algo algo, void* stream);
 
+/*
+ * Standalone collectives from the same barrier-free primitives. The paper notes that AllReduce is
+ * commonly decomposed into ReduceScatter + AllGather or Reduce + Broadcast (Every µs Matters,
+ * §III opening paragraph), and the Pith review of it ("If this is right") expects these
+ * collectives to be rebuilt with the same LL / sentinel / double-buffering pattern. All three
+ * push raw 16-byte units into sentinel-armed scratch slots, poll until the sentinel is gone,
+ * consume and re-arm (§IV "Sentinel"), with step s on scratch buffer s & 1 (§IV "Bidirectional
+ * Communication Double Buffering"). Common rules: host arrays of N device pointers, every
+ * buffer 16-byte aligned; outputs of different ranks must not overlap; count 0 is a no-op that
+ * still advances the sequence number; the call only enqueues work on `stream` (ordering and
+ * ownership as for ar_allreduce); device timeouts are reported through ar_check(); AR_ETOOBIG
+ * when an input or output exceeds the handle's max_bytes per rank.
+ *
+ * ar_reducescatter: out[r][i] = in[0][r*recvcount + i] + ... + in[N-1][r*recvcount + i] for
+ *   i < recvcount (the AllReduce fold: rank order, fp32 accumulation for bf16, one rounding).
+ *   in[r] holds N * recvcount elements, out[r] recvcount; recvcount * sizeof(dtype) must be a
+ *   multiple of 16 bytes (AR_EINVAL otherwise). In place: out[r] == in[r] + r * recvcount
+ *   elements; any other overlap of an output with an input is AR_EINVAL.
+ */
+int ar_reducescatter(ar_handle* h, const void* const in[], void* const out[], size_t recvcount,
+                     void* stream);
+
+/*
+ * ar_allgather: out[r][q*sendcount + i] = in[q][i] for every rank r, source q and i < sendcount.
+ *   in[r] holds sendcount elements, out[r] N * sendcount; sendcount * sizeof(dtype) must be a
+ *   multiple of 16 bytes (AR_EINVAL otherwise). In place: in[r] == out[r] + r * sendcount
+ *   elements; any other overlap of an output with an input is AR_EINVAL.
+ */
+int ar_allgather(ar_handle* h, const void* const in[], void* const out[], size_t sendcount,
+                 void* stream);
+
+/*
+ * ar_broadcast: out[r][i] = in[i] for every rank r and i < count, where `in` is the input of
+ *   rank `root` (0..N-1; AR_EINVAL otherwise). Any count. out[root] == in is allowed; any other
+ *   overlap of an output with `in` is AR_EINVAL. Only the root sends data, so each receiver hands
+ *   its scratch buffer back to the root with a flag after consuming a step (the root reuses a
+ *   buffer only after every receiver's flag of two steps before).
+ */
+int ar_broadcast(ar_handle* h, const void* in, void* const out[], size_t count, int root,
+                 void* stream);
+
 /* ar_destroy: synchronise the handle's last stream and free everything. NULL is ignored. */
 void ar_destroy(ar_handle* h);
 
@@ -136,6 +182,9 @@ int ar_check(ar_handle* h);
  *   elapsed_ms        : if not NULL, the launch's duration from HIP events on `stream`.
  * Synchronous. Ticks convert to seconds with ar_wallclock_hz(). AR_BARRIER_ONLY measures one
  * cross-rank barrier per iteration and ignores the data arguments (they may be NULL).
+ * AR_REDUCESCATTER, AR_ALLGATHER and AR_BROADCAST run the standalone collectives instead, with
+ * `count` as their entry points take it (recvcount, sendcount, count) and buffers sized as
+ * there; the broadcast root is AR_OPT_ROOT (only the root's input pointers are read).
  */
 int ar_bench(ar_handle* h, const void* const* in_sets, void* const* out_sets, int nsets,
              size_t count, ar_algo algo, int iters, uint64_t* t_start, uint64_t* t_end,
@@ -158,6 +207,7 @@ double ar_wallclock_hz(void);
  *                        are 0), the one-pass sentinel kernels (one-shot and two-shot) move
  *                        8-byte units if the message still fits one pass of co-resident lanes
  *                        (twice the lanes, half the fold per lane); 0: always 16-byte units [1]
+ *   AR_OPT_ROOT          ar_bench of AR_BROADCAST only: the root rank [0]
  */
 typedef enum {
   AR_OPT_TIMEOUT_US = 0,
@@ -166,7 +216,8 @@ typedef enum {
   AR_OPT_THREADS = 3,
   AR_OPT_PLACEMENT = 4,
   AR_OPT_DRIFT = 5,
-  AR_OPT_NARROW = 6
+  AR_OPT_NARROW = 6,
+  AR_OPT_ROOT = 7
 } ar_option;
 int ar_set_option(ar_handle* h, ar_option opt, int64_t value);
 
@@ -190,8 +241,9 @@ int64_t ar_region_bytes(ar_handle* h, int region);
  * outputs; an LL line is 16 bytes per 8 bytes of payload). One-shot LL 2NS + 4N(N-1)S; one-shot
  * sentinel 2NS + 3N(N-1)S; two-shot (one pass) (N+1)S + 7(N-1)S; two-shot (bulk, completion
  * flags) (N+1)S + 5(N-1)S; LL128-style 2NS + 3S + 4(N-1)S; two-barrier 2NS + 2N(N-1)S, with S
- * the bytes per rank. Returns the count, or a negative error code (bad handle or algorithm,
- * AR_ETOOBIG).
+ * the bytes per rank. For AR_REDUCESCATTER and AR_ALLGATHER (count as their entry points take
+ * it, x = count * sizeof(dtype)): N ((N+1) x + 3 (N-1) x); for AR_BROADCAST (N+1) x + 3 (N-1) x.
+ * Returns the count, or a negative error code (bad handle or algorithm, AR_ETOOBIG).
  */
 int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo);
 int ar_read_region(ar_handle* h, int rank, int region, void* host_dst, size_t bytes);

@@ -19,10 +19,11 @@ LIB_PATH = os.path.join(_PKG, "libar.so")
 AR_FLOAT32, AR_BFLOAT16, AR_INT32 = 0, 1, 2
 (AR_ALGO_AUTO, AR_ONESHOT_LL, AR_ONESHOT_SENTINEL, AR_TWOSHOT, AR_LL128_ATOMIC, AR_BARRIER2,
  AR_BARRIER_ONLY) = range(7)
+AR_REDUCESCATTER, AR_ALLGATHER, AR_BROADCAST = 12, 13, 14
 AR_OK, AR_EINVAL, AR_ETOOBIG, AR_ENOTSUP, AR_EHIP, AR_ETIMEOUT, AR_ENORES = 0, -1, -2, -3, -4, -5, -6
 AR_PLACE_XCD, AR_PLACE_SAME, AR_PLACE_LINEAR = 0, 1, 2
 (AR_OPT_TIMEOUT_US, AR_OPT_WITHHOLD_RANK, AR_OPT_CTAS, AR_OPT_THREADS, AR_OPT_PLACEMENT,
- AR_OPT_DRIFT, AR_OPT_NARROW) = range(7)
+ AR_OPT_DRIFT, AR_OPT_NARROW, AR_OPT_ROOT) = range(8)
 (REGION_P1, REGION_P2, REGION_LL, REGION_ACC, REGION_CNT, REGION_BAR, REGION_BDAT,
  REGION_LL_NEAR, REGION_P1_NEAR, REGION_P2_NEAR, REGION_PF1, REGION_PF2, REGION_FLG) = range(13)
 
@@ -34,12 +35,15 @@ ALGOS = {
     "ll128_atomic": AR_LL128_ATOMIC,
     "barrier2": AR_BARRIER2,
     "barrier_only": AR_BARRIER_ONLY,
+    "reducescatter": AR_REDUCESCATTER,
+    "allgather": AR_ALLGATHER,
+    "broadcast": AR_BROADCAST,
 }
 DTYPES = {"f32": AR_FLOAT32, "bf16": AR_BFLOAT16, "i32": AR_INT32}
 
 # Every symbol include/ar.h declares.
 EXPORTS = (
-    "ar_create", "ar_allreduce", "ar_destroy", "ar_last_error", "ar_check", "ar_bench",
+    "ar_create", "ar_allreduce", "ar_reducescatter", "ar_allgather", "ar_broadcast", "ar_destroy", "ar_last_error", "ar_check", "ar_bench",
     "ar_wallclock_hz", "ar_set_option", "ar_region_bytes", "ar_alg_bytes", "ar_read_region",
     "ar_epoch",
     "ar_sol", "ar_pingpong", "ar_torn_lines", "ar_stream_copy",
@@ -94,6 +98,9 @@ def lib() -> ctypes.CDLL:
     sig = {
         "ar_create": ([i32, sz, i32], vp),
         "ar_allreduce": ([vp, pp, pp, sz, i32, vp], i32),
+        "ar_reducescatter": ([vp, pp, pp, sz, vp], i32),
+        "ar_allgather": ([vp, pp, pp, sz, vp], i32),
+        "ar_broadcast": ([vp, vp, pp, sz, i32, vp], i32),
         "ar_destroy": ([vp], None),
         "ar_last_error": ([], ctypes.c_char_p),
         "ar_check": ([vp], i32),
@@ -165,6 +172,18 @@ def ar_destroy(h: int) -> None:
 
 def ar_allreduce(h: int, ins, outs, count: int, algo: int, stream=None) -> None:
     _ok(lib().ar_allreduce(h, _table(ins), _table(outs), int(count), int(algo), _stream(stream)))
+
+
+def ar_reducescatter(h: int, ins, outs, recvcount: int, stream=None) -> None:
+    _ok(lib().ar_reducescatter(h, _table(ins), _table(outs), int(recvcount), _stream(stream)))
+
+
+def ar_allgather(h: int, ins, outs, sendcount: int, stream=None) -> None:
+    _ok(lib().ar_allgather(h, _table(ins), _table(outs), int(sendcount), _stream(stream)))
+
+
+def ar_broadcast(h: int, inp, outs, count: int, root: int, stream=None) -> None:
+    _ok(lib().ar_broadcast(h, _ptr(inp), _table(outs), int(count), int(root), _stream(stream)))
 
 
 def ar_check(h: int) -> None:

@@ -25,6 +25,10 @@ enum Algo : int {
   // internal: one-pass sentinel kernels with 8-byte units (two lanes per 16 bytes)
   ALGO_ONESHOT_SENTINEL_NARROW = 10,
   ALGO_TWOSHOT_NARROW = 11,
+  // the standalone collectives built from the same primitives
+  ALGO_REDUCESCATTER = 12,
+  ALGO_ALLGATHER = 13,
+  ALGO_BROADCAST = 14,
 };
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).
@@ -102,7 +106,8 @@ struct Args {
   uint64_t* ts_end;
   uint64_t e0;          // sequence number of the first step of this launch
   uint64_t timeout_ticks;
-  uint32_t nbytes;      // bytes per rank
+  uint32_t nbytes;      // input bytes per rank
+  uint32_t out_nbytes;  // output bytes per rank (equal to nbytes for AllReduce)
   uint32_t chunk_units; // units per chunk: one-shot message chunk, or two-shot partition chunk
   uint32_t part_units;  // two-shot partition size in units (a multiple of chunk_units)
   int nranks;
@@ -116,6 +121,7 @@ struct Args {
   int withhold;         // fault injection: this rank sends nothing (-1: off)
   int drift;            // rank-drift stress: up to this many sleeps per iteration (0: off)
   int algo;
+  int root;             // broadcast: the rank whose input every rank receives
 };
 
 }  // namespace ar

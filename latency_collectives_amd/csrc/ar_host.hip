@@ -122,6 +122,7 @@ struct ar_handle {
   int placement = AR_PLACE_XCD;
   int drift = 0;
   int narrow = 1;  // one-pass sentinel kernels may use 8-byte units
+  int root = 0;    // ar_bench of AR_BROADCAST: the root rank
   void** tab = nullptr;
   size_t tab_cap = 0;
   uint64_t* ts = nullptr;
@@ -179,6 +180,15 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
       units = ceil_div(nbytes, 16);
       cap_units = h->rg[RG_BDAT].slot / 16;
       break;
+    case AR_REDUCESCATTER:  // nbytes is the whole input: N partitions of whole units
+      units = ceil_div(nbytes, 16ull * static_cast<uint64_t>(N));
+      cap_units = h->rg[RG_P1].slot / 16;
+      break;
+    case AR_ALLGATHER:
+    case AR_BROADCAST:
+      units = ceil_div(nbytes, 16);
+      cap_units = h->rg[RG_P1].slot / 16;
+      break;
     case AR_TWOSHOT:
     case AR_LL128_ATOMIC:
       units = ceil_div(ceil_div(nbytes, line), N);  // one partition
@@ -230,7 +240,9 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
     // wider workgroup at N = 4..16, the barrier baseline included). The multi-pass and bulk
     // kernels that take over wider chunks use 256-thread workgroups.
     const bool one_pass = algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL ||
-                          algo == AR_TWOSHOT || algo == AR_LL128_ATOMIC || algo == AR_BARRIER2;
+                          algo == AR_TWOSHOT || algo == AR_LL128_ATOMIC || algo == AR_BARRIER2 ||
+                          algo == AR_REDUCESCATTER || algo == AR_ALLGATHER ||
+                          algo == AR_BROADCAST;
     const uint64_t spread = round_up(ceil_div(C, static_cast<uint64_t>(rank_cus)), 64);
     L.threads = h->threads ? h->threads
                 : one_pass ? static_cast<int>(std::min<uint64_t>(256, std::max<uint64_t>(64, spread)))
@@ -378,6 +390,8 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
   const double ticks = static_cast<double>(h->timeout_us) * h->clock_hz * 1e-6;
   a.timeout_ticks = ticks < 1.0 ? 1ull : static_cast<uint64_t>(ticks);
   a.nbytes = static_cast<uint32_t>(nbytes);
+  a.out_nbytes = static_cast<uint32_t>(nbytes);
+  a.root = 0;
   a.chunk_units = L.chunk_units;
   a.part_units = L.part_units;
   a.nranks = h->nranks;
@@ -427,6 +441,43 @@ int resolve_algo(ar_handle* h, int algo, uint64_t nbytes) {
 bool overlap(const void* a, const void* b, uint64_t n) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + n && y < x + n;
+}
+
+bool overlap2(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+bool is_collective(int algo) {
+  return algo == AR_REDUCESCATTER || algo == AR_ALLGATHER || algo == AR_BROADCAST;
+}
+
+// Input and output bytes per rank of one call (count as the entry point takes it: output
+// elements per rank for reduce-scatter, input elements per rank for all-gather, elements for
+// broadcast and AllReduce), checked against the handle.
+int op_bytes(ar_handle* h, int algo, size_t count, uint64_t& in_b, uint64_t& out_b) {
+  const uint64_t es = static_cast<uint64_t>(elem_bytes(h->dtype));
+  const uint64_t N = static_cast<uint64_t>(h->nranks);
+  const uint64_t x = static_cast<uint64_t>(count) * es;
+  if (count != 0 && (x / count != es || x > (1ull << 40))) return ar_fail(AR_ETOOBIG, "count overflows");
+  in_b = algo == AR_REDUCESCATTER ? x * N : x;
+  out_b = algo == AR_ALLGATHER ? x * N : x;
+  if ((algo == AR_REDUCESCATTER || algo == AR_ALLGATHER) && x % 16 != 0)
+    return ar_fail(AR_EINVAL, "a partition of %llu bytes is not a multiple of 16 bytes",
+                   static_cast<unsigned long long>(x));
+  if (std::max(in_b, out_b) > h->max_bytes)
+    return ar_fail(AR_ETOOBIG, "%llu bytes per rank exceed max_bytes %zu",
+                   static_cast<unsigned long long>(std::max(in_b, out_b)), h->max_bytes);
+  return AR_OK;
+}
+
+// Kernel arguments of a standalone collective that differ from AllReduce's.
+void collective_args(int algo, uint64_t in_b, uint64_t out_b, int N, int root, ar::Args& a) {
+  a.nbytes = static_cast<uint32_t>(in_b);
+  a.out_nbytes = static_cast<uint32_t>(out_b);
+  if (algo == AR_REDUCESCATTER) a.part_units = static_cast<uint32_t>(in_b / N / 16);
+  if (algo == AR_ALLGATHER) a.part_units = static_cast<uint32_t>(in_b / 16);
+  a.root = root;
 }
 
 int check_status(ar_handle* h) {
@@ -622,6 +673,10 @@ int ar_set_option(ar_handle* h, ar_option opt, int64_t v) {
       if (v != 0 && v != 1) return ar_fail(AR_EINVAL, "narrow must be 0 or 1");
       h->narrow = static_cast<int>(v);
       return AR_OK;
+    case AR_OPT_ROOT:
+      if (v < 0 || v >= h->nranks) return ar_fail(AR_EINVAL, "root out of range");
+      h->root = static_cast<int>(v);
+      return AR_OK;
   }
   return ar_fail(AR_EINVAL, "unknown option %d", static_cast<int>(opt));
 }
@@ -679,6 +734,95 @@ int ar_allreduce(ar_handle* h, const void* const in[], void* const out[], size_t
   return AR_OK;
 }
 
+namespace {
+
+// Shared body of ar_reducescatter, ar_allgather and ar_broadcast (`in` has N entries; only
+// in[root] is read for broadcast).
+int run_collective(ar_handle* h, int algo, const void* const in[], void* const out[],
+                   size_t count, int root, void* stream) {
+  if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
+  if (in == nullptr || out == nullptr) return ar_fail(AR_EINVAL, "null pointer table");
+  const int N = h->nranks;
+  if (algo == AR_BROADCAST && (root < 0 || root >= N))
+    return ar_fail(AR_EINVAL, "root %d out of range", root);
+  int rc = check_status(h);
+  if (rc != AR_OK) return rc;
+  uint64_t in_b = 0, out_b = 0;
+  rc = op_bytes(h, algo, count, in_b, out_b);
+  if (rc != AR_OK) return rc;
+  for (int r = 0; r < N; ++r) {
+    const bool reads = algo != AR_BROADCAST || r == root;
+    if ((reads && in[r] == nullptr) || out[r] == nullptr)
+      return ar_fail(AR_EINVAL, "null buffer for rank %d", r);
+    if (((reads ? reinterpret_cast<uintptr_t>(in[r]) : 0) | reinterpret_cast<uintptr_t>(out[r])) & 15u)
+      return ar_fail(AR_EINVAL, "buffers of rank %d are not 16-byte aligned", r);
+  }
+  if (count > 0) {
+    // in place only in the usual forms: a reduce-scatter output at its own partition of the
+    // input, an all-gather input at its own partition of the output, the broadcast root's output
+    // on its input
+    const uint64_t x = algo == AR_REDUCESCATTER ? out_b : in_b;
+    for (int r = 0; r < N; ++r)
+      for (int q = 0; q < N; ++q) {
+        if (q != r && overlap(out[r], out[q], out_b))
+          return ar_fail(AR_EINVAL, "outputs of ranks %d and %d overlap", r, q);
+        if (algo == AR_BROADCAST && q != root) continue;
+        const bool in_place =
+            q == r && (algo == AR_REDUCESCATTER
+                           ? static_cast<const uint8_t*>(out[r]) ==
+                                 static_cast<const uint8_t*>(in[r]) + r * x
+                       : algo == AR_ALLGATHER
+                           ? static_cast<const uint8_t*>(in[r]) ==
+                                 static_cast<const uint8_t*>(out[r]) + r * x
+                           : out[r] == in[r]);
+        if (overlap2(out[r], out_b, in[q], in_b) && !in_place)
+          return ar_fail(AR_EINVAL, "output of rank %d overlaps input of rank %d", r, q);
+      }
+  }
+  if (count == 0) {
+    h->epoch += 1;
+    return AR_OK;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Launch L;
+  rc = plan(h, algo, in_b, L);
+  if (rc != AR_OK) return rc;
+  ar::Args a = base_args(h, algo, in_b, L);
+  collective_args(algo, in_b, out_b, N, root, a);
+  for (int r = 0; r < N; ++r) {
+    a.in[r] = (algo != AR_BROADCAST || r == root) ? in[r] : nullptr;
+    a.out[r] = out[r];
+  }
+  if (algo == AR_BROADCAST) {
+    // non-root ranks never load their input: give them the root's (a valid descriptor base)
+    for (int r = 0; r < N; ++r) a.in[r] = in[root];
+  }
+  rc = launch(L.fn, L.grid, L.threads, a, s);
+  if (rc != AR_OK) return rc;
+  h->epoch += static_cast<uint64_t>(L.chunks);
+  h->last_stream = s;
+  return AR_OK;
+}
+
+}  // namespace
+
+int ar_reducescatter(ar_handle* h, const void* const in[], void* const out[], size_t recvcount,
+                     void* stream) {
+  return run_collective(h, AR_REDUCESCATTER, in, out, recvcount, 0, stream);
+}
+
+int ar_allgather(ar_handle* h, const void* const in[], void* const out[], size_t sendcount,
+                 void* stream) {
+  return run_collective(h, AR_ALLGATHER, in, out, sendcount, 0, stream);
+}
+
+int ar_broadcast(ar_handle* h, const void* in, void* const out[], size_t count, int root,
+                 void* stream) {
+  if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
+  std::vector<const void*> tab(static_cast<size_t>(h->nranks), in);
+  return run_collective(h, AR_BROADCAST, tab.data(), out, count, root, stream);
+}
+
 int ar_check(ar_handle* h) {
   if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
   hipError_t e = h->last_stream ? hipStreamSynchronize(h->last_stream) : hipDeviceSynchronize();
@@ -691,19 +835,19 @@ int ar_bench(ar_handle* h, const void* const* in_sets, void* const* out_sets, in
              double* elapsed_ms, void* stream) {
   if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
   if (iters < 1 || iters > 1000000) return ar_fail(AR_EINVAL, "iters must be in [1, 1e6]");
-  if (algo < AR_ALGO_AUTO || algo > AR_BARRIER_ONLY)
+  if ((algo < AR_ALGO_AUTO || algo > AR_BARRIER_ONLY) && !is_collective(algo))
     return ar_fail(AR_EINVAL, "unknown algorithm %d", static_cast<int>(algo));
   int rc = check_status(h);
   if (rc != AR_OK) return rc;
   const int N = h->nranks;
   const bool barrier_only = algo == AR_BARRIER_ONLY;
-  uint64_t nbytes = 0;
+  uint64_t nbytes = 0, out_bytes = 0;
   if (!barrier_only) {
     if (in_sets == nullptr || out_sets == nullptr) return ar_fail(AR_EINVAL, "null set tables");
     if (nsets < 1 || nsets > 65536) return ar_fail(AR_EINVAL, "nsets must be in [1, 65536]");
-    nbytes = static_cast<uint64_t>(count) * elem_bytes(h->dtype);
-    if (nbytes == 0) return ar_fail(AR_EINVAL, "ar_bench needs count > 0");
-    if (nbytes > h->max_bytes) return ar_fail(AR_ETOOBIG, "message exceeds max_bytes");
+    if (count == 0) return ar_fail(AR_EINVAL, "ar_bench needs count > 0");
+    rc = op_bytes(h, algo, count, nbytes, out_bytes);
+    if (rc != AR_OK) return rc;
     for (int i = 0; i < nsets * N; ++i) {
       if (in_sets[i] == nullptr || out_sets[i] == nullptr)
         return ar_fail(AR_EINVAL, "null buffer in set table");
@@ -719,6 +863,7 @@ int ar_bench(ar_handle* h, const void* const* in_sets, void* const* out_sets, in
   rc = plan(h, alg, nbytes, L);
   if (rc != AR_OK) return rc;
   ar::Args a = base_args(h, alg, nbytes, L);
+  if (is_collective(alg)) collective_args(alg, nbytes, out_bytes, N, h->root, a);
   a.iters = iters;
   a.drift = h->drift;
   a.nsets = nsets;
@@ -809,6 +954,20 @@ int ar_bench(ar_handle* h, const void* const* in_sets, void* const* out_sets, in
 
 int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
   if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
+  if (is_collective(algo)) {
+    // Every logical read and write once. Per rank of a reduce-scatter (x = output bytes): its
+    // N input partitions, N-1 pushes, N-1 slot reads and re-arms, x out. Per rank of an
+    // all-gather (x = input bytes): x in, N-1 pushes, N x out, N-1 slot reads and re-arms. A
+    // broadcast of x: the root reads x, pushes N-1 and writes x; each other rank reads, writes
+    // out and re-arms x. All three are (N+1) x + 3 (N-1) x, per rank for the first two.
+    uint64_t in_b = 0, out_b = 0;
+    const int rc = op_bytes(h, algo, count, in_b, out_b);
+    if (rc != AR_OK) return rc;
+    const uint64_t N = static_cast<uint64_t>(h->nranks);
+    const uint64_t x = algo == AR_REDUCESCATTER ? out_b : in_b;
+    const uint64_t one = (N + 1) * x + 3 * (N - 1) * x;
+    return static_cast<int64_t>(algo == AR_BROADCAST ? one : N * one);
+  }
   if (algo < AR_ALGO_AUTO || algo > AR_BARRIER2)
     return ar_fail(AR_EINVAL, "algorithm %d is not valid", static_cast<int>(algo));
   const uint64_t S = static_cast<uint64_t>(count) * elem_bytes(h->dtype);

@@ -971,6 +971,180 @@ __device__ bool step_barrier2(const Args& a, const Ctx& c, uint64_t s, rsrc_t in
   return true;
 }
 
+// ------------------------------------------------------------------ standalone collectives
+//
+// Reduce-scatter, all-gather and broadcast from the same primitives as the AllReduce kernels
+// (the paper notes that AllReduce is commonly split into reduce-scatter + all-gather or
+// reduce + broadcast, §III opening paragraph; the Pith review expects these to be rebuilt with
+// the same barrier-free pattern): 16-byte units pushed raw into the sentinel-armed p1 slots,
+// polled until the sentinel is gone, consumed and re-armed; step s uses buffer s & 1. Each lane
+// handles units t0 + lane + j * T of the chunk, the same units on every rank and in every step,
+// so every credit below is a per-lane fact. Every step first waits for all of its wave's older
+// stores (the re-arms of the previous step) before it pushes. Reduce-scatter and all-gather
+// partitions are whole units; `part_units` is their exact size and the last chunk may be short.
+
+// Units of chunk k (the last one may be shorter than chunk_units).
+__device__ __forceinline__ uint32_t chunk_len(const Args& a, int k, uint32_t total) {
+  const uint32_t u0 = static_cast<uint32_t>(k) * a.chunk_units;
+  return u0 >= total ? 0u : min(a.chunk_units, total - u0);
+}
+
+// Reduce-scatter: rank r's input holds N partitions of part_units units. Partition (r + j) % N
+// goes to that owner's slot r; the owner folds its own partition and the N - 1 received ones in
+// rank order into its output. Every pair of ranks exchanges data in every step, so, as in the
+// one-shot kernels, receiving a peer's step s-1 data is the credit to overwrite its buffer of
+// step s-2.
+template <int DT, int NMAX>
+__device__ bool step_reducescatter(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
+                                   rsrc_t out_r, int k, uint64_t& t0, uint64_t& t1) {
+  const int N = a.nranks, r = c.rank;
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t slot = a.p1.slot, P = a.part_units;
+  const uint32_t unit0 = static_cast<uint32_t>(k) * a.chunk_units;
+  const uint32_t CK = chunk_len(a, k, P);
+  const uint32_t mine = (b * N + r) * slot;
+  const rsrc_t own = region_rsrc(a, r, a.p1);
+  const uint32_t peers = peer_mask(N, r);
+  const u32x4 sent = sentinel_unit<DT, 16>();
+  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+  stamp_start(t0, k);
+  wait_all_mem();
+  if (r != a.withhold) {
+    for (uint32_t i0 = c.t0; i0 < CK; i0 += c.T) {
+      const uint32_t i = i0 + c.lane;
+      const bool act = i < CK;
+      uint32_t w[NMAX][4];
+      load_partitions<DT, NMAX>(a, r, in_r, k, i, act, 1, w);
+      const uint32_t off = act ? mine + i * 16u : kDrop;
+#pragma unroll
+      for (int j = 1; j < NMAX; ++j)
+        st16<kCoh>(peer_rsrc(a, r, j, a.p1), off, u32x4{w[j][0], w[j][1], w[j][2], w[j][3]});
+    }
+  }
+  for (uint32_t i0 = c.t0; i0 < CK; i0 += c.T) {
+    const uint32_t i = i0 + c.lane;
+    const bool act = i < CK;
+    const uint32_t mask = act ? peers : 0u;
+    const uint32_t off0 = b * N * slot + i * 16u;
+    uint32_t x[4];
+    load_unit<DT, 16, kPlain, false>(in_r, act ? (r * P + unit0 + i) * 16u : kDrop, a.nbytes, x);
+    u32x4 v[NMAX];
+    if (!poll_lines<NMAX>(a, own, off0, slot, mask, v, ready, r, s)) return false;
+    uint32_t o[4];
+    fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
+    store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.out_nbytes, o);
+    rearm<NMAX>(own, off0, slot, mask, sent);
+  }
+  wait_all_mem();
+  t1 = now_ticks();
+  return true;
+}
+
+// All-gather: rank r's input (part_units units) goes to every peer's slot r and to partition r
+// of its own output; every other rank's input is copied from its slot into partition q. The
+// credit is the one of the reduce-scatter: every pair exchanges data in every step.
+template <int DT, int NMAX>
+__device__ bool step_allgather(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
+                               rsrc_t out_r, int k, uint64_t& t0, uint64_t& t1) {
+  const int N = a.nranks, r = c.rank;
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t slot = a.p1.slot, P = a.part_units;
+  const uint32_t unit0 = static_cast<uint32_t>(k) * a.chunk_units;
+  const uint32_t CK = chunk_len(a, k, P);
+  const bool sends = r != a.withhold;
+  const uint32_t mine = (b * N + r) * slot;
+  const rsrc_t own = region_rsrc(a, r, a.p1);
+  const uint32_t peers = peer_mask(N, r);
+  const u32x4 sent = sentinel_unit<DT, 16>();
+  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+  stamp_start(t0, k);
+  wait_all_mem();
+  for (uint32_t i0 = c.t0; i0 < CK; i0 += c.T) {
+    const uint32_t i = i0 + c.lane;
+    const bool act = i < CK;
+    uint32_t x[4];
+    load_unit<DT, 16, kPlain, false>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
+    if (sends) push_peers<NMAX>(a, r, a.p1, act ? mine + i * 16u : kDrop, u32x4{x[0], x[1], x[2], x[3]});
+    store_unit<DT, 16>(out_r, act ? (r * P + unit0 + i) * 16u : kDrop, a.out_nbytes, x);
+  }
+  for (uint32_t i0 = c.t0; i0 < CK; i0 += c.T) {
+    const uint32_t i = i0 + c.lane;
+    const bool act = i < CK;
+    const uint32_t mask = act ? peers : 0u;
+    const uint32_t off0 = b * N * slot + i * 16u;
+    u32x4 v[NMAX];
+    if (!poll_lines<NMAX>(a, own, off0, slot, mask, v, ready, r, s)) return false;
+#pragma unroll
+    for (int q = 0; q < NMAX; ++q) {
+      const uint32_t o[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+      store_unit<DT, 16>(out_r, ((mask >> q) & 1u) ? (q * P + unit0 + i) * 16u : kDrop,
+                         a.out_nbytes, o);
+    }
+    rearm<NMAX>(own, off0, slot, mask, sent);
+  }
+  wait_all_mem();
+  t1 = now_ticks();
+  return true;
+}
+
+// Broadcast: the root pushes every unit of its input into slot `root` of every peer and copies it
+// to its own output; every other rank polls that one slot, copies the unit out and re-arms it.
+// Only the root sends data, so receiving gives it no credit: after consuming (and re-arming) step
+// s, each receiving wave stores s into its flag in the root's block (the bulk two-shot's flag
+// region, phase 0, indexed by the receiver), and the root's matching wave waits for every
+// receiver's flag to reach s - 2 before it writes buffer s & 1 again in step s. Flags only grow;
+// values left by earlier launches are below this launch's first step, so only steps from the
+// third of a launch on wait (the kernel boundary covers the earlier ones).
+template <int DT, int NMAX>
+__device__ bool step_broadcast(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
+                               rsrc_t out_r, int k, uint64_t& t0, uint64_t& t1) {
+  const int N = a.nranks, r = c.rank, R = a.root;
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t slot = a.p1.slot;
+  const uint32_t unit0 = static_cast<uint32_t>(k) * a.chunk_units;
+  const uint32_t CK = chunk_len(a, k, (a.nbytes + 15u) / 16u);
+  const rsrc_t own = region_rsrc(a, r, a.p1);
+  stamp_start(t0, k);
+  if (r == R) {
+    if (s >= a.e0 + 2 && !bulk_wait(a, c, 0, s - 2)) return false;
+    wait_all_mem();
+    const bool sends = r != a.withhold;
+    const uint32_t mine = (b * N + r) * slot;
+    for (uint32_t i0 = c.t0; i0 < CK; i0 += c.T) {
+      const uint32_t i = i0 + c.lane;
+      const bool act = i < CK;
+      uint32_t x[4];
+      load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
+      if (sends)
+        push_peers<NMAX>(a, r, a.p1, act ? mine + i * 16u : kDrop, u32x4{x[0], x[1], x[2], x[3]});
+      store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.out_nbytes, x);
+    }
+  } else {
+    const u32x4 sent = sentinel_unit<DT, 16>();
+    auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+    for (uint32_t i0 = c.t0; i0 < CK; i0 += c.T) {
+      const uint32_t i = i0 + c.lane;
+      const bool act = i < CK;
+      const uint32_t mask = act ? (1u << R) : 0u;
+      const uint32_t off0 = b * N * slot + i * 16u;
+      u32x4 v[NMAX] = {};
+      if (!poll_lines<NMAX>(a, own, off0, slot, mask, v, ready, r, s)) return false;
+      u32x4 got = v[0];
+#pragma unroll
+      for (int q = 1; q < NMAX; ++q) got = (q == R) ? v[q] : got;
+      const uint32_t o[4] = {got.x, got.y, got.z, got.w};
+      store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.out_nbytes, o);
+      rearm<NMAX>(own, off0, slot, mask, sent);
+    }
+    wait_all_mem();  // the re-arms have completed before the flag that hands the buffer back
+    if (c.lane == 0)
+      __hip_atomic_store(bulk_flag(a, R, 0, r, c), s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  wait_all_mem();
+  t1 = now_ticks();
+  return true;
+}
+
 // ------------------------------------------------------------------ persistent driver
 
 __device__ __forceinline__ void drift_sleep(const Args& a, int it, int r, int cta) {
@@ -1060,7 +1234,7 @@ __device__ __forceinline__ void ar_body(const Args& a) {
     }
     if (++set == a.nsets) set = 0;
     const rsrc_t in_r = in_rsrc(uniform_ptr(inp), a.nbytes);
-    const rsrc_t out_r = out_rsrc(const_cast<void*>(uniform_ptr(outp)), a.nbytes);
+    const rsrc_t out_r = out_rsrc(const_cast<void*>(uniform_ptr(outp)), a.out_nbytes);
     if (a.drift > 0) drift_sleep(a, it, c.rank, c.cta);
     if (table && it + 1 < a.iters) {
       next_in = a.in_tab[set * N + c.rank];
@@ -1094,6 +1268,12 @@ __device__ __forceinline__ void ar_body(const Args& a) {
         ok = step_ll128<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_BARRIER2) {
         ok = step_barrier2<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_REDUCESCATTER) {
+        ok = step_reducescatter<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_ALLGATHER) {
+        ok = step_allgather<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_BROADCAST) {
+        ok = step_broadcast<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else {
         stamp_start(t_start, k);
         ok = xrank_barrier(a, c, 2 * s, s);
@@ -1202,6 +1382,9 @@ ar_kernel_fn ar_select_kernel(int algo, int dt, int nmax) {
       return nullptr;
     case ar::ALGO_BARRIER2: return pick_dt<ar::ALGO_BARRIER2>(dt, nmax);
     case ar::ALGO_BARRIER_ONLY: return pick_n<ar::ALGO_BARRIER_ONLY, ar::DT_F32>(nmax);
+    case ar::ALGO_REDUCESCATTER: return pick_dt<ar::ALGO_REDUCESCATTER>(dt, nmax);
+    case ar::ALGO_ALLGATHER: return pick_dt<ar::ALGO_ALLGATHER>(dt, nmax);
+    case ar::ALGO_BROADCAST: return pick_dt<ar::ALGO_BROADCAST>(dt, nmax);
     default: return nullptr;
   }
 }

@@ -1,0 +1,270 @@
+"""GPU parity of the standalone reduce-scatter, all-gather and broadcast, through the C ABI,
+against the CPU oracle's plain definitions. Every comparison is bit-exact: the reduce-scatter
+folds in rank order like the AllReduce, and the other two move bytes."""
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import draw, elem_bytes, from_device, handle, to_device
+
+pytestmark = pytest.mark.gpu
+
+# partition sizes in elements: whole 16-byte units, one to several passes of a rank's lanes
+PART_COUNTS = {"f32": [4, 12, 64, 1028, 17500], "i32": [4, 12, 64, 1028, 17500],
+               "bf16": [8, 24, 1032, 17504, 35000]}
+BCAST_COUNTS = [1, 3, 33, 1000, 4099, 70001]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _np_dtype(x):
+    return x.dtype
+
+
+def _rows(x):
+    return [np.ascontiguousarray(x[r]) for r in range(x.shape[0])]
+
+
+def _same_bytes(got, want, what):
+    g, w = got.view(np.uint8), np.ascontiguousarray(want).view(np.uint8)
+    assert g.shape == w.shape, f"{what}: shape {g.shape} != {w.shape}"
+    bad = np.nonzero(g != w)[0]
+    assert bad.size == 0, f"{what}: {bad.size} bytes differ, first at byte {bad[:4]}"
+
+
+def run_rs(h, x, n, inplace=False):
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    rc = x.shape[1] // n
+    ins = to_device(x)
+    if inplace:
+        outs = [ins[r][r * rc:(r + 1) * rc] for r in range(n)]
+    else:
+        outs = [torch.full((rc,), 0x55, dtype=ins[0].dtype, device="cuda") for _ in range(n)]
+    A.ar_reducescatter(h, ins, outs, rc)
+    A.ar_check(h)
+    return [o.cpu().numpy().view(x.dtype) for o in outs]
+
+
+def run_ag(h, x, n, inplace=False):
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    sc = x.shape[1]
+    dev = to_device(x)
+    outs = [torch.full((n * sc,), 0x55, dtype=dev[0].dtype, device="cuda") for _ in range(n)]
+    if inplace:
+        for r in range(n):
+            outs[r][r * sc:(r + 1) * sc].copy_(dev[r])
+        ins = [outs[r][r * sc:(r + 1) * sc] for r in range(n)]
+    else:
+        ins = dev
+    A.ar_allgather(h, ins, outs, sc)
+    A.ar_check(h)
+    return [o.cpu().numpy().view(x.dtype) for o in outs]
+
+
+def run_bc(h, x, n, root, inplace=False):
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    dev = to_device(x[root:root + 1])[0]
+    outs = [torch.full_like(dev, 0x55) for _ in range(n)]
+    if inplace:
+        outs[root] = dev
+    A.ar_broadcast(h, dev, outs, x.shape[1], root)
+    A.ar_check(h)
+    return [o.cpu().numpy().view(x.dtype) for o in outs]
+
+
+def check_rs(got, x, n):
+    from oracle import oracle
+
+    want = oracle.reducescatter(_rows(x))
+    for r in range(n):
+        _same_bytes(got[r], want[r], f"reduce-scatter rank {r}")
+
+
+def check_ag(got, x, n):
+    from oracle import oracle
+
+    want = oracle.allgather(_rows(x))
+    for r in range(n):
+        _same_bytes(got[r], want[r], f"all-gather rank {r}")
+
+
+def check_bc(got, x, n, root):
+    from oracle import oracle
+
+    want = oracle.broadcast(np.ascontiguousarray(x[root]), n)
+    for r in range(n):
+        _same_bytes(got[r], want[r], f"broadcast rank {r}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
+def test_reducescatter_and_allgather(n, dtype):
+    counts = PART_COUNTS[dtype]
+    with handle(n, n * max(counts) * elem_bytes(dtype), dtype) as h:
+        for i, c in enumerate(counts):
+            _say(f"case reduce-scatter n={n} dtype={dtype} recvcount={c}")
+            x = draw(dtype, n, n * c, seed=3000 + 10 * n + i)
+            check_rs(run_rs(h, x, n), x, n)
+            _say(f"case all-gather n={n} dtype={dtype} sendcount={c}")
+            y = draw(dtype, n, c, seed=4000 + 10 * n + i)
+            check_ag(run_ag(h, y, n), y, n)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
+def test_broadcast_every_root_kind(n, dtype):
+    with handle(n, max(BCAST_COUNTS) * elem_bytes(dtype), dtype) as h:
+        for i, c in enumerate(BCAST_COUNTS):
+            for root in sorted({0, n // 2, n - 1}):
+                _say(f"case broadcast n={n} dtype={dtype} count={c} root={root}")
+                x = draw(dtype, n, c, seed=5000 + 10 * n + i)
+                check_bc(run_bc(h, x, n, root), x, n, root)
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_collectives_chunked_scratch(n):
+    """Scratch slots of 1 KiB: every call is several chunks (several steps of one launch), the
+    broadcast root waiting for its receivers' buffer flags from the third chunk on."""
+    env = {"AR_SCRATCH_ONESHOT": 2048 * n, "AR_SCRATCH_TWOSHOT": 2048 * n}
+    dtype = "f32"
+    with handle(n, max(n * 1028, 3001) * 4, dtype, env=env) as h:
+        for it in range(2):
+            _say(f"case chunked n={n} it={it}")
+            x = draw(dtype, n, n * 1028, seed=6000 + it)
+            check_rs(run_rs(h, x, n), x, n)
+            y = draw(dtype, n, 1028, seed=6100 + it)
+            check_ag(run_ag(h, y, n), y, n)
+            z = draw(dtype, n, 3001, seed=6200 + it)
+            check_bc(run_bc(h, z, n, n - 1), z, n, n - 1)
+
+
+@pytest.mark.parametrize("op", ["reducescatter", "allgather", "broadcast"])
+@pytest.mark.parametrize("drift", [0, 3])
+def test_collectives_persistent_loop(op, drift):
+    """ar_bench: 40 collectives in one launch over 8 input sets, with and without random rank
+    drift; afterwards every set's output is checked (each set's last run wrote it)."""
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    n, dtype, c, iters, nsets = 4, "f32", 1028, 40, 8
+    root = 2
+    in_c = n * c if op == "reducescatter" else c
+    out_c = n * c if op == "allgather" else c
+    with handle(n, n * c * 4, dtype, drift=drift, root=root) as h:
+        xs = [draw(dtype, n, in_c, seed=7000 + k) for k in range(nsets)]
+        ins, outs = [], []
+        for x in xs:
+            ins += to_device(x)
+            outs += [torch.full((out_c,), 0x55, dtype=torch.float32, device="cuda")
+                     for _ in range(n)]
+        _say(f"case persistent {op} drift={drift}")
+        ts, te, ms = A.ar_bench(h, ins, outs, nsets, c, A.ALGOS[op], iters)
+        assert ms > 0
+        for k, x in enumerate(xs):
+            got = [o.cpu().numpy() for o in outs[k * n:(k + 1) * n]]
+            if op == "reducescatter":
+                check_rs(got, x, n)
+            elif op == "allgather":
+                check_ag(got, x, n)
+            else:
+                check_bc(got, x, n, root)
+        assert np.all(te.reshape(iters, n) >= ts.reshape(iters, n))
+
+
+def test_collectives_in_place_and_rearmed():
+    """The usual in-place forms give the same bytes, and every sentinel slot is armed again
+    after the calls."""
+    from latency_collectives_amd import _ar as A
+
+    n, dtype, c = 4, "bf16", 1032
+    with handle(n, n * c * 2, dtype) as h:
+        for it in range(3):
+            x = draw(dtype, n, n * c, seed=8000 + it)
+            check_rs(run_rs(h, x, n, inplace=True), x, n)
+            y = draw(dtype, n, c, seed=8100 + it)
+            check_ag(run_ag(h, y, n, inplace=True), y, n)
+            z = draw(dtype, n, 777, seed=8200 + it)
+            check_bc(run_bc(h, z, n, 1, inplace=True), z, n, 1)
+        for r in range(n):
+            w = A.ar_read_region(h, r, A.REGION_P1).view(np.uint32)
+            assert np.all(w == 0xFFFFFFFF), f"rank {r} slots not re-armed"
+
+
+def test_collectives_argument_errors():
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    n = 2
+    with handle(n, 4096, "f32") as h:
+        a = [torch.zeros(2 * 6, device="cuda") for _ in range(n)]
+        o = [torch.zeros(6, device="cuda") for _ in range(n)]
+        with pytest.raises(A.ArError) as e:  # 6 fp32 = 24 bytes: not whole 16-byte units
+            A.ar_reducescatter(h, a, o, 6)
+        assert e.value.code == A.AR_EINVAL
+        with pytest.raises(A.ArError) as e:
+            A.ar_allgather(h, o, a, 6)
+        assert e.value.code == A.AR_EINVAL
+        big = [torch.zeros(4096, device="cuda") for _ in range(n)]
+        with pytest.raises(A.ArError) as e:  # input 2 * 2048 fp32 > 4096 bytes
+            A.ar_reducescatter(h, big, big, 1024)
+        assert e.value.code == A.AR_ETOOBIG
+        b = [torch.zeros(16, device="cuda") for _ in range(n)]
+        with pytest.raises(A.ArError) as e:
+            A.ar_broadcast(h, b[0], b, 16, 2)  # root out of range
+        assert e.value.code == A.AR_EINVAL
+        with pytest.raises(A.ArError) as e:
+            A.ar_broadcast(h, b[0], [b[1], b[1]], 16, 0)  # outputs overlap
+        assert e.value.code == A.AR_EINVAL
+        x = [torch.zeros(2 * 8, device="cuda") for _ in range(n)]
+        with pytest.raises(A.ArError) as e:  # output inside another rank's input
+            A.ar_reducescatter(h, x, [x[1][:8], x[0][8:]], 8)
+        assert e.value.code == A.AR_EINVAL
+        e0 = A.ar_epoch(h)
+        A.ar_reducescatter(h, x, o, 0)
+        assert A.ar_epoch(h) == e0 + 1
+        A.ar_check(h)
+
+
+@pytest.mark.parametrize("op", ["reducescatter", "allgather", "broadcast"])
+def test_collectives_withheld_rank_times_out(op):
+    """Rank 0 (the broadcast root) sends nothing: the others' bounded polls give up, ar_check
+    reports AR_ETIMEOUT and no wave is left running."""
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    n, c = 4, 1024
+    with handle(n, n * c * 4, "f32", timeout_us=20000, withhold_rank=0) as h:
+        x = draw("f32", n, n * c, seed=9)
+        ins = to_device(x)
+        if op == "reducescatter":
+            A.ar_reducescatter(h, ins, [torch.empty(c, device="cuda") for _ in range(n)], c)
+        elif op == "allgather":
+            A.ar_allgather(h, [t[:c] for t in ins], [torch.empty(n * c, device="cuda")
+                                                     for _ in range(n)], c)
+        else:
+            A.ar_broadcast(h, ins[0], [torch.empty(n * c, device="cuda") for _ in range(n)],
+                           n * c, 0)
+        with pytest.raises(A.ArError) as e:
+            A.ar_check(h)
+        assert e.value.code == A.AR_ETIMEOUT
+
+
+def test_full_size_tp_decode_shapes():
+    """8 ranks, bf16, the [tokens, 8192] decode activation at 64 tokens: reduce-scatter of the
+    whole activation (output 64 x 1024 per rank), all-gather of a 64 x 1024 shard and broadcast
+    of the whole activation, checked element by element."""
+    n, dtype, t = 8, "bf16", 64
+    with handle(n, t * 8192 * 2, dtype) as h:
+        x = draw(dtype, n, t * 8192, seed=10, dist="normal")
+        check_rs(run_rs(h, x, n), x, n)
+        y = draw(dtype, n, t * 1024, seed=11, dist="normal")
+        check_ag(run_ag(h, y, n), y, n)
+        check_bc(run_bc(h, x, n, 5), x, n, 5)
