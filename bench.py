@@ -54,12 +54,16 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
     n, dt = wl["nranks"], wl["dtype"]
     eb = I.ELEM_BYTES[dt]
     count = size // eb
-    nsets = max(1, min(iters, set_cap_bytes // (n * size)))
+    # the standalone collectives: `size` is the per-rank partition; inputs and outputs differ
+    in_count = n * count if algo == "reducescatter" else count
+    out_count = n * count if algo == "allgather" else count
+    io_bytes = max(in_count, out_count) * eb
+    nsets = max(1, min(iters, set_cap_bytes // (n * io_bytes)))
     host_sets = []
-    if n * size <= (8 << 20):
+    if n * io_bytes <= (8 << 20):
         xs = []
         for k in range(nsets):
-            x = I.rank_inputs(wl["dist"], dt, n, count, wid, size_idx, k, wl["sigma"])
+            x = I.rank_inputs(wl["dist"], dt, n, in_count, wid, size_idx, k, wl["sigma"])
             I.assert_finite(x, dt)
             xs.append(x)
         if check:
@@ -72,9 +76,9 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
         del xs
     else:
         big = [t.view(1, -1) for t in
-               I.device_draw(wl["dist"], dt, n, count, wid, size_idx, 0, wl["sigma"])]
+               I.device_draw(wl["dist"], dt, n, in_count, wid, size_idx, 0, wl["sigma"])]
         nsets = 1
-    outs_big = [torch.empty_like(b) for b in big]
+    outs_big = [torch.empty((nsets, out_count), dtype=b.dtype, device=b.device) for b in big]
     ins = [big[r][k] for k in range(nsets) for r in range(n)]
     outs = [outs_big[r][k] for k in range(nsets) for r in range(n)]
     torch.cuda.synchronize()
@@ -88,10 +92,21 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
     # launch-inclusive: host-issued ar_allreduce calls back to back, timed with events
     calls = 50
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    A.ar_allreduce(h, ins[:n], outs[:n], count, aid)
+
+    def one_call():
+        if algo == "reducescatter":
+            A.ar_reducescatter(h, ins[:n], outs[:n], count)
+        elif algo == "allgather":
+            A.ar_allgather(h, ins[:n], outs[:n], count)
+        elif algo == "broadcast":
+            A.ar_broadcast(h, ins[0], outs[:n], count, 0)
+        else:
+            A.ar_allreduce(h, ins[:n], outs[:n], count, aid)
+
+    one_call()
     ev0.record()
     for _ in range(calls):
-        A.ar_allreduce(h, ins[:n], outs[:n], count, aid)
+        one_call()
     ev1.record()
     torch.cuda.synchronize()
     launch_us = ev0.elapsed_time(ev1) * 1e3 / calls
@@ -120,7 +135,19 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
         from oracle import oracle
 
         k, x = host_sets[-1]
-        want = oracle.allreduce([np.ascontiguousarray(x[r]) for r in range(n)])[0]
+        rows = [np.ascontiguousarray(x[r]) for r in range(n)]
+        if algo in I.COLLECTIVES:
+            want_all = (oracle.reducescatter(rows) if algo == "reducescatter"
+                        else oracle.allgather(rows) if algo == "allgather"
+                        else oracle.broadcast(rows[0], n))
+            ok = all(np.array_equal(outs[k * n + r].cpu().numpy().view(np.uint8),
+                                    want_all[r].view(np.uint8)) for r in range(n))
+            res["spot_check"] = bool(ok)
+            if not ok:
+                raise AssertionError(f"spot check failed: {algo} n={n} size={size}")
+            del ins, outs, big, outs_big
+            return res
+        want = oracle.allreduce(rows)[0]
         got = outs[k * n].cpu().numpy().view(want.dtype)
         if algo == "ll128_atomic":
             ok = np.allclose(got.astype(np.float64), want.astype(np.float64), rtol=0,
@@ -223,7 +250,9 @@ def run_workload(A, I, wid: int, algo: str | None, iters: int | None, warmup: in
         wl["sizes"] = sizes
     algo = algo or wl["algo"]
     iters = iters or wl["iters"]
-    h = A.ar_create(wl["nranks"], max(wl["sizes"]), A.DTYPES[wl["dtype"]])
+    # reduce-scatter inputs and all-gather outputs are N partitions per rank
+    widen = wl["nranks"] if algo in ("reducescatter", "allgather") else 1
+    h = A.ar_create(wl["nranks"], max(wl["sizes"]) * widen, A.DTYPES[wl["dtype"]])
     try:
         A.ar_set_option(h, A.AR_OPT_PLACEMENT, placement)
         rows = []
@@ -241,7 +270,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed iterations per size")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=sorted([1, 2, 3, 4, 5]))
+    ap.add_argument("--workload", type=int, default=2, choices=sorted([1, 2, 3, 4, 5, 6, 7, 8]))
     ap.add_argument("--algo", default=None)
     ap.add_argument("--placement", type=int, default=0, help="0 XCD per rank, 1 same XCD")
     ap.add_argument("--all", action="store_true", help="also run every workload; see --report")
@@ -305,7 +334,7 @@ def main() -> int:
     p50s = [r["p50_us"] for r in rows]
     value = math.exp(sum(math.log(v) for v in p50s) / len(p50s))
     barrier = None
-    if algo != "barrier2" and not args.no_barrier_baseline:
+    if algo != "barrier2" and algo not in I.COLLECTIVES and not args.no_barrier_baseline:
         # the two-barrier baseline at the same sizes, same inputs, same run
         _, _, _, brows = run_workload(A, I, wid, "barrier2", args.steps, args.warmup, hz,
                                       args.placement, sizes)
@@ -384,7 +413,7 @@ def main() -> int:
     }
     if barrier is not None:
         line["barrier_baseline"] = barrier
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and algo not in I.COLLECTIVES:
         line["cpu_baseline"] = cpu_baseline(I, wid, wl)
     report = {"main": line, "sol": sol}
     if args.all:
@@ -429,6 +458,9 @@ def run_all(A, I, hz, warmup, placement):
         (3, ["twoshot", "oneshot_sentinel", "barrier2"]),
         (4, ["ll128_atomic", "oneshot_ll", "oneshot_sentinel", "twoshot", "barrier2"]),
         (5, ["twoshot"]),
+        (6, ["reducescatter"]),
+        (7, ["allgather"]),
+        (8, ["broadcast"]),
     ]
     for wid, algos in plan:
         for algo in algos:

@@ -113,7 +113,20 @@ WORKLOADS = {
             algo="ll128_atomic"),
     5: dict(name="twoshot_n8_bandwidth_16M-256M", nranks=8, dtype=I32, dist="int20", sigma=1.0,
             sizes=[1 << k for k in range(24, 29)], iters=20, algo="twoshot"),
+    # the standalone collectives on the same decode activation [tokens, 8192] bf16 at 8 ranks;
+    # sizes are the per-rank partition: the reduce-scatter output [t, 1024], the all-gather
+    # input [t, 1024], the whole broadcast activation [t, 8192]
+    6: dict(name="reducescatter_n8_bf16_tp_decode_8192", nranks=8, dtype=BF16, dist="normal",
+            sigma=0.5, sizes=[t * 1024 * 2 for t in (1, 2, 4, 8, 16, 32, 64)], iters=100,
+            algo="reducescatter"),
+    7: dict(name="allgather_n8_bf16_tp_decode_8192", nranks=8, dtype=BF16, dist="normal",
+            sigma=0.5, sizes=[t * 1024 * 2 for t in (1, 2, 4, 8, 16, 32, 64)], iters=100,
+            algo="allgather"),
+    8: dict(name="broadcast_n8_bf16_tp_decode_8192", nranks=8, dtype=BF16, dist="normal",
+            sigma=0.5, sizes=[t * 8192 * 2 for t in (1, 2, 4, 8, 16, 32, 64)], iters=100,
+            algo="broadcast"),
 }
+COLLECTIVES = ("reducescatter", "allgather", "broadcast")
 
 
 def device_draw(dist: str, dtype: str, nranks: int, count: int, workload: int, size_idx: int,
