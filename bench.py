@@ -126,6 +126,7 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
         "launch_inclusive_us": float(launch_us),
         "iters": iters,
         "alg_bytes_per_call": A.ar_alg_bytes(h, count, aid),
+        "launch": A.ar_plan_info(h, count, aid),
     }
     res["algbw_GBps"] = size / (res["p50_us"] * 1e-6) / 1e9
     res["busbw_like_GBps"] = res["alg_bytes_per_call"] * iters / (ms * 1e-3) / 1e9 if ms > 0 else 0

@@ -246,6 +246,26 @@ int64_t ar_region_bytes(ar_handle* h, int region);
  * Returns the count, or a negative error code (bad handle or algorithm, AR_ETOOBIG).
  */
 int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo);
+
+/*
+ * ar_plan_info: the launch that an ar_allreduce (or, for AR_REDUCESCATTER, AR_ALLGATHER and
+ * AR_BROADCAST, the standalone collective with `count` as its entry point takes it) of `count`
+ * elements with `algo` would make on handle h, written to *info. Host only: nothing is launched.
+ * Returns AR_OK, or AR_EINVAL / AR_ETOOBIG / AR_ENOTSUP / AR_ENORES as the call itself would.
+ */
+typedef struct {
+  int kernel;     /* kernel family: the public algorithm id, or 7..11 for the internal ones
+                     (7 bulk two-shot, 8 / 9 multi-pass LL / sentinel, 10 / 11 one-pass sentinel
+                     one-shot / two-shot with 8-byte units) */
+  int chunks;     /* steps per call (the message is cut into equal chunks at the scratch cap) */
+  int ctas;       /* workgroups per rank */
+  int threads;    /* threads per workgroup */
+  int grid;       /* workgroups launched; those beyond the ranks' (on XCDs no rank uses) exit at
+                     once */
+  int unit_bytes; /* payload bytes per lane and unit: 16, or 8 for LL and the 8-byte kernels */
+  int near;       /* 1 when the slots are in the near regions */
+} ar_plan;
+int ar_plan_info(ar_handle* h, size_t count, ar_algo algo, ar_plan* info);
 int ar_read_region(ar_handle* h, int rank, int region, void* host_dst, size_t bytes);
 
 /* Sequence number the next step will use. */

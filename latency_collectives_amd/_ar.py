@@ -44,7 +44,8 @@ DTYPES = {"f32": AR_FLOAT32, "bf16": AR_BFLOAT16, "i32": AR_INT32}
 # Every symbol include/ar.h declares.
 EXPORTS = (
     "ar_create", "ar_allreduce", "ar_reducescatter", "ar_allgather", "ar_broadcast", "ar_destroy", "ar_last_error", "ar_check", "ar_bench",
-    "ar_wallclock_hz", "ar_set_option", "ar_region_bytes", "ar_alg_bytes", "ar_read_region",
+    "ar_wallclock_hz", "ar_set_option", "ar_region_bytes", "ar_alg_bytes", "ar_plan_info",
+    "ar_read_region",
     "ar_epoch",
     "ar_sol", "ar_pingpong", "ar_torn_lines", "ar_stream_copy",
 )
@@ -54,6 +55,14 @@ class ArError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"[{code}] {msg}")
         self.code = code
+
+
+class ar_plan(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int) for f in
+                ("kernel", "chunks", "ctas", "threads", "grid", "unit_bytes", "near")]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 
 class ar_sol_result(ctypes.Structure):
@@ -109,6 +118,7 @@ def lib() -> ctypes.CDLL:
         "ar_set_option": ([vp, i32, i64], i32),
         "ar_region_bytes": ([vp, i32], i64),
         "ar_alg_bytes": ([vp, sz, i32], i64),
+        "ar_plan_info": ([vp, sz, i32, ctypes.POINTER(ar_plan)], i32),
         "ar_read_region": ([vp, i32, i32, vp, sz], i32),
         "ar_epoch": ([vp], u64),
         "ar_sol": ([i32, ctypes.POINTER(ar_sol_result)], i32),
@@ -224,6 +234,12 @@ def ar_alg_bytes(h: int, count: int, algo: int) -> int:
     if v < 0:
         raise ArError(v, ar_last_error())
     return v
+
+
+def ar_plan_info(h: int, count: int, algo: int) -> dict:
+    p = ar_plan()
+    _ok(lib().ar_plan_info(h, int(count), int(algo), ctypes.byref(p)))
+    return p.as_dict()
 
 
 def ar_region_bytes(h: int, region: int) -> int:

@@ -952,6 +952,32 @@ int ar_bench(ar_handle* h, const void* const* in_sets, void* const* out_sets, in
   return AR_OK;
 }
 
+int ar_plan_info(ar_handle* h, size_t count, ar_algo algo, ar_plan* info) {
+  if (h == nullptr || info == nullptr) return ar_fail(AR_EINVAL, "null argument");
+  if ((algo < AR_ALGO_AUTO || algo > AR_BARRIER2) && !is_collective(algo))
+    return ar_fail(AR_EINVAL, "algorithm %d is not valid", static_cast<int>(algo));
+  uint64_t in_b = 0, out_b = 0;
+  int rc = op_bytes(h, algo, count, in_b, out_b);
+  if (rc != AR_OK) return rc;
+  if (in_b == 0) return ar_fail(AR_EINVAL, "count 0 launches nothing");
+  const int alg = resolve_algo(h, algo, in_b);
+  Launch L;
+  rc = plan(h, alg, in_b, L);
+  if (rc != AR_OK) return rc;
+  info->kernel = L.kernel_algo;
+  info->chunks = L.chunks;
+  info->ctas = L.ctas;
+  info->threads = L.threads;
+  info->grid = static_cast<int>(L.grid);
+  info->unit_bytes = (L.kernel_algo == AR_ONESHOT_LL || L.kernel_algo == ar::ALGO_ONESHOT_LL_MULTI ||
+                      L.kernel_algo == ar::ALGO_ONESHOT_SENTINEL_NARROW ||
+                      L.kernel_algo == ar::ALGO_TWOSHOT_NARROW)
+                         ? 8
+                         : 16;
+  info->near = L.near ? 1 : 0;
+  return AR_OK;
+}
+
 int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
   if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
   if (is_collective(algo)) {

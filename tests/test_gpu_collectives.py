@@ -268,3 +268,30 @@ def test_full_size_tp_decode_shapes():
         y = draw(dtype, n, t * 1024, seed=11, dist="normal")
         check_ag(run_ag(h, y, n), y, n)
         check_bc(run_bc(h, x, n, 5), x, n, 5)
+
+
+def test_plan_info_reports_the_launch():
+    """ar_plan_info describes the launch the calls make: the bulk two-shot with whole multiples
+    of the rank's compute units as workgroups at 16 MiB, a near-region one-pass kernel for a
+    small message, and the collectives' own kernels."""
+    from latency_collectives_amd import _ar as A
+
+    n = 8
+    with handle(n, 16 << 20, "i32") as h:
+        big = A.ar_plan_info(h, (16 << 20) // 4, A.AR_TWOSHOT)
+        assert big["kernel"] == 7 and big["threads"] == 256 and big["chunks"] == 1
+        small = A.ar_plan_info(h, 256, A.AR_TWOSHOT)
+        assert small["kernel"] in (3, 11) and small["near"] == 1 and small["chunks"] == 1
+        rs = A.ar_plan_info(h, 1024, A.AR_REDUCESCATTER)
+        ag = A.ar_plan_info(h, 1024, A.AR_ALLGATHER)
+        bc = A.ar_plan_info(h, 1024, A.AR_BROADCAST)
+        assert (rs["kernel"], ag["kernel"], bc["kernel"]) == (12, 13, 14)
+        for p in (big, small, rs, ag, bc):
+            assert p["grid"] >= n * p["ctas"]
+        import torch
+
+        rank_cus = torch.cuda.get_device_properties(0).multi_processor_count // 8
+        assert big["ctas"] % rank_cus == 0, (big, rank_cus)
+        with pytest.raises(A.ArError) as e:
+            A.ar_plan_info(h, 6, A.AR_REDUCESCATTER)  # 24 bytes: not whole units
+        assert e.value.code == A.AR_EINVAL
