@@ -292,17 +292,21 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
         if (h->ctas == 0 && max_ctas >= rank_cus) {
           // Every lane of the rank makes the same number of passes, and every compute unit of
           // the rank holds the same number of workgroups: among whole multiples of the rank's
-          // compute units, the one with the least padded work (passes x lanes), the wider on a
-          // tie. A rank only moves on to its next AllReduce once its slowest wave is done, so a
-          // last pass that only some lanes take costs a whole pass (16 MiB per rank at N = 8:
-          // 6 % slower with 3 workgroups per compute unit and 5.3 passes than with 2 and 8).
+          // compute units, the one with the least padded work (passes x lanes). A rank only
+          // moves on to its next AllReduce once its slowest wave is done, so a last pass that
+          // only some lanes take costs a whole pass (16 MiB per rank at N = 8: 6 % slower with 3
+          // workgroups per compute unit and 5.3 passes than with 2 and 8). On a tie the narrower
+          // shape wins once it makes at least 8 passes (one workgroup per compute unit measured
+          // 0.5-2 % faster than two at 16-256 MiB); below that, the wider one (fewer passes).
           const uint64_t T = static_cast<uint64_t>(L.threads);
-          uint64_t best_work = ~0ull;
+          uint64_t best_work = ~0ull, best_passes = 0;
           for (int m = 1; m * rank_cus <= max_ctas; ++m) {
             const uint64_t w = static_cast<uint64_t>(m) * rank_cus;
-            const uint64_t work = ceil_div(C, w * T) * w;
-            if (work <= best_work) {
+            const uint64_t passes = ceil_div(C, w * T);
+            const uint64_t work = passes * w;
+            if (work < best_work || (work == best_work && best_passes < 8)) {
               best_work = work;
+              best_passes = passes;
               ctas = static_cast<int>(w);
             }
           }
@@ -579,8 +583,11 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
   sz[RG_CNT] = {0, 2ull * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 4};
   sz[RG_BAR] = {0, 1ull * ar::kMaxRanks * ar::kMaxCtasPerRank * 8};
   sz[RG_BDAT] = {slot_os, 1ull * N * slot_os};
-  sz[RG_PF1] = {slot_ts, 2ull * N * slot_ts};
-  sz[RG_PF2] = {slot_ts, 2ull * N * slot_ts};
+  // The bulk two-shot's slots are 4 KiB longer than their data: an owner reads all N sources'
+  // slots at one offset at once, and streams exactly a power of two apart measured ~5 % slower.
+  const uint64_t pitch_pf = slot_ts + 4096;
+  sz[RG_PF1] = {pitch_pf, 2ull * N * pitch_pf};
+  sz[RG_PF2] = {pitch_pf, 2ull * N * pitch_pf};
   sz[RG_FLG] = {0, 2ull * ar::kMaxRanks * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 8};
   // near area: the near ll, p1 and p2 regions, one 2 MiB page each (pitch set per launch)
   uint64_t off = 0;
