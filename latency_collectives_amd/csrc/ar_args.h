@@ -29,6 +29,12 @@ enum Algo : int {
   ALGO_REDUCESCATTER = 12,
   ALGO_ALLGATHER = 13,
   ALGO_BROADCAST = 14,
+  // internal: reduce-scatter / all-gather as one half of the one-pass two-shot, 16- or 8-byte
+  // units (12 and 13 are then their loop kernels for chunks wider than one pass)
+  ALGO_RS_ONEPASS = 15,
+  ALGO_AG_ONEPASS = 16,
+  ALGO_RS_NARROW = 17,
+  ALGO_AG_NARROW = 18,
 };
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).

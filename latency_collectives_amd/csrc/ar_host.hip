@@ -157,9 +157,14 @@ constexpr int kNoNarrow = 1;
 int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   const int N = h->nranks;
   const int nmax = N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16;
-  const int one_pass = ub == 8 ? (algo == AR_TWOSHOT ? ar::ALGO_TWOSHOT_NARROW
-                                                     : ar::ALGO_ONESHOT_SENTINEL_NARROW)
-                               : algo;
+  // the kernel for a chunk that fits one pass of the rank's lanes
+  const int one_pass = ub == 8 ? (algo == AR_TWOSHOT         ? ar::ALGO_TWOSHOT_NARROW
+                                  : algo == AR_REDUCESCATTER ? ar::ALGO_RS_NARROW
+                                  : algo == AR_ALLGATHER     ? ar::ALGO_AG_NARROW
+                                                             : ar::ALGO_ONESHOT_SENTINEL_NARROW)
+                               : (algo == AR_REDUCESCATTER ? ar::ALGO_RS_ONEPASS
+                                  : algo == AR_ALLGATHER   ? ar::ALGO_AG_ONEPASS
+                                                           : algo);
   L.fn = ar_select_kernel(one_pass, h->dtype, nmax);
   L.kernel_algo = one_pass;
   if (L.fn == nullptr)
@@ -181,10 +186,13 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
       cap_units = h->rg[RG_BDAT].slot / 16;
       break;
     case AR_REDUCESCATTER:  // nbytes is the whole input: N partitions of whole units
-      units = ceil_div(nbytes, 16ull * static_cast<uint64_t>(N));
-      cap_units = h->rg[RG_P1].slot / 16;
+      units = ceil_div(nbytes, line * static_cast<uint64_t>(N));
+      cap_units = h->rg[RG_P1].slot / line;
       break;
-    case AR_ALLGATHER:
+    case AR_ALLGATHER:  // one-pass on the all-gather slots, the loop kernel on p1 (larger)
+      units = ceil_div(nbytes, line);
+      cap_units = h->rg[RG_P2].slot / line;
+      break;
     case AR_BROADCAST:
       units = ceil_div(nbytes, 16);
       cap_units = h->rg[RG_P1].slot / 16;
@@ -209,7 +217,7 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   const uint64_t near_chunks = ceil_div(units * line, ar::kGranule);
   const bool near_fits = units > 0 && 2ull * N * near_chunks * 2 * ar::kGranule <= ar::kNearPage &&
                          (algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL ||
-                          algo == AR_TWOSHOT ||
+                          algo == AR_TWOSHOT || algo == AR_REDUCESCATTER || algo == AR_ALLGATHER ||
                           (algo == AR_LL128_ATOMIC && units <= h->rg[RG_ACC].slot / 16));
   const int cus_per_xcd = std::max(1, h->cu_count / kXcds);
   L.ranks_per_xcd = h->placement == AR_PLACE_XCD ? static_cast<int>(ceil_div(N, kXcds)) : 1;
@@ -282,6 +290,8 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
       const int multi = algo == AR_TWOSHOT             ? ar::ALGO_TWOSHOT_BULK
                         : algo == AR_ONESHOT_LL        ? ar::ALGO_ONESHOT_LL_MULTI
                         : algo == AR_ONESHOT_SENTINEL  ? ar::ALGO_ONESHOT_SENTINEL_MULTI
+                        : algo == AR_REDUCESCATTER     ? ar::ALGO_REDUCESCATTER
+                        : algo == AR_ALLGATHER         ? ar::ALGO_ALLGATHER
                                                        : 0;
       if (multi != 0) {
         L.kernel_algo = multi;
@@ -321,8 +331,12 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
     return AR_OK;
   };
   int rc = shape(near_fits);
-  // The bulk two-shot has slots of its own (no near copies): it takes the regular chunking.
-  if (rc == AR_OK && L.near && L.kernel_algo == ar::ALGO_TWOSHOT_BULK) rc = shape(false);
+  // The multi-pass two-shot kernels (the bulk AllReduce, the loop kernels of the standalone
+  // collectives) address regular slots only: they take the regular chunking.
+  if (rc == AR_OK && L.near &&
+      (L.kernel_algo == ar::ALGO_TWOSHOT_BULK || L.kernel_algo == ar::ALGO_REDUCESCATTER ||
+       L.kernel_algo == ar::ALGO_ALLGATHER))
+    rc = shape(false);
   if (rc != AR_OK) return rc;
   if (L.near) {
     // Each rank's slot data goes to the fastest calibrated position of each near region, for the
@@ -360,7 +374,9 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
 // sentinel kernels (one-shot and two-shot) move 8-byte units when the chunk still fits one pass
 // of co-resident lanes and the launch shape is not forced; 16-byte units otherwise.
 int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
-  if ((algo == AR_ONESHOT_SENTINEL || algo == AR_TWOSHOT) && h->narrow && h->ctas == 0 &&
+  if ((algo == AR_ONESHOT_SENTINEL || algo == AR_TWOSHOT || algo == AR_REDUCESCATTER ||
+       algo == AR_ALLGATHER) &&
+      h->narrow && h->ctas == 0 &&
       h->threads == 0 && nbytes > 0) {
     Launch narrow;
     const int rc = plan_units(h, algo, nbytes, 8, narrow);
@@ -475,12 +491,21 @@ int op_bytes(ar_handle* h, int algo, size_t count, uint64_t& in_b, uint64_t& out
   return AR_OK;
 }
 
-// Kernel arguments of a standalone collective that differ from AllReduce's.
-void collective_args(int algo, uint64_t in_b, uint64_t out_b, int N, int root, ar::Args& a) {
+bool narrow_kernel(int kernel_algo) {
+  return kernel_algo == ar::ALGO_ONESHOT_SENTINEL_NARROW ||
+         kernel_algo == ar::ALGO_TWOSHOT_NARROW || kernel_algo == ar::ALGO_RS_NARROW ||
+         kernel_algo == ar::ALGO_AG_NARROW;
+}
+
+// Kernel arguments of a standalone collective that differ from AllReduce's: the partitions are
+// exact (in the launched kernel's unit size), not padded to whole chunks.
+void collective_args(int algo, int kernel_algo, uint64_t in_b, uint64_t out_b, int N, int root,
+                     ar::Args& a) {
+  const uint64_t ub = narrow_kernel(kernel_algo) ? 8 : 16;
   a.nbytes = static_cast<uint32_t>(in_b);
   a.out_nbytes = static_cast<uint32_t>(out_b);
-  if (algo == AR_REDUCESCATTER) a.part_units = static_cast<uint32_t>(in_b / N / 16);
-  if (algo == AR_ALLGATHER) a.part_units = static_cast<uint32_t>(in_b / 16);
+  if (algo == AR_REDUCESCATTER) a.part_units = static_cast<uint32_t>(in_b / N / ub);
+  if (algo == AR_ALLGATHER) a.part_units = static_cast<uint32_t>(in_b / ub);
   a.root = root;
 }
 
@@ -795,7 +820,7 @@ int run_collective(ar_handle* h, int algo, const void* const in[], void* const o
   rc = plan(h, algo, in_b, L);
   if (rc != AR_OK) return rc;
   ar::Args a = base_args(h, algo, in_b, L);
-  collective_args(algo, in_b, out_b, N, root, a);
+  collective_args(algo, L.kernel_algo, in_b, out_b, N, root, a);
   for (int r = 0; r < N; ++r) {
     a.in[r] = (algo != AR_BROADCAST || r == root) ? in[r] : nullptr;
     a.out[r] = out[r];
@@ -870,7 +895,7 @@ int ar_bench(ar_handle* h, const void* const* in_sets, void* const* out_sets, in
   rc = plan(h, alg, nbytes, L);
   if (rc != AR_OK) return rc;
   ar::Args a = base_args(h, alg, nbytes, L);
-  if (is_collective(alg)) collective_args(alg, nbytes, out_bytes, N, h->root, a);
+  if (is_collective(alg)) collective_args(alg, L.kernel_algo, nbytes, out_bytes, N, h->root, a);
   a.iters = iters;
   a.drift = h->drift;
   a.nsets = nsets;
@@ -976,9 +1001,8 @@ int ar_plan_info(ar_handle* h, size_t count, ar_algo algo, ar_plan* info) {
   info->ctas = L.ctas;
   info->threads = L.threads;
   info->grid = static_cast<int>(L.grid);
-  info->unit_bytes = (L.kernel_algo == AR_ONESHOT_LL || L.kernel_algo == ar::ALGO_ONESHOT_LL_MULTI ||
-                      L.kernel_algo == ar::ALGO_ONESHOT_SENTINEL_NARROW ||
-                      L.kernel_algo == ar::ALGO_TWOSHOT_NARROW)
+  info->unit_bytes = (L.kernel_algo == AR_ONESHOT_LL ||
+                      L.kernel_algo == ar::ALGO_ONESHOT_LL_MULTI || narrow_kernel(L.kernel_algo))
                          ? 8
                          : 16;
   info->near = L.near ? 1 : 0;

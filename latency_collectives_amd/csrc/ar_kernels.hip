@@ -541,8 +541,8 @@ __device__ __forceinline__ void allgather_out(const Args& a, int r, rsrc_t out_r
     uint32_t o[UB / 4];
 #pragma unroll
     for (int e = 0; e < UB / 4; ++e) o[e] = v[p][e];
-    store_unit<DT, UB>(out_r, ((mask >> p) & 1u) ? (p * P + k * CU + i) * UB : kDrop, a.nbytes,
-                       o);
+    store_unit<DT, UB>(out_r, ((mask >> p) & 1u) ? (p * P + k * CU + i) * UB : kDrop,
+                       a.out_nbytes, o);
   }
   rearm<NMAX>(own2, off0, a.p2.slot, mask, sent);
 }
@@ -552,7 +552,11 @@ __device__ __forceinline__ void allgather_out(const Args& a, int r, rsrc_t out_r
 // Reduce-scatter: partition p's chunk goes to owner p's slot r. The owner folds its partition in
 // rank order, writes it to its own output and pushes the result to every peer's all-gather slot
 // r; every rank copies the other owners' results into its output (§III.A "Two-shot").
-template <int DT, int NMAX, int UB = 16>
+// MODE 0 is that AllReduce. The standalone collectives run one half of it on the same slots:
+// MODE 1 the reduce-scatter alone (the folded partition is the whole output), MODE 2 the
+// all-gather alone (the rank's input is the partition it owns). Their partitions are exact, so
+// the last chunk may be short; an AllReduce's partitions are padded to whole chunks.
+template <int DT, int NMAX, int UB = 16, int MODE = 0>
 __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r, rsrc_t out_r,
                              int k, uint64_t& t0,
                              uint64_t& t1) {
@@ -569,45 +573,56 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
   auto ready = [](V l) { return vec_clear<DT>(l); };
   const uint32_t mine1 = (b * N + r) * slot1, mine2 = (b * N + r) * slot2;
   // one pass: the plan gives this rank at least one lane per unit of the chunk (wider chunks
-  // run step_twoshot_bulk)
+  // run step_twoshot_bulk, or the loop kernels of the standalone collectives)
   {
     const uint32_t i = c.t0 + c.lane;
-    const bool act = i < CU;
+    const bool act = i < CU && k * CU + i < P;
     const uint32_t mask = act ? peers : 0u;
     uint32_t off1 = b * N * slot1 + slot_off<UB>(a.p1, i);
     const uint32_t off2 = b * N * slot2 + slot_off<UB>(a.p2, i);
     const uint32_t uoff = (r * P + k * CU + i) * UB;
     pin(off1);
     stamp_start(t0, k);
-    uint32_t w[NMAX][W];
-    load_partitions<DT, NMAX, kPlain, UB>(a, r, in_r, k, i, act, 0, w);  // w[0]: own partition
-    compiler_fence();
-    wait_vm<0>();
-    if (sends) {
-      const uint32_t off = act ? mine1 + slot_off<UB>(a.p1, i) : kDrop;
+    uint32_t o[W];
+    if constexpr (MODE == 2) {
+      load_unit<DT, UB>(in_r, act ? (k * CU + i) * UB : kDrop, a.nbytes, o);
+      compiler_fence();
+      wait_vm<0>();
+    } else {
+      uint32_t w[NMAX][W];
+      load_partitions<DT, NMAX, kPlain, UB>(a, r, in_r, k, i, act, 0, w);  // w[0]: own partition
+      compiler_fence();
+      wait_vm<0>();
+      if (sends) {
+        const uint32_t off = act ? mine1 + slot_off<UB>(a.p1, i) : kDrop;
 #pragma unroll
-      for (int j = 1; j < NMAX; ++j) {
+        for (int j = 1; j < NMAX; ++j) {
+          V line;
+#pragma unroll
+          for (int e = 0; e < W; ++e) line[e] = w[j][e];
+          st_vec<kCoh>(peer_rsrc(a, r, j, a.p1), off, line);
+        }
+      }
+      V v[NMAX];
+      if (!poll_all<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
+      fold_rank_order<DT, NMAX, W>(N, r, w[0], v, o);
+    }
+    if constexpr (MODE == 1) {
+      store_unit<DT, UB>(out_r, act ? (k * CU + i) * UB : kDrop, a.out_nbytes, o);
+      rearm<NMAX>(own1, off1, slot1, mask, sent);
+    } else {
+      if (sends) {
         V line;
 #pragma unroll
-        for (int e = 0; e < W; ++e) line[e] = w[j][e];
-        st_vec<kCoh>(peer_rsrc(a, r, j, a.p1), off, line);
+        for (int e = 0; e < W; ++e) line[e] = o[e];
+        push_peers<NMAX>(a, r, a.p2, act ? mine2 + slot_off<UB>(a.p2, i) : kDrop, line);
       }
+      store_unit<DT, UB>(out_r, act ? uoff : kDrop, a.out_nbytes, o);
+      if constexpr (MODE == 0) rearm<NMAX>(own1, off1, slot1, mask, sent);
+      V v2[NMAX];
+      if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
+      allgather_out<DT, NMAX, UB>(a, r, out_r, own2, off2, mask, k, i, v2, sent);
     }
-    V v[NMAX];
-    if (!poll_all<NMAX>(a, own1, off1, slot1, mask, v, ready, r, s)) return false;
-    uint32_t o[W];
-    fold_rank_order<DT, NMAX, W>(N, r, w[0], v, o);
-    if (sends) {
-      V line;
-#pragma unroll
-      for (int e = 0; e < W; ++e) line[e] = o[e];
-      push_peers<NMAX>(a, r, a.p2, act ? mine2 + slot_off<UB>(a.p2, i) : kDrop, line);
-    }
-    store_unit<DT, UB>(out_r, act ? uoff : kDrop, a.nbytes, o);
-    rearm<NMAX>(own1, off1, slot1, mask, sent);
-    V v2[NMAX];
-    if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
-    allgather_out<DT, NMAX, UB>(a, r, out_r, own2, off2, mask, k, i, v2, sent);
     compiler_fence();
     wait_vm<NMAX>();  // every output store has landed; the NMAX re-arm stores may be in flight
     t1 = now_ticks();
@@ -1314,6 +1329,14 @@ __device__ __forceinline__ void ar_body(const Args& a) {
         ok = step_ll128<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_BARRIER2) {
         ok = step_barrier2<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_RS_ONEPASS) {
+        ok = step_twoshot<DT, NMAX, 16, 1>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_RS_NARROW) {
+        ok = step_twoshot<DT, NMAX, 8, 1>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_AG_ONEPASS) {
+        ok = step_twoshot<DT, NMAX, 16, 2>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_AG_NARROW) {
+        ok = step_twoshot<DT, NMAX, 8, 2>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_REDUCESCATTER) {
         ok = step_reducescatter<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_ALLGATHER) {
@@ -1431,6 +1454,10 @@ ar_kernel_fn ar_select_kernel(int algo, int dt, int nmax) {
     case ar::ALGO_REDUCESCATTER: return pick_dt<ar::ALGO_REDUCESCATTER>(dt, nmax);
     case ar::ALGO_ALLGATHER: return pick_dt<ar::ALGO_ALLGATHER>(dt, nmax);
     case ar::ALGO_BROADCAST: return pick_dt<ar::ALGO_BROADCAST>(dt, nmax);
+    case ar::ALGO_RS_ONEPASS: return pick_dt<ar::ALGO_RS_ONEPASS>(dt, nmax);
+    case ar::ALGO_AG_ONEPASS: return pick_dt<ar::ALGO_AG_ONEPASS>(dt, nmax);
+    case ar::ALGO_RS_NARROW: return pick_dt<ar::ALGO_RS_NARROW>(dt, nmax);
+    case ar::ALGO_AG_NARROW: return pick_dt<ar::ALGO_AG_NARROW>(dt, nmax);
     default: return nullptr;
   }
 }

@@ -104,16 +104,23 @@ def check_bc(got, x, n, root):
         _same_bytes(got[r], want[r], f"broadcast rank {r}")
 
 
+# launch shapes: the planner's choice (one-pass halves of the two-shot kernel with 8- or 16-byte
+# units where a chunk fits one pass, the loop kernels beyond), 16-byte units only, and one
+# 64-thread workgroup per rank (every size but the smallest on the loop kernels)
+SHAPES = {"auto": {}, "wide_units": {"narrow": 0}, "loop": {"ctas": 1, "threads": 64}}
+
+
+@pytest.mark.parametrize("shape", sorted(SHAPES))
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
-def test_reducescatter_and_allgather(n, dtype):
+def test_reducescatter_and_allgather(n, dtype, shape):
     counts = PART_COUNTS[dtype]
-    with handle(n, n * max(counts) * elem_bytes(dtype), dtype) as h:
+    with handle(n, n * max(counts) * elem_bytes(dtype), dtype, **SHAPES[shape]) as h:
         for i, c in enumerate(counts):
-            _say(f"case reduce-scatter n={n} dtype={dtype} recvcount={c}")
+            _say(f"case reduce-scatter n={n} dtype={dtype} recvcount={c} shape={shape}")
             x = draw(dtype, n, n * c, seed=3000 + 10 * n + i)
             check_rs(run_rs(h, x, n), x, n)
-            _say(f"case all-gather n={n} dtype={dtype} sendcount={c}")
+            _say(f"case all-gather n={n} dtype={dtype} sendcount={c} shape={shape}")
             y = draw(dtype, n, c, seed=4000 + 10 * n + i)
             check_ag(run_ag(h, y, n), y, n)
 
@@ -146,9 +153,10 @@ def test_collectives_chunked_scratch(n):
             check_bc(run_bc(h, z, n, n - 1), z, n, n - 1)
 
 
+@pytest.mark.parametrize("shape", sorted(SHAPES))
 @pytest.mark.parametrize("op", ["reducescatter", "allgather", "broadcast"])
 @pytest.mark.parametrize("drift", [0, 3])
-def test_collectives_persistent_loop(op, drift):
+def test_collectives_persistent_loop(op, drift, shape):
     """ar_bench: 40 collectives in one launch over 8 input sets, with and without random rank
     drift; afterwards every set's output is checked (each set's last run wrote it)."""
     from latency_collectives_amd import _ar as A
@@ -158,14 +166,14 @@ def test_collectives_persistent_loop(op, drift):
     root = 2
     in_c = n * c if op == "reducescatter" else c
     out_c = n * c if op == "allgather" else c
-    with handle(n, n * c * 4, dtype, drift=drift, root=root) as h:
+    with handle(n, n * c * 4, dtype, drift=drift, root=root, **SHAPES[shape]) as h:
         xs = [draw(dtype, n, in_c, seed=7000 + k) for k in range(nsets)]
         ins, outs = [], []
         for x in xs:
             ins += to_device(x)
             outs += [torch.full((out_c,), 0x55, dtype=torch.float32, device="cuda")
                      for _ in range(n)]
-        _say(f"case persistent {op} drift={drift}")
+        _say(f"case persistent {op} drift={drift} shape={shape}")
         ts, te, ms = A.ar_bench(h, ins, outs, nsets, c, A.ALGOS[op], iters)
         assert ms > 0
         for k, x in enumerate(xs):
@@ -285,7 +293,9 @@ def test_plan_info_reports_the_launch():
         rs = A.ar_plan_info(h, 1024, A.AR_REDUCESCATTER)
         ag = A.ar_plan_info(h, 1024, A.AR_ALLGATHER)
         bc = A.ar_plan_info(h, 1024, A.AR_BROADCAST)
-        assert (rs["kernel"], ag["kernel"], bc["kernel"]) == (12, 13, 14)
+        # one-pass halves of the two-shot kernel (8-byte units here), the loop kernel for broadcast
+        assert (rs["kernel"], ag["kernel"], bc["kernel"]) == (17, 18, 14)
+        assert rs["near"] == 1 and ag["near"] == 1 and rs["unit_bytes"] == 8
         for p in (big, small, rs, ag, bc):
             assert p["grid"] >= n * p["ctas"]
         import torch
@@ -295,3 +305,8 @@ def test_plan_info_reports_the_launch():
         with pytest.raises(A.ArError) as e:
             A.ar_plan_info(h, 6, A.AR_REDUCESCATTER)  # 24 bytes: not whole units
         assert e.value.code == A.AR_EINVAL
+        # a partition wider than one pass of the rank's lanes runs the loop kernels on regular slots
+        wide_rs = A.ar_plan_info(h, (16 << 20) // 4 // n, A.AR_REDUCESCATTER)
+        wide_ag = A.ar_plan_info(h, (16 << 20) // 4 // n, A.AR_ALLGATHER)
+        assert (wide_rs["kernel"], wide_ag["kernel"]) == (12, 13)
+        assert wide_rs["near"] == 0 and wide_ag["near"] == 0
