@@ -35,6 +35,9 @@ enum Algo : int {
   ALGO_AG_ONEPASS = 16,
   ALGO_RS_NARROW = 17,
   ALGO_AG_NARROW = 18,
+  // internal: one-pass broadcast, 16- or 8-byte units (14 is then its loop kernel)
+  ALGO_BCAST_ONEPASS = 19,
+  ALGO_BCAST_NARROW = 20,
 };
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).

@@ -161,9 +161,11 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   const int one_pass = ub == 8 ? (algo == AR_TWOSHOT         ? ar::ALGO_TWOSHOT_NARROW
                                   : algo == AR_REDUCESCATTER ? ar::ALGO_RS_NARROW
                                   : algo == AR_ALLGATHER     ? ar::ALGO_AG_NARROW
+                                  : algo == AR_BROADCAST     ? ar::ALGO_BCAST_NARROW
                                                              : ar::ALGO_ONESHOT_SENTINEL_NARROW)
                                : (algo == AR_REDUCESCATTER ? ar::ALGO_RS_ONEPASS
                                   : algo == AR_ALLGATHER   ? ar::ALGO_AG_ONEPASS
+                                  : algo == AR_BROADCAST   ? ar::ALGO_BCAST_ONEPASS
                                                            : algo);
   L.fn = ar_select_kernel(one_pass, h->dtype, nmax);
   L.kernel_algo = one_pass;
@@ -194,8 +196,8 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
       cap_units = h->rg[RG_P2].slot / line;
       break;
     case AR_BROADCAST:
-      units = ceil_div(nbytes, 16);
-      cap_units = h->rg[RG_P1].slot / 16;
+      units = ceil_div(nbytes, line);
+      cap_units = h->rg[RG_P1].slot / line;
       break;
     case AR_TWOSHOT:
     case AR_LL128_ATOMIC:
@@ -218,6 +220,7 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   const bool near_fits = units > 0 && 2ull * N * near_chunks * 2 * ar::kGranule <= ar::kNearPage &&
                          (algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL ||
                           algo == AR_TWOSHOT || algo == AR_REDUCESCATTER || algo == AR_ALLGATHER ||
+                          algo == AR_BROADCAST ||
                           (algo == AR_LL128_ATOMIC && units <= h->rg[RG_ACC].slot / 16));
   const int cus_per_xcd = std::max(1, h->cu_count / kXcds);
   L.ranks_per_xcd = h->placement == AR_PLACE_XCD ? static_cast<int>(ceil_div(N, kXcds)) : 1;
@@ -278,13 +281,18 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
     };
     int max_ctas = co_resident(L.fn);
     int ctas = pick_ctas(max_ctas);
+    // All-gather and broadcast take their one-pass kernels only on the near slots: on the
+    // regular slots the loop kernels measured faster (8 ranks, bf16: all-gather of 128 KiB per
+    // rank 6.3 against 7.6 µs, broadcast of 256 KiB 3.0 against 7.9 µs).
+    const bool loop_only = !near && (algo == AR_ALLGATHER || algo == AR_BROADCAST);
     if (ub == 8) {
       // Narrow units only while the rank's workgroups still get a compute unit each: beyond
       // that the doubled lane count measured slower than 16-byte units (128 KiB and more per
       // rank at N = 4).
-      if (static_cast<uint64_t>(ctas) * L.threads < C || ctas > rank_cus) return kNoNarrow;
+      if (static_cast<uint64_t>(ctas) * L.threads < C || ctas > rank_cus || loop_only)
+        return kNoNarrow;
     }
-    if (static_cast<uint64_t>(ctas) * L.threads < C) {
+    if (static_cast<uint64_t>(ctas) * L.threads < C || loop_only) {
       // The chunk does not fit one pass of the rank's lanes: the kernels built for one pass (the
       // latency path) hand it to their multi-pass counterparts.
       const int multi = algo == AR_TWOSHOT             ? ar::ALGO_TWOSHOT_BULK
@@ -292,6 +300,7 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
                         : algo == AR_ONESHOT_SENTINEL  ? ar::ALGO_ONESHOT_SENTINEL_MULTI
                         : algo == AR_REDUCESCATTER     ? ar::ALGO_REDUCESCATTER
                         : algo == AR_ALLGATHER         ? ar::ALGO_ALLGATHER
+                        : algo == AR_BROADCAST         ? ar::ALGO_BROADCAST
                                                        : 0;
       if (multi != 0) {
         L.kernel_algo = multi;
@@ -307,14 +316,19 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
           // only some lanes take costs a whole pass (16 MiB per rank at N = 8: 6 % slower with 3
           // workgroups per compute unit and 5.3 passes than with 2 and 8). On a tie the narrower
           // shape wins once it makes at least 8 passes (one workgroup per compute unit measured
-          // 0.5-2 % faster than two at 16-256 MiB); below that, the wider one (fewer passes).
+          // 0.5-2 % faster than two at 16-256 MiB); below that, the wider one (fewer passes),
+          // except for the loop kernels of the standalone collectives, where the narrower one
+          // measured faster at every size (8 ranks, bf16 broadcast of 256 KiB: 3.0 against
+          // 5.0 µs with two workgroups per compute unit).
+          const bool narrow_ties = multi == ar::ALGO_REDUCESCATTER ||
+                                   multi == ar::ALGO_ALLGATHER || multi == ar::ALGO_BROADCAST;
           const uint64_t T = static_cast<uint64_t>(L.threads);
           uint64_t best_work = ~0ull, best_passes = 0;
           for (int m = 1; m * rank_cus <= max_ctas; ++m) {
             const uint64_t w = static_cast<uint64_t>(m) * rank_cus;
             const uint64_t passes = ceil_div(C, w * T);
             const uint64_t work = passes * w;
-            if (work < best_work || (work == best_work && best_passes < 8)) {
+            if (work < best_work || (work == best_work && !narrow_ties && best_passes < 8)) {
               best_work = work;
               best_passes = passes;
               ctas = static_cast<int>(w);
@@ -335,7 +349,7 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   // collectives) address regular slots only: they take the regular chunking.
   if (rc == AR_OK && L.near &&
       (L.kernel_algo == ar::ALGO_TWOSHOT_BULK || L.kernel_algo == ar::ALGO_REDUCESCATTER ||
-       L.kernel_algo == ar::ALGO_ALLGATHER))
+       L.kernel_algo == ar::ALGO_ALLGATHER || L.kernel_algo == ar::ALGO_BROADCAST))
     rc = shape(false);
   if (rc != AR_OK) return rc;
   if (L.near) {
@@ -375,7 +389,7 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
 // of co-resident lanes and the launch shape is not forced; 16-byte units otherwise.
 int plan(ar_handle* h, int algo, uint64_t nbytes, Launch& L) {
   if ((algo == AR_ONESHOT_SENTINEL || algo == AR_TWOSHOT || algo == AR_REDUCESCATTER ||
-       algo == AR_ALLGATHER) &&
+       algo == AR_ALLGATHER || algo == AR_BROADCAST) &&
       h->narrow && h->ctas == 0 &&
       h->threads == 0 && nbytes > 0) {
     Launch narrow;
@@ -494,7 +508,7 @@ int op_bytes(ar_handle* h, int algo, size_t count, uint64_t& in_b, uint64_t& out
 bool narrow_kernel(int kernel_algo) {
   return kernel_algo == ar::ALGO_ONESHOT_SENTINEL_NARROW ||
          kernel_algo == ar::ALGO_TWOSHOT_NARROW || kernel_algo == ar::ALGO_RS_NARROW ||
-         kernel_algo == ar::ALGO_AG_NARROW;
+         kernel_algo == ar::ALGO_AG_NARROW || kernel_algo == ar::ALGO_BCAST_NARROW;
 }
 
 // Kernel arguments of a standalone collective that differ from AllReduce's: the partitions are

@@ -1206,6 +1206,63 @@ __device__ bool step_broadcast(const Args& a, const Ctx& c, uint64_t s, rsrc_t i
   return true;
 }
 
+// One-pass broadcast (every unit of the chunk has its own lane), on the near slots when the
+// message fits them: the same protocol as step_broadcast, with 8- or 16-byte units and a single
+// round of polls per lane.
+template <int DT, int NMAX, int UB>
+__device__ bool step_broadcast_1p(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
+                                  rsrc_t out_r, int k, uint64_t& t0, uint64_t& t1) {
+  using V = unit_t<UB>;
+  constexpr int W = UB / 4;
+  const int N = a.nranks, r = c.rank, R = a.root;
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t slot = a.p1.slot, CU = a.chunk_units;
+  const uint32_t U = (a.nbytes + UB - 1) / UB;
+  const uint32_t i = c.t0 + c.lane;
+  const bool act = i < CU && k * CU + i < U;
+  const uint32_t uoff = (k * CU + i) * UB;
+  uint32_t off0 = b * N * slot + slot_off<UB>(a.p1, i);
+  pin(off0);
+  stamp_start(t0, k);
+  if (r == R) {
+    if (s >= a.e0 + 2 && !bulk_wait(a, c, 0, s - 2)) return false;
+    uint32_t x[W];
+    load_unit<DT, UB>(in_r, act ? uoff : kDrop, a.nbytes, x);
+    compiler_fence();
+    wait_vm<0>();
+    store_unit<DT, UB>(out_r, act ? uoff : kDrop, a.out_nbytes, x);
+    if (r != a.withhold) {
+      V line;
+#pragma unroll
+      for (int e = 0; e < W; ++e) line[e] = x[e];
+      push_peers<NMAX>(a, r, a.p1, act ? off0 + static_cast<uint32_t>(R) * slot : kDrop, line);
+    }
+    compiler_fence();
+    wait_vm<NMAX - 1>();  // the output store has landed; the pushes may be in flight
+  } else {
+    const V sent = sentinel_unit<DT, UB>();
+    auto ready = [](V l) { return vec_clear<DT>(l); };
+    const uint32_t mask = act ? (1u << R) : 0u;
+    V v[NMAX] = {};
+    if (!poll_all<NMAX>(a, region_rsrc(a, r, a.p1), off0, slot, mask, v, ready, r, s))
+      return false;
+    V got = v[0];
+#pragma unroll
+    for (int q = 1; q < NMAX; ++q) got = (q == R) ? v[q] : got;
+    uint32_t o[W];
+#pragma unroll
+    for (int e = 0; e < W; ++e) o[e] = got[e];
+    store_unit<DT, UB>(out_r, act ? uoff : kDrop, a.out_nbytes, o);
+    rearm<NMAX>(region_rsrc(a, r, a.p1), off0, slot, mask, sent);
+    compiler_fence();
+    wait_vm<0>();  // output and re-arm have completed before the flag that hands the buffer back
+    if (c.lane == 0)
+      __hip_atomic_store(bulk_flag(a, R, 0, r, c), s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  t1 = now_ticks();
+  return true;
+}
+
 // ------------------------------------------------------------------ persistent driver
 
 __device__ __forceinline__ void drift_sleep(const Args& a, int it, int r, int cta) {
@@ -1341,6 +1398,10 @@ __device__ __forceinline__ void ar_body(const Args& a) {
         ok = step_reducescatter<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_ALLGATHER) {
         ok = step_allgather<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_BCAST_ONEPASS) {
+        ok = step_broadcast_1p<DT, NMAX, 16>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_BCAST_NARROW) {
+        ok = step_broadcast_1p<DT, NMAX, 8>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_BROADCAST) {
         ok = step_broadcast<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else {
@@ -1458,6 +1519,8 @@ ar_kernel_fn ar_select_kernel(int algo, int dt, int nmax) {
     case ar::ALGO_AG_ONEPASS: return pick_dt<ar::ALGO_AG_ONEPASS>(dt, nmax);
     case ar::ALGO_RS_NARROW: return pick_dt<ar::ALGO_RS_NARROW>(dt, nmax);
     case ar::ALGO_AG_NARROW: return pick_dt<ar::ALGO_AG_NARROW>(dt, nmax);
+    case ar::ALGO_BCAST_ONEPASS: return pick_dt<ar::ALGO_BCAST_ONEPASS>(dt, nmax);
+    case ar::ALGO_BCAST_NARROW: return pick_dt<ar::ALGO_BCAST_NARROW>(dt, nmax);
     default: return nullptr;
   }
 }

@@ -125,26 +125,29 @@ def test_reducescatter_and_allgather(n, dtype, shape):
             check_ag(run_ag(h, y, n), y, n)
 
 
+@pytest.mark.parametrize("shape", sorted(SHAPES))
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
-def test_broadcast_every_root_kind(n, dtype):
-    with handle(n, max(BCAST_COUNTS) * elem_bytes(dtype), dtype) as h:
+def test_broadcast_every_root_kind(n, dtype, shape):
+    with handle(n, max(BCAST_COUNTS) * elem_bytes(dtype), dtype, **SHAPES[shape]) as h:
         for i, c in enumerate(BCAST_COUNTS):
             for root in sorted({0, n // 2, n - 1}):
-                _say(f"case broadcast n={n} dtype={dtype} count={c} root={root}")
+                _say(f"case broadcast n={n} dtype={dtype} count={c} root={root} shape={shape}")
                 x = draw(dtype, n, c, seed=5000 + 10 * n + i)
                 check_bc(run_bc(h, x, n, root), x, n, root)
 
 
+@pytest.mark.parametrize("shape", sorted(SHAPES))
 @pytest.mark.parametrize("n", [2, 4, 8])
-def test_collectives_chunked_scratch(n):
-    """Scratch slots of 1 KiB: every call is several chunks (several steps of one launch), the
-    broadcast root waiting for its receivers' buffer flags from the third chunk on."""
+def test_collectives_chunked_scratch(n, shape):
+    """Scratch slots of 1 KiB: every call that does not fit the near slots is several chunks
+    (several steps of one launch), the broadcast root waiting for its receivers' buffer flags
+    from the third chunk on."""
     env = {"AR_SCRATCH_ONESHOT": 2048 * n, "AR_SCRATCH_TWOSHOT": 2048 * n}
     dtype = "f32"
-    with handle(n, max(n * 1028, 3001) * 4, dtype, env=env) as h:
+    with handle(n, max(n * 1028, 3001) * 4, dtype, env=env, **SHAPES[shape]) as h:
         for it in range(2):
-            _say(f"case chunked n={n} it={it}")
+            _say(f"case chunked n={n} it={it} shape={shape}")
             x = draw(dtype, n, n * 1028, seed=6000 + it)
             check_rs(run_rs(h, x, n), x, n)
             y = draw(dtype, n, 1028, seed=6100 + it)
@@ -293,8 +296,9 @@ def test_plan_info_reports_the_launch():
         rs = A.ar_plan_info(h, 1024, A.AR_REDUCESCATTER)
         ag = A.ar_plan_info(h, 1024, A.AR_ALLGATHER)
         bc = A.ar_plan_info(h, 1024, A.AR_BROADCAST)
-        # one-pass halves of the two-shot kernel (8-byte units here), the loop kernel for broadcast
-        assert (rs["kernel"], ag["kernel"], bc["kernel"]) == (17, 18, 14)
+        # one-pass kernels with 8-byte units on the near slots
+        assert (rs["kernel"], ag["kernel"], bc["kernel"]) == (17, 18, 20)
+        assert bc["near"] == 1
         assert rs["near"] == 1 and ag["near"] == 1 and rs["unit_bytes"] == 8
         for p in (big, small, rs, ag, bc):
             assert p["grid"] >= n * p["ctas"]
@@ -308,5 +312,6 @@ def test_plan_info_reports_the_launch():
         # a partition wider than one pass of the rank's lanes runs the loop kernels on regular slots
         wide_rs = A.ar_plan_info(h, (16 << 20) // 4 // n, A.AR_REDUCESCATTER)
         wide_ag = A.ar_plan_info(h, (16 << 20) // 4 // n, A.AR_ALLGATHER)
-        assert (wide_rs["kernel"], wide_ag["kernel"]) == (12, 13)
+        wide_bc = A.ar_plan_info(h, (16 << 20) // 4, A.AR_BROADCAST)
+        assert (wide_rs["kernel"], wide_ag["kernel"], wide_bc["kernel"]) == (12, 13, 14)
         assert wide_rs["near"] == 0 and wide_ag["near"] == 0
