@@ -61,8 +61,9 @@ typedef enum {
   AR_LL128_ATOMIC = 4,
   AR_BARRIER2 = 5,
   AR_BARRIER_ONLY = 6,
-  /* values 7..11 are internal kernel families; the standalone collectives below are called
-     through their own entry points and named by these ids in ar_bench and ar_alg_bytes */
+  /* values 7..11 and 15..20 are internal kernel families (see ar_plan_info); the standalone
+     collectives below are called through their own entry points and named by these ids in
+     ar_bench, ar_alg_bytes and ar_plan_info */
   AR_REDUCESCATTER = 12,
   AR_ALLGATHER = 13,
   AR_BROADCAST = 14
@@ -254,9 +255,12 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo);
  * Returns AR_OK, or AR_EINVAL / AR_ETOOBIG / AR_ENOTSUP / AR_ENORES as the call itself would.
  */
 typedef struct {
-  int kernel;     /* kernel family: the public algorithm id, or 7..11 for the internal ones
-                     (7 bulk two-shot, 8 / 9 multi-pass LL / sentinel, 10 / 11 one-pass sentinel
-                     one-shot / two-shot with 8-byte units) */
+  int kernel;     /* kernel family: the public algorithm id, or an internal one: 7 bulk
+                     two-shot; 8 / 9 multi-pass LL / sentinel one-shot; 10 / 11 one-pass sentinel
+                     one-shot / two-shot with 8-byte units; 12 / 13 / 14 the reduce-scatter /
+                     all-gather / broadcast loop kernels; 15 / 16 reduce-scatter / all-gather as
+                     one half of the one-pass two-shot (17 / 18 with 8-byte units); 19 / 20
+                     one-pass broadcast with 16- / 8-byte units */
   int chunks;     /* steps per call (the message is cut into equal chunks at the scratch cap) */
   int ctas;       /* workgroups per rank */
   int threads;    /* threads per workgroup */

@@ -836,12 +836,10 @@ int run_collective(ar_handle* h, int algo, const void* const in[], void* const o
   ar::Args a = base_args(h, algo, in_b, L);
   collective_args(algo, L.kernel_algo, in_b, out_b, N, root, a);
   for (int r = 0; r < N; ++r) {
-    a.in[r] = (algo != AR_BROADCAST || r == root) ? in[r] : nullptr;
+    // broadcast: ranks other than the root never load their input; they get the root's pointer
+    // (a valid descriptor base) instead of one the caller may have left null
+    a.in[r] = algo == AR_BROADCAST ? in[root] : in[r];
     a.out[r] = out[r];
-  }
-  if (algo == AR_BROADCAST) {
-    // non-root ranks never load their input: give them the root's (a valid descriptor base)
-    for (int r = 0; r < N; ++r) a.in[r] = in[root];
   }
   rc = launch(L.fn, L.grid, L.threads, a, s);
   if (rc != AR_OK) return rc;
