@@ -244,6 +244,38 @@ def cpu_baseline(I, wid: int, wl: dict, budget_s: float = 12.0) -> dict:
     }
 
 
+def cpu_baseline_threads(I, wid: int, wl: dict, threads: int, budget_s: float = 6.0) -> dict:
+    """The same oracle run on `threads` host threads at once, each on an equal slice of the
+    element range of every rank (the C call releases the interpreter lock); the rank order per
+    element is unchanged, so the result is the same. Reported beside the single-threaded value."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import oracle
+
+    n, dt = wl["nranks"], wl["dtype"]
+    sizes = wl["sizes"]
+    per_budget = budget_s / len(sizes)
+    per_size = []
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        for si, size in enumerate(sizes):
+            count = size // I.ELEM_BYTES[dt]
+            x = I.rank_inputs(wl["dist"], dt, n, count, wid, si, 0, wl["sigma"])
+            rows = [np.ascontiguousarray(x[r]) for r in range(n)]
+            t = min(threads, count)
+            cuts = [count * j // t for j in range(t + 1)]
+            slices = [[row[cuts[j]:cuts[j + 1]] for row in rows] for j in range(t)]
+            t0 = time.perf_counter()
+            list(pool.map(lambda sl: oracle.time_allreduce(sl, 1), slices))
+            one = max(time.perf_counter() - t0, 1e-7)
+            reps = max(1, min(100000, int(per_budget / one)))
+            t0 = time.perf_counter()
+            list(pool.map(lambda sl: oracle.time_allreduce(sl, reps), slices))
+            per_size.append({"bytes": size, "reps": reps, "threads": t,
+                             "us_per_call": (time.perf_counter() - t0) / reps * 1e6})
+    gm = math.exp(sum(math.log(p["us_per_call"]) for p in per_size) / len(per_size))
+    return {"value": gm, "unit": "us", "cores": threads, "per_size": per_size}
+
+
 def run_workload(A, I, wid: int, algo: str | None, iters: int | None, warmup: int, hz: float,
                  placement: int, sizes=None):
     wl = dict(I.WORKLOADS[wid])
@@ -416,6 +448,9 @@ def main() -> int:
         line["barrier_baseline"] = barrier
     if not args.no_cpu_baseline and algo not in I.COLLECTIVES:
         line["cpu_baseline"] = cpu_baseline(I, wid, wl)
+        # the machine's CPU share is 16 cores whatever os.cpu_count() reports
+        line["cpu_baseline"]["multi_thread"] = cpu_baseline_threads(
+            I, wid, wl, max(1, min(16, os.cpu_count() or 1)))
     report = {"main": line, "sol": sol}
     if args.all:
         report["workloads"] = run_all(A, I, hz, args.warmup, args.placement)
