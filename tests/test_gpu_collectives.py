@@ -315,3 +315,30 @@ def test_plan_info_reports_the_launch():
         wide_bc = A.ar_plan_info(h, (16 << 20) // 4, A.AR_BROADCAST)
         assert (wide_rs["kernel"], wide_ag["kernel"], wide_bc["kernel"]) == (12, 13, 14)
         assert wide_rs["near"] == 0 and wide_ag["near"] == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_one_pass_collectives_several_chunks(dtype):
+    """8 ranks, 16 KiB slots: an 81 KiB partition misses the near slots but each 16 KiB chunk
+    fits one pass, so the one-pass reduce-scatter runs six chunks per call, the last one short;
+    all-gather and broadcast take their loop kernels on the regular slots, also in chunks."""
+    from latency_collectives_amd import _ar as A
+
+    n = 8
+    env = {"AR_SCRATCH_ONESHOT": 2 * n * 16384, "AR_SCRATCH_TWOSHOT": 2 * n * 16384}
+    part = 81 * 1024 // elem_bytes(dtype)
+    bcount = 100003
+    with handle(n, max(n * part * elem_bytes(dtype), bcount * elem_bytes(dtype)), dtype,
+                env=env) as h:
+        rs = A.ar_plan_info(h, part, A.AR_REDUCESCATTER)
+        ag = A.ar_plan_info(h, part, A.AR_ALLGATHER)
+        assert rs["kernel"] in (15, 17) and rs["chunks"] > 1 and rs["near"] == 0, rs
+        assert ag["kernel"] == 13 and ag["chunks"] > 1 and ag["near"] == 0, ag
+        for it in range(2):
+            _say(f"case several chunks dtype={dtype} it={it}")
+            x = draw(dtype, n, n * part, seed=9100 + it)
+            check_rs(run_rs(h, x, n), x, n)
+            y = draw(dtype, n, part, seed=9200 + it)
+            check_ag(run_ag(h, y, n), y, n)
+            z = draw(dtype, n, bcount, seed=9300 + it)
+            check_bc(run_bc(h, z, n, 3), z, n, 3)
