@@ -377,3 +377,22 @@ def test_broadcast_copies_root(oracle_mod, n):
     assert len(outs) == n
     for o in outs:
         assert np.array_equal(o, root)
+
+
+@pytest.mark.parametrize("n", [2, 3, 5, 8, 16])
+def test_int_rank_permutation_invariance(oracle_mod, n):
+    """Integer sums are exact, so permuting which rank holds which input must not change any
+    output bit (a dropped, doubled or mis-indexed rank would change the sum for some order)."""
+    g = np.random.default_rng(500 + n)
+    x = [g.integers(-(1 << 20), (1 << 20) + 1, size=333).astype(np.int32) for _ in range(n)]
+    want = oracle_mod.allreduce(x)[0]
+    for _ in range(5):
+        perm = g.permutation(n)
+        got = oracle_mod.allreduce([x[p] for p in perm])
+        for o in got:
+            assert np.array_equal(o, want)
+    rs_want = oracle_mod.reducescatter([np.tile(a, n) for a in x])
+    perm = g.permutation(n)
+    rs_got = oracle_mod.reducescatter([np.tile(x[p], n) for p in perm])
+    for a, b in zip(rs_got, rs_want):
+        assert np.array_equal(a, b)
