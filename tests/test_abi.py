@@ -60,6 +60,11 @@ def test_null_handle_calls_fail_cleanly(arlib):
     assert L.ar_bench(None, None, None, 1, 1, 1, 1, None, None, None, None) == arlib.AR_EINVAL
     assert L.ar_region_bytes(None, 0) == arlib.AR_EINVAL
     assert L.ar_epoch(None) == 0
+    assert L.ar_reducescatter(None, None, None, 4, None) == arlib.AR_EINVAL
+    assert L.ar_allgather(None, None, None, 4, None) == arlib.AR_EINVAL
+    assert L.ar_broadcast(None, None, None, 4, 0, None) == arlib.AR_EINVAL
+    assert L.ar_alg_bytes(None, 4, 1) == arlib.AR_EINVAL
+    assert L.ar_plan_info(None, 4, 1, None) == arlib.AR_EINVAL
     L.ar_destroy(None)  # must be a no-op
 
 
