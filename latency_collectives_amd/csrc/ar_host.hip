@@ -444,16 +444,17 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
 
 // Automatic choice by rank count and message size (the pages select by size and rank count,
 // Fig. 12): the fastest of one-shot LL (L), one-shot sentinel (S) and two-shot (T) measured on
-// MI355X (`python bench.py --auto-sweep`, fp32, p50 of 100 back-to-back calls) for
-// N in {2,3,4,8,16} and 128 B .. 2 MiB per rank. A call uses the row of the smallest measured N
+// MI355X (`python bench.py --auto-sweep`, fp32, p50 of 100 back-to-back calls; two sweeps, a
+// cell taking the later one's winner when it led by 3 % or more) for N in {2,3,4,8,16} and
+// 128 B .. 2 MiB per rank. A call uses the row of the smallest measured N
 // >= its N and the column of the smallest measured size >= its size; above 2 MiB, two-shot.
 constexpr int kAutoN[5] = {2, 3, 4, 8, 16};
 constexpr uint64_t kAutoBytes[8] = {128, 512, 2048, 8192, 32768, 131072, 524288, 2097152};
 constexpr char kAutoTable[5][9] = {
-    "SLSLSSSS",  // N = 2 (LL and sentinel within 10 % of each other up to 32 KiB)
-    "SSLLLSTL",  // N = 3
-    "SSLLSSTT",  // N = 4
-    "SSLLSTTT",  // N = 8
+    "SSSSLSSS",  // N = 2 (LL and sentinel within 10 % of each other up to 32 KiB)
+    "SSLLLSTS",  // N = 3
+    "SSSLSSTT",  // N = 4
+    "SSSSSTTT",  // N = 8
     "SSSSSTTT",  // N = 16
 };
 
