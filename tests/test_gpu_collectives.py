@@ -342,3 +342,66 @@ def test_one_pass_collectives_several_chunks(dtype):
             check_ag(run_ag(h, y, n), y, n)
             z = draw(dtype, n, bcount, seed=9300 + it)
             check_bc(run_bc(h, z, n, 3), z, n, 3)
+
+
+def test_every_algorithm_and_collective_interleaved_on_one_handle():
+    """A seeded random sequence of AllReduces (every algorithm, near, regular and bulk sizes)
+    and reduce-scatters, all-gathers and broadcasts on ONE handle, every result checked: the
+    protocols share scratch regions (sentinel slots, near pages, the monotonic flag region that
+    both the bulk two-shot and the broadcast credits use), so each call must leave them as the
+    next one expects; persistent broadcast loops run after bulk two-shots."""
+    from latency_collectives_amd import _ar as A
+    from tests.gpu_util import assert_matches, run_allreduce
+
+    n, dtype = 4, "f32"
+    algos = ["auto", "oneshot_ll", "oneshot_sentinel", "twoshot", "ll128_atomic", "barrier2"]
+    ar_counts = [5, 300, 4096, 70000, 600000]  # near, near, near, regular, bulk two-shot
+    part_counts = [4, 256, 4100, 65536]
+    g = np.random.default_rng(77)
+    with handle(n, 600000 * 4, dtype) as h:
+        for step in range(40):
+            kind = g.integers(0, 4)
+            seed = 12000 + step
+            if kind == 0:
+                algo = algos[g.integers(0, len(algos))]
+                count = int(ar_counts[g.integers(0, len(ar_counts))])
+                _say(f"case interleaved step={step} allreduce {algo} count={count}")
+                x = draw(dtype, n, count, seed=seed)
+                assert_matches(run_allreduce(h, x, algo), x, algo, dtype)
+            elif kind == 1:
+                c = int(part_counts[g.integers(0, len(part_counts))])
+                _say(f"case interleaved step={step} reduce-scatter {c}")
+                x = draw(dtype, n, n * c, seed=seed)
+                check_rs(run_rs(h, x, n), x, n)
+            elif kind == 2:
+                c = int(part_counts[g.integers(0, len(part_counts))])
+                _say(f"case interleaved step={step} all-gather {c}")
+                x = draw(dtype, n, c, seed=seed)
+                check_ag(run_ag(h, x, n), x, n)
+            else:
+                c = int(ar_counts[g.integers(0, len(ar_counts))])
+                root = int(g.integers(0, n))
+                _say(f"case interleaved step={step} broadcast {c} root={root}")
+                x = draw(dtype, n, c, seed=seed)
+                check_bc(run_bc(h, x, n, root), x, n, root)
+        # a bulk two-shot, then a persistent broadcast loop (credit flags over the same region)
+        x = draw(dtype, n, 600000, seed=13000)
+        assert_matches(run_allreduce(h, x, "twoshot"), x, "twoshot", dtype)
+        import torch
+
+        A.ar_set_option(h, A.AR_OPT_ROOT, 1)
+        for c in (300, 70000):
+            xs = [draw(dtype, n, c, seed=13100 + c + k) for k in range(4)]
+            ins, outs = [], []
+            for xk in xs:
+                ins += to_device(xk)
+                outs += [torch.full((c,), 0x55, dtype=torch.float32, device="cuda")
+                         for _ in range(n)]
+            _say(f"case interleaved persistent broadcast count={c}")
+            A.ar_bench(h, ins, outs, 4, c, A.AR_BROADCAST, 20, timestamps=False)
+            for k, xk in enumerate(xs):
+                check_bc([o.cpu().numpy() for o in outs[k * n:(k + 1) * n]], xk, n, 1)
+        for r in range(n):
+            for reg in (A.REGION_P1, A.REGION_P2, A.REGION_P1_NEAR, A.REGION_P2_NEAR):
+                w = A.ar_read_region(h, r, reg).view(np.uint32)
+                assert np.all(w == 0xFFFFFFFF), f"rank {r} region {reg} not re-armed"
