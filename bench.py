@@ -88,7 +88,7 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
     warm = max(warmup, nsets)
     if warm > 0:
         A.ar_bench(h, ins, outs, nsets, count, aid, warm, timestamps=False)
-    ts, te, ms = A.ar_bench(h, ins, outs, nsets, count, aid, iters)
+    ts, te, ms = A.ar_bench_ex(h, ins, outs, nsets, count, aid, iters)
     # launch-inclusive: host-issued ar_allreduce calls back to back, timed with events
     calls = 50
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -355,7 +355,7 @@ def main() -> int:
         rows = auto_sweep(A, I, hz, args.warmup, args.placement)
         print(json.dumps({"auto_sweep": rows}), flush=True)
         return 0
-    sol = A.ar_sol(args.placement)
+    sol = A.ar_sol_ex(args.placement)
     print(f"# sol {json.dumps(sol)}", file=sys.stderr, flush=True)
     peak = copy_peak(A)
     print(f"# streaming copy {peak['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
@@ -518,7 +518,7 @@ def run_all(A, I, hz, warmup, placement):
         try:
             A.ar_set_option(h, A.AR_OPT_PLACEMENT, placement)
             A.ar_bench(h, None, None, 1, 0, A.AR_BARRIER_ONLY, 50)
-            _, _, ms = A.ar_bench(h, None, None, 1, 0, A.AR_BARRIER_ONLY, 2000)
+            _, _, ms = A.ar_bench_ex(h, None, None, 1, 0, A.AR_BARRIER_ONLY, 2000)
             bar.append({"nranks": n, "us_per_barrier": ms * 1e3 / 2000})
         finally:
             A.ar_destroy(h)

@@ -38,10 +38,12 @@ typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_INT32 = 2 } ar_dtype;
  *   AR_ONESHOT_SENTINEL one-shot push into sentinel-filled scratch, polled until the sentinel is
  *                       gone, then re-armed (§IV "Sentinel").
  *   AR_TWOSHOT          reduce-scatter to partition owners + all-gather, sentinel synchronised
- *                       (§III.A "Two-shot AllReduce").
+ *                       (§III.A "Two-shot AllReduce"). For int32 the all-gather carries sums,
+ *                       any of which may equal the sentinel, so int32 always runs the
+ *                       bandwidth kernel, whose per-wave completion flags ignore the data.
  *   AR_LL128_ATOMIC     reduce-scatter by atomic adds into the owner's shared destination, then
- *                       the two-shot all-gather. fp32 and int32 only. The fp32 summation order
- *                       is not deterministic.
+ *                       the two-shot all-gather (for int32 with completion flags, as above).
+ *                       fp32 and int32 only. The fp32 summation order is not deterministic.
  *   AR_BARRIER2         one-shot push between two cross-rank flag barriers: the conventional
  *                       design whose barrier cost the pages measure (§III.B). A baseline.
  *   AR_BARRIER_ONLY     (ar_bench only) one cross-rank barrier per iteration, no data: the
@@ -92,12 +94,18 @@ typedef struct ar_handle ar_handle;
  * base + r * stride) and fills it: LL lines, atomic destinations, counters and barrier flags
  * with zeros, sentinel slots with the dtype's sentinel (fp32 0xFFFFFFFF, bf16 0xFFFF: negative
  * quiet NaNs, compared bitwise; int32 INT32_MIN). The sequence number starts at 1. Scratch
- * per rank per protocol is capped by the environment variables AR_SCRATCH_ONESHOT and
- * AR_SCRATCH_TWOSHOT (bytes, default 256 MiB each); larger messages are sent in equal chunks.
+ * per rank per protocol is capped by the environment variables AR_SCRATCH_ONESHOT (default
+ * 4 MiB) and AR_SCRATCH_TWOSHOT (default 64 MiB; also the LL128 cap), the sizes the Pith
+ * review of the paper lists as the outcome of its scratch-size sweep ("Assumptions & free
+ * parameters"; Fig. 12); larger messages are sent in equal chunks.
  * AR_POLL_TIMEOUT_US sets the initial poll timeout (default 2000000).
  * Synchronous on the current device. Returns NULL on error (see ar_last_error()).
  *
- * Caller obligation (§IV "Sentinel"): input values must never equal the sentinel bit pattern.
+ * Caller obligation (§IV "Sentinel"): input values must never equal the sentinel bit pattern
+ * (AR_OPT_CHECK_INPUTS checks it). Only inputs travel through sentinel slots as they are; the
+ * sums that the two-shot all-gather sends are fp32 / bf16 values that a fold of such inputs
+ * can produce (a fold of finite values never yields a NaN; a NaN input may propagate, so
+ * callers keep NaNs out of float inputs) or int32 sums, which use completion flags instead.
  */
 ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype);
 
@@ -167,12 +175,17 @@ const char* ar_last_error(void);
  * ar_check: wait for the work of the handle's last stream and report a device-side poll
  * timeout. Returns AR_OK, AR_ETIMEOUT (the message names rank, peer, step and algorithm; the
  * handle stays poisoned and every later call returns AR_ETIMEOUT) or AR_EHIP.
+ * A timed-out launch raises a device abort word: every launch on the handle enqueued after it
+ * (before ar_check has seen the timeout) exits at entry without reading or writing anything,
+ * so its outputs keep whatever they held before the call.
  */
 int ar_check(ar_handle* h);
 
 /*
  * ar_bench: run `iters` AllReduces back to back inside ONE persistent launch, with no host
- * involvement between iterations. Iteration k uses input/output set k % nsets:
+ * involvement between iterations (a persistent loop measures µs-scale latency without the
+ * launch overhead; the pages' latency is that of back-to-back collectives). Iteration k uses
+ * input/output set k % nsets:
  *   in_sets, out_sets : host arrays of nsets * N device pointers, set-major (set j, rank r at
  *                       index j * N + r); nsets in [1, 65536].
  *   t_start, t_end    : host arrays of iters * N entries (iteration-major) receiving, per
@@ -180,7 +193,6 @@ int ar_check(ar_handle* h);
  *                       first wave entered the iteration (before its first input load) and the
  *                       tick at which its last wave had completed its last output store.
  *                       Either may be NULL to skip timestamps.
- *   elapsed_ms        : if not NULL, the launch's duration from HIP events on `stream`.
  * Synchronous. Ticks convert to seconds with ar_wallclock_hz(). AR_BARRIER_ONLY measures one
  * cross-rank barrier per iteration and ignores the data arguments (they may be NULL).
  * AR_REDUCESCATTER, AR_ALLGATHER and AR_BROADCAST run the standalone collectives instead, with
@@ -189,7 +201,13 @@ int ar_check(ar_handle* h);
  */
 int ar_bench(ar_handle* h, const void* const* in_sets, void* const* out_sets, int nsets,
              size_t count, ar_algo algo, int iters, uint64_t* t_start, uint64_t* t_end,
-             double* elapsed_ms, void* stream);
+             void* stream);
+
+/* ar_bench_ex: ar_bench that also returns the launch's duration from HIP events recorded on
+ * `stream` around it (*elapsed_ms, if not NULL). */
+int ar_bench_ex(ar_handle* h, const void* const* in_sets, void* const* out_sets, int nsets,
+                size_t count, ar_algo algo, int iters, uint64_t* t_start, uint64_t* t_end,
+                double* elapsed_ms, void* stream);
 
 /* Rate of the device wall clock used by ar_bench and ar_sol, in Hz (0 on error). */
 double ar_wallclock_hz(void);
@@ -209,6 +227,14 @@ double ar_wallclock_hz(void);
  *                        8-byte units if the message still fits one pass of co-resident lanes
  *                        (twice the lanes, half the fold per lane); 0: always 16-byte units [1]
  *   AR_OPT_ROOT          ar_bench of AR_BROADCAST only: the root rank [0]
+ *   AR_OPT_CHECK_INPUTS  1: every ar_allreduce / ar_reducescatter / ar_allgather / ar_broadcast
+ *                        first scans the inputs for the sentinel bit pattern on `stream`, waits
+ *                        for the scan, and returns AR_EINVAL (naming the first rank and element)
+ *                        instead of launching when one is found. A debugging aid: it makes
+ *                        every call synchronous [0]
+ *   AR_OPT_RECORD_LAUNCH 1: every launch writes, per workgroup, its XCC id and the rank and
+ *                        workgroup index it decoded into region 13 of rank 0 (ar_read_region)
+ *                        [0]
  */
 typedef enum {
   AR_OPT_TIMEOUT_US = 0,
@@ -218,7 +244,9 @@ typedef enum {
   AR_OPT_PLACEMENT = 4,
   AR_OPT_DRIFT = 5,
   AR_OPT_NARROW = 6,
-  AR_OPT_ROOT = 7
+  AR_OPT_ROOT = 7,
+  AR_OPT_CHECK_INPUTS = 8,
+  AR_OPT_RECORD_LAUNCH = 9
 } ar_option;
 int ar_set_option(ar_handle* h, ar_option opt, int64_t value);
 
@@ -232,6 +260,9 @@ int ar_set_option(ar_handle* h, ar_option opt, int64_t value);
  *   7, 8, 9 = the near LL, one-shot / reduce-scatter and all-gather regions that small messages
  *   use (slot data in 8 KiB chunks, each in the granule homed near its rank)
  *   10, 11 = bulk two-shot reduce-scatter and all-gather data slots  12 = their completion flags
+ *   13 = launch record (rank 0 only): one uint32 per workgroup of the last launch made with
+ *        AR_OPT_RECORD_LAUNCH, XCC id in bits 7:0, rank + 1 in bits 15:8 (0: the workgroup maps
+ *        to no rank and exits), workgroup index within the rank in bits 31:16
  */
 int64_t ar_region_bytes(ar_handle* h, int region);
 
@@ -279,8 +310,14 @@ uint64_t ar_epoch(ar_handle* h);
  * ar_sol: speed-of-light microbenchmarks on the current device (the pages' bound
  * L_SoL = 2 * L_L2 + L_remote_store; Every µs Matters §VI as summarised in the Pith review).
  * `placement` is AR_PLACE_XCD (the two workgroups of the ping-pong on different XCDs) or
- * AR_PLACE_SAME (same XCD). Fills `res` (all latencies in nanoseconds). Synchronous.
+ * AR_PLACE_SAME (same XCD). Writes out_ns[0] = L_fence (store + agent-scope release fence),
+ * out_ns[1] = L_L2 (dependent-load L2 latency), out_ns[2] = L_store (store -> poll half round
+ * trip on the nearest memory position), all in nanoseconds; the floor is
+ * 2 * out_ns[1] + out_ns[2]. Synchronous. ar_sol_ex returns every probe.
  */
+int ar_sol(int placement, double* out_ns);
+
+/* ar_sol_ex: the same probes with all their results in `res`. */
 typedef struct {
   double fence_ns;         /* plain store + agent-scope release fence, per iteration        */
   double l2_load_ns;       /* dependent load, 1 MiB footprint (L2 hit, per-CU cache miss)    */
@@ -294,7 +331,25 @@ typedef struct {
   double floor_fence_ns;   /* the pages' form: 2 * fence_ns + store_half_rtt_ns              */
   int xcc_a, xcc_b;        /* XCC ids the two ping-pong workgroups ran on                     */
 } ar_sol_result;
-int ar_sol(int placement, ar_sol_result* res);
+int ar_sol_ex(int placement, ar_sol_result* res);
+
+/*
+ * ar_sol_ranks: the store term of the floor for the XCD pairs an N-rank placement uses. The
+ * latency of one AllReduce is a maximum over ranks (the last rank's data decides), so the
+ * floor of an N-rank configuration takes the slowest sender -> receiver pair among the ranks'
+ * XCDs (the Pith review's referee comment on §VII.C: the bound grows with the rank count). For
+ * every ordered pair of XCDs holding ranks (the same XCD twice when two ranks share one), a
+ * store -> poll ping-pong on a fresh 2 MiB page at the position the planner would pick for the
+ * receiving XCD (the fastest for its partner XCD x ^ 1). nranks 2..16, placement AR_PLACE_XCD
+ * or AR_PLACE_SAME. Synchronous.
+ */
+typedef struct {
+  double store_half_rtt_worst_ns; /* slowest pair: the store term of the N-rank floor           */
+  double store_half_rtt_best_ns;  /* fastest pair                                               */
+  int worst_sender_xcc, worst_receiver_xcc;
+  int pairs;                      /* distinct (sender XCD, receiver XCD) pairs measured         */
+} ar_sol_ranks_result;
+int ar_sol_ranks(int nranks, int placement, ar_sol_ranks_result* res);
 
 /*
  * ar_pingpong: the store -> poll ping-pong alone with explicit cache policies, for studying

@@ -23,9 +23,10 @@ AR_REDUCESCATTER, AR_ALLGATHER, AR_BROADCAST = 12, 13, 14
 AR_OK, AR_EINVAL, AR_ETOOBIG, AR_ENOTSUP, AR_EHIP, AR_ETIMEOUT, AR_ENORES = 0, -1, -2, -3, -4, -5, -6
 AR_PLACE_XCD, AR_PLACE_SAME, AR_PLACE_LINEAR = 0, 1, 2
 (AR_OPT_TIMEOUT_US, AR_OPT_WITHHOLD_RANK, AR_OPT_CTAS, AR_OPT_THREADS, AR_OPT_PLACEMENT,
- AR_OPT_DRIFT, AR_OPT_NARROW, AR_OPT_ROOT) = range(8)
+ AR_OPT_DRIFT, AR_OPT_NARROW, AR_OPT_ROOT, AR_OPT_CHECK_INPUTS, AR_OPT_RECORD_LAUNCH) = range(10)
 (REGION_P1, REGION_P2, REGION_LL, REGION_ACC, REGION_CNT, REGION_BAR, REGION_BDAT,
- REGION_LL_NEAR, REGION_P1_NEAR, REGION_P2_NEAR, REGION_PF1, REGION_PF2, REGION_FLG) = range(13)
+ REGION_LL_NEAR, REGION_P1_NEAR, REGION_P2_NEAR, REGION_PF1, REGION_PF2, REGION_FLG,
+ REGION_LAUNCH_RECORD) = range(14)
 
 ALGOS = {
     "auto": AR_ALGO_AUTO,
@@ -43,11 +44,12 @@ DTYPES = {"f32": AR_FLOAT32, "bf16": AR_BFLOAT16, "i32": AR_INT32}
 
 # Every symbol include/ar.h declares.
 EXPORTS = (
-    "ar_create", "ar_allreduce", "ar_reducescatter", "ar_allgather", "ar_broadcast", "ar_destroy", "ar_last_error", "ar_check", "ar_bench",
+    "ar_create", "ar_allreduce", "ar_reducescatter", "ar_allgather", "ar_broadcast",
+    "ar_destroy", "ar_last_error", "ar_check", "ar_bench", "ar_bench_ex",
     "ar_wallclock_hz", "ar_set_option", "ar_region_bytes", "ar_alg_bytes", "ar_plan_info",
     "ar_read_region",
     "ar_epoch",
-    "ar_sol", "ar_pingpong", "ar_torn_lines", "ar_stream_copy",
+    "ar_sol", "ar_sol_ex", "ar_sol_ranks", "ar_pingpong", "ar_torn_lines", "ar_stream_copy",
 )
 
 
@@ -84,6 +86,19 @@ class ar_sol_result(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class ar_sol_ranks_result(ctypes.Structure):
+    _fields_ = [
+        ("store_half_rtt_worst_ns", ctypes.c_double),
+        ("store_half_rtt_best_ns", ctypes.c_double),
+        ("worst_sender_xcc", ctypes.c_int),
+        ("worst_receiver_xcc", ctypes.c_int),
+        ("pairs", ctypes.c_int),
+    ]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
 _lib = None
 
 
@@ -113,7 +128,8 @@ def lib() -> ctypes.CDLL:
         "ar_destroy": ([vp], None),
         "ar_last_error": ([], ctypes.c_char_p),
         "ar_check": ([vp], i32),
-        "ar_bench": ([vp, pp, pp, i32, sz, i32, i32, pu64, pu64, pdbl, vp], i32),
+        "ar_bench": ([vp, pp, pp, i32, sz, i32, i32, pu64, pu64, vp], i32),
+        "ar_bench_ex": ([vp, pp, pp, i32, sz, i32, i32, pu64, pu64, pdbl, vp], i32),
         "ar_wallclock_hz": ([], ctypes.c_double),
         "ar_set_option": ([vp, i32, i64], i32),
         "ar_region_bytes": ([vp, i32], i64),
@@ -121,7 +137,9 @@ def lib() -> ctypes.CDLL:
         "ar_plan_info": ([vp, sz, i32, ctypes.POINTER(ar_plan)], i32),
         "ar_read_region": ([vp, i32, i32, vp, sz], i32),
         "ar_epoch": ([vp], u64),
-        "ar_sol": ([i32, ctypes.POINTER(ar_sol_result)], i32),
+        "ar_sol": ([i32, pdbl], i32),
+        "ar_sol_ex": ([i32, ctypes.POINTER(ar_sol_result)], i32),
+        "ar_sol_ranks": ([i32, i32, ctypes.POINTER(ar_sol_ranks_result)], i32),
         "ar_pingpong": ([i32, i32, i32, i32, pdbl, ctypes.POINTER(ctypes.c_int)], i32),
         "ar_torn_lines": ([i32, i32, i32, pu64, pu64], i32),
         "ar_stream_copy": ([vp, vp, sz, vp], i32),
@@ -200,9 +218,7 @@ def ar_check(h: int) -> None:
     _ok(lib().ar_check(h))
 
 
-def ar_bench(h: int, in_sets, out_sets, nsets: int, count: int, algo: int, iters: int,
-             timestamps: bool = True, stream=None):
-    """Returns (t_start, t_end, elapsed_ms); t_* are lists of iters * N ticks or None."""
+def _bench_args(in_sets, out_sets, nsets: int, iters: int, timestamps: bool):
     import numpy as np
 
     n = len(in_sets) // max(nsets, 1) if in_sets else 0
@@ -213,11 +229,27 @@ def ar_bench(h: int, in_sets, out_sets, nsets: int, count: int, algo: int, iters
         te = np.zeros(iters * n, dtype=np.uint64)
         p_ts = ts.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
         p_te = te.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
-    ms = ctypes.c_double(0.0)
     tin = _table(in_sets) if in_sets else None
     tout = _table(out_sets) if out_sets else None
+    return ts, te, p_ts, p_te, tin, tout
+
+
+def ar_bench(h: int, in_sets, out_sets, nsets: int, count: int, algo: int, iters: int,
+             timestamps: bool = True, stream=None):
+    """Returns (t_start, t_end): arrays of iters * N ticks, or None without timestamps."""
+    ts, te, p_ts, p_te, tin, tout = _bench_args(in_sets, out_sets, nsets, iters, timestamps)
     _ok(lib().ar_bench(h, tin, tout, int(nsets), int(count), int(algo), int(iters), p_ts, p_te,
-                       ctypes.byref(ms), _stream(stream)))
+                       _stream(stream)))
+    return ts, te
+
+
+def ar_bench_ex(h: int, in_sets, out_sets, nsets: int, count: int, algo: int, iters: int,
+                timestamps: bool = True, stream=None):
+    """Returns (t_start, t_end, elapsed_ms)."""
+    ts, te, p_ts, p_te, tin, tout = _bench_args(in_sets, out_sets, nsets, iters, timestamps)
+    ms = ctypes.c_double(0.0)
+    _ok(lib().ar_bench_ex(h, tin, tout, int(nsets), int(count), int(algo), int(iters), p_ts,
+                          p_te, ctypes.byref(ms), _stream(stream)))
     return ts, te, ms.value
 
 
@@ -264,8 +296,21 @@ def ar_epoch(h: int) -> int:
 
 
 def ar_sol(placement: int = AR_PLACE_XCD) -> dict:
+    """{fence_ns, l2_load_ns, store_half_rtt_ns} (the three terms of the pages' bound)."""
+    out = (ctypes.c_double * 3)()
+    _ok(lib().ar_sol(int(placement), out))
+    return {"fence_ns": out[0], "l2_load_ns": out[1], "store_half_rtt_ns": out[2]}
+
+
+def ar_sol_ex(placement: int = AR_PLACE_XCD) -> dict:
     res = ar_sol_result()
-    _ok(lib().ar_sol(int(placement), ctypes.byref(res)))
+    _ok(lib().ar_sol_ex(int(placement), ctypes.byref(res)))
+    return res.as_dict()
+
+
+def ar_sol_ranks(nranks: int, placement: int = AR_PLACE_XCD) -> dict:
+    res = ar_sol_ranks_result()
+    _ok(lib().ar_sol_ranks(int(nranks), int(placement), ctypes.byref(res)))
     return res.as_dict()
 
 

@@ -35,16 +35,34 @@ def sources() -> list[str]:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the library unconditionally and return its path."""
+    """Compile the library unconditionally and return its path. Every source is compiled to an
+    object file in its own hipcc process (in parallel), then the objects are linked."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed to build libar.so")
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="ar_build_") as d:
+        objs = [os.path.join(d, os.path.basename(src) + ".o") for src in sources()]
+        cmds = [[hipcc, *compile_flags, "-c", src, "-o", obj]
+                for src, obj in zip(sources(), objs)]
+        cmds.append([hipcc, *HIPCC_FLAGS, *objs, "-o", tmp])
+
+        def run(cmd):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            return subprocess.run(cmd, capture_output=True, text=True)
+
+        with ThreadPoolExecutor(max_workers=len(objs)) as pool:
+            results = list(pool.map(run, cmds[:-1]))
+        results.append(run(cmds[-1]) if all(r.returncode == 0 for r in results) else None)
+        for r in results:
+            if r is None or r.returncode != 0:
+                for q in results:
+                    if q is not None:
+                        sys.stderr.write(q.stdout + q.stderr)
+                raise RuntimeError("hipcc failed to build libar.so")
     os.replace(tmp, LIB)
     return LIB
 

@@ -77,9 +77,16 @@ constexpr uint32_t kNearSub = 2048;
 
 // Control words (device memory). The host-visible status copy lives in pinned host memory.
 enum Ctl : int {
-  CTL_ABORT = 0,   // set to 1 by the first wave that times out; polls give up when they see it
+  CTL_ABORT = 0,   // set to 1 by the first wave that times out; polls give up when they see it,
+                   // and a kernel that finds it set at entry exits without touching anything
+  CTL_CHECK_HITS = 1,  // input check (AR_OPT_CHECK_INPUTS): inputs found equal to the sentinel
+  CTL_CHECK_FIRST = 2, // u64 at words 2-3: (rank << 40) | element of the first such input
   CTL_WORDS = 16,
 };
+
+// Largest grid any plan launches (AR_PLACE_SAME: 8 * 16 ranks * 256 workgroups); the launch
+// record (AR_OPT_RECORD_LAUNCH) has one word per workgroup.
+constexpr int kMaxGrid = 8 * kMaxRanks * kMaxCtasPerRank;
 enum Status : int {
   ST_CODE = 0,     // 0 ok, 1 poll timed out
   ST_RANK = 1,
@@ -113,6 +120,8 @@ struct Args {
   uint32_t* status;     // host-mapped status words (pinned host memory)
   uint64_t* ts_start;   // optional [iters][nranks][ctas][waves] timestamps
   uint64_t* ts_end;
+  uint32_t* launch_rec; // optional [grid] words: XCC id | (rank + 1) << 8 | cta << 16 of every
+                        // workgroup (rank + 1 = 0 for workgroups that map to no rank)
   uint64_t e0;          // sequence number of the first step of this launch
   uint64_t timeout_ticks;
   uint32_t nbytes;      // input bytes per rank

@@ -37,13 +37,18 @@ namespace {
 
 thread_local std::string g_err;
 
-constexpr int kRegions = 13;
+constexpr int kRegions = 14;
 enum RegionId {
   RG_P1 = 0, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT,
   RG_LLN, RG_P1N, RG_P2N,  // near copies of ll, p1, p2 for small messages
   RG_PF1, RG_PF2, RG_FLG,  // bulk two-shot data slots and completion flags
+  RG_REC,                  // launch record (AR_OPT_RECORD_LAUNCH), written in rank 0's block only
 };
-constexpr uint64_t kDefaultCap = 256ull << 20;
+// Default scratch per rank per protocol: the sizes the pages settle on after their scratch-size
+// sweep (Pith review, "Assumptions & free parameters": 4 MiB for the one-shot, 64 MiB for the
+// two-shot and LL128; Fig. 12 caption). Larger messages run in equal chunks.
+constexpr uint64_t kDefaultCapOneShot = 4ull << 20;
+constexpr uint64_t kDefaultCapTwoShot = 64ull << 20;
 constexpr uint64_t kMaxCap = 1ull << 30;  // keeps every region below the drop offset (2 GiB)
 constexpr int kXcds = 8;
 
@@ -123,6 +128,8 @@ struct ar_handle {
   int drift = 0;
   int narrow = 1;  // one-pass sentinel kernels may use 8-byte units
   int root = 0;    // ar_bench of AR_BROADCAST: the root rank
+  int check_inputs = 0;   // check every call's inputs against the sentinel before launching
+  int record_launch = 0;  // kernels write the launch record (region RG_REC of rank 0)
   void** tab = nullptr;
   size_t tab_cap = 0;
   uint64_t* ts = nullptr;
@@ -292,7 +299,12 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
       if (static_cast<uint64_t>(ctas) * L.threads < C || ctas > rank_cus || loop_only)
         return kNoNarrow;
     }
-    if (static_cast<uint64_t>(ctas) * L.threads < C || loop_only) {
+    // int32 two-shot: the all-gather carries sums, and a sum may equal the sentinel (INT32_MIN
+    // is a legal int32 sum), so int32 always takes the bulk kernel, whose completion flags do not
+    // look at the data.
+    const bool flag_protocol = algo == AR_TWOSHOT && h->dtype == AR_INT32;
+    if (flag_protocol && ub == 8) return kNoNarrow;
+    if (static_cast<uint64_t>(ctas) * L.threads < C || loop_only || flag_protocol) {
       // The chunk does not fit one pass of the rank's lanes: the kernels built for one pass (the
       // latency path) hand it to their multi-pass counterparts.
       const int multi = algo == AR_TWOSHOT             ? ar::ALGO_TWOSHOT_BULK
@@ -308,7 +320,11 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
         if (h->threads == 0) L.threads = 256;
         max_ctas = co_resident(L.fn);
         ctas = pick_ctas(max_ctas);
-        if (h->ctas == 0 && max_ctas >= rank_cus) {
+        // (the int32 two-shot takes this kernel at every size; a chunk that one workgroup per
+        // compute unit covers in one pass keeps the plain count of workgroups)
+        const bool one_pass_bulk =
+            flag_protocol && C <= static_cast<uint64_t>(rank_cus) * static_cast<uint64_t>(L.threads);
+        if (h->ctas == 0 && max_ctas >= rank_cus && !one_pass_bulk) {
           // Every lane of the rank makes the same number of passes, and every compute unit of
           // the rank holds the same number of workgroups: among whole multiples of the rank's
           // compute units, the one with the least padded work (passes x lanes). A rank only
@@ -420,6 +436,9 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
   a.flg = h->rg[RG_FLG];
   a.ctl = h->ctl;
   a.status = h->status_dev;
+  a.launch_rec = h->record_launch
+                     ? reinterpret_cast<uint32_t*>(h->base + h->rg[RG_REC].off)
+                     : nullptr;
   a.e0 = h->epoch;
   const double ticks = static_cast<double>(h->timeout_us) * h->clock_hz * 1e-6;
   a.timeout_ticks = ticks < 1.0 ? 1ull : static_cast<uint64_t>(ticks);
@@ -540,6 +559,33 @@ int check_status(ar_handle* h) {
   return AR_OK;
 }
 
+// AR_OPT_CHECK_INPUTS: before a launch, look for inputs equal to the sentinel (the caller's
+// obligation under the sentinel protocol, Every µs Matters §IV "Sentinel"). Synchronous on
+// `stream`; AR_EINVAL names the first offending rank and element. `in` holds N pointers of
+// `nbytes` bytes each; with root >= 0 only in[root] is checked.
+int check_inputs(ar_handle* h, const void* const in[], uint64_t nbytes, int root,
+                 hipStream_t stream) {
+  if (nbytes == 0) return AR_OK;
+  AR_HIP(hipMemsetAsync(h->ctl + ar::CTL_CHECK_HITS, 0, 4, stream));
+  AR_HIP(hipMemsetAsync(h->ctl + ar::CTL_CHECK_FIRST, 0xFF, 8, stream));
+  const void* tab[ar::kMaxRanks];
+  const int n = root >= 0 ? 1 : h->nranks;
+  for (int r = 0; r < n; ++r) tab[r] = in[root >= 0 ? root : r];
+  AR_HIP(static_cast<hipError_t>(ar_launch_check(tab, n, static_cast<uint32_t>(nbytes), h->dtype,
+                                                 h->ctl, stream)));
+  uint32_t w[4] = {0, 0, 0, 0};
+  AR_HIP(hipMemcpyAsync(w, h->ctl + ar::CTL_CHECK_HITS, sizeof w, hipMemcpyDeviceToHost, stream));
+  AR_HIP(hipStreamSynchronize(stream));
+  if (w[0] != 0) {
+    const uint64_t first = (static_cast<uint64_t>(w[2]) << 32) | w[1];
+    const int rank = root >= 0 ? root : static_cast<int>(first >> 40);
+    return ar_fail(AR_EINVAL,
+                   "%u input element(s) equal the sentinel; the first is element %llu of rank %d",
+                   w[0], static_cast<unsigned long long>(first & ((1ull << 40) - 1)), rank);
+  }
+  return AR_OK;
+}
+
 int launch(ar_kernel_fn fn, unsigned grid, int threads, ar::Args& a, hipStream_t stream) {
   void* args[] = {&a};
   AR_HIP(hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(threads), args, 0,
@@ -590,8 +636,8 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
   h->dtype = dtype;
   h->max_bytes = max_bytes;
   const int N = nranks;
-  const uint64_t cap_os = std::min(env_u64("AR_SCRATCH_ONESHOT", kDefaultCap), kMaxCap);
-  const uint64_t cap_ts = std::min(env_u64("AR_SCRATCH_TWOSHOT", kDefaultCap), kMaxCap);
+  const uint64_t cap_os = std::min(env_u64("AR_SCRATCH_ONESHOT", kDefaultCapOneShot), kMaxCap);
+  const uint64_t cap_ts = std::min(env_u64("AR_SCRATCH_TWOSHOT", kDefaultCapTwoShot), kMaxCap);
   h->timeout_us = static_cast<int64_t>(env_u64("AR_POLL_TIMEOUT_US", 2000000));
   auto fail = [&](hipError_t e, const char* what) {
     ar_fail_hip(e, what);
@@ -629,6 +675,7 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
   sz[RG_PF1] = {pitch_pf, 2ull * N * pitch_pf};
   sz[RG_PF2] = {pitch_pf, 2ull * N * pitch_pf};
   sz[RG_FLG] = {0, 2ull * ar::kMaxRanks * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 8};
+  sz[RG_REC] = {0, 4ull * ar::kMaxGrid};
   // near area: the near ll, p1 and p2 regions, one 2 MiB page each (pitch set per launch)
   uint64_t off = 0;
   for (int i = RG_LLN; i <= RG_P2N; ++i) {
@@ -638,7 +685,8 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
     h->rg[i].near = 1;
     off += ar::kNearPage;
   }
-  for (int i : {RG_P1, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT, RG_PF1, RG_PF2, RG_FLG}) {
+  for (int i : {RG_P1, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT, RG_PF1, RG_PF2, RG_FLG,
+                RG_REC}) {
     if (sz[i].bytes >= (1ull << 31)) {
       ar_fail(AR_ETOOBIG, "scratch region %d would exceed 2 GiB per rank", i);
       release(h);
@@ -724,6 +772,14 @@ int ar_set_option(ar_handle* h, ar_option opt, int64_t v) {
       if (v < 0 || v >= h->nranks) return ar_fail(AR_EINVAL, "root out of range");
       h->root = static_cast<int>(v);
       return AR_OK;
+    case AR_OPT_CHECK_INPUTS:
+      if (v != 0 && v != 1) return ar_fail(AR_EINVAL, "check_inputs must be 0 or 1");
+      h->check_inputs = static_cast<int>(v);
+      return AR_OK;
+    case AR_OPT_RECORD_LAUNCH:
+      if (v != 0 && v != 1) return ar_fail(AR_EINVAL, "record_launch must be 0 or 1");
+      h->record_launch = static_cast<int>(v);
+      return AR_OK;
   }
   return ar_fail(AR_EINVAL, "unknown option %d", static_cast<int>(opt));
 }
@@ -769,6 +825,7 @@ int ar_allreduce(ar_handle* h, const void* const in[], void* const out[], size_t
   Launch L;
   rc = plan(h, alg, nbytes, L);
   if (rc != AR_OK) return rc;
+  if (h->check_inputs && (rc = check_inputs(h, in, nbytes, -1, s)) != AR_OK) return rc;
   ar::Args a = base_args(h, alg, nbytes, L);
   for (int r = 0; r < N; ++r) {
     a.in[r] = in[r];
@@ -834,6 +891,9 @@ int run_collective(ar_handle* h, int algo, const void* const in[], void* const o
   Launch L;
   rc = plan(h, algo, in_b, L);
   if (rc != AR_OK) return rc;
+  if (h->check_inputs &&
+      (rc = check_inputs(h, in, in_b, algo == AR_BROADCAST ? root : -1, s)) != AR_OK)
+    return rc;
   ar::Args a = base_args(h, algo, in_b, L);
   collective_args(algo, L.kernel_algo, in_b, out_b, N, root, a);
   for (int r = 0; r < N; ++r) {
@@ -877,7 +937,14 @@ int ar_check(ar_handle* h) {
 
 int ar_bench(ar_handle* h, const void* const* in_sets, void* const* out_sets, int nsets,
              size_t count, ar_algo algo, int iters, uint64_t* t_start, uint64_t* t_end,
-             double* elapsed_ms, void* stream) {
+             void* stream) {
+  return ar_bench_ex(h, in_sets, out_sets, nsets, count, algo, iters, t_start, t_end, nullptr,
+                     stream);
+}
+
+int ar_bench_ex(ar_handle* h, const void* const* in_sets, void* const* out_sets, int nsets,
+                size_t count, ar_algo algo, int iters, uint64_t* t_start, uint64_t* t_end,
+                double* elapsed_ms, void* stream) {
   if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
   if (iters < 1 || iters > 1000000) return ar_fail(AR_EINVAL, "iters must be in [1, 1e6]");
   if ((algo < AR_ALGO_AUTO || algo > AR_BARRIER_ONLY) && !is_collective(algo))
@@ -1075,6 +1142,7 @@ int ar_read_region(ar_handle* h, int rank, int region, void* host_dst, size_t by
   if (rank < 0 || rank >= h->nranks || region < 0 || region >= kRegions)
     return ar_fail(AR_EINVAL, "bad rank or region");
   if (bytes > h->rg[region].bytes) return ar_fail(AR_EINVAL, "read past the region");
+  if (region == RG_REC && rank != 0) return ar_fail(AR_EINVAL, "the launch record is in rank 0");
   if (h->last_stream) AR_HIP(hipStreamSynchronize(h->last_stream));
   AR_HIP(hipDeviceSynchronize());
   AR_HIP(hipMemcpy(host_dst, h->base + static_cast<uint64_t>(rank) * h->stride + h->rg[region].off,

@@ -8,10 +8,18 @@
 
 typedef void (*ar_kernel_fn)(ar::Args);
 
-// Defined in ar_kernels.hip.
+// Defined in ar_kernels.hip (dispatch) and ar_kernels_{f32,bf16,i32}.hip (per data type).
 ar_kernel_fn ar_select_kernel(int algo, int dt, int nmax);
+ar_kernel_fn ar_select_kernel_f32(int algo, int nmax);
+ar_kernel_fn ar_select_kernel_bf16(int algo, int nmax);
+ar_kernel_fn ar_select_kernel_i32(int algo, int nmax);
 void ar_launch_fill(uint8_t* base, uint64_t stride, int nranks, uint64_t off, uint32_t bytes,
                     uint32_t word, hipStream_t stream);
+// Count the inputs of `nranks` ranks (nbytes each) that equal the dtype's sentinel into
+// ctl[CTL_CHECK_HITS] / ctl[CTL_CHECK_FIRST] (the caller clears them first). Returns a
+// hipError_t value.
+int ar_launch_check(const void* const* in, int nranks, uint32_t nbytes, int dt, uint32_t* ctl,
+                    hipStream_t stream);
 
 // Defined in ar_sol.hip: calibrate every near page of every rank block (the first kNearArea
 // bytes of each block, 2 MiB aligned, zero): ns[r][g][p][k] = store -> poll half round trip

@@ -370,7 +370,64 @@ int ar_pingpong(int placement, int store_policy, int load_policy, int rounds, do
   return run_pingpong(placement, store_policy, load_policy, rounds, half_rtt_ns, xcc);
 }
 
-int ar_sol(int placement, ar_sol_result* res) {
+int ar_sol(int placement, double* out_ns) {
+  if (out_ns == nullptr) return ar_fail(AR_EINVAL, "null result pointer");
+  ar_sol_result res;
+  const int rc = ar_sol_ex(placement, &res);
+  if (rc != AR_OK) return rc;
+  out_ns[0] = res.fence_ns;
+  out_ns[1] = res.l2_load_ns;
+  out_ns[2] = res.store_half_rtt_ns;
+  return AR_OK;
+}
+
+int ar_sol_ranks(int nranks, int placement, ar_sol_ranks_result* res) {
+  if (res == nullptr) return ar_fail(AR_EINVAL, "null result pointer");
+  if (nranks < 2 || nranks > ar::kMaxRanks)
+    return ar_fail(AR_EINVAL, "nranks must be in [2, %d]", ar::kMaxRanks);
+  if (placement != AR_PLACE_XCD && placement != AR_PLACE_SAME)
+    return ar_fail(AR_EINVAL, "placement must be AR_PLACE_XCD or AR_PLACE_SAME");
+  std::memset(res, 0, sizeof *res);
+  PageBuf page;
+  int rc;
+  if ((rc = page.alloc(ar::kNearPage)) != AR_OK) return rc;
+  // XCD of every rank's (first) workgroups, as the planner places them; workgroup w of the
+  // 16-workgroup probe runs on XCD w % 8, so the same XCD twice is workgroups x and x + 8
+  int xcd[ar::kMaxRanks];
+  for (int r = 0; r < nranks; ++r) xcd[r] = placement == AR_PLACE_XCD ? r % 8 : 0;
+  // each receiving XCD's slot position: the fastest for its partner pair {x, x ^ 1}, as the
+  // planner calibrates it
+  int pos[8];
+  for (int x = 0; x < 8; ++x) {
+    float ns[ar::kNearPositions];
+    if ((rc = pingpong_positions(page.p, x & ~1, (x & ~1) + 1, 200, ns)) != AR_OK) return rc;
+    pos[x] = static_cast<int>(std::min_element(ns, ns + ar::kNearPositions) - ns);
+  }
+  double worst = 0.0, best = 1e300;
+  bool seen[8][8] = {};
+  for (int r = 0; r < nranks; ++r) {
+    for (int q = 0; q < nranks; ++q) {
+      if (q == r || seen[xcd[q]][xcd[r]]) continue;
+      seen[xcd[q]][xcd[r]] = true;
+      const int a = xcd[q], b = xcd[q] == xcd[r] ? xcd[r] + 8 : xcd[r];
+      float ns[ar::kNearPositions];
+      if ((rc = pingpong_positions(page.p, a, b, 200, ns)) != AR_OK) return rc;
+      const double v = ns[pos[xcd[r]]];
+      res->pairs += 1;
+      if (v > worst) {
+        worst = v;
+        res->worst_sender_xcc = xcd[q];
+        res->worst_receiver_xcc = xcd[r];
+      }
+      best = std::min(best, v);
+    }
+  }
+  res->store_half_rtt_worst_ns = worst;
+  res->store_half_rtt_best_ns = best;
+  return AR_OK;
+}
+
+int ar_sol_ex(int placement, ar_sol_result* res) {
   if (res == nullptr) return ar_fail(AR_EINVAL, "null result pointer");
   if (placement != AR_PLACE_XCD && placement != AR_PLACE_SAME)
     return ar_fail(AR_EINVAL, "placement must be AR_PLACE_XCD or AR_PLACE_SAME");

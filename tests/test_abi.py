@@ -57,7 +57,8 @@ def test_null_handle_calls_fail_cleanly(arlib):
     assert L.ar_allreduce(None, None, None, 0, 0, None) == arlib.AR_EINVAL
     assert L.ar_check(None) == arlib.AR_EINVAL
     assert L.ar_set_option(None, 0, 1) == arlib.AR_EINVAL
-    assert L.ar_bench(None, None, None, 1, 1, 1, 1, None, None, None, None) == arlib.AR_EINVAL
+    assert L.ar_bench(None, None, None, 1, 1, 1, 1, None, None, None) == arlib.AR_EINVAL
+    assert L.ar_bench_ex(None, None, None, 1, 1, 1, 1, None, None, None, None) == arlib.AR_EINVAL
     assert L.ar_region_bytes(None, 0) == arlib.AR_EINVAL
     assert L.ar_epoch(None) == 0
     assert L.ar_reducescatter(None, None, None, 4, None) == arlib.AR_EINVAL
@@ -71,6 +72,8 @@ def test_null_handle_calls_fail_cleanly(arlib):
 def test_sol_and_probe_argument_checks(arlib):
     L = arlib.lib()
     assert L.ar_sol(0, None) == arlib.AR_EINVAL
+    assert L.ar_sol_ex(0, None) == arlib.AR_EINVAL
+    assert L.ar_sol_ranks(4, 0, None) == arlib.AR_EINVAL
     assert L.ar_stream_copy(None, None, 16, None) == arlib.AR_EINVAL
     half = ctypes.c_double()
     assert L.ar_pingpong(0, 3, 16, 10, ctypes.byref(half), None) == arlib.AR_EINVAL

@@ -177,7 +177,7 @@ def test_collectives_persistent_loop(op, drift, shape):
             outs += [torch.full((out_c,), 0x55, dtype=torch.float32, device="cuda")
                      for _ in range(n)]
         _say(f"case persistent {op} drift={drift} shape={shape}")
-        ts, te, ms = A.ar_bench(h, ins, outs, nsets, c, A.ALGOS[op], iters)
+        ts, te, ms = A.ar_bench_ex(h, ins, outs, nsets, c, A.ALGOS[op], iters)
         assert ms > 0
         for k, x in enumerate(xs):
             got = [o.cpu().numpy() for o in outs[k * n:(k + 1) * n]]
@@ -291,8 +291,16 @@ def test_plan_info_reports_the_launch():
     with handle(n, 16 << 20, "i32") as h:
         big = A.ar_plan_info(h, (16 << 20) // 4, A.AR_TWOSHOT)
         assert big["kernel"] == 7 and big["threads"] == 256 and big["chunks"] == 1
+        # int32 sums may equal the sentinel: the int32 two-shot always runs the bulk kernel
+        # (completion flags), on the regular slots, with one workgroup per 256 units when small
         small = A.ar_plan_info(h, 256, A.AR_TWOSHOT)
-        assert small["kernel"] in (3, 11) and small["near"] == 1 and small["chunks"] == 1
+        assert small["kernel"] == 7 and small["near"] == 0 and small["chunks"] == 1
+        assert small["ctas"] == 1
+    with handle(n, 16 << 20, "f32") as hf:
+        small_f = A.ar_plan_info(hf, 256, A.AR_TWOSHOT)
+        assert small_f["kernel"] in (3, 11) and small_f["near"] == 1 and small_f["chunks"] == 1
+        assert small_f["grid"] >= n * small_f["ctas"]
+    with handle(n, 16 << 20, "i32") as h:
         rs = A.ar_plan_info(h, 1024, A.AR_REDUCESCATTER)
         ag = A.ar_plan_info(h, 1024, A.AR_ALLGATHER)
         bc = A.ar_plan_info(h, 1024, A.AR_BROADCAST)

@@ -214,7 +214,7 @@ def test_persistent_loop_every_iteration(algo, drift):
             d = to_device(x)
             ins += d
             outs += [torch.empty_like(t) for t in d]
-        ts, te, ms = A.ar_bench(h, ins, outs, iters, count, A.ALGOS[algo], iters)
+        ts, te, ms = A.ar_bench_ex(h, ins, outs, iters, count, A.ALGOS[algo], iters)
         assert ms > 0
         for k in range(iters):
             got = from_device(outs[k * n:(k + 1) * n], np.float32)
@@ -256,16 +256,43 @@ def test_placements(placement):
 def test_sol_microbench_sane():
     from latency_collectives_amd import _ar as A
 
-    x = A.ar_sol(A.AR_PLACE_XCD)
+    x = A.ar_sol_ex(A.AR_PLACE_XCD)
     _say("sol xcd", x)
     assert x["l2_load_ns"] > 0 and x["store_half_rtt_ns"] > 0 and x["fence_ns"] > 0
     assert x["xcc_a"] != x["xcc_b"]
-    s = A.ar_sol(A.AR_PLACE_SAME)
+    s = A.ar_sol_ex(A.AR_PLACE_SAME)
     _say("sol same", s)
     assert s["xcc_a"] == s["xcc_b"]
     assert x["floor_ns"] == pytest.approx(2 * x["l2_load_ns"] + x["store_half_rtt_ns"])
     # the floor's store term is the line homed near the pair; the other half's is reported too
     assert x["store_half_rtt_far_ns"] >= x["store_half_rtt_ns"] > 0
+    # sanity pins of the bound's terms: a store seen from another XCD is no faster than one seen
+    # on the same XCD, and a dependent L2 hit is no slower than a store plus release fence
+    assert x["store_half_rtt_ns"] >= s["store_half_rtt_ns"]
+    assert x["l2_load_ns"] <= x["fence_ns"]
+    # the three-value form returns the same terms
+    b = A.ar_sol(A.AR_PLACE_XCD)
+    assert set(b) == {"fence_ns", "l2_load_ns", "store_half_rtt_ns"}
+    assert all(v > 0 for v in b.values())
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16])
+def test_sol_ranks_floor_covers_every_pair(n):
+    """The N-rank store term is the slowest (sender, receiver) XCD pair of the placement: at
+    least the nearest pair's, and it names two XCDs that hold ranks."""
+    from latency_collectives_amd import _ar as A
+
+    near = A.ar_sol_ex(A.AR_PLACE_XCD)
+    r = A.ar_sol_ranks(n, A.AR_PLACE_XCD)
+    _say(f"sol ranks n={n}", r)
+    xcds = {q % 8 for q in range(n)}
+    assert r["worst_sender_xcc"] in xcds and r["worst_receiver_xcc"] in xcds
+    distinct = len(xcds) * (len(xcds) - 1) + (len(xcds) if n > 8 else 0)
+    assert r["pairs"] == distinct
+    assert r["store_half_rtt_worst_ns"] >= r["store_half_rtt_best_ns"] > 0
+    # the nearest 0-1 position is one of the candidates the worst pair is chosen over, up to the
+    # run-to-run spread of a ping-pong
+    assert r["store_half_rtt_worst_ns"] >= 0.9 * near["store_half_rtt_ns"]
 
 
 def test_sixteen_byte_lines_not_torn():

@@ -27,12 +27,22 @@ def kernels(tmp_path_factory):
     if not (os.path.exists(bundler) and os.path.exists(objdump) and shutil.which("objcopy")):
         pytest.skip("ROCm LLVM tools or objcopy not available")
     d = tmp_path_factory.mktemp("isa")
-    fat, co = str(d / "fat.bin"), str(d / "co.o")
+    fat = str(d / "fat.bin")
     subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", lib], check=True)
-    subprocess.run([bundler, "--unbundle", "--type=o", f"--input={fat}",
-                    "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={co}"], check=True)
-    text = subprocess.run([objdump, "-d", "--mcpu=gfx950", co], check=True, capture_output=True,
-                          text=True).stdout
+    # one offload bundle per translation unit, concatenated (each starts with the magic string)
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    raw = open(fat, "rb").read()
+    starts = [m.start() for m in re.finditer(re.escape(magic), raw)]
+    text = ""
+    for j, a in enumerate(starts):
+        part, co = str(d / f"fat{j}.bin"), str(d / f"co{j}.o")
+        with open(part, "wb") as f:
+            f.write(raw[a:starts[j + 1] if j + 1 < len(starts) else len(raw)])
+        subprocess.run([bundler, "--unbundle", "--type=o", f"--input={part}",
+                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={co}"],
+                       check=True)
+        text += subprocess.run([objdump, "-d", "--mcpu=gfx950", co], check=True,
+                               capture_output=True, text=True).stdout
     out, name = {}, None
     for line in text.splitlines():
         m = re.match(r"^[0-9a-f]+ <(\S+)>:$", line)
