@@ -125,6 +125,29 @@ int ar_allreduce(ar_handle* h, const void* const in[], void* const out[], size_t
                  ar_algo algo, void* stream);
 
 /*
+ * ar_allreduce_noalloc: ar_allreduce for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation. It makes no
+ * allocation of any kind; there is no handle. The symmetric scratch is a static device array
+ * of 32 MiB that the library holds on every GPU it runs on until the process ends (scratch per
+ * rank per protocol 256 KiB, so larger messages run in more chunks than through a handle).
+ *   nranks, dtype          : as for ar_create (1..16; AR_FLOAT32, AR_BFLOAT16, AR_INT32).
+ *   in, out, count, algo   : as for ar_allreduce (count * sizeof(dtype) < 2^31 bytes per rank,
+ *                            AR_ETOOBIG beyond; every algorithm of ar_allreduce is accepted).
+ *   stream                 : hipStream_t; the call only enqueues work on it.
+ * The array keeps the last call's state (sequence number, armed slots). When nranks or dtype
+ * differs from the previous call on the current GPU, the call first clears the array and
+ * re-arms its slots on `stream`. Calls on one GPU must not overlap: two calls in flight at once
+ * on one GPU (on different streams, or from different threads) race on the shared array, and
+ * calls must be issued in order, as on one handle. Device poll timeouts are not reported to the
+ * host (there is no status block to read without allocating): the timed-out kernel raises the
+ * abort word in the array, every later call on that GPU then exits without writing its outputs,
+ * until a call with another (nranks, dtype) sets the array up again. Argument errors are
+ * synchronous return codes, as for ar_allreduce.
+ */
+int ar_allreduce_noalloc(int nranks, ar_dtype dtype, const void* const in[], void* const out[],
+                         size_t count, ar_algo algo, void* stream);
+
+/*
  * Standalone collectives from the same barrier-free primitives. The paper notes that AllReduce is
  * commonly decomposed into ReduceScatter + AllGather or Reduce + Broadcast (Every µs Matters,
  * §III opening paragraph), and the Pith review of it ("If this is right") expects these

@@ -44,7 +44,7 @@ DTYPES = {"f32": AR_FLOAT32, "bf16": AR_BFLOAT16, "i32": AR_INT32}
 
 # Every symbol include/ar.h declares.
 EXPORTS = (
-    "ar_create", "ar_allreduce", "ar_reducescatter", "ar_allgather", "ar_broadcast",
+    "ar_create", "ar_allreduce", "ar_allreduce_noalloc", "ar_reducescatter", "ar_allgather", "ar_broadcast",
     "ar_destroy", "ar_last_error", "ar_check", "ar_bench", "ar_bench_ex",
     "ar_wallclock_hz", "ar_set_option", "ar_region_bytes", "ar_alg_bytes", "ar_plan_info",
     "ar_read_region",
@@ -122,6 +122,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "ar_create": ([i32, sz, i32], vp),
         "ar_allreduce": ([vp, pp, pp, sz, i32, vp], i32),
+        "ar_allreduce_noalloc": ([i32, i32, pp, pp, sz, i32, vp], i32),
         "ar_reducescatter": ([vp, pp, pp, sz, vp], i32),
         "ar_allgather": ([vp, pp, pp, sz, vp], i32),
         "ar_broadcast": ([vp, vp, pp, sz, i32, vp], i32),
@@ -200,6 +201,12 @@ def ar_destroy(h: int) -> None:
 
 def ar_allreduce(h: int, ins, outs, count: int, algo: int, stream=None) -> None:
     _ok(lib().ar_allreduce(h, _table(ins), _table(outs), int(count), int(algo), _stream(stream)))
+
+
+def ar_allreduce_noalloc(nranks: int, dtype: int, ins, outs, count: int, algo: int,
+                         stream=None) -> None:
+    _ok(lib().ar_allreduce_noalloc(int(nranks), int(dtype), _table(ins), _table(outs),
+                                   int(count), int(algo), _stream(stream)))
 
 
 def ar_reducescatter(h: int, ins, outs, recvcount: int, stream=None) -> None:

@@ -24,10 +24,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <map>
-#include <utility>
 #include <mutex>
-#include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/ar.h"
@@ -35,7 +33,9 @@
 
 namespace {
 
-thread_local std::string g_err;
+// Message of the last failing call on this thread. A fixed buffer: recording an error never
+// allocates (the allocation-free entry point shares this path).
+thread_local char g_err[512];
 
 constexpr int kRegions = 14;
 enum RegionId {
@@ -68,24 +68,90 @@ int elem_bytes(int dt) { return dt == AR_BFLOAT16 ? 2 : 4; }
 
 uint32_t sentinel_word(int dt) { return dt == AR_INT32 ? 0x80000000u : 0xFFFFFFFFu; }
 
-// Resident workgroups per compute unit for (kernel, block size), cached. The key keeps both
-// parts: the host handles of different kernels are only a few bytes apart, so any mixing of the
-// two into one number could give a kernel the occupancy of another, and a grid planned on a
-// too-high occupancy cannot be co-resident.
+// Resident workgroups per compute unit for (kernel, block size), cached in a fixed table (no
+// allocation). The key keeps both parts: the host handles of different kernels are only a few
+// bytes apart, so any mixing of the two into one number could give a kernel the occupancy of
+// another, and a grid planned on a too-high occupancy cannot be co-resident.
+struct OccEntry {
+  const void* fn;
+  int threads;
+  int blocks;
+};
+constexpr int kOccSlots = 2048;  // > kernels (about 250) x block sizes (3)
 std::mutex g_occ_mu;
-std::map<std::pair<const void*, int>, int> g_occ;
+OccEntry g_occ[kOccSlots];
 
 int occupancy(ar_kernel_fn fn, int threads) {
   std::lock_guard<std::mutex> lk(g_occ_mu);
-  const auto key = std::make_pair(reinterpret_cast<const void*>(fn), threads);
-  auto it = g_occ.find(key);
-  if (it != g_occ.end()) return it->second;
-  int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn),
-                                                   threads, 0) != hipSuccess)
-    nb = 0;
-  g_occ[key] = nb;
-  return nb;
+  const void* key = reinterpret_cast<const void*>(fn);
+  size_t i = (reinterpret_cast<uintptr_t>(key) / 16 * 31 + static_cast<size_t>(threads)) % kOccSlots;
+  for (int probe = 0; probe < kOccSlots; ++probe, i = (i + 1) % kOccSlots) {
+    if (g_occ[i].fn == key && g_occ[i].threads == threads) return g_occ[i].blocks;
+    if (g_occ[i].fn == nullptr) {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, key, threads, 0) != hipSuccess)
+        nb = 0;
+      g_occ[i] = OccEntry{key, threads, nb};
+      return nb;
+    }
+  }
+  return 0;
+}
+
+// Region layout of one rank block (the same in every block: symmetric memory, §II.B) for N ranks
+// and messages of up to max_bytes per rank, with per-protocol scratch caps. With `near` the block
+// starts with the three 2 MiB near pages and is a whole number of 2 MiB pages; `record` adds the
+// launch record region. Writes the regions and the block size (*stride).
+int layout(int N, uint64_t max_bytes, uint64_t cap_os, uint64_t cap_ts, bool near, bool record,
+           ar::Region* rg, uint64_t* stride) {
+  // Slot sizes: large enough for the whole message unless the per-protocol cap says otherwise.
+  const uint64_t need_os = round_up(max_bytes, 16);
+  const uint64_t need_ts = ceil_div(ceil_div(max_bytes, 16), N) * 16;
+  const uint64_t per_slot_os = std::max<uint64_t>(256, (cap_os / (2 * N)) / 256 * 256);
+  const uint64_t per_slot_ts = std::max<uint64_t>(256, (cap_ts / (2 * N)) / 256 * 256);
+  const uint64_t slot_os = std::min(round_up(need_os, 256), per_slot_os);
+  const uint64_t slot_ts = std::min(round_up(need_ts, 256), per_slot_ts);
+  const uint64_t ll_payload = std::min(round_up(max_bytes, 8), std::max<uint64_t>(128, per_slot_os / 2));
+  const uint64_t slot_ll = round_up(2 * ll_payload, 256);
+  struct { uint64_t slot, bytes; } sz[kRegions] = {};
+  sz[RG_P1] = {std::max(slot_os, slot_ts), 2ull * N * std::max(slot_os, slot_ts)};
+  sz[RG_P2] = {slot_ts, 2ull * N * slot_ts};
+  sz[RG_LL] = {slot_ll, 2ull * N * slot_ll};
+  sz[RG_ACC] = {slot_ts, 2ull * slot_ts};
+  sz[RG_CNT] = {0, 2ull * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 4};
+  sz[RG_BAR] = {0, 1ull * ar::kMaxRanks * ar::kMaxCtasPerRank * 8};
+  sz[RG_BDAT] = {slot_os, 1ull * N * slot_os};
+  // The bulk two-shot's slots are 4 KiB longer than their data: an owner reads all N sources'
+  // slots at one offset at once, and streams exactly a power of two apart measured ~5 % slower.
+  const uint64_t pitch_pf = slot_ts + 4096;
+  sz[RG_PF1] = {pitch_pf, 2ull * N * pitch_pf};
+  sz[RG_PF2] = {pitch_pf, 2ull * N * pitch_pf};
+  sz[RG_FLG] = {0, 2ull * ar::kMaxRanks * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 8};
+  sz[RG_REC] = {0, record ? 4ull * ar::kMaxGrid : 0ull};
+  // near area: the near ll, p1 and p2 regions, one 2 MiB page each (pitch set per launch)
+  uint64_t off = 0;
+  for (int i = RG_LLN; i <= RG_P2N; ++i) {
+    rg[i] = ar::Region{};
+    rg[i].near = 1;
+    if (!near) continue;
+    rg[i].off = off;
+    rg[i].bytes = static_cast<uint32_t>(ar::kNearPage);
+    off += ar::kNearPage;
+  }
+  for (int i : {RG_P1, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT, RG_PF1, RG_PF2, RG_FLG,
+                RG_REC}) {
+    if (sz[i].bytes >= (1ull << 31)) {
+      return ar_fail(AR_ETOOBIG, "scratch region %d would exceed 2 GiB per rank", i);
+    }
+    rg[i] = ar::Region{};
+    rg[i].off = off;
+    rg[i].bytes = static_cast<uint32_t>(sz[i].bytes);
+    rg[i].slot = static_cast<uint32_t>(sz[i].slot);
+    off = round_up(off + sz[i].bytes, 4096);
+  }
+  // Rank blocks with near pages start on 2 MiB boundaries so that every near region is one page.
+  *stride = near ? round_up(off, ar::kNearPage) : round_up(off, 4096);
+  return AR_OK;
 }
 
 }  // namespace
@@ -96,7 +162,7 @@ int ar_fail(int code, const char* fmt, ...) {
   va_start(ap, fmt);
   std::vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
-  g_err = buf;
+  std::memcpy(g_err, buf, sizeof g_err);
   return code;
 }
 
@@ -128,6 +194,7 @@ struct ar_handle {
   int drift = 0;
   int narrow = 1;  // one-pass sentinel kernels may use 8-byte units
   int root = 0;    // ar_bench of AR_BROADCAST: the root rank
+  bool near_ok = true;    // the blocks start with calibrated near pages
   int check_inputs = 0;   // check every call's inputs against the sentinel before launching
   int record_launch = 0;  // kernels write the launch record (region RG_REC of rank 0)
   void** tab = nullptr;
@@ -224,7 +291,8 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   // Messages whose 2 * N slots fit a near page in one chunk use the near regions: the slot data
   // goes in 8 KiB chunks at a pitch of 16 KiB per chunk.
   const uint64_t near_chunks = ceil_div(units * line, ar::kGranule);
-  const bool near_fits = units > 0 && 2ull * N * near_chunks * 2 * ar::kGranule <= ar::kNearPage &&
+  const bool near_fits = h->near_ok && units > 0 &&
+                         2ull * N * near_chunks * 2 * ar::kGranule <= ar::kNearPage &&
                          (algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL ||
                           algo == AR_TWOSHOT || algo == AR_REDUCESCATTER || algo == AR_ALLGATHER ||
                           algo == AR_BROADCAST ||
@@ -604,11 +672,65 @@ void release(ar_handle* h) {
   delete h;
 }
 
+// Argument checks, plan and launch of one AllReduce on handle h (ar_allreduce and the
+// allocation-free entry point). A handle without host status words (status_host == nullptr)
+// skips the status check.
+int allreduce_enqueue(ar_handle* h, const void* const in[], void* const out[], size_t count,
+                      ar_algo algo, hipStream_t s) {
+  if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
+  if (in == nullptr || out == nullptr) return ar_fail(AR_EINVAL, "null pointer table");
+  if (algo < AR_ALGO_AUTO || algo > AR_BARRIER2)
+    return ar_fail(AR_EINVAL, "algorithm %d is not valid for ar_allreduce", static_cast<int>(algo));
+  int rc = h->status_host != nullptr ? check_status(h) : AR_OK;
+  if (rc != AR_OK) return rc;
+  const int N = h->nranks;
+  const uint64_t nbytes = static_cast<uint64_t>(count) * elem_bytes(h->dtype);
+  if (count != 0 && nbytes / count != static_cast<uint64_t>(elem_bytes(h->dtype)))
+    return ar_fail(AR_ETOOBIG, "count overflows");
+  if (nbytes > h->max_bytes)
+    return ar_fail(AR_ETOOBIG, "%llu bytes per rank exceed max_bytes %zu",
+                   static_cast<unsigned long long>(nbytes), h->max_bytes);
+  for (int r = 0; r < N; ++r) {
+    if (in[r] == nullptr || out[r] == nullptr)
+      return ar_fail(AR_EINVAL, "null buffer for rank %d", r);
+    if ((reinterpret_cast<uintptr_t>(in[r]) | reinterpret_cast<uintptr_t>(out[r])) & 15u)
+      return ar_fail(AR_EINVAL, "buffers of rank %d are not 16-byte aligned", r);
+  }
+  if (nbytes > 0) {
+    for (int r = 0; r < N; ++r)
+      for (int q = 0; q < N; ++q) {
+        if (q != r && overlap(out[r], out[q], nbytes))
+          return ar_fail(AR_EINVAL, "outputs of ranks %d and %d overlap", r, q);
+        if (overlap(out[r], in[q], nbytes) && !(q == r && out[r] == in[r]))
+          return ar_fail(AR_EINVAL, "output of rank %d overlaps input of rank %d", r, q);
+      }
+  }
+  if (nbytes == 0) {
+    h->epoch += 1;
+    return AR_OK;
+  }
+  const int alg = resolve_algo(h, algo, nbytes);
+  Launch L;
+  rc = plan(h, alg, nbytes, L);
+  if (rc != AR_OK) return rc;
+  if (h->check_inputs && (rc = check_inputs(h, in, nbytes, -1, s)) != AR_OK) return rc;
+  ar::Args a = base_args(h, alg, nbytes, L);
+  for (int r = 0; r < N; ++r) {
+    a.in[r] = in[r];
+    a.out[r] = out[r];
+  }
+  rc = launch(L.fn, L.grid, L.threads, a, s);
+  if (rc != AR_OK) return rc;
+  h->epoch += static_cast<uint64_t>(L.chunks);
+  h->last_stream = s;
+  return AR_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-const char* ar_last_error(void) { return g_err.c_str(); }
+const char* ar_last_error(void) { return g_err; }
 
 double ar_wallclock_hz(void) {
   int dev = 0, khz = 0;
@@ -618,7 +740,7 @@ double ar_wallclock_hz(void) {
 }
 
 ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
-  g_err.clear();
+  g_err[0] = '\0';
   if (nranks < 1 || nranks > ar::kMaxRanks) {
     ar_fail(AR_EINVAL, "nranks must be in [1, %d], got %d", ar::kMaxRanks, nranks);
     return nullptr;
@@ -652,53 +774,10 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
   h->clock_hz = ar_wallclock_hz();
   if (h->clock_hz <= 0.0) h->clock_hz = 100e6;
 
-  // Slot sizes: large enough for the whole message unless the per-protocol cap says otherwise.
-  const uint64_t need_os = round_up(max_bytes, 16);
-  const uint64_t need_ts = ceil_div(ceil_div(max_bytes, 16), N) * 16;
-  const uint64_t per_slot_os = std::max<uint64_t>(256, (cap_os / (2 * N)) / 256 * 256);
-  const uint64_t per_slot_ts = std::max<uint64_t>(256, (cap_ts / (2 * N)) / 256 * 256);
-  const uint64_t slot_os = std::min(round_up(need_os, 256), per_slot_os);
-  const uint64_t slot_ts = std::min(round_up(need_ts, 256), per_slot_ts);
-  const uint64_t ll_payload = std::min(round_up(max_bytes, 8), std::max<uint64_t>(128, per_slot_os / 2));
-  const uint64_t slot_ll = round_up(2 * ll_payload, 256);
-  struct { uint64_t slot, bytes; } sz[kRegions];
-  sz[RG_P1] = {std::max(slot_os, slot_ts), 2ull * N * std::max(slot_os, slot_ts)};
-  sz[RG_P2] = {slot_ts, 2ull * N * slot_ts};
-  sz[RG_LL] = {slot_ll, 2ull * N * slot_ll};
-  sz[RG_ACC] = {slot_ts, 2ull * slot_ts};
-  sz[RG_CNT] = {0, 2ull * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 4};
-  sz[RG_BAR] = {0, 1ull * ar::kMaxRanks * ar::kMaxCtasPerRank * 8};
-  sz[RG_BDAT] = {slot_os, 1ull * N * slot_os};
-  // The bulk two-shot's slots are 4 KiB longer than their data: an owner reads all N sources'
-  // slots at one offset at once, and streams exactly a power of two apart measured ~5 % slower.
-  const uint64_t pitch_pf = slot_ts + 4096;
-  sz[RG_PF1] = {pitch_pf, 2ull * N * pitch_pf};
-  sz[RG_PF2] = {pitch_pf, 2ull * N * pitch_pf};
-  sz[RG_FLG] = {0, 2ull * ar::kMaxRanks * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 8};
-  sz[RG_REC] = {0, 4ull * ar::kMaxGrid};
-  // near area: the near ll, p1 and p2 regions, one 2 MiB page each (pitch set per launch)
-  uint64_t off = 0;
-  for (int i = RG_LLN; i <= RG_P2N; ++i) {
-    sz[i] = {0, ar::kNearPage};
-    h->rg[i].off = off;
-    h->rg[i].bytes = static_cast<uint32_t>(ar::kNearPage);
-    h->rg[i].near = 1;
-    off += ar::kNearPage;
+  if (layout(N, max_bytes, cap_os, cap_ts, true, true, h->rg, &h->stride) != AR_OK) {
+    release(h);
+    return nullptr;
   }
-  for (int i : {RG_P1, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT, RG_PF1, RG_PF2, RG_FLG,
-                RG_REC}) {
-    if (sz[i].bytes >= (1ull << 31)) {
-      ar_fail(AR_ETOOBIG, "scratch region %d would exceed 2 GiB per rank", i);
-      release(h);
-      return nullptr;
-    }
-    h->rg[i].off = off;
-    h->rg[i].bytes = static_cast<uint32_t>(sz[i].bytes);
-    h->rg[i].slot = static_cast<uint32_t>(sz[i].slot);
-    off = round_up(off + sz[i].bytes, 4096);
-  }
-  // Rank blocks start on 2 MiB boundaries so that every near region is one 2 MiB page.
-  h->stride = round_up(off, ar::kNearPage);
   const uint64_t total = h->stride * N;
   if ((e = hipMalloc(&h->raw, total + ar::kNearPage)) != hipSuccess)
     return fail(e, "hipMalloc(scratch)");
@@ -788,54 +867,7 @@ uint64_t ar_epoch(ar_handle* h) { return h ? h->epoch : 0; }
 
 int ar_allreduce(ar_handle* h, const void* const in[], void* const out[], size_t count,
                  ar_algo algo, void* stream) {
-  if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
-  if (in == nullptr || out == nullptr) return ar_fail(AR_EINVAL, "null pointer table");
-  if (algo < AR_ALGO_AUTO || algo > AR_BARRIER2)
-    return ar_fail(AR_EINVAL, "algorithm %d is not valid for ar_allreduce", static_cast<int>(algo));
-  int rc = check_status(h);
-  if (rc != AR_OK) return rc;
-  const int N = h->nranks;
-  const uint64_t nbytes = static_cast<uint64_t>(count) * elem_bytes(h->dtype);
-  if (count != 0 && nbytes / count != static_cast<uint64_t>(elem_bytes(h->dtype)))
-    return ar_fail(AR_ETOOBIG, "count overflows");
-  if (nbytes > h->max_bytes)
-    return ar_fail(AR_ETOOBIG, "%llu bytes per rank exceed max_bytes %zu",
-                   static_cast<unsigned long long>(nbytes), h->max_bytes);
-  for (int r = 0; r < N; ++r) {
-    if (in[r] == nullptr || out[r] == nullptr)
-      return ar_fail(AR_EINVAL, "null buffer for rank %d", r);
-    if ((reinterpret_cast<uintptr_t>(in[r]) | reinterpret_cast<uintptr_t>(out[r])) & 15u)
-      return ar_fail(AR_EINVAL, "buffers of rank %d are not 16-byte aligned", r);
-  }
-  if (nbytes > 0) {
-    for (int r = 0; r < N; ++r)
-      for (int q = 0; q < N; ++q) {
-        if (q != r && overlap(out[r], out[q], nbytes))
-          return ar_fail(AR_EINVAL, "outputs of ranks %d and %d overlap", r, q);
-        if (overlap(out[r], in[q], nbytes) && !(q == r && out[r] == in[r]))
-          return ar_fail(AR_EINVAL, "output of rank %d overlaps input of rank %d", r, q);
-      }
-  }
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (nbytes == 0) {
-    h->epoch += 1;
-    return AR_OK;
-  }
-  const int alg = resolve_algo(h, algo, nbytes);
-  Launch L;
-  rc = plan(h, alg, nbytes, L);
-  if (rc != AR_OK) return rc;
-  if (h->check_inputs && (rc = check_inputs(h, in, nbytes, -1, s)) != AR_OK) return rc;
-  ar::Args a = base_args(h, alg, nbytes, L);
-  for (int r = 0; r < N; ++r) {
-    a.in[r] = in[r];
-    a.out[r] = out[r];
-  }
-  rc = launch(L.fn, L.grid, L.threads, a, s);
-  if (rc != AR_OK) return rc;
-  h->epoch += static_cast<uint64_t>(L.chunks);
-  h->last_stream = s;
-  return AR_OK;
+  return allreduce_enqueue(h, in, out, count, algo, reinterpret_cast<hipStream_t>(stream));
 }
 
 namespace {
@@ -1151,3 +1183,108 @@ int ar_read_region(ar_handle* h, int rank, int region, void* host_dst, size_t by
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free AllReduce
+//
+// ar_allreduce_noalloc: ar_allreduce for callers that cannot allocate device memory (code under
+// HIP graph capture, tight serving loops, harnesses that forbid allocation). Its symmetric
+// scratch is the file-scope device array `scratch` below, one copy per GPU the library runs on;
+// its handle-shaped state (region layout, sequence number) lives in static host storage. It calls
+// no allocating routine: set-up is hipGetSymbolAddress once per device plus fill kernels on the
+// caller's stream whenever the (rank count, dtype) the scratch is laid out for changes.
+
+namespace {
+
+// Scratch per rank per protocol: a quarter MiB, so that 16 rank blocks with every region fit the
+// array; larger messages run in more chunks than with a handle (whose default caps are 4 MiB /
+// 64 MiB).
+constexpr uint64_t kNoAllocCap = 256ull << 10;
+constexpr uint64_t kNoAllocCtl = 4096;  // control words (16 x u32) and status words (8 x u32)
+constexpr uint64_t kNoAllocScratchBytes = 32ull << 20;
+constexpr int kNoAllocDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+struct NoAllocDevice {
+  uint8_t* ptr = nullptr;  // this device's copy of `scratch` (from hipGetSymbolAddress)
+  int nranks = 0;          // layout the scratch holds (0: not laid out yet)
+  int dtype = -1;
+  ar_handle h;             // handle-shaped state over the scratch; owns nothing
+};
+std::mutex g_na_mu;
+NoAllocDevice g_na[kNoAllocDevices];
+
+// Lay the scratch of device `dev` out for (nranks, dtype): clear everything (LL lines, flags,
+// counters, atomic destinations, control and status words) and arm the sentinel slots, on
+// `stream`; the sequence number restarts at 1.
+int noalloc_setup(NoAllocDevice& d, int dev, int nranks, int dtype, hipStream_t stream) {
+  ar_handle& h = d.h;
+  h.nranks = nranks;
+  h.dtype = dtype;
+  h.max_bytes = 0x7FFFFFFFull;
+  h.device = dev;
+  h.near_ok = false;  // the array is neither 2 MiB aligned nor calibrated: regular regions only
+  h.placement = AR_PLACE_XCD;
+  h.timeout_us = static_cast<int64_t>(env_u64("AR_POLL_TIMEOUT_US", 2000000));
+  AR_HIP(hipDeviceGetAttribute(&h.cu_count, hipDeviceAttributeMultiprocessorCount, dev));
+  h.clock_hz = ar_wallclock_hz();
+  if (h.clock_hz <= 0.0) h.clock_hz = 100e6;
+  int rc = layout(nranks, h.max_bytes, kNoAllocCap, kNoAllocCap, false, false, h.rg, &h.stride);
+  if (rc != AR_OK) return rc;
+  const uint64_t total = kNoAllocCtl + h.stride * static_cast<uint64_t>(nranks);
+  if (total > kNoAllocScratchBytes)
+    return ar_fail(AR_ETOOBIG, "%d ranks need %llu bytes of scratch, the array holds %llu", nranks,
+                   static_cast<unsigned long long>(total),
+                   static_cast<unsigned long long>(kNoAllocScratchBytes));
+  h.ctl = reinterpret_cast<uint32_t*>(d.ptr);
+  h.status_host = nullptr;  // no host-mapped status: timeouts stay in the status words below
+  h.status_dev = reinterpret_cast<uint32_t*>(d.ptr + 64);
+  h.base = d.ptr + kNoAllocCtl;
+  ar_launch_fill(d.ptr, 0, 1, 0, static_cast<uint32_t>(total), 0u, stream);
+  const uint32_t sw = sentinel_word(dtype);
+  for (int i : {RG_P1, RG_P2})
+    ar_launch_fill(h.base, h.stride, nranks, h.rg[i].off, h.rg[i].bytes, sw, stream);
+  AR_HIP(hipGetLastError());
+  h.epoch = 1;
+  d.nranks = nranks;
+  d.dtype = dtype;
+  return AR_OK;
+}
+
+}  // namespace
+
+extern "C" int ar_allreduce_noalloc(int nranks, ar_dtype dtype, const void* const in[],
+                                    void* const out[], size_t count, ar_algo algo,
+                                    void* stream) {
+  if (nranks < 1 || nranks > ar::kMaxRanks)
+    return ar_fail(AR_EINVAL, "nranks must be in [1, %d], got %d", ar::kMaxRanks, nranks);
+  if (dtype != AR_FLOAT32 && dtype != AR_BFLOAT16 && dtype != AR_INT32)
+    return ar_fail(AR_EINVAL, "unknown dtype %d", static_cast<int>(dtype));
+  int dev = 0;
+  AR_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kNoAllocDevices)
+    return ar_fail(AR_EINVAL, "device %d beyond the %d the library keeps state for", dev,
+                   kNoAllocDevices);
+  std::lock_guard<std::mutex> lk(g_na_mu);
+  NoAllocDevice& d = g_na[dev];
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (d.ptr == nullptr) {
+    // once per device, with that device current: the device address of this GPU's copy of the
+    // array (the array's name in host code is only a host-side stand-in)
+    void* p = nullptr;
+    AR_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    d.ptr = static_cast<uint8_t*>(p);
+  }
+  if (d.nranks != nranks || d.dtype != static_cast<int>(dtype)) {
+    const int rc = noalloc_setup(d, dev, nranks, dtype, s);
+    if (rc != AR_OK) {
+      d.nranks = 0;
+      return rc;
+    }
+  }
+  return allreduce_enqueue(&d.h, in, out, count, algo, s);
+}
