@@ -1,17 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of the barrier-free AllReduce on one MI355X with emulated ranks.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2] [--all --report out.json]
+    python bench.py [--steps K] [--warmup W] [--configs C1,C2,...] [--report out.json]
 
-Default workload: 4 emulated ranks, bf16 sum, one-shot sentinel with double buffering, messages
-of 1 KiB .. 256 KiB per rank (powers of two). A step is one AllReduce of every message size of
-the workload; K steps run back to back inside one persistent launch per size (no host work
-between iterations), each iteration on a fresh input set. Per iteration k the latency is
-max_r t_end[r][k] - max_r t_start[r][k] on the device wall clock (from the moment the last rank
-enters until the last rank has completed its last output store). The JSON line reports the p50,
-the on-chip latency floor 2 * L_L2 + L_store measured in the same run, the roofline of the
-dominant kernel (algorithmic bytes per launch / launch time from HIP events on the launch
-stream) and the single-threaded CPU oracle on a bounded sample.
+A step is one AllReduce of every message size of every configuration below (all five are
+measured in the default run); K steps run back to back inside one persistent launch per
+(configuration, algorithm, size), each iteration on a fresh input set where the sets fit in
+memory. Per iteration k the latency is max_r t_end[r][k] - max_r t_start[r][k] on the device
+wall clock (from the moment the last rank enters until the last rank has completed its last
+output store).
+
+    C1  2 ranks, fp32, 128 B, one-shot LL (also the one-shot sentinel and the two-barrier baseline)
+    C2  4 ranks, bf16, 1 KiB - 256 KiB, one-shot sentinel + double buffering   <- `value`
+    C3  8 ranks, bf16, [tokens, 8192] for tokens 1..64 (16 KiB - 1 MiB), two-shot (and one-shot)
+    C4  16 ranks, fp32, 4 KiB - 4 MiB, LL128-style atomic vs one-shot LL vs two-barrier baseline
+    C5  8 ranks, int32 and fp32, 16 - 256 MiB, two-shot (bandwidth regime: algBW = S / p50)
+
+The JSON line's `value` is the geometric mean of C2's per-size p50; `configs` holds every
+configuration's per-size p50 / p99, its latency roofline (p50 against the on-chip floor
+2 * L_L2 + L_store of the slowest XCD pair the configuration uses, plus its algorithmic bytes at
+8 TB/s) or, for C5, its HBM roofline; `roofline` is the headline kernel's. The CPU oracle is
+timed on a bounded sample of C2 (`cpu_baseline`).
 
 Only one GPU is used: ranks are emulated on it. ``--gpus`` above 1 is refused.
 """
@@ -34,21 +43,30 @@ if ROOT not in sys.path:
 METRIC = "p50 AllReduce latency µs @128B–1MB; algBW GB/s @≥16MB (1 GPU)"
 HBM_PEAK_GBPS = 8000.0
 
+# Configuration -> (workload id in inputs.WORKLOADS, algorithms measured, extra dtypes). The first
+# algorithm is the one the configuration names; the others run at the same sizes for comparison.
+CONFIGS = {
+    "C1": (1, ["oneshot_ll", "oneshot_sentinel", "barrier2"], []),
+    "C2": (2, ["oneshot_sentinel", "barrier2"], []),
+    "C3": (3, ["twoshot", "oneshot_sentinel"], []),
+    "C4": (4, ["ll128_atomic", "oneshot_ll", "barrier2"], []),
+    "C5": (5, ["twoshot"], ["f32"]),
+}
 
-def _to_device(x):
-    import torch
+# Kernel dispatches of the AllReduce kernels made so far by this process (ar_bench and every
+# ar_allreduce / collective call is one dispatch): lets a rocprofv3 trace be matched to the
+# per-size records (`dispatch` in each record is the index of its timed launch).
+_DISPATCHES = [0]
 
-    out = []
-    for r in range(x.shape[0]):
-        row = np.ascontiguousarray(x[r])
-        if row.dtype == np.uint16:
-            row = row.view(np.int16)
-        out.append(torch.from_numpy(row).cuda())
-    return out
+
+def _gm(xs):
+    xs = [x for x in xs if x and x > 0]
+    return math.exp(sum(math.log(v) for v in xs) / len(xs)) if xs else float("nan")
 
 
 def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str, iters: int,
-               warmup: int, hz: float, set_cap_bytes: int = 256 << 20, check: bool = True):
+               warmup: int, hz: float, set_cap_bytes: int = 256 << 20, check: bool = True,
+               launch_calls: int = 20):
     import torch
 
     n, dt = wl["nranks"], wl["dtype"]
@@ -88,9 +106,11 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
     warm = max(warmup, nsets)
     if warm > 0:
         A.ar_bench(h, ins, outs, nsets, count, aid, warm, timestamps=False)
+        _DISPATCHES[0] += 1
+    dispatch = _DISPATCHES[0]
     ts, te, ms = A.ar_bench_ex(h, ins, outs, nsets, count, aid, iters)
-    # launch-inclusive: host-issued ar_allreduce calls back to back, timed with events
-    calls = 50
+    _DISPATCHES[0] += 1
+    # launch-inclusive: host-issued calls back to back, timed with events
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def one_call():
@@ -102,14 +122,17 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
             A.ar_broadcast(h, ins[0], outs[:n], count, 0)
         else:
             A.ar_allreduce(h, ins[:n], outs[:n], count, aid)
+        _DISPATCHES[0] += 1
 
-    one_call()
-    ev0.record()
-    for _ in range(calls):
+    launch_us = float("nan")
+    if launch_calls > 0:
         one_call()
-    ev1.record()
-    torch.cuda.synchronize()
-    launch_us = ev0.elapsed_time(ev1) * 1e3 / calls
+        ev0.record()
+        for _ in range(launch_calls):
+            one_call()
+        ev1.record()
+        torch.cuda.synchronize()
+        launch_us = ev0.elapsed_time(ev1) * 1e3 / launch_calls
     ts = ts.reshape(iters, n).astype(np.int64)
     te = te.reshape(iters, n).astype(np.int64)
     lat_us = (te.max(axis=1) - ts.max(axis=1)) / hz * 1e6
@@ -125,11 +148,14 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
         "launch_ms": float(ms),
         "launch_inclusive_us": float(launch_us),
         "iters": iters,
+        "nsets": nsets,
+        "dispatch": dispatch,
         "alg_bytes_per_call": A.ar_alg_bytes(h, count, aid),
         "launch": A.ar_plan_info(h, count, aid),
     }
     res["algbw_GBps"] = size / (res["p50_us"] * 1e-6) / 1e9
-    res["busbw_like_GBps"] = res["alg_bytes_per_call"] * iters / (ms * 1e-3) / 1e9 if ms > 0 else 0
+    res["alg_GBps_event"] = (res["alg_bytes_per_call"] * iters / (ms * 1e-3) / 1e9
+                             if ms > 0 else 0.0)
     if check and host_sets:
         # spot check: the last set's output equals the oracle's result (the parity tests proper
         # live in tests/)
@@ -143,18 +169,18 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
                         else oracle.broadcast(rows[0], n))
             ok = all(np.array_equal(outs[k * n + r].cpu().numpy().view(np.uint8),
                                     want_all[r].view(np.uint8)) for r in range(n))
-            res["spot_check"] = bool(ok)
-            if not ok:
-                raise AssertionError(f"spot check failed: {algo} n={n} size={size}")
-            del ins, outs, big, outs_big
-            return res
-        want = oracle.allreduce(rows)[0]
-        got = outs[k * n].cpu().numpy().view(want.dtype)
-        if algo == "ll128_atomic":
-            ok = np.allclose(got.astype(np.float64), want.astype(np.float64), rtol=0,
-                             atol=float(n * 2.0 ** -23 * np.abs(x.astype(np.float64)).sum(0).max()))
         else:
-            ok = np.array_equal(got.view(np.uint8), want.view(np.uint8))
+            want = oracle.allreduce(rows)[0]
+            ok = True
+            for r in range(n):
+                got = outs[k * n + r].cpu().numpy().view(want.dtype)
+                if algo == "ll128_atomic" and dt == "f32":
+                    # per element: |gpu - oracle| <= N * 2^-23 * sum_r |x_r[i]|
+                    bound = n * 2.0 ** -23 * np.abs(x.astype(np.float64)).sum(0)
+                    ok &= bool(np.all(np.abs(got.astype(np.float64) - want.astype(np.float64))
+                                      <= bound))
+                else:
+                    ok &= bool(np.array_equal(got.view(np.uint8), want.view(np.uint8)))
         res["spot_check"] = bool(ok)
         if not ok:
             raise AssertionError(f"spot check failed: {algo} n={n} size={size}")
@@ -200,18 +226,79 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload_key: str):
-    """HBM bytes per timed launch from the committed counter summary (profiles/traffic.json),
-    or None when there is none for this workload or the kernels have changed since."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    try:
-        with open(path) as f:
-            rec = json.load(f).get(workload_key)
-    except (OSError, ValueError):
-        return None
-    if not rec or rec.get("source_sha256") != kernel_source_hash():
-        return None
-    return rec
+_TRAFFIC = {}
+
+
+def traffic_table() -> dict:
+    """Counter-measured HBM bytes per AllReduce, keyed by config:algo:dtype:n<N>:<bytes>
+    (profiles/traffic.json), or {} when the kernels have changed since they were taken."""
+    if "t" not in _TRAFFIC:
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        try:
+            with open(path) as f:
+                rec = json.load(f)
+        except (OSError, ValueError):
+            rec = {}
+        ok = rec.get("source_sha256") == kernel_source_hash()
+        _TRAFFIC["t"] = rec.get("entries", {}) if ok else {}
+    return _TRAFFIC["t"]
+
+
+def traffic_key(cfg: str, algo: str, dtype: str, n: int, size: int) -> str:
+    return f"{cfg}:{algo}:{dtype}:n{n}:{size}"
+
+
+def measured_traffic(cfg: str, algo: str, dtype: str, n: int, rows: list):
+    """HBM bytes per timed launch (mean over the rows' launches) from the per-AllReduce counter
+    record of every size, or None when any size has none."""
+    t = traffic_table()
+    per_launch = []
+    for r in rows:
+        e = t.get(traffic_key(cfg, algo, dtype, n, r["bytes"]))
+        if e is None:
+            return None
+        per_launch.append(e["hbm_bytes_per_ar"] * r["iters"])
+    return sum(per_launch) / len(per_launch)
+
+
+def latency_roofline(rows: list, floor_us: float) -> dict:
+    """Latency roofline of a small-message configuration: per size the bound is the on-chip floor
+    plus the algorithmic bytes at the nominal HBM bandwidth (the floor alone below ~4 KiB);
+    `frac` = bound / p50 (geometric mean over the sizes; 1 would be at the bound)."""
+    bounds = [floor_us + r["alg_bytes_per_call"] / (HBM_PEAK_GBPS * 1e9) * 1e6 for r in rows]
+    ratios = [r["p50_us"] / b for r, b in zip(rows, bounds)]
+    return {
+        "bound": "latency",
+        "unit": "us",
+        "achieved": _gm([r["p50_us"] for r in rows]),
+        "peak": _gm(bounds),
+        "frac": _gm([1.0 / x for x in ratios]),
+        "p50_over_bound": [round(x, 3) for x in ratios],
+        "bound_us": [round(b, 4) for b in bounds],
+        "bound_definition": ("floor_us + alg_bytes_per_call / 8 TB/s per size; floor = 2*L_L2 + "
+                             "L_store of the slowest sender->receiver XCD pair of the placement"),
+    }
+
+
+def hbm_roofline(rows: list, copy_gbps: float) -> dict:
+    """HBM roofline of the dominant kernel: algorithmic bytes per launch / launch time (HIP
+    events on the launch stream), against the nominal 8 TB/s and the streaming copy."""
+    tot_bytes = sum(r["alg_bytes_per_call"] * r["iters"] for r in rows)
+    tot_ms = sum(r["launch_ms"] for r in rows)
+    achieved = tot_bytes / (tot_ms * 1e-3) / 1e9
+    return {
+        "bound": "hbm",
+        "unit": "GB/s",
+        "achieved": achieved,
+        "peak": HBM_PEAK_GBPS,
+        "frac": achieved / HBM_PEAK_GBPS,
+        "alg_bytes_per_launch": tot_bytes / len(rows),
+        "launches": len(rows),
+        "mean_launch_ms": tot_ms / len(rows),
+        "copy_peak_GBps": copy_gbps,
+        "frac_of_copy_peak": achieved / copy_gbps,
+        "per_size_GBps": [round(r["alg_GBps_event"], 1) for r in rows],
+    }
 
 
 def cpu_baseline(I, wid: int, wl: dict, budget_s: float = 12.0) -> dict:
@@ -230,9 +317,8 @@ def cpu_baseline(I, wid: int, wl: dict, budget_s: float = 12.0) -> dict:
         reps = max(1, min(100000, int(per_budget / max(t1, 1e-7))))
         t = oracle.time_allreduce(rows, reps)
         per_size.append({"bytes": size, "reps": reps, "us_per_call": t / reps * 1e6})
-    gm = math.exp(sum(math.log(p["us_per_call"]) for p in per_size) / len(per_size))
     return {
-        "value": gm,
+        "value": _gm([p["us_per_call"] for p in per_size]),
         "unit": "us",
         "cores": 1,
         "kind": "oracle",
@@ -272,15 +358,18 @@ def cpu_baseline_threads(I, wid: int, wl: dict, threads: int, budget_s: float = 
             list(pool.map(lambda sl: oracle.time_allreduce(sl, reps), slices))
             per_size.append({"bytes": size, "reps": reps, "threads": t,
                              "us_per_call": (time.perf_counter() - t0) / reps * 1e6})
-    gm = math.exp(sum(math.log(p["us_per_call"]) for p in per_size) / len(per_size))
-    return {"value": gm, "unit": "us", "cores": threads, "per_size": per_size}
+    return {"value": _gm([p["us_per_call"] for p in per_size]), "unit": "us", "cores": threads,
+            "per_size": per_size}
 
 
 def run_workload(A, I, wid: int, algo: str | None, iters: int | None, warmup: int, hz: float,
-                 placement: int, sizes=None):
+                 placement: int, sizes=None, dtype: str | None = None, launch_calls: int = 20):
     wl = dict(I.WORKLOADS[wid])
     if sizes is not None:
         wl["sizes"] = sizes
+    if dtype is not None and dtype != wl["dtype"]:
+        wl["dtype"] = dtype
+        wl["dist"] = {"f32": "uniform", "bf16": "normal", "i32": "int20"}[dtype]
     algo = algo or wl["algo"]
     iters = iters or wl["iters"]
     # reduce-scatter inputs and all-gather outputs are N partitions per rank
@@ -290,30 +379,96 @@ def run_workload(A, I, wid: int, algo: str | None, iters: int | None, warmup: in
         A.ar_set_option(h, A.AR_OPT_PLACEMENT, placement)
         rows = []
         for si, size in enumerate(wl["sizes"]):
-            rows.append(bench_size(A, I, h, wid, wl, si, size, algo, iters, warmup, hz))
-            print(f"# workload {wid} {algo} size {size}: p50 {rows[-1]['p50_us']:.3f} us "
-                  f"p99 {rows[-1]['p99_us']:.3f} us", file=sys.stderr, flush=True)
+            rows.append(bench_size(A, I, h, wid, wl, si, size, algo, iters, warmup, hz,
+                                   launch_calls=launch_calls))
+            print(f"# workload {wid} {algo} {wl['dtype']} size {size}: p50 "
+                  f"{rows[-1]['p50_us']:.3f} us p99 {rows[-1]['p99_us']:.3f} us",
+                  file=sys.stderr, flush=True)
     finally:
         A.ar_destroy(h)
     return wl, algo, iters, rows
 
 
+def _round_rows(rows):
+    return [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+            for r in rows]
+
+
+def floors(A, placement: int) -> dict:
+    """The on-chip floor 2 * L_L2 + L_store: on the nearest XCD pair and position (ar_sol_ex),
+    and per rank count on the slowest sender -> receiver XCD pair of the placement."""
+    sol = A.ar_sol_ex(placement)
+    out = {"sol": sol, "floor_nearest_us": sol["floor_ns"] * 1e-3, "by_nranks": {}}
+    for n in (2, 4, 8, 16):
+        r = A.ar_sol_ranks(n, placement)
+        out["by_nranks"][n] = {
+            "store_half_rtt_worst_ns": r["store_half_rtt_worst_ns"],
+            "store_half_rtt_best_ns": r["store_half_rtt_best_ns"],
+            "worst_pair_xcc": [r["worst_sender_xcc"], r["worst_receiver_xcc"]],
+            "floor_us": (2 * sol["l2_load_ns"] + r["store_half_rtt_worst_ns"]) * 1e-3,
+        }
+    return out
+
+
+def run_config(A, I, cfg: str, steps, warmup: int, hz: float, placement: int, fl: dict,
+               copy_gbps: float, algos=None) -> dict:
+    wid, names, extra_dtypes = CONFIGS[cfg]
+    wl0 = I.WORKLOADS[wid]
+    n = wl0["nranks"]
+    floor = fl["by_nranks"][max(2, n)]["floor_us"] if n > 1 else fl["floor_nearest_us"]
+    rec = {"workload": wl0["name"], "nranks": n, "algos": {}, "floor_us": floor,
+           "floor_nearest_us": fl["floor_nearest_us"]}
+    for dtype in [wl0["dtype"]] + extra_dtypes:
+        for algo in (algos or names):
+            wl, algo, iters, rows = run_workload(A, I, wid, algo, steps, warmup, hz, placement,
+                                                 dtype=dtype)
+            key = algo if dtype == wl0["dtype"] else f"{algo}:{dtype}"
+            ent = {"dtype": dtype, "iters": iters, "p50_us": [round(r["p50_us"], 4) for r in rows],
+                   "p99_us": [round(r["p99_us"], 4) for r in rows],
+                   "p50_gm_us": _gm([r["p50_us"] for r in rows]),
+                   "per_size": _round_rows(rows)}
+            tr = measured_traffic(cfg, algo, dtype, n, rows)
+            if cfg == "C5":
+                rl = hbm_roofline(rows, copy_gbps)
+                rl["traffic"] = tr
+                ent["algbw_GBps"] = [round(r["algbw_GBps"], 2) for r in rows]
+            else:
+                rl = latency_roofline(rows, floor)
+                rl["traffic"] = tr
+                rl["hbm"] = hbm_roofline(rows, copy_gbps)
+                ent["p50_over_floor"] = [round(r["p50_us"] / floor, 3) for r in rows]
+                ent["p50_over_floor_nearest"] = [round(r["p50_us"] / fl["floor_nearest_us"], 3)
+                                                 for r in rows]
+            ent["roofline"] = rl
+            rec["algos"][key] = ent
+    return rec
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed iterations per size")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed iterations per size (default: each configuration's own count)")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=sorted([1, 2, 3, 4, 5, 6, 7, 8]))
+    ap.add_argument("--configs", default="C1,C2,C3,C4,C5",
+                    help="comma-separated configurations to measure beside the headline C2")
+    ap.add_argument("--workload", type=int, default=None, choices=sorted(range(1, 9)),
+                    help="measure this workload alone (with --algo) instead of the configurations")
     ap.add_argument("--algo", default=None)
     ap.add_argument("--placement", type=int, default=0, help="0 XCD per rank, 1 same XCD")
-    ap.add_argument("--all", action="store_true", help="also run every workload; see --report")
+    ap.add_argument("--all", action="store_true", help="also run the standalone collectives")
     ap.add_argument("--auto-sweep", action="store_true",
-                    help="only measure the one-shot / two-shot crossovers behind AR_ALGO_AUTO")
-    ap.add_argument("--report", default=None, help="write the full per-size report here")
+                    help="only measure the crossovers behind AR_ALGO_AUTO (every dtype)")
+    ap.add_argument("--scratch-sweep", action="store_true",
+                    help="only measure latency versus scratch size (AR_SCRATCH_* caps)")
+    ap.add_argument("--sweep-caps", default=None,
+                    help="with --scratch-sweep: comma-separated caps in MiB")
+    ap.add_argument("--sweep-only", default=None,
+                    help="with --scratch-sweep: AR_SCRATCH_ONESHOT or AR_SCRATCH_TWOSHOT only")
+    ap.add_argument("--report", default=None, help="write the full report (JSON) here")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-barrier-baseline", action="store_true")
     ap.add_argument("--sizes", default=None,
-                    help="comma-separated message sizes in bytes (default: the workload's)")
+                    help="comma-separated message sizes in bytes (with --workload)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run the streaming copy kernel over MIB MiB (5 times) and exit; "
                          "its known byte count scales rocprof FETCH_SIZE / WRITE_SIZE")
@@ -355,39 +510,43 @@ def main() -> int:
         rows = auto_sweep(A, I, hz, args.warmup, args.placement)
         print(json.dumps({"auto_sweep": rows}), flush=True)
         return 0
-    sol = A.ar_sol_ex(args.placement)
-    print(f"# sol {json.dumps(sol)}", file=sys.stderr, flush=True)
+    if args.scratch_sweep:
+        caps = ([int(float(x) * (1 << 20)) for x in args.sweep_caps.split(",")]
+                if args.sweep_caps else None)
+        rows = scratch_sweep(A, I, hz, args.warmup, args.placement, caps=caps,
+                             only=args.sweep_only)
+        print(json.dumps({"scratch_sweep": rows}), flush=True)
+        return 0
+    fl = floors(A, args.placement)
+    print(f"# floors {json.dumps(fl)}", file=sys.stderr, flush=True)
     peak = copy_peak(A)
     print(f"# streaming copy {peak['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
 
-    wid = args.workload
-    sizes = [int(x) for x in args.sizes.split(",")] if args.sizes else None
-    wl, algo, iters, rows = run_workload(A, I, wid, args.algo, args.steps, args.warmup, hz,
-                                         args.placement, sizes)
-    p50s = [r["p50_us"] for r in rows]
-    value = math.exp(sum(math.log(v) for v in p50s) / len(p50s))
-    barrier = None
-    if algo != "barrier2" and algo not in I.COLLECTIVES and not args.no_barrier_baseline:
-        # the two-barrier baseline at the same sizes, same inputs, same run
-        _, _, _, brows = run_workload(A, I, wid, "barrier2", args.steps, args.warmup, hz,
-                                      args.placement, sizes)
-        bp50 = [r["p50_us"] for r in brows]
-        barrier = {
-            "algo": "barrier2",
-            "value": math.exp(sum(math.log(v) for v in bp50) / len(bp50)),
-            "unit": "us",
-            "p50_us": [round(v, 4) for v in bp50],
-            "p99_us": [round(r["p99_us"], 4) for r in brows],
-        }
-    total_launch_ms = sum(r["launch_ms"] for r in rows)
-    floor_us = sol["floor_ns"] * 1e-3
-    # Dominant kernel: the one this workload runs; roofline over all its timed launches.
-    tot_bytes = sum(r["alg_bytes_per_call"] * r["iters"] for r in rows)
-    achieved = tot_bytes / (total_launch_ms * 1e-3) / 1e9
-    launches = len(rows)
-    tkey = f"workload{wid}:{algo}:{wl['dtype']}:" + ",".join(str(x) for x in wl["sizes"]) + \
-        f":steps{iters}"
-    traffic_rec = measured_traffic(tkey)
+    if args.workload is not None:
+        sizes = [int(x) for x in args.sizes.split(",")] if args.sizes else None
+        wl, algo, iters, rows = run_workload(A, I, args.workload, args.algo, args.steps,
+                                             args.warmup, hz, args.placement, sizes)
+        print(json.dumps({"workload": args.workload, "algo": algo, "dtype": wl["dtype"],
+                          "per_size": _round_rows(rows)}), flush=True)
+        return 0
+
+    # the headline: C2, then every other configuration
+    wanted = [c for c in args.configs.split(",") if c]
+    configs = {"C2": run_config(A, I, "C2", args.steps, args.warmup, hz, args.placement, fl,
+                                peak["GBps"])}
+    for cfg in wanted:
+        if cfg != "C2":
+            configs[cfg] = run_config(A, I, cfg, args.steps, args.warmup, hz, args.placement, fl,
+                                      peak["GBps"])
+    head = configs["C2"]["algos"]["oneshot_sentinel"]
+    rows = head["per_size"]
+    wl = I.WORKLOADS[2]
+    iters = head["iters"]
+    value = head["p50_gm_us"]
+    # one step = one AllReduce of every size of every configuration measured
+    total_ms = sum(r["launch_ms"] for c in configs.values() for e in c["algos"].values()
+                   for r in e["per_size"])
+    roof = dict(head["roofline"])
     line = {
         "metric": METRIC,
         "value": value,
@@ -395,7 +554,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": iters,
         "warmup": args.warmup,
-        "ms_per_step": total_launch_ms / iters,
+        "ms_per_step": total_ms / iters,
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -403,57 +562,47 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": (f"{wl['nranks']} emulated ranks on one MI355X, {wl['dtype']} sum "
-                         f"(fp32 accumulation), {algo}, {min(wl['sizes'])}-{max(wl['sizes'])} "
-                         f"bytes per rank (powers of two), {iters} back-to-back iterations per "
-                         "size, fresh inputs per iteration"),
+                         f"(fp32 accumulation), oneshot_sentinel with double buffering, "
+                         f"{min(wl['sizes'])}-{max(wl['sizes'])} bytes per rank (powers of two), "
+                         f"{iters} back-to-back iterations per size, fresh inputs per iteration"),
             "nranks": wl["nranks"],
-            "algo": algo,
+            "algo": "oneshot_sentinel",
             "placement": ["rank per XCD", "all ranks on one XCD"][args.placement],
             "sizes_bytes": wl["sizes"],
         },
-        "value_definition": ("geometric mean over the message sizes of the per-size p50 "
+        "value_definition": ("geometric mean over C2's message sizes of the per-size p50 "
                              "latency (device wall clock, last rank in to last rank out)"),
-        "per_size": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
-                     for r in rows],
         "latency_floor": {
-            "floor_us": floor_us,
-            "formula": "2*L_L2 + L_store (dependent-load L2 latency; store->poll half RTT)",
-            "l2_load_ns": sol["l2_load_ns"],
-            "store_half_rtt_ns": sol["store_half_rtt_ns"],
-            "fence_ns": sol["fence_ns"],
-            "p50_smallest_over_floor": p50s[0] / floor_us,
+            "floor_us": configs["C2"]["floor_us"],
+            "floor_nearest_us": fl["floor_nearest_us"],
+            "formula": ("2*L_L2 + L_store (dependent-load L2 latency; store->poll half round "
+                        "trip); floor_us on the slowest XCD pair of the 4-rank placement, "
+                        "floor_nearest_us on XCDs 0-1 at their nearest memory position"),
+            "l2_load_ns": fl["sol"]["l2_load_ns"],
+            "store_half_rtt_ns": fl["sol"]["store_half_rtt_ns"],
+            "fence_ns": fl["sol"]["fence_ns"],
+            "by_nranks": fl["by_nranks"],
+            "p50_smallest_over_floor": head["p50_us"][0] / configs["C2"]["floor_us"],
+            "p50_smallest_over_floor_nearest": head["p50_us"][0] / fl["floor_nearest_us"],
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": (traffic_rec["hbm_bytes_per_launch"] if traffic_rec else None),
-            "alg_bytes_per_launch": tot_bytes / launches,
-            "launches": launches,
-            "mean_launch_ms": total_launch_ms / launches,
-            "kernel": f"ar_kernel<{algo}, {wl['dtype']}, N={wl['nranks']}>",
-            "bytes_definition": ("ar_alg_bytes() per AllReduce x iterations per launch; achieved = "
-                                 "bytes over all timed launches / their summed event time"),
-            "traffic_definition": ("rocprofv3 FETCH_SIZE + WRITE_SIZE per timed launch, each "
-                                   "scaled by the streaming copy's counter-to-bytes factor "
-                                   "(profiles/traffic.json); null when the kernel sources "
-                                   "differ from those the counters were taken on"),
-            "copy_peak_GBps": peak["GBps"],
-            "frac_of_copy_peak": achieved / peak["GBps"],
+        "roofline": roof,
+        "barrier_baseline": {
+            "algo": "barrier2",
+            "value": configs["C2"]["algos"]["barrier2"]["p50_gm_us"],
+            "unit": "us",
+            "p50_us": configs["C2"]["algos"]["barrier2"]["p50_us"],
         },
+        "configs": {c: _summary(rec) for c, rec in configs.items()},
+        "copy_peak_GBps": peak["GBps"],
     }
-    if barrier is not None:
-        line["barrier_baseline"] = barrier
-    if not args.no_cpu_baseline and algo not in I.COLLECTIVES:
-        line["cpu_baseline"] = cpu_baseline(I, wid, wl)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(I, 2, wl)
         # the machine's CPU share is 16 cores whatever os.cpu_count() reports
         line["cpu_baseline"]["multi_thread"] = cpu_baseline_threads(
-            I, wid, wl, max(1, min(16, os.cpu_count() or 1)))
-    report = {"main": line, "sol": sol}
+            I, 2, wl, max(1, min(16, os.cpu_count() or 1)))
+    report = {"main": line, "configs": configs, "floors": fl}
     if args.all:
-        report["workloads"] = run_all(A, I, hz, args.warmup, args.placement)
+        report["collectives"] = run_collectives(A, I, hz, args.warmup, args.placement)
     if args.report:
         with open(args.report, "w") as f:
             json.dump(report, f, indent=1)
@@ -461,56 +610,109 @@ def main() -> int:
     return 0
 
 
-def auto_sweep(A, I, hz, warmup, placement, iters=100):
-    """p50 of the one-shot LL, one-shot sentinel and two-shot kernels for N in {2,3,4,8,16} and
-    per-rank sizes 128 B .. 2 MiB (fp32, uniform inputs): the measurements behind the automatic
-    algorithm choice (ar_allreduce with AR_ALGO_AUTO)."""
-    sizes = [128 << (2 * k) for k in range(7)] + [2 << 20]
-    out = []
-    for n in (2, 3, 4, 8, 16):
-        wl = dict(nranks=n, dtype="f32", dist="uniform", sigma=1.0, sizes=sizes)
-        h = A.ar_create(n, max(sizes), A.AR_FLOAT32)
-        try:
-            A.ar_set_option(h, A.AR_OPT_PLACEMENT, placement)
-            for si, size in enumerate(sizes):
-                row = {"nranks": n, "bytes": size}
-                for algo in ("oneshot_ll", "oneshot_sentinel", "twoshot"):
-                    r = bench_size(A, I, h, 6, wl, si, size, algo, iters, warmup, hz)
-                    row[algo] = round(r["p50_us"], 3)
-                best = min(("oneshot_ll", "oneshot_sentinel", "twoshot"), key=lambda a: row[a])
-                row["best"] = best
-                print(f"# sweep {json.dumps(row)}", file=sys.stderr, flush=True)
-                out.append(row)
-        finally:
-            A.ar_destroy(h)
+def _summary(rec: dict) -> dict:
+    """A configuration's record for the JSON line: per algorithm the per-size p50 / p99, the
+    roofline and (latency configurations) p50 over the floor; the full per-size records go to
+    --report."""
+    out = {"workload": rec["workload"], "nranks": rec["nranks"], "floor_us": rec["floor_us"],
+           "floor_nearest_us": rec["floor_nearest_us"], "algos": {}}
+    for k, e in rec["algos"].items():
+        s = {kk: e[kk] for kk in ("dtype", "iters", "p50_us", "p99_us", "p50_gm_us",
+                                  "p50_over_floor", "algbw_GBps") if kk in e}
+        s["sizes_bytes"] = [r["bytes"] for r in e["per_size"]]
+        s["kernels"] = sorted({r["launch"]["kernel"] for r in e["per_size"]})
+        rl = dict(e["roofline"])
+        rl.pop("bound_us", None)
+        s["roofline"] = rl
+        out["algos"][k] = s
     return out
 
 
-def run_all(A, I, hz, warmup, placement):
-    out = {}
-    plan = [
-        (1, ["oneshot_ll", "oneshot_sentinel", "barrier2"]),
-        (2, ["oneshot_sentinel", "oneshot_ll", "twoshot", "barrier2"]),
-        (3, ["twoshot", "oneshot_sentinel", "barrier2"]),
-        (4, ["ll128_atomic", "oneshot_ll", "oneshot_sentinel", "twoshot", "barrier2"]),
-        (5, ["twoshot"]),
-        (6, ["reducescatter"]),
-        (7, ["allgather"]),
-        (8, ["broadcast"]),
-    ]
-    for wid, algos in plan:
-        for algo in algos:
-            wl, algo, iters, rows = run_workload(A, I, wid, algo, None, warmup, hz, placement)
-            out[f"{wid}:{algo}:{wl['dtype']}"] = rows
-        if wid == 5:
-            wl = dict(I.WORKLOADS[5], dtype="f32", dist="uniform")
-            h = A.ar_create(8, max(wl["sizes"]), A.AR_FLOAT32)
+def auto_sweep(A, I, hz, warmup, placement, iters=100):
+    """p50 of the candidate kernels for N in {2,3,4,8,16} and per-rank sizes 128 B .. 2 MiB, for
+    every dtype: the measurements behind the automatic algorithm choice (AR_ALGO_AUTO). The
+    LL128-style kernel is a candidate for fp32 and int32."""
+    sizes = [128 << (2 * k) for k in range(7)] + [2 << 20]
+    dists = {"f32": "uniform", "bf16": "normal", "i32": "int20"}
+    out = []
+    for dtype in ("f32", "bf16", "i32"):
+        algos = ["oneshot_ll", "oneshot_sentinel", "twoshot"]
+        if dtype != "bf16":
+            algos.append("ll128_atomic")
+        for n in (2, 3, 4, 8, 16):
+            wl = dict(nranks=n, dtype=dtype, dist=dists[dtype], sigma=1.0, sizes=sizes)
+            h = A.ar_create(n, max(sizes), A.DTYPES[dtype])
             try:
-                rows = [bench_size(A, I, h, 5, wl, si, s, "twoshot", wl["iters"], warmup, hz)
-                        for si, s in enumerate(wl["sizes"])]
+                A.ar_set_option(h, A.AR_OPT_PLACEMENT, placement)
+                for si, size in enumerate(sizes):
+                    row = {"dtype": dtype, "nranks": n, "bytes": size}
+                    for algo in algos:
+                        r = bench_size(A, I, h, 6, wl, si, size, algo, iters, warmup, hz,
+                                       launch_calls=0)
+                        row[algo] = round(r["p50_us"], 3)
+                    row["best"] = min(algos, key=lambda a: row[a])
+                    print(f"# sweep {json.dumps(row)}", file=sys.stderr, flush=True)
+                    out.append(row)
             finally:
                 A.ar_destroy(h)
-            out["5:twoshot:f32"] = rows
+    return out
+
+
+def scratch_sweep(A, I, hz, warmup, placement, iters=50, caps=None, only=None):
+    """Latency (p50) and algBW versus the scratch caps (AR_SCRATCH_ONESHOT / AR_SCRATCH_TWOSHOT,
+    bytes per rank per protocol): the MI355X counterpart of the pages' scratch-size sweep. Each
+    cap is applied to the protocol it governs; messages larger than a slot run in chunks."""
+    caps = caps or [1 << 20, 4 << 20, 16 << 20, 64 << 20, 256 << 20]
+    plan = [
+        # (cap variable, workload, algo, dtype, sizes)
+        ("AR_SCRATCH_ONESHOT", 2, "oneshot_sentinel", "bf16", [1 << 14, 1 << 17, 1 << 18]),
+        ("AR_SCRATCH_ONESHOT", 4, "oneshot_sentinel", "f32", [1 << 15, 1 << 18, 1 << 20]),
+        ("AR_SCRATCH_TWOSHOT", 3, "twoshot", "bf16", [1 << 17, 1 << 20]),
+        ("AR_SCRATCH_TWOSHOT", 4, "ll128_atomic", "f32", [1 << 18, 1 << 22]),
+        ("AR_SCRATCH_TWOSHOT", 4, "twoshot", "f32", [1 << 20, 1 << 22]),
+        ("AR_SCRATCH_TWOSHOT", 5, "twoshot", "i32", [16 << 20, 64 << 20, 256 << 20]),
+        ("AR_SCRATCH_TWOSHOT", 5, "twoshot", "f32", [16 << 20, 256 << 20]),
+    ]
+    if only:
+        plan = [p for p in plan if p[0] == only]
+    out = []
+    saved = {k: os.environ.get(k) for k in ("AR_SCRATCH_ONESHOT", "AR_SCRATCH_TWOSHOT")}
+    try:
+        for var, wid, algo, dtype, sizes in plan:
+            for cap in caps:
+                os.environ[var] = str(cap)
+                wl = dict(I.WORKLOADS[wid], dtype=dtype, sizes=sizes,
+                          dist={"f32": "uniform", "bf16": "normal", "i32": "int20"}[dtype])
+                it = 20 if wid == 5 else iters
+                h = A.ar_create(wl["nranks"], max(sizes), A.DTYPES[dtype])
+                try:
+                    A.ar_set_option(h, A.AR_OPT_PLACEMENT, placement)
+                    for si, size in enumerate(sizes):
+                        r = bench_size(A, I, h, wid, wl, si, size, algo, it, warmup, hz,
+                                       launch_calls=0, check=False)
+                        row = {"cap_var": var, "cap_bytes": cap, "workload": wid, "algo": algo,
+                               "dtype": dtype, "nranks": wl["nranks"], "bytes": size,
+                               "chunks": r["launch"]["chunks"], "p50_us": round(r["p50_us"], 3),
+                               "algbw_GBps": round(r["algbw_GBps"], 2),
+                               "alg_GBps_event": round(r["alg_GBps_event"], 1)}
+                        print(f"# scratch {json.dumps(row)}", file=sys.stderr, flush=True)
+                        out.append(row)
+                finally:
+                    A.ar_destroy(h)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return out
+
+
+def run_collectives(A, I, hz, warmup, placement):
+    out = {}
+    for wid in (6, 7, 8):
+        wl, algo, iters, rows = run_workload(A, I, wid, None, None, warmup, hz, placement)
+        out[f"{wid}:{algo}:{wl['dtype']}"] = _round_rows(rows)
     # barrier latency versus N (one cross-rank barrier per iteration)
     bar = []
     for n in (2, 4, 8, 16):

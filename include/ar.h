@@ -95,9 +95,10 @@ typedef struct ar_handle ar_handle;
  * with zeros, sentinel slots with the dtype's sentinel (fp32 0xFFFFFFFF, bf16 0xFFFF: negative
  * quiet NaNs, compared bitwise; int32 INT32_MIN). The sequence number starts at 1. Scratch
  * per rank per protocol is capped by the environment variables AR_SCRATCH_ONESHOT (default
- * 4 MiB) and AR_SCRATCH_TWOSHOT (default 64 MiB; also the LL128 cap), the sizes the Pith
- * review of the paper lists as the outcome of its scratch-size sweep ("Assumptions & free
- * parameters"; Fig. 12); larger messages are sent in equal chunks.
+ * 4 MiB) and AR_SCRATCH_TWOSHOT (default 16 MiB; also the LL128 cap): the outcome of a
+ * scratch-size sweep on MI355X, the counterpart of the pages' Fig. 12 (the Pith review lists
+ * 4 MiB / 64 MiB for their hardware, "Assumptions & free parameters"); larger messages are sent
+ * in equal chunks.
  * AR_POLL_TIMEOUT_US sets the initial poll timeout (default 2000000).
  * Synchronous on the current device. Returns NULL on error (see ar_last_error()).
  *

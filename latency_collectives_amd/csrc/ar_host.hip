@@ -44,11 +44,17 @@ enum RegionId {
   RG_PF1, RG_PF2, RG_FLG,  // bulk two-shot data slots and completion flags
   RG_REC,                  // launch record (AR_OPT_RECORD_LAUNCH), written in rank 0's block only
 };
-// Default scratch per rank per protocol: the sizes the pages settle on after their scratch-size
-// sweep (Pith review, "Assumptions & free parameters": 4 MiB for the one-shot, 64 MiB for the
-// two-shot and LL128; Fig. 12 caption). Larger messages run in equal chunks.
+// Default scratch per rank per protocol, from a scratch-size sweep on MI355X (the counterpart of
+// the pages' Fig. 12; the Pith review's "Assumptions & free parameters" give 4 MiB for the
+// one-shot and 64 MiB for the two-shot and LL128 on their hardware). One-shot: 4 MiB, as on the
+// pages (1-256 MiB measured within noise below 1 MiB per rank; 1 MiB at 16 ranks 11 % faster in
+// chunks than whole). Two-shot and LL128: 16 MiB, one 1 MiB slot per (buffer, source) at 8
+// ranks, so that one step's scratch (about 128 MiB over all ranks) stays in the 256 MB MALL:
+// 256 MiB x 8 ranks in 1.90 ms against 2.20 ms at 64 MiB and 2.28 ms at 256 MiB; 6-48 MiB
+// were measured, 16 MiB was the fastest at 16, 64 and 256 MiB per rank. Larger messages run in
+// equal chunks.
 constexpr uint64_t kDefaultCapOneShot = 4ull << 20;
-constexpr uint64_t kDefaultCapTwoShot = 64ull << 20;
+constexpr uint64_t kDefaultCapTwoShot = 16ull << 20;
 constexpr uint64_t kMaxCap = 1ull << 30;  // keeps every region below the drop offset (2 GiB)
 constexpr int kXcds = 8;
 
