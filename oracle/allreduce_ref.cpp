@@ -34,6 +34,20 @@
 // With these readings, an all-gather of a reduce-scatter is exactly the AllReduce above (the
 // decomposition the paper cites), which is how the tests pin them.
 //
+// The deterministic variant of the LL128-style atomic AllReduce. The Pith review of the paper
+// notes that the atomic algorithm's floating-point sum is not reproducible and imagines a
+// deterministic variant "using per-chunk grouping or hierarchical accumulation" ("If this is
+// right", third item). The pages give no order for it; the reading used here is hierarchical
+// accumulation in a fixed order: the ranks form groups of `group` consecutive ranks
+// (0..group-1, group..2*group-1, ...; the last group may be shorter); each group's values are
+// added in rank order into a group sum, and the group sums are added in group order:
+//
+//     g_j[i] = x_{j*group}[i] + x_{j*group+1}[i] + ... (left fold over the group's ranks)
+//     out[r][i] = g_0[i] + g_1[i] + ... + g_{G-1}[i]      (left fold over the groups)
+//
+// in binary32 (bf16: widened inputs, binary32 group sums and fold, one rounding at the end).
+// group == 1 and group >= N are both the plain left fold above.
+//
 // Every function returns 0 on success and -1 on a bad argument (nranks outside [1, 64], a
 // null pointer table or a null rank pointer while count > 0). count == 0 is a no-op.
 // Output buffers may alias the matching input buffer (in-place); the fold for element i reads
@@ -123,6 +137,32 @@ int fold_scatter(int nranks, const T* const* in, T* const* out, size_t recvcount
   return 0;
 }
 
+// The grouped fold described at the top (groups of `group` consecutive ranks).
+template <typename T, typename Load, typename Store>
+int fold_grouped(int nranks, int group, const T* const* in, T* const* out, size_t count,
+                 Load load, Store store) {
+  if (count == 0) return 0;
+  if (bad_args(nranks, in, out) || group < 1) return -1;
+  for (int r = 0; r < nranks; ++r) {
+    if (in[r] == nullptr || out[r] == nullptr) return -1;
+  }
+  for (size_t i = 0; i < count; ++i) {
+    float total = 0.0f;
+    for (int first = 0; first < nranks; first += group) {
+      const int last = first + group < nranks ? first + group : nranks;
+      float g = load(in[first][i]);
+      for (int q = first + 1; q < last; ++q) {
+        g = g + load(in[q][i]);
+      }
+      total = first == 0 ? g : total + g;
+    }
+    for (int r = 0; r < nranks; ++r) {
+      out[r][i] = store(total);
+    }
+  }
+  return 0;
+}
+
 uint32_t i32_bits(int32_t v) { return static_cast<uint32_t>(v); }
 int32_t bits_i32(uint32_t a) {
   int32_t s;
@@ -158,6 +198,17 @@ int oracle_allreduce_i32(int nranks, const int32_t* const* in, int32_t* const* o
         std::memcpy(&s, &a, sizeof s);
         return s;
       });
+}
+
+int oracle_allreduce_grouped_f32(int nranks, int group, const float* const* in,
+                                 float* const* out, size_t count) {
+  return fold_grouped<float>(
+      nranks, group, in, out, count, [](float v) { return v; }, [](float a) { return a; });
+}
+
+int oracle_allreduce_grouped_bf16(int nranks, int group, const uint16_t* const* in,
+                                  uint16_t* const* out, size_t count) {
+  return fold_grouped<uint16_t>(nranks, group, in, out, count, widen_bf16, narrow_to_bf16);
 }
 
 int oracle_reducescatter_f32(int nranks, const float* const* in, float* const* out,

@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [ctypes.c_int, pp, pp, ctypes.c_size_t]
             fn.restype = ctypes.c_int
+        for name in ("oracle_allreduce_grouped_f32", "oracle_allreduce_grouped_bf16"):
+            fn = getattr(L, name)
+            fn.argtypes = [ctypes.c_int, ctypes.c_int, pp, pp, ctypes.c_size_t]
+            fn.restype = ctypes.c_int
         L.oracle_broadcast.argtypes = [ctypes.c_int, ctypes.c_void_p, pp, ctypes.c_size_t]
         L.oracle_broadcast.restype = ctypes.c_int
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -107,6 +111,28 @@ def allreduce(arrays, out=None):
     _check(out)
     fn = getattr(lib(), _FN[dt])
     rc = fn(len(arrays), _ptr_table(arrays), _ptr_table(out), n)
+    if rc != 0:
+        raise ValueError(f"oracle rejected arguments (rc={rc})")
+    return out
+
+
+_GROUPED_FN = {
+    np.dtype(np.float32): "oracle_allreduce_grouped_f32",
+    np.dtype(np.uint16): "oracle_allreduce_grouped_bf16",
+}
+
+
+def allreduce_grouped(arrays, group: int):
+    """AllReduce-sum in the hierarchical order of the deterministic atomic variant: groups of
+    ``group`` consecutive ranks are folded in rank order, then the group sums in group order
+    (binary32; bfloat16 rounded once). fp32 and bf16 only (an int32 sum does not depend on the
+    order). Returns one output array per rank."""
+    dt, n = _check(arrays)
+    if dt not in _GROUPED_FN:
+        raise TypeError(f"no grouped fold for {dt}")
+    out = [np.empty(n, dtype=dt) for _ in arrays]
+    rc = getattr(lib(), _GROUPED_FN[dt])(len(arrays), int(group), _ptr_table(arrays),
+                                         _ptr_table(out), n)
     if rc != 0:
         raise ValueError(f"oracle rejected arguments (rc={rc})")
     return out

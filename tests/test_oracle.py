@@ -291,6 +291,80 @@ def test_bf16_allreduce_vs_float64_then_round(oracle_mod):
     assert np.all(np.abs(got - exact) <= ulp)
 
 
+# ---------------------------------------------------------------- grouped (deterministic atomic) fold
+
+def test_golden_grouped_fold(oracle_mod):
+    """Hand-worked cases of the hierarchical order (groups of G consecutive ranks in rank order,
+    then the group sums in group order): the same inputs give different binary32 results for
+    G = 1, 2, 3, so a wrong group boundary, a dropped short last group or a plain left fold
+    fails one of them."""
+    for ln in _lines("grouped_fold.txt"):
+        dt, grp, lhs, rhs = [p.strip() for p in ln.split(";")[:4]]
+        if dt == "f32":
+            vals = [float(v) for v in lhs.split()]
+            ranks = [np.array([v], dtype=np.float32) for v in vals]
+            assert all(float(r[0]) == v for r, v in zip(ranks, vals))  # exact inputs
+            out = oracle_mod.allreduce_grouped(ranks, int(grp))
+            for o in out:
+                assert float(o[0]) == float(rhs), ln
+        else:
+            ranks = [np.array([int(v, 16)], dtype=np.uint16) for v in lhs.split()]
+            out = oracle_mod.allreduce_grouped(ranks, int(grp))
+            for o in out:
+                assert int(o[0]) == int(rhs, 16), ln
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 16])
+def test_grouped_fold_special_cases_are_the_left_fold(oracle_mod, n):
+    """G = 1 and G >= N reduce to the plain left fold (pinned above), for fp32 and bf16."""
+    import torch
+
+    g = np.random.default_rng(40 + n)
+    x = [g.standard_normal(777).astype(np.float32) * np.float32(10.0 ** g.integers(-2, 3))
+         for _ in range(n)]
+    want = oracle_mod.allreduce(x)[0]
+    for grp in (1, n, n + 3):
+        got = oracle_mod.allreduce_grouped(x, grp)[0]
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), grp
+    xb = [torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+          for a in x]
+    wantb = oracle_mod.allreduce(xb)[0]
+    for grp in (1, n):
+        assert np.array_equal(oracle_mod.allreduce_grouped(xb, grp)[0], wantb), grp
+
+
+@pytest.mark.parametrize("n,grp", [(4, 2), (8, 3), (16, 4), (16, 5)])
+def test_grouped_fold_closed_forms_and_exactness(oracle_mod, n, grp):
+    """Rank r filled with r sums to N(N-1)/2 in any order; dyadic inputs k * 2^-10 have exact
+    partial sums, so the grouped fold equals the integer sum; every rank's output is the same."""
+    x = [np.full(100, r, dtype=np.float32) for r in range(n)]
+    out = oracle_mod.allreduce_grouped(x, grp)
+    for o in out:
+        assert np.all(o == n * (n - 1) / 2)
+    g = np.random.default_rng(50 + n + grp)
+    k = g.integers(-(1 << 10), 1 << 10, size=(n, 2048), endpoint=True)
+    xd = [(k[r] / 1024.0).astype(np.float32) for r in range(n)]
+    got = oracle_mod.allreduce_grouped(xd, grp)[0]
+    assert np.array_equal(got.astype(np.float64), k.sum(axis=0) / 1024.0)
+
+
+@pytest.mark.parametrize("n,grp", [(8, 4), (16, 4), (16, 2)])
+def test_grouped_fold_within_its_summation_bound(oracle_mod, n, grp):
+    """Error against math.fsum within the recursive-summation bound of the grouped order: a term
+    passes through at most (G - 1) group additions and (ceil(N / G) - 1) group-sum additions,
+    each with unit roundoff u = 2^-24."""
+    g = np.random.default_rng(60 + n + grp)
+    count = 2000
+    x = [g.uniform(-1, 1, count).astype(np.float32) for _ in range(n)]
+    out = oracle_mod.allreduce_grouped(x, grp)[0].astype(np.float64)
+    steps = (grp - 1) + (-(-n // grp) - 1)
+    u = 2.0 ** -24
+    for i in range(count):
+        col = [float(x[r][i]) for r in range(n)]
+        bound = steps * u * sum(abs(v) for v in col) / (1 - steps * u)
+        assert abs(out[i] - math.fsum(col)) <= bound
+
+
 # ---------------------------------------------------------------- standalone collectives
 #
 # Reduce-scatter, all-gather and broadcast have no printed worked example on the pages; they are
