@@ -43,15 +43,25 @@ typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_INT32 = 2 } ar_dtype;
  *                       bandwidth kernel, whose per-wave completion flags ignore the data.
  *   AR_LL128_ATOMIC     reduce-scatter by atomic adds into the owner's shared destination, then
  *                       the two-shot all-gather (for int32 with completion flags, as above).
- *                       fp32 and int32 only. The fp32 summation order is not deterministic.
+ *                       bf16 adds two elements per atomic and rounds to bf16 at every addition.
+ *                       The fp32 and bf16 summation order is not deterministic: per element
+ *                       |result - rank-order fold| <= N * 2^-23 * sum_r |x_r| (fp32),
+ *                       <= N * 2^-8 * sum_r |x_r| (bf16).
+ *   AR_LL128_DET        the deterministic variant (the Pith review's "per-chunk grouping or
+ *                       hierarchical accumulation"): ranks form groups of AR_OPT_GROUP
+ *                       consecutive ranks; each group's values are added into the owner's
+ *                       group destination in rank order (ticket-ordered atomics), and the owner
+ *                       adds the group sums in group order; binary32 throughout (bf16 inputs
+ *                       widened, rounded once). Bit-reproducible; fp32 and bf16 (int32 runs
+ *                       AR_LL128_ATOMIC, whose integer sum does not depend on the order).
  *   AR_BARRIER2         one-shot push between two cross-rank flag barriers: the conventional
  *                       design whose barrier cost the pages measure (§III.B). A baseline.
  *   AR_BARRIER_ONLY     (ar_bench only) one cross-rank barrier per iteration, no data: the
  *                       barrier latency versus N (§III.B, Fig. 3).
  *   AR_ALGO_AUTO        picks one-shot LL, one-shot sentinel or two-shot from the rank count and
  *                       the message size, by a table of the fastest measured on MI355X.
- * Every algorithm except AR_LL128_ATOMIC adds in rank order 0..N-1 (fp32 accumulation for
- * bf16, rounded once to nearest even; wrapping int32) and is bit-reproducible.
+ * Every algorithm except AR_LL128_ATOMIC and AR_LL128_DET adds in rank order 0..N-1 (fp32
+ * accumulation for bf16, rounded once to nearest even; wrapping int32) and is bit-reproducible.
  * Double buffering (§IV "Bidirectional Communication Double Buffering", Fig. 4) is used by
  * every algorithm except AR_BARRIER2: step s uses scratch buffer s & 1.
  */
@@ -63,12 +73,13 @@ typedef enum {
   AR_LL128_ATOMIC = 4,
   AR_BARRIER2 = 5,
   AR_BARRIER_ONLY = 6,
-  /* values 7..11 and 15..20 are internal kernel families (see ar_plan_info); the standalone
+  /* values 7..11, 15..20 and 22..25 are internal kernel families (see ar_plan_info); the standalone
      collectives below are called through their own entry points and named by these ids in
      ar_bench, ar_alg_bytes and ar_plan_info */
   AR_REDUCESCATTER = 12,
   AR_ALLGATHER = 13,
-  AR_BROADCAST = 14
+  AR_BROADCAST = 14,
+  AR_LL128_DET = 21
 } ar_algo;
 
 enum {
@@ -129,7 +140,7 @@ int ar_allreduce(ar_handle* h, const void* const in[], void* const out[], size_t
  * ar_allreduce_noalloc: ar_allreduce for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation. It makes no
  * allocation of any kind; there is no handle. The symmetric scratch is a static device array
- * of 32 MiB that the library holds on every GPU it runs on until the process ends (scratch per
+ * of 40 MiB that the library holds on every GPU it runs on until the process ends (scratch per
  * rank per protocol 256 KiB, so larger messages run in more chunks than through a handle).
  *   nranks, dtype          : as for ar_create (1..16; AR_FLOAT32, AR_BFLOAT16, AR_INT32).
  *   in, out, count, algo   : as for ar_allreduce (count * sizeof(dtype) < 2^31 bytes per rank,
@@ -259,6 +270,8 @@ double ar_wallclock_hz(void);
  *   AR_OPT_RECORD_LAUNCH 1: every launch writes, per workgroup, its XCC id and the rank and
  *                        workgroup index it decoded into region 13 of rank 0 (ar_read_region)
  *                        [0]
+ *   AR_OPT_GROUP         AR_LL128_DET: ranks per group, 2..16; the result depends on it (it is
+ *                        the summation order) [4]
  */
 typedef enum {
   AR_OPT_TIMEOUT_US = 0,
@@ -270,7 +283,8 @@ typedef enum {
   AR_OPT_NARROW = 6,
   AR_OPT_ROOT = 7,
   AR_OPT_CHECK_INPUTS = 8,
-  AR_OPT_RECORD_LAUNCH = 9
+  AR_OPT_RECORD_LAUNCH = 9,
+  AR_OPT_GROUP = 10
 } ar_option;
 int ar_set_option(ar_handle* h, ar_option opt, int64_t value);
 
@@ -287,6 +301,7 @@ int ar_set_option(ar_handle* h, ar_option opt, int64_t value);
  *   13 = launch record (rank 0 only): one uint32 per workgroup of the last launch made with
  *        AR_OPT_RECORD_LAUNCH, XCC id in bits 7:0, rank + 1 in bits 15:8 (0: the workgroup maps
  *        to no rank and exits), workgroup index within the rank in bits 31:16
+ *   14 = sink: 16 KiB that idle lanes of the bf16 LL128-style kernel add zero into (stays zero)
  */
 int64_t ar_region_bytes(ar_handle* h, int region);
 
@@ -310,7 +325,9 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo);
  * Returns AR_OK, or AR_EINVAL / AR_ETOOBIG / AR_ENOTSUP / AR_ENORES as the call itself would.
  */
 typedef struct {
-  int kernel;     /* kernel family: the public algorithm id, or an internal one: 7 bulk
+  int kernel;     /* kernel family: the public algorithm id (21 = AR_LL128_DET), or an internal one:
+                     22 / 23 LL128-style with one / two word slices per lane (24 / 25
+                     deterministic), 7 bulk
                      two-shot; 8 / 9 multi-pass LL / sentinel one-shot; 10 / 11 one-pass sentinel
                      one-shot / two-shot with 8-byte units; 12 / 13 / 14 the reduce-scatter /
                      all-gather / broadcast loop kernels; 15 / 16 reduce-scatter / all-gather as

@@ -20,13 +20,15 @@ AR_FLOAT32, AR_BFLOAT16, AR_INT32 = 0, 1, 2
 (AR_ALGO_AUTO, AR_ONESHOT_LL, AR_ONESHOT_SENTINEL, AR_TWOSHOT, AR_LL128_ATOMIC, AR_BARRIER2,
  AR_BARRIER_ONLY) = range(7)
 AR_REDUCESCATTER, AR_ALLGATHER, AR_BROADCAST = 12, 13, 14
+AR_LL128_DET = 21
 AR_OK, AR_EINVAL, AR_ETOOBIG, AR_ENOTSUP, AR_EHIP, AR_ETIMEOUT, AR_ENORES = 0, -1, -2, -3, -4, -5, -6
 AR_PLACE_XCD, AR_PLACE_SAME, AR_PLACE_LINEAR = 0, 1, 2
 (AR_OPT_TIMEOUT_US, AR_OPT_WITHHOLD_RANK, AR_OPT_CTAS, AR_OPT_THREADS, AR_OPT_PLACEMENT,
- AR_OPT_DRIFT, AR_OPT_NARROW, AR_OPT_ROOT, AR_OPT_CHECK_INPUTS, AR_OPT_RECORD_LAUNCH) = range(10)
+ AR_OPT_DRIFT, AR_OPT_NARROW, AR_OPT_ROOT, AR_OPT_CHECK_INPUTS, AR_OPT_RECORD_LAUNCH,
+ AR_OPT_GROUP) = range(11)
 (REGION_P1, REGION_P2, REGION_LL, REGION_ACC, REGION_CNT, REGION_BAR, REGION_BDAT,
  REGION_LL_NEAR, REGION_P1_NEAR, REGION_P2_NEAR, REGION_PF1, REGION_PF2, REGION_FLG,
- REGION_LAUNCH_RECORD) = range(14)
+ REGION_LAUNCH_RECORD, REGION_SINK) = range(15)
 
 ALGOS = {
     "auto": AR_ALGO_AUTO,
@@ -34,6 +36,7 @@ ALGOS = {
     "oneshot_sentinel": AR_ONESHOT_SENTINEL,
     "twoshot": AR_TWOSHOT,
     "ll128_atomic": AR_LL128_ATOMIC,
+    "ll128_det": AR_LL128_DET,
     "barrier2": AR_BARRIER2,
     "barrier_only": AR_BARRIER_ONLY,
     "reducescatter": AR_REDUCESCATTER,

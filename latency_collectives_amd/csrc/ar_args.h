@@ -38,6 +38,13 @@ enum Algo : int {
   // internal: one-pass broadcast, 16- or 8-byte units (14 is then its loop kernel)
   ALGO_BCAST_ONEPASS = 19,
   ALGO_BCAST_NARROW = 20,
+  // the deterministic LL128-style variant (groups added in a fixed order)
+  ALGO_LL128_DET = 21,
+  // internal: LL128-style kernels for a chunk of at most 16 (E1) or 32 (E2) units in one wave
+  ALGO_LL128_E1 = 22,
+  ALGO_LL128_E2 = 23,
+  ALGO_LL128_DET_E1 = 24,
+  ALGO_LL128_DET_E2 = 25,
 };
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).
@@ -109,13 +116,15 @@ struct Args {
   Region p1;    // one-shot sentinel slots / two-shot reduce-scatter slots (sentinel)
   Region p2;    // two-shot all-gather slots (sentinel)
   Region ll;    // one-shot LL lines (zeroed, epoch flags)
-  Region acc;   // LL128-style shared atomic destination (zeroed)
-  Region cnt;   // LL128-style arrival counters [buf][cta][wave] (zeroed)
+  Region acc;   // LL128-style shared atomic destinations [buf][group][slot] (zeroed)
+  Region cnt;   // LL128-style arrival counters [buf][cta][wave], then the deterministic
+                // variant's tickets [buf][group][cta][wave] (zeroed)
   Region bar;   // barrier flags [src][cta] (zeroed, monotonic)
   Region bdat;  // barrier-baseline data slots [src] (single buffer, plain)
   Region pf1;   // bulk two-shot reduce-scatter slots (data only; completion flags below)
   Region pf2;   // bulk two-shot all-gather slots
   Region flg;   // bulk two-shot completion flags [phase 2][src][cta][wave] u64 (zeroed, monotonic)
+  Region sink;  // 16 KiB that idle lanes' packed bf16 atomics add zero into (zeroed)
   uint32_t* ctl;        // device control words
   uint32_t* status;     // host-mapped status words (pinned host memory)
   uint64_t* ts_start;   // optional [iters][nranks][ctas][waves] timestamps
@@ -140,6 +149,7 @@ struct Args {
   int drift;            // rank-drift stress: up to this many sleeps per iteration (0: off)
   int algo;
   int root;             // broadcast: the rank whose input every rank receives
+  int group;            // deterministic LL128-style variant: ranks per group
 };
 
 }  // namespace ar

@@ -37,12 +37,13 @@ namespace {
 // allocates (the allocation-free entry point shares this path).
 thread_local char g_err[512];
 
-constexpr int kRegions = 14;
+constexpr int kRegions = 15;
 enum RegionId {
   RG_P1 = 0, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT,
   RG_LLN, RG_P1N, RG_P2N,  // near copies of ll, p1, p2 for small messages
   RG_PF1, RG_PF2, RG_FLG,  // bulk two-shot data slots and completion flags
   RG_REC,                  // launch record (AR_OPT_RECORD_LAUNCH), written in rank 0's block only
+  RG_SINK,                 // where idle lanes' packed bf16 atomics add zero
 };
 // Default scratch per rank per protocol, from a scratch-size sweep on MI355X (the counterpart of
 // the pages' Fig. 12; the Pith review's "Assumptions & free parameters" give 4 MiB for the
@@ -123,8 +124,11 @@ int layout(int N, uint64_t max_bytes, uint64_t cap_os, uint64_t cap_ts, bool nea
   sz[RG_P1] = {std::max(slot_os, slot_ts), 2ull * N * std::max(slot_os, slot_ts)};
   sz[RG_P2] = {slot_ts, 2ull * N * slot_ts};
   sz[RG_LL] = {slot_ll, 2ull * N * slot_ll};
-  sz[RG_ACC] = {slot_ts, 2ull * slot_ts};
-  sz[RG_CNT] = {0, 2ull * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 4};
+  // LL128-style destinations: [buffer 2][group ceil(N / 2)][slot], a slot holding a partition
+  // chunk in binary32 (twice the bytes of a bf16 chunk, for the deterministic variant)
+  sz[RG_ACC] = {2 * slot_ts, 2ull * ((N + 1) / 2) * 2 * slot_ts};
+  // arrival counters [buffer 2][cta][wave], then the deterministic tickets [buffer][group][cta][wave]
+  sz[RG_CNT] = {0, (2ull + 2ull * ar::kMaxRanks) * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 4};
   sz[RG_BAR] = {0, 1ull * ar::kMaxRanks * ar::kMaxCtasPerRank * 8};
   sz[RG_BDAT] = {slot_os, 1ull * N * slot_os};
   // The bulk two-shot's slots are 4 KiB longer than their data: an owner reads all N sources'
@@ -134,6 +138,7 @@ int layout(int N, uint64_t max_bytes, uint64_t cap_os, uint64_t cap_ts, bool nea
   sz[RG_PF2] = {pitch_pf, 2ull * N * pitch_pf};
   sz[RG_FLG] = {0, 2ull * ar::kMaxRanks * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 8};
   sz[RG_REC] = {0, record ? 4ull * ar::kMaxGrid : 0ull};
+  sz[RG_SINK] = {0, 16384};
   // near area: the near ll, p1 and p2 regions, one 2 MiB page each (pitch set per launch)
   uint64_t off = 0;
   for (int i = RG_LLN; i <= RG_P2N; ++i) {
@@ -145,7 +150,7 @@ int layout(int N, uint64_t max_bytes, uint64_t cap_os, uint64_t cap_ts, bool nea
     off += ar::kNearPage;
   }
   for (int i : {RG_P1, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT, RG_PF1, RG_PF2, RG_FLG,
-                RG_REC}) {
+                RG_REC, RG_SINK}) {
     if (sz[i].bytes >= (1ull << 31)) {
       return ar_fail(AR_ETOOBIG, "scratch region %d would exceed 2 GiB per rank", i);
     }
@@ -201,6 +206,7 @@ struct ar_handle {
   int narrow = 1;  // one-pass sentinel kernels may use 8-byte units
   int root = 0;    // ar_bench of AR_BROADCAST: the root rank
   bool near_ok = true;    // the blocks start with calibrated near pages
+  int group = 4;          // deterministic LL128-style variant: ranks per group
   int check_inputs = 0;   // check every call's inputs against the sentinel before launching
   int record_launch = 0;  // kernels write the launch record (region RG_REC of rank 0)
   void** tab = nullptr;
@@ -281,8 +287,13 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
       break;
     case AR_TWOSHOT:
     case AR_LL128_ATOMIC:
+    case AR_LL128_DET:
       units = ceil_div(ceil_div(nbytes, line), N);  // one partition
-      cap_units = std::min({h->rg[RG_P1].slot, h->rg[RG_P2].slot, h->rg[RG_ACC].slot,
+      // a destination slot holds a chunk in binary32: 32 bytes per 16-byte bf16 unit for the
+      // deterministic variant
+      cap_units = std::min({h->rg[RG_P1].slot, h->rg[RG_P2].slot,
+                            h->rg[RG_ACC].slot / (algo == AR_LL128_DET && h->dtype == AR_BFLOAT16
+                                                      ? 2u : 1u),
                             h->rg[RG_PF1].slot, h->rg[RG_PF2].slot}) /
                   line;
       break;
@@ -302,7 +313,8 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
                          (algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL ||
                           algo == AR_TWOSHOT || algo == AR_REDUCESCATTER || algo == AR_ALLGATHER ||
                           algo == AR_BROADCAST ||
-                          (algo == AR_LL128_ATOMIC && units <= h->rg[RG_ACC].slot / 16));
+                          ((algo == AR_LL128_ATOMIC || algo == AR_LL128_DET) &&
+                           units <= h->rg[RG_ACC].slot / 32));
   const int cus_per_xcd = std::max(1, h->cu_count / kXcds);
   L.ranks_per_xcd = h->placement == AR_PLACE_XCD ? static_cast<int>(ceil_div(N, kXcds)) : 1;
   // Chunk geometry, workgroup shape and kernel for the near or the regular slots.
@@ -332,7 +344,8 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
     // wider workgroup at N = 4..16, the barrier baseline included). The multi-pass and bulk
     // kernels that take over wider chunks use 256-thread workgroups.
     const bool one_pass = algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL ||
-                          algo == AR_TWOSHOT || algo == AR_LL128_ATOMIC || algo == AR_BARRIER2 ||
+                          algo == AR_TWOSHOT || algo == AR_LL128_ATOMIC ||
+                          algo == AR_LL128_DET || algo == AR_BARRIER2 ||
                           algo == AR_REDUCESCATTER || algo == AR_ALLGATHER ||
                           algo == AR_BROADCAST;
     const uint64_t spread = round_up(ceil_div(C, static_cast<uint64_t>(rank_cus)), 64);
@@ -432,6 +445,19 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
       return ar_fail(AR_ENORES, "%d workgroups per rank exceed the co-resident limit %d", ctas,
                      max_ctas);
     L.ctas = ctas;
+    // LL128-style kernels whose whole chunk fits one wave with 16 or 32 units issue only the
+    // word slices that hold data
+    if ((algo == AR_LL128_ATOMIC || algo == AR_LL128_DET) && ctas == 1 && L.threads == 64 &&
+        C <= 32) {
+      const bool det = algo == AR_LL128_DET;
+      const int e = C <= 16 ? (det ? ar::ALGO_LL128_DET_E1 : ar::ALGO_LL128_E1)
+                            : (det ? ar::ALGO_LL128_DET_E2 : ar::ALGO_LL128_E2);
+      ar_kernel_fn fe = ar_select_kernel(e, h->dtype, nmax);
+      if (fe != nullptr && occupancy(fe, L.threads) >= 1) {
+        L.fn = fe;
+        L.kernel_algo = e;
+      }
+    }
     return AR_OK;
   };
   int rc = shape(near_fits);
@@ -508,6 +534,7 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
   a.pf1 = h->rg[RG_PF1];
   a.pf2 = h->rg[RG_PF2];
   a.flg = h->rg[RG_FLG];
+  a.sink = h->rg[RG_SINK];
   a.ctl = h->ctl;
   a.status = h->status_dev;
   a.launch_rec = h->record_launch
@@ -532,6 +559,7 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
   a.withhold = h->withhold;
   a.drift = 0;
   a.algo = algo;
+  a.group = h->group;
   return a;
 }
 
@@ -552,6 +580,8 @@ constexpr char kAutoTable[5][9] = {
 };
 
 int resolve_algo(ar_handle* h, int algo, uint64_t nbytes) {
+  // int32 additions are exact and associative: the plain atomic variant is already deterministic
+  if (algo == AR_LL128_DET && h->dtype == AR_INT32) return AR_LL128_ATOMIC;
   if (algo != AR_ALGO_AUTO) return algo;
   if (h->nranks == 1) return AR_ONESHOT_SENTINEL;
   int row = 0;
@@ -564,6 +594,11 @@ int resolve_algo(ar_handle* h, int algo, uint64_t nbytes) {
     case 'S': return AR_ONESHOT_SENTINEL;
     default: return AR_TWOSHOT;
   }
+}
+
+// Algorithms ar_allreduce accepts.
+bool is_allreduce_algo(int algo) {
+  return (algo >= AR_ALGO_AUTO && algo <= AR_BARRIER2) || algo == AR_LL128_DET;
 }
 
 bool overlap(const void* a, const void* b, uint64_t n) {
@@ -685,7 +720,7 @@ int allreduce_enqueue(ar_handle* h, const void* const in[], void* const out[], s
                       ar_algo algo, hipStream_t s) {
   if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
   if (in == nullptr || out == nullptr) return ar_fail(AR_EINVAL, "null pointer table");
-  if (algo < AR_ALGO_AUTO || algo > AR_BARRIER2)
+  if (!is_allreduce_algo(algo))
     return ar_fail(AR_EINVAL, "algorithm %d is not valid for ar_allreduce", static_cast<int>(algo));
   int rc = h->status_host != nullptr ? check_status(h) : AR_OK;
   if (rc != AR_OK) return rc;
@@ -865,6 +900,10 @@ int ar_set_option(ar_handle* h, ar_option opt, int64_t v) {
       if (v != 0 && v != 1) return ar_fail(AR_EINVAL, "record_launch must be 0 or 1");
       h->record_launch = static_cast<int>(v);
       return AR_OK;
+    case AR_OPT_GROUP:
+      if (v < 2 || v > ar::kMaxRanks) return ar_fail(AR_EINVAL, "group must be in [2, 16]");
+      h->group = static_cast<int>(v);
+      return AR_OK;
   }
   return ar_fail(AR_EINVAL, "unknown option %d", static_cast<int>(opt));
 }
@@ -985,7 +1024,7 @@ int ar_bench_ex(ar_handle* h, const void* const* in_sets, void* const* out_sets,
                 double* elapsed_ms, void* stream) {
   if (h == nullptr) return ar_fail(AR_EINVAL, "null handle");
   if (iters < 1 || iters > 1000000) return ar_fail(AR_EINVAL, "iters must be in [1, 1e6]");
-  if ((algo < AR_ALGO_AUTO || algo > AR_BARRIER_ONLY) && !is_collective(algo))
+  if (!is_allreduce_algo(algo) && algo != AR_BARRIER_ONLY && !is_collective(algo))
     return ar_fail(AR_EINVAL, "unknown algorithm %d", static_cast<int>(algo));
   int rc = check_status(h);
   if (rc != AR_OK) return rc;
@@ -1104,7 +1143,7 @@ int ar_bench_ex(ar_handle* h, const void* const* in_sets, void* const* out_sets,
 
 int ar_plan_info(ar_handle* h, size_t count, ar_algo algo, ar_plan* info) {
   if (h == nullptr || info == nullptr) return ar_fail(AR_EINVAL, "null argument");
-  if ((algo < AR_ALGO_AUTO || algo > AR_BARRIER2) && !is_collective(algo))
+  if (!is_allreduce_algo(algo) && !is_collective(algo))
     return ar_fail(AR_EINVAL, "algorithm %d is not valid", static_cast<int>(algo));
   uint64_t in_b = 0, out_b = 0;
   int rc = op_bytes(h, algo, count, in_b, out_b);
@@ -1143,7 +1182,7 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
     const uint64_t one = (N + 1) * x + 3 * (N - 1) * x;
     return static_cast<int64_t>(algo == AR_BROADCAST ? one : N * one);
   }
-  if (algo < AR_ALGO_AUTO || algo > AR_BARRIER2)
+  if (!is_allreduce_algo(algo))
     return ar_fail(AR_EINVAL, "algorithm %d is not valid", static_cast<int>(algo));
   const uint64_t S = static_cast<uint64_t>(count) * elem_bytes(h->dtype);
   if (S > h->max_bytes) return ar_fail(AR_ETOOBIG, "message exceeds max_bytes");
@@ -1164,7 +1203,18 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
     case AR_TWOSHOT:
     case ar::ALGO_TWOSHOT_NARROW: return static_cast<int64_t>((N + 1) * S + 7 * (N - 1) * S);
     case ar::ALGO_TWOSHOT_BULK: return static_cast<int64_t>((N + 1) * S + 5 * (N - 1) * S);
-    case AR_LL128_ATOMIC: return static_cast<int64_t>(2 * N * S + 3 * S + 4 * (N - 1) * S);
+    case AR_LL128_ATOMIC:
+    case ar::ALGO_LL128_E1:
+    case ar::ALGO_LL128_E2: return static_cast<int64_t>(2 * N * S + 3 * S + 4 * (N - 1) * S);
+    case AR_LL128_DET:
+    case ar::ALGO_LL128_DET_E1:
+    case ar::ALGO_LL128_DET_E2: {
+      // inputs N S; contributions N S (binary32: twice that for bf16); the owners read and clear
+      // G group sums, 2 G S (binary32); own partition out S; all-gather 4 (N - 1) S
+      const uint64_t w = h->dtype == AR_BFLOAT16 ? 2 : 1;
+      const uint64_t G = (N + static_cast<uint64_t>(h->group) - 1) / static_cast<uint64_t>(h->group);
+      return static_cast<int64_t>(N * S + w * N * S + 2 * w * G * S + S + 4 * (N - 1) * S);
+    }
     case AR_BARRIER2: return static_cast<int64_t>(2 * N * S + 2 * N * (N - 1) * S);
     default: return 0;
   }
@@ -1206,7 +1256,7 @@ namespace {
 // 64 MiB).
 constexpr uint64_t kNoAllocCap = 256ull << 10;
 constexpr uint64_t kNoAllocCtl = 4096;  // control words (16 x u32) and status words (8 x u32)
-constexpr uint64_t kNoAllocScratchBytes = 32ull << 20;
+constexpr uint64_t kNoAllocScratchBytes = 40ull << 20;
 constexpr int kNoAllocDevices = 64;
 
 }  // namespace

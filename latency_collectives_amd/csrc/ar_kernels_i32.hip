@@ -39,6 +39,8 @@ ar_kernel_fn ar_select_kernel_i32(int algo, int nmax) {
     case ar::ALGO_TWOSHOT_NARROW: return pick_n<ar::ALGO_TWOSHOT_NARROW>(nmax);
     case ar::ALGO_TWOSHOT_BULK: return pick_n<ar::ALGO_TWOSHOT_BULK>(nmax);
     case ar::ALGO_LL128_ATOMIC: return pick_n<ar::ALGO_LL128_ATOMIC>(nmax);
+    case ar::ALGO_LL128_E1: return pick_n<ar::ALGO_LL128_E1>(nmax);
+    case ar::ALGO_LL128_E2: return pick_n<ar::ALGO_LL128_E2>(nmax);
     case ar::ALGO_BARRIER2: return pick_n<ar::ALGO_BARRIER2>(nmax);
     case ar::ALGO_REDUCESCATTER: return pick_n<ar::ALGO_REDUCESCATTER>(nmax);
     case ar::ALGO_ALLGATHER: return pick_n<ar::ALGO_ALLGATHER>(nmax);

@@ -814,12 +814,52 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
 // from an empty slot. The int32 all-gather therefore uses the bulk two-shot's protocol instead,
 // which does not look at the data: plain coherent pushes into the all-gather data slots, a wait
 // for their completion, then a completion flag per peer (phase 1) that the receivers poll.
-template <int DT, int NMAX>
+//
+// bf16 adds two elements per atomic (gfx950's packed bf16 atomic add): the destination holds
+// bf16 and every addition rounds to bf16, so the sum's error is that of a bf16 accumulation in
+// an unknown order.
+//
+// The deterministic variant (DET; a reading of the Pith review's "deterministic variant using
+// per-chunk grouping or hierarchical accumulation") keeps the shared destinations and the
+// atomics but fixes the order: the ranks form groups of `group` consecutive ranks, and owner p
+// holds one binary32 destination per group. Within a group the members add in rank order: the
+// first member stores its values, member m waits until the group's ticket in the owner's block
+// reads m, adds (binary32 atomics; bf16 inputs widened), waits until its adds have been
+// performed and sets the ticket to m + 1. The owner waits for every group's ticket to reach the
+// group's size, takes each group sum with an atomic exchange against zero, adds the group sums in
+// group order (bf16 rounded once), resets the tickets and runs the all-gather. Every addition
+// then happens in one fixed order, so the result is the same bit pattern on every run.
+//
+// The wave's units are handled as words: lane l takes words e * 64 + l of the wave's 64 units
+// (e = 0..E-1), so that every atomic instruction adds into 256 contiguous bytes (whole cache
+// lines) rather than one word of each of 64 units. E < 4 is used when the whole chunk is fewer
+// than 16 E units in one wave: the word slices that hold nothing are then not issued at all.
+
+// Byte offset of group g's destination of buffer b in a rank block's `acc` region, laid out as
+// [buffer 2][group ceil(N / 2)][slot]; the plain atomic variant uses group 0.
+__device__ __forceinline__ uint32_t acc_off(const Args& a, uint32_t b, int g) {
+  return (b * static_cast<uint32_t>((a.nranks + 1) / 2) + static_cast<uint32_t>(g)) * a.acc.slot;
+}
+
+// Ticket word of (buffer b, group g, this workgroup and wave) in rank `owner`'s counter region,
+// after the plain variant's arrival counters [buffer 2][cta][wave].
+__device__ __forceinline__ uint32_t* det_ticket(const Args& a, int owner, uint32_t b, int g,
+                                                const Ctx& c) {
+  constexpr uint32_t kBase = 2u * kMaxCtasPerRank * kMaxWavesPerCta;
+  return reinterpret_cast<uint32_t*>(a.base + static_cast<uint64_t>(owner) * a.stride +
+                                     a.cnt.off) +
+         kBase + ((b * kMaxRanks + static_cast<uint32_t>(g)) * kMaxCtasPerRank + c.cta) *
+                     kMaxWavesPerCta + c.wave;
+}
+
+template <int DT, int NMAX, int E = 4, bool DET = false>
 __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r, rsrc_t out_r,
-                           int k, uint64_t& t0,
-                           uint64_t& t1) {
-  static_assert(DT == DT_F32 || DT == DT_I32, "atomic reduction is for fp32 and int32");
+                           int k, uint64_t& t0, uint64_t& t1) {
+  static_assert(!DET || DT != DT_I32, "an int32 sum does not depend on the order");
+  static_assert(E == 1 || E == 2 || E == 4, "word slices per lane");
   constexpr bool kFlagAG = DT == DT_I32;
+  // binary32 words of the destination per payload word: 2 for the deterministic bf16 variant
+  constexpr uint32_t kAW = (DET && DT == DT_BF16) ? 2u : 1u;
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t CU = a.chunk_units, P = a.part_units;
@@ -830,53 +870,171 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
   const uint32_t peers = peer_mask(N, r);
   const u32x4 sent = sentinel_unit<DT, 16>();
   auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+  const int M = DET ? a.group : N;  // group size (the plain variant: one group of N)
+  const int G = DET ? (N + M - 1) / M : 1;
+  const int gme = DET ? r / M : 0, mme = DET ? r - gme * M : 0;
   stamp_start(t0, k);
   wait_all_mem();
-  if (has_units && r != a.withhold) {
-    for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
-      // The wave's 64 units are 256 words; lane l takes words e * 64 + l (e = 0..3), so that
-      // every atomic instruction adds into 256 contiguous bytes (whole cache lines) rather than
-      // one word of each of 64 units.
-      uint32_t woff[4];
-      bool wact[4];
+  // The wave's words of chunk k (pass i0): word d = i0 * 4 + e * 64 + lane.
+  auto words = [&](uint32_t i0, uint32_t (&woff)[E], bool (&wact)[E]) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t d = i0 * 4u + static_cast<uint32_t>(e) * 64u + c.lane;  // word in chunk
-        wact[e] = d < CU * 4u;
-        woff[e] = d * 4u;
-      }
-      uint32_t w[NMAX][4];
+    for (int e = 0; e < E; ++e) {
+      const uint32_t d = i0 * 4u + static_cast<uint32_t>(e) * 64u + c.lane;
+      wact[e] = d < CU * 4u;
+      woff[e] = d * 4u;
+    }
+  };
+  if constexpr (!DET) {
+    if (has_units && r != a.withhold) {
+      for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+        uint32_t woff[E];
+        bool wact[E];
+        words(i0, woff, wact);
+        uint32_t w[NMAX][E];
 #pragma unroll
-      for (int j = 0; j < NMAX; ++j) {
-        int p = r + j;
-        if (p >= N) p -= N;
-        const bool live = j < N;
-        const uint32_t pbase = (p * P + k * CU) * 16u;
+        for (int j = 0; j < NMAX; ++j) {
+          int p = r + j;
+          if (p >= N) p -= N;
+          const bool live = j < N;
+          const uint32_t pbase = (p * P + k * CU) * 16u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[j][e] = ld4<kPlain>(in_r, live && wact[e] ? pbase + woff[e] : kDrop);
-      }
+          for (int e = 0; e < E; ++e)
+            w[j][e] = ld4<kPlain>(in_r, live && wact[e] ? pbase + woff[e] : kDrop);
+        }
+        // bf16 of odd length: the half word past the last element reads as zero (it would
+        // otherwise be added like data, and a sum there that equals the sentinel would stall
+        // the all-gather poll)
+        if (odd_tail<DT>(a.nbytes)) {
+          asm volatile("");
+          const uint32_t last = a.nbytes & ~3u;
 #pragma unroll
-      for (int j = 0; j < NMAX; ++j) {
-        const rsrc_t dst = j == 0 ? region_rsrc(a, r, a.acc) : peer_rsrc(a, r, j, a.acc);
+          for (int j = 0; j < NMAX; ++j) {
+            int p = r + j;
+            if (p >= N) p -= N;
+            const uint32_t pbase = (p * P + k * CU) * 16u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t off = wact[e] ? b * a.acc.slot + woff[e] : kDrop;
-          if constexpr (DT == DT_F32) {
-            (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(__uint_as_float(w[j][e]), dst,
-                                                                 off, 0, 0);
+            for (int e = 0; e < E; ++e)
+              w[j][e] = pbase + woff[e] == last ? (w[j][e] & 0xFFFFu) : w[j][e];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NMAX; ++j) {
+          if constexpr (DT == DT_BF16) {
+            // Packed bf16 atomics take a global address, so nothing drops them: lanes of absent
+            // peers and idle words add zero into a word of this rank's sink region instead (no
+            // branch, so the atomics stay in one basic block without waits between them).
+            typedef short s16x2 __attribute__((ext_vector_type(2)));
+            int q = r + j;
+            if (q >= N) q -= N;
+            uint8_t* dst = a.base + static_cast<uint64_t>(j < N ? q : r) * a.stride + a.acc.off +
+                           acc_off(a, b, 0);
+            uint8_t* sink = a.base + static_cast<uint64_t>(r) * a.stride + a.sink.off +
+                            ((c.cta * kMaxWavesPerCta + c.wave) % 64u) * 256u + c.lane * 4u;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const bool live = j < N && wact[e];
+              __builtin_amdgcn_global_atomic_fadd_v2bf16(
+                  reinterpret_cast<s16x2*>(live ? dst + woff[e] : sink),
+                  __builtin_bit_cast(s16x2, live ? w[j][e] : 0u));
+            }
           } else {
-            (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(static_cast<int>(w[j][e]), dst,
-                                                                off, 0, 0);
+            const rsrc_t dst = j == 0 ? region_rsrc(a, r, a.acc) : peer_rsrc(a, r, j, a.acc);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const uint32_t off = wact[e] ? acc_off(a, b, 0) + woff[e] : kDrop;
+              if constexpr (DT == DT_F32) {
+                (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(__uint_as_float(w[j][e]),
+                                                                     dst, off, 0, 0);
+              } else {
+                (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(static_cast<int>(w[j][e]),
+                                                                    dst, off, 0, 0);
+              }
+            }
           }
         }
       }
+      wait_all_mem();  // every add of this wave has been performed
+      if (c.lane < N) {
+        uint32_t* cnt = reinterpret_cast<uint32_t*>(a.base +
+                                                    static_cast<uint64_t>(c.lane) * a.stride +
+                                                    a.cnt.off) + cnt_idx;
+        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    wait_all_mem();  // every add of this wave has been performed
-    if (c.lane < N) {
-      uint32_t* cnt = reinterpret_cast<uint32_t*>(a.base + static_cast<uint64_t>(c.lane) * a.stride +
-                                                  a.cnt.off) + cnt_idx;
-      __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    // Deterministic: lane q watches owner q's ticket of this rank's group; every owner whose
+    // ticket has reached this rank's place gets this rank's chunk of its partition, then its
+    // ticket moves on. Owners become ready independently, so several may be served per round.
+    if (has_units && r != a.withhold) {
+      uint32_t todo = (N >= 32 ? 0xFFFFFFFFu : ((1u << N) - 1u));
+      uint32_t spins = 0;
+      uint64_t t_first = 0;
+      while (todo != 0) {
+        const int q = c.lane;
+        const bool watch = q < N && ((todo >> q) & 1u);
+        uint32_t tv = 0xFFFFFFFFu;
+        if (watch)
+          tv = __hip_atomic_load(det_ticket(a, q, b, gme, c), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t go = static_cast<uint32_t>(__ballot(watch && tv == static_cast<uint32_t>(mme)));
+        if (go == 0) {
+          if ((++spins & 1023u) == 0) {
+            t_first = poll_check(poll_env(a), t_first, r, __builtin_ctz(todo), s);
+            if (t_first == 0) return false;
+          }
+          continue;
+        }
+        for (uint32_t rest = go; rest != 0; rest &= rest - 1u) {
+          const int p = __builtin_ctz(rest);  // owner, wave-uniform
+          uint8_t* dst = a.base + static_cast<uint64_t>(p) * a.stride + a.acc.off +
+                         acc_off(a, b, gme);
+          const rsrc_t dst_r = make_rsrc(dst, a.acc.slot);
+          for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
+            uint32_t woff[E];
+            bool wact[E];
+            words(i0, woff, wact);
+            const uint32_t pbase = (p * P + k * CU) * 16u;
+            uint32_t w[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) w[e] = ld4<kPlain>(in_r, wact[e] ? pbase + woff[e] : kDrop);
+            if (odd_tail<DT>(a.nbytes)) {  // the half word past the last bf16 element reads as 0
+              asm volatile("");
+#pragma unroll
+              for (int e = 0; e < E; ++e)
+                w[e] = pbase + woff[e] == (a.nbytes & ~3u) ? (w[e] & 0xFFFFu) : w[e];
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              // binary32 value(s) of the word: fp32 as is, bf16 widened (low element first)
+              float v0, v1 = 0.0f;
+              if constexpr (DT == DT_BF16) {
+                v0 = __uint_as_float(w[e] << 16);
+                v1 = __uint_as_float(w[e] & 0xFFFF0000u);
+              } else {
+                v0 = __uint_as_float(w[e]);
+              }
+              const uint32_t off = wact[e] ? woff[e] * kAW : kDrop;
+              if (mme == 0) {
+                // the group's first member writes: the destination then holds exactly its values
+                if constexpr (kAW == 2)
+                  st8<kCoh>(dst_r, off, u32x2{__float_as_uint(v0), __float_as_uint(v1)});
+                else
+                  st4<kCoh>(dst_r, off, __float_as_uint(v0));
+              } else {
+                (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v0, dst_r, off, 0, 0);
+                if constexpr (kAW == 2)
+                  (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                      v1, dst_r, wact[e] ? off + 4u : kDrop, 0, 0);
+              }
+            }
+          }
+        }
+        wait_all_mem();  // this rank's values are in the destinations before the tickets move
+        if (q < N && ((go >> q) & 1u))
+          __hip_atomic_store(det_ticket(a, q, b, gme, c), static_cast<uint32_t>(mme + 1),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        todo &= ~go;
+      }
     }
   }
   if (has_units) {
@@ -885,27 +1043,70 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
         cnt_idx;
     uint32_t spins = 0;
     uint64_t t_first = 0;
-    while (uni(__hip_atomic_load(my_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) !=
-           static_cast<uint32_t>(N)) {
-      if ((++spins & 1023u) == 0) {
-        t_first = poll_check(poll_env(a), t_first, r, -1, s);
-        if (t_first == 0) return false;
+    if constexpr (!DET) {
+      while (uni(__hip_atomic_load(my_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) !=
+             static_cast<uint32_t>(N)) {
+        if ((++spins & 1023u) == 0) {
+          t_first = poll_check(poll_env(a), t_first, r, -1, s);
+          if (t_first == 0) return false;
+        }
+      }
+    } else {
+      // lane g < G waits until group g's ticket in this rank's block equals the group's size
+      const int g = c.lane;
+      bool need = g < G;
+      const uint32_t size = static_cast<uint32_t>(g < G ? min(M, N - g * M) : 0);
+      while (true) {
+        if (need && __hip_atomic_load(det_ticket(a, r, b, g, c), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == size)
+          need = false;
+        if (__ballot(need) == 0) break;
+        if ((++spins & 1023u) == 0) {
+          t_first = poll_check(poll_env(a), t_first, r, -1, s);
+          if (t_first == 0) return false;
+        }
       }
     }
-    uint8_t* acc = a.base + static_cast<uint64_t>(r) * a.stride + a.acc.off +
-                   static_cast<uint64_t>(b) * a.acc.slot;
+    uint8_t* acc = a.base + static_cast<uint64_t>(r) * a.stride + a.acc.off;
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;
       const bool act = i < CU;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (act) {
-        uint64_t* q = reinterpret_cast<uint64_t*>(acc + static_cast<uint64_t>(i) * 16u);
-        const uint64_t lo =
-            __hip_atomic_exchange(q, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t hi =
-            __hip_atomic_exchange(q + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v = u32x4{static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
-                  static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
+        if constexpr (!DET) {
+          uint64_t* q = reinterpret_cast<uint64_t*>(acc + acc_off(a, b, 0) +
+                                                    static_cast<uint64_t>(i) * 16u);
+          const uint64_t lo =
+              __hip_atomic_exchange(q, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t hi =
+              __hip_atomic_exchange(q + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v = u32x4{static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
+                    static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
+        } else {
+          // group sums in group order: 4 (fp32) or 8 (bf16) binary32 values per unit
+          constexpr int V = 4 * static_cast<int>(kAW);
+          float sum[V];
+          for (int g = 0; g < G; ++g) {
+            uint64_t* q = reinterpret_cast<uint64_t*>(acc + acc_off(a, b, g) +
+                                                      static_cast<uint64_t>(i) * 16u * kAW);
+#pragma unroll
+            for (int h = 0; h < V / 2; ++h) {
+              const uint64_t x =
+                  __hip_atomic_exchange(q + h, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              const float lo = __uint_as_float(static_cast<uint32_t>(x));
+              const float hi = __uint_as_float(static_cast<uint32_t>(x >> 32));
+              sum[2 * h] = g == 0 ? lo : sum[2 * h] + lo;
+              sum[2 * h + 1] = g == 0 ? hi : sum[2 * h + 1] + hi;
+            }
+          }
+          if constexpr (DT == DT_BF16) {
+            v = u32x4{bf16x2_rne(sum[0], sum[1]), bf16x2_rne(sum[2], sum[3]),
+                      bf16x2_rne(sum[4], sum[5]), bf16x2_rne(sum[6], sum[7])};
+          } else {
+            v = u32x4{__float_as_uint(sum[0]), __float_as_uint(sum[1]), __float_as_uint(sum[2]),
+                      __float_as_uint(sum[3])};
+          }
+        }
       }
       if (r != a.withhold) {
         if constexpr (kFlagAG)
@@ -916,7 +1117,14 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
       const uint32_t o[4] = {v.x, v.y, v.z, v.w};
       store_unit<DT, 16>(out_r, act ? (r * P + k * CU + i) * 16u : kDrop, a.nbytes, o);
     }
-    if (c.lane == 0) __hip_atomic_store(my_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (!DET) {
+      if (c.lane == 0) __hip_atomic_store(my_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      // the exchanges have returned (their values were used above): the destinations are clear
+      if (c.lane < G)
+        __hip_atomic_store(det_ticket(a, r, b, c.lane, c), 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
     if constexpr (kFlagAG) {
       if (r != a.withhold) {
         wait_all_mem();  // the pushed sums are performed before the flags that announce them
@@ -1447,6 +1655,16 @@ __device__ __forceinline__ void ar_body(const Args& a) {
         ok = step_twoshot_bulk<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_ATOMIC) {
         ok = step_ll128<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_LL128_E1) {
+        ok = step_ll128<DT, NMAX, 1>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_LL128_E2) {
+        ok = step_ll128<DT, NMAX, 2>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_LL128_DET) {
+        ok = step_ll128<DT, NMAX, 4, true>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_LL128_DET_E1) {
+        ok = step_ll128<DT, NMAX, 1, true>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_LL128_DET_E2) {
+        ok = step_ll128<DT, NMAX, 2, true>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_BARRIER2) {
         ok = step_barrier2<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_RS_ONEPASS) {

@@ -290,7 +290,8 @@ def test_plan_info_reports_the_launch():
     n = 8
     with handle(n, 16 << 20, "i32") as h:
         big = A.ar_plan_info(h, (16 << 20) // 4, A.AR_TWOSHOT)
-        assert big["kernel"] == 7 and big["threads"] == 256 and big["chunks"] == 1
+        # 16 MiB two-shot cap: 1 MiB per (buffer, source) slot, so a 2 MiB partition is 2 chunks
+        assert big["kernel"] == 7 and big["threads"] == 256 and big["chunks"] == 2
         # int32 sums may equal the sentinel: the int32 two-shot always runs the bulk kernel
         # (completion flags), on the regular slots, with one workgroup per 256 units when small
         small = A.ar_plan_info(h, 256, A.AR_TWOSHOT)

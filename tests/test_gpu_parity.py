@@ -166,11 +166,10 @@ def test_argument_errors_on_device():
         with pytest.raises(A.ArError) as e:
             A.ar_allreduce(h, b, [b[0], b[0]], 64, A.AR_ONESHOT_LL)
         assert e.value.code == A.AR_EINVAL
-    with handle(2, 1024, "bf16") as h:
-        b = [torch.zeros(64, dtype=torch.int16, device="cuda") for _ in range(2)]
+    with handle(2, 1024, "f32", group=2) as h:
         with pytest.raises(A.ArError) as e:
-            A.ar_allreduce(h, b, [torch.empty_like(t) for t in b], 64, A.AR_LL128_ATOMIC)
-        assert e.value.code == A.AR_ENOTSUP
+            A.ar_set_option(h, A.AR_OPT_GROUP, 1)  # a group of one rank is the two-shot
+        assert e.value.code == A.AR_EINVAL
 
 
 @pytest.mark.parametrize("algo", ALGO_NAMES)
