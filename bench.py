@@ -66,7 +66,7 @@ def _gm(xs):
 
 def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str, iters: int,
                warmup: int, hz: float, set_cap_bytes: int = 256 << 20, check: bool = True,
-               launch_calls: int = 20):
+               launch_calls: int = 20, group: int = 4):
     import torch
 
     n, dt = wl["nranks"], wl["dtype"]
@@ -170,7 +170,8 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
             ok = all(np.array_equal(outs[k * n + r].cpu().numpy().view(np.uint8),
                                     want_all[r].view(np.uint8)) for r in range(n))
         else:
-            want = oracle.allreduce(rows)[0]
+            want = (oracle.allreduce_grouped(rows, group)[0]
+                    if algo == "ll128_det" and dt != "i32" else oracle.allreduce(rows)[0])
             ok = True
             for r in range(n):
                 got = outs[k * n + r].cpu().numpy().view(want.dtype)
@@ -179,6 +180,12 @@ def bench_size(A, I, h, wid: int, wl: dict, size_idx: int, size: int, algo: str,
                     bound = n * 2.0 ** -23 * np.abs(x.astype(np.float64)).sum(0)
                     ok &= bool(np.all(np.abs(got.astype(np.float64) - want.astype(np.float64))
                                       <= bound))
+                elif algo == "ll128_atomic" and dt == "bf16":
+                    # bf16 accumulation: N * 2^-8 * sum_r |x_r[i]| (plus N subnormal spacings)
+                    def wide(b):
+                        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                    bound = n * 2.0 ** -8 * np.abs(wide(x)).sum(0) + n * 2.0 ** -133
+                    ok &= bool(np.all(np.abs(wide(got) - wide(want)) <= bound))
                 else:
                     ok &= bool(np.array_equal(got.view(np.uint8), want.view(np.uint8)))
         res["spot_check"] = bool(ok)
@@ -363,7 +370,8 @@ def cpu_baseline_threads(I, wid: int, wl: dict, threads: int, budget_s: float = 
 
 
 def run_workload(A, I, wid: int, algo: str | None, iters: int | None, warmup: int, hz: float,
-                 placement: int, sizes=None, dtype: str | None = None, launch_calls: int = 20):
+                 placement: int, sizes=None, dtype: str | None = None, launch_calls: int = 20,
+                 group: int | None = None):
     wl = dict(I.WORKLOADS[wid])
     if sizes is not None:
         wl["sizes"] = sizes
@@ -377,10 +385,12 @@ def run_workload(A, I, wid: int, algo: str | None, iters: int | None, warmup: in
     h = A.ar_create(wl["nranks"], max(wl["sizes"]) * widen, A.DTYPES[wl["dtype"]])
     try:
         A.ar_set_option(h, A.AR_OPT_PLACEMENT, placement)
+        if group is not None:
+            A.ar_set_option(h, A.AR_OPT_GROUP, group)
         rows = []
         for si, size in enumerate(wl["sizes"]):
             rows.append(bench_size(A, I, h, wid, wl, si, size, algo, iters, warmup, hz,
-                                   launch_calls=launch_calls))
+                                   launch_calls=launch_calls, group=group or 4))
             print(f"# workload {wid} {algo} {wl['dtype']} size {size}: p50 "
                   f"{rows[-1]['p50_us']:.3f} us p99 {rows[-1]['p99_us']:.3f} us",
                   file=sys.stderr, flush=True)
@@ -455,6 +465,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=None, choices=sorted(range(1, 9)),
                     help="measure this workload alone (with --algo) instead of the configurations")
     ap.add_argument("--algo", default=None)
+    ap.add_argument("--dtype", default=None, help="with --workload: override the dtype")
+    ap.add_argument("--group", type=int, default=None,
+                    help="with --workload: ranks per group of the deterministic LL128 variant")
     ap.add_argument("--placement", type=int, default=0, help="0 XCD per rank, 1 same XCD")
     ap.add_argument("--all", action="store_true", help="also run the standalone collectives")
     ap.add_argument("--auto-sweep", action="store_true",
@@ -525,7 +538,8 @@ def main() -> int:
     if args.workload is not None:
         sizes = [int(x) for x in args.sizes.split(",")] if args.sizes else None
         wl, algo, iters, rows = run_workload(A, I, args.workload, args.algo, args.steps,
-                                             args.warmup, hz, args.placement, sizes)
+                                             args.warmup, hz, args.placement, sizes,
+                                             dtype=args.dtype, group=args.group)
         print(json.dumps({"workload": args.workload, "algo": algo, "dtype": wl["dtype"],
                           "per_size": _round_rows(rows)}), flush=True)
         return 0

@@ -58,8 +58,10 @@ typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_INT32 = 2 } ar_dtype;
  *                       design whose barrier cost the pages measure (§III.B). A baseline.
  *   AR_BARRIER_ONLY     (ar_bench only) one cross-rank barrier per iteration, no data: the
  *                       barrier latency versus N (§III.B, Fig. 3).
- *   AR_ALGO_AUTO        picks one-shot LL, one-shot sentinel or two-shot from the rank count and
- *                       the message size, by a table of the fastest measured on MI355X.
+ *   AR_ALGO_AUTO        picks one-shot LL, one-shot sentinel, two-shot or (int32 only) the
+ *                       LL128-style kernel from the dtype, the rank count and the message size,
+ *                       by tables of the fastest measured on MI355X; for fp32 and bf16 only
+ *                       fixed-order kernels, so the result stays bit-reproducible.
  * Every algorithm except AR_LL128_ATOMIC and AR_LL128_DET adds in rank order 0..N-1 (fp32
  * accumulation for bf16, rounded once to nearest even; wrapping int32) and is bit-reproducible.
  * Double buffering (§IV "Bidirectional Communication Double Buffering", Fig. 4) is used by
@@ -271,7 +273,7 @@ double ar_wallclock_hz(void);
  *                        workgroup index it decoded into region 13 of rank 0 (ar_read_region)
  *                        [0]
  *   AR_OPT_GROUP         AR_LL128_DET: ranks per group, 2..16; the result depends on it (it is
- *                        the summation order) [4]
+ *                        the summation order) [2]
  */
 typedef enum {
   AR_OPT_TIMEOUT_US = 0,

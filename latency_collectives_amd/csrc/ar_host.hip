@@ -206,7 +206,7 @@ struct ar_handle {
   int narrow = 1;  // one-pass sentinel kernels may use 8-byte units
   int root = 0;    // ar_bench of AR_BROADCAST: the root rank
   bool near_ok = true;    // the blocks start with calibrated near pages
-  int group = 4;          // deterministic LL128-style variant: ranks per group
+  int group = 2;          // deterministic LL128-style variant: ranks per group
   int check_inputs = 0;   // check every call's inputs against the sentinel before launching
   int record_launch = 0;  // kernels write the launch record (region RG_REC of rank 0)
   void** tab = nullptr;
@@ -304,6 +304,18 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
     default:
       return ar_fail(AR_EINVAL, "unknown algorithm %d", algo);
   }
+  const int cus_per_xcd = std::max(1, h->cu_count / kXcds);
+  if (algo == AR_LL128_DET) {
+    // The deterministic variant orders each member's adds by a ticket per wave, so every unit of
+    // a chunk needs its own lane: a chunk is at most one 256-thread workgroup per compute unit
+    // of the smallest share of the chip the placement gives a rank.
+    const int min_rank_cus = h->placement == AR_PLACE_XCD
+                                 ? cus_per_xcd / static_cast<int>(ceil_div(N, kXcds))
+                             : h->placement == AR_PLACE_SAME ? cus_per_xcd / N
+                                                             : h->cu_count / N;
+    const uint64_t wgs = h->ctas ? h->ctas : std::max(1, min_rank_cus);
+    cap_units = std::min<uint64_t>(cap_units, wgs * (h->threads ? h->threads : 256));
+  }
   if (cap_units == 0) return ar_fail(AR_EINVAL, "scratch slots are too small");
   // Messages whose 2 * N slots fit a near page in one chunk use the near regions: the slot data
   // goes in 8 KiB chunks at a pitch of 16 KiB per chunk.
@@ -314,8 +326,8 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
                           algo == AR_TWOSHOT || algo == AR_REDUCESCATTER || algo == AR_ALLGATHER ||
                           algo == AR_BROADCAST ||
                           ((algo == AR_LL128_ATOMIC || algo == AR_LL128_DET) &&
-                           units <= h->rg[RG_ACC].slot / 32));
-  const int cus_per_xcd = std::max(1, h->cu_count / kXcds);
+                           units <= h->rg[RG_ACC].slot / 32 &&
+                           (algo != AR_LL128_DET || units <= cap_units)));
   L.ranks_per_xcd = h->placement == AR_PLACE_XCD ? static_cast<int>(ceil_div(N, kXcds)) : 1;
   // Chunk geometry, workgroup shape and kernel for the near or the regular slots.
   auto shape = [&](bool near) -> int {
@@ -445,6 +457,8 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
       return ar_fail(AR_ENORES, "%d workgroups per rank exceed the co-resident limit %d", ctas,
                      max_ctas);
     L.ctas = ctas;
+    if (algo == AR_LL128_DET && static_cast<uint64_t>(ctas) * L.threads < C)
+      return ar_fail(AR_ENORES, "the deterministic variant needs a lane per unit of a chunk");
     // LL128-style kernels whose whole chunk fits one wave with 16 or 32 units issue only the
     // word slices that hold data
     if ((algo == AR_LL128_ATOMIC || algo == AR_LL128_DET) && ctas == 1 && L.threads == 64 &&
@@ -563,20 +577,43 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
   return a;
 }
 
-// Automatic choice by rank count and message size (the pages select by size and rank count,
-// Fig. 12): the fastest of one-shot LL (L), one-shot sentinel (S) and two-shot (T) measured on
-// MI355X (`python bench.py --auto-sweep`, fp32, p50 of 100 back-to-back calls; two sweeps, a
-// cell taking the later one's winner when it led by 3 % or more) for N in {2,3,4,8,16} and
-// 128 B .. 2 MiB per rank. A call uses the row of the smallest measured N
-// >= its N and the column of the smallest measured size >= its size; above 2 MiB, two-shot.
+// Automatic choice by data type, rank count and message size (the pages select by size and
+// rank count; the Pith review's "kernel_selection_thresholds", Fig. 12): the fastest of
+// one-shot LL (L), one-shot sentinel (S), two-shot (T) and, for int32, the LL128-style atomic
+// kernel (A) measured on MI355X (`python bench.py --auto-sweep`: p50 of 100 back-to-back calls,
+// fp32 uniform, bf16 normal, int32 on [-2^20, 2^20]) for N in {2,3,4,8,16} and 128 B .. 2 MiB
+// per rank; a cell keeps S when another kernel led by less than 3 %. A call uses the row of the
+// smallest measured N >= its N and the column of the smallest measured size >= its size; above
+// 2 MiB, the last column. For fp32 and bf16 only the fixed-order kernels are candidates, so that
+// AUTO stays bit-reproducible; the int32 atomic sum is exact in any order. (int32 two-shot runs
+// the completion-flag kernel at every size, hence its late crossover.)
 constexpr int kAutoN[5] = {2, 3, 4, 8, 16};
 constexpr uint64_t kAutoBytes[8] = {128, 512, 2048, 8192, 32768, 131072, 524288, 2097152};
-constexpr char kAutoTable[5][9] = {
-    "SSSSLSSS",  // N = 2 (LL and sentinel within 10 % of each other up to 32 KiB)
-    "SSLLLSTS",  // N = 3
-    "SSSLSSTT",  // N = 4
-    "SSSSSTTT",  // N = 8
-    "SSSSSTTT",  // N = 16
+constexpr char kAutoTable[3][5][9] = {
+    {
+        // fp32
+        "SSSSLSST",  // N = 2
+        "SSSSLSTT",  // N = 3
+        "SSSSSSTT",  // N = 4
+        "SSSSSTTT",  // N = 8
+        "SSSSSTTT",  // N = 16
+    },
+    {
+        // bf16
+        "SSSSLSST",  // N = 2
+        "SSSLLSTT",  // N = 3
+        "SSLLSSTT",  // N = 4
+        "SSSSSTTT",  // N = 8
+        "LLLLSTTT",  // N = 16
+    },
+    {
+        // int32
+        "SSLSLSSS",  // N = 2
+        "SSSSSSST",  // N = 3
+        "SSSSSSTT",  // N = 4
+        "SSSSSSTT",  // N = 8
+        "SSSSSAAA",  // N = 16
+    },
 };
 
 int resolve_algo(ar_handle* h, int algo, uint64_t nbytes) {
@@ -587,11 +624,12 @@ int resolve_algo(ar_handle* h, int algo, uint64_t nbytes) {
   int row = 0;
   while (row < 4 && kAutoN[row] < h->nranks) ++row;
   int col = 0;
-  while (col < 8 && kAutoBytes[col] < nbytes) ++col;
-  if (col == 8) return AR_TWOSHOT;
-  switch (kAutoTable[row][col]) {
+  while (col < 7 && kAutoBytes[col] < nbytes) ++col;
+  const int t = h->dtype == AR_BFLOAT16 ? 1 : h->dtype == AR_INT32 ? 2 : 0;
+  switch (kAutoTable[t][row][col]) {
     case 'L': return AR_ONESHOT_LL;
     case 'S': return AR_ONESHOT_SENTINEL;
+    case 'A': return AR_LL128_ATOMIC;
     default: return AR_TWOSHOT;
   }
 }

@@ -835,6 +835,9 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
 // lines) rather than one word of each of 64 units. E < 4 is used when the whole chunk is fewer
 // than 16 E units in one wave: the word slices that hold nothing are then not issued at all.
 
+// Most groups of the deterministic variant: groups of at least two ranks, at most 16 ranks.
+constexpr int kMaxDetGroups = kMaxRanks / 2;
+
 // Byte offset of group g's destination of buffer b in a rank block's `acc` region, laid out as
 // [buffer 2][group ceil(N / 2)][slot]; the plain atomic variant uses group 0.
 __device__ __forceinline__ uint32_t acc_off(const Args& a, uint32_t b, int g) {
@@ -965,7 +968,35 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
     // Deterministic: lane q watches owner q's ticket of this rank's group; every owner whose
     // ticket has reached this rank's place gets this rank's chunk of its partition, then its
     // ticket moves on. Owners become ready independently, so several may be served per round.
+    // The plan gives this variant one pass per chunk (every unit has its own lane's words), so
+    // the input words of every partition are loaded once, before the first round.
     if (has_units && r != a.withhold) {
+      uint32_t woff[E];
+      bool wact[E];
+      words(c.t0, woff, wact);
+      uint32_t w[NMAX][E];
+#pragma unroll
+      for (int j = 0; j < NMAX; ++j) {
+        int p = r + j;
+        if (p >= N) p -= N;
+        const uint32_t pbase = (p * P + k * CU) * 16u;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          w[j][e] = ld4<kPlain>(in_r, j < N && wact[e] ? pbase + woff[e] : kDrop);
+      }
+      if (odd_tail<DT>(a.nbytes)) {  // the half word past the last bf16 element reads as 0
+        asm volatile("");
+#pragma unroll
+        for (int j = 0; j < NMAX; ++j) {
+          int p = r + j;
+          if (p >= N) p -= N;
+          const uint32_t pbase = (p * P + k * CU) * 16u;
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            w[j][e] = pbase + woff[e] == (a.nbytes & ~3u) ? (w[j][e] & 0xFFFFu) : w[j][e];
+        }
+      }
+      const uint32_t goff = acc_off(a, b, gme);
       uint32_t todo = (N >= 32 ? 0xFFFFFFFFu : ((1u << N) - 1u));
       uint32_t spins = 0;
       uint64_t t_first = 0;
@@ -976,7 +1007,8 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
         if (watch)
           tv = __hip_atomic_load(det_ticket(a, q, b, gme, c), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t go = static_cast<uint32_t>(__ballot(watch && tv == static_cast<uint32_t>(mme)));
+        const uint32_t go =
+            static_cast<uint32_t>(__ballot(watch && tv == static_cast<uint32_t>(mme)));
         if (go == 0) {
           if ((++spins & 1023u) == 0) {
             t_first = poll_check(poll_env(a), t_first, r, __builtin_ctz(todo), s);
@@ -984,48 +1016,35 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
           }
           continue;
         }
-        for (uint32_t rest = go; rest != 0; rest &= rest - 1u) {
-          const int p = __builtin_ctz(rest);  // owner, wave-uniform
-          uint8_t* dst = a.base + static_cast<uint64_t>(p) * a.stride + a.acc.off +
-                         acc_off(a, b, gme);
-          const rsrc_t dst_r = make_rsrc(dst, a.acc.slot);
-          for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
-            uint32_t woff[E];
-            bool wact[E];
-            words(i0, woff, wact);
-            const uint32_t pbase = (p * P + k * CU) * 16u;
-            uint32_t w[E];
+        // every owner in `go` at once: branch-free, absent or waiting owners drop their accesses
 #pragma unroll
-            for (int e = 0; e < E; ++e) w[e] = ld4<kPlain>(in_r, wact[e] ? pbase + woff[e] : kDrop);
-            if (odd_tail<DT>(a.nbytes)) {  // the half word past the last bf16 element reads as 0
-              asm volatile("");
+        for (int j = 0; j < NMAX; ++j) {
+          int p = r + j;
+          if (p >= N) p -= N;
+          const bool live = j < N && ((go >> p) & 1u);
+          const rsrc_t dst = j == 0 ? region_rsrc(a, r, a.acc) : peer_rsrc(a, r, j, a.acc);
 #pragma unroll
-              for (int e = 0; e < E; ++e)
-                w[e] = pbase + woff[e] == (a.nbytes & ~3u) ? (w[e] & 0xFFFFu) : w[e];
+          for (int e = 0; e < E; ++e) {
+            // binary32 value(s) of the word: fp32 as is, bf16 widened (low element first)
+            float v0, v1 = 0.0f;
+            if constexpr (DT == DT_BF16) {
+              v0 = __uint_as_float(w[j][e] << 16);
+              v1 = __uint_as_float(w[j][e] & 0xFFFF0000u);
+            } else {
+              v0 = __uint_as_float(w[j][e]);
             }
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-              // binary32 value(s) of the word: fp32 as is, bf16 widened (low element first)
-              float v0, v1 = 0.0f;
-              if constexpr (DT == DT_BF16) {
-                v0 = __uint_as_float(w[e] << 16);
-                v1 = __uint_as_float(w[e] & 0xFFFF0000u);
-              } else {
-                v0 = __uint_as_float(w[e]);
-              }
-              const uint32_t off = wact[e] ? woff[e] * kAW : kDrop;
-              if (mme == 0) {
-                // the group's first member writes: the destination then holds exactly its values
-                if constexpr (kAW == 2)
-                  st8<kCoh>(dst_r, off, u32x2{__float_as_uint(v0), __float_as_uint(v1)});
-                else
-                  st4<kCoh>(dst_r, off, __float_as_uint(v0));
-              } else {
-                (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v0, dst_r, off, 0, 0);
-                if constexpr (kAW == 2)
-                  (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
-                      v1, dst_r, wact[e] ? off + 4u : kDrop, 0, 0);
-              }
+            const uint32_t off = live && wact[e] ? goff + woff[e] * kAW : kDrop;
+            if (mme == 0) {
+              // the group's first member writes: the destination then holds exactly its values
+              if constexpr (kAW == 2)
+                st8<kCoh>(dst, off, u32x2{__float_as_uint(v0), __float_as_uint(v1)});
+              else
+                st4<kCoh>(dst, off, __float_as_uint(v0));
+            } else {
+              (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v0, dst, off, 0, 0);
+              if constexpr (kAW == 2)
+                (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                    v1, dst, off == kDrop ? kDrop : off + 4u, 0, 0);
             }
           }
         }
@@ -1083,22 +1102,35 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
           v = u32x4{static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
                     static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
         } else {
-          // group sums in group order: 4 (fp32) or 8 (bf16) binary32 values per unit
+          // Group sums in group order: 4 (fp32) or 8 (bf16) binary32 values per unit. Every
+          // member's adds were performed before its ticket moved, so coherent loads read the
+          // final sums; all groups' loads are in flight at once (groups beyond G drop theirs),
+          // then the destinations are cleared with coherent stores for the plain variant, which
+          // expects zeros.
           constexpr int V = 4 * static_cast<int>(kAW);
-          float sum[V];
-          for (int g = 0; g < G; ++g) {
-            uint64_t* q = reinterpret_cast<uint64_t*>(acc + acc_off(a, b, g) +
-                                                      static_cast<uint64_t>(i) * 16u * kAW);
+          const rsrc_t accr = region_rsrc(a, r, a.acc);
+          u32x4 gs[kMaxDetGroups][kAW];
 #pragma unroll
-            for (int h = 0; h < V / 2; ++h) {
-              const uint64_t x =
-                  __hip_atomic_exchange(q + h, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              const float lo = __uint_as_float(static_cast<uint32_t>(x));
-              const float hi = __uint_as_float(static_cast<uint32_t>(x >> 32));
-              sum[2 * h] = g == 0 ? lo : sum[2 * h] + lo;
-              sum[2 * h + 1] = g == 0 ? hi : sum[2 * h + 1] + hi;
+          for (int g = 0; g < kMaxDetGroups; ++g)
+#pragma unroll
+            for (uint32_t h = 0; h < kAW; ++h)
+              gs[g][h] = ld16<kCoh>(accr, g < G ? acc_off(a, b, g) + i * 16u * kAW + h * 16u
+                                               : kDrop);
+          float sum[V];
+#pragma unroll
+          for (int g = 0; g < kMaxDetGroups; ++g) {
+#pragma unroll
+            for (int t = 0; t < V; ++t) {
+              const float x = __uint_as_float(gs[g][t / 4][t % 4]);
+              sum[t] = g == 0 ? x : (g < G ? sum[t] + x : sum[t]);
             }
           }
+#pragma unroll
+          for (int g = 0; g < kMaxDetGroups; ++g)
+#pragma unroll
+            for (uint32_t h = 0; h < kAW; ++h)
+              st16<kCoh>(accr, g < G ? acc_off(a, b, g) + i * 16u * kAW + h * 16u : kDrop,
+                         u32x4{0u, 0u, 0u, 0u});
           if constexpr (DT == DT_BF16) {
             v = u32x4{bf16x2_rne(sum[0], sum[1]), bf16x2_rne(sum[2], sum[3]),
                       bf16x2_rne(sum[4], sum[5]), bf16x2_rne(sum[6], sum[7])};
@@ -1120,7 +1152,7 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
     if constexpr (!DET) {
       if (c.lane == 0) __hip_atomic_store(my_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      // the exchanges have returned (their values were used above): the destinations are clear
+      wait_all_mem();  // the destinations are clear before the tickets are reset
       if (c.lane < G)
         __hip_atomic_store(det_ticket(a, r, b, c.lane, c), 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);

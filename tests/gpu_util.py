@@ -14,7 +14,7 @@ from latency_collectives_amd import inputs as I
 ALGO_NAMES = ["oneshot_ll", "oneshot_sentinel", "twoshot", "ll128_atomic", "barrier2",
               "ll128_det"]
 FIXED_ORDER = {"oneshot_ll", "oneshot_sentinel", "twoshot", "barrier2"}
-DET_GROUP = 4  # the deterministic LL128-style variant's default ranks per group
+DET_GROUP = 2  # the deterministic LL128-style variant's default ranks per group
 
 
 def torch_mod():

@@ -58,14 +58,30 @@ def test_sentinel_kernels_both_unit_widths(n, dtype):
                 f"{algo} count={count}: 8-byte and 16-byte units differ"
 
 
-def test_auto_selection_matches_oracle():
-    """AR_ALGO_AUTO over rank counts and sizes that select each of its three kernels."""
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+def test_auto_selection_matches_oracle(dtype):
+    """AR_ALGO_AUTO over rank counts and sizes that select each of its kernels, for every dtype.
+    fp32 and bf16 must stay bit-exact with the rank-order oracle (AUTO only picks fixed-order
+    kernels for floats: never an LL128-style one); int32 may also pick the LL128-style kernel
+    (an exact integer sum) and is bit-exact as well."""
+    from latency_collectives_amd import _ar as A
+
+    fixed = {1, 2, 3, 7, 8, 9, 10, 11}  # LL, sentinel, two-shot and their internal kernels
+    seen = set()
+    eb = elem_bytes(dtype)
     for n in (2, 3, 4, 6, 8, 16):
-        for count in (32, 700, 5000, 40000, 300000):
-            with handle(n, count * 4, "f32") as h:
-                x = draw("f32", n, count, seed=n * 7 + count % 97)
+        for nbytes in (128, 2800, 20000, 160000, 600000, 3 << 20):
+            count = nbytes // eb
+            with handle(n, count * eb, dtype) as h:
+                plan = A.ar_plan_info(h, count, A.AR_ALGO_AUTO)
+                seen.add(plan["kernel"])
+                if dtype != "i32":
+                    assert plan["kernel"] in fixed, plan
+                x = draw(dtype, n, count, seed=n * 7 + count % 97)
                 got = run_allreduce(h, x, "auto")
-                assert_matches(got, x, "oneshot_ll", "f32")
+                assert_matches(got, x, "oneshot_ll", dtype)
+    _say(f"auto {dtype}: kernel families {sorted(seen)}")
+    assert len(seen) >= 3
 
 
 @pytest.mark.parametrize("algo", ALGO_NAMES)
