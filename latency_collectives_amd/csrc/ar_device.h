@@ -146,9 +146,10 @@ template <>
 struct Ty<DT_BF16> {
   static constexpr int kElem = 2;
   static constexpr uint32_t kSentinelWord = 0xFFFFFFFFu;  // two bf16 negative quiet NaNs
-  __device__ static bool word_clear(uint32_t w) {
-    return ((w & 0xFFFFu) != 0xFFFFu) & (w < 0xFFFF0000u);
-  }
+  // A naturally aligned 32-bit word is written as a whole (single-copy atomic), so a slot word
+  // holds either both sentinels or two transmitted elements, neither of which may be the
+  // sentinel: comparing the word with two sentinels is the per-element test.
+  __device__ static bool word_clear(uint32_t w) { return w != 0xFFFFFFFFu; }
 };
 template <>
 struct Ty<DT_I32> {

@@ -267,22 +267,24 @@ __device__ __forceinline__ bool poll_lines(const Args& a, rsrc_t own, uint32_t o
 }
 
 // Fold the N sources of one unit in rank order 0..N-1; the rank's own value is `x`. The first W
-// words of each v[q] are payload.
+// words of each v[q] are payload. Sources q >= N (the kernel is built for NMAX >= N ranks) add
+// the additive identity of the fold, -0.0 for binary32 (x + -0.0 is x for every x, +0 and -0
+// included) and 0 for int32, so the fold needs no branch on the run-time rank count.
 template <int DT, int NMAX, int W, class V>
 __device__ __forceinline__ void fold_rank_order(int N, int r, const uint32_t* x,
                                                 const V (&v)[NMAX], uint32_t* o) {
+  // identity word: two bf16 -0.0 (each widens to binary32 -0.0), one binary32 -0.0, int32 0
+  constexpr uint32_t kId = DT == DT_I32 ? 0u : DT == DT_BF16 ? 0x80008000u : 0x80000000u;
   Fold<DT, W> f;
 #pragma unroll
   for (int q = 0; q < NMAX; ++q) {
-    if (q < N) {
-      uint32_t src[W];
+    uint32_t src[W];
 #pragma unroll
-      for (int i = 0; i < W; ++i) src[i] = (q == r) ? x[i] : v[q][i];
-      if (q == 0)
-        f.init(src);
-      else
-        f.add(src);
-    }
+    for (int i = 0; i < W; ++i) src[i] = (q == r) ? x[i] : (q < N ? v[q][i] : kId);
+    if (q == 0)
+      f.init(src);
+    else
+      f.add(src);
   }
   f.pack(o);
 }
@@ -459,10 +461,15 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
     // one round of polls at a time: with a second round in flight the sentinel path measured
     // slower (the exit then waits for the other round's loads)
     if (!poll_all<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
-    finish(i, act, x, v, off0);
+    uint32_t o[W];
+    fold_rank_order<DT, NMAX, W>(N, r, x, v, o);
+    store_unit<DT, UB>(out_r, act ? (unit0 + i) * UB : kDrop, a.nbytes, o);
     compiler_fence();
-    wait_vm<NMAX>();  // the output store(s) have landed; the NMAX re-arm stores may be in flight
+    wait_vm<0>();  // the output has landed: the AllReduce is complete for this lane
     t1 = now_ticks();
+    // Re-arm the slots for step s + 2 after the output: the next step's first push waits for
+    // these stores, and the credit chain only needs them before that push.
+    rearm<NMAX>(own, off0, slot, act ? peers : 0u, sent);
     return true;
   } else {
     stamp_start(t0, k);
@@ -531,21 +538,42 @@ __device__ __forceinline__ void load_partitions(const Args& a, int r, rsrc_t in_
   }
 }
 
+// Store the reduced unit i of every owner in `mask` (already in v[]) into the output; an odd bf16
+// tail is written after all of them, behind one branch.
+template <int DT, int NMAX, int UB = 16>
+__device__ __forceinline__ void allgather_store(const Args& a, rsrc_t out_r, uint32_t mask, int k,
+                                                uint32_t i, const unit_t<UB> (&v)[NMAX]) {
+  const uint32_t CU = a.chunk_units, P = a.part_units;
+#pragma unroll
+  for (int p = 0; p < NMAX; ++p) {
+    const uint32_t off = ((mask >> p) & 1u) ? (p * P + k * CU + i) * UB : kDrop;
+    if constexpr (UB == 16)
+      st16<kPlain>(out_r, off, v[p]);
+    else
+      st8<kPlain>(out_r, off, v[p]);
+  }
+  if (odd_tail<DT>(a.out_nbytes)) {
+    asm volatile("");
+    const uint32_t last = a.out_nbytes & ~3u;
+#pragma unroll
+    for (int p = 0; p < NMAX; ++p) {
+      const uint32_t off = (p * P + k * CU + i) * UB;
+      const bool tail = ((mask >> p) & 1u) && off <= last && last < off + UB;
+      uint32_t word = v[p][0];
+#pragma unroll
+      for (int e = 1; e < UB / 4; ++e) word = (off + 4u * e == last) ? v[p][e] : word;
+      st2<kPlain>(out_r, tail ? last : kDrop, static_cast<uint16_t>(word & 0xFFFFu));
+    }
+  }
+}
+
 // All-gather receive of unit i: the reduced unit of every other owner, already polled into v[],
 // is copied to `out` and its slot re-armed.
 template <int DT, int NMAX, int UB = 16>
 __device__ __forceinline__ void allgather_out(const Args& a, int r, rsrc_t out_r, rsrc_t own2,
                                               uint32_t off0, uint32_t mask, int k, uint32_t i,
                                               const unit_t<UB> (&v)[NMAX], unit_t<UB> sent) {
-  const uint32_t CU = a.chunk_units, P = a.part_units;
-#pragma unroll
-  for (int p = 0; p < NMAX; ++p) {
-    uint32_t o[UB / 4];
-#pragma unroll
-    for (int e = 0; e < UB / 4; ++e) o[e] = v[p][e];
-    store_unit<DT, UB>(out_r, ((mask >> p) & 1u) ? (p * P + k * CU + i) * UB : kDrop,
-                       a.out_nbytes, o);
-  }
+  allgather_store<DT, NMAX, UB>(a, out_r, mask, k, i, v);
   rearm<NMAX>(own2, off0, a.p2.slot, mask, sent);
 }
 
@@ -620,10 +648,18 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
         push_peers<NMAX>(a, r, a.p2, act ? mine2 + slot_off<UB>(a.p2, i) : kDrop, line);
       }
       store_unit<DT, UB>(out_r, act ? uoff : kDrop, a.out_nbytes, o);
-      if constexpr (MODE == 0) rearm<NMAX>(own1, off1, slot1, mask, sent);
       V v2[NMAX];
       if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
-      allgather_out<DT, NMAX, UB>(a, r, out_r, own2, off2, mask, k, i, v2, sent);
+      // every other owner's reduced unit into the output
+      allgather_store<DT, NMAX, UB>(a, out_r, mask, k, i, v2);
+      compiler_fence();
+      wait_vm<0>();  // every output store has landed: the AllReduce is complete for this lane
+      t1 = now_ticks();
+      // Re-arm both phases' slots for step s + 2 after the outputs: the next step's first push
+      // waits for these stores, and the credit chain only needs them before that push.
+      if constexpr (MODE == 0) rearm<NMAX>(own1, off1, slot1, mask, sent);
+      rearm<NMAX>(own2, off2, slot2, mask, sent);
+      return true;
     }
     compiler_fence();
     wait_vm<NMAX>();  // every output store has landed; the NMAX re-arm stores may be in flight
@@ -1187,6 +1223,16 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
                            a.nbytes, o);
       }
     }
+  } else if (CU <= c.T) {
+    // one pass (every unit has its own lane): one round of loads for all sources at a time, as
+    // in the one-pass two-shot
+    const uint32_t i = c.t0 + c.lane;
+    const bool act = i < CU;
+    const uint32_t mask = act ? peers : 0u;
+    const uint32_t off2 = b * N * slot2 + slot_off(a.p2, i);
+    u32x4 v[NMAX];
+    if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v, ready, r, s)) return false;
+    allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v, sent);
   } else {
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
       const uint32_t i = i0 + c.lane;

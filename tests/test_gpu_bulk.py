@@ -118,9 +118,10 @@ def test_bulk_twoshot_persistent_loop(drift):
 # ------------------------------------------------------------------ full workload sizes
 
 
-def _bench_sets(h, xs, algo, dtype):
-    """Run the sets xs[k] ([N, count] each) through one persistent launch, as the benchmark
-    does (evenly spaced sets of one buffer per rank), and check every set."""
+def _bench_sets(h, xs, algo, dtype, iters=None):
+    """Run the sets xs[k] ([N, count] each) through one persistent launch of `iters` AllReduces
+    (default two per set), as the benchmark does (evenly spaced sets of one buffer per rank),
+    and check every set."""
     from latency_collectives_amd import _ar as A
     import torch
 
@@ -131,7 +132,7 @@ def _bench_sets(h, xs, algo, dtype):
     obig = [torch.empty_like(b) for b in big]
     ins = [big[r][k] for k in range(len(xs)) for r in range(n)]
     outs = [obig[r][k] for k in range(len(xs)) for r in range(n)]
-    A.ar_bench(h, ins, outs, len(xs), count, A.ALGOS[algo], 2 * len(xs))
+    A.ar_bench(h, ins, outs, len(xs), count, A.ALGOS[algo], iters or 2 * len(xs))
     for k, x in enumerate(xs):
         got = np.stack([obig[r][k].cpu().numpy().view(x.dtype) for r in range(n)])
         assert_matches(got, x, algo, dtype)
@@ -147,6 +148,32 @@ def test_full_size_c2_oneshot_sentinel():
             _say(f"case c2 size={size}")
             xs = [I.rank_inputs("normal", "bf16", 4, size // 2, 2, si, k) for k in range(3)]
             _bench_sets(h, xs, "oneshot_sentinel", "bf16")
+
+
+def test_c2_persistent_loop_at_full_iteration_count():
+    """The headline configuration's 200 back-to-back iterations in one launch (40 fresh input
+    sets, each used five times), every set's output checked, at the smallest, a middle and the
+    largest size."""
+    from latency_collectives_amd import inputs as I
+
+    with handle(4, 1 << 18, "bf16") as h:
+        for si, size in ((0, 1 << 10), (4, 1 << 14), (8, 1 << 18)):
+            _say(f"case c2 200 iterations size={size}")
+            xs = [I.rank_inputs("normal", "bf16", 4, size // 2, 2, si, k) for k in range(40)]
+            _bench_sets(h, xs, "oneshot_sentinel", "bf16", iters=200)
+
+
+def test_c3_persistent_loop_at_full_iteration_count():
+    """The decode configuration's 100 back-to-back two-shot iterations (20 fresh sets, each used
+    five times), every set checked, at 1, 8 and 64 tokens."""
+    from latency_collectives_amd import inputs as I
+
+    with handle(8, 64 * 8192 * 2, "bf16") as h:
+        for si, tokens in ((0, 1), (3, 8), (6, 64)):
+            size = tokens * 8192 * 2
+            _say(f"case c3 100 iterations tokens={tokens}")
+            xs = [I.rank_inputs("normal", "bf16", 8, size // 2, 3, si, k, 0.5) for k in range(20)]
+            _bench_sets(h, xs, "twoshot", "bf16", iters=100)
 
 
 def test_full_size_c3_twoshot():
@@ -188,10 +215,10 @@ def _device_check(outs, want: np.ndarray):
     assert bad.size == 0, f"mismatch at {bad[:8]}: got {got[bad[:8]]} want {want[bad[:8]]}"
 
 
-@pytest.mark.parametrize("size_mib", [16, 256])
+@pytest.mark.parametrize("size_mib", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("dtype", ["i32", "f32"])
 def test_full_size_c5_twoshot(dtype, size_mib):
-    """8 ranks, 16 MiB and 256 MiB per rank, two-shot in the benchmark's launch shape: int32
+    """8 ranks, 16 .. 256 MiB per rank, two-shot in the benchmark's launch shape: int32
     uniform in [-2^20, 2^20] and fp32 uniform[-1,1], every element against the oracle."""
     from latency_collectives_amd import _ar as A
     from latency_collectives_amd import inputs as I
