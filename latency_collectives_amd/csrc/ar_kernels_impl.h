@@ -611,7 +611,21 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
     uint32_t off1 = b * N * slot1 + slot_off<UB>(a.p1, i);
     const uint32_t off2 = b * N * slot2 + slot_off<UB>(a.p2, i);
     const uint32_t uoff = (r * P + k * CU + i) * UB;
+    // Address arithmetic of the step before its start stamp: the input offset of unit i in the
+    // partition of the j-th rank after r, and the push offsets of both phases.
+    uint32_t in_off[NMAX];
+#pragma unroll
+    for (int j = 0; j < NMAX; ++j) {
+      int p = r + j;
+      if (p >= N) p -= N;
+      in_off[j] = act && j < N ? (p * P + k * CU + i) * UB : kDrop;
+      pin(in_off[j]);
+    }
+    uint32_t push1 = act ? mine1 + slot_off<UB>(a.p1, i) : kDrop;
+    uint32_t push2 = act ? mine2 + slot_off<UB>(a.p2, i) : kDrop;
     pin(off1);
+    pin(push1);
+    pin(push2);
     stamp_start(t0, k);
     uint32_t o[W];
     if constexpr (MODE == 2) {
@@ -620,11 +634,19 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
       wait_vm<0>();
     } else {
       uint32_t w[NMAX][W];
-      load_partitions<DT, NMAX, kPlain, UB>(a, r, in_r, k, i, act, 0, w);  // w[0]: own partition
+#pragma unroll
+      for (int j = 0; j < NMAX; ++j)
+        load_unit<DT, UB, kPlain, false>(in_r, in_off[j], a.nbytes, w[j]);  // w[0]: own partition
+      // all loads are in flight before the one scalar branch for an odd bf16 tail
+      if (odd_tail<DT>(a.nbytes)) {
+        asm volatile("");
+#pragma unroll
+        for (int j = 0; j < NMAX; ++j) clear_odd_tail<UB>(in_off[j], a.nbytes, w[j]);
+      }
       compiler_fence();
       wait_vm<0>();
       if (sends) {
-        const uint32_t off = act ? mine1 + slot_off<UB>(a.p1, i) : kDrop;
+        const uint32_t off = push1;
 #pragma unroll
         for (int j = 1; j < NMAX; ++j) {
           V line;
@@ -645,7 +667,7 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
         V line;
 #pragma unroll
         for (int e = 0; e < W; ++e) line[e] = o[e];
-        push_peers<NMAX>(a, r, a.p2, act ? mine2 + slot_off<UB>(a.p2, i) : kDrop, line);
+        push_peers<NMAX>(a, r, a.p2, push2, line);
       }
       store_unit<DT, UB>(out_r, act ? uoff : kDrop, a.out_nbytes, o);
       V v2[NMAX];
