@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the barrier-free AllReduce on one MI355X with emulated ranks.
 
-    python bench.py [--steps K] [--warmup W] [--configs C1,C2,...] [--report out.json]
+    python bench.py [--steps K] [--warmup W] [--configs 1,2,3,4,5] [--report out.json]
 
 A step is one AllReduce of every message size of every configuration below (all five are
 measured in the default run); K steps run back to back inside one persistent launch per
@@ -10,17 +10,23 @@ memory. Per iteration k the latency is max_r t_end[r][k] - max_r t_start[r][k] o
 wall clock (from the moment the last rank enters until the last rank has completed its last
 output store).
 
-    C1  2 ranks, fp32, 128 B, one-shot LL (also the one-shot sentinel and the two-barrier baseline)
-    C2  4 ranks, bf16, 1 KiB - 256 KiB, one-shot sentinel + double buffering   <- `value`
-    C3  8 ranks, bf16, [tokens, 8192] for tokens 1..64 (16 KiB - 1 MiB), two-shot (and one-shot)
-    C4  16 ranks, fp32, 4 KiB - 4 MiB, LL128-style atomic vs one-shot LL vs two-barrier baseline
-    C5  8 ranks, int32 and fp32, 16 - 256 MiB, two-shot (bandwidth regime: algBW = S / p50)
+    1  oneshot_ll_n2_f32_128B: 2 ranks, fp32, 128 B, one-shot LL (also the one-shot sentinel and
+       the two-barrier baseline)
+    2  oneshot_sentinel_n4_bf16_1K-256K: 4 ranks, bf16, 1 KiB - 256 KiB, one-shot sentinel +
+       double buffering                                                   <- `value`
+    3  twoshot_n8_bf16_tp_decode_8192: 8 ranks, bf16, [tokens, 8192] for tokens 1..64
+       (16 KiB - 1 MiB), two-shot (and the one-shot for comparison)
+    4  ll128_vs_oneshot_vs_barrier_n16_f32_4K-4M: 16 ranks, fp32, 4 KiB - 4 MiB, LL128-style
+       atomic vs one-shot LL vs two-barrier baseline
+    5  twoshot_n8_bandwidth_16M-256M: 8 ranks, int32 and fp32, 16 - 256 MiB, two-shot (bandwidth
+       regime: algBW = S / p50)
 
-The JSON line's `value` is the geometric mean of C2's per-size p50; `configs` holds every
-configuration's per-size p50 / p99, its latency roofline (p50 against the on-chip floor
-2 * L_L2 + L_store of the slowest XCD pair the configuration uses, plus its algorithmic bytes at
-8 TB/s) or, for C5, its HBM roofline; `roofline` is the headline kernel's. The CPU oracle is
-timed on a bounded sample of C2 (`cpu_baseline`).
+The JSON line's `value` is the geometric mean of the 4-rank bf16 workload's per-size p50;
+`configs` holds every workload's per-size p50 / p99, its latency roofline (p50 against the
+on-chip floor 2 * L_L2 + L_store of the slowest XCD pair the workload uses, plus its algorithmic
+bytes at 8 TB/s) or, for the bandwidth workload, its HBM roofline; `roofline` is the headline
+kernel's. The CPU oracle is timed on a bounded sample of the headline workload
+(`cpu_baseline`).
 
 Only one GPU is used: ranks are emulated on it. ``--gpus`` above 1 is refused.
 """
@@ -43,15 +49,17 @@ if ROOT not in sys.path:
 METRIC = "p50 AllReduce latency µs @128B–1MB; algBW GB/s @≥16MB (1 GPU)"
 HBM_PEAK_GBPS = 8000.0
 
-# Configuration -> (workload id in inputs.WORKLOADS, algorithms measured, extra dtypes). The first
-# algorithm is the one the configuration names; the others run at the same sizes for comparison.
+# Workload id in inputs.WORKLOADS -> (algorithms measured, extra dtypes). The first algorithm is
+# the one the workload names; the others run at the same sizes for comparison.
 CONFIGS = {
-    "C1": (1, ["oneshot_ll", "oneshot_sentinel", "barrier2"], []),
-    "C2": (2, ["oneshot_sentinel", "barrier2"], []),
-    "C3": (3, ["twoshot", "oneshot_sentinel"], []),
-    "C4": (4, ["ll128_atomic", "oneshot_ll", "barrier2"], []),
-    "C5": (5, ["twoshot"], ["f32"]),
+    1: (["oneshot_ll", "oneshot_sentinel", "barrier2"], []),
+    2: (["oneshot_sentinel", "barrier2"], []),
+    3: (["twoshot", "oneshot_sentinel"], []),
+    4: (["ll128_atomic", "oneshot_ll", "barrier2"], []),
+    5: (["twoshot"], ["f32"]),
 }
+HEADLINE = 2  # `value`: the 4-rank bf16 one-shot sentinel workload
+BANDWIDTH = 5  # reported against the HBM roofline
 
 # Kernel dispatches of the AllReduce kernels made so far by this process (ar_bench and every
 # ar_allreduce / collective call is one dispatch): lets a rocprofv3 trace be matched to the
@@ -251,8 +259,8 @@ def traffic_table() -> dict:
     return _TRAFFIC["t"]
 
 
-def traffic_key(cfg: str, algo: str, dtype: str, n: int, size: int) -> str:
-    return f"{cfg}:{algo}:{dtype}:n{n}:{size}"
+def traffic_key(workload: str, algo: str, dtype: str, n: int, size: int) -> str:
+    return f"{workload}:{algo}:{dtype}:n{n}:{size}"
 
 
 def measured_traffic(cfg: str, algo: str, dtype: str, n: int, rows: list):
@@ -420,10 +428,11 @@ def floors(A, placement: int) -> dict:
     return out
 
 
-def run_config(A, I, cfg: str, steps, warmup: int, hz: float, placement: int, fl: dict,
+def run_config(A, I, wid: int, steps, warmup: int, hz: float, placement: int, fl: dict,
                copy_gbps: float, algos=None) -> dict:
-    wid, names, extra_dtypes = CONFIGS[cfg]
+    names, extra_dtypes = CONFIGS[wid]
     wl0 = I.WORKLOADS[wid]
+    cfg = wl0["name"]
     n = wl0["nranks"]
     floor = fl["by_nranks"][max(2, n)]["floor_us"] if n > 1 else fl["floor_nearest_us"]
     rec = {"workload": wl0["name"], "nranks": n, "algos": {}, "floor_us": floor,
@@ -438,7 +447,7 @@ def run_config(A, I, cfg: str, steps, warmup: int, hz: float, placement: int, fl
                    "p50_gm_us": _gm([r["p50_us"] for r in rows]),
                    "per_size": _round_rows(rows)}
             tr = measured_traffic(cfg, algo, dtype, n, rows)
-            if cfg == "C5":
+            if wid == BANDWIDTH:
                 rl = hbm_roofline(rows, copy_gbps)
                 rl["traffic"] = tr
                 ent["algbw_GBps"] = [round(r["algbw_GBps"], 2) for r in rows]
@@ -460,8 +469,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=None,
                     help="timed iterations per size (default: each configuration's own count)")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="C1,C2,C3,C4,C5",
-                    help="comma-separated configurations to measure beside the headline C2")
+    ap.add_argument("--configs", default="1,2,3,4,5",
+                    help="comma-separated workload ids to measure beside the headline (2)")
     ap.add_argument("--workload", type=int, default=None, choices=sorted(range(1, 9)),
                     help="measure this workload alone (with --algo) instead of the configurations")
     ap.add_argument("--algo", default=None)
@@ -544,17 +553,18 @@ def main() -> int:
                           "per_size": _round_rows(rows)}), flush=True)
         return 0
 
-    # the headline: C2, then every other configuration
-    wanted = [c for c in args.configs.split(",") if c]
-    configs = {"C2": run_config(A, I, "C2", args.steps, args.warmup, hz, args.placement, fl,
-                                peak["GBps"])}
-    for cfg in wanted:
-        if cfg != "C2":
-            configs[cfg] = run_config(A, I, cfg, args.steps, args.warmup, hz, args.placement, fl,
-                                      peak["GBps"])
-    head = configs["C2"]["algos"]["oneshot_sentinel"]
+    # the headline workload, then every other one
+    wanted = [int(c) for c in args.configs.split(",") if c]
+    hname = I.WORKLOADS[HEADLINE]["name"]
+    configs = {hname: run_config(A, I, HEADLINE, args.steps, args.warmup, hz, args.placement, fl,
+                                 peak["GBps"])}
+    for wid in wanted:
+        if wid != HEADLINE:
+            configs[I.WORKLOADS[wid]["name"]] = run_config(A, I, wid, args.steps, args.warmup, hz,
+                                                           args.placement, fl, peak["GBps"])
+    head = configs[hname]["algos"]["oneshot_sentinel"]
     rows = head["per_size"]
-    wl = I.WORKLOADS[2]
+    wl = I.WORKLOADS[HEADLINE]
     iters = head["iters"]
     value = head["p50_gm_us"]
     # one step = one AllReduce of every size of every configuration measured
@@ -584,10 +594,11 @@ def main() -> int:
             "placement": ["rank per XCD", "all ranks on one XCD"][args.placement],
             "sizes_bytes": wl["sizes"],
         },
-        "value_definition": ("geometric mean over C2's message sizes of the per-size p50 "
-                             "latency (device wall clock, last rank in to last rank out)"),
+        "value_definition": ("geometric mean over the headline workload's message sizes of the "
+                             "per-size p50 latency (device wall clock, last rank in to last rank "
+                             "out)"),
         "latency_floor": {
-            "floor_us": configs["C2"]["floor_us"],
+            "floor_us": configs[hname]["floor_us"],
             "floor_nearest_us": fl["floor_nearest_us"],
             "formula": ("2*L_L2 + L_store (dependent-load L2 latency; store->poll half round "
                         "trip); floor_us on the slowest XCD pair of the 4-rank placement, "
@@ -596,24 +607,24 @@ def main() -> int:
             "store_half_rtt_ns": fl["sol"]["store_half_rtt_ns"],
             "fence_ns": fl["sol"]["fence_ns"],
             "by_nranks": fl["by_nranks"],
-            "p50_smallest_over_floor": head["p50_us"][0] / configs["C2"]["floor_us"],
+            "p50_smallest_over_floor": head["p50_us"][0] / configs[hname]["floor_us"],
             "p50_smallest_over_floor_nearest": head["p50_us"][0] / fl["floor_nearest_us"],
         },
         "roofline": roof,
         "barrier_baseline": {
             "algo": "barrier2",
-            "value": configs["C2"]["algos"]["barrier2"]["p50_gm_us"],
+            "value": configs[hname]["algos"]["barrier2"]["p50_gm_us"],
             "unit": "us",
-            "p50_us": configs["C2"]["algos"]["barrier2"]["p50_us"],
+            "p50_us": configs[hname]["algos"]["barrier2"]["p50_us"],
         },
         "configs": {c: _summary(rec) for c, rec in configs.items()},
         "copy_peak_GBps": peak["GBps"],
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(I, 2, wl)
+        line["cpu_baseline"] = cpu_baseline(I, HEADLINE, wl)
         # the machine's CPU share is 16 cores whatever os.cpu_count() reports
         line["cpu_baseline"]["multi_thread"] = cpu_baseline_threads(
-            I, 2, wl, max(1, min(16, os.cpu_count() or 1)))
+            I, HEADLINE, wl, max(1, min(16, os.cpu_count() or 1)))
     report = {"main": line, "configs": configs, "floors": fl}
     if args.all:
         report["collectives"] = run_collectives(A, I, hz, args.warmup, args.placement)
