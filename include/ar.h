@@ -274,6 +274,11 @@ double ar_wallclock_hz(void);
  *                        [0]
  *   AR_OPT_GROUP         AR_LL128_DET: ranks per group, 2..16; the result depends on it (it is
  *                        the summation order) [2]
+ *   AR_OPT_COOPERATIVE   1: kernels are started with the cooperative launch, which makes the
+ *                        runtime check that the whole grid can be resident at once (every
+ *                        workgroup waits for others, Every µs Matters §II.B) and refuse it
+ *                        otherwise (AR_ENORES) instead of starting part of it; no grid-wide
+ *                        synchronisation is used. Costs launch time, not device time [0]
  */
 typedef enum {
   AR_OPT_TIMEOUT_US = 0,
@@ -286,7 +291,8 @@ typedef enum {
   AR_OPT_ROOT = 7,
   AR_OPT_CHECK_INPUTS = 8,
   AR_OPT_RECORD_LAUNCH = 9,
-  AR_OPT_GROUP = 10
+  AR_OPT_GROUP = 10,
+  AR_OPT_COOPERATIVE = 11
 } ar_option;
 int ar_set_option(ar_handle* h, ar_option opt, int64_t value);
 
@@ -342,6 +348,10 @@ typedef struct {
                      once */
   int unit_bytes; /* payload bytes per lane and unit: 16, or 8 for LL and the 8-byte kernels */
   int near;       /* 1 when the slots are in the near regions */
+  int resident_per_cu; /* workgroups of this kernel and block size that one compute unit holds at
+                          once (the HIP occupancy query); the plan leaves one of them free per
+                          compute unit whenever this is above 1 */
+  int cu_count;   /* compute units of the device (8 XCDs share them equally) */
 } ar_plan;
 int ar_plan_info(ar_handle* h, size_t count, ar_algo algo, ar_plan* info);
 int ar_read_region(ar_handle* h, int rank, int region, void* host_dst, size_t bytes);

@@ -209,6 +209,7 @@ struct ar_handle {
   int group = 2;          // deterministic LL128-style variant: ranks per group
   int check_inputs = 0;   // check every call's inputs against the sentinel before launching
   int record_launch = 0;  // kernels write the launch record (region RG_REC of rank 0)
+  int cooperative = 0;    // launches go through the cooperative launch (residency checked)
   void** tab = nullptr;
   size_t tab_cap = 0;
   uint64_t* ts = nullptr;
@@ -733,10 +734,21 @@ int check_inputs(ar_handle* h, const void* const in[], uint64_t nbytes, int root
   return AR_OK;
 }
 
-int launch(ar_kernel_fn fn, unsigned grid, int threads, ar::Args& a, hipStream_t stream) {
+// A cooperative launch (AR_OPT_COOPERATIVE) has the runtime refuse a grid that it cannot make
+// resident at once, instead of starting part of it; the kernels use no grid-wide sync.
+int launch(ar_kernel_fn fn, unsigned grid, int threads, ar::Args& a, hipStream_t stream,
+           bool cooperative) {
   void* args[] = {&a};
-  AR_HIP(hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(threads), args, 0,
-                         stream));
+  const void* f = reinterpret_cast<const void*>(fn);
+  if (cooperative) {
+    const hipError_t e = hipLaunchCooperativeKernel(f, dim3(grid), dim3(threads), args, 0, stream);
+    if (e == hipErrorCooperativeLaunchTooLarge)
+      return ar_fail(AR_ENORES, "the runtime cannot make %u workgroups of %d threads resident",
+                     grid, threads);
+    AR_HIP(e);
+    return AR_OK;
+  }
+  AR_HIP(hipLaunchKernel(f, dim3(grid), dim3(threads), args, 0, stream));
   return AR_OK;
 }
 
@@ -798,7 +810,7 @@ int allreduce_enqueue(ar_handle* h, const void* const in[], void* const out[], s
     a.in[r] = in[r];
     a.out[r] = out[r];
   }
-  rc = launch(L.fn, L.grid, L.threads, a, s);
+  rc = launch(L.fn, L.grid, L.threads, a, s, h->cooperative != 0);
   if (rc != AR_OK) return rc;
   h->epoch += static_cast<uint64_t>(L.chunks);
   h->last_stream = s;
@@ -942,6 +954,10 @@ int ar_set_option(ar_handle* h, ar_option opt, int64_t v) {
       if (v < 2 || v > ar::kMaxRanks) return ar_fail(AR_EINVAL, "group must be in [2, 16]");
       h->group = static_cast<int>(v);
       return AR_OK;
+    case AR_OPT_COOPERATIVE:
+      if (v != 0 && v != 1) return ar_fail(AR_EINVAL, "cooperative must be 0 or 1");
+      h->cooperative = static_cast<int>(v);
+      return AR_OK;
   }
   return ar_fail(AR_EINVAL, "unknown option %d", static_cast<int>(opt));
 }
@@ -1017,7 +1033,7 @@ int run_collective(ar_handle* h, int algo, const void* const in[], void* const o
     a.in[r] = algo == AR_BROADCAST ? in[root] : in[r];
     a.out[r] = out[r];
   }
-  rc = launch(L.fn, L.grid, L.threads, a, s);
+  rc = launch(L.fn, L.grid, L.threads, a, s, h->cooperative != 0);
   if (rc != AR_OK) return rc;
   h->epoch += static_cast<uint64_t>(L.chunks);
   h->last_stream = s;
@@ -1149,7 +1165,7 @@ int ar_bench_ex(ar_handle* h, const void* const* in_sets, void* const* out_sets,
     a.ts_end = h->ts + per;
   }
   AR_HIP(hipEventRecord(h->ev0, s));
-  rc = launch(L.fn, L.grid, L.threads, a, s);
+  rc = launch(L.fn, L.grid, L.threads, a, s, h->cooperative != 0);
   if (rc != AR_OK) return rc;
   AR_HIP(hipEventRecord(h->ev1, s));
   h->epoch += static_cast<uint64_t>(iters) * L.chunks;
@@ -1201,6 +1217,8 @@ int ar_plan_info(ar_handle* h, size_t count, ar_algo algo, ar_plan* info) {
                          ? 8
                          : 16;
   info->near = L.near ? 1 : 0;
+  info->resident_per_cu = occupancy(L.fn, L.threads);
+  info->cu_count = h->cu_count;
   return AR_OK;
 }
 

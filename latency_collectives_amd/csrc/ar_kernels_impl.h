@@ -1818,11 +1818,20 @@ __global__ __launch_bounds__(256) void ar_kernel(Args a) {
   ar_body<ALGO, DT, NMAX>(a);
 }
 
-// The bandwidth-regime two-shot in a kernel of its own, with a register budget (at most 128
-// VGPRs) that lets 4 waves share every SIMD: twice the streaming loads in flight per compute
-// unit of the latency kernel, which needs 178 VGPRs. At 8 waves per SIMD it would spill.
+// The bandwidth-regime two-shot in a kernel of its own, with a register budget that lets
+// several waves share every SIMD (more streaming loads in flight per compute unit than the
+// latency kernel's one wave per SIMD) and still spills nothing to the private segment: a
+// kernel with a private segment can have fewer waves resident than the occupancy arithmetic
+// counts (the runtime sizes the scratch it backs them with), and every wave of these grids
+// polls for the others.
+// bf16 folds in binary32, two values per input word, and needs about twice the registers.
+constexpr int bulk_waves_per_eu(int dt, int nmax) {
+  return dt == DT_BF16 ? (nmax >= 16 ? 1 : nmax >= 8 ? 2 : 3) : (nmax >= 16 ? 2 : 3);
+}
+
 template <int DT, int NMAX>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(bulk_waves_per_eu(DT, NMAX))))
 void ar_kernel_bulk(Args a) {
   ar_body<ALGO_TWOSHOT_BULK, DT, NMAX>(a);
 }

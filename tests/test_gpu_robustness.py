@@ -187,25 +187,74 @@ def test_input_check_names_the_sentinel():
                 A.ar_broadcast(h, ins[3], outs, count, 3)
 
 
+@pytest.fixture(scope="module")
+def kernel_resources():
+    """Code-object metadata of every kernel of the library (register counts, LDS, private
+    segment), read from the library file in plain Python."""
+    from latency_collectives_amd import build
+    from tests import kernel_meta as KM
+
+    return KM.metadata_from_library(build.ensure_built())
+
+
+def _check_capacity(kernel_resources, plan, dt_id, n, xcc, mapped):
+    """The workgroups that wait for one another (the ranks' workgroups) fit at once on the XCDs
+    they ran on: per XCD at most (its compute units) x (workgroups per compute unit), counted
+    from the kernel's code-object metadata independently of the occupancy query; the query
+    gives the same count as the metadata (registers, SGPRs, wave slots and LDS are all it needs
+    to count: no kernel has a private segment), and the plan keeps one workgroup per compute
+    unit free whenever the query allows more than one."""
+    import torch
+
+    from tests import kernel_meta as KM
+
+    nmax = 2 if n <= 2 else 4 if n <= 4 else 8 if n <= 8 else 16
+    sym = KM.kernel_symbol(plan["kernel"], dt_id, nmax)
+    meta = kernel_resources[sym]
+    assert meta[".private_segment_fixed_size"] == 0, sym
+    props = torch.cuda.get_device_properties(0)
+    max_waves = props.max_threads_per_multi_processor // 64 // KM.SIMDS_PER_CU
+    by_meta = KM.workgroups_per_cu(meta, plan["threads"], max_waves)
+    upper = KM.workgroups_per_cu(meta, plan["threads"], max_waves, sgpr_rule=False)
+    api = plan["resident_per_cu"]
+    _say(f"  {sym}: {plan['threads']} threads, occupancy query {api}, from metadata {by_meta} "
+         f"(VGPR / wave-slot / LDS bound {upper})")
+    assert 1 <= api <= upper, (sym, api, upper)
+    assert api == by_meta, (sym, api, by_meta)  # the query counts what the metadata says
+    cus_per_xcd = plan["cu_count"] // 8
+    planned_per_cu = api - 1 if api > 1 else api
+    per_xcc = np.bincount(xcc[mapped].astype(np.int64), minlength=8)
+    assert per_xcc.max() <= cus_per_xcd * planned_per_cu, (sym, per_xcc.tolist(), api)
+    assert per_xcc.max() <= cus_per_xcd * by_meta
+
+
 @pytest.mark.parametrize("placement", [0, 1, 2])
 @pytest.mark.parametrize("n", [2, 3, 4, 8, 16])
-def test_launch_record_matches_decode(n, placement):
+def test_launch_record_matches_decode(n, placement, kernel_resources):
     """Every workgroup of a real AllReduce grid records the XCC it ran on and the rank it
     decoded. Dispatch is round-robin over the 8 XCDs (workgroup w on XCD w % 8), every (rank,
-    workgroup) pair appears exactly once, and each rank sits on the XCDs its placement gives it:
+    workgroup) pair appears exactly once, each rank sits on the XCDs its placement gives it:
     rank r on XCD r % 8 (and r + N, r + 2N, ... when it spans several), all on XCD 0 for the
-    same-XCD placement."""
+    same-XCD placement; and the ranks' workgroups fit on their XCDs at once (counted from the
+    kernels' register and LDS use). The cases cover the one-pass, multi-pass and bulk kernels."""
     from latency_collectives_amd import _ar as A
 
-    for count, algo in ((64, "oneshot_sentinel"), (1 << 16, "oneshot_sentinel"),
-                        (1 << 18, "twoshot"), (1 << 14, "ll128_atomic")):
+    cases = [(64, "oneshot_sentinel"), (1 << 16, "oneshot_sentinel"), (1 << 18, "twoshot"),
+             (1 << 14, "ll128_atomic"), (1 << 12, "ll128_det"), (1 << 12, "barrier2"),
+             (1 << 18, "oneshot_ll"), (1 << 20, "oneshot_sentinel"), (1 << 21, "twoshot")]
+    for count, algo in cases:
         with handle(n, count * 4, "f32", placement=placement, record_launch=1) as h:
+            try:
+                plan = A.ar_plan_info(h, count, A.ALGOS[algo])
+            except A.ArError as e:  # a shape the placement cannot hold is refused, not launched
+                assert e.code == A.AR_ENORES, e
+                _say(f"case n={n} placement={placement} {algo} count={count}: refused ({e})")
+                continue
+            _say(f"case n={n} placement={placement} {algo} count={count} plan={plan}")
             x = draw("f32", n, count, seed=5)
             got = run_allreduce(h, x, algo)
             assert_matches(got, x, algo, "f32")
-            plan = A.ar_plan_info(h, count, A.ALGOS[algo])
             rec = A.ar_read_region(h, 0, A.REGION_LAUNCH_RECORD, 4 * plan["grid"]).view(np.uint32)
-        _say(f"case n={n} placement={placement} {algo} count={count} plan={plan}")
         xcc = rec & 0xFF
         rank = ((rec >> 8) & 0xFF).astype(np.int64) - 1
         cta = (rec >> 16).astype(np.int64)
@@ -214,6 +263,7 @@ def test_launch_record_matches_decode(n, placement):
         mapped = rank >= 0
         pairs = set(zip(rank[mapped].tolist(), cta[mapped].tolist()))
         assert len(pairs) == mapped.sum() == n * plan["ctas"]
+        _check_capacity(kernel_resources, plan, 0, n, xcc, mapped)
         for r in range(n):
             on = set(xcc[rank == r].tolist())
             if placement == 0:
@@ -221,3 +271,52 @@ def test_launch_record_matches_decode(n, placement):
                 assert on <= allowed and (r % 8) in on, f"rank {r} on XCDs {on}"
             elif placement == 1:
                 assert on == {0}, f"rank {r} on XCDs {on}"
+
+
+@pytest.mark.parametrize("n", [2, 8, 16])
+def test_cooperative_launch(n):
+    """AR_OPT_COOPERATIVE: the runtime checks that each grid can be resident at once before it
+    starts it. Every planned grid passes the check (one-pass, multi-pass and bulk kernels, the
+    standalone collectives too) and the results are unchanged."""
+    import time
+
+    import torch
+
+    from latency_collectives_amd import _ar as A
+
+    cases = [(64, "oneshot_ll"), (1000, "oneshot_sentinel"), (1 << 16, "twoshot"),
+             (1 << 21, "twoshot"), (4096, "ll128_atomic"), (4096, "ll128_det"),
+             (777, "barrier2"), (1 << 20, "oneshot_sentinel")]
+    for count, algo in cases:
+        _say(f"case n={n} {algo} count={count}")
+        x = draw("f32", n, count, seed=count % 97)
+        with handle(n, count * 4, "f32", cooperative=1) as h:
+            got = run_allreduce(h, x, algo)
+            assert_matches(got, x, algo, "f32")
+            if count == 1000:
+                ins = to_device(x)
+                outs = [torch.empty_like(t) for t in ins]
+                for coop in (1, 0):
+                    A.ar_set_option(h, A.AR_OPT_COOPERATIVE, coop)
+                    A.ar_allreduce(h, ins, outs, count, A.AR_ONESHOT_SENTINEL)
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    for _ in range(50):
+                        A.ar_allreduce(h, ins, outs, count, A.AR_ONESHOT_SENTINEL)
+                    torch.cuda.synchronize()
+                    _say(f"  cooperative={coop}: {(time.perf_counter() - t0) / 50 * 1e6:.1f} "
+                         "us per call (host, back to back)")
+                A.ar_check(h)
+                assert_matches(from_device(outs, x.dtype), x, algo, "f32")
+    # a standalone collective with the option on
+    count = n * 1024  # partitions of whole 16-byte units
+    x = draw("bf16", n, count, seed=3)
+    with handle(n, count * 2, "bf16", cooperative=1) as h:
+        ins = to_device(x)
+        outs = [torch.empty((count // n,), dtype=torch.int16, device="cuda") for _ in range(n)]
+        A.ar_reducescatter(h, ins, outs, count // n)
+        A.ar_check(h)
+        got = from_device(outs, x.dtype)
+    ref = oracle_sum(x)
+    for r in range(n):
+        assert np.array_equal(got[r], ref[r * (count // n):(r + 1) * (count // n)])

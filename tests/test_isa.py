@@ -6,52 +6,31 @@ They pin the properties the design relies on: LL lines and sentinel slots move a
 agent-coherent policy and the bulk kernel's input and output streams the non-temporal one, and
 no packed fp32 arithmetic appears anywhere (the build disables it)."""
 
-import os
 import re
-import shutil
-import subprocess
 
 import pytest
 
-LLVM = "/opt/rocm/llvm/bin"
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+from tests import kernel_meta as KM
 
 
 @pytest.fixture(scope="module")
-def kernels(tmp_path_factory):
+def objs(tmp_path_factory):
     from latency_collectives_amd import build
 
     lib = build.ensure_built()
-    bundler = os.path.join(LLVM, "clang-offload-bundler")
-    objdump = os.path.join(LLVM, "llvm-objdump")
-    if not (os.path.exists(bundler) and os.path.exists(objdump) and shutil.which("objcopy")):
+    if not KM.tools_available():
         pytest.skip("ROCm LLVM tools or objcopy not available")
-    d = tmp_path_factory.mktemp("isa")
-    fat = str(d / "fat.bin")
-    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", lib], check=True)
-    # one offload bundle per translation unit, concatenated (each starts with the magic string)
-    magic = b"__CLANG_OFFLOAD_BUNDLE__"
-    raw = open(fat, "rb").read()
-    starts = [m.start() for m in re.finditer(re.escape(magic), raw)]
-    text = ""
-    for j, a in enumerate(starts):
-        part, co = str(d / f"fat{j}.bin"), str(d / f"co{j}.o")
-        with open(part, "wb") as f:
-            f.write(raw[a:starts[j + 1] if j + 1 < len(starts) else len(raw)])
-        subprocess.run([bundler, "--unbundle", "--type=o", f"--input={part}",
-                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={co}"],
-                       check=True)
-        text += subprocess.run([objdump, "-d", "--mcpu=gfx950", co], check=True,
-                               capture_output=True, text=True).stdout
-    out, name = {}, None
-    for line in text.splitlines():
-        m = re.match(r"^[0-9a-f]+ <(\S+)>:$", line)
-        if m:
-            name = m.group(1)
-            out[name] = []
-        elif name is not None and line.startswith("\t"):
-            out[name].append(line.strip())
-    return out
+    return KM.code_objects(lib, str(tmp_path_factory.mktemp("isa")))
+
+
+@pytest.fixture(scope="module")
+def kernels(objs):
+    return KM.disassembly(objs)
+
+
+@pytest.fixture(scope="module")
+def meta(objs):
+    return KM.metadata(objs)
 
 
 def _kernel(kernels, algo, dt, nmax, bulk=False):
@@ -101,3 +80,45 @@ def test_no_packed_fp32_arithmetic(kernels):
     bad = [(k, i) for k, ins in kernels.items() for i in ins
            if i.split()[0] in ("v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32")]
     assert not bad, bad[:4]
+
+
+def test_no_kernel_has_a_private_segment(meta):
+    """Every wave of an AllReduce grid polls for the others, so the whole grid must be resident
+    at once, and the planner counts residency from registers and LDS (the occupancy query). A
+    kernel that spills to the private segment also needs scratch, which the runtime may back for
+    fewer waves than the registers allow: no kernel of the library has a private segment or a
+    dynamic stack."""
+    assert meta
+    bad = {k: (m[".private_segment_fixed_size"], m[".vgpr_spill_count"])
+           for k, m in meta.items()
+           if m[".private_segment_fixed_size"] or m[".uses_dynamic_stack"]}
+    assert not bad, bad
+
+
+def test_every_allreduce_kernel_fits_the_planner_shapes(meta):
+    """The planner launches 64..256 threads per workgroup and at least one workgroup per compute
+    unit: every AllReduce kernel accepts 256-thread workgroups and one compute unit holds at
+    least one of them, with 64-lane waves; the bulk two-shot kernels for up to 8 ranks hold at
+    least two (the planner keeps one free; with 16 ranks and bf16 the register budget gives one
+    workgroup per compute unit)."""
+    ar = {k: m for k, m in meta.items() if k.startswith(("_ZN2ar9ar_kernel", "_ZN2ar14ar_kernel"))}
+    assert len(ar) > 100
+    for k, m in ar.items():
+        assert m[".wavefront_size"] == 64, k
+        assert m[".max_flat_workgroup_size"] >= 256, k
+        assert KM.workgroups_per_cu(m, 256) >= 1, k
+        if "bulk" in k and not k.endswith("ELi16EEEvNS_4ArgsE"):
+            assert KM.workgroups_per_cu(m, 256) >= 2, (k, m[".vgpr_count"])
+
+
+def test_metadata_reader_agrees_with_llvm_readelf(meta):
+    """The plain-Python reader of the code-object metadata (used by GPU tests, which must not
+    start tools from a process that uses the GPU) gives llvm-readelf's records."""
+    from latency_collectives_amd import build
+
+    mine = KM.metadata_from_library(build.ensure_built())
+    assert set(mine) == set(meta)
+    keys = (".vgpr_count", ".agpr_count", ".sgpr_count", ".group_segment_fixed_size",
+            ".private_segment_fixed_size", ".max_flat_workgroup_size", ".wavefront_size")
+    for k, m in meta.items():
+        assert [mine[k][x] for x in keys] == [m[x] for x in keys], k
