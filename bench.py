@@ -59,6 +59,7 @@ CONFIGS = {
     5: (["twoshot"], ["f32"]),
 }
 HEADLINE = 2  # `value`: the 4-rank bf16 one-shot sentinel workload
+SPLIT = None  # --split: force the peer-split kernels on (1) or off (0); None = library default
 BANDWIDTH = 5  # reported against the HBM roofline
 
 # Kernel dispatches of the AllReduce kernels made so far by this process (ar_bench and every
@@ -395,6 +396,8 @@ def run_workload(A, I, wid: int, algo: str | None, iters: int | None, warmup: in
         A.ar_set_option(h, A.AR_OPT_PLACEMENT, placement)
         if group is not None:
             A.ar_set_option(h, A.AR_OPT_GROUP, group)
+        if SPLIT is not None:
+            A.ar_set_option(h, A.AR_OPT_SPLIT, SPLIT)
         rows = []
         for si, size in enumerate(wl["sizes"]):
             rows.append(bench_size(A, I, h, wid, wl, si, size, algo, iters, warmup, hz,
@@ -478,6 +481,8 @@ def main() -> int:
     ap.add_argument("--group", type=int, default=None,
                     help="with --workload: ranks per group of the deterministic LL128 variant")
     ap.add_argument("--placement", type=int, default=0, help="0 XCD per rank, 1 same XCD")
+    ap.add_argument("--split", type=int, default=None, choices=(0, 1),
+                    help="peer-split one-pass kernels on (1) or off (0) [library default: on]")
     ap.add_argument("--all", action="store_true", help="also run the standalone collectives")
     ap.add_argument("--auto-sweep", action="store_true",
                     help="only measure the crossovers behind AR_ALGO_AUTO (every dtype)")
@@ -495,6 +500,8 @@ def main() -> int:
                     help="only run the streaming copy kernel over MIB MiB (5 times) and exit; "
                          "its known byte count scales rocprof FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
+    global SPLIT
+    SPLIT = args.split
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the ranks are emulated on a single MI355X; "

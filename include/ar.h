@@ -75,7 +75,7 @@ typedef enum {
   AR_LL128_ATOMIC = 4,
   AR_BARRIER2 = 5,
   AR_BARRIER_ONLY = 6,
-  /* values 7..11, 15..20 and 22..25 are internal kernel families (see ar_plan_info); the standalone
+  /* values 7..11, 15..20 and 22..29 are internal kernel families (see ar_plan_info); the standalone
      collectives below are called through their own entry points and named by these ids in
      ar_bench, ar_alg_bytes and ar_plan_info */
   AR_REDUCESCATTER = 12,
@@ -279,6 +279,11 @@ double ar_wallclock_hz(void);
  *                        workgroup waits for others, Every µs Matters §II.B) and refuse it
  *                        otherwise (AR_ENORES) instead of starting part of it; no grid-wide
  *                        synchronisation is used. Costs launch time, not device time [0]
+ *   AR_OPT_SPLIT         1: with 5..16 ranks, when the launch shape is not forced, the one-pass
+ *                        one-shot sentinel and two-shot kernels give each 64 units of a chunk
+ *                        a workgroup of 4 waves, each pushing to and polling a quarter of the
+ *                        peers (the kernel families 26..29 of ar_plan_info); 0: one wave per 64
+ *                        units with every peer [1]
  */
 typedef enum {
   AR_OPT_TIMEOUT_US = 0,
@@ -292,7 +297,8 @@ typedef enum {
   AR_OPT_CHECK_INPUTS = 8,
   AR_OPT_RECORD_LAUNCH = 9,
   AR_OPT_GROUP = 10,
-  AR_OPT_COOPERATIVE = 11
+  AR_OPT_COOPERATIVE = 11,
+  AR_OPT_SPLIT = 12
 } ar_option;
 int ar_set_option(ar_handle* h, ar_option opt, int64_t value);
 
@@ -340,7 +346,8 @@ typedef struct {
                      one-shot / two-shot with 8-byte units; 12 / 13 / 14 the reduce-scatter /
                      all-gather / broadcast loop kernels; 15 / 16 reduce-scatter / all-gather as
                      one half of the one-pass two-shot (17 / 18 with 8-byte units); 19 / 20
-                     one-pass broadcast with 16- / 8-byte units */
+                     one-pass broadcast with 16- / 8-byte units; 26 / 27 peer-split one-shot
+                     sentinel, 28 / 29 peer-split two-shot, with 16- / 8-byte units */
   int chunks;     /* steps per call (the message is cut into equal chunks at the scratch cap) */
   int ctas;       /* workgroups per rank */
   int threads;    /* threads per workgroup */

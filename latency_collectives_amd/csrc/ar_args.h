@@ -9,6 +9,7 @@ constexpr int kMaxRanks = 16;
 constexpr int kMaxCtasPerRank = 256;
 constexpr int kMaxWavesPerCta = 4;  // blocks of at most 256 threads
 constexpr int kWave = 64;
+constexpr int kSplitWaves = 4;  // waves per workgroup of the peer-split kernels (one per peer group)
 
 // Algorithms (values match ar_algo in include/ar.h).
 enum Algo : int {
@@ -45,6 +46,12 @@ enum Algo : int {
   ALGO_LL128_E2 = 23,
   ALGO_LL128_DET_E1 = 24,
   ALGO_LL128_DET_E2 = 25,
+  // peer-split one-pass kernels (several waves share a chunk's units, each with a few peers):
+  // one-shot sentinel with 16- / 8-byte units, two-shot with 16- / 8-byte units
+  ALGO_ONESHOT_SPLIT = 26,
+  ALGO_ONESHOT_SPLIT_NARROW = 27,
+  ALGO_TWOSHOT_SPLIT = 28,
+  ALGO_TWOSHOT_SPLIT_NARROW = 29,
 };
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).

@@ -26,6 +26,18 @@ ar_kernel_fn pick_n(int nmax) {
   }
 }
 
+// The peer-split kernels only for 8 and 16 ranks: with fewer peers a wave has few stores to
+// spread.
+template <int ALGO>
+ar_kernel_fn pick_split(int nmax) {
+  constexpr int DT = ar::DT_I32;
+  switch (nmax) {
+    case 8: return ar::ar_kernel<ALGO, DT, 8>;
+    case 16: return ar::ar_kernel<ALGO, DT, 16>;
+    default: return nullptr;
+  }
+}
+
 }  // namespace
 
 ar_kernel_fn ar_select_kernel_i32(int algo, int nmax) {
@@ -51,6 +63,9 @@ ar_kernel_fn ar_select_kernel_i32(int algo, int nmax) {
     case ar::ALGO_AG_NARROW: return pick_n<ar::ALGO_AG_NARROW>(nmax);
     case ar::ALGO_BCAST_ONEPASS: return pick_n<ar::ALGO_BCAST_ONEPASS>(nmax);
     case ar::ALGO_BCAST_NARROW: return pick_n<ar::ALGO_BCAST_NARROW>(nmax);
+    case ar::ALGO_ONESHOT_SPLIT: return pick_split<ar::ALGO_ONESHOT_SPLIT>(nmax);
+    case ar::ALGO_ONESHOT_SPLIT_NARROW: return pick_split<ar::ALGO_ONESHOT_SPLIT_NARROW>(nmax);
+    // (no split two-shot: an int32 two-shot always takes the bulk kernel's completion flags)
     default: return nullptr;
   }
 }

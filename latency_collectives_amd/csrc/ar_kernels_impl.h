@@ -690,6 +690,300 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
   }
 }
 
+// ------------------------------------------------------------------ peer-split one-pass kernels
+//
+// A wave's coherent stores complete one after another: on MI355X every further store of one
+// wave (8 bytes per lane, any number of active lanes) adds ~13-24 ns before the last of them
+// has completed, while stores of different waves complete in parallel (16 single stores from
+// 16 waves of one workgroup: ~350 ns for the last, against ~600 ns from one wave). With N-1
+// pushes per wave the last peer's unit therefore lands (N-2) store times after the first. The
+// split kernels give every 64 units of a chunk a workgroup of kSplit waves that share those
+// units: wave g pushes to, polls and re-arms only the peers j = 1 + g + m * kSplit after this
+// rank (m = 0..J-1, J = ceil((NMAX - 1) / kSplit)), so each wave issues J stores per phase and
+// J loads per poll round. The polled units meet in LDS, one row per source rank, double-buffered
+// by step parity; after one workgroup barrier the rank-order fold reads them back. A peer q is
+// pushed to, polled and re-armed by the same wave, so the double-buffer credit chain of the
+// unsplit kernels holds per (lane, peer) unchanged.
+constexpr int kSplit = kSplitWaves;
+
+template <int NMAX>
+constexpr int split_j() {
+  return (NMAX - 1 + kSplit - 1) / kSplit;
+}
+
+// Set by a wave whose poll timed out before the barrier, so that the other waves of the
+// workgroup, released by the same barrier, fail the step too (zeroed at kernel entry).
+__shared__ uint32_t g_split_fail;
+
+// Workgroup barrier after this wave's LDS writes have completed. No wait on vector memory: the
+// pushes of the step may still be in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The m-th peer of wave g: its distance j after rank r and its rank q (r itself when j >= N, so
+// that an absent peer's LDS row is one nobody reads).
+struct SplitPeer {
+  int j;
+  int q;
+  bool live;
+};
+__device__ __forceinline__ SplitPeer split_peer(int N, int r, int g, int m) {
+  SplitPeer p;
+  p.j = 1 + g + m * kSplit;
+  p.live = p.j < N;
+  int q = r + p.j;
+  if (q >= N) q -= N;
+  p.q = p.live ? q : r;
+  return p;
+}
+
+// Base address of region g of the peer (a descriptor that drops every access when the peer is
+// absent), computed before the step's start stamp and kept in scalar registers, so that only
+// the descriptor's assembly stands between two pushes.
+struct PeerBase {
+  uint64_t base;
+  uint32_t bytes;
+};
+__device__ __forceinline__ PeerBase peer_base(const Args& a, const SplitPeer& p, const Region& g) {
+  PeerBase b;
+  b.base = reinterpret_cast<uint64_t>(region_base(a, p.live ? p.q : 0, g));
+  b.bytes = p.live ? g.bytes : 0u;
+  asm volatile("" : "+s"(b.base), "+s"(b.bytes));
+  return b;
+}
+__device__ __forceinline__ rsrc_t peer_rsrc(const PeerBase& b) {
+  return make_rsrc(reinterpret_cast<const void*>(b.base), b.bytes);
+}
+
+// Poll the J units at the given offsets of the own slots (kDrop: nothing to wait for) until
+// every one passes `ready` (bounded, like poll_all).
+template <int J, class Ready, class V>
+__device__ __forceinline__ bool poll_list(const Args& a, rsrc_t own, const uint32_t (&off)[J],
+                                          V (&u)[J], Ready ready, int rank, uint64_t step) {
+  uint32_t spins = 0;
+  uint64_t t_first = 0;
+  while (true) {
+#pragma unroll
+    for (int m = 0; m < J; ++m) ld_vec<kCoh>(own, off[m], u[m]);
+    compiler_fence();
+    bool ok = true;
+#pragma unroll
+    for (int m = 0; m < J; ++m) ok = ok & ((off[m] == kDrop) | ready(u[m]));
+    const uint64_t waiting = __ballot(!ok);
+    if (waiting == 0) return true;
+    if ((++spins & 1023u) == 0) {
+      t_first = poll_check(poll_env(a), t_first, rank, -1, step);
+      if (t_first == 0) return false;
+    }
+  }
+}
+
+// Exchange of the polled units through LDS and the rank-order fold of all of them with this
+// rank's own unit x (every wave folds; only the caller decides who stores). Returns false when
+// any wave of the workgroup timed out before the barrier.
+template <int DT, int NMAX, int UB, int J>
+__device__ __forceinline__ bool split_fold(const Ctx& c, uint32_t b, int N, int r,
+                                           const SplitPeer (&pe)[J], bool polled,
+                                           const unit_t<UB> (&u)[J], const uint32_t* x,
+                                           uint32_t* o) {
+  using V = unit_t<UB>;
+  constexpr int W = UB / 4;
+  __shared__ V xch[2][NMAX][kWave];
+#pragma unroll
+  for (int m = 0; m < J; ++m) xch[b][pe[m].q][c.lane] = u[m];
+  if (!polled) g_split_fail = 1u;
+  lds_barrier();
+  if (g_split_fail != 0u) return false;
+  V v[NMAX];
+#pragma unroll
+  for (int q = 0; q < NMAX; ++q) v[q] = xch[b][q][c.lane];
+  fold_rank_order<DT, NMAX, W>(N, r, x, v, o);
+  return true;
+}
+
+// One-shot sentinel AllReduce, peer-split (see above): every wave of the workgroup loads the
+// same 64 units, pushes them to its J peers and polls their units; wave 0 stores the output.
+template <int DT, int NMAX, int UB>
+__device__ bool step_oneshot_split(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
+                                   rsrc_t out_r, int k, uint64_t& t0, uint64_t& t1) {
+  using V = unit_t<UB>;
+  constexpr int W = UB / 4;
+  constexpr int J = split_j<NMAX>();
+  const int N = a.nranks, r = c.rank;
+  const int g = static_cast<int>(uni(static_cast<uint32_t>(c.wave)));  // wave-uniform
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t slot = a.p1.slot, CU = a.chunk_units;
+  const uint32_t unit0 = static_cast<uint32_t>(k) * CU;
+  const bool sends = r != a.withhold;
+  const rsrc_t own = region_rsrc(a, r, a.p1);
+  const V sent = sentinel_unit<DT, UB>();
+  auto ready = [](V l) { return vec_clear<DT>(l); };
+  const uint32_t i = static_cast<uint32_t>(c.cta) * kWave + c.lane;  // shared by the waves
+  const bool act = i < CU;
+  SplitPeer pe[J];
+  PeerBase pb[J];
+  uint32_t poll_off[J];
+  const uint32_t slot0 = b * N * slot + slot_off<UB>(a.p1, i);
+#pragma unroll
+  for (int m = 0; m < J; ++m) {
+    pe[m] = split_peer(N, r, g, m);
+    pb[m] = peer_base(a, pe[m], a.p1);
+    poll_off[m] = act && pe[m].live ? slot0 + static_cast<uint32_t>(pe[m].q) * slot : kDrop;
+    pin(poll_off[m]);
+  }
+  uint32_t in_off = act ? (unit0 + i) * UB : kDrop;
+  uint32_t push_off = act ? (b * N + r) * slot + slot_off<UB>(a.p1, i) : kDrop;
+  uint32_t out_off = act && g == 0 ? (unit0 + i) * UB : kDrop;
+  pin(in_off);
+  pin(push_off);
+  pin(out_off);
+  stamp_start(t0, k);
+  uint32_t x[W];
+  load_unit<DT, UB>(in_r, in_off, a.nbytes, x);
+  compiler_fence();
+  wait_vm<0>();
+  if (sends) {
+    V line;
+#pragma unroll
+    for (int e = 0; e < W; ++e) line[e] = x[e];
+#pragma unroll
+    for (int m = 0; m < J; ++m) st_vec<kCoh>(peer_rsrc(pb[m]), push_off, line);
+  }
+  V u[J];
+  const bool polled = poll_list<J>(a, own, poll_off, u, ready, r, s);
+  uint32_t o[W];
+  if (!split_fold<DT, NMAX, UB, J>(c, b, N, r, pe, polled, u, x, o)) return false;
+  store_unit<DT, UB>(out_r, out_off, a.nbytes, o);
+  compiler_fence();
+  wait_vm<0>();  // the output has landed (wave 0); the others have folded
+  t1 = now_ticks();
+  // re-arm this wave's sources for step s + 2 (the next step's first push waits for it)
+#pragma unroll
+  for (int m = 0; m < J; ++m) st_vec<kCoh>(own, poll_off[m], sent);
+  return true;
+}
+
+// Two-shot AllReduce, peer-split: wave g sends its J peers their partitions (reduce-scatter),
+// polls their contributions to this rank's partition, and after the exchange and the fold (in
+// every wave) sends them the reduced partition and polls theirs into the output (all-gather).
+// Wave 0 writes the rank's own partition of the output.
+template <int DT, int NMAX, int UB>
+__device__ bool step_twoshot_split(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
+                                   rsrc_t out_r, int k, uint64_t& t0, uint64_t& t1) {
+  using V = unit_t<UB>;
+  constexpr int W = UB / 4;
+  constexpr int J = split_j<NMAX>();
+  const int N = a.nranks, r = c.rank;
+  const int g = static_cast<int>(uni(static_cast<uint32_t>(c.wave)));  // wave-uniform
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t slot1 = a.p1.slot, slot2 = a.p2.slot, CU = a.chunk_units, P = a.part_units;
+  const bool sends = r != a.withhold;
+  const rsrc_t own1 = region_rsrc(a, r, a.p1);
+  const rsrc_t own2 = region_rsrc(a, r, a.p2);
+  const V sent = sentinel_unit<DT, UB>();
+  auto ready = [](V l) { return vec_clear<DT>(l); };
+  const uint32_t i = static_cast<uint32_t>(c.cta) * kWave + c.lane;
+  const bool act = i < CU && k * CU + i < P;
+  const uint32_t base1 = b * N * slot1 + slot_off<UB>(a.p1, i);
+  const uint32_t base2 = b * N * slot2 + slot_off<UB>(a.p2, i);
+  SplitPeer pe[J];
+  PeerBase pb1[J], pb2[J];
+  uint32_t in_off[J], poll1[J], poll2[J], ag_off[J];
+#pragma unroll
+  for (int m = 0; m < J; ++m) {
+    pe[m] = split_peer(N, r, g, m);
+    pb1[m] = peer_base(a, pe[m], a.p1);
+    pb2[m] = peer_base(a, pe[m], a.p2);
+    const bool live = act && pe[m].live;
+    const uint32_t q = static_cast<uint32_t>(pe[m].q);
+    in_off[m] = live ? (q * P + k * CU + i) * UB : kDrop;      // partition owned by peer q
+    poll1[m] = live ? base1 + q * slot1 : kDrop;
+    poll2[m] = live ? base2 + q * slot2 : kDrop;
+    ag_off[m] = live ? (q * P + k * CU + i) * UB : kDrop;      // peer q's reduced partition
+    pin(in_off[m]);
+    pin(poll1[m]);
+    pin(poll2[m]);
+  }
+  uint32_t own_off = act ? (r * P + k * CU + i) * UB : kDrop;
+  uint32_t out_own = act && g == 0 ? own_off : kDrop;
+  uint32_t push1 = act ? (b * N + r) * slot1 + slot_off<UB>(a.p1, i) : kDrop;
+  uint32_t push2 = act ? (b * N + r) * slot2 + slot_off<UB>(a.p2, i) : kDrop;
+  pin(own_off);
+  pin(out_own);
+  pin(push1);
+  pin(push2);
+  stamp_start(t0, k);
+  uint32_t x[W];
+  uint32_t w[J][W];
+  load_unit<DT, UB, kPlain, false>(in_r, own_off, a.nbytes, x);
+#pragma unroll
+  for (int m = 0; m < J; ++m) load_unit<DT, UB, kPlain, false>(in_r, in_off[m], a.nbytes, w[m]);
+  // all loads are in flight before the one scalar branch for an odd bf16 tail
+  if (odd_tail<DT>(a.nbytes)) {
+    asm volatile("");
+    clear_odd_tail<UB>(own_off, a.nbytes, x);
+#pragma unroll
+    for (int m = 0; m < J; ++m) clear_odd_tail<UB>(in_off[m], a.nbytes, w[m]);
+  }
+  compiler_fence();
+  wait_vm<0>();
+  if (sends) {
+#pragma unroll
+    for (int m = 0; m < J; ++m) {
+      V line;
+#pragma unroll
+      for (int e = 0; e < W; ++e) line[e] = w[m][e];
+      st_vec<kCoh>(peer_rsrc(pb1[m]), push1, line);
+    }
+  }
+  V u[J];
+  const bool polled = poll_list<J>(a, own1, poll1, u, ready, r, s);
+  uint32_t o[W];
+  if (!split_fold<DT, NMAX, UB, J>(c, b, N, r, pe, polled, u, x, o)) return false;
+  if (sends) {
+    V line;
+#pragma unroll
+    for (int e = 0; e < W; ++e) line[e] = o[e];
+#pragma unroll
+    for (int m = 0; m < J; ++m) st_vec<kCoh>(peer_rsrc(pb2[m]), push2, line);
+  }
+  store_unit<DT, UB>(out_r, out_own, a.out_nbytes, o);
+  V u2[J];
+  if (!poll_list<J>(a, own2, poll2, u2, ready, r, s)) return false;
+#pragma unroll
+  for (int m = 0; m < J; ++m) {
+    if constexpr (UB == 16)
+      st16<kPlain>(out_r, ag_off[m], u2[m]);
+    else
+      st8<kPlain>(out_r, ag_off[m], u2[m]);
+  }
+  if (odd_tail<DT>(a.out_nbytes)) {
+    // the last element of an odd-length message, if it is in one of this wave's partitions
+    asm volatile("");
+    const uint32_t last = a.out_nbytes & ~3u;
+#pragma unroll
+    for (int m = 0; m < J; ++m) {
+      const uint32_t off = ag_off[m];
+      const bool tail = off != kDrop && off <= last && last < off + UB;
+      uint32_t word = u2[m][0];
+#pragma unroll
+      for (int e = 1; e < W; ++e) word = (off + 4u * e == last) ? u2[m][e] : word;
+      st2<kPlain>(out_r, tail ? last : kDrop, static_cast<uint16_t>(word & 0xFFFFu));
+    }
+  }
+  compiler_fence();
+  wait_vm<0>();  // every output store of this wave has landed
+  t1 = now_ticks();
+  // re-arm both phases' slots of this wave's peers for step s + 2
+#pragma unroll
+  for (int m = 0; m < J; ++m) {
+    st_vec<kCoh>(own1, poll1[m], sent);
+    st_vec<kCoh>(own2, poll2[m], sent);
+  }
+  return true;
+}
+
 // Bulk two-shot, for chunks wider than one pass of the rank's workgroups (the bandwidth
 // regime). The same reduce-scatter + all-gather as above, but each wave announces its data with
 // one completion flag per peer instead of a sentinel in every unit: a wave pushes all its units
@@ -1680,8 +1974,10 @@ __device__ bool rank_join(const Args& a, const Ctx& c, uint64_t token, bool fail
 __shared__ uint32_t g_abort_seen;
 
 __device__ __forceinline__ bool enter(const Args& a, Ctx& c) {
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0) {
     g_abort_seen = __hip_atomic_load(&a.ctl[CTL_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    g_split_fail = 0u;
+  }
   const bool mapped = decode(a, c);
   if (a.launch_rec != nullptr && threadIdx.x == 0)
     a.launch_rec[blockIdx.x] =
@@ -1751,6 +2047,14 @@ __device__ __forceinline__ void ar_body(const Args& a) {
         ok = step_twoshot<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_TWOSHOT_NARROW) {
         ok = step_twoshot<DT, NMAX, 8>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_ONESHOT_SPLIT) {
+        ok = step_oneshot_split<DT, NMAX, 16>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_ONESHOT_SPLIT_NARROW) {
+        ok = step_oneshot_split<DT, NMAX, 8>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_TWOSHOT_SPLIT) {
+        ok = step_twoshot_split<DT, NMAX, 16>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_TWOSHOT_SPLIT_NARROW) {
+        ok = step_twoshot_split<DT, NMAX, 8>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_TWOSHOT_BULK) {
         ok = step_twoshot_bulk<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_ATOMIC) {
