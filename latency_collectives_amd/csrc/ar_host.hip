@@ -465,7 +465,8 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
     // of a workgroup (the peer-split kernels) while those workgroups still get a compute unit
     // each and the launch shape is not forced. Measured (p50, split against unsplit): 8 ranks,
     // bf16 two-shot 16-128 KiB 6-7 % lower; 16 ranks, fp32 one-shot 4-8 KiB 14-16 % lower;
-    // with two or more such workgroups per compute unit 30 % to 3x higher.
+    // with two or more such workgroups per compute unit 30 % to 3x higher; with 4 ranks (three
+    // peers, one per wave) 3-5 % higher at 1-8 KiB.
     const bool splittable = L.kernel_algo == ar::ALGO_ONESHOT_SENTINEL ||
                             L.kernel_algo == ar::ALGO_ONESHOT_SENTINEL_NARROW ||
                             L.kernel_algo == ar::ALGO_TWOSHOT ||
