@@ -299,7 +299,7 @@ def test_plan_info_reports_the_launch():
         assert small["ctas"] == 1
     with handle(n, 16 << 20, "f32") as hf:
         small_f = A.ar_plan_info(hf, 256, A.AR_TWOSHOT)
-        assert small_f["kernel"] in (3, 11) and small_f["near"] == 1 and small_f["chunks"] == 1
+        assert small_f["kernel"] in (3, 11, 28, 29) and small_f["near"] == 1 and small_f["chunks"] == 1
         assert small_f["grid"] >= n * small_f["ctas"]
     with handle(n, 16 << 20, "i32") as h:
         rs = A.ar_plan_info(h, 1024, A.AR_REDUCESCATTER)

@@ -66,7 +66,8 @@ def test_auto_selection_matches_oracle(dtype):
     (an exact integer sum) and is bit-exact as well."""
     from latency_collectives_amd import _ar as A
 
-    fixed = {1, 2, 3, 7, 8, 9, 10, 11}  # LL, sentinel, two-shot and their internal kernels
+    # LL, sentinel, two-shot and their internal kernels (multi-pass, narrow, bulk, peer-split)
+    fixed = {1, 2, 3, 7, 8, 9, 10, 11, 26, 27, 28, 29}
     seen = set()
     eb = elem_bytes(dtype)
     for n in (2, 3, 4, 6, 8, 16):
