@@ -277,11 +277,21 @@ def measured_traffic(cfg: str, algo: str, dtype: str, n: int, rows: list):
     return sum(per_launch) / len(per_launch)
 
 
-def latency_roofline(rows: list, floor_us: float) -> dict:
-    """Latency roofline of a small-message configuration: per size the bound is the on-chip floor
-    plus the algorithmic bytes at the nominal HBM bandwidth (the floor alone below ~4 KiB);
-    `frac` = bound / p50 (geometric mean over the sizes; 1 would be at the bound)."""
-    bounds = [floor_us + r["alg_bytes_per_call"] / (HBM_PEAK_GBPS * 1e9) * 1e6 for r in rows]
+# Dependent cross-rank exchanges on an algorithm's critical path: a one-shot pushes once; a
+# two-shot (and the LL128-style kernel) reduce-scatters and then all-gathers, each phase waiting
+# for the previous one's data; the barrier baseline is charged its data exchange only (the
+# barriers are the cost it exists to show).
+EXCHANGES = {"oneshot_ll": 1, "oneshot_sentinel": 1, "barrier2": 1, "twoshot": 2,
+             "ll128_atomic": 2, "ll128_det": 2}
+
+
+def latency_roofline(rows: list, floor_us: float, exchanges: int = 1) -> dict:
+    """Latency roofline of a small-message configuration: per size the bound is `exchanges`
+    times the on-chip floor plus the algorithmic bytes at the nominal HBM bandwidth (the floor
+    term dominates below ~4 KiB); `frac` = bound / p50 (geometric mean over the sizes; 1 would
+    be at the bound)."""
+    bounds = [exchanges * floor_us + r["alg_bytes_per_call"] / (HBM_PEAK_GBPS * 1e9) * 1e6
+              for r in rows]
     ratios = [r["p50_us"] / b for r, b in zip(rows, bounds)]
     return {
         "bound": "latency",
@@ -291,8 +301,11 @@ def latency_roofline(rows: list, floor_us: float) -> dict:
         "frac": _gm([1.0 / x for x in ratios]),
         "p50_over_bound": [round(x, 3) for x in ratios],
         "bound_us": [round(b, 4) for b in bounds],
-        "bound_definition": ("floor_us + alg_bytes_per_call / 8 TB/s per size; floor = 2*L_L2 + "
-                             "L_store of the slowest sender->receiver XCD pair of the placement"),
+        "exchanges": exchanges,
+        "bound_definition": ("exchanges * floor_us + alg_bytes_per_call / 8 TB/s per size; floor "
+                             "= 2*L_L2 + L_store of the slowest sender->receiver XCD pair of the "
+                             "placement; exchanges = dependent cross-rank exchanges of the "
+                             "algorithm (1 one-shot, 2 two-shot)"),
     }
 
 
@@ -455,7 +468,7 @@ def run_config(A, I, wid: int, steps, warmup: int, hz: float, placement: int, fl
                 rl["traffic"] = tr
                 ent["algbw_GBps"] = [round(r["algbw_GBps"], 2) for r in rows]
             else:
-                rl = latency_roofline(rows, floor)
+                rl = latency_roofline(rows, floor, EXCHANGES.get(algo, 1))
                 rl["traffic"] = tr
                 rl["hbm"] = hbm_roofline(rows, copy_gbps)
                 ent["p50_over_floor"] = [round(r["p50_us"] / floor, 3) for r in rows]
