@@ -52,6 +52,10 @@ enum Algo : int {
   ALGO_ONESHOT_SPLIT_NARROW = 27,
   ALGO_TWOSHOT_SPLIT = 28,
   ALGO_TWOSHOT_SPLIT_NARROW = 29,
+  // peer-split LL128-style kernels (fp32, bf16): 4 / 1 / 2 word slices per lane
+  ALGO_LL128_SPLIT = 30,
+  ALGO_LL128_SPLIT_E1 = 31,
+  ALGO_LL128_SPLIT_E2 = 32,
 };
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).

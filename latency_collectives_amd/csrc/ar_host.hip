@@ -471,6 +471,27 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
                             L.kernel_algo == ar::ALGO_ONESHOT_SENTINEL_NARROW ||
                             L.kernel_algo == ar::ALGO_TWOSHOT ||
                             L.kernel_algo == ar::ALGO_TWOSHOT_NARROW;
+    // The LL128-style kernel (fp32, bf16) splits the same way: a chunk of at most one 64-unit
+    // block per compute unit of the rank, 1, 2 or 4 word slices per lane as the chunk needs.
+    if (algo == AR_LL128_ATOMIC && h->dtype != AR_INT32 && h->split && N > 4 && h->ctas == 0 &&
+        h->threads == 0 && C > 0) {
+      const int id = C <= 16 ? ar::ALGO_LL128_SPLIT_E1
+                     : C <= 32 ? ar::ALGO_LL128_SPLIT_E2
+                               : ar::ALGO_LL128_SPLIT;
+      ar_kernel_fn fs = ar_select_kernel(id, h->dtype, nmax);
+      const uint64_t wgs = ceil_div(C, static_cast<uint64_t>(ar::kWave));
+      if (fs != nullptr && wgs <= static_cast<uint64_t>(rank_cus)) {
+        const int saved = L.threads;
+        L.threads = ar::kSplitWaves * ar::kWave;
+        if (wgs <= static_cast<uint64_t>(co_resident(fs))) {
+          L.fn = fs;
+          L.kernel_algo = id;
+          L.ctas = static_cast<int>(wgs);
+          return AR_OK;
+        }
+        L.threads = saved;
+      }
+    }
     if (splittable && h->split && N > 4 && h->ctas == 0 && h->threads == 0 && C > 0) {
       const bool two = L.kernel_algo == ar::ALGO_TWOSHOT || L.kernel_algo == ar::ALGO_TWOSHOT_NARROW;
       const int id = two ? (ub == 8 ? ar::ALGO_TWOSHOT_SPLIT_NARROW : ar::ALGO_TWOSHOT_SPLIT)
@@ -1301,7 +1322,10 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
     case ar::ALGO_TWOSHOT_BULK: return static_cast<int64_t>((N + 1) * S + 5 * (N - 1) * S);
     case AR_LL128_ATOMIC:
     case ar::ALGO_LL128_E1:
-    case ar::ALGO_LL128_E2: return static_cast<int64_t>(2 * N * S + 3 * S + 4 * (N - 1) * S);
+    case ar::ALGO_LL128_E2:
+    case ar::ALGO_LL128_SPLIT:
+    case ar::ALGO_LL128_SPLIT_E1:
+    case ar::ALGO_LL128_SPLIT_E2: return static_cast<int64_t>(2 * N * S + 3 * S + 4 * (N - 1) * S);
     case AR_LL128_DET:
     case ar::ALGO_LL128_DET_E1:
     case ar::ALGO_LL128_DET_E2: {

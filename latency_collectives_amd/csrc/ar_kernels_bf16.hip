@@ -70,6 +70,9 @@ ar_kernel_fn ar_select_kernel_bf16(int algo, int nmax) {
     case ar::ALGO_ONESHOT_SPLIT_NARROW: return pick_split<ar::ALGO_ONESHOT_SPLIT_NARROW>(nmax);
     case ar::ALGO_TWOSHOT_SPLIT: return pick_split<ar::ALGO_TWOSHOT_SPLIT>(nmax);
     case ar::ALGO_TWOSHOT_SPLIT_NARROW: return pick_split<ar::ALGO_TWOSHOT_SPLIT_NARROW>(nmax);
+    case ar::ALGO_LL128_SPLIT: return pick_split<ar::ALGO_LL128_SPLIT>(nmax);
+    case ar::ALGO_LL128_SPLIT_E1: return pick_split<ar::ALGO_LL128_SPLIT_E1>(nmax);
+    case ar::ALGO_LL128_SPLIT_E2: return pick_split<ar::ALGO_LL128_SPLIT_E2>(nmax);
     default: return nullptr;
   }
 }

@@ -1565,6 +1565,212 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
   return true;
 }
 
+// LL128-style atomic AllReduce, peer-split (fp32 and bf16; a chunk of at most one 64-unit block
+// per workgroup, E word slices per lane as in step_ll128). The workgroup's 4 waves share the
+// block: wave g adds this rank's words of the partitions of owners j = g + m * kSplit after it
+// (j = 0 is the rank itself) into their shared destinations, waits until its adds have been
+// performed and counts itself in on each of those owners (one counter per owner, buffer and
+// workgroup: N arrivals complete a block). Wave 0 of the owner waits for the N arrivals, takes
+// the sums with atomic exchanges against zero and hands them to the other waves through LDS;
+// after one barrier every wave pushes the sums to its all-gather peers (j = 1 + g + m * kSplit)
+// and polls theirs into the output. A wave's atomics, like its stores, complete one after
+// another, so each wave issues ceil(N / 4) owners' worth instead of N.
+template <int DT, int NMAX, int E>
+__device__ bool step_ll128_split(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
+                                 rsrc_t out_r, int k, uint64_t& t0, uint64_t& t1) {
+  static_assert(DT != DT_I32, "the int32 all-gather carries sums: step_ll128's completion flags");
+  static_assert(E == 1 || E == 2 || E == 4, "word slices per lane");
+  constexpr int JO = (NMAX + kSplit - 1) / kSplit;  // owners per wave (j = 0 .. NMAX-1)
+  constexpr int JP = split_j<NMAX>();               // all-gather peers per wave (j = 1 .. NMAX-1)
+  __shared__ u32x4 sums[2][kWave];
+  const int N = a.nranks, r = c.rank;
+  const int g = static_cast<int>(uni(static_cast<uint32_t>(c.wave)));  // wave-uniform
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t CU = a.chunk_units, P = a.part_units;
+  const uint32_t unit0 = static_cast<uint32_t>(c.cta) * kWave;  // the workgroup's 64 units
+  const uint32_t i = unit0 + c.lane;
+  const bool act = i < CU;
+  const bool sends = r != a.withhold;
+  const rsrc_t own2 = region_rsrc(a, r, a.p2);
+  const uint32_t slot2 = a.p2.slot;
+  const u32x4 sent = sentinel_unit<DT, 16>();
+  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
+  const uint32_t cnt_idx = (b * kMaxCtasPerRank + static_cast<uint32_t>(c.cta)) * kMaxWavesPerCta;
+  // this wave's owners and the words of the block each lane adds
+  SplitPeer po[JO];
+  PeerBase pa[JO];
+  uint32_t in_off[JO][E], woff[E];
+  bool wact[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t d = unit0 * 4u + static_cast<uint32_t>(e) * 64u + c.lane;
+    wact[e] = d < CU * 4u;
+    woff[e] = d * 4u;
+  }
+#pragma unroll
+  for (int m = 0; m < JO; ++m) {
+    po[m].j = g + m * kSplit;
+    po[m].live = po[m].j < N;
+    int q = r + po[m].j;
+    if (q >= N) q -= N;
+    po[m].q = po[m].live ? q : r;
+    pa[m] = peer_base(a, po[m], a.acc);
+    const uint32_t pbase = (static_cast<uint32_t>(po[m].q) * P + k * CU) * 16u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      in_off[m][e] = po[m].live && wact[e] ? pbase + woff[e] : kDrop;
+      pin(in_off[m][e]);
+    }
+  }
+  // this wave's all-gather peers
+  SplitPeer pe[JP];
+  PeerBase pb2[JP];
+  uint32_t poll2[JP], ag_off[JP];
+  const uint32_t base2 = b * N * slot2 + slot_off(a.p2, i);
+#pragma unroll
+  for (int m = 0; m < JP; ++m) {
+    pe[m] = split_peer(N, r, g, m);
+    pb2[m] = peer_base(a, pe[m], a.p2);
+    const bool live = act && pe[m].live;
+    const uint32_t q = static_cast<uint32_t>(pe[m].q);
+    poll2[m] = live ? base2 + q * slot2 : kDrop;
+    ag_off[m] = live ? (q * P + k * CU + i) * 16u : kDrop;
+    pin(poll2[m]);
+  }
+  uint32_t push2 = act ? (b * N + r) * slot2 + slot_off(a.p2, i) : kDrop;
+  uint32_t out_own = act && g == 0 ? (r * P + k * CU + i) * 16u : kDrop;
+  pin(push2);
+  pin(out_own);
+  stamp_start(t0, k);
+  uint32_t w[JO][E];
+#pragma unroll
+  for (int m = 0; m < JO; ++m)
+#pragma unroll
+    for (int e = 0; e < E; ++e) w[m][e] = ld4<kPlain>(in_r, in_off[m][e]);
+  // bf16 of odd length: the half word past the last element reads as zero (it would otherwise be
+  // added like data)
+  if (odd_tail<DT>(a.nbytes)) {
+    asm volatile("");
+    const uint32_t last = a.nbytes & ~3u;
+#pragma unroll
+    for (int m = 0; m < JO; ++m)
+#pragma unroll
+      for (int e = 0; e < E; ++e) w[m][e] = in_off[m][e] == last ? (w[m][e] & 0xFFFFu) : w[m][e];
+  }
+  if (sends) {
+#pragma unroll
+    for (int m = 0; m < JO; ++m) {
+      if constexpr (DT == DT_BF16) {
+        // packed bf16 atomics take a global address: absent owners and idle words add zero into
+        // this rank's sink region instead (branch-free, no waits between the atomics)
+        typedef short s16x2 __attribute__((ext_vector_type(2)));
+        uint8_t* dst = reinterpret_cast<uint8_t*>(pa[m].base) + acc_off(a, b, 0);
+        uint8_t* sink = a.base + static_cast<uint64_t>(r) * a.stride + a.sink.off +
+                        ((c.cta * kMaxWavesPerCta + c.wave) % 64u) * 256u + c.lane * 4u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const bool live = po[m].live && wact[e];
+          __builtin_amdgcn_global_atomic_fadd_v2bf16(
+              reinterpret_cast<s16x2*>(live ? dst + woff[e] : sink),
+              __builtin_bit_cast(s16x2, live ? w[m][e] : 0u));
+        }
+      } else {
+        const rsrc_t dst = peer_rsrc(pa[m]);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+              __uint_as_float(w[m][e]), dst, wact[e] ? acc_off(a, b, 0) + woff[e] : kDrop, 0, 0);
+      }
+    }
+    wait_all_mem();  // every add of this wave has been performed
+    if (c.lane < JO) {
+      int q = r;
+      bool live = false;
+#pragma unroll
+      for (int m = 0; m < JO; ++m) {
+        q = c.lane == m ? po[m].q : q;
+        live = c.lane == m ? po[m].live : live;
+      }
+      if (live) {
+        uint32_t* cnt = reinterpret_cast<uint32_t*>(a.base + static_cast<uint64_t>(q) * a.stride +
+                                                    a.cnt.off) + cnt_idx;
+        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  // owner: wave 0 waits for the N arrivals of this block and takes the sums
+  bool ok = true;
+  if (g == 0) {
+    uint32_t* my_cnt =
+        reinterpret_cast<uint32_t*>(a.base + static_cast<uint64_t>(r) * a.stride + a.cnt.off) +
+        cnt_idx;
+    uint32_t spins = 0;
+    uint64_t t_first = 0;
+    while (uni(__hip_atomic_load(my_cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) !=
+           static_cast<uint32_t>(N)) {
+      if ((++spins & 1023u) == 0) {
+        t_first = poll_check(poll_env(a), t_first, r, -1, s);
+        if (t_first == 0) {
+          ok = false;
+          break;
+        }
+      }
+    }
+    if (ok) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (act) {
+        uint64_t* q = reinterpret_cast<uint64_t*>(a.base + static_cast<uint64_t>(r) * a.stride +
+                                                  a.acc.off + acc_off(a, b, 0) +
+                                                  static_cast<uint64_t>(i) * 16u);
+        const uint64_t lo =
+            __hip_atomic_exchange(q, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t hi =
+            __hip_atomic_exchange(q + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v = u32x4{static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
+                  static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
+      }
+      sums[b][c.lane] = v;
+      if (c.lane == 0) __hip_atomic_store(my_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (!ok) g_split_fail = 1u;
+  lds_barrier();
+  if (g_split_fail != 0u) return false;
+  const u32x4 v = sums[b][c.lane];
+  if (sends) {
+#pragma unroll
+    for (int m = 0; m < JP; ++m) st16<kCoh>(peer_rsrc(pb2[m]), push2, v);
+  }
+  {
+    const uint32_t o[4] = {v.x, v.y, v.z, v.w};
+    store_unit<DT, 16>(out_r, out_own, a.nbytes, o);
+  }
+  u32x4 u2[JP];
+  if (!poll_list<JP>(a, own2, poll2, u2, ready, r, s)) return false;
+#pragma unroll
+  for (int m = 0; m < JP; ++m) st16<kPlain>(out_r, ag_off[m], u2[m]);
+  if (odd_tail<DT>(a.nbytes)) {
+    // the last element of an odd-length message, if it is in one of this wave's partitions
+    asm volatile("");
+    const uint32_t last = a.nbytes & ~3u;
+#pragma unroll
+    for (int m = 0; m < JP; ++m) {
+      const uint32_t off = ag_off[m];
+      const bool tail = off != kDrop && off <= last && last < off + 16u;
+      uint32_t word = u2[m][0];
+#pragma unroll
+      for (int e = 1; e < 4; ++e) word = (off + 4u * e == last) ? u2[m][e] : word;
+      st2<kPlain>(out_r, tail ? last : kDrop, static_cast<uint16_t>(word & 0xFFFFu));
+    }
+  }
+  wait_all_mem();  // every output store of this wave has landed
+  t1 = now_ticks();
+  // re-arm this wave's all-gather slots for step s + 2
+#pragma unroll
+  for (int m = 0; m < JP; ++m) st16<kCoh>(own2, poll2[m], sent);
+  return true;
+}
+
 // ------------------------------------------------------------------ barrier baseline
 //
 // Workgroup-level cross-rank barrier (§III.B): every workgroup writes `val` into its flag slot
@@ -2055,6 +2261,12 @@ __device__ __forceinline__ void ar_body(const Args& a) {
         ok = step_twoshot_split<DT, NMAX, 16>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_TWOSHOT_SPLIT_NARROW) {
         ok = step_twoshot_split<DT, NMAX, 8>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_LL128_SPLIT) {
+        ok = step_ll128_split<DT, NMAX, 4>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_LL128_SPLIT_E1) {
+        ok = step_ll128_split<DT, NMAX, 1>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_LL128_SPLIT_E2) {
+        ok = step_ll128_split<DT, NMAX, 2>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_TWOSHOT_BULK) {
         ok = step_twoshot_bulk<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_ATOMIC) {

@@ -12,6 +12,7 @@ from tests.gpu_util import (assert_matches, draw, elem_bytes, from_device, handl
 pytestmark = pytest.mark.gpu
 
 SPLIT_KERNELS = {26, 27, 28, 29}
+LL128_SPLIT = {30, 31, 32}
 COUNTS = [1, 7, 33, 64, 1000, 4097]
 
 
@@ -119,3 +120,65 @@ def test_split_leaves_slots_rearmed():
             for reg in (A.REGION_P1, A.REGION_P2, A.REGION_P1_NEAR, A.REGION_P2_NEAR):
                 w = A.ar_read_region(h, r, reg).view(np.uint32)
                 assert np.all(w == 0xFFFFFFFF), f"rank {r} region {reg} not re-armed"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [5, 8, 12, 16])
+def test_ll128_split_within_bound_and_dyadic_exact(n, dtype):
+    """The peer-split LL128-style kernel: within the atomic-order bound on ragged counts (1, 2
+    and 4 word slices per lane, one and several 64-unit blocks), bit-exact on inputs whose
+    partial sums are exact in any order, and its destinations and counters clear afterwards."""
+    import torch
+
+    from latency_collectives_amd import _ar as A
+
+    eb = elem_bytes(dtype)
+    counts = [1, 7, 33, 64 * n // eb + 5, 256 * n // eb + 3, 2048 * n // eb]
+    with handle(n, (max(counts) + 1) * eb, dtype) as h:
+        for count in counts:
+            if dtype == "bf16" and count % 2 == 0:
+                count += 1
+            plan = A.ar_plan_info(h, count, A.AR_LL128_ATOMIC)
+            _say(f"case n={n} {dtype} count={count} plan={plan}")
+            assert plan["kernel"] in LL128_SPLIT, plan
+            x = draw(dtype, n, count, seed=3000 + n + count)
+            assert_matches(run_allreduce(h, x, "ll128_atomic"), x, "ll128_atomic", dtype)
+            # dyadic values k * 2^-3, |k| <= 8: every partial sum is exact in fp32 and bf16
+            g = np.random.default_rng(count)
+            k = g.integers(-8, 8, size=(n, count), endpoint=True)
+            xf = (k / 8.0).astype(np.float32)
+            xd = (torch.from_numpy(xf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+                  if dtype == "bf16" else xf)
+            assert_matches(run_allreduce(h, xd, "ll128_atomic"), xd, "twoshot", dtype)
+        for r in range(n):
+            for reg in (A.REGION_ACC, A.REGION_CNT):
+                w = A.ar_read_region(h, r, reg).view(np.uint32)
+                assert np.all(w == 0), f"rank {r} region {reg} not clear"
+
+
+def test_ll128_split_persistent_loop_and_timeout():
+    """A persistent loop of 60 calls over 6 input sets with rank drift (every set within the
+    bound), then a withheld rank ending in AR_ETIMEOUT."""
+    import torch
+
+    from latency_collectives_amd import _ar as A
+
+    n, count = 16, 4096
+    xs = [draw("f32", n, count, seed=500 + k) for k in range(6)]
+    with handle(n, count * 4, "f32", drift=3) as h:
+        assert A.ar_plan_info(h, count, A.AR_LL128_ATOMIC)["kernel"] in LL128_SPLIT
+        ins = [t for x1 in xs for t in to_device(x1)]
+        outs = [torch.empty_like(t) for t in ins]
+        A.ar_bench(h, ins, outs, len(xs), count, A.AR_LL128_ATOMIC, 60)
+        for k, x1 in enumerate(xs):
+            assert_matches(from_device(outs[k * n:(k + 1) * n], x1.dtype), x1, "ll128_atomic",
+                           "f32")
+    x = xs[0]
+    with handle(n, count * 4, "f32", timeout_us=20000, withhold_rank=5) as h:
+        ins = to_device(x)
+        outs = [torch.empty_like(t) for t in ins]
+        A.ar_allreduce(h, ins, outs, count, A.AR_LL128_ATOMIC)
+        torch.cuda.synchronize()
+        with pytest.raises(A.ArError) as e:
+            A.ar_check(h)
+        assert e.value.code == A.AR_ETIMEOUT
