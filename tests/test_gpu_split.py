@@ -46,6 +46,29 @@ def test_split_matches_oracle_and_unsplit(n, dtype):
                 assert plan["threads"] == 256
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [6, 8, 16])
+def test_split_with_16_byte_units(n, dtype):
+    """AR_OPT_NARROW = 0: the peer-split kernels with 16-byte units (families 26 and 28), equal
+    to the oracle and to the 8-byte-unit split kernels."""
+    from latency_collectives_amd import _ar as A
+
+    for algo, fam in (("oneshot_sentinel", 26), ("twoshot", 28)):
+        for count in (1, 9, 333, 64 * n + 7):
+            if dtype == "bf16" and count % 2 == 0:
+                count += 1
+            x = draw(dtype, n, count, seed=7000 + n * count)
+            with handle(n, count * elem_bytes(dtype), dtype, narrow=0) as h:
+                plan = A.ar_plan_info(h, count, A.ALGOS[algo])
+                _say(f"case n={n} {dtype} {algo} count={count} plan={plan}")
+                assert plan["kernel"] == fam and plan["unit_bytes"] == 16, plan
+                got = run_allreduce(h, x, algo)
+                assert_matches(got, x, algo, dtype)
+                A.ar_set_option(h, A.AR_OPT_NARROW, 1)
+                ref = run_allreduce(h, x, algo)
+            assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
+
+
 def test_split_kernels_planned_for_the_decode_shapes():
     """8 ranks, bf16 [tokens, 8192]: the kernels split while a chunk's 64-unit blocks get a
     compute unit each (32 per rank): the two-shot up to 8 tokens, the one-shot at 1 token (2048
