@@ -346,7 +346,7 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
   auto finish = [&](uint32_t i, bool act, const uint32_t* x, const u32x4 (&v)[NMAX]) {
     uint32_t o[2];
     fold_rank_order<DT, NMAX, 2>(N, r, x, v, o);
-    store_unit<DT, 8>(out_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, o);
+    store_unit<DT, 8, kOut>(out_r, act ? (unit0 + i) * 8u : kDrop, a.nbytes, o);
   };
   if constexpr (!kMulti) {
     // one pass: the plan gives this rank at least one lane per unit of the chunk
@@ -433,7 +433,7 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
                     uint32_t off0) {
     uint32_t o[W];
     fold_rank_order<DT, NMAX, W>(N, r, x, v, o);
-    store_unit<DT, UB>(out_r, act ? (unit0 + i) * UB : kDrop, a.nbytes, o);
+    store_unit<DT, UB, kOut>(out_r, act ? (unit0 + i) * UB : kDrop, a.nbytes, o);
     rearm<NMAX>(own, off0, slot, act ? peers : 0u, sent);
   };
   if constexpr (!kMulti) {
@@ -463,7 +463,7 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
     if (!poll_all<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
     uint32_t o[W];
     fold_rank_order<DT, NMAX, W>(N, r, x, v, o);
-    store_unit<DT, UB>(out_r, act ? (unit0 + i) * UB : kDrop, a.nbytes, o);
+    store_unit<DT, UB, kOut>(out_r, act ? (unit0 + i) * UB : kDrop, a.nbytes, o);
     compiler_fence();
     wait_vm<0>();  // the output has landed: the AllReduce is complete for this lane
     t1 = now_ticks();
@@ -548,9 +548,9 @@ __device__ __forceinline__ void allgather_store(const Args& a, rsrc_t out_r, uin
   for (int p = 0; p < NMAX; ++p) {
     const uint32_t off = ((mask >> p) & 1u) ? (p * P + k * CU + i) * UB : kDrop;
     if constexpr (UB == 16)
-      st16<kPlain>(out_r, off, v[p]);
+      st16<kOut>(out_r, off, v[p]);
     else
-      st8<kPlain>(out_r, off, v[p]);
+      st8<kOut>(out_r, off, v[p]);
   }
   if (odd_tail<DT>(a.out_nbytes)) {
     asm volatile("");
@@ -562,7 +562,7 @@ __device__ __forceinline__ void allgather_store(const Args& a, rsrc_t out_r, uin
       uint32_t word = v[p][0];
 #pragma unroll
       for (int e = 1; e < UB / 4; ++e) word = (off + 4u * e == last) ? v[p][e] : word;
-      st2<kPlain>(out_r, tail ? last : kDrop, static_cast<uint16_t>(word & 0xFFFFu));
+      st2<kOut>(out_r, tail ? last : kDrop, static_cast<uint16_t>(word & 0xFFFFu));
     }
   }
 }
@@ -660,7 +660,7 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
       fold_rank_order<DT, NMAX, W>(N, r, w[0], v, o);
     }
     if constexpr (MODE == 1) {
-      store_unit<DT, UB>(out_r, act ? (k * CU + i) * UB : kDrop, a.out_nbytes, o);
+      store_unit<DT, UB, kOut>(out_r, act ? (k * CU + i) * UB : kDrop, a.out_nbytes, o);
       rearm<NMAX>(own1, off1, slot1, mask, sent);
     } else {
       if (sends) {
@@ -669,7 +669,7 @@ __device__ bool step_twoshot(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_
         for (int e = 0; e < W; ++e) line[e] = o[e];
         push_peers<NMAX>(a, r, a.p2, push2, line);
       }
-      store_unit<DT, UB>(out_r, act ? uoff : kDrop, a.out_nbytes, o);
+      store_unit<DT, UB, kOut>(out_r, act ? uoff : kDrop, a.out_nbytes, o);
       V v2[NMAX];
       if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v2, ready, r, s)) return false;
       // every other owner's reduced unit into the output
@@ -854,7 +854,7 @@ __device__ bool step_oneshot_split(const Args& a, const Ctx& c, uint64_t s, rsrc
   const bool polled = poll_list<J>(a, own, poll_off, u, ready, r, s);
   uint32_t o[W];
   if (!split_fold<DT, NMAX, UB, J>(c, b, N, r, pe, polled, u, x, o)) return false;
-  store_unit<DT, UB>(out_r, out_off, a.nbytes, o);
+  store_unit<DT, UB, kOut>(out_r, out_off, a.nbytes, o);
   compiler_fence();
   wait_vm<0>();  // the output has landed (wave 0); the others have folded
   t1 = now_ticks();
@@ -948,15 +948,15 @@ __device__ bool step_twoshot_split(const Args& a, const Ctx& c, uint64_t s, rsrc
 #pragma unroll
     for (int m = 0; m < J; ++m) st_vec<kCoh>(peer_rsrc(pb2[m]), push2, line);
   }
-  store_unit<DT, UB>(out_r, out_own, a.out_nbytes, o);
+  store_unit<DT, UB, kOut>(out_r, out_own, a.out_nbytes, o);
   V u2[J];
   if (!poll_list<J>(a, own2, poll2, u2, ready, r, s)) return false;
 #pragma unroll
   for (int m = 0; m < J; ++m) {
     if constexpr (UB == 16)
-      st16<kPlain>(out_r, ag_off[m], u2[m]);
+      st16<kOut>(out_r, ag_off[m], u2[m]);
     else
-      st8<kPlain>(out_r, ag_off[m], u2[m]);
+      st8<kOut>(out_r, ag_off[m], u2[m]);
   }
   if (odd_tail<DT>(a.out_nbytes)) {
     // the last element of an odd-length message, if it is in one of this wave's partitions
@@ -969,7 +969,7 @@ __device__ bool step_twoshot_split(const Args& a, const Ctx& c, uint64_t s, rsrc
       uint32_t word = u2[m][0];
 #pragma unroll
       for (int e = 1; e < W; ++e) word = (off + 4u * e == last) ? u2[m][e] : word;
-      st2<kPlain>(out_r, tail ? last : kDrop, static_cast<uint16_t>(word & 0xFFFFu));
+      st2<kOut>(out_r, tail ? last : kDrop, static_cast<uint16_t>(word & 0xFFFFu));
     }
   }
   compiler_fence();
@@ -1117,7 +1117,7 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
     fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
     if (sends)
       push_peers<NMAX>(a, r, a.pf2, act ? mine2 + u * 16u : kDrop, u32x4{o[0], o[1], o[2], o[3]});
-    store_unit<DT, 16, kNt>(out_r, act ? uoff : kDrop, a.nbytes, o);
+    store_unit<DT, 16, kOut>(out_r, act ? uoff : kDrop, a.nbytes, o);
   }
   if (sends) {
     wait_all_mem();
@@ -1142,7 +1142,7 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
 #pragma unroll
     for (int q = 0; q < NMAX; ++q) {
       const uint32_t o[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
-      store_unit<DT, 16, kNt>(out_r, ((mask >> q) & 1u) ? (q * P + k * CU + u[q]) * 16u : kDrop,
+      store_unit<DT, 16, kOut>(out_r, ((mask >> q) & 1u) ? (q * P + k * CU + u[q]) * 16u : kDrop,
                               a.nbytes, o);
     }
   }
@@ -1499,7 +1499,7 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
           push_peers<NMAX>(a, r, a.p2, act ? (b * N + r) * slot2 + slot_off(a.p2, i) : kDrop, v);
       }
       const uint32_t o[4] = {v.x, v.y, v.z, v.w};
-      store_unit<DT, 16>(out_r, act ? (r * P + k * CU + i) * 16u : kDrop, a.nbytes, o);
+      store_unit<DT, 16, kOut>(out_r, act ? (r * P + k * CU + i) * 16u : kDrop, a.nbytes, o);
     }
     if constexpr (!DET) {
       if (c.lane == 0) __hip_atomic_store(my_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1535,7 +1535,7 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
 #pragma unroll
       for (int q = 0; q < NMAX; ++q) {
         const uint32_t o[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
-        store_unit<DT, 16>(out_r, ((mask >> q) & 1u) ? (q * P + k * CU + i) * 16u : kDrop,
+        store_unit<DT, 16, kOut>(out_r, ((mask >> q) & 1u) ? (q * P + k * CU + i) * 16u : kDrop,
                            a.nbytes, o);
       }
     }
@@ -1743,12 +1743,12 @@ __device__ bool step_ll128_split(const Args& a, const Ctx& c, uint64_t s, rsrc_t
   }
   {
     const uint32_t o[4] = {v.x, v.y, v.z, v.w};
-    store_unit<DT, 16>(out_r, out_own, a.nbytes, o);
+    store_unit<DT, 16, kOut>(out_r, out_own, a.nbytes, o);
   }
   u32x4 u2[JP];
   if (!poll_list<JP>(a, own2, poll2, u2, ready, r, s)) return false;
 #pragma unroll
-  for (int m = 0; m < JP; ++m) st16<kPlain>(out_r, ag_off[m], u2[m]);
+  for (int m = 0; m < JP; ++m) st16<kOut>(out_r, ag_off[m], u2[m]);
   if (odd_tail<DT>(a.nbytes)) {
     // the last element of an odd-length message, if it is in one of this wave's partitions
     asm volatile("");
@@ -1760,7 +1760,7 @@ __device__ bool step_ll128_split(const Args& a, const Ctx& c, uint64_t s, rsrc_t
       uint32_t word = u2[m][0];
 #pragma unroll
       for (int e = 1; e < 4; ++e) word = (off + 4u * e == last) ? u2[m][e] : word;
-      st2<kPlain>(out_r, tail ? last : kDrop, static_cast<uint16_t>(word & 0xFFFFu));
+      st2<kOut>(out_r, tail ? last : kDrop, static_cast<uint16_t>(word & 0xFFFFu));
     }
   }
   wait_all_mem();  // every output store of this wave has landed
@@ -1875,7 +1875,7 @@ __device__ bool step_barrier2(const Args& a, const Ctx& c, uint64_t s, rsrc_t in
       v[q] = ld16<kCoh>(own, ((mask >> q) & 1u) ? static_cast<uint32_t>(q) * slot + i * 16u : kDrop);
     uint32_t o[4];
     fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
-    store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, o);
+    store_unit<DT, 16, kOut>(out_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, o);
   }
   wait_all_mem();
   t1 = now_ticks();
@@ -1943,7 +1943,7 @@ __device__ bool step_reducescatter(const Args& a, const Ctx& c, uint64_t s, rsrc
     if (!poll_lines<NMAX>(a, own, off0, slot, mask, v, ready, r, s)) return false;
     uint32_t o[4];
     fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
-    store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.out_nbytes, o);
+    store_unit<DT, 16, kOut>(out_r, act ? (unit0 + i) * 16u : kDrop, a.out_nbytes, o);
     rearm<NMAX>(own, off0, slot, mask, sent);
   }
   wait_all_mem();
@@ -1976,7 +1976,7 @@ __device__ bool step_allgather(const Args& a, const Ctx& c, uint64_t s, rsrc_t i
     uint32_t x[4];
     load_unit<DT, 16, kPlain, false>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
     if (sends) push_peers<NMAX>(a, r, a.p1, act ? mine + i * 16u : kDrop, u32x4{x[0], x[1], x[2], x[3]});
-    store_unit<DT, 16>(out_r, act ? (r * P + unit0 + i) * 16u : kDrop, a.out_nbytes, x);
+    store_unit<DT, 16, kOut>(out_r, act ? (r * P + unit0 + i) * 16u : kDrop, a.out_nbytes, x);
   }
   for (uint32_t i0 = c.t0; i0 < CK; i0 += c.T) {
     const uint32_t i = i0 + c.lane;
@@ -1988,7 +1988,7 @@ __device__ bool step_allgather(const Args& a, const Ctx& c, uint64_t s, rsrc_t i
 #pragma unroll
     for (int q = 0; q < NMAX; ++q) {
       const uint32_t o[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
-      store_unit<DT, 16>(out_r, ((mask >> q) & 1u) ? (q * P + unit0 + i) * 16u : kDrop,
+      store_unit<DT, 16, kOut>(out_r, ((mask >> q) & 1u) ? (q * P + unit0 + i) * 16u : kDrop,
                          a.out_nbytes, o);
     }
     rearm<NMAX>(own, off0, slot, mask, sent);
@@ -2028,7 +2028,7 @@ __device__ bool step_broadcast(const Args& a, const Ctx& c, uint64_t s, rsrc_t i
       load_unit<DT, 16>(in_r, act ? (unit0 + i) * 16u : kDrop, a.nbytes, x);
       if (sends)
         push_peers<NMAX>(a, r, a.p1, act ? mine + i * 16u : kDrop, u32x4{x[0], x[1], x[2], x[3]});
-      store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.out_nbytes, x);
+      store_unit<DT, 16, kOut>(out_r, act ? (unit0 + i) * 16u : kDrop, a.out_nbytes, x);
     }
   } else {
     const u32x4 sent = sentinel_unit<DT, 16>();
@@ -2044,7 +2044,7 @@ __device__ bool step_broadcast(const Args& a, const Ctx& c, uint64_t s, rsrc_t i
 #pragma unroll
       for (int q = 1; q < NMAX; ++q) got = (q == R) ? v[q] : got;
       const uint32_t o[4] = {got.x, got.y, got.z, got.w};
-      store_unit<DT, 16>(out_r, act ? (unit0 + i) * 16u : kDrop, a.out_nbytes, o);
+      store_unit<DT, 16, kOut>(out_r, act ? (unit0 + i) * 16u : kDrop, a.out_nbytes, o);
       rearm<NMAX>(own, off0, slot, mask, sent);
     }
     wait_all_mem();  // the re-arms have completed before the flag that hands the buffer back
@@ -2080,7 +2080,7 @@ __device__ bool step_broadcast_1p(const Args& a, const Ctx& c, uint64_t s, rsrc_
     load_unit<DT, UB>(in_r, act ? uoff : kDrop, a.nbytes, x);
     compiler_fence();
     wait_vm<0>();
-    store_unit<DT, UB>(out_r, act ? uoff : kDrop, a.out_nbytes, x);
+    store_unit<DT, UB, kOut>(out_r, act ? uoff : kDrop, a.out_nbytes, x);
     if (r != a.withhold) {
       V line;
 #pragma unroll
@@ -2102,7 +2102,7 @@ __device__ bool step_broadcast_1p(const Args& a, const Ctx& c, uint64_t s, rsrc_
     uint32_t o[W];
 #pragma unroll
     for (int e = 0; e < W; ++e) o[e] = got[e];
-    store_unit<DT, UB>(out_r, act ? uoff : kDrop, a.out_nbytes, o);
+    store_unit<DT, UB, kOut>(out_r, act ? uoff : kDrop, a.out_nbytes, o);
     rearm<NMAX>(region_rsrc(a, r, a.p1), off0, slot, mask, sent);
     compiler_fence();
     wait_vm<0>();  // output and re-arm have completed before the flag that hands the buffer back
