@@ -227,14 +227,14 @@ def copy_peak(A, mib: int = 1024, reps: int = 5) -> dict:
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources and the C header: counters taken on another version of the
-    kernels do not describe this one."""
+    """sha256 over the HIP sources (kernels, planner, launch code): counters taken on another
+    version of them do not describe this one. The C header's text is documentation and is not
+    part of it."""
     import glob
     import hashlib
 
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(ROOT, "latency_collectives_amd", "csrc", "*")))
-    files.append(os.path.join(ROOT, "include", "ar.h"))
     for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())

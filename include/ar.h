@@ -17,6 +17,11 @@
  *     message for the calling thread. Functions returning a pointer return NULL on error.
  *   - A handle is not thread-safe. Calls on one handle must be issued in order on one stream:
  *     the sequence number and the scratch reuse depend on call order (as with a communicator).
+ *   - Every workgroup of a call's grid waits for others, so a grid must be resident as a whole.
+ *     Each call is planned to fit the GPU on its own; two calls in flight at once on one GPU
+ *     (two handles on two streams) may each get only part of the GPU and then wait for each
+ *     other forever (each side's poll times out after AR_OPT_TIMEOUT_US). Keep the calls of all
+ *     handles on one GPU on one stream, or order the streams.
  */
 #ifndef LATENCY_COLLECTIVES_AR_H
 #define LATENCY_COLLECTIVES_AR_H
