@@ -290,3 +290,32 @@ def test_launch_shape_beyond_co_residency_is_refused():
         A.ar_check(h)
         assert bool(torch.all(y[3] == 0))
 
+
+
+@pytest.mark.parametrize("algo", ["twoshot", "oneshot_sentinel", "ll128_atomic", "oneshot_ll"])
+def test_largest_message_a_handle_takes(algo):
+    """The largest message per rank the boundary accepts (max_bytes < 2^31): 2 ranks, int32,
+    2^31 - 64 bytes per rank, with inputs whose sums have a closed form (rank r element i =
+    (i mod 4093) + 7919 r, so every output element is 2 (i mod 4093) + 7919), checked on the
+    device for every element; one element more is refused (AR_ETOOBIG)."""
+    import torch
+
+    from latency_collectives_amd import _ar as A
+
+    n = 2
+    nbytes = (1 << 31) - 64
+    count = nbytes // 4
+    base = torch.arange(count, dtype=torch.int64, device="cuda") % 4093
+    ins = [(base + 7919 * r).to(torch.int32) for r in range(n)]
+    want = (2 * base + 7919).to(torch.int32)
+    del base
+    outs = [torch.empty_like(ins[0]) for _ in range(n)]
+    print(f"case {algo} count={count}", flush=True)
+    with handle(n, nbytes, "i32") as h:
+        A.ar_allreduce(h, ins, outs, count, A.ALGOS[algo])
+        A.ar_check(h)
+        for r in range(n):
+            assert torch.equal(outs[r], want), f"rank {r}"
+        with pytest.raises(A.ArError) as e:
+            A.ar_allreduce(h, ins, outs, count + 16, A.ALGOS[algo])
+        assert e.value.code == A.AR_ETOOBIG
