@@ -642,7 +642,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(I, HEADLINE, wl)
-        # the machine's CPU share is 16 cores whatever os.cpu_count() reports
+        # at most 16 host threads, whatever os.cpu_count() reports
         line["cpu_baseline"]["multi_thread"] = cpu_baseline_threads(
             I, HEADLINE, wl, max(1, min(16, os.cpu_count() or 1)))
     report = {"main": line, "configs": configs, "floors": fl}

@@ -437,7 +437,7 @@ int ar_torn_lines(int placement, int nlines, int gens, uint64_t* torn, uint64_t*
 /*
  * ar_stream_copy: copy `bytes` (a multiple of 16) from device `src` to device `dst` (both 16-byte
  * aligned, not overlapping) on `stream`, with non-temporal 16-byte loads and stores in launches
- * of at most 1 GiB each. It is the box's reference for achievable HBM bandwidth (every byte read
+ * of at most 1 GiB each. It is the device's reference for achievable HBM bandwidth (every byte read
  * once and written once) and the kernel of known size that scales rocprof's HBM byte counters.
  * Asynchronous; AR_EINVAL for null, misaligned or ragged arguments.
  */

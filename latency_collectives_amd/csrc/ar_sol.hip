@@ -172,7 +172,7 @@ __global__ void sol_torn(u32x4* lines, int nlines, int gens, int w_blk, int r_bl
 
 // --------------------------------------------------------------- streaming copy
 // Copy `bytes` (a multiple of 16, below 2^31) with non-temporal 16-byte loads and stores, two
-// units per lane per round: the reference point for HBM bandwidth on the box (a plain copy
+// units per lane per round: the reference point for HBM bandwidth on the device (a plain copy
 // reads and writes every byte once) and the kernel of known size that scales the HBM byte
 // counters.
 __global__ __launch_bounds__(512) void stream_copy(const void* src, void* dst, uint32_t bytes) {

@@ -186,4 +186,6 @@ def summarise(out: str) -> None:
 if __name__ == "__main__":
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
-    summarise(sys.argv[1] if len(sys.argv) > 1 else os.path.join(ROOT, "gpurun_out", "prof"))
+    if len(sys.argv) != 2:
+        sys.exit("usage: python -m latency_collectives_amd.profile_summary OUT")
+    summarise(sys.argv[1])
