@@ -1717,6 +1717,14 @@ __device__ bool step_ll128_split(const Args& a, const Ctx& c, uint64_t s, rsrc_t
       }
     }
     if (ok) {
+      // The counter is reset first, with one branch-free store: vector memory operations of a
+      // wave complete in issue order, so once the exchanges below have returned the reset has
+      // completed too, before this wave reaches the barrier. The other waves' next
+      // contributions (step s + 1) come after that barrier, and a contributor's adds into this
+      // buffer again (step s + 2) only after it has received those; the reset and the cleared
+      // destination are in place by then.
+      st4<kCoh>(region_rsrc(a, r, a.cnt), c.lane == 0 ? cnt_idx * 4u : kDrop, 0u);
+      compiler_fence();
       u32x4 v = {0u, 0u, 0u, 0u};
       if (act) {
         uint64_t* q = reinterpret_cast<uint64_t*>(a.base + static_cast<uint64_t>(r) * a.stride +
@@ -1730,7 +1738,6 @@ __device__ bool step_ll128_split(const Args& a, const Ctx& c, uint64_t s, rsrc_t
                   static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
       }
       sums[b][c.lane] = v;
-      if (c.lane == 0) __hip_atomic_store(my_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (!ok) g_split_fail = 1u;
