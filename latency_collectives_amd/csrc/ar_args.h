@@ -161,6 +161,7 @@ struct Args {
   int algo;
   int root;             // broadcast: the rank whose input every rank receives
   int group;            // deterministic LL128-style variant: ranks per group
+  int block;            // peer-split LL128-style kernel: units per workgroup (1..64)
 };
 
 }  // namespace ar

@@ -231,6 +231,7 @@ struct Launch {
   uint32_t part_units = 0;
   int threads = 64;
   int ctas = 1;
+  int block = ar::kWave;  // peer-split LL128-style kernel: units per workgroup
   int ranks_per_xcd = 1;
   int xcds_per_rank = 1;
   bool near = false;        // slots in the near regions (ll, p1, p2 below, with their pitch and
@@ -471,15 +472,19 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
                             L.kernel_algo == ar::ALGO_ONESHOT_SENTINEL_NARROW ||
                             L.kernel_algo == ar::ALGO_TWOSHOT ||
                             L.kernel_algo == ar::ALGO_TWOSHOT_NARROW;
-    // The LL128-style kernel (fp32, bf16) splits the same way: a chunk of at most one 64-unit
-    // block per compute unit of the rank, 1, 2 or 4 word slices per lane as the chunk needs.
+    // The LL128-style kernel (fp32, bf16) splits the same way: blocks of at most 64 units, one
+    // workgroup each (1, 2 or 4 word slices per lane as the block needs), and at least two
+    // blocks. Measured at 16 ranks, fp32 (p50 against one 64-unit block per workgroup): two
+    // workgroups for 4-16 KiB 2-6 % lower; four or more 5 % to 2x higher (the owners'
+    // destination lines then take more, smaller atomic requests).
     if (algo == AR_LL128_ATOMIC && h->dtype != AR_INT32 && h->split && N > 4 && h->ctas == 0 &&
         h->threads == 0 && C > 0) {
-      const int id = C <= 16 ? ar::ALGO_LL128_SPLIT_E1
-                     : C <= 32 ? ar::ALGO_LL128_SPLIT_E2
-                               : ar::ALGO_LL128_SPLIT;
+      const uint64_t blk = std::min<uint64_t>(ar::kWave, std::max<uint64_t>(1, ceil_div(C, 2)));
+      const uint64_t wgs = ceil_div(C, blk);
+      const int id = blk <= 16 ? ar::ALGO_LL128_SPLIT_E1
+                     : blk <= 32 ? ar::ALGO_LL128_SPLIT_E2
+                                 : ar::ALGO_LL128_SPLIT;
       ar_kernel_fn fs = ar_select_kernel(id, h->dtype, nmax);
-      const uint64_t wgs = ceil_div(C, static_cast<uint64_t>(ar::kWave));
       if (fs != nullptr && wgs <= static_cast<uint64_t>(rank_cus)) {
         const int saved = L.threads;
         L.threads = ar::kSplitWaves * ar::kWave;
@@ -487,6 +492,7 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
           L.fn = fs;
           L.kernel_algo = id;
           L.ctas = static_cast<int>(wgs);
+          L.block = static_cast<int>(blk);
           return AR_OK;
         }
         L.threads = saved;
@@ -625,6 +631,7 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
   a.drift = 0;
   a.algo = algo;
   a.group = h->group;
+  a.block = L.block;
   return a;
 }
 

@@ -1620,9 +1620,10 @@ __device__ bool step_ll128_split(const Args& a, const Ctx& c, uint64_t s, rsrc_t
   const int g = static_cast<int>(uni(static_cast<uint32_t>(c.wave)));  // wave-uniform
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t CU = a.chunk_units, P = a.part_units;
-  const uint32_t unit0 = static_cast<uint32_t>(c.cta) * kWave;  // the workgroup's 64 units
+  const uint32_t B = static_cast<uint32_t>(a.block);        // units of the workgroup's block
+  const uint32_t unit0 = static_cast<uint32_t>(c.cta) * B;
   const uint32_t i = unit0 + c.lane;
-  const bool act = i < CU;
+  const bool act = c.lane < B && i < CU;
   const bool sends = r != a.withhold;
   const rsrc_t own2 = region_rsrc(a, r, a.p2);
   const uint32_t slot2 = a.p2.slot;
@@ -1636,8 +1637,9 @@ __device__ bool step_ll128_split(const Args& a, const Ctx& c, uint64_t s, rsrc_t
   bool wact[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const uint32_t d = unit0 * 4u + static_cast<uint32_t>(e) * 64u + c.lane;
-    wact[e] = d < CU * 4u;
+    const uint32_t w_in = static_cast<uint32_t>(e) * 64u + c.lane;  // word within the block
+    const uint32_t d = unit0 * 4u + w_in;
+    wact[e] = w_in < B * 4u && d < CU * 4u;
     woff[e] = d * 4u;
   }
 #pragma unroll

@@ -149,8 +149,9 @@ def test_split_leaves_slots_rearmed():
 @pytest.mark.parametrize("n", [5, 8, 12, 16])
 def test_ll128_split_within_bound_and_dyadic_exact(n, dtype):
     """The peer-split LL128-style kernel: within the atomic-order bound on ragged counts (1, 2
-    and 4 word slices per lane, one and several 64-unit blocks), bit-exact on inputs whose
-    partial sums are exact in any order, and its destinations and counters clear afterwards."""
+    and 4 word slices per lane; blocks of 1 to 64 units, one or several per chunk), bit-exact on
+    inputs whose partial sums are exact in any order, and its destinations and counters clear
+    afterwards."""
     import torch
 
     from latency_collectives_amd import _ar as A
