@@ -80,7 +80,7 @@ typedef enum {
   AR_LL128_ATOMIC = 4,
   AR_BARRIER2 = 5,
   AR_BARRIER_ONLY = 6,
-  /* values 7..11, 15..20 and 22..32 are internal kernel families (see ar_plan_info); the standalone
+  /* values 7..11, 15..20 and 22..33 are internal kernel families (see ar_plan_info); the standalone
      collectives below are called through their own entry points and named by these ids in
      ar_bench, ar_alg_bytes and ar_plan_info */
   AR_REDUCESCATTER = 12,
@@ -285,11 +285,12 @@ double ar_wallclock_hz(void);
  *                        otherwise (AR_ENORES) instead of starting part of it; no grid-wide
  *                        synchronisation is used. Costs launch time, not device time [0]
  *   AR_OPT_SPLIT         1: with 5..16 ranks, when the launch shape is not forced, the one-pass
- *                        one-shot sentinel and two-shot kernels and the fp32 / bf16 LL128-style
- *                        kernel give each 64 units of a chunk a workgroup of 4 waves, each
- *                        pushing to (adding into) and polling a quarter of the peers (the
- *                        kernel families 26..32 of ar_plan_info), while those workgroups get a
- *                        compute unit each; 0: one wave per 64 units with every peer [1]
+ *                        one-shot LL, one-shot sentinel and two-shot kernels and the fp32 / bf16
+ *                        LL128-style kernel give each 64 units of a chunk a workgroup of 4
+ *                        waves, each pushing to (adding into) and polling a quarter of the
+ *                        peers (the kernel families 26..33 of ar_plan_info), while those
+ *                        workgroups get a compute unit each; 0: one wave per 64 units with every
+ *                        peer [1]
  */
 typedef enum {
   AR_OPT_TIMEOUT_US = 0,
@@ -354,7 +355,8 @@ typedef struct {
                      one half of the one-pass two-shot (17 / 18 with 8-byte units); 19 / 20
                      one-pass broadcast with 16- / 8-byte units; 26 / 27 peer-split one-shot
                      sentinel, 28 / 29 peer-split two-shot, with 16- / 8-byte units; 30 / 31 /
-                     32 peer-split LL128-style with 4 / 1 / 2 word slices per lane */
+                     32 peer-split LL128-style with 4 / 1 / 2 word slices per lane; 33
+                     peer-split one-shot LL */
   int chunks;     /* steps per call (the message is cut into equal chunks at the scratch cap) */
   int ctas;       /* workgroups per rank */
   int threads;    /* threads per workgroup */

@@ -56,6 +56,8 @@ enum Algo : int {
   ALGO_LL128_SPLIT = 30,
   ALGO_LL128_SPLIT_E1 = 31,
   ALGO_LL128_SPLIT_E2 = 32,
+  // peer-split one-shot LL (16-byte lines of 8 bytes of payload)
+  ALGO_ONESHOT_LL_SPLIT = 33,
 };
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).

@@ -471,7 +471,8 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
     const bool splittable = L.kernel_algo == ar::ALGO_ONESHOT_SENTINEL ||
                             L.kernel_algo == ar::ALGO_ONESHOT_SENTINEL_NARROW ||
                             L.kernel_algo == ar::ALGO_TWOSHOT ||
-                            L.kernel_algo == ar::ALGO_TWOSHOT_NARROW;
+                            L.kernel_algo == ar::ALGO_TWOSHOT_NARROW ||
+                            L.kernel_algo == ar::ALGO_ONESHOT_LL;
     // The LL128-style kernel (fp32, bf16) splits the same way: blocks of at most 64 units, one
     // workgroup each (1, 2 or 4 word slices per lane as the block needs), and at least two
     // blocks. Measured at 16 ranks, fp32 (p50 against one 64-unit block per workgroup): two
@@ -500,8 +501,9 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
     }
     if (splittable && h->split && N > 4 && h->ctas == 0 && h->threads == 0 && C > 0) {
       const bool two = L.kernel_algo == ar::ALGO_TWOSHOT || L.kernel_algo == ar::ALGO_TWOSHOT_NARROW;
-      const int id = two ? (ub == 8 ? ar::ALGO_TWOSHOT_SPLIT_NARROW : ar::ALGO_TWOSHOT_SPLIT)
-                         : (ub == 8 ? ar::ALGO_ONESHOT_SPLIT_NARROW : ar::ALGO_ONESHOT_SPLIT);
+      const int id = L.kernel_algo == ar::ALGO_ONESHOT_LL ? ar::ALGO_ONESHOT_LL_SPLIT
+                     : two ? (ub == 8 ? ar::ALGO_TWOSHOT_SPLIT_NARROW : ar::ALGO_TWOSHOT_SPLIT)
+                           : (ub == 8 ? ar::ALGO_ONESHOT_SPLIT_NARROW : ar::ALGO_ONESHOT_SPLIT);
       ar_kernel_fn fs = ar_select_kernel(id, h->dtype, nmax);
       const uint64_t wgs = ceil_div(C, static_cast<uint64_t>(ar::kWave));
       if (fs != nullptr && wgs <= static_cast<uint64_t>(rank_cus)) {
@@ -1315,6 +1317,7 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
   // every logical read and write once: inputs, pushes, slot reads, re-arms, outputs
   switch (L.kernel_algo) {
     case AR_ONESHOT_LL:
+    case ar::ALGO_ONESHOT_LL_SPLIT:
     case ar::ALGO_ONESHOT_LL_MULTI: return static_cast<int64_t>(2 * N * S + 4 * N * (N - 1) * S);
     case AR_ONESHOT_SENTINEL:
     case ar::ALGO_ONESHOT_SENTINEL_MULTI:

@@ -911,6 +911,66 @@ __device__ bool step_oneshot_split(const Args& a, const Ctx& c, uint64_t s, rsrc
   return true;
 }
 
+// One-shot LL AllReduce, peer-split: the LL protocol (§IV "LL") with the peers of each 64
+// lines spread over the waves as in step_oneshot_split. Every wave loads the same 8 bytes per
+// lane, pushes the line {payload, s} to its J peers and polls their lines until the flag equals
+// s; the payloads meet in LDS and wave 0 stores the output. Nothing is re-armed.
+template <int DT, int NMAX>
+__device__ bool step_oneshot_ll_split(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
+                                      rsrc_t out_r, int k, uint64_t& t0, uint64_t& t1) {
+  constexpr int J = split_j<NMAX>();
+  const int N = a.nranks, r = c.rank;
+  const int g = static_cast<int>(uni(static_cast<uint32_t>(c.wave)));  // wave-uniform
+  const uint32_t b = static_cast<uint32_t>(s & 1u);
+  const uint32_t elo = static_cast<uint32_t>(s), ehi = static_cast<uint32_t>(s >> 32);
+  const uint32_t slot = a.ll.slot, CU = a.chunk_units;
+  const uint32_t unit0 = static_cast<uint32_t>(k) * CU;
+  const bool sends = r != a.withhold;
+  const rsrc_t own = region_rsrc(a, r, a.ll);
+  auto ready = [elo, ehi](u32x4 l) { return (l.z == elo) & (l.w == ehi); };
+  const uint32_t i = static_cast<uint32_t>(c.cta) * kWave + c.lane;  // shared by the waves
+  const bool act = i < CU;
+  SplitPeer pe[J];
+  PeerBase pb[J];
+  uint32_t poll_off[J];
+  const uint32_t line0 = b * N * slot + slot_off(a.ll, i);
+#pragma unroll
+  for (int m = 0; m < J; ++m) {
+    pe[m] = split_peer(N, r, g, m);
+    pb[m] = peer_base(a, pe[m], a.ll);
+    poll_off[m] = act && pe[m].live ? line0 + static_cast<uint32_t>(pe[m].q) * slot : kDrop;
+    pin(poll_off[m]);
+  }
+  uint32_t in_off = act ? (unit0 + i) * 8u : kDrop;
+  uint32_t push_off = act ? (b * N + r) * slot + slot_off(a.ll, i) : kDrop;
+  uint32_t out_off = act && g == 0 ? (unit0 + i) * 8u : kDrop;
+  pin(in_off);
+  pin(push_off);
+  pin(out_off);
+  stamp_start(t0, k);
+  uint32_t x[2];
+  load_unit<DT, 8>(in_r, in_off, a.nbytes, x);
+  compiler_fence();
+  wait_vm<0>();
+  if (sends) {
+    const u32x4 line = {x[0], x[1], elo, ehi};
+#pragma unroll
+    for (int m = 0; m < J; ++m) st16<kCoh>(peer_rsrc(pb[m]), push_off, line);
+  }
+  u32x4 l[J];
+  const bool polled = poll_list<J>(a, own, poll_off, l, ready, r, s);
+  u32x2 u[J];
+#pragma unroll
+  for (int m = 0; m < J; ++m) u[m] = u32x2{l[m].x, l[m].y};
+  uint32_t o[2];
+  if (!split_fold<DT, NMAX, 8, J>(c, b, N, r, pe, polled, u, x, o)) return false;
+  store_unit<DT, 8, kOut>(out_r, out_off, a.nbytes, o);
+  compiler_fence();
+  wait_vm<0>();  // the output has landed (wave 0); the others have folded
+  t1 = now_ticks();
+  return true;
+}
+
 // Two-shot AllReduce, peer-split: wave g sends its J peers their partitions (reduce-scatter),
 // polls their contributions to this rank's partition, and after the exchange and the fold (in
 // every wave) sends them the reduced partition and polls theirs into the output (all-gather).
@@ -2311,6 +2371,8 @@ __device__ __forceinline__ void ar_body(const Args& a) {
         ok = step_twoshot<DT, NMAX, 8>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_ONESHOT_SPLIT) {
         ok = step_oneshot_split<DT, NMAX, 16>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_ONESHOT_LL_SPLIT) {
+        ok = step_oneshot_ll_split<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_ONESHOT_SPLIT_NARROW) {
         ok = step_oneshot_split<DT, NMAX, 8>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_TWOSHOT_SPLIT) {

@@ -11,7 +11,7 @@ from tests.gpu_util import (assert_matches, draw, elem_bytes, from_device, handl
 
 pytestmark = pytest.mark.gpu
 
-SPLIT_KERNELS = {26, 27, 28, 29}
+SPLIT_KERNELS = {26, 27, 28, 29, 33}
 LL128_SPLIT = {30, 31, 32}
 COUNTS = [1, 7, 33, 64, 1000, 4097]
 
@@ -25,7 +25,7 @@ def _say(*a):
 def test_split_matches_oracle_and_unsplit(n, dtype):
     from latency_collectives_amd import _ar as A
 
-    algos = ["oneshot_sentinel"] + (["twoshot"] if dtype != "i32" else [])
+    algos = ["oneshot_sentinel", "oneshot_ll"] + (["twoshot"] if dtype != "i32" else [])
     for algo in algos:
         for count in COUNTS + [n * 517 + 3]:
             if dtype == "bf16" and count % 2 == 0:
@@ -88,7 +88,7 @@ def test_split_kernels_planned_for_the_decode_shapes():
         assert A.ar_plan_info(h, 1024, A.AR_ONESHOT_SENTINEL)["kernel"] not in SPLIT_KERNELS
 
 
-@pytest.mark.parametrize("algo", ["oneshot_sentinel", "twoshot"])
+@pytest.mark.parametrize("algo", ["oneshot_sentinel", "oneshot_ll", "twoshot"])
 @pytest.mark.parametrize("n", [8, 16])
 def test_split_persistent_loop_with_drift(n, algo):
     """60 back-to-back AllReduces over 6 input sets with random per-rank delays, every set
@@ -108,7 +108,7 @@ def test_split_persistent_loop_with_drift(n, algo):
             assert_matches(from_device(outs[k * n:(k + 1) * n], x1.dtype), x1, algo, "bf16")
 
 
-@pytest.mark.parametrize("algo", ["oneshot_sentinel", "twoshot"])
+@pytest.mark.parametrize("algo", ["oneshot_sentinel", "oneshot_ll", "twoshot"])
 def test_split_withheld_rank_times_out(algo):
     """A rank that sends nothing: its peers' polls time out (bounded), every wave of a split
     workgroup leaves the step, and the handle reports AR_ETIMEOUT."""
