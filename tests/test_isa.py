@@ -45,12 +45,14 @@ def _ops(ins, op):
 
 
 def test_ll_lines_are_single_16_byte_accesses(kernels):
-    """One-shot LL, fp32, N = 2: pushes and polls are 16-byte buffer accesses with the
-    agent-coherent policy ({8 bytes payload, 8 bytes sequence number} in one store)."""
-    ins = _kernel(kernels, 1, 0, 2)
-    st = [i for i in _ops(ins, "buffer_store_dwordx4") if "sc1" in i]
-    ld = [i for i in _ops(ins, "buffer_load_dwordx4") if "sc1" in i]
-    assert st and ld
+    """One-shot LL, fp32, N = 2, and the peer-split LL kernel, N = 16: pushes and polls are
+    16-byte buffer accesses with the agent-coherent policy ({8 bytes payload, 8 bytes sequence
+    number} in one store)."""
+    for fam, nmax in ((1, 2), (33, 16)):
+        ins = _kernel(kernels, fam, 0, nmax)
+        st = [i for i in _ops(ins, "buffer_store_dwordx4") if "sc1" in i]
+        ld = [i for i in _ops(ins, "buffer_load_dwordx4") if "sc1" in i]
+        assert st and ld, fam
 
 
 def test_sentinel_kernels_unit_widths(kernels):
