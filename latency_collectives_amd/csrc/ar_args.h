@@ -74,7 +74,8 @@ struct Region {
   uint32_t bytes;     // region bytes per rank
   uint32_t slot;      // bytes of one (buffer, source) slot (its pitch), or of one buffer for `acc`
   uint64_t home_pos;  // near region: bits 4r..4r+2 = position of rank r's data in each pitch
-  uint32_t near;      // 1: a near region (slot data in 8 KiB chunks, one per 16 KiB of pitch)
+  uint32_t near;      // 1: a near region (slot data in 8 KiB chunks, one per 16 KiB of pitch);
+                      // kNearTwoHalves: a two-half near region (slot_off)
   uint32_t pad;
 };
 
@@ -94,6 +95,7 @@ constexpr uint64_t kNearArea = kNearRegions * kNearPage;
 // granules; the sub-blocks of one granule differ by a few tens of ns as well).
 constexpr int kNearPositions = 8;
 constexpr uint32_t kNearSub = 2048;
+constexpr uint32_t kNearTwoHalves = 2;  // Region::near of a two-half near region
 
 // Control words (device memory). The host-visible status copy lives in pinned host memory.
 enum Ctl : int {

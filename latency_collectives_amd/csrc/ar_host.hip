@@ -211,6 +211,7 @@ struct ar_handle {
   int record_launch = 0;  // kernels write the launch record (region RG_REC of rank 0)
   int cooperative = 0;    // launches go through the cooperative launch (residency checked)
   int split = 1;          // the peer-split one-pass kernels may be planned
+  int two_halves = 1;     // two-half near slots may be planned (one-shot on two XCDs per rank)
   void** tab = nullptr;
   size_t tab_cap = 0;
   uint64_t* ts = nullptr;
@@ -234,6 +235,7 @@ struct Launch {
   int block = ar::kWave;  // peer-split LL128-style kernel: units per workgroup
   int ranks_per_xcd = 1;
   int xcds_per_rank = 1;
+  bool two_halves = false;  // p1 is a two-half near region (the rank spans one XCD of each half)
   bool near = false;        // slots in the near regions (ll, p1, p2 below, with their pitch and
   ar::Region near_rg[ar::kNearRegions] = {};  //   each rank's data position for this launch)
   unsigned grid = 1;
@@ -540,8 +542,72 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
       (L.kernel_algo == ar::ALGO_TWOSHOT_BULK || L.kernel_algo == ar::ALGO_REDUCESCATTER ||
        L.kernel_algo == ar::ALGO_ALLGATHER || L.kernel_algo == ar::ALGO_BROADCAST))
     rc = shape(false);
+  // Two-half near slots for the one-shot sentinel: the rank runs on two XCDs (one in each half of
+  // the chip, its workgroups alternating over them) and its slots fill the near p1 page, every
+  // granule used: each workgroup's units go to the granules homed in its own XCD's half
+  // (slot_off, region_base). Taken when the message does not fit the near slots of one XCD, and
+  // when one XCD would hold more than one wave per compute unit. Measured at 4 ranks, bf16 (p50,
+  // two halves against the best other plan): 32 KiB 1.21 against 1.34 us, 64 KiB 1.46 against
+  // 1.50, 128 KiB 1.64 against 2.05, 256 KiB 2.21 against 4.2; 1-16 KiB 3-9 % higher (kept on
+  // one XCD).
+  auto two_halves = [&]() -> bool {
+    if (!(h->near_ok && h->two_halves && h->placement == AR_PLACE_XCD &&
+          algo == AR_ONESHOT_SENTINEL && L.xcds_per_rank == 2 && L.chunks == 1 &&
+          (L.kernel_algo == ar::ALGO_ONESHOT_SENTINEL ||
+           L.kernel_algo == ar::ALGO_ONESHOT_SENTINEL_NARROW)))
+      return false;
+    const uint64_t bw = static_cast<uint64_t>(L.threads) * ub;  // bytes per workgroup
+    const uint64_t per_granule = ar::kGranule / bw;  // whole workgroup blocks per granule
+    // workgroups 0, 2, 4, ... run on the first XCD: ceil(ctas / 2) blocks per half
+    const uint64_t slot =
+        ceil_div(ceil_div(static_cast<uint64_t>(L.ctas), 2), per_granule) * 2 * ar::kGranule;
+    if (2ull * N * slot > ar::kNearPage) return false;
+    uint64_t home = 0;
+    for (int r = 0; r < N; ++r) {
+      // The granule of a pitch homed near the half of the rank's first XCD: the one whose four
+      // calibrated positions poll faster from both XCD pairs of that half; the pairs of the other
+      // half must prefer the other granule (else the page is left to the regular plan).
+      const float(*ns)[ar::kNearPositions] = h->near_ns[r][1];
+      auto lead = [&](int half) {  // > 0: the second granule is faster from this half
+        float d = 0.f;
+        for (int p = 2 * half; p < 2 * half + 2; ++p)
+          for (int k = 0; k < 4; ++k) d += ns[p][k] - ns[p][4 + k];
+        return d;
+      };
+      const int h0 = (r % kXcds) / (kXcds / 2);
+      const float d0 = lead(h0), d1 = lead(1 - h0);
+      if (!(d0 * d1 < 0.f)) return false;
+      home |= static_cast<uint64_t>(d0 > 0.f ? 1 : 0) << (4 * r);
+    }
+    L.near = true;
+    L.two_halves = true;
+    L.near_rg[0] = h->rg[RG_LL];
+    L.near_rg[2] = h->rg[RG_P2];
+    ar::Region& rg = L.near_rg[1];
+    rg = h->rg[RG_P1N];
+    rg.near = ar::kNearTwoHalves;
+    rg.slot = static_cast<uint32_t>(slot);
+    rg.home_pos = home;
+    // the descriptor of either half's granules ends inside the page
+    rg.bytes = static_cast<uint32_t>(2ull * N * slot - ar::kGranule);
+    return true;
+  };
+  // (with 8-byte units also when the one-XCD plan could not give every unit a lane)
+  if (near_fits && algo == AR_ONESHOT_SENTINEL && h->two_halves &&
+      (rc == kNoNarrow || (rc == AR_OK && static_cast<uint64_t>(L.ctas) * (L.threads / ar::kWave) >
+                                              static_cast<uint64_t>(cus_per_xcd)))) {
+    const Launch one_xcd = L;
+    const int rc_one = rc;
+    if (shape(false) == AR_OK && two_halves()) {
+      rc = AR_OK;
+    } else {
+      L = one_xcd;
+      rc = rc_one;
+    }
+  }
   if (rc != AR_OK) return rc;
-  if (L.near) {
+  if (!L.near) two_halves();
+  if (L.near && !L.two_halves) {
     // Each rank's slot data goes to the fastest calibrated position of each near region, for the
     // XCD pair of the XCD of its first workgroup: any 2 KiB sub-block of either granule where a
     // single chunk fits, else the start of either granule.
@@ -1024,6 +1090,10 @@ int ar_set_option(ar_handle* h, ar_option opt, int64_t v) {
       if (v != 0 && v != 1) return ar_fail(AR_EINVAL, "cooperative must be 0 or 1");
       h->cooperative = static_cast<int>(v);
       return AR_OK;
+    case AR_OPT_TWO_HALVES:
+      if (v != 0 && v != 1) return ar_fail(AR_EINVAL, "two_halves must be 0 or 1");
+      h->two_halves = static_cast<int>(v);
+      return AR_OK;
   }
   return ar_fail(AR_EINVAL, "unknown option %d", static_cast<int>(opt));
 }
@@ -1282,7 +1352,7 @@ int ar_plan_info(ar_handle* h, size_t count, ar_algo algo, ar_plan* info) {
                       L.kernel_algo == ar::ALGO_ONESHOT_LL_MULTI || narrow_kernel(L.kernel_algo))
                          ? 8
                          : 16;
-  info->near = L.near ? 1 : 0;
+  info->near = L.two_halves ? 2 : L.near ? 1 : 0;
   info->resident_per_cu = occupancy(L.fn, L.threads);
   info->cu_count = h->cu_count;
   return AR_OK;

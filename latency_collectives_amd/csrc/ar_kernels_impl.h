@@ -68,31 +68,44 @@ __device__ __forceinline__ bool decode(const Args& a, Ctx& c) {
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Start of region g in rank `rank`'s block; in a near region every slot's data starts at the
-// rank's position inside the slot's pitch.
-__device__ __forceinline__ uint8_t* region_base(const Args& a, int rank, const Region& g) {
+// rank's position inside the slot's pitch; in a two-half near region at the granule of each pitch
+// homed near the XCD half `half` of the workgroups that poll it (0: the rank's first XCD).
+__device__ __forceinline__ uint8_t* region_base(const Args& a, int rank, const Region& g,
+                                                uint32_t half = 0) {
   const uint32_t pos = static_cast<uint32_t>((g.home_pos >> (4 * rank)) & 7u);
-  return a.base + static_cast<uint64_t>(rank) * a.stride + g.off + pos * kNearSub;
+  const uint32_t lead = g.near == kNearTwoHalves ? ((pos ^ half) & 1u) * kGranule : pos * kNearSub;
+  return a.base + static_cast<uint64_t>(rank) * a.stride + g.off + lead;
 }
 
 // Byte offset of unit i (UB bytes) inside a slot: contiguous in the regular regions; in a near
-// region, 8 KiB chunks of units, one per 16 KiB (2 granules) of the slot's pitch.
+// region, 8 KiB chunks of units, one per 16 KiB (2 granules) of the slot's pitch. In a two-half
+// near region (a rank on two XCDs, one in each half of the chip, its workgroups alternating over
+// them) workgroup w's units go to the granules of w's half: workgroups 2k and 2k + 1 share the
+// k-th block of their granules, and region_base picks the granule.
 template <int UB = 16>
 __device__ __forceinline__ uint32_t slot_off(const Region& g, uint32_t i) {
   const uint32_t byte = i * static_cast<uint32_t>(UB);
+  if (g.near == kNearTwoHalves) {
+    const uint32_t T = blockDim.x, bw = T * static_cast<uint32_t>(UB);
+    const uint32_t w = i / T, k = w >> 1, m = kGranule / bw;
+    return (k / m) * (2 * kGranule) + (k % m) * bw + (byte - w * bw);
+  }
   return g.near ? ((byte / kGranule) * (2 * kGranule) + byte % kGranule) : byte;
 }
 
-__device__ __forceinline__ rsrc_t region_rsrc(const Args& a, int rank, const Region& g) {
-  return make_rsrc(region_base(a, rank, g), g.bytes);
+__device__ __forceinline__ rsrc_t region_rsrc(const Args& a, int rank, const Region& g,
+                                              uint32_t half = 0) {
+  return make_rsrc(region_base(a, rank, g, half), g.bytes);
 }
 
 // Region of the j-th peer after rank r (q = (r + j) mod N), or a descriptor that drops every
 // access when j >= N (the peer does not exist); keeps the push loops free of branches.
-__device__ __forceinline__ rsrc_t peer_rsrc(const Args& a, int r, int j, const Region& g) {
+__device__ __forceinline__ rsrc_t peer_rsrc(const Args& a, int r, int j, const Region& g,
+                                            uint32_t half = 0) {
   int q = r + j;
   if (q >= a.nranks) q -= a.nranks;
   const bool live = j < a.nranks;
-  return make_rsrc(region_base(a, live ? q : 0, g), live ? g.bytes : 0u);
+  return make_rsrc(region_base(a, live ? q : 0, g, half), live ? g.bytes : 0u);
 }
 
 // Where a poll loop reports a timeout: the few kernel arguments the slow path needs, passed by
@@ -322,9 +335,9 @@ __device__ __forceinline__ void rearm(rsrc_t own, uint32_t off0, uint32_t qstrid
 // (NMAX-1 stores, branch-free; peers that do not exist and idle lanes drop their store).
 template <int NMAX, class V>
 __device__ __forceinline__ void push_peers(const Args& a, int r, const Region& g, uint32_t off,
-                                           V line) {
+                                           V line, uint32_t half = 0) {
 #pragma unroll
-  for (int j = 1; j < NMAX; ++j) st_vec<kCoh>(peer_rsrc(a, r, j, g), off, line);
+  for (int j = 1; j < NMAX; ++j) st_vec<kCoh>(peer_rsrc(a, r, j, g, half), off, line);
 }
 
 // Ordering of a step (every step function follows it):
@@ -439,7 +452,9 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
   const uint32_t unit0 = static_cast<uint32_t>(k) * CU;
   const bool sends = r != a.withhold;
   const uint32_t mine = (b * N + r) * slot;
-  const rsrc_t own = region_rsrc(a, r, a.p1);
+  // the XCD half of this workgroup (two-half near slots; 0 elsewhere)
+  const uint32_t half = a.p1.near == kNearTwoHalves ? static_cast<uint32_t>(c.cta) & 1u : 0u;
+  const rsrc_t own = region_rsrc(a, r, a.p1, half);
   const uint32_t peers = peer_mask(N, r);
   const V sent = sentinel_unit<DT, UB>();
   auto ready = [](V l) { return vec_clear<DT>(l); };
@@ -469,7 +484,7 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
       V line;
 #pragma unroll
       for (int e = 0; e < W; ++e) line[e] = x[e];
-      push_peers<NMAX>(a, r, a.p1, push_off, line);
+      push_peers<NMAX>(a, r, a.p1, push_off, line, half);
     }
     V v[NMAX];
     // one round of polls at a time: with a second round in flight the sentinel path measured

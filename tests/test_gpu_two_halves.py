@@ -1,0 +1,125 @@
+"""GPU parity of the one-shot sentinel on two-half near slots (4 ranks, two XCDs per rank, one in
+each half of the chip; every workgroup's units in the near-page granules homed in its own XCD's
+half), through the C ABI, against the CPU oracle: bit-exact for every dtype, equal to the same
+call on regular slots, in persistent loops with rank drift, the slots re-armed afterwards, and a
+withheld rank ending in a bounded timeout."""
+
+import contextlib
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import (assert_matches, draw, elem_bytes, from_device, handle, run_allreduce,
+                            to_device)
+
+pytestmark = pytest.mark.gpu
+
+# bytes per rank: just above the one-XCD near limit of one wave per compute unit, several
+# workgroup shapes (64..256 threads, 8- and 16-byte units), ragged ends, the largest that fits
+SIZES = [16 * 1024 + 8, 32 * 1024, 65536 + 24, 131072, 163840 + 16, 196608 + 40, 262144]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@contextlib.contextmanager
+def two_half_handle(n, max_bytes, dtype, count, **opts):
+    """A handle whose plan for `count` uses two-half slots. The plan takes them only when the
+    calibration of every rank's near page shows the two halves preferring opposite granules;
+    a fresh allocation is tried if a page was ambiguous (at most three)."""
+    from latency_collectives_amd import _ar as A
+
+    with contextlib.ExitStack() as rejected:  # kept open so the next allocation gets other pages
+        for attempt in range(3):
+            cm = handle(n, max_bytes, dtype, **opts)
+            h = cm.__enter__()
+            if A.ar_plan_info(h, count, A.AR_ONESHOT_SENTINEL)["near"] == 2:
+                break
+            _say(f"attempt {attempt}: near page calibration ambiguous, new handle")
+            rejected.push(cm)
+        else:
+            raise AssertionError("no handle planned two-half slots")
+    with contextlib.ExitStack() as keep:
+        keep.push(cm)
+        yield h
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+def test_two_halves_match_oracle_and_regular_slots(dtype):
+    from latency_collectives_amd import _ar as A
+
+    n, eb = 4, elem_bytes(dtype)
+    with two_half_handle(n, max(SIZES), dtype, max(SIZES) // eb) as h:
+        for size in SIZES:
+            count = size // eb
+            if dtype == "bf16" and count % 2 == 0:
+                count -= 1  # odd bf16 lengths: the 2-byte tail path
+            plan = A.ar_plan_info(h, count, A.AR_ONESHOT_SENTINEL)
+            _say(f"case {dtype} count={count} plan={plan}")
+            assert plan["near"] == 2, plan
+            x = draw(dtype, n, count, seed=4000 + count)
+            got = run_allreduce(h, x, "oneshot_sentinel")
+            assert_matches(got, x, "oneshot_sentinel", dtype)
+            A.ar_set_option(h, A.AR_OPT_TWO_HALVES, 0)
+            regular = A.ar_plan_info(h, count, A.AR_ONESHOT_SENTINEL)
+            assert regular["near"] != 2, regular
+            ref = run_allreduce(h, x, "oneshot_sentinel")
+            A.ar_set_option(h, A.AR_OPT_TWO_HALVES, 1)
+            assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
+        for r in range(n):
+            w = A.ar_read_region(h, r, A.REGION_P1_NEAR).view(np.uint32)
+            sentinel = 0xFFFFFFFF if dtype != "i32" else 0x80000000
+            assert np.all(w == sentinel), f"rank {r}: near p1 page not re-armed"
+
+
+def test_two_halves_small_messages_stay_on_one_xcd():
+    """Up to one wave per compute unit of one XCD (16 KiB of bf16) the one-XCD near slots are
+    kept; other rank counts and the two-shot never take two-half slots."""
+    from latency_collectives_amd import _ar as A
+
+    with handle(4, 16384, "bf16") as h:
+        for count in (512, 4096, 8192):
+            assert A.ar_plan_info(h, count, A.AR_ONESHOT_SENTINEL)["near"] == 1
+    for n in (2, 3, 8):
+        with handle(n, 262144, "bf16") as h:
+            for count in (16384, 131072):
+                assert A.ar_plan_info(h, count, A.AR_ONESHOT_SENTINEL)["near"] != 2
+    with handle(4, 262144, "bf16") as h:
+        assert A.ar_plan_info(h, 131072, A.AR_TWOSHOT)["near"] != 2
+
+
+@pytest.mark.parametrize("size", [65536, 262144])
+def test_two_halves_persistent_loop_with_drift(size):
+    """200 back-to-back AllReduces over 5 input sets with random per-rank delays (the 4-rank
+    bf16 workload's iteration count), every set checked."""
+    import torch
+
+    from latency_collectives_amd import _ar as A
+
+    n, count = 4, size // 2
+    xs = [draw("bf16", n, count, seed=900 + k) for k in range(5)]
+    with two_half_handle(n, size, "bf16", count, drift=3) as h:
+        ins = [t for x1 in xs for t in to_device(x1)]
+        outs = [torch.empty_like(t) for t in ins]
+        A.ar_bench(h, ins, outs, len(xs), count, A.AR_ONESHOT_SENTINEL, 200)
+        for k, x1 in enumerate(xs):
+            assert_matches(from_device(outs[k * n:(k + 1) * n], x1.dtype), x1,
+                           "oneshot_sentinel", "bf16")
+
+
+def test_two_halves_withheld_rank_times_out():
+    from latency_collectives_amd import _ar as A
+
+    n, count = 4, 65536
+    x = draw("f32", n, count, seed=11)
+    with two_half_handle(n, count * 4, "f32", count, timeout_us=20000, withhold_rank=2) as h:
+        import torch
+
+        ins = to_device(x)
+        outs = [torch.empty_like(t) for t in ins]
+        A.ar_allreduce(h, ins, outs, count, A.AR_ONESHOT_SENTINEL)
+        torch.cuda.synchronize()
+        with pytest.raises(A.ArError) as e:
+            A.ar_check(h)
+        assert e.value.code == A.AR_ETIMEOUT
