@@ -84,3 +84,16 @@ def test_sol_and_probe_argument_checks(arlib):
 def test_binding_names_match_c_entry_points(arlib):
     for name in arlib.EXPORTS:
         assert callable(getattr(arlib, name)), name
+
+
+def test_binding_constants_match_the_header(arlib):
+    """Every AR_* constant the header defines with an explicit value (data types, algorithms,
+    error codes, placements, options) has the same value in the Python binding."""
+    with open(os.path.join(ROOT, "include", "ar.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    consts = dict((k, int(v)) for k, v in re.findall(r"\b(AR_[A-Z0-9_]+)\s*=\s*(-?\d+)", text))
+    assert len(consts) > 30
+    missing = [k for k in consts if not hasattr(arlib, k)]
+    assert not missing, missing
+    wrong = {k: (v, getattr(arlib, k)) for k, v in consts.items() if getattr(arlib, k) != v}
+    assert not wrong, wrong

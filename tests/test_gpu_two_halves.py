@@ -87,6 +87,9 @@ def test_two_halves_small_messages_stay_on_one_xcd():
                 assert A.ar_plan_info(h, count, A.AR_ONESHOT_SENTINEL)["near"] != 2
     with handle(4, 262144, "bf16") as h:
         assert A.ar_plan_info(h, 131072, A.AR_TWOSHOT)["near"] != 2
+        with pytest.raises(A.ArError) as e:
+            A.ar_set_option(h, A.AR_OPT_TWO_HALVES, 2)
+        assert e.value.code == A.AR_EINVAL
 
 
 @pytest.mark.parametrize("size", [65536, 262144])
