@@ -166,6 +166,8 @@ struct Args {
   int root;             // broadcast: the rank whose input every rank receives
   int group;            // deterministic LL128-style variant: ranks per group
   int block;            // peer-split LL128-style kernel: units per workgroup (1..64)
+  int ag_direct;        // bulk two-shot: owners store their reduced partition straight into
+                        // every rank's output (0: through the all-gather slots)
 };
 
 }  // namespace ar

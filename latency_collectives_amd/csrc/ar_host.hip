@@ -700,6 +700,7 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
   a.algo = algo;
   a.group = h->group;
   a.block = L.block;
+  a.ag_direct = 1;
   return a;
 }
 
@@ -1246,6 +1247,27 @@ int ar_bench_ex(ar_handle* h, const void* const* in_sets, void* const* out_sets,
   a.iters = iters;
   a.drift = h->drift;
   a.nsets = nsets;
+  // The bulk two-shot's owners store into every rank's output during the launch. When a later
+  // iteration could read those bytes as input (an output set overlapping any input set), it
+  // takes the all-gather slots instead, so that every rank writes only its own output.
+  if (iters > 1 && !barrier_only) {
+    std::vector<uintptr_t> lo_in(N, UINTPTR_MAX), hi_in(N, 0), lo_out(N, UINTPTR_MAX), hi_out(N, 0);
+    for (int j = 0; j < nsets; ++j)
+      for (int r = 0; r < N; ++r) {
+        const uintptr_t pi = reinterpret_cast<uintptr_t>(in_sets[j * N + r]);
+        const uintptr_t po = reinterpret_cast<uintptr_t>(out_sets[j * N + r]);
+        lo_in[r] = std::min(lo_in[r], pi);
+        hi_in[r] = std::max(hi_in[r], pi + nbytes);
+        lo_out[r] = std::min(lo_out[r], po);
+        hi_out[r] = std::max(hi_out[r], po + out_bytes);
+      }
+    for (int r1 = 0; r1 < N && a.ag_direct; ++r1)
+      for (int r2 = 0; r2 < N; ++r2)
+        if (lo_in[r1] < hi_out[r2] && lo_out[r2] < hi_in[r1]) {
+          a.ag_direct = 0;
+          break;
+        }
+  }
   // Evenly spaced sets (set j of rank r at set 0's address + j * stride) need no table.
   bool affine = !barrier_only && nsets > 1;
   int64_t sin = 0, sout = 0;
@@ -1399,7 +1421,8 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
     case ar::ALGO_TWOSHOT_SPLIT:
     case ar::ALGO_TWOSHOT_SPLIT_NARROW:
     case ar::ALGO_TWOSHOT_NARROW: return static_cast<int64_t>((N + 1) * S + 7 * (N - 1) * S);
-    case ar::ALGO_TWOSHOT_BULK: return static_cast<int64_t>((N + 1) * S + 5 * (N - 1) * S);
+    // owners store their reduced partition straight into every output (no all-gather slots)
+    case ar::ALGO_TWOSHOT_BULK: return static_cast<int64_t>(2 * N * S + 2 * (N - 1) * S);
     case AR_LL128_ATOMIC:
     case ar::ALGO_LL128_E1:
     case ar::ALGO_LL128_E2:

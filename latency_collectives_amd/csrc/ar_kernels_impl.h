@@ -1113,10 +1113,18 @@ __device__ bool step_twoshot_split(const Args& a, const Ctx& c, uint64_t s, rsrc
 // the coherence point), then stores the step number into its flag slot in each peer's block; the
 // peer's matching wave (same workgroup and wave index, hence the same units) waits for the flags
 // of every source before reading the data. Flags only grow, so nothing is re-armed and no unit
-// is checked: 44 S of traffic at N = 8 instead of 58 S. Double buffering and its credit are
-// those of the sentinel protocol (step s writes buffer s & 1; a peer writes the same buffer again
-// only two steps later, after this rank's flags of the step in between). Inputs are read once
-// and outputs written once, so both carry the non-temporal hint.
+// is checked. Double buffering and its credit are those of the sentinel protocol (step s writes
+// buffer s & 1; a peer writes the same buffer again only two steps later, after this rank's
+// flags of the step in between). Inputs are read once and outputs written once, so both carry
+// the non-temporal hint.
+// The all-gather goes straight into the outputs: every rank's output pointers are kernel
+// arguments, so an owner stores its reduced partition into each rank's output (and its own),
+// waits for those stores and raises its phase-1 flags; a rank whose flags have all arrived has
+// its whole output. No all-gather slot is written or read: 30 S of traffic at N = 8 (44 S through
+// slots, 58 S with sentinels). An owner reaches the all-gather only after every peer's input
+// partition for it has arrived, so an in-place call never overwrites input that is still to be
+// sent. A persistent launch whose output sets overlap its input sets (a later iteration would
+// read bytes other ranks store) keeps the all-gather in the slots (ag_direct = 0).
 __device__ __forceinline__ uint64_t* bulk_flag(const Args& a, int dst, int phase, int src,
                                                const Ctx& c) {
   return reinterpret_cast<uint64_t*>(a.base + static_cast<uint64_t>(dst) * a.stride + a.flg.off) +
@@ -1163,9 +1171,24 @@ __device__ __forceinline__ uint32_t bulk_rot(uint32_t i, uint32_t sk, uint32_t C
   return u >= CU ? u - CU : u;
 }
 
+// Output of the j-th rank after r for the iteration using input/output set `set` (a descriptor
+// that drops every access when j >= N).
+__device__ __forceinline__ rsrc_t peer_out_rsrc(const Args& a, int r, int j, int set) {
+  int q = r + j;
+  if (q >= a.nranks) q -= a.nranks;
+  const bool live = j < a.nranks;
+  const bool affine = a.in_set_stride != 0 || a.out_set_stride != 0;
+  const uint8_t* p;
+  if (affine || a.out_tab == nullptr)
+    p = static_cast<const uint8_t*>(a.out[live ? q : 0]) + static_cast<int64_t>(set) * a.out_set_stride;
+  else
+    p = static_cast<const uint8_t*>(a.out_tab[static_cast<uint32_t>(set) * a.nranks + (live ? q : 0)]);
+  return make_rsrc(uniform_ptr(p), live ? a.out_nbytes : 0u);
+}
+
 template <int DT, int NMAX>
 __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
-                                  rsrc_t out_r, int k, uint64_t& t0, uint64_t& t1) {
+                                  rsrc_t out_r, int k, int set, uint64_t& t0, uint64_t& t1) {
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
   const uint32_t slot1 = a.pf1.slot, slot2 = a.pf2.slot, CU = a.chunk_units, P = a.part_units;
@@ -1184,6 +1207,11 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
     skj[q] = uni((static_cast<uint32_t>(p < N ? p : 0) * kBulkSkew) % CU);
   }
   const uint32_t skr = uni((static_cast<uint32_t>(r) * kBulkSkew) % CU);
+  // all-gather straight into the outputs: the peers' output descriptors of this iteration
+  const bool direct = a.ag_direct != 0;
+  rsrc_t peer_out[NMAX];
+#pragma unroll
+  for (int j = 1; j < NMAX; ++j) peer_out[j] = peer_out_rsrc(a, r, direct ? j : NMAX, set);
   stamp_start(t0, k);
   wait_all_mem();
   // reduce-scatter: partition (r + j) % N of this rank's input to peer j's slot r
@@ -1237,8 +1265,16 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
       v[q] = ld16<kCoh>(own1, ((mask >> q) & 1u) ? off1 + static_cast<uint32_t>(q) * slot1 : kDrop);
     uint32_t o[4];
     fold_rank_order<DT, NMAX, 4>(N, r, x, v, o);
-    if (sends)
-      push_peers<NMAX>(a, r, a.pf2, act ? mine2 + u * 16u : kDrop, u32x4{o[0], o[1], o[2], o[3]});
+    if (sends) {
+      if (direct) {
+#pragma unroll
+        for (int j = 1; j < NMAX; ++j)
+          store_unit<DT, 16, kOut>(peer_out[j], act ? uoff : kDrop, a.nbytes, o);
+      } else {
+        push_peers<NMAX>(a, r, a.pf2, act ? mine2 + u * 16u : kDrop,
+                         u32x4{o[0], o[1], o[2], o[3]});
+      }
+    }
     store_unit<DT, 16, kOut>(out_r, act ? uoff : kDrop, a.nbytes, o);
   }
   if (sends) {
@@ -1247,6 +1283,12 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
   }
   if (!bulk_wait(a, c, 1, s)) return false;
   compiler_fence();
+  if (direct) {
+    // every other owner has stored its partition into this rank's output and waited for the
+    // stores to complete before its flag
+    t1 = now_ticks();
+    return true;
+  }
   // all-gather: every other owner's reduced partition into the output
   for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
     const uint32_t i = i0 + c.lane;
@@ -2350,6 +2392,7 @@ __device__ __forceinline__ void ar_body(const Args& a) {
   for (int it = 0; it < a.iters; ++it) {
     const void* inp = next_in;
     void* outp = next_out;
+    const int cur = set;  // this iteration's input/output set
     if (affine) {
       inp = static_cast<const uint8_t*>(a.in[c.rank]) + set * a.in_set_stride;
       outp = static_cast<uint8_t*>(a.out[c.rank]) + set * a.out_set_stride;
@@ -2401,7 +2444,7 @@ __device__ __forceinline__ void ar_body(const Args& a) {
       } else if constexpr (ALGO == ALGO_LL128_SPLIT_E2) {
         ok = step_ll128_split<DT, NMAX, 2>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_TWOSHOT_BULK) {
-        ok = step_twoshot_bulk<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
+        ok = step_twoshot_bulk<DT, NMAX>(a, c, s, in_r, out_r, k, cur, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_ATOMIC) {
         ok = step_ll128<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_E1) {

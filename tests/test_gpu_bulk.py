@@ -75,7 +75,7 @@ def test_bulk_twoshot_small_slots_near_sized(n):
             got = run_allreduce(h, x, "twoshot")
             assert_matches(got, x, "twoshot", "f32")
         S = count * 4
-        assert A.ar_alg_bytes(h, count, A.AR_TWOSHOT) == (n + 1) * S + 5 * (n - 1) * S, \
+        assert A.ar_alg_bytes(h, count, A.AR_TWOSHOT) == 2 * n * S + 2 * (n - 1) * S, \
             "the bulk two-shot kernel was not the one planned"
 
 
@@ -113,6 +113,39 @@ def test_bulk_twoshot_persistent_loop(drift):
         for k in range(iters):
             got = from_device(outs[k * n:(k + 1) * n], np.uint16)
             assert_matches(got, xs[k], "twoshot", dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "i32"])
+def test_bulk_twoshot_in_place(dtype):
+    """In place (output = input): the owners store the all-gather straight into every rank's
+    buffer, which is also that rank's input; each owner does so only after all its peers' input
+    partitions have reached it, so no input is overwritten before it was sent."""
+    from latency_collectives_amd import _ar as A
+
+    n, count = 8, 250007
+    x = draw(dtype, n, count, seed=77)
+    with handle(n, count * 4, dtype, ctas=2) as h:
+        got = run_allreduce(h, x, "twoshot", inplace=True)
+    assert_matches(got, x, "twoshot", dtype)
+
+
+def test_bulk_twoshot_persistent_in_place_loop():
+    """A persistent in-place loop on one set (each iteration reduces the previous result): the
+    outputs overlap the inputs, so the launch keeps the all-gather in the slots; after k
+    iterations every element is N^(k-1) times the first sum (wrapping int32)."""
+    from latency_collectives_amd import _ar as A
+    import torch
+
+    n, count, iters = 8, 70001, 3
+    x = draw("i32", n, count, seed=78)
+    with handle(n, count * 4, "i32", ctas=2) as h:
+        bufs = to_device(x)
+        A.ar_bench(h, bufs, bufs, 1, count, A.AR_TWOSHOT, iters)
+        got = from_device(bufs, np.int32)
+    first = x.astype(np.int64).sum(axis=0)
+    want = ((first * n ** (iters - 1) + 2 ** 31) % 2 ** 32 - 2 ** 31).astype(np.int32)
+    for r in range(n):
+        assert np.array_equal(got[r], want), f"rank {r}"
 
 
 # ------------------------------------------------------------------ full workload sizes
@@ -259,14 +292,14 @@ def test_full_size_c5_rank_constant():
 def test_alg_bytes_follow_the_launched_kernel():
     """ar_alg_bytes counts each logical read and write once for the protocol actually used: the
     one-pass two-shot re-arms sentinels (58 S at N = 8), the bulk two-shot uses completion flags
-    (44 S)."""
+    and stores the all-gather straight into the outputs (30 S)."""
     from latency_collectives_amd import _ar as A
 
     n = 8
     with handle(n, 64 << 20, "f32") as h:
         s_small, s_big = 4096 * 4, 16 << 20
         assert A.ar_alg_bytes(h, s_small // 4, A.AR_TWOSHOT) == (n + 1) * s_small + 7 * (n - 1) * s_small
-        assert A.ar_alg_bytes(h, s_big // 4, A.AR_TWOSHOT) == (n + 1) * s_big + 5 * (n - 1) * s_big
+        assert A.ar_alg_bytes(h, s_big // 4, A.AR_TWOSHOT) == 2 * n * s_big + 2 * (n - 1) * s_big
         assert A.ar_alg_bytes(h, 1000, A.AR_ONESHOT_LL) == 2 * n * 4000 + 4 * n * (n - 1) * 4000
         assert A.ar_alg_bytes(h, 0, A.AR_ONESHOT_SENTINEL) == 0
 
