@@ -45,7 +45,12 @@ typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_INT32 = 2 } ar_dtype;
  *   AR_TWOSHOT          reduce-scatter to partition owners + all-gather, sentinel synchronised
  *                       (§III.A "Two-shot AllReduce"). For int32 the all-gather carries sums,
  *                       any of which may equal the sentinel, so int32 always runs the
- *                       bandwidth kernel, whose per-wave completion flags ignore the data.
+ *                       bandwidth kernel, whose per-wave completion flags ignore the data; so
+ *                       do fp32 and bf16 messages with up to 8 ranks whose slots do not fit the
+ *                       near pages. The bandwidth kernel's owners store their reduced partition
+ *                       into every rank's output directly (the outputs are all kernel
+ *                       arguments), except in an ar_bench launch whose output sets overlap its
+ *                       input sets.
  *   AR_LL128_ATOMIC     reduce-scatter by atomic adds into the owner's shared destination, then
  *                       the two-shot all-gather (for int32 with completion flags, as above).
  *                       bf16 adds two elements per atomic and rounds to bf16 at every addition.
