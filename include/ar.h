@@ -47,7 +47,9 @@ typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_INT32 = 2 } ar_dtype;
  *                       any of which may equal the sentinel, so int32 always runs the
  *                       bandwidth kernel, whose per-wave completion flags ignore the data; so
  *                       do fp32 and bf16 messages with up to 8 ranks whose slots do not fit the
- *                       near pages. The bandwidth kernel's owners store their reduced partition
+ *                       near pages. With more than 8 ranks, messages whose slots need two near
+ *                       pages per region keep the one-pass kernel on two-page near slots
+ *                       (AR_OPT_TWO_PAGE). The bandwidth kernel's owners store their reduced partition
  *                       into every rank's output directly (the outputs are all kernel
  *                       arguments), except in an ar_bench launch whose output sets overlap its
  *                       input sets.
@@ -85,7 +87,7 @@ typedef enum {
   AR_LL128_ATOMIC = 4,
   AR_BARRIER2 = 5,
   AR_BARRIER_ONLY = 6,
-  /* values 7..11, 15..20 and 22..33 are internal kernel families (see ar_plan_info); the standalone
+  /* values 7..11, 15..20 and 22..34 are internal kernel families (see ar_plan_info); the standalone
      collectives below are called through their own entry points and named by these ids in
      ar_bench, ar_alg_bytes and ar_plan_info */
   AR_REDUCESCATTER = 12,
@@ -300,6 +302,13 @@ double ar_wallclock_hz(void);
  *                        half of the chip) and whose slots fit a near page when every 8 KiB
  *                        granule is used puts each workgroup's units in the granules homed in
  *                        its own XCD's half (ar_plan_info near = 2); 0: regular slots [1]
+ *   AR_OPT_TWO_PAGE      1: a two-shot of more than 8 ranks (AR_PLACE_XCD) whose 2 N slots need
+ *                        more than one near page but whose N slots of one double buffer fit one
+ *                        uses two-page near slots, buffer b in page b of the p1 and p2 near
+ *                        regions (ar_plan_info near = 3), when every rank's second pages are
+ *                        calibrated as mirror images of its first; 0: regular slots [1]. The
+ *                        two-page regions exist in handles of more than 8 ranks whose
+ *                        max_bytes needs them (4 MiB more scratch per rank).
  */
 typedef enum {
   AR_OPT_TIMEOUT_US = 0,
@@ -315,7 +324,8 @@ typedef enum {
   AR_OPT_GROUP = 10,
   AR_OPT_COOPERATIVE = 11,
   AR_OPT_SPLIT = 12,
-  AR_OPT_TWO_HALVES = 13
+  AR_OPT_TWO_HALVES = 13,
+  AR_OPT_TWO_PAGE = 14
 } ar_option;
 int ar_set_option(ar_handle* h, ar_option opt, int64_t value);
 
@@ -366,14 +376,15 @@ typedef struct {
                      one-pass broadcast with 16- / 8-byte units; 26 / 27 peer-split one-shot
                      sentinel, 28 / 29 peer-split two-shot, with 16- / 8-byte units; 30 / 31 /
                      32 peer-split LL128-style with 4 / 1 / 2 word slices per lane; 33
-                     peer-split one-shot LL */
+                     peer-split one-shot LL; 34 one-pass two-shot on two-page near slots */
   int chunks;     /* steps per call (the message is cut into equal chunks at the scratch cap) */
   int ctas;       /* workgroups per rank */
   int threads;    /* threads per workgroup */
   int grid;       /* workgroups launched; those beyond the ranks' (on XCDs no rank uses) exit at
                      once */
   int unit_bytes; /* payload bytes per lane and unit: 16, or 8 for LL and the 8-byte kernels */
-  int near;       /* 1: the slots are in the near regions; 2: two-half near p1 slots */
+  int near;       /* 1: the slots are in the near regions; 2: two-half near p1 slots;
+                     3: two-page near p1 and p2 slots */
   int resident_per_cu; /* workgroups of this kernel and block size that one compute unit holds at
                           once (the HIP occupancy query); the plan leaves one of them free per
                           compute unit whenever this is above 1 */

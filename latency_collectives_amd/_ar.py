@@ -25,7 +25,7 @@ AR_OK, AR_EINVAL, AR_ETOOBIG, AR_ENOTSUP, AR_EHIP, AR_ETIMEOUT, AR_ENORES = 0, -
 AR_PLACE_XCD, AR_PLACE_SAME, AR_PLACE_LINEAR = 0, 1, 2
 (AR_OPT_TIMEOUT_US, AR_OPT_WITHHOLD_RANK, AR_OPT_CTAS, AR_OPT_THREADS, AR_OPT_PLACEMENT,
  AR_OPT_DRIFT, AR_OPT_NARROW, AR_OPT_ROOT, AR_OPT_CHECK_INPUTS, AR_OPT_RECORD_LAUNCH,
- AR_OPT_GROUP, AR_OPT_COOPERATIVE, AR_OPT_SPLIT, AR_OPT_TWO_HALVES) = range(14)
+ AR_OPT_GROUP, AR_OPT_COOPERATIVE, AR_OPT_SPLIT, AR_OPT_TWO_HALVES, AR_OPT_TWO_PAGE) = range(15)
 (REGION_P1, REGION_P2, REGION_LL, REGION_ACC, REGION_CNT, REGION_BAR, REGION_BDAT,
  REGION_LL_NEAR, REGION_P1_NEAR, REGION_P2_NEAR, REGION_PF1, REGION_PF2, REGION_FLG,
  REGION_LAUNCH_RECORD, REGION_SINK) = range(15)

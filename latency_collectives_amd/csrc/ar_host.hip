@@ -107,10 +107,11 @@ int occupancy(ar_kernel_fn fn, int threads) {
 
 // Region layout of one rank block (the same in every block: symmetric memory, §II.B) for N ranks
 // and messages of up to max_bytes per rank, with per-protocol scratch caps. With `near` the block
-// starts with the three 2 MiB near pages and is a whole number of 2 MiB pages; `record` adds the
-// launch record region. Writes the regions and the block size (*stride).
-int layout(int N, uint64_t max_bytes, uint64_t cap_os, uint64_t cap_ts, bool near, bool record,
-           ar::Region* rg, uint64_t* stride) {
+// starts with the near pages (ll, p1, p2: one 2 MiB page each, or with `two_page` two each for p1
+// and p2) and is a whole number of 2 MiB pages; `record` adds the launch record region. Writes the
+// regions and the block size (*stride).
+int layout(int N, uint64_t max_bytes, uint64_t cap_os, uint64_t cap_ts, bool near, bool two_page,
+           bool record, ar::Region* rg, uint64_t* stride) {
   // Slot sizes: large enough for the whole message unless the per-protocol cap says otherwise.
   const uint64_t need_os = round_up(max_bytes, 16);
   const uint64_t need_ts = ceil_div(ceil_div(max_bytes, 16), N) * 16;
@@ -139,15 +140,17 @@ int layout(int N, uint64_t max_bytes, uint64_t cap_os, uint64_t cap_ts, bool nea
   sz[RG_FLG] = {0, 2ull * ar::kMaxRanks * ar::kMaxCtasPerRank * ar::kMaxWavesPerCta * 8};
   sz[RG_REC] = {0, record ? 4ull * ar::kMaxGrid : 0ull};
   sz[RG_SINK] = {0, 16384};
-  // near area: the near ll, p1 and p2 regions, one 2 MiB page each (pitch set per launch)
+  // near area: the near ll, p1 and p2 regions, one 2 MiB page each or two for p1 and p2 (pitch
+  // set per launch)
   uint64_t off = 0;
   for (int i = RG_LLN; i <= RG_P2N; ++i) {
     rg[i] = ar::Region{};
     rg[i].near = 1;
     if (!near) continue;
     rg[i].off = off;
-    rg[i].bytes = static_cast<uint32_t>(ar::kNearPage);
-    off += ar::kNearPage;
+    const uint64_t pages = two_page && i != RG_LLN ? 2 : 1;
+    rg[i].bytes = static_cast<uint32_t>(pages * ar::kNearPage);
+    off += pages * ar::kNearPage;
   }
   for (int i : {RG_P1, RG_P2, RG_LL, RG_ACC, RG_CNT, RG_BAR, RG_BDAT, RG_PF1, RG_PF2, RG_FLG,
                 RG_REC, RG_SINK}) {
@@ -191,6 +194,10 @@ struct ar_handle {
   uint64_t stride = 0;
   // calibrated store -> poll latency of every position, per rank block, near region, XCD pair
   float near_ns[ar::kMaxRanks][ar::kNearRegions][4][ar::kNearPositions] = {};
+  // the same for the second pages of two-page p1 and p2 near regions
+  float near_ns2[ar::kMaxRanks][2][4][ar::kNearPositions] = {};
+  bool two_page = false;  // p1 and p2 near regions span two pages
+  int use_two_page = 1;   // two-page near slots may be planned
   ar::Region rg[kRegions] = {};
   uint32_t* ctl = nullptr;          // device control words
   uint32_t* status_host = nullptr;  // pinned host status words
@@ -236,6 +243,7 @@ struct Launch {
   int ranks_per_xcd = 1;
   int xcds_per_rank = 1;
   bool two_halves = false;  // p1 is a two-half near region (the rank spans one XCD of each half)
+  bool two_page = false;    // p1 and p2 are two-page near regions (buffer b in page b)
   bool near = false;        // slots in the near regions (ll, p1, p2 below, with their pitch and
   ar::Region near_rg[ar::kNearRegions] = {};  //   each rank's data position for this launch)
   unsigned grid = 1;
@@ -325,8 +333,14 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   // Messages whose 2 * N slots fit a near page in one chunk use the near regions: the slot data
   // goes in 8 KiB chunks at a pitch of 16 KiB per chunk.
   const uint64_t near_chunks = ceil_div(units * line, ar::kGranule);
+  // Two-page near slots (handles with more than 8 ranks): the two-shot's 2 N slots need more than
+  // one page and the N slots of one buffer fit one.
+  const bool two_page = h->two_page && h->use_two_page && h->near_ok && units > 0 &&
+                        algo == AR_TWOSHOT && h->placement == AR_PLACE_XCD &&
+                        2ull * N * near_chunks * 2 * ar::kGranule > ar::kNearPage &&
+                        1ull * N * near_chunks * 2 * ar::kGranule <= ar::kNearPage;
   const bool near_fits = h->near_ok && units > 0 &&
-                         2ull * N * near_chunks * 2 * ar::kGranule <= ar::kNearPage &&
+                         (two_page || 2ull * N * near_chunks * 2 * ar::kGranule <= ar::kNearPage) &&
                          (algo == AR_ONESHOT_LL || algo == AR_ONESHOT_SENTINEL ||
                           algo == AR_TWOSHOT || algo == AR_REDUCESCATTER || algo == AR_ALLGATHER ||
                           algo == AR_BROADCAST ||
@@ -545,10 +559,23 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   int rc = shape(near_fits);
   // The multi-pass two-shot kernels (the bulk AllReduce, the loop kernels of the standalone
   // collectives) address regular slots only: they take the regular chunking.
+  // Two-page regions are laid out for the one-pass two-shot kernel with 16-byte units only,
+  // which has an instance of its own for them (the others keep their addressing unchanged).
   if (rc == AR_OK && L.near &&
       (L.kernel_algo == ar::ALGO_TWOSHOT_BULK || L.kernel_algo == ar::ALGO_REDUCESCATTER ||
-       L.kernel_algo == ar::ALGO_ALLGATHER || L.kernel_algo == ar::ALGO_BROADCAST))
+       L.kernel_algo == ar::ALGO_ALLGATHER || L.kernel_algo == ar::ALGO_BROADCAST ||
+       (two_page && L.kernel_algo != ar::ALGO_TWOSHOT)))
     rc = shape(false);
+  if (rc == AR_OK && L.near && two_page) {
+    ar_kernel_fn fp = ar_select_kernel(ar::ALGO_TWOSHOT_TWO_PAGE, h->dtype, nmax);
+    if (fp != nullptr && occupancy(fp, L.threads) >= occupancy(L.fn, L.threads)) {
+      L.fn = fp;
+      L.kernel_algo = ar::ALGO_TWOSHOT_TWO_PAGE;
+      L.two_page = true;
+    } else {
+      rc = shape(false);
+    }
+  }
   // Two-half near slots for the one-shot sentinel: the rank runs on two XCDs (one in each half of
   // the chip, its workgroups alternating over them) and its slots fill the near p1 page, every
   // granule used: each workgroup's units go to the granules homed in its own XCD's half
@@ -633,7 +660,17 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
         for (int k = 0; k < ar::kNearPositions; ++k)
           if (k % 4 <= max_sub && ns[k] < ns[best]) best = k;
         rg.home_pos |= static_cast<uint64_t>(best) << (4 * r);
+        // Two-page region: buffer 1 in the second page, one granule before it when that page
+        // polls faster at the other granule of the pitch (its homes mirror the first page's)
+        // and at its start otherwise (N slots of one buffer fill at most the page, so either
+        // start keeps buffer 1 inside the region; the granules the two buffers share at the
+        // page boundary hold data of different granule classes).
+        if (L.two_page && g > 0) {
+          const float* second = h->near_ns2[r][g - 1][x / 2];
+          if (second[best ^ 4] < second[best]) rg.home_pos |= 8ull << (4 * r);
+        }
       }
+      if (L.two_page && g > 0) rg.bstride = static_cast<uint32_t>(ar::kNearPage);
     }
   }
   if (h->placement == AR_PLACE_XCD)
@@ -1001,7 +1038,17 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
   h->clock_hz = ar_wallclock_hz();
   if (h->clock_hz <= 0.0) h->clock_hz = 100e6;
 
-  if (layout(N, max_bytes, cap_os, cap_ts, true, true, h->rg, &h->stride) != AR_OK) {
+  // Two-page p1 and p2 near regions when more than 8 ranks may run two-shot messages whose
+  // slots (2 N of one partition each) do not fit one page: the one-pass two-shot then keeps its
+  // slots near up to N partition slots per page (16 ranks, fp32, 1 MiB: 13.5 against 17.6 us on
+  // the regular slots; at 8 ranks the bulk two-shot stays faster, 9.3 against 10.1 us).
+  {
+    const uint64_t part = ceil_div(ceil_div(max_bytes, 16), N) * 16;
+    const uint64_t part_slot = std::min(part, std::max<uint64_t>(256, cap_ts / (2 * N)));
+    h->two_page = N > 8 && 2ull * N * ceil_div(part_slot, ar::kGranule) * 2 * ar::kGranule >
+                               ar::kNearPage;
+  }
+  if (layout(N, max_bytes, cap_os, cap_ts, true, h->two_page, true, h->rg, &h->stride) != AR_OK) {
     release(h);
     return nullptr;
   }
@@ -1010,9 +1057,18 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
     return fail(e, "hipMalloc(scratch)");
   h->base = reinterpret_cast<uint8_t*>(round_up(reinterpret_cast<uintptr_t>(h->raw), ar::kNearPage));
   if ((e = hipMemset(h->base, 0, total)) != hipSuccess) return fail(e, "hipMemset(scratch)");
-  if (ar_near_positions(h->base, h->stride, N, h->near_ns) != AR_OK) {
-    release(h);
-    return nullptr;
+  {
+    const uint64_t first[ar::kNearRegions] = {h->rg[RG_LLN].off, h->rg[RG_P1N].off,
+                                              h->rg[RG_P2N].off};
+    const uint64_t second[2] = {h->rg[RG_P1N].off + ar::kNearPage,
+                                h->rg[RG_P2N].off + ar::kNearPage};
+    if (ar_near_positions(h->base, h->stride, N, first, ar::kNearRegions, &h->near_ns[0][0][0][0]) !=
+            AR_OK ||
+        (h->two_page &&
+         ar_near_positions(h->base, h->stride, N, second, 2, &h->near_ns2[0][0][0][0]) != AR_OK)) {
+      release(h);
+      return nullptr;
+    }
   }
   const uint32_t sw = sentinel_word(dtype);
   for (int i : {RG_P1, RG_P2, RG_P1N, RG_P2N})
@@ -1101,6 +1157,10 @@ int ar_set_option(ar_handle* h, ar_option opt, int64_t v) {
     case AR_OPT_TWO_HALVES:
       if (v != 0 && v != 1) return ar_fail(AR_EINVAL, "two_halves must be 0 or 1");
       h->two_halves = static_cast<int>(v);
+      return AR_OK;
+    case AR_OPT_TWO_PAGE:
+      if (v != 0 && v != 1) return ar_fail(AR_EINVAL, "two_page must be 0 or 1");
+      h->use_two_page = static_cast<int>(v);
       return AR_OK;
   }
   return ar_fail(AR_EINVAL, "unknown option %d", static_cast<int>(opt));
@@ -1381,7 +1441,7 @@ int ar_plan_info(ar_handle* h, size_t count, ar_algo algo, ar_plan* info) {
                       L.kernel_algo == ar::ALGO_ONESHOT_LL_MULTI || narrow_kernel(L.kernel_algo))
                          ? 8
                          : 16;
-  info->near = L.two_halves ? 2 : L.near ? 1 : 0;
+  info->near = L.two_page ? 3 : L.two_halves ? 2 : L.near ? 1 : 0;
   info->resident_per_cu = occupancy(L.fn, L.threads);
   info->cu_count = h->cu_count;
   return AR_OK;
@@ -1427,7 +1487,8 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
     case AR_TWOSHOT:
     case ar::ALGO_TWOSHOT_SPLIT:
     case ar::ALGO_TWOSHOT_SPLIT_NARROW:
-    case ar::ALGO_TWOSHOT_NARROW: return static_cast<int64_t>((N + 1) * S + 7 * (N - 1) * S);
+    case ar::ALGO_TWOSHOT_NARROW:
+    case ar::ALGO_TWOSHOT_TWO_PAGE: return static_cast<int64_t>((N + 1) * S + 7 * (N - 1) * S);
     // owners store their reduced partition straight into every output (no all-gather slots)
     case ar::ALGO_TWOSHOT_BULK: return static_cast<int64_t>(2 * N * S + 2 * (N - 1) * S);
     case AR_LL128_ATOMIC:
@@ -1519,7 +1580,8 @@ int noalloc_setup(NoAllocDevice& d, int dev, int nranks, int dtype, hipStream_t 
   AR_HIP(hipDeviceGetAttribute(&h.cu_count, hipDeviceAttributeMultiprocessorCount, dev));
   h.clock_hz = ar_wallclock_hz();
   if (h.clock_hz <= 0.0) h.clock_hz = 100e6;
-  int rc = layout(nranks, h.max_bytes, kNoAllocCap, kNoAllocCap, false, false, h.rg, &h.stride);
+  int rc = layout(nranks, h.max_bytes, kNoAllocCap, kNoAllocCap, false, false, false, h.rg,
+                  &h.stride);
   if (rc != AR_OK) return rc;
   const uint64_t total = kNoAllocCtl + h.stride * static_cast<uint64_t>(nranks);
   if (total > kNoAllocScratchBytes)

@@ -21,11 +21,12 @@ void ar_launch_fill(uint8_t* base, uint64_t stride, int nranks, uint64_t off, ui
 int ar_launch_check(const void* const* in, int nranks, uint32_t nbytes, int dt, uint32_t* ctl,
                     hipStream_t stream);
 
-// Defined in ar_sol.hip: calibrate every near page of every rank block (the first kNearArea
-// bytes of each block, 2 MiB aligned, zero): ns[r][g][p][k] = store -> poll half round trip
-// between XCDs 2p and 2p+1 at position k (granule k / 4, 2 KiB sub-block k % 4) of page g.
-int ar_near_positions(uint8_t* base, uint64_t stride, int nranks,
-                      float (*ns)[ar::kNearRegions][4][ar::kNearPositions]);
+// Defined in ar_sol.hip: calibrate near pages of every rank block (2 MiB aligned, zero, at the
+// byte offsets page_off[0..npages) of each block): ns[((r * npages + g) * 4 + p) * 8 + k] =
+// store -> poll half round trip between XCDs 2p and 2p+1 at position k (granule k / 4, 2 KiB
+// sub-block k % 4) of page g of rank block r.
+int ar_near_positions(uint8_t* base, uint64_t stride, int nranks, const uint64_t* page_off,
+                      int npages, float* ns);
 
 // Defined in ar_host.hip: record an error message for ar_last_error() and return `code`.
 int ar_fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

@@ -65,6 +65,7 @@ ar_kernel_fn ar_select_kernel_i32(int algo, int nmax) {
     case ar::ALGO_BCAST_NARROW: return pick_n<ar::ALGO_BCAST_NARROW>(nmax);
     case ar::ALGO_ONESHOT_SPLIT: return pick_split<ar::ALGO_ONESHOT_SPLIT>(nmax);
     case ar::ALGO_ONESHOT_LL_SPLIT: return pick_split<ar::ALGO_ONESHOT_LL_SPLIT>(nmax);
+    // (no two-page instance: the int32 two-shot always runs the bulk kernel)
     case ar::ALGO_ONESHOT_SPLIT_NARROW: return pick_split<ar::ALGO_ONESHOT_SPLIT_NARROW>(nmax);
     // (no split two-shot: an int32 two-shot always takes the bulk kernel's completion flags)
     default: return nullptr;

@@ -346,15 +346,16 @@ int run_chase(uint64_t bytes, int hops, bool warm_full, double* ns) {
 
 }  // namespace
 
-int ar_near_positions(uint8_t* base, uint64_t stride, int nranks,
-                      float (*ns)[ar::kNearRegions][4][ar::kNearPositions]) {
-  // For every near page of every rank block and every pair of XCDs {2p, 2p+1}: the half round
+int ar_near_positions(uint8_t* base, uint64_t stride, int nranks, const uint64_t* page_off,
+                      int npages, float* ns) {
+  // For every listed page of every rank block and every pair of XCDs {2p, 2p+1}: the half round
   // trip of the pair's ping-pong at each of the positions. The pages are zero before and after.
   for (int r = 0; r < nranks; ++r) {
-    for (int g = 0; g < ar::kNearRegions; ++g) {
-      uint8_t* page = base + static_cast<uint64_t>(r) * stride + g * ar::kNearPage;
+    for (int g = 0; g < npages; ++g) {
+      uint8_t* page = base + static_cast<uint64_t>(r) * stride + page_off[g];
       for (int p = 0; p < 4; ++p) {
-        const int rc = pingpong_positions(page, 2 * p, 2 * p + 1, 24, ns[r][g][p]);
+        float* out = ns + ((static_cast<size_t>(r) * npages + g) * 4 + p) * ar::kNearPositions;
+        const int rc = pingpong_positions(page, 2 * p, 2 * p + 1, 24, out);
         if (rc != AR_OK) return rc;
       }
     }

@@ -67,7 +67,7 @@ def test_auto_selection_matches_oracle(dtype):
     from latency_collectives_amd import _ar as A
 
     # LL, sentinel, two-shot and their internal kernels (multi-pass, narrow, bulk, peer-split)
-    fixed = {1, 2, 3, 7, 8, 9, 10, 11, 26, 27, 28, 29, 33}
+    fixed = {1, 2, 3, 7, 8, 9, 10, 11, 26, 27, 28, 29, 33, 34}
     seen = set()
     eb = elem_bytes(dtype)
     for n in (2, 3, 4, 6, 8, 16):

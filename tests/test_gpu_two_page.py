@@ -1,0 +1,127 @@
+"""GPU parity of the one-pass two-shot on two-page near slots (more than 8 ranks, messages whose
+2 N slots need more than one near page: buffer b of the p1 and p2 near regions in page b, the
+second buffer at its page's start or one granule before it), through the C ABI, against the CPU
+oracle: bit-exact for fp32 and bf16, equal to the same call on regular slots, in persistent loops
+with rank drift, the slots re-armed afterwards, and a withheld rank ending in a bounded timeout."""
+
+import contextlib
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import (assert_matches, draw, elem_bytes, from_device, handle, run_allreduce,
+                            to_device)
+
+pytestmark = pytest.mark.gpu
+
+# bytes per rank at 16 ranks: just above the one-page limit (32 KiB partitions, ragged), between,
+# and the largest whose 16 slots of one buffer fill one page (64 KiB partitions)
+SIZES16 = [524288 + 16, 786432 + 48, 1048576]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@contextlib.contextmanager
+def two_page_handle(n, max_bytes, dtype, count, **opts):
+    """A handle whose plan for `count` uses two-page slots (whatever the calibration of the second
+    pages said: mirrored pages move buffer 1 one granule down, others keep it at the page)."""
+    from latency_collectives_amd import _ar as A
+
+    with handle(n, max_bytes, dtype, **opts) as h:
+        plan = A.ar_plan_info(h, count, A.AR_TWOSHOT)
+        assert plan["near"] == 3, plan
+        yield h
+
+
+def _sentinel(dtype):
+    return {"f32": 0xFFFFFFFF, "bf16": 0xFFFFFFFF, "i32": 0x80000000}[dtype]
+
+
+@pytest.mark.parametrize("n,dtype,sizes", [(16, "f32", SIZES16), (16, "bf16", SIZES16),
+                                           (12, "f32", [786432 + 4])])
+def test_two_page_matches_oracle_and_regular_slots(n, dtype, sizes):
+    from latency_collectives_amd import _ar as A
+
+    eb = elem_bytes(dtype)
+    with two_page_handle(n, max(sizes), dtype, max(sizes) // eb) as h:
+        for size in sizes:
+            count = size // eb
+            if dtype == "bf16" and count % 2 == 0:
+                count -= 1  # odd bf16 lengths: the 2-byte tail path
+            plan = A.ar_plan_info(h, count, A.AR_TWOSHOT)
+            _say(f"case n={n} {dtype} count={count} plan={plan}")
+            assert plan["near"] == 3, plan
+            assert plan["kernel"] == 34, plan
+            x = draw(dtype, n, count, seed=5000 + count)
+            got = run_allreduce(h, x, "twoshot")
+            assert_matches(got, x, "twoshot", dtype)
+            got2 = run_allreduce(h, x, "twoshot")  # the other buffer (page)
+            assert np.array_equal(got.view(np.uint8), got2.view(np.uint8))
+            A.ar_set_option(h, A.AR_OPT_TWO_PAGE, 0)
+            regular = A.ar_plan_info(h, count, A.AR_TWOSHOT)
+            assert regular["near"] == 0, regular
+            ref = run_allreduce(h, x, "twoshot")
+            A.ar_set_option(h, A.AR_OPT_TWO_PAGE, 1)
+            assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
+        for r in range(n):
+            for region in (A.REGION_P1_NEAR, A.REGION_P2_NEAR):
+                w = A.ar_read_region(h, r, region).view(np.uint32)
+                assert w.size * 4 == 2 * (2 << 20), w.size
+                assert np.all(w == _sentinel(dtype)), f"rank {r} region {region}: not re-armed"
+
+
+def test_two_page_only_where_planned():
+    """Small messages of a two-page handle stay on the one-page near slots; int32 (the bulk
+    kernel), 8 ranks (the bulk kernel is faster there) and other placements never take two-page
+    slots; the option takes 0 and 1 only."""
+    from latency_collectives_amd import _ar as A
+
+    with handle(16, 1 << 20, "f32") as h:
+        assert A.ar_plan_info(h, 4096, A.AR_TWOSHOT)["near"] == 1
+        assert A.ar_plan_info(h, 1 << 18, A.AR_ONESHOT_SENTINEL)["near"] != 3
+        A.ar_set_option(h, A.AR_OPT_PLACEMENT, A.AR_PLACE_SAME)
+        assert A.ar_plan_info(h, 1 << 18, A.AR_TWOSHOT)["near"] != 3
+        with pytest.raises(A.ArError) as e:
+            A.ar_set_option(h, A.AR_OPT_TWO_PAGE, 2)
+        assert e.value.code == A.AR_EINVAL
+    with handle(16, 1 << 20, "i32") as h:
+        assert A.ar_plan_info(h, 1 << 18, A.AR_TWOSHOT)["near"] == 0
+    with handle(8, 1 << 20, "f32") as h:
+        assert A.ar_plan_info(h, 1 << 18, A.AR_TWOSHOT)["near"] != 3
+        assert A.ar_region_bytes(h, A.REGION_P1_NEAR) == 2 << 20
+
+
+def test_two_page_persistent_loop_with_drift():
+    """60 back-to-back AllReduces over 3 input sets with random per-rank delays, both buffers
+    (pages) in turn, every set checked."""
+    import torch
+
+    from latency_collectives_amd import _ar as A
+
+    n, count = 16, (1 << 20) // 4
+    xs = [draw("f32", n, count, seed=950 + k) for k in range(3)]
+    with two_page_handle(n, 1 << 20, "f32", count, drift=3) as h:
+        ins = [t for x1 in xs for t in to_device(x1)]
+        outs = [torch.empty_like(t) for t in ins]
+        A.ar_bench(h, ins, outs, len(xs), count, A.AR_TWOSHOT, 60)
+        for k, x1 in enumerate(xs):
+            assert_matches(from_device(outs[k * n:(k + 1) * n], x1.dtype), x1, "twoshot", "f32")
+
+
+def test_two_page_withheld_rank_times_out():
+    from latency_collectives_amd import _ar as A
+
+    n, count = 16, (1 << 20) // 4
+    x = draw("f32", n, count, seed=12)
+    with two_page_handle(n, 1 << 20, "f32", count, timeout_us=20000, withhold_rank=5) as h:
+        import torch
+
+        ins = to_device(x)
+        outs = [torch.empty_like(t) for t in ins]
+        A.ar_allreduce(h, ins, outs, count, A.AR_TWOSHOT)
+        torch.cuda.synchronize()
+        with pytest.raises(A.ArError) as e:
+            A.ar_check(h)
+        assert e.value.code == A.AR_ETIMEOUT
