@@ -1043,9 +1043,9 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
   // slots near up to N partition slots per page (16 ranks, fp32, 1 MiB: 13.5 against 17.6 us on
   // the regular slots; at 8 ranks the bulk two-shot stays faster, 9.3 against 10.1 us).
   {
+    // (near slots hold a whole partition: the scratch caps only chunk the regular slots)
     const uint64_t part = ceil_div(ceil_div(max_bytes, 16), N) * 16;
-    const uint64_t part_slot = std::min(part, std::max<uint64_t>(256, cap_ts / (2 * N)));
-    h->two_page = N > 8 && 2ull * N * ceil_div(part_slot, ar::kGranule) * 2 * ar::kGranule >
+    h->two_page = N > 8 && 2ull * N * ceil_div(part, ar::kGranule) * 2 * ar::kGranule >
                                ar::kNearPage;
   }
   if (layout(N, max_bytes, cap_os, cap_ts, true, h->two_page, true, h->rg, &h->stride) != AR_OK) {
