@@ -54,7 +54,9 @@ typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_INT32 = 2 } ar_dtype;
  *                       arguments), except in an ar_bench launch whose output sets overlap its
  *                       input sets.
  *   AR_LL128_ATOMIC     reduce-scatter by atomic adds into the owner's shared destination, then
- *                       the two-shot all-gather (for int32 with completion flags, as above).
+ *                       an all-gather with completion flags: the owners store their sums
+ *                       straight into every rank's output (as the bandwidth kernel above; the
+ *                       peer-split kernels of small messages keep the sentinel all-gather).
  *                       bf16 adds two elements per atomic and rounds to bf16 at every addition.
  *                       The fp32 and bf16 summation order is not deterministic: per element
  *                       |result - rank-order fold| <= N * 2^-23 * sum_r |x_r| (fp32),

@@ -1314,9 +1314,10 @@ int ar_bench_ex(ar_handle* h, const void* const* in_sets, void* const* out_sets,
   a.iters = iters;
   a.drift = h->drift;
   a.nsets = nsets;
-  // The bulk two-shot's owners store into every rank's output during the launch. When a later
-  // iteration could read those bytes as input (an output set overlapping any input set), it
-  // takes the all-gather slots instead, so that every rank writes only its own output.
+  // The owners of the bulk two-shot and of the flag all-gather of the LL128-style kernel store
+  // into every rank's output during the launch. When a later iteration could read those bytes
+  // as input (an output set overlapping any input set), they take the all-gather slots instead,
+  // so that every rank writes only its own output.
   if (iters > 1 && !barrier_only) {
     std::vector<uintptr_t> lo_in(N, UINTPTR_MAX), hi_in(N, 0), lo_out(N, UINTPTR_MAX), hi_out(N, 0);
     for (int j = 0; j < nsets; ++j)
@@ -1491,9 +1492,12 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
     case ar::ALGO_TWOSHOT_TWO_PAGE: return static_cast<int64_t>((N + 1) * S + 7 * (N - 1) * S);
     // owners store their reduced partition straight into every output (no all-gather slots)
     case ar::ALGO_TWOSHOT_BULK: return static_cast<int64_t>(2 * N * S + 2 * (N - 1) * S);
+    // inputs N S, contributions N S, the owners read, clear and keep their sums 3 S, the
+    // all-gather stored straight into the other outputs (N - 1) S
     case AR_LL128_ATOMIC:
     case ar::ALGO_LL128_E1:
-    case ar::ALGO_LL128_E2:
+    case ar::ALGO_LL128_E2: return static_cast<int64_t>(2 * N * S + 3 * S + (N - 1) * S);
+    // the peer-split kernel's all-gather goes through sentinel slots: 4 (N - 1) S
     case ar::ALGO_LL128_SPLIT:
     case ar::ALGO_LL128_SPLIT_E1:
     case ar::ALGO_LL128_SPLIT_E2: return static_cast<int64_t>(2 * N * S + 3 * S + 4 * (N - 1) * S);
@@ -1501,10 +1505,10 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
     case ar::ALGO_LL128_DET_E1:
     case ar::ALGO_LL128_DET_E2: {
       // inputs N S; contributions N S (binary32: twice that for bf16); the owners read and clear
-      // G group sums, 2 G S (binary32); own partition out S; all-gather 4 (N - 1) S
+      // G group sums, 2 G S (binary32); own partition out S; all-gather into the outputs (N - 1) S
       const uint64_t w = h->dtype == AR_BFLOAT16 ? 2 : 1;
       const uint64_t G = (N + static_cast<uint64_t>(h->group) - 1) / static_cast<uint64_t>(h->group);
-      return static_cast<int64_t>(N * S + w * N * S + 2 * w * G * S + S + 4 * (N - 1) * S);
+      return static_cast<int64_t>(N * S + w * N * S + 2 * w * G * S + S + (N - 1) * S);
     }
     case AR_BARRIER2: return static_cast<int64_t>(2 * N * S + 2 * N * (N - 1) * S);
     default: return 0;

@@ -1337,11 +1337,18 @@ __device__ bool step_twoshot_bulk(const Args& a, const Ctx& c, uint64_t s, rsrc_
 // point for the whole device) and only then increments the counter; the owner, once it reads N
 // arrivals, takes each sum with an atomic exchange against zero, which both reads the final value
 // at that coherence point and clears the destination for step s+2. It then resets the counter
-// and runs the all-gather of the plain two-shot. For int32 the all-gather carries sums, and any
-// int32 value, INT32_MIN included, is a legal sum: a sentinel slot could never tell such a sum
-// from an empty slot. The int32 all-gather therefore uses the bulk two-shot's protocol instead,
-// which does not look at the data: plain coherent pushes into the all-gather data slots, a wait
-// for their completion, then a completion flag per peer (phase 1) that the receivers poll.
+// and runs the all-gather with the bulk two-shot's protocol, which does not look at the data
+// (an int32 sum may be any value, INT32_MIN included, so a sentinel slot could not tell it from
+// an empty one): the owner stores its sums straight into every rank's output (all output
+// pointers are kernel arguments; into the peers' bulk all-gather slots when an ar_bench launch's
+// output sets overlap its input sets), waits for those stores to complete, then raises a
+// completion flag per peer (phase 1) that the receivers poll. Against the sentinel all-gather
+// of the plain two-shot (measured at 16 ranks, fp32, the kernel forced at every size): 4 KiB
+// the same, 16-256 KiB 3-7 % lower, 2 MiB 51 -> 46 us, 4 MiB 92 -> 78 us; int32 against
+// pushes into the slots 4 KiB 4.75 -> 4.1 us, 4 MiB 81 -> 68 us. An owner reaches the
+// all-gather only after every contributor's adds from its input partition have been performed,
+// so an in-place call never overwrites input that is still to be read. (The peer-split kernel
+// of small messages keeps the sentinel all-gather.)
 //
 // bf16 adds two elements per atomic (gfx950's packed bf16 atomic add): the destination holds
 // bf16 and every addition rounds to bf16, so the sum's error is that of a bf16 accumulation in
@@ -1385,10 +1392,12 @@ __device__ __forceinline__ uint32_t* det_ticket(const Args& a, int owner, uint32
 
 template <int DT, int NMAX, int E = 4, bool DET = false>
 __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r, rsrc_t out_r,
-                           int k, uint64_t& t0, uint64_t& t1) {
+                           int k, int set, uint64_t& t0, uint64_t& t1) {
   static_assert(!DET || DT != DT_I32, "an int32 sum does not depend on the order");
   static_assert(E == 1 || E == 2 || E == 4, "word slices per lane");
-  constexpr bool kFlagAG = DT == DT_I32;
+  // The all-gather: owners store their sums straight into every rank's output (ag_direct; else
+  // into the peers' bulk all-gather slots), wait for those stores, then raise completion flags.
+  const bool direct = a.ag_direct != 0;
   // binary32 words of the destination per payload word: 2 for the deterministic bf16 variant
   constexpr uint32_t kAW = (DET && DT == DT_BF16) ? 2u : 1u;
   const int N = a.nranks, r = c.rank;
@@ -1396,14 +1405,14 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
   const uint32_t CU = a.chunk_units, P = a.part_units;
   const bool has_units = c.t0 < CU;
   const uint32_t cnt_idx = (b * kMaxCtasPerRank + c.cta) * kMaxWavesPerCta + c.wave;
-  const rsrc_t own2 = region_rsrc(a, r, a.p2);
-  const uint32_t slot2 = a.p2.slot;
   const uint32_t peers = peer_mask(N, r);
-  const u32x4 sent = sentinel_unit<DT, 16>();
-  auto ready = [](u32x4 l) { return vec_clear<DT>(l); };
   const int M = DET ? a.group : N;  // group size (the plain variant: one group of N)
   const int G = DET ? (N + M - 1) / M : 1;
   const int gme = DET ? r / M : 0, mme = DET ? r - gme * M : 0;
+  // the peers' outputs of this iteration (descriptors that drop every access unless direct)
+  rsrc_t peer_out[NMAX];
+#pragma unroll
+  for (int j = 1; j < NMAX; ++j) peer_out[j] = peer_out_rsrc(a, r, direct ? j : NMAX, set);
   stamp_start(t0, k);
   wait_all_mem();
   // The wave's words of chunk k (pass i0): word d = i0 * 4 + e * 64 + lane.
@@ -1668,14 +1677,18 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
           }
         }
       }
-      if (r != a.withhold) {
-        if constexpr (kFlagAG)
-          push_peers<NMAX>(a, r, a.pf2, act ? (b * N + r) * a.pf2.slot + i * 16u : kDrop, v);
-        else
-          push_peers<NMAX>(a, r, a.p2, act ? (b * N + r) * slot2 + slot_off(a.p2, i) : kDrop, v);
-      }
       const uint32_t o[4] = {v.x, v.y, v.z, v.w};
-      store_unit<DT, 16, kOut>(out_r, act ? (r * P + k * CU + i) * 16u : kDrop, a.nbytes, o);
+      const uint32_t uoff = (r * P + k * CU + i) * 16u;
+      if (r != a.withhold) {
+        if (direct) {
+#pragma unroll
+          for (int j = 1; j < NMAX; ++j)
+            store_unit<DT, 16, kOut>(peer_out[j], act ? uoff : kDrop, a.nbytes, o);
+        } else {
+          push_peers<NMAX>(a, r, a.pf2, act ? (b * N + r) * a.pf2.slot + i * 16u : kDrop, v);
+        }
+      }
+      store_unit<DT, 16, kOut>(out_r, act ? uoff : kDrop, a.nbytes, o);
     }
     if constexpr (!DET) {
       if (c.lane == 0) __hip_atomic_store(my_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1685,17 +1698,15 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
         __hip_atomic_store(det_ticket(a, r, b, c.lane, c), 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    if constexpr (kFlagAG) {
-      if (r != a.withhold) {
-        wait_all_mem();  // the pushed sums are performed before the flags that announce them
-        bulk_signal(a, c, 1, s);
-      }
+    if (r != a.withhold) {
+      wait_all_mem();  // the stored sums are performed before the flags that announce them
+      bulk_signal(a, c, 1, s);
     }
   }
-  if constexpr (kFlagAG) {
-    // a wave with no units of this chunk neither signals nor waits, on every rank alike
-    if (has_units && !bulk_wait(a, c, 1, s)) return false;
-    compiler_fence();
+  // a wave with no units of this chunk neither signals nor waits, on every rank alike
+  if (has_units && !bulk_wait(a, c, 1, s)) return false;
+  compiler_fence();
+  if (!direct) {
     const rsrc_t own_f = region_rsrc(a, r, a.pf2);
     const uint32_t slotf = a.pf2.slot;
     for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
@@ -1714,26 +1725,6 @@ __device__ bool step_ll128(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
         store_unit<DT, 16, kOut>(out_r, ((mask >> q) & 1u) ? (q * P + k * CU + i) * 16u : kDrop,
                            a.nbytes, o);
       }
-    }
-  } else if (CU <= c.T) {
-    // one pass (every unit has its own lane): one round of loads for all sources at a time, as
-    // in the one-pass two-shot
-    const uint32_t i = c.t0 + c.lane;
-    const bool act = i < CU;
-    const uint32_t mask = act ? peers : 0u;
-    const uint32_t off2 = b * N * slot2 + slot_off(a.p2, i);
-    u32x4 v[NMAX];
-    if (!poll_all<NMAX>(a, own2, off2, slot2, mask, v, ready, r, s)) return false;
-    allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v, sent);
-  } else {
-    for (uint32_t i0 = c.t0; i0 < CU; i0 += c.T) {
-      const uint32_t i = i0 + c.lane;
-      const bool act = i < CU;
-      const uint32_t mask = act ? peers : 0u;
-      const uint32_t off2 = b * N * slot2 + slot_off(a.p2, i);
-      u32x4 v[NMAX];
-      if (!poll_lines<NMAX>(a, own2, off2, slot2, mask, v, ready, r, s)) return false;
-      allgather_out<DT, NMAX>(a, r, out_r, own2, off2, mask, k, i, v, sent);
     }
   }
   wait_all_mem();
@@ -2460,17 +2451,17 @@ __device__ __forceinline__ void ar_body(const Args& a) {
       } else if constexpr (ALGO == ALGO_TWOSHOT_BULK) {
         ok = step_twoshot_bulk<DT, NMAX>(a, c, s, in_r, out_r, k, cur, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_ATOMIC) {
-        ok = step_ll128<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
+        ok = step_ll128<DT, NMAX>(a, c, s, in_r, out_r, k, cur, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_E1) {
-        ok = step_ll128<DT, NMAX, 1>(a, c, s, in_r, out_r, k, t_start, t_end);
+        ok = step_ll128<DT, NMAX, 1>(a, c, s, in_r, out_r, k, cur, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_E2) {
-        ok = step_ll128<DT, NMAX, 2>(a, c, s, in_r, out_r, k, t_start, t_end);
+        ok = step_ll128<DT, NMAX, 2>(a, c, s, in_r, out_r, k, cur, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_DET) {
-        ok = step_ll128<DT, NMAX, 4, true>(a, c, s, in_r, out_r, k, t_start, t_end);
+        ok = step_ll128<DT, NMAX, 4, true>(a, c, s, in_r, out_r, k, cur, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_DET_E1) {
-        ok = step_ll128<DT, NMAX, 1, true>(a, c, s, in_r, out_r, k, t_start, t_end);
+        ok = step_ll128<DT, NMAX, 1, true>(a, c, s, in_r, out_r, k, cur, t_start, t_end);
       } else if constexpr (ALGO == ALGO_LL128_DET_E2) {
-        ok = step_ll128<DT, NMAX, 2, true>(a, c, s, in_r, out_r, k, t_start, t_end);
+        ok = step_ll128<DT, NMAX, 2, true>(a, c, s, in_r, out_r, k, cur, t_start, t_end);
       } else if constexpr (ALGO == ALGO_BARRIER2) {
         ok = step_barrier2<DT, NMAX>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_RS_ONEPASS) {
