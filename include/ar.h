@@ -46,8 +46,9 @@ typedef enum { AR_FLOAT32 = 0, AR_BFLOAT16 = 1, AR_INT32 = 2 } ar_dtype;
  *                       (§III.A "Two-shot AllReduce"). For int32 the all-gather carries sums,
  *                       any of which may equal the sentinel, so int32 always runs the
  *                       bandwidth kernel, whose per-wave completion flags ignore the data; so
- *                       do fp32 and bf16 messages with up to 8 ranks whose slots do not fit the
- *                       near pages. With more than 8 ranks, messages whose slots need two near
+ *                       do fp32 and bf16 messages whose slots do not fit the near pages with up
+ *                       to 8 ranks, and with more over 1 MiB per rank. With more than 8 ranks,
+ *                       messages whose slots need two near
  *                       pages per region keep the one-pass kernel on two-page near slots
  *                       (AR_OPT_TWO_PAGE). The bandwidth kernel's owners store their reduced partition
  *                       into every rank's output directly (the outputs are all kernel

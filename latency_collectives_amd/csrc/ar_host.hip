@@ -421,12 +421,14 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
     // is a legal int32 sum), so int32 always takes the bulk kernel, whose completion flags do not
     // look at the data.
     // The fp32 / bf16 two-shot on regular slots (the message does not fit the near pages) with
-    // up to 8 ranks takes the bulk kernel too: its all-gather goes straight into the outputs.
-    // Measured (p50, bulk against the one-pass sentinel kernel): 8 ranks bf16 1 MiB 9.6 against
-    // 11.8 µs, 2 MiB 14.9 against 22.6; 4 ranks bf16 1 MiB 6.1 against 7.1; at 16 ranks fp32
-    // 1 MiB the one-pass kernel stays ahead (18.1 against 20.5 µs).
-    const bool prefer_bulk = algo == AR_TWOSHOT && !near && N <= 8 && h->ctas == 0 &&
-                             h->threads == 0;
+    // up to 8 ranks, or with more and over 1 MiB per rank (beyond the two-page near slots), takes
+    // the bulk kernel too: its all-gather goes straight into the outputs. Measured (p50, bulk
+    // against the one-pass sentinel kernel): 8 ranks bf16 1 MiB 9.6 against 11.8 µs, 2 MiB 14.9
+    // against 22.6; 4 ranks bf16 1 MiB 6.1 against 7.1; 16 ranks fp32 and bf16 2 MiB 31.0 against
+    // 37.9; at 16 ranks fp32 1 MiB on regular slots the one-pass kernel stays ahead (18.1 against
+    // 20.5 µs).
+    const bool prefer_bulk = algo == AR_TWOSHOT && !near && (N <= 8 || nbytes > (1u << 20)) &&
+                             h->ctas == 0 && h->threads == 0;
     const bool flag_protocol = algo == AR_TWOSHOT && (h->dtype == AR_INT32 || prefer_bulk);
     if (flag_protocol && ub == 8) return kNoNarrow;
     if (static_cast<uint64_t>(ctas) * L.threads < C || loop_only || flag_protocol) {

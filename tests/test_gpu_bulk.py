@@ -115,6 +115,27 @@ def test_bulk_twoshot_persistent_loop(drift):
             assert_matches(got, xs[k], "twoshot", dtype)
 
 
+@pytest.mark.parametrize("n,dtype", [(16, "f32"), (16, "bf16"), (12, "f32")])
+def test_bulk_twoshot_above_the_two_page_slots(n, dtype):
+    """More than 8 ranks and over 1 MiB per rank: the fp32 / bf16 two-shot takes the bulk kernel
+    (ragged, odd bf16 length), out of place and in place, against the oracle."""
+    from latency_collectives_amd import _ar as A
+
+    size = (2 << 20) + 48
+    count = size // (2 if dtype == "bf16" else 4)
+    if dtype == "bf16":
+        count -= 1
+    x = draw(dtype, n, count, seed=90 + n)
+    with handle(n, size, dtype) as h:
+        plan = A.ar_plan_info(h, count, A.AR_TWOSHOT)
+        assert plan["kernel"] == 7 and plan["near"] == 0, plan
+        assert A.ar_plan_info(h, (1 << 20) // (2 if dtype == "bf16" else 4), A.AR_TWOSHOT)["kernel"] != 7
+        got = run_allreduce(h, x, "twoshot")
+        assert_matches(got, x, "twoshot", dtype)
+        got_in = run_allreduce(h, x, "twoshot", inplace=True)
+        assert np.array_equal(got.view(np.uint8), got_in.view(np.uint8))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "i32"])
 def test_bulk_twoshot_in_place(dtype):
     """In place (output = input): the owners store the all-gather straight into every rank's
