@@ -60,6 +60,8 @@ enum Algo : int {
   ALGO_ONESHOT_LL_SPLIT = 33,
   // the one-pass two-shot on two-page near slots (more than 8 ranks)
   ALGO_TWOSHOT_TWO_PAGE = 34,
+  // the one-pass one-shot LL on a two-page near ll region (more than 8 ranks)
+  ALGO_ONESHOT_LL_TWO_PAGE = 35,
 };
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).

@@ -107,11 +107,11 @@ int occupancy(ar_kernel_fn fn, int threads) {
 
 // Region layout of one rank block (the same in every block: symmetric memory, §II.B) for N ranks
 // and messages of up to max_bytes per rank, with per-protocol scratch caps. With `near` the block
-// starts with the near pages (ll, p1, p2: one 2 MiB page each, or with `two_page` two each for p1
-// and p2) and is a whole number of 2 MiB pages; `record` adds the launch record region. Writes the
+// starts with the near pages (ll, p1, p2: one 2 MiB page each, two for the regions `two_page`
+// marks) and is a whole number of 2 MiB pages; `record` adds the launch record region. Writes the
 // regions and the block size (*stride).
-int layout(int N, uint64_t max_bytes, uint64_t cap_os, uint64_t cap_ts, bool near, bool two_page,
-           bool record, ar::Region* rg, uint64_t* stride) {
+int layout(int N, uint64_t max_bytes, uint64_t cap_os, uint64_t cap_ts, bool near,
+           const bool* two_page, bool record, ar::Region* rg, uint64_t* stride) {
   // Slot sizes: large enough for the whole message unless the per-protocol cap says otherwise.
   const uint64_t need_os = round_up(max_bytes, 16);
   const uint64_t need_ts = ceil_div(ceil_div(max_bytes, 16), N) * 16;
@@ -148,7 +148,7 @@ int layout(int N, uint64_t max_bytes, uint64_t cap_os, uint64_t cap_ts, bool nea
     rg[i].near = 1;
     if (!near) continue;
     rg[i].off = off;
-    const uint64_t pages = two_page && i != RG_LLN ? 2 : 1;
+    const uint64_t pages = two_page != nullptr && two_page[i - RG_LLN] ? 2 : 1;
     rg[i].bytes = static_cast<uint32_t>(pages * ar::kNearPage);
     off += pages * ar::kNearPage;
   }
@@ -194,9 +194,9 @@ struct ar_handle {
   uint64_t stride = 0;
   // calibrated store -> poll latency of every position, per rank block, near region, XCD pair
   float near_ns[ar::kMaxRanks][ar::kNearRegions][4][ar::kNearPositions] = {};
-  // the same for the second pages of two-page p1 and p2 near regions
-  float near_ns2[ar::kMaxRanks][2][4][ar::kNearPositions] = {};
-  bool two_page = false;  // p1 and p2 near regions span two pages
+  // the same for the second pages of two-page near regions
+  float near_ns2[ar::kMaxRanks][ar::kNearRegions][4][ar::kNearPositions] = {};
+  bool two_page[ar::kNearRegions] = {};  // which near regions (ll, p1, p2) span two pages
   int use_two_page = 1;   // two-page near slots may be planned
   ar::Region rg[kRegions] = {};
   uint32_t* ctl = nullptr;          // device control words
@@ -243,7 +243,8 @@ struct Launch {
   int ranks_per_xcd = 1;
   int xcds_per_rank = 1;
   bool two_halves = false;  // p1 is a two-half near region (the rank spans one XCD of each half)
-  bool two_page = false;    // p1 and p2 are two-page near regions (buffer b in page b)
+  bool two_page = false;    // the plan's near regions span two pages (buffer b in page b): p1
+                            // and p2 for the two-shot, ll for the one-shot LL
   bool near = false;        // slots in the near regions (ll, p1, p2 below, with their pitch and
   ar::Region near_rg[ar::kNearRegions] = {};  //   each rank's data position for this launch)
   unsigned grid = 1;
@@ -335,8 +336,10 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   const uint64_t near_chunks = ceil_div(units * line, ar::kGranule);
   // Two-page near slots (handles with more than 8 ranks): the two-shot's 2 N slots need more than
   // one page and the N slots of one buffer fit one.
-  const bool two_page = h->two_page && h->use_two_page && h->near_ok && units > 0 &&
-                        algo == AR_TWOSHOT && h->placement == AR_PLACE_XCD &&
+  const bool two_page = h->use_two_page && h->near_ok && units > 0 &&
+                        ((algo == AR_TWOSHOT && h->two_page[1] && h->two_page[2]) ||
+                         (algo == AR_ONESHOT_LL && h->two_page[0])) &&
+                        h->placement == AR_PLACE_XCD &&
                         2ull * N * near_chunks * 2 * ar::kGranule > ar::kNearPage &&
                         1ull * N * near_chunks * 2 * ar::kGranule <= ar::kNearPage;
   const bool near_fits = h->near_ok && units > 0 &&
@@ -561,18 +564,21 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   int rc = shape(near_fits);
   // The multi-pass two-shot kernels (the bulk AllReduce, the loop kernels of the standalone
   // collectives) address regular slots only: they take the regular chunking.
-  // Two-page regions are laid out for the one-pass two-shot kernel with 16-byte units only,
-  // which has an instance of its own for them (the others keep their addressing unchanged).
+  // Two-page regions are laid out for the one-pass two-shot kernel with 16-byte units and the
+  // one-pass one-shot LL kernel only, each with an instance of its own for them (the others keep
+  // their addressing unchanged).
   if (rc == AR_OK && L.near &&
       (L.kernel_algo == ar::ALGO_TWOSHOT_BULK || L.kernel_algo == ar::ALGO_REDUCESCATTER ||
        L.kernel_algo == ar::ALGO_ALLGATHER || L.kernel_algo == ar::ALGO_BROADCAST ||
-       (two_page && L.kernel_algo != ar::ALGO_TWOSHOT)))
+       (two_page && L.kernel_algo != ar::ALGO_TWOSHOT && L.kernel_algo != AR_ONESHOT_LL)))
     rc = shape(false);
   if (rc == AR_OK && L.near && two_page) {
-    ar_kernel_fn fp = ar_select_kernel(ar::ALGO_TWOSHOT_TWO_PAGE, h->dtype, nmax);
+    const int tp = L.kernel_algo == ar::ALGO_TWOSHOT ? ar::ALGO_TWOSHOT_TWO_PAGE
+                                                     : ar::ALGO_ONESHOT_LL_TWO_PAGE;
+    ar_kernel_fn fp = ar_select_kernel(tp, h->dtype, nmax);
     if (fp != nullptr && occupancy(fp, L.threads) >= occupancy(L.fn, L.threads)) {
       L.fn = fp;
-      L.kernel_algo = ar::ALGO_TWOSHOT_TWO_PAGE;
+      L.kernel_algo = tp;
       L.two_page = true;
     } else {
       rc = shape(false);
@@ -652,6 +658,9 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
     for (int g = 0; g < ar::kNearRegions; ++g) {
       ar::Region& rg = L.near_rg[g];
       rg = h->rg[RG_LLN + g];
+      // the plan's two-page regions: ll for the one-shot LL, p1 and p2 for the two-shot
+      const bool tp_g =
+          L.two_page && (L.kernel_algo == ar::ALGO_ONESHOT_LL_TWO_PAGE ? g == 0 : g > 0);
       rg.slot = static_cast<uint32_t>(near_chunks * 2 * ar::kGranule);
       for (int r = 0; r < N; ++r) {
         const int x = h->placement == AR_PLACE_XCD    ? r % kXcds
@@ -667,12 +676,12 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
         // and at its start otherwise (N slots of one buffer fill at most the page, so either
         // start keeps buffer 1 inside the region; the granules the two buffers share at the
         // page boundary hold data of different granule classes).
-        if (L.two_page && g > 0) {
-          const float* second = h->near_ns2[r][g - 1][x / 2];
+        if (tp_g) {
+          const float* second = h->near_ns2[r][g][x / 2];
           if (second[best ^ 4] < second[best]) rg.home_pos |= 8ull << (4 * r);
         }
       }
-      if (L.two_page && g > 0) rg.bstride = static_cast<uint32_t>(ar::kNearPage);
+      if (tp_g) rg.bstride = static_cast<uint32_t>(ar::kNearPage);
     }
   }
   if (h->placement == AR_PLACE_XCD)
@@ -1044,11 +1053,18 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
   // slots (2 N of one partition each) do not fit one page: the one-pass two-shot then keeps its
   // slots near up to N partition slots per page (16 ranks, fp32, 1 MiB: 13.5 against 17.6 us on
   // the regular slots; at 8 ranks the bulk two-shot stays faster, 9.3 against 10.1 us).
+  // The one-shot LL likewise gets a two-page ll region when its slots (16-byte lines of 8 bytes of
+  // payload) need it (16 ranks, fp32, 32 KiB: see plan_units).
   {
-    // (near slots hold a whole partition: the scratch caps only chunk the regular slots)
+    // (near slots hold a whole partition or message: the scratch caps only chunk the regular
+    // slots)
+    auto needs_two = [&](uint64_t slot_bytes) {
+      return N > 8 && 2ull * N * ceil_div(slot_bytes, ar::kGranule) * 2 * ar::kGranule >
+                          ar::kNearPage;
+    };
     const uint64_t part = ceil_div(ceil_div(max_bytes, 16), N) * 16;
-    h->two_page = N > 8 && 2ull * N * ceil_div(part, ar::kGranule) * 2 * ar::kGranule >
-                               ar::kNearPage;
+    h->two_page[0] = needs_two(2 * round_up(max_bytes, 8));
+    h->two_page[1] = h->two_page[2] = needs_two(part);
   }
   if (layout(N, max_bytes, cap_os, cap_ts, true, h->two_page, true, h->rg, &h->stride) != AR_OK) {
     release(h);
@@ -1060,14 +1076,17 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
   h->base = reinterpret_cast<uint8_t*>(round_up(reinterpret_cast<uintptr_t>(h->raw), ar::kNearPage));
   if ((e = hipMemset(h->base, 0, total)) != hipSuccess) return fail(e, "hipMemset(scratch)");
   {
-    const uint64_t first[ar::kNearRegions] = {h->rg[RG_LLN].off, h->rg[RG_P1N].off,
-                                              h->rg[RG_P2N].off};
-    const uint64_t second[2] = {h->rg[RG_P1N].off + ar::kNearPage,
-                                h->rg[RG_P2N].off + ar::kNearPage};
+    uint64_t first[ar::kNearRegions], second[ar::kNearRegions];
+    for (int g = 0; g < ar::kNearRegions; ++g) {
+      first[g] = h->rg[RG_LLN + g].off;
+      // (a region of one page calibrates its first page twice: never read)
+      second[g] = first[g] + (h->two_page[g] ? ar::kNearPage : 0);
+    }
+    const bool any = h->two_page[0] || h->two_page[1] || h->two_page[2];
     if (ar_near_positions(h->base, h->stride, N, first, ar::kNearRegions, &h->near_ns[0][0][0][0]) !=
             AR_OK ||
-        (h->two_page &&
-         ar_near_positions(h->base, h->stride, N, second, 2, &h->near_ns2[0][0][0][0]) != AR_OK)) {
+        (any && ar_near_positions(h->base, h->stride, N, second, ar::kNearRegions,
+                                  &h->near_ns2[0][0][0][0]) != AR_OK)) {
       release(h);
       return nullptr;
     }
@@ -1441,7 +1460,9 @@ int ar_plan_info(ar_handle* h, size_t count, ar_algo algo, ar_plan* info) {
   info->threads = L.threads;
   info->grid = static_cast<int>(L.grid);
   info->unit_bytes = (L.kernel_algo == AR_ONESHOT_LL ||
-                      L.kernel_algo == ar::ALGO_ONESHOT_LL_MULTI || narrow_kernel(L.kernel_algo))
+                      L.kernel_algo == ar::ALGO_ONESHOT_LL_MULTI ||
+                      L.kernel_algo == ar::ALGO_ONESHOT_LL_SPLIT ||
+                      L.kernel_algo == ar::ALGO_ONESHOT_LL_TWO_PAGE || narrow_kernel(L.kernel_algo))
                          ? 8
                          : 16;
   info->near = L.two_page ? 3 : L.two_halves ? 2 : L.near ? 1 : 0;
@@ -1480,6 +1501,7 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
   switch (L.kernel_algo) {
     case AR_ONESHOT_LL:
     case ar::ALGO_ONESHOT_LL_SPLIT:
+    case ar::ALGO_ONESHOT_LL_TWO_PAGE:
     case ar::ALGO_ONESHOT_LL_MULTI: return static_cast<int64_t>(2 * N * S + 4 * N * (N - 1) * S);
     case AR_ONESHOT_SENTINEL:
     case ar::ALGO_ONESHOT_SENTINEL_MULTI:
@@ -1586,7 +1608,7 @@ int noalloc_setup(NoAllocDevice& d, int dev, int nranks, int dtype, hipStream_t 
   AR_HIP(hipDeviceGetAttribute(&h.cu_count, hipDeviceAttributeMultiprocessorCount, dev));
   h.clock_hz = ar_wallclock_hz();
   if (h.clock_hz <= 0.0) h.clock_hz = 100e6;
-  int rc = layout(nranks, h.max_bytes, kNoAllocCap, kNoAllocCap, false, false, false, h.rg,
+  int rc = layout(nranks, h.max_bytes, kNoAllocCap, kNoAllocCap, false, nullptr, false, h.rg,
                   &h.stride);
   if (rc != AR_OK) return rc;
   const uint64_t total = kNoAllocCtl + h.stride * static_cast<uint64_t>(nranks);

@@ -365,18 +365,22 @@ __device__ __forceinline__ void push_peers(const Args& a, int r, const Region& g
 // Push: every 8 bytes of the rank's chunk go to every peer as one 16-byte line {payload, s}
 // (§IV "LL"). Receive: poll each peer's line until its flag equals s, then fold in rank order.
 // Nothing needs resetting: an old line carries an older sequence number.
-template <int DT, int NMAX, bool kMulti>
+template <int DT, int NMAX, bool kMulti, bool TWO_PAGE = false>
 __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
                                 rsrc_t out_r, int k, uint64_t& t0,
                                 uint64_t& t1) {
+  static_assert(!TWO_PAGE || !kMulti, "two-page near slots are planned for the one-pass kernel");
   const int N = a.nranks, r = c.rank;
   const uint32_t b = static_cast<uint32_t>(s & 1u);
+  // two-page near ll region (TWO_PAGE, the only instance planned on it): the step's ll
+  // descriptors are those of buffer b
+  const uint32_t bd = TWO_PAGE ? b : 0u;
   const uint32_t elo = static_cast<uint32_t>(s), ehi = static_cast<uint32_t>(s >> 32);
   const uint32_t slot = a.ll.slot, CU = a.chunk_units;
   const uint32_t unit0 = static_cast<uint32_t>(k) * CU;
   const bool sends = r != a.withhold;
   const uint32_t mine = (b * N + r) * slot;
-  const rsrc_t own = region_rsrc(a, r, a.ll);
+  const rsrc_t own = region_rsrc(a, r, a.ll, 0, bd);
   const uint32_t peers = peer_mask(N, r);
   auto ready = [elo, ehi](u32x4 l) { return (l.z == elo) & (l.w == ehi); };
   auto finish = [&](uint32_t i, bool act, const uint32_t* x, const u32x4 (&v)[NMAX]) {
@@ -399,7 +403,7 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
     load_unit<DT, 8>(in_r, in_off, a.nbytes, x);
     compiler_fence();
     wait_vm<0>();
-    if (sends) push_peers<NMAX>(a, r, a.ll, push_off, u32x4{x[0], x[1], elo, ehi});
+    if (sends) push_peers<NMAX>(a, r, a.ll, push_off, u32x4{x[0], x[1], elo, ehi}, 0, bd);
     u32x4 v[NMAX];
     if constexpr (NMAX <= 8) {
       if (!poll_all2<NMAX>(a, own, off0, slot, act ? peers : 0u, v, ready, r, s)) return false;
@@ -2418,6 +2422,8 @@ __device__ __forceinline__ void ar_body(const Args& a) {
       bool ok;
       if constexpr (ALGO == ALGO_ONESHOT_LL) {
         ok = step_oneshot_ll<DT, NMAX, false>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_ONESHOT_LL_TWO_PAGE) {
+        ok = step_oneshot_ll<DT, NMAX, false, true>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_ONESHOT_LL_MULTI) {
         ok = step_oneshot_ll<DT, NMAX, true>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_ONESHOT_SENTINEL) {

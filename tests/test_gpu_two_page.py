@@ -1,5 +1,6 @@
-"""GPU parity of the one-pass two-shot on two-page near slots (more than 8 ranks, messages whose
-2 N slots need more than one near page: buffer b of the p1 and p2 near regions in page b, the
+"""GPU parity of the one-pass two-shot and one-shot LL on two-page near slots (more than 8 ranks,
+messages whose 2 N slots need more than one near page: buffer b of the p1 and p2 (two-shot) or
+ll (LL) near regions in page b, the
 second buffer at its page's start or one granule before it), through the C ABI, against the CPU
 oracle: bit-exact for fp32 and bf16, equal to the same call on regular slots, in persistent loops
 with rank drift, the slots re-armed afterwards, and a withheld rank ending in a bounded timeout."""
@@ -125,3 +126,51 @@ def test_two_page_withheld_rank_times_out():
         with pytest.raises(A.ArError) as e:
             A.ar_check(h)
         assert e.value.code == A.AR_ETIMEOUT
+
+
+# one-shot LL at 16 ranks: 16-byte lines of 8 bytes of payload, so the ll slots of a message
+# above 16 KiB need two pages; 32 KiB fills one page with the 16 slots of one buffer
+LL_SIZES16 = [16384 + 8, 24576 + 4, 32768]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+def test_two_page_oneshot_ll_matches_oracle_and_regular_slots(dtype):
+    from latency_collectives_amd import _ar as A
+
+    n, eb = 16, elem_bytes(dtype)
+    with handle(n, max(LL_SIZES16), dtype) as h:
+        for size in LL_SIZES16:
+            count = size // eb
+            if dtype == "bf16" and count % 2 == 0:
+                count -= 1
+            plan = A.ar_plan_info(h, count, A.AR_ONESHOT_LL)
+            _say(f"case LL n={n} {dtype} count={count} plan={plan}")
+            assert plan["near"] == 3 and plan["kernel"] == 35 and plan["unit_bytes"] == 8, plan
+            x = draw(dtype, n, count, seed=5100 + count)
+            got = run_allreduce(h, x, "oneshot_ll")
+            assert_matches(got, x, "oneshot_ll", dtype)
+            got2 = run_allreduce(h, x, "oneshot_ll")  # the other buffer (page)
+            assert np.array_equal(got.view(np.uint8), got2.view(np.uint8))
+            A.ar_set_option(h, A.AR_OPT_TWO_PAGE, 0)
+            assert A.ar_plan_info(h, count, A.AR_ONESHOT_LL)["near"] == 0
+            ref = run_allreduce(h, x, "oneshot_ll")
+            A.ar_set_option(h, A.AR_OPT_TWO_PAGE, 1)
+            assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
+        # a message that fits one page keeps the one-page slots
+        assert A.ar_plan_info(h, 16384 // eb, A.AR_ONESHOT_LL)["near"] == 1
+
+
+def test_two_page_oneshot_ll_persistent_loop_with_drift():
+    import torch
+
+    from latency_collectives_amd import _ar as A
+
+    n, count = 16, 32768 // 4
+    xs = [draw("f32", n, count, seed=960 + k) for k in range(3)]
+    with handle(n, 32768, "f32", drift=3) as h:
+        assert A.ar_plan_info(h, count, A.AR_ONESHOT_LL)["near"] == 3
+        ins = [t for x1 in xs for t in to_device(x1)]
+        outs = [torch.empty_like(t) for t in ins]
+        A.ar_bench(h, ins, outs, len(xs), count, A.AR_ONESHOT_LL, 60)
+        for k, x1 in enumerate(xs):
+            assert_matches(from_device(outs[k * n:(k + 1) * n], x1.dtype), x1, "oneshot_ll", "f32")
