@@ -81,8 +81,9 @@ struct Region {
                       // bit 4r+3 (two-page region): rank r's second page is mirrored
   uint32_t near;      // 1: a near region (slot data in 8 KiB chunks, one per 16 KiB of pitch);
                       // kNearTwoHalves: a two-half near region (slot_off)
-  uint32_t bstride;   // two-page near region (planned for the one-pass two-shot kernels only):
-                      // the page size, buffer 1 in the second page (region_base); else 0
+  uint32_t bstride;   // two-page near region (planned for the two-page instances of the
+                      // one-pass two-shot and one-shot LL only): the page size, buffer 1 in
+                      // the second page (region_base); else 0
 };
 
 // Memory homes (measured on MI355X): the device's memory is interleaved over the two halves of
@@ -91,8 +92,8 @@ struct Region {
 // line lives in a granule of that half, ~600 ns when it lives in the other half. A near region
 // is one 2 MiB page per rank block; its slots lay their data out in 8 KiB chunks, one chunk per
 // 16 KiB of pitch (one granule of each class), always in the granule homed near the receiving
-// rank. A two-page near region (p1 and p2 of handles with more than 8 ranks, for messages whose
-// slots need more than one page) holds double buffer b in page b. The second page's homes are
+// rank. A two-page near region (ll, p1 and p2 of handles with more than 8 ranks, for messages
+// whose slots need more than one page) holds double buffer b in page b. The second page's homes are
 // calibrated too: when they are the mirror image of the first page's (as consecutive pages of a
 // fresh allocation are: 2 MiB on, a granule of the other half), buffer 1 starts one granule
 // before that page, so that every slot's data stays in a granule of the same class.
