@@ -62,6 +62,8 @@ enum Algo : int {
   ALGO_TWOSHOT_TWO_PAGE = 34,
   // the one-pass one-shot LL on a two-page near ll region (more than 8 ranks)
   ALGO_ONESHOT_LL_TWO_PAGE = 35,
+  // the one-pass one-shot sentinel on a two-page near p1 region (8 and more ranks)
+  ALGO_ONESHOT_SENTINEL_TWO_PAGE = 36,
 };
 
 // How workgroups map to emulated ranks (values match ar_placement in include/ar.h).

@@ -337,8 +337,9 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   // Two-page near slots (handles with more than 8 ranks): the two-shot's 2 N slots need more than
   // one page and the N slots of one buffer fit one.
   const bool two_page = h->use_two_page && h->near_ok && units > 0 &&
-                        ((algo == AR_TWOSHOT && h->two_page[1] && h->two_page[2]) ||
-                         (algo == AR_ONESHOT_LL && h->two_page[0])) &&
+                        ((algo == AR_TWOSHOT && N > 8 && h->two_page[1] && h->two_page[2]) ||
+                         (algo == AR_ONESHOT_LL && h->two_page[0]) ||
+                         (algo == AR_ONESHOT_SENTINEL && N >= 8 && h->two_page[1])) &&
                         h->placement == AR_PLACE_XCD &&
                         2ull * N * near_chunks * 2 * ar::kGranule > ar::kNearPage &&
                         1ull * N * near_chunks * 2 * ar::kGranule <= ar::kNearPage;
@@ -570,13 +571,22 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
   if (rc == AR_OK && L.near &&
       (L.kernel_algo == ar::ALGO_TWOSHOT_BULK || L.kernel_algo == ar::ALGO_REDUCESCATTER ||
        L.kernel_algo == ar::ALGO_ALLGATHER || L.kernel_algo == ar::ALGO_BROADCAST ||
-       (two_page && L.kernel_algo != ar::ALGO_TWOSHOT && L.kernel_algo != AR_ONESHOT_LL)))
+       (two_page && L.kernel_algo != ar::ALGO_TWOSHOT && L.kernel_algo != AR_ONESHOT_LL &&
+        L.kernel_algo != AR_ONESHOT_SENTINEL)))
     rc = shape(false);
   if (rc == AR_OK && L.near && two_page) {
-    const int tp = L.kernel_algo == ar::ALGO_TWOSHOT ? ar::ALGO_TWOSHOT_TWO_PAGE
-                                                     : ar::ALGO_ONESHOT_LL_TWO_PAGE;
+    const int tp = L.kernel_algo == ar::ALGO_TWOSHOT    ? ar::ALGO_TWOSHOT_TWO_PAGE
+                   : L.kernel_algo == AR_ONESHOT_LL     ? ar::ALGO_ONESHOT_LL_TWO_PAGE
+                                                        : ar::ALGO_ONESHOT_SENTINEL_TWO_PAGE;
     ar_kernel_fn fp = ar_select_kernel(tp, h->dtype, nmax);
-    if (fp != nullptr && occupancy(fp, L.threads) >= occupancy(L.fn, L.threads)) {
+    // the plan's workgroups must stay co-resident with the two-page instance (its own register
+    // count), with the same one-workgroup headroom per compute unit as co_resident (XCD
+    // placement)
+    const int occ_api = fp != nullptr ? occupancy(fp, L.threads) : 0;
+    const int occ = occ_api > 1 ? occ_api - 1 : occ_api;
+    const int fit = std::min(cus_per_xcd * occ * L.xcds_per_rank / L.ranks_per_xcd,
+                             ar::kMaxCtasPerRank);
+    if (fp != nullptr && occ >= 1 && L.ctas <= fit) {
       L.fn = fp;
       L.kernel_algo = tp;
       L.two_page = true;
@@ -659,8 +669,9 @@ int plan_units(ar_handle* h, int algo, uint64_t nbytes, int ub, Launch& L) {
       ar::Region& rg = L.near_rg[g];
       rg = h->rg[RG_LLN + g];
       // the plan's two-page regions: ll for the one-shot LL, p1 and p2 for the two-shot
-      const bool tp_g =
-          L.two_page && (L.kernel_algo == ar::ALGO_ONESHOT_LL_TWO_PAGE ? g == 0 : g > 0);
+      const bool tp_g = L.two_page && (L.kernel_algo == ar::ALGO_ONESHOT_LL_TWO_PAGE     ? g == 0
+                                       : L.kernel_algo == ar::ALGO_ONESHOT_SENTINEL_TWO_PAGE ? g == 1
+                                                                                              : g > 0);
       rg.slot = static_cast<uint32_t>(near_chunks * 2 * ar::kGranule);
       for (int r = 0; r < N; ++r) {
         const int x = h->placement == AR_PLACE_XCD    ? r % kXcds
@@ -1065,6 +1076,10 @@ ar_handle* ar_create(int nranks, size_t max_bytes, ar_dtype dtype) {
     const uint64_t part = ceil_div(ceil_div(max_bytes, 16), N) * 16;
     h->two_page[0] = needs_two(2 * round_up(max_bytes, 8));
     h->two_page[1] = h->two_page[2] = needs_two(part);
+    // the one-shot sentinel's p1 slots (a whole message each) from 8 ranks on
+    if (N >= 8 && 2ull * N * ceil_div(round_up(max_bytes, 16), ar::kGranule) * 2 * ar::kGranule >
+                      ar::kNearPage)
+      h->two_page[1] = true;
   }
   if (layout(N, max_bytes, cap_os, cap_ts, true, h->two_page, true, h->rg, &h->stride) != AR_OK) {
     release(h);
@@ -1504,6 +1519,7 @@ int64_t ar_alg_bytes(ar_handle* h, size_t count, ar_algo algo) {
     case ar::ALGO_ONESHOT_LL_TWO_PAGE:
     case ar::ALGO_ONESHOT_LL_MULTI: return static_cast<int64_t>(2 * N * S + 4 * N * (N - 1) * S);
     case AR_ONESHOT_SENTINEL:
+    case ar::ALGO_ONESHOT_SENTINEL_TWO_PAGE:
     case ar::ALGO_ONESHOT_SENTINEL_MULTI:
     case ar::ALGO_ONESHOT_SENTINEL_NARROW:
     case ar::ALGO_ONESHOT_SPLIT:

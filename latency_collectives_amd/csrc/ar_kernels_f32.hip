@@ -69,6 +69,10 @@ ar_kernel_fn ar_select_kernel_f32(int algo, int nmax) {
     case ar::ALGO_BCAST_NARROW: return pick_n<ar::ALGO_BCAST_NARROW>(nmax);
     case ar::ALGO_ONESHOT_SPLIT: return pick_split<ar::ALGO_ONESHOT_SPLIT>(nmax);
     case ar::ALGO_ONESHOT_LL_SPLIT: return pick_split<ar::ALGO_ONESHOT_LL_SPLIT>(nmax);
+    case ar::ALGO_ONESHOT_SENTINEL_TWO_PAGE:  // 8 and more ranks only
+      return nmax == 8 ? ar::ar_kernel<ar::ALGO_ONESHOT_SENTINEL_TWO_PAGE, ar::DT_F32, 8>
+             : nmax == 16 ? ar::ar_kernel<ar::ALGO_ONESHOT_SENTINEL_TWO_PAGE, ar::DT_F32, 16>
+                          : nullptr;
     case ar::ALGO_ONESHOT_LL_TWO_PAGE:  // more than 8 ranks only
       return nmax == 16 ? ar::ar_kernel<ar::ALGO_ONESHOT_LL_TWO_PAGE, ar::DT_F32, 16> : nullptr;
     case ar::ALGO_TWOSHOT_TWO_PAGE:  // more than 8 ranks only

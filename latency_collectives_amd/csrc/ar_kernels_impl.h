@@ -452,11 +452,12 @@ __device__ bool step_oneshot_ll(const Args& a, const Ctx& c, uint64_t s, rsrc_t 
 // the step can return as soon as the output has landed. A unit is UB = 16 bytes, or 8 bytes in
 // the narrow one-pass kernel: twice the lanes, each folding half as many words, which shortens
 // the serial fold of every wave (the fold is one dependent add chain per word and source).
-template <int DT, int NMAX, bool kMulti, int UB = 16>
+template <int DT, int NMAX, bool kMulti, int UB = 16, bool TWO_PAGE = false>
 __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, rsrc_t in_r,
                                       rsrc_t out_r, int k, uint64_t& t0,
                                       uint64_t& t1) {
   static_assert(!kMulti || UB == 16, "the multi-pass path moves 16-byte units");
+  static_assert(!TWO_PAGE || !kMulti, "two-page near slots are planned for the one-pass kernel");
   using V = unit_t<UB>;
   constexpr int W = UB / 4;
   const int N = a.nranks, r = c.rank;
@@ -467,7 +468,10 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
   const uint32_t mine = (b * N + r) * slot;
   // the XCD half of this workgroup (two-half near slots; 0 elsewhere)
   const uint32_t half = a.p1.near == kNearTwoHalves ? static_cast<uint32_t>(c.cta) & 1u : 0u;
-  const rsrc_t own = region_rsrc(a, r, a.p1, half);
+  // two-page near p1 region (TWO_PAGE, the only instance planned on it): the step's p1
+  // descriptors are those of buffer b
+  const uint32_t bd = TWO_PAGE ? b : 0u;
+  const rsrc_t own = region_rsrc(a, r, a.p1, half, bd);
   const uint32_t peers = peer_mask(N, r);
   const V sent = sentinel_unit<DT, UB>();
   auto ready = [](V l) { return vec_clear<DT>(l); };
@@ -497,7 +501,7 @@ __device__ bool step_oneshot_sentinel(const Args& a, const Ctx& c, uint64_t s, r
       V line;
 #pragma unroll
       for (int e = 0; e < W; ++e) line[e] = x[e];
-      push_peers<NMAX>(a, r, a.p1, push_off, line, half);
+      push_peers<NMAX>(a, r, a.p1, push_off, line, half, bd);
     }
     V v[NMAX];
     // one round of polls at a time: with a second round in flight the sentinel path measured
@@ -2430,6 +2434,9 @@ __device__ __forceinline__ void ar_body(const Args& a) {
         ok = step_oneshot_sentinel<DT, NMAX, false>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_ONESHOT_SENTINEL_MULTI) {
         ok = step_oneshot_sentinel<DT, NMAX, true>(a, c, s, in_r, out_r, k, t_start, t_end);
+      } else if constexpr (ALGO == ALGO_ONESHOT_SENTINEL_TWO_PAGE) {
+        ok = step_oneshot_sentinel<DT, NMAX, false, 16, true>(a, c, s, in_r, out_r, k, t_start,
+                                                              t_end);
       } else if constexpr (ALGO == ALGO_ONESHOT_SENTINEL_NARROW) {
         ok = step_oneshot_sentinel<DT, NMAX, false, 8>(a, c, s, in_r, out_r, k, t_start, t_end);
       } else if constexpr (ALGO == ALGO_TWOSHOT) {

@@ -74,9 +74,9 @@ def test_two_page_matches_oracle_and_regular_slots(n, dtype, sizes):
 
 
 def test_two_page_only_where_planned():
-    """Small messages of a two-page handle stay on the one-page near slots; int32 (the bulk
-    kernel), 8 ranks (the bulk kernel is faster there) and other placements never take two-page
-    slots; the option takes 0 and 1 only."""
+    """Small messages of a two-page handle stay on the one-page near slots; the int32 two-shot
+    (the bulk kernel), the 8-rank two-shot (the bulk kernel is faster there) and other placements
+    never take two-page slots; the option takes 0 and 1 only."""
     from latency_collectives_amd import _ar as A
 
     with handle(16, 1 << 20, "f32") as h:
@@ -91,7 +91,9 @@ def test_two_page_only_where_planned():
         assert A.ar_plan_info(h, 1 << 18, A.AR_TWOSHOT)["near"] == 0
     with handle(8, 1 << 20, "f32") as h:
         assert A.ar_plan_info(h, 1 << 18, A.AR_TWOSHOT)["near"] != 3
-        assert A.ar_region_bytes(h, A.REGION_P1_NEAR) == 2 << 20
+        # p2 keeps one page at 8 ranks; p1 has two for the one-shot sentinel's slots
+        assert A.ar_region_bytes(h, A.REGION_P2_NEAR) == 2 << 20
+        assert A.ar_region_bytes(h, A.REGION_P1_NEAR) == 4 << 20
 
 
 def test_two_page_persistent_loop_with_drift():
@@ -174,3 +176,40 @@ def test_two_page_oneshot_ll_persistent_loop_with_drift():
         A.ar_bench(h, ins, outs, len(xs), count, A.AR_ONESHOT_LL, 60)
         for k, x1 in enumerate(xs):
             assert_matches(from_device(outs[k * n:(k + 1) * n], x1.dtype), x1, "oneshot_ll", "f32")
+
+
+# one-shot sentinel from 8 ranks on: its p1 slots hold a whole message, so above 64 KiB (8 ranks)
+# or 32 KiB (16 ranks) they need two pages; 128 KiB and 64 KiB fill one page per buffer
+SENT_CASES = [(8, [65536 + 16, 98304 + 4, 131072]), (16, [32768 + 16, 65536])]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("n,sizes", SENT_CASES)
+def test_two_page_oneshot_sentinel_matches_oracle_and_regular_slots(n, sizes, dtype):
+    from latency_collectives_amd import _ar as A
+
+    eb = elem_bytes(dtype)
+    with handle(n, max(sizes), dtype) as h:
+        for size in sizes:
+            count = size // eb
+            if dtype == "bf16" and count % 2 == 0:
+                count -= 1
+            plan = A.ar_plan_info(h, count, A.AR_ONESHOT_SENTINEL)
+            _say(f"case sentinel n={n} {dtype} count={count} plan={plan}")
+            assert plan["near"] == 3 and plan["kernel"] == 36, plan
+            x = draw(dtype, n, count, seed=5200 + count)
+            got = run_allreduce(h, x, "oneshot_sentinel")
+            assert_matches(got, x, "oneshot_sentinel", dtype)
+            got2 = run_allreduce(h, x, "oneshot_sentinel")  # the other buffer (page)
+            assert np.array_equal(got.view(np.uint8), got2.view(np.uint8))
+            A.ar_set_option(h, A.AR_OPT_TWO_PAGE, 0)
+            assert A.ar_plan_info(h, count, A.AR_ONESHOT_SENTINEL)["near"] == 0
+            ref = run_allreduce(h, x, "oneshot_sentinel")
+            A.ar_set_option(h, A.AR_OPT_TWO_PAGE, 1)
+            assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
+        for r in range(n):
+            w = A.ar_read_region(h, r, A.REGION_P1_NEAR).view(np.uint32)
+            assert w.size * 4 == 2 * (2 << 20), w.size
+            assert np.all(w == _sentinel(dtype)), f"rank {r}: p1 near region not re-armed"
+        if n == 8:  # the two-shot of 8 ranks keeps the bulk kernel on regular slots
+            assert A.ar_plan_info(h, count, A.AR_TWOSHOT)["near"] != 3
