@@ -776,7 +776,7 @@ ar::Args base_args(ar_handle* h, int algo, uint64_t nbytes, const Launch& L) {
 // kernel (A) measured on MI355X (`python bench.py --auto-sweep`: p50 of 100 back-to-back calls,
 // fp32 uniform, bf16 normal, int32 on [-2^20, 2^20]) for N in {2,3,4,8,16} and 128 B .. 2 MiB
 // per rank; a cell changed its kernel only when another led by 3 % or more in the latest of
-// five sweeps (the fifth on the current kernels). A call uses the row of the
+// six sweeps (the sixth on the current kernels). A call uses the row of the
 // smallest measured N >= its N and the column of the smallest measured size >= its size; above
 // 2 MiB, the last column. For fp32 and bf16 only the fixed-order kernels are candidates, so that
 // AUTO stays bit-reproducible; the int32 atomic sum is exact in any order. (int32 two-shot runs
@@ -794,7 +794,7 @@ constexpr char kAutoTable[3][5][9] = {
     },
     {
         // bf16
-        "SLLLLSST",  // N = 2
+        "SSLLLSST",  // N = 2
         "SSSSSSTT",  // N = 3
         "SSLSSSTT",  // N = 4
         "SSSSSTTT",  // N = 8
